@@ -1,0 +1,206 @@
+"""fp64 CPU oracle for the selective state-space scans.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this package.  It shares no code
+with the HIP library in ``selective_state_space_amd``: the loops live in
+``oracle.c`` (plain C, fp64, OpenMP over independent units) and this module only
+converts numpy arrays to contiguous float64 and calls them through ctypes.
+
+Each function returns ``(y, h_out)`` as float64 numpy arrays.  Inputs are taken
+exactly as given (a bf16 input is expected already rounded to bf16 and then
+widened, so that the oracle sees the values the GPU sees).
+
+Which passage each loop follows is cited at the loop in ``oracle.c``:
+  m1_scan / m1_step  - TorchMamba README (Models table, Math notes M1);
+                       burn_mamba Mamba1 docs (selective_scan, selective_scan_step)
+  ssd                - TorchMamba README (Models table, Math notes M2)
+  trap               - TorchMamba README (Math notes M3 SISO);
+                       mamba3-minimal README (Two-SSD Decomposition)
+  mimo               - TorchMamba README (Math notes MIMO)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lock = threading.Lock()
+_lib = None
+
+_D = ctypes.POINTER(ctypes.c_double)
+_I = ctypes.c_int64
+
+
+def build(force: bool = False) -> str:
+    """Compile oracle.c into liboracle.so with gcc (-O2, OpenMP, no fast-math)."""
+    with _lock:
+        if force or not os.path.exists(_LIB_PATH) or (
+            os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC)
+        ):
+            tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+            subprocess.check_call(
+                ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared",
+                 "-Wall", "-o", tmp, _SRC, "-lm"]
+            )
+            os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        build()
+        lib = ctypes.CDLL(_LIB_PATH)
+        lib.oracle_m1_scan.argtypes = [_D] * 9 + [_I] * 4
+        lib.oracle_m1_step.argtypes = [_D] * 9 + [_I] * 3
+        lib.oracle_ssd.argtypes = [_D] * 7 + [_I] * 6
+        lib.oracle_trap.argtypes = [_D] * 10 + [_I] * 6
+        lib.oracle_mimo.argtypes = [_D] * 10 + [_I] * 6
+        lib.oracle_set_threads.argtypes = [ctypes.c_int]
+        lib.oracle_get_threads.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def set_threads(n: int) -> None:
+    _load().oracle_set_threads(int(n))
+
+
+def get_threads() -> int:
+    return int(_load().oracle_get_threads())
+
+
+def _f64(a):
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+
+def _p(a):
+    if a is None:
+        return ctypes.cast(None, _D)
+    return a.ctypes.data_as(_D)
+
+
+def _opt(a, shape):
+    if a is None:
+        return None
+    a = _f64(a)
+    if a.shape != tuple(shape):
+        raise ValueError("shape %s, expected %s" % (a.shape, tuple(shape)))
+    return a
+
+
+def _chk(a, shape, name):
+    a = _f64(a)
+    if a.shape != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, a.shape, tuple(shape)))
+    return a
+
+
+def m1_scan(x, dt, A, B, C, D=None, h0=None):
+    """Mamba-1 selective scan.  x, dt (b, L, D); A (D, N); B, C (b, L, N)."""
+    x = _f64(x)
+    b, L, Dm = x.shape
+    A = _f64(A)
+    N = A.shape[1]
+    dt = _chk(dt, (b, L, Dm), "dt")
+    A = _chk(A, (Dm, N), "A")
+    B = _chk(B, (b, L, N), "B")
+    C = _chk(C, (b, L, N), "C")
+    D = _opt(D, (Dm,))
+    h0 = _opt(h0, (b, Dm, N))
+    y = np.empty((b, L, Dm))
+    h = np.empty((b, Dm, N))
+    _load().oracle_m1_scan(_p(x), _p(dt), _p(A), _p(B), _p(C), _p(D), _p(h0),
+                           _p(y), _p(h), b, L, Dm, N)
+    return y, h
+
+
+def m1_step(x, dt, A, B, C, D, h):
+    """One Mamba-1 step.  x, dt (b, D); B, C (b, N); h (b, D, N)."""
+    x = _f64(x)
+    b, Dm = x.shape
+    A = _f64(A)
+    N = A.shape[1]
+    dt = _chk(dt, (b, Dm), "dt")
+    B = _chk(B, (b, N), "B")
+    C = _chk(C, (b, N), "C")
+    D = _opt(D, (Dm,))
+    h = _chk(h, (b, Dm, N), "h")
+    y = np.empty((b, Dm))
+    h_out = np.empty((b, Dm, N))
+    _load().oracle_m1_step(_p(x), _p(dt), _p(A), _p(B), _p(C), _p(D), _p(h),
+                           _p(h_out), _p(y), b, Dm, N)
+    return y, h_out
+
+
+def ssd(X, logdecay, B, C, h0=None):
+    """Mamba-2 SSD.  X (b, L, H, P); logdecay (b, L, H); B, C (b, L, G, N)."""
+    X = _f64(X)
+    b, L, H, P = X.shape
+    B = _f64(B)
+    G, N = B.shape[2], B.shape[3]
+    if G <= 0 or H % G:
+        raise ValueError("H must be a multiple of G")
+    logdecay = _chk(logdecay, (b, L, H), "logdecay")
+    B = _chk(B, (b, L, G, N), "B")
+    C = _chk(C, (b, L, G, N), "C")
+    h0 = _opt(h0, (b, H, N, P))
+    Y = np.empty((b, L, H, P))
+    h = np.empty((b, H, N, P))
+    _load().oracle_ssd(_p(X), _p(logdecay), _p(B), _p(C), _p(h0), _p(Y), _p(h),
+                       b, L, H, P, G, N)
+    return Y, h
+
+
+def trap(X, logdecay, B, C, beta, gamma, theta=None, h0=None):
+    """Mamba-3 SISO.  X (b, L, H, P); logdecay, beta, gamma (b, L, H);
+    B, C (b, L, G, N); theta (b, L, H, N/2) or None."""
+    X = _f64(X)
+    b, L, H, P = X.shape
+    B = _f64(B)
+    G, N = B.shape[2], B.shape[3]
+    if G <= 0 or H % G:
+        raise ValueError("H must be a multiple of G")
+    if theta is not None and N % 2:
+        raise ValueError("rotation needs an even N")
+    logdecay = _chk(logdecay, (b, L, H), "logdecay")
+    beta = _chk(beta, (b, L, H), "beta")
+    gamma = _chk(gamma, (b, L, H), "gamma")
+    B = _chk(B, (b, L, G, N), "B")
+    C = _chk(C, (b, L, G, N), "C")
+    theta = _opt(theta, (b, L, H, N // 2))
+    h0 = _opt(h0, (b, H, N, P))
+    Y = np.empty((b, L, H, P))
+    h = np.empty((b, H, N, P))
+    _load().oracle_trap(_p(X), _p(logdecay), _p(B), _p(C), _p(beta), _p(gamma),
+                        _p(theta), _p(h0), _p(Y), _p(h), b, L, H, P, G, N)
+    return Y, h
+
+
+def mimo(X, logdecay, B, C, beta, gamma, theta=None, h0=None):
+    """Mamba-3 MIMO.  X (b, L, H, P, R); B, C (b, L, H, N, R);
+    logdecay, beta, gamma (b, L, H); theta (b, L, H, N/2) or None."""
+    X = _f64(X)
+    b, L, H, P, R = X.shape
+    B = _f64(B)
+    N = B.shape[3]
+    if theta is not None and N % 2:
+        raise ValueError("rotation needs an even N")
+    logdecay = _chk(logdecay, (b, L, H), "logdecay")
+    beta = _chk(beta, (b, L, H), "beta")
+    gamma = _chk(gamma, (b, L, H), "gamma")
+    B = _chk(B, (b, L, H, N, R), "B")
+    C = _chk(C, (b, L, H, N, R), "C")
+    theta = _opt(theta, (b, L, H, N // 2))
+    h0 = _opt(h0, (b, H, N, P))
+    Y = np.empty((b, L, H, P, R))
+    h = np.empty((b, H, N, P))
+    _load().oracle_mimo(_p(X), _p(logdecay), _p(B), _p(C), _p(beta), _p(gamma),
+                        _p(theta), _p(h0), _p(Y), _p(h), b, L, H, P, N, R)
+    return Y, h

@@ -1,0 +1,332 @@
+/*
+ * oracle.c -- plain fp64 CPU reference loops for the selective state-space
+ * scans (Mamba-1 selective scan and its decode step, Mamba-2 scalar-decay SSD,
+ * Mamba-3 SISO exponential-trapezoidal recurrence with data-dependent RoPE,
+ * Mamba-3 MIMO rank-R recurrence).
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the oracle that the GPU library is
+ * checked against.  It shares no code, header, table or helper with the HIP
+ * library under selective_state_space_amd/, and nothing in the product path
+ * may call it.  Every function is one sequential-in-time loop written straight
+ * from the recurrence it names; the only parallelism is OpenMP over
+ * independent (batch, channel) or (batch, head) units.  Built -O2, no
+ * fast-math, so the arithmetic follows IEEE double as written.
+ *
+ * Layouts are row-major and contiguous, last-named axis fastest:
+ *   Mamba-1:  x, dt, y (batch, L, D); B, C (batch, L, N); A (D, N); Dskip (D);
+ *             h0, h_out (batch, D, N)
+ *   SSD/SISO: X, Y (batch, L, H, P); logdecay, beta, gamma (batch, L, H);
+ *             B, C (batch, L, G, N); theta (batch, L, H, N/2);
+ *             h0, h_out (batch, H, N, P)
+ *   MIMO:     X, Y (batch, L, H, P, R); B, C (batch, L, H, N, R); the rest as
+ *             SISO; the state has no R axis.
+ * Optional inputs (Dskip, h0, theta) may be NULL and then mean zero / no
+ * rotation.  h_out may be NULL.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+void oracle_set_threads(int n)
+{
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
+int oracle_get_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/*
+ * Mamba-1 selective scan (TorchMamba README, "Models" table row Mamba-1 and
+ * "Math notes" M1 bullet; burn_mamba `struct Mamba1` docs, `selective_scan`,
+ * which points at Algorithm 2 of the Mamba paper).
+ *
+ * Per (b, c, n), exponential-Euler discretisation:
+ *     h_t = exp(dt_t[c] * A[c,n]) * h_{t-1} + (dt_t[c] * B_t[n]) * x_t[c]
+ * and the output uses the updated state:
+ *     y_t[c] = sum_n C_t[n] * h_t[c,n] + Dskip[c] * x_t[c].
+ * B and C are per (b, t) and shared by every channel.
+ */
+void oracle_m1_scan(const double *x, const double *dt, const double *A,
+                    const double *B, const double *C, const double *Dskip,
+                    const double *h0, double *y, double *h_out,
+                    int64_t batch, int64_t L, int64_t D, int64_t N)
+{
+    int64_t units = batch * D;
+#pragma omp parallel for schedule(static)
+    for (int64_t u = 0; u < units; ++u) {
+        int64_t b = u / D, c = u % D;
+        double *h = (double *)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1));
+        for (int64_t n = 0; n < N; ++n)
+            h[n] = h0 ? h0[(b * D + c) * N + n] : 0.0;
+        for (int64_t t = 0; t < L; ++t) {
+            double xv = x[(b * L + t) * D + c];
+            double dtv = dt[(b * L + t) * D + c];
+            const double *Bt = B + (b * L + t) * N;
+            const double *Ct = C + (b * L + t) * N;
+            double acc = 0.0;
+            for (int64_t n = 0; n < N; ++n) {
+                double a = exp(dtv * A[c * N + n]);
+                h[n] = a * h[n] + (dtv * Bt[n]) * xv;
+                acc += Ct[n] * h[n];
+            }
+            y[(b * L + t) * D + c] = acc + (Dskip ? Dskip[c] * xv : 0.0);
+        }
+        if (h_out)
+            for (int64_t n = 0; n < N; ++n) h_out[(b * D + c) * N + n] = h[n];
+        free(h);
+    }
+}
+
+/*
+ * Mamba-1 single-token step (burn_mamba `struct Mamba1` docs,
+ * `selective_scan_step`; mamba-rs "Quick Start" step call).  One iteration of
+ * the loop above on a state of shape (batch, D, N):
+ *     h <- exp(dt*A) * h + dt*B*x ;  y = sum_n C*h + Dskip*x.
+ * x, dt, y are (batch, D); B, C are (batch, N).  h_out may equal h_in.
+ */
+void oracle_m1_step(const double *x, const double *dt, const double *A,
+                    const double *B, const double *C, const double *Dskip,
+                    const double *h_in, double *h_out, double *y,
+                    int64_t batch, int64_t D, int64_t N)
+{
+    int64_t units = batch * D;
+#pragma omp parallel for schedule(static)
+    for (int64_t u = 0; u < units; ++u) {
+        int64_t b = u / D, c = u % D;
+        double xv = x[b * D + c], dtv = dt[b * D + c];
+        double acc = 0.0;
+        for (int64_t n = 0; n < N; ++n) {
+            double a = exp(dtv * A[c * N + n]);
+            double h = a * h_in[(b * D + c) * N + n] + (dtv * B[b * N + n]) * xv;
+            h_out[(b * D + c) * N + n] = h;
+            acc += C[b * N + n] * h;
+        }
+        y[b * D + c] = acc + (Dskip ? Dskip[c] * xv : 0.0);
+    }
+}
+
+/*
+ * Mamba-2 scalar-decay SSD, recurrent form (TorchMamba README, "Models" table
+ * row Mamba-2 and "Math notes" M2 bullet; `ssd_recurrent` in its functional
+ * cores).  Per (b, h) with group g = h / (H/G), state S of shape (N, P):
+ *     S_t = exp(logdecay_t) * S_{t-1} + B_t (outer) X_t
+ *     Y_t = S_t^T C_t
+ */
+void oracle_ssd(const double *X, const double *logdecay, const double *B,
+                const double *C, const double *h0, double *Y, double *h_out,
+                int64_t batch, int64_t L, int64_t H, int64_t P, int64_t G,
+                int64_t N)
+{
+    int64_t units = batch * H;
+    int64_t hpg = H / G;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t u = 0; u < units; ++u) {
+        int64_t b = u / H, h = u % H, g = h / hpg;
+        double *S = (double *)malloc(sizeof(double) * (size_t)(N * P > 0 ? N * P : 1));
+        for (int64_t i = 0; i < N * P; ++i)
+            S[i] = h0 ? h0[(b * H + h) * N * P + i] : 0.0;
+        for (int64_t t = 0; t < L; ++t) {
+            double a = exp(logdecay[(b * L + t) * H + h]);
+            const double *Bt = B + ((b * L + t) * G + g) * N;
+            const double *Ct = C + ((b * L + t) * G + g) * N;
+            const double *Xt = X + ((b * L + t) * H + h) * P;
+            double *Yt = Y + ((b * L + t) * H + h) * P;
+            for (int64_t n = 0; n < N; ++n)
+                for (int64_t p = 0; p < P; ++p)
+                    S[n * P + p] = a * S[n * P + p] + Bt[n] * Xt[p];
+            for (int64_t p = 0; p < P; ++p) {
+                double acc = 0.0;
+                for (int64_t n = 0; n < N; ++n) acc += S[n * P + p] * Ct[n];
+                Yt[p] = acc;
+            }
+        }
+        if (h_out)
+            for (int64_t i = 0; i < N * P; ++i) h_out[(b * H + h) * N * P + i] = S[i];
+        free(S);
+    }
+}
+
+/* Rotate consecutive pairs (2k, 2k+1) of v[0..N) by angle phi[k]:
+ * (v0, v1) -> (cos*v0 - sin*v1, sin*v0 + cos*v1).  `stride` is the distance in
+ * elements between v[n] and v[n+1]. */
+static void rotate_pairs(double *dst, const double *src, const double *phi,
+                         int64_t N, int64_t stride, double sign)
+{
+    for (int64_t k = 0; k < N / 2; ++k) {
+        double cs = cos(phi[k]), sn = sign * sin(phi[k]);
+        double v0 = src[(2 * k) * stride], v1 = src[(2 * k + 1) * stride];
+        dst[(2 * k) * stride] = cs * v0 - sn * v1;
+        dst[(2 * k + 1) * stride] = sn * v0 + cs * v1;
+    }
+}
+
+/*
+ * Mamba-3 SISO, exponential-trapezoidal recurrence with data-dependent RoPE
+ * (TorchMamba README, "Models" table row Mamba-3 SISO and "Math notes" M3
+ * SISO bullet; mamba3-minimal README, "Two-SSD Decomposition" gives the same
+ * three-term update).  Per (b, h), rotated frame:
+ *     Theta_t[k] = sum_{s<=t} theta_s[k]                (restarts at 0 per call)
+ *     Bt_t = R(Theta_t) B_t,  Ct_t = R(Theta_t) C_t     (pairs 2k, 2k+1)
+ *     S_t = exp(ld_t) S_{t-1} + beta_t Bt_{t-1} (x) X_{t-1} + gamma_t Bt_t (x) X_t
+ *     Y_t = S_t^T Ct_t
+ * with Bt_{-1} = X_{-1} = 0.  h0 is given in the physical (unrotated) frame,
+ * which equals the rotated frame at Theta = 0, and h_out is returned in the
+ * physical frame: h_out = R(-Theta_{L-1}) S_{L-1}.  theta == NULL means no
+ * rotation (the real-valued path).
+ */
+void oracle_trap(const double *X, const double *logdecay, const double *B,
+                 const double *C, const double *beta, const double *gamma,
+                 const double *theta, const double *h0, double *Y,
+                 double *h_out, int64_t batch, int64_t L, int64_t H, int64_t P,
+                 int64_t G, int64_t N)
+{
+    int64_t units = batch * H;
+    int64_t hpg = H / G;
+    int64_t K = N / 2;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t u = 0; u < units; ++u) {
+        int64_t b = u / H, h = u % H, g = h / hpg;
+        size_t np = (size_t)(N * P > 0 ? N * P : 1);
+        double *S = (double *)malloc(sizeof(double) * np);
+        double *Theta = (double *)calloc((size_t)(K > 0 ? K : 1), sizeof(double));
+        double *Bt = (double *)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1));
+        double *Ct = (double *)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1));
+        double *Bprev = (double *)calloc((size_t)(N > 0 ? N : 1), sizeof(double));
+        double *Xprev = (double *)calloc((size_t)(P > 0 ? P : 1), sizeof(double));
+        for (int64_t i = 0; i < N * P; ++i)
+            S[i] = h0 ? h0[(b * H + h) * N * P + i] : 0.0;
+        for (int64_t t = 0; t < L; ++t) {
+            int64_t bth = (b * L + t) * H + h;
+            const double *Bsrc = B + ((b * L + t) * G + g) * N;
+            const double *Csrc = C + ((b * L + t) * G + g) * N;
+            const double *Xt = X + bth * P;
+            if (theta) {
+                for (int64_t k = 0; k < K; ++k) Theta[k] += theta[bth * K + k];
+                rotate_pairs(Bt, Bsrc, Theta, N, 1, 1.0);
+                rotate_pairs(Ct, Csrc, Theta, N, 1, 1.0);
+            } else {
+                memcpy(Bt, Bsrc, sizeof(double) * (size_t)N);
+                memcpy(Ct, Csrc, sizeof(double) * (size_t)N);
+            }
+            double a = exp(logdecay[bth]);
+            double be = beta[bth], ga = gamma[bth];
+            for (int64_t n = 0; n < N; ++n)
+                for (int64_t p = 0; p < P; ++p)
+                    S[n * P + p] = a * S[n * P + p] + be * Bprev[n] * Xprev[p]
+                                   + ga * Bt[n] * Xt[p];
+            double *Yt = Y + bth * P;
+            for (int64_t p = 0; p < P; ++p) {
+                double acc = 0.0;
+                for (int64_t n = 0; n < N; ++n) acc += S[n * P + p] * Ct[n];
+                Yt[p] = acc;
+            }
+            memcpy(Bprev, Bt, sizeof(double) * (size_t)N);
+            memcpy(Xprev, Xt, sizeof(double) * (size_t)P);
+        }
+        if (h_out) {
+            double *dst = h_out + (b * H + h) * N * P;
+            if (theta && L > 0) {
+                for (int64_t p = 0; p < P; ++p)
+                    rotate_pairs(dst + p, S + p, Theta, N, P, -1.0);
+            } else {
+                memcpy(dst, S, sizeof(double) * (size_t)(N * P));
+            }
+        }
+        free(S); free(Theta); free(Bt); free(Ct); free(Bprev); free(Xprev);
+    }
+}
+
+/*
+ * Mamba-3 MIMO rank-R recurrence (TorchMamba README, "Models" table row
+ * Mamba-3 MIMO and "Math notes" MIMO bullet: the outer product B x^T becomes a
+ * rank-R matrix product on one shared (N, P) state).  Per (b, h):
+ *     S_t = exp(ld_t) S_{t-1} + beta_t sum_r Bt_{t-1,r} (x) X_{t-1,r}
+ *                              + gamma_t sum_r Bt_{t,r} (x) X_{t,r}
+ *     Y_{t,r} = S_t^T Ct_{t,r}
+ * where every rank r of step t is rotated by the same per-head Theta_t as in
+ * the SISO loop above.  h0 / h_out in the physical frame.
+ */
+void oracle_mimo(const double *X, const double *logdecay, const double *B,
+                 const double *C, const double *beta, const double *gamma,
+                 const double *theta, const double *h0, double *Y,
+                 double *h_out, int64_t batch, int64_t L, int64_t H, int64_t P,
+                 int64_t N, int64_t R)
+{
+    int64_t units = batch * H;
+    int64_t K = N / 2;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t u = 0; u < units; ++u) {
+        int64_t b = u / H, h = u % H;
+        size_t np = (size_t)(N * P > 0 ? N * P : 1);
+        size_t nr = (size_t)(N * R > 0 ? N * R : 1);
+        size_t pr = (size_t)(P * R > 0 ? P * R : 1);
+        double *S = (double *)malloc(sizeof(double) * np);
+        double *Theta = (double *)calloc((size_t)(K > 0 ? K : 1), sizeof(double));
+        double *Bt = (double *)malloc(sizeof(double) * nr);
+        double *Ct = (double *)malloc(sizeof(double) * nr);
+        double *Bprev = (double *)calloc(nr, sizeof(double));
+        double *Xprev = (double *)calloc(pr, sizeof(double));
+        for (int64_t i = 0; i < N * P; ++i)
+            S[i] = h0 ? h0[(b * H + h) * N * P + i] : 0.0;
+        for (int64_t t = 0; t < L; ++t) {
+            int64_t bth = (b * L + t) * H + h;
+            const double *Bsrc = B + bth * N * R;   /* [n][r] */
+            const double *Csrc = C + bth * N * R;
+            const double *Xt = X + bth * P * R;     /* [p][r] */
+            if (theta) {
+                for (int64_t k = 0; k < K; ++k) Theta[k] += theta[bth * K + k];
+                for (int64_t r = 0; r < R; ++r) {
+                    rotate_pairs(Bt + r, Bsrc + r, Theta, N, R, 1.0);
+                    rotate_pairs(Ct + r, Csrc + r, Theta, N, R, 1.0);
+                }
+            } else {
+                memcpy(Bt, Bsrc, sizeof(double) * (size_t)(N * R));
+                memcpy(Ct, Csrc, sizeof(double) * (size_t)(N * R));
+            }
+            double a = exp(logdecay[bth]);
+            double be = beta[bth], ga = gamma[bth];
+            for (int64_t n = 0; n < N; ++n)
+                for (int64_t p = 0; p < P; ++p) {
+                    double prev = 0.0, cur = 0.0;
+                    for (int64_t r = 0; r < R; ++r) {
+                        prev += Bprev[n * R + r] * Xprev[p * R + r];
+                        cur += Bt[n * R + r] * Xt[p * R + r];
+                    }
+                    S[n * P + p] = a * S[n * P + p] + be * prev + ga * cur;
+                }
+            double *Yt = Y + bth * P * R;
+            for (int64_t p = 0; p < P; ++p)
+                for (int64_t r = 0; r < R; ++r) {
+                    double acc = 0.0;
+                    for (int64_t n = 0; n < N; ++n) acc += S[n * P + p] * Ct[n * R + r];
+                    Yt[p * R + r] = acc;
+                }
+            memcpy(Bprev, Bt, sizeof(double) * (size_t)(N * R));
+            memcpy(Xprev, Xt, sizeof(double) * (size_t)(P * R));
+        }
+        if (h_out) {
+            double *dst = h_out + (b * H + h) * N * P;
+            if (theta && L > 0) {
+                for (int64_t p = 0; p < P; ++p)
+                    rotate_pairs(dst + p, S + p, Theta, N, P, -1.0);
+            } else {
+                memcpy(dst, S, sizeof(double) * (size_t)(N * P));
+            }
+        }
+        free(S); free(Theta); free(Bt); free(Ct); free(Bprev); free(Xprev);
+    }
+}

@@ -1,0 +1,161 @@
+"""Seeded synthetic inputs for the scans (shared by the tests and the bench).
+
+This module only draws random numbers and applies the input recipes of the
+workloads (softplus for step sizes, sigmoid for the trapezoid mix, the
+alpha/beta/gamma coefficients the Mamba-3 configurations are defined with).  It
+holds none of the scans' arithmetic.  Draws use ``numpy.random.default_rng``
+(PCG64) in float64, in the order written in each function, so a seed fixes every
+value; callers cast to the run dtype.
+
+Workload recipes (shapes are the ones the pages' blocks use: d_model 768 with
+expand 2 for Mamba-1, d_head 64 / d_state 128 for the SSD family):
+
+* m1_tiny     seed 101: batch 1, L 64, D 16, N 4.
+* m1_block    seed 102: batch 8, L 2048, D 1536, N 16.
+* m1_decode   seed 106: batch 256, D 1536, N 16 (state ~ N(0, 0.1)).
+* ssd_block   seed 103: batch 4, L 4096, H 24, P 64, N 128, G 1.
+* siso_block  seed 104: as ssd_block, with trapezoid mix and rotary angles.
+* mimo_block  seed 105: batch 2, L 8192, H 16, P 64, N 128, R 4.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def _softplus(v):
+    return np.logaddexp(0.0, v)
+
+
+def _sigmoid(v):
+    return 1.0 / (1.0 + np.exp(-v))
+
+
+def s4d_real_A(D: int, N: int) -> np.ndarray:
+    """A[c, n] = -(n + 1) for every channel (S4D-real initialisation)."""
+    return -np.tile(np.arange(1, N + 1, dtype=np.float64), (D, 1))
+
+
+# --------------------------------------------------------------------------
+# Mamba-1
+# --------------------------------------------------------------------------
+def m1_inputs(rng, batch, L, D, N, dt_mu=-3.0, dt_sd=1.0, with_D=True,
+              h0_sd=0.0, A=None):
+    """Order: Dskip, x, B, C, dt, (h0)."""
+    Dskip = rng.standard_normal(D) if with_D else None
+    x = rng.standard_normal((batch, L, D))
+    B = rng.standard_normal((batch, L, N))
+    C = rng.standard_normal((batch, L, N))
+    dt = _softplus(rng.normal(dt_mu, dt_sd, size=(batch, L, D)))
+    h0 = rng.normal(0.0, h0_sd, size=(batch, D, N)) if h0_sd > 0 else None
+    if A is None:
+        A = s4d_real_A(D, N)
+    return dict(x=x, dt=dt, A=A, B=B, C=C, D=Dskip, h0=h0)
+
+
+def m1_tiny(seed=101):
+    """batch 1, L 64, D 16, N 4; dt = softplus(N(-2, 0.5)).
+    Order: x, B, C, dt, Dskip.  h0 = 0."""
+    rng = np.random.default_rng(seed)
+    b, L, D, N = 1, 64, 16, 4
+    x = rng.standard_normal((b, L, D))
+    B = rng.standard_normal((b, L, N))
+    C = rng.standard_normal((b, L, N))
+    dt = _softplus(rng.normal(-2.0, 0.5, size=(b, L, D)))
+    Dskip = rng.standard_normal(D)
+    return dict(x=x, dt=dt, A=s4d_real_A(D, N), B=B, C=C, D=Dskip, h0=None)
+
+
+def m1_block(seed=102, batch=8, L=2048, D=1536, N=16):
+    """batch 8, L 2048, D 1536, N 16; dt = softplus(N(-3, 1)).
+    Order: Dskip (drawn first), x, B, C, dt.  h0 = 0."""
+    rng = np.random.default_rng(seed)
+    Dskip = rng.standard_normal(D)
+    x = rng.standard_normal((batch, L, D))
+    B = rng.standard_normal((batch, L, N))
+    C = rng.standard_normal((batch, L, N))
+    dt = _softplus(rng.normal(-3.0, 1.0, size=(batch, L, D)))
+    return dict(x=x, dt=dt, A=s4d_real_A(D, N), B=B, C=C, D=Dskip, h0=None)
+
+
+def m1_decode(seed=106, batch=256, D=1536, N=16, model_seed=102):
+    """One batched decode step on the block model: A = -(n+1) and Dskip is the
+    first draw of the block seed.  From `seed`: state ~ N(0, 0.1) (batch, D, N),
+    x (batch, D), B, C (batch, N), dt = softplus(N(-3, 1)) (batch, D)."""
+    Dskip = np.random.default_rng(model_seed).standard_normal(D)
+    rng = np.random.default_rng(seed)
+    h = rng.normal(0.0, 0.1, size=(batch, D, N))
+    x = rng.standard_normal((batch, D))
+    B = rng.standard_normal((batch, N))
+    C = rng.standard_normal((batch, N))
+    dt = _softplus(rng.normal(-3.0, 1.0, size=(batch, D)))
+    return dict(x=x, dt=dt, A=s4d_real_A(D, N), B=B, C=C, D=Dskip, h=h)
+
+
+# --------------------------------------------------------------------------
+# Mamba-2 / Mamba-3
+# --------------------------------------------------------------------------
+def ssd_inputs(rng, batch, L, H, P, N, G=1, h0_sd=0.0):
+    """X, B, C ~ N(0,1)/sqrt(N); A_h = -U(1,16); dt = softplus(N(-3,1));
+    logdecay = dt * A_h.  Order: X, B, C, A_h, dt, (h0)."""
+    s = 1.0 / np.sqrt(N)
+    X = rng.standard_normal((batch, L, H, P)) * s
+    B = rng.standard_normal((batch, L, G, N)) * s
+    C = rng.standard_normal((batch, L, G, N)) * s
+    A_h = -rng.uniform(1.0, 16.0, size=H)
+    dt = _softplus(rng.normal(-3.0, 1.0, size=(batch, L, H)))
+    ld = dt * A_h
+    h0 = rng.normal(0.0, h0_sd, size=(batch, H, N, P)) if h0_sd > 0 else None
+    return dict(X=X, logdecay=ld, B=B, C=C, h0=h0)
+
+
+def ssd_block(seed=103, batch=4, L=4096, H=24, P=64, N=128, G=1):
+    return ssd_inputs(np.random.default_rng(seed), batch, L, H, P, N, G)
+
+
+def _trap_coeffs(rng, batch, L, H, N):
+    """dt = softplus(N(-3,1)); A_h = -U(1,16); alpha = exp(dt*A_h);
+    lambda = sigmoid(N(0,1)); gamma = lambda*dt; beta = (1-lambda)*dt*alpha;
+    theta = U(0, pi) * dt (dt broadcast over N/2).  Order: dt, A_h, lambda,
+    theta-uniforms."""
+    dt = _softplus(rng.normal(-3.0, 1.0, size=(batch, L, H)))
+    A_h = -rng.uniform(1.0, 16.0, size=H)
+    ld = dt * A_h
+    alpha = np.exp(ld)
+    lam = _sigmoid(rng.standard_normal((batch, L, H)))
+    gamma = lam * dt
+    beta = (1.0 - lam) * dt * alpha
+    theta = rng.uniform(0.0, np.pi, size=(batch, L, H, N // 2)) * dt[..., None]
+    return ld, beta, gamma, theta
+
+
+def trap_inputs(rng, batch, L, H, P, N, G=1, h0_sd=0.0, rotate=True):
+    """Order: X, B, C, then the coefficients of _trap_coeffs, then (h0)."""
+    s = 1.0 / np.sqrt(N)
+    X = rng.standard_normal((batch, L, H, P)) * s
+    B = rng.standard_normal((batch, L, G, N)) * s
+    C = rng.standard_normal((batch, L, G, N)) * s
+    ld, beta, gamma, theta = _trap_coeffs(rng, batch, L, H, N)
+    h0 = rng.normal(0.0, h0_sd, size=(batch, H, N, P)) if h0_sd > 0 else None
+    return dict(X=X, logdecay=ld, B=B, C=C, beta=beta, gamma=gamma,
+                theta=theta if rotate else None, h0=h0)
+
+
+def siso_block(seed=104, batch=4, L=4096, H=24, P=64, N=128, G=1):
+    return trap_inputs(np.random.default_rng(seed), batch, L, H, P, N, G)
+
+
+def mimo_inputs(rng, batch, L, H, P, N, R, h0_sd=0.0, rotate=True):
+    """Xr (b,L,H,P,R), Br, Cr (b,L,H,N,R) ~ N(0,1)/sqrt(N*R); then the SISO
+    coefficients.  Order: X, B, C, coefficients, (h0)."""
+    s = 1.0 / np.sqrt(N * R)
+    X = rng.standard_normal((batch, L, H, P, R)) * s
+    B = rng.standard_normal((batch, L, H, N, R)) * s
+    C = rng.standard_normal((batch, L, H, N, R)) * s
+    ld, beta, gamma, theta = _trap_coeffs(rng, batch, L, H, N)
+    h0 = rng.normal(0.0, h0_sd, size=(batch, H, N, P)) if h0_sd > 0 else None
+    return dict(X=X, logdecay=ld, B=B, C=C, beta=beta, gamma=gamma,
+                theta=theta if rotate else None, h0=h0)
+
+
+def mimo_block(seed=105, batch=2, L=8192, H=16, P=64, N=128, R=4):
+    return mimo_inputs(np.random.default_rng(seed), batch, L, H, P, N, R)

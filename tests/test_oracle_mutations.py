@@ -1,0 +1,108 @@
+"""Planted-mistake check of the oracle pins (CPU only).
+
+Each case copies oracle.c, plants one plausible mistake (a dropped factor, a
+swapped operand, a wrong sign or index), builds the copy into a temporary
+library and runs a compact battery of the pins used in test_oracle_*.py.  The
+case passes when at least one pin rejects the planted mistake, which shows the
+pins would catch that class of error in the real oracle."""
+import importlib.util
+import os
+import shutil
+import sys
+
+import numpy as np
+import pytest
+
+import forms
+from selective_state_space_amd import workloads as wl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+MUTATIONS = {
+    "m1_drop_dt_in_input": ("h[n] = a * h[n] + (dtv * Bt[n]) * xv;", "h[n] = a * h[n] + Bt[n] * xv;"),
+    "m1_drop_dt_in_decay": ("double a = exp(dtv * A[c * N + n]);", "double a = exp(A[c * N + n]);"),
+    "m1_skip_sign": ("acc + (Dskip ? Dskip[c] * xv", "acc - (Dskip ? Dskip[c] * xv"),
+    "step_wrong_state_index": ("a * h_in[(b * D + c) * N + n]", "a * h_in[(b * D + c) * N]"),
+    "ssd_B_C_swapped_in_update": ("S[n * P + p] = a * S[n * P + p] + Bt[n] * Xt[p];",
+                                  "S[n * P + p] = a * S[n * P + p] + Ct[n] * Xt[p];"),
+    "ssd_output_uses_B": ("for (int64_t n = 0; n < N; ++n) acc += S[n * P + p] * Ct[n];\n                Yt[p] = acc;\n            }\n        }\n        if (h_out)\n            for (int64_t i = 0; i < N * P; ++i) h_out[(b * H + h) * N * P + i] = S[i];",
+                          "for (int64_t n = 0; n < N; ++n) acc += S[n * P + p] * Bt[n];\n                Yt[p] = acc;\n            }\n        }\n        if (h_out)\n            for (int64_t i = 0; i < N * P; ++i) h_out[(b * H + h) * N * P + i] = S[i];"),
+    "ssd_group_map": ("int64_t b = u / H, h = u % H, g = h / hpg;\n        double *S = (double *)malloc(sizeof(double) * (size_t)(N * P > 0 ? N * P : 1));",
+                      "int64_t b = u / H, h = u % H, g = h % G;\n        double *S = (double *)malloc(sizeof(double) * (size_t)(N * P > 0 ? N * P : 1));"),
+    "trap_beta_uses_current_B": ("be * Bprev[n] * Xprev[p]", "be * Bt[n] * Xprev[p]"),
+    "trap_gamma_dropped": ("+ ga * Bt[n] * Xt[p];", "+ Bt[n] * Xt[p];"),
+    "rotation_sign": ("dst[(2 * k) * stride] = cs * v0 - sn * v1;", "dst[(2 * k) * stride] = cs * v0 + sn * v1;"),
+    "trap_state_not_derotated": ("rotate_pairs(dst + p, S + p, Theta, N, P, -1.0);",
+                                 "rotate_pairs(dst + p, S + p, Theta, N, P, 1.0);"),
+    "mimo_rank_index": ("cur += Bt[n * R + r] * Xt[p * R + r];", "cur += Bt[n * R + r] * Xt[p * R];"),
+    "mimo_output_rank": ("acc += S[n * P + p] * Ct[n * R + r];", "acc += S[n * P + p] * Ct[n * R];"),
+    "decay_halved": ("double a = exp(logdecay[bth]);", "double a = exp(0.5 * logdecay[bth]);"),
+}
+
+
+def _battery(o):
+    """Return the list of pins that fail for oracle module `o`."""
+    failed = []
+    rng = np.random.default_rng(99)
+
+    def ok(a, b):
+        return np.allclose(a, b, rtol=1e-10, atol=1e-12)
+
+    inp = wl.m1_inputs(rng, 2, 9, 4, 3, dt_mu=-1.0, h0_sd=0.5, A=-rng.uniform(0.1, 2.0, (4, 3)))
+    y, h = o.m1_scan(**inp)
+    ym, hm = forms.m1_matrix(**inp)
+    if not (ok(y, ym) and ok(h, hm)):
+        failed.append("m1_matrix")
+    hs = inp["h0"].copy()
+    ys = []
+    for t in range(9):
+        yt, hs = o.m1_step(inp["x"][:, t], inp["dt"][:, t], inp["A"], inp["B"][:, t], inp["C"][:, t], inp["D"], hs)
+        ys.append(yt)
+    if not (ok(np.stack(ys, 1), ym) and ok(hs, hm)):
+        failed.append("m1_step_vs_matrix")
+
+    inp = wl.ssd_inputs(rng, 2, 20, 4, 3, 5, G=2, h0_sd=0.5)
+    Y, h = o.ssd(**inp)
+    Yq, hq = forms.ssd_quadratic(**inp)
+    if not (ok(Y, Yq) and ok(h, hq)):
+        failed.append("ssd_quadratic")
+
+    inp = wl.trap_inputs(rng, 2, 11, 4, 3, 6, G=2, h0_sd=0.5)
+    Y, h = o.trap(**inp)
+    Ym, hm = forms.trap_matrix(**inp)
+    if not (ok(Y, Ym) and ok(h, hm)):
+        failed.append("trap_matrix")
+
+    inp = wl.mimo_inputs(rng, 1, 12, 2, 3, 6, 3, h0_sd=0.5)
+    Y, h = o.mimo(**inp)
+    Yp, hp = forms.mimo_physical_step_loop(**inp)
+    if not (np.allclose(Y, Yp, rtol=1e-9, atol=1e-11) and np.allclose(h, hp, rtol=1e-9, atol=1e-11)):
+        failed.append("mimo_physical_step")
+    return failed
+
+
+def _load_variant(tmp_path, src_text, tag):
+    d = tmp_path / ("oracle_" + tag)
+    d.mkdir()
+    shutil.copy(os.path.join(ROOT, "oracle", "__init__.py"), d / "__init__.py")
+    (d / "oracle.c").write_text(src_text)
+    name = "oracle_variant_" + tag
+    spec = importlib.util.spec_from_file_location(name, str(d / "__init__.py"))
+    mod = importlib.util.module_from_spec(spec)
+    sys.modules[name] = mod
+    spec.loader.exec_module(mod)
+    mod.build(force=True)
+    return mod
+
+
+def test_unmutated_battery_passes(oracle_mod):
+    assert _battery(oracle_mod) == []
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_planted_mistake_is_caught(tmp_path, name):
+    src = open(os.path.join(ROOT, "oracle", "oracle.c")).read()
+    old, new = MUTATIONS[name]
+    assert src.count(old) >= 1, "mutation anchor not found: " + name
+    mod = _load_variant(tmp_path, src.replace(old, new, 1), name)
+    assert _battery(mod), "no pin caught the planted mistake " + name

@@ -1,0 +1,170 @@
+"""Pins of the Mamba-3 SISO and MIMO oracles: hand examples, the parallel
+"1SS @ band" mask form, the two-SSD decomposition (quadratic and chunked), the
+physical-frame step loop, the reductions (beta = 0 and theta = 0 gives the SSD
+of gamma X; full-turn angles change nothing; R = 1 MIMO is SISO; MIMO is a sum
+of R^2 SISO calls), the zero-input closed form and split-sequence chaining."""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import forms
+from selective_state_space_amd import workloads as wl
+
+RTOL, ATOL = 1e-10, 1e-12
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def close(a, b, rtol=RTOL, atol=ATOL):
+    np.testing.assert_allclose(a, b, rtol=rtol, atol=atol)
+
+
+def _gold(name):
+    g = json.load(open(os.path.join(GOLD, name)))
+    return {k: np.array(v) for k, v in g["inputs"].items()}, g["expected"]
+
+
+def test_siso_hand_example(oracle_mod):
+    i, e = _gold("trap_hand.json")
+    Y, h = oracle_mod.trap(**i)
+    close(Y, np.array(e["Y"]))
+    close(h, np.array(e["h"]))
+
+
+def test_mimo_hand_example(oracle_mod):
+    i, e = _gold("mimo_hand.json")
+    Y, h = oracle_mod.mimo(**i)
+    close(Y, np.array(e["Y"]))
+    close(h, np.array(e["h"]))
+
+
+@pytest.mark.parametrize("L", [1, 2, 3, 9, 16])
+@pytest.mark.parametrize("rotate", [False, True])
+def test_siso_matrix_form(oracle_mod, L, rotate):
+    rng = np.random.default_rng(4000 + L + 50 * rotate)
+    inp = wl.trap_inputs(rng, 2, L, 4, 3, 6, G=2, h0_sd=0.5, rotate=rotate)
+    Y, h = oracle_mod.trap(**inp)
+    Ym, hm = forms.trap_matrix(**inp)
+    close(Y, Ym)
+    close(h, hm)
+
+
+@pytest.mark.parametrize("Q", [None, 1, 3, 4, 13])
+def test_siso_two_ssd(oracle_mod, Q):
+    rng = np.random.default_rng(4100 + (Q or 0))
+    inp = wl.trap_inputs(rng, 2, 13, 3, 4, 6, G=1, h0_sd=0.4)
+    Y, h = oracle_mod.trap(**inp)
+    Y2, h2 = forms.trap_two_ssd(**inp, Q=Q)
+    close(Y, Y2)
+    close(h, h2)
+
+
+def test_siso_physical_frame_step(oracle_mod):
+    rng = np.random.default_rng(4200)
+    inp = wl.trap_inputs(rng, 2, 150, 3, 5, 8, G=3, h0_sd=0.6)
+    Y, h = oracle_mod.trap(**inp)
+    Yp, hp = forms.trap_physical_step_loop(**inp)
+    close(Y, Yp, rtol=1e-9, atol=1e-11)
+    close(h, hp, rtol=1e-9, atol=1e-11)
+
+
+def test_siso_reduces_to_ssd(oracle_mod):
+    """lambda = 1 (beta = 0) and no rotation is the SSD of gamma * X
+    (TorchMamba README, reductions: M2 -> SISO at lambda = 1, theta = 0)."""
+    rng = np.random.default_rng(4300)
+    inp = wl.trap_inputs(rng, 2, 60, 4, 3, 5, G=2, h0_sd=0.5, rotate=False)
+    inp["beta"] = np.zeros_like(inp["beta"])
+    Y, h = oracle_mod.trap(**inp)
+    Ys, hs = oracle_mod.ssd(inp["X"] * inp["gamma"][..., None], inp["logdecay"],
+                            inp["B"], inp["C"], inp["h0"])
+    close(Y, Ys)
+    close(h, hs)
+
+
+def test_siso_full_turns_are_identity(oracle_mod):
+    rng = np.random.default_rng(4400)
+    inp = wl.trap_inputs(rng, 1, 40, 2, 3, 4, h0_sd=0.5)
+    Y, h = oracle_mod.trap(**dict(inp, theta=None))
+    Yt, ht = oracle_mod.trap(**dict(inp, theta=np.full_like(inp["theta"], 2 * np.pi)))
+    close(Yt, Y, rtol=1e-9, atol=1e-11)
+    close(ht, h, rtol=1e-9, atol=1e-11)
+
+
+def test_siso_zero_input_closed_form(oracle_mod):
+    """x = 0: the physical state is exp(sum ld) R(-Theta_{L-1}) h0 and
+    y_t = exp(cum_t) C_t^T R(-Theta_t) h0, at any L."""
+    rng = np.random.default_rng(4500)
+    inp = wl.trap_inputs(rng, 2, 700, 3, 4, 6, G=1, h0_sd=1.0)
+    inp["X"] = np.zeros_like(inp["X"])
+    inp["logdecay"] *= 0.01
+    Y, h = oracle_mod.trap(**inp)
+    cum = np.cumsum(inp["logdecay"], axis=1)
+    Th = np.cumsum(inp["theta"], axis=1)
+    h0T = np.swapaxes(inp["h0"], -1, -2)                         # (b, H, P, N)
+    b, L = Th.shape[:2]
+    h0L = np.broadcast_to(h0T[:, None], (b, L) + h0T.shape[1:]).copy()
+    rot = np.swapaxes(forms.rot_pairs(h0L, Th[:, :, :, None, :], -1.0), -1, -2)  # (b,L,H,N,P)
+    href = np.exp(cum[:, -1])[..., None, None] * rot[:, -1]
+    close(h, href, rtol=1e-9, atol=1e-11)
+    Yref = np.exp(cum)[..., None] * np.einsum("blhnp,blhn->blhp", rot, inp["C"][:, :, [0, 0, 0], :])
+    close(Y, Yref, rtol=1e-9, atol=1e-11)
+
+
+def test_siso_split_chaining(oracle_mod):
+    """Chaining two calls through the physical-frame state is exact when the
+    trapezoid's cross-boundary weight at the split is zero (each call starts
+    with x_{-1} = B_{-1} = 0)."""
+    rng = np.random.default_rng(4600)
+    inp = wl.trap_inputs(rng, 2, 90, 3, 4, 6, G=3, h0_sd=0.5)
+    s = 37
+    inp["beta"][:, s] = 0.0
+    Y, h = oracle_mod.trap(**inp)
+    cut = lambda sl: {k: (v[:, sl] if k not in ("h0",) and v is not None else v) for k, v in inp.items()}
+    a = cut(slice(0, s))
+    Ya, ha = oracle_mod.trap(**a)
+    b = cut(slice(s, None))
+    b["h0"] = ha
+    Yb, hb = oracle_mod.trap(**b)
+    close(np.concatenate([Ya, Yb], 1), Y, rtol=1e-9, atol=1e-11)
+    close(hb, h, rtol=1e-9, atol=1e-11)
+
+
+@pytest.mark.parametrize("rotate", [False, True])
+def test_mimo_as_r2_siso_calls(oracle_mod, rotate):
+    """MIMO equals R^2 SISO calls (TorchMamba README, Math notes MIMO):
+    Y_r = sum_r' SISO(X_r', B_r', C_r), with h0 entered in one term only."""
+    rng = np.random.default_rng(4700 + rotate)
+    R, H = 3, 2
+    inp = wl.mimo_inputs(rng, 2, 21, H, 4, 6, R, h0_sd=0.5, rotate=rotate)
+    Y, h = oracle_mod.mimo(**inp)
+    Yref = np.zeros_like(Y)
+    href = 0.0
+    for rp in range(R):
+        for r in range(R):
+            Ys, hs = oracle_mod.trap(inp["X"][..., rp], inp["logdecay"], inp["B"][..., rp],
+                                     inp["C"][..., r], inp["beta"], inp["gamma"], inp["theta"],
+                                     inp["h0"] if rp == 0 else None)
+            Yref[..., r] += Ys
+        href = href + hs
+    close(Y, Yref)
+    close(h, href)
+
+
+def test_mimo_rank_one_is_siso(oracle_mod):
+    rng = np.random.default_rng(4800)
+    inp = wl.mimo_inputs(rng, 2, 33, 3, 4, 6, 1, h0_sd=0.5)
+    Y, h = oracle_mod.mimo(**inp)
+    Ys, hs = oracle_mod.trap(inp["X"][..., 0], inp["logdecay"], inp["B"][..., 0], inp["C"][..., 0],
+                             inp["beta"], inp["gamma"], inp["theta"], inp["h0"])
+    close(Y[..., 0], Ys)
+    close(h, hs)
+
+
+def test_mimo_physical_frame_step(oracle_mod):
+    rng = np.random.default_rng(4900)
+    inp = wl.mimo_inputs(rng, 2, 120, 2, 5, 8, 4, h0_sd=0.5)
+    Y, h = oracle_mod.mimo(**inp)
+    Yp, hp = forms.mimo_physical_step_loop(**inp)
+    close(Y, Yp, rtol=1e-9, atol=1e-11)
+    close(h, hp, rtol=1e-9, atol=1e-11)
