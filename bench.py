@@ -1,0 +1,405 @@
+#!/usr/bin/env python3
+"""Benchmark of the selective state-space scans on one MI355X.
+
+One *step* runs every scan of the library once on its workload, with inputs
+already resident in HBM:
+
+  m1_scan    Mamba-1 selective scan, batch 8, L 2048, D 1536, N 16, fp32
+  m1_step    Mamba-1 decode step, 256 sequences, D 1536, N 16, fp32, in place
+  ssd_f32    Mamba-2 SSD, batch 4, L 4096, H 24, P 64, N 128, G 1, fp32
+  ssd_bf16   the same with bf16 X/B/C/Y (fp32 accumulation and state)
+  siso       Mamba-3 SISO trapezoid + rotations, shapes of ssd_f32, fp32
+  mimo       Mamba-3 MIMO rank 4, batch 2, L 8192, H 16, P 64, N 128, fp32
+
+The printed metric is scanned tokens per second over the whole step (a token
+is one (batch, time) position of a workload; the decode step counts its 256
+sequences).  Per-workload times come from HIP events recorded on the stream the
+kernels run on, over the same timed steps.  The `roofline` object is for the
+workload whose kernels take the largest share of the step; `kernels` lists
+every workload.  `cpu_baseline` times the fp64 oracle on a bounded sample of the
+same workloads on the host cores.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--only a,b] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+FP32_PEAK_TFLOPS = 157.3       # MI355X dense fp32 (vector and MFMA)
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+VALU_F32_LANE_OPS = 256 * 2.4e9 * 64   # non-packed fp32 VALU lane-ops/s (256 CU x 2.4 GHz x 64 lanes)
+
+
+# ----------------------------------------------------------------------------
+# algorithmic work per workload (bytes: each input read once, each output
+# written once; flops at the canonical chunk length 64, causal half only)
+# ----------------------------------------------------------------------------
+def m1_scan_work(b, L, D, N, es=4):
+    nbytes = es * (3 * b * L * D + 2 * b * L * N) + 4 * (D * N + D + b * D * N)
+    return nbytes, b * L * D * N      # (bytes, exp count)
+
+
+def m1_step_work(b, D, N, es=4):
+    nbytes = 4 * (2 * b * D * N) + es * (3 * b * D + 2 * b * N) + 4 * (D * N + D)
+    return nbytes, b * D * N
+
+
+def ssd_work(b, L, H, P, N, G, es=4, Q=64):
+    nbytes = es * (2 * b * L * H * P + 2 * b * L * G * N) + 4 * (b * L * H + b * H * N * P)
+    flops = b * L * H * (4 * N * P + P * (Q + 1) + N * (Q + 1) * G / H)
+    return nbytes, flops
+
+
+def siso_work(b, L, H, P, N, G, Q=64):
+    nbytes = 4 * (2 * b * L * H * P + 2 * b * L * G * N + 3 * b * L * H + b * L * H * N // 2 + b * H * N * P)
+    flops = b * L * H * (4 * N * P + P * (Q + 1) + N * (Q + 1))
+    return nbytes, flops
+
+
+def mimo_work(b, L, H, P, N, R, Q=64):
+    Qt = Q // R
+    nbytes = 4 * (2 * b * L * H * P * R + 2 * b * L * H * N * R + 3 * b * L * H + b * L * H * N // 2 + b * H * N * P)
+    flops = b * L * H * (4 * N * P * R + R * R * (Qt + 1) * (N + P))
+    return nbytes, flops
+
+
+# ----------------------------------------------------------------------------
+# workloads
+# ----------------------------------------------------------------------------
+class Workload:
+    name = ""
+    tokens = 0
+    bound = "hbm"
+
+    def run(self):
+        raise NotImplementedError
+
+
+def _dev(a, dtype):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dtype).cuda()
+
+
+class M1Scan(Workload):
+    name = "m1_scan"
+    kernel = "k_m1_scan"
+    source = "selective_state_space_amd/csrc/m1.hip"
+
+    def __init__(self, mb, wl, torch):
+        self.mb = mb
+        b, L, D, N = 8, 2048, 1536, 16
+        self.shape = dict(batch=b, L=L, D=D, N=N)
+        inp = wl.m1_block()
+        f = torch.float32
+        self.x, self.dt, self.B, self.C = (_dev(inp[k], f) for k in ("x", "dt", "B", "C"))
+        self.A, self.D = _dev(inp["A"], f), _dev(inp["D"], f)
+        self.y = torch.empty_like(self.x)
+        self.h = torch.empty((b, D, N), dtype=f, device="cuda")
+        self.tokens = b * L
+        self.bytes, self.exps = m1_scan_work(b, L, D, N)
+        self.flops = None
+
+    def run(self):
+        self.mb.mb_selective_scan(self.x, self.dt, self.A, self.B, self.C, self.D, None, y=self.y, h_out=self.h)
+
+
+class M1Step(Workload):
+    name = "m1_step"
+    kernel = "k_m1_step_q"
+    source = "selective_state_space_amd/csrc/m1.hip"
+
+    def __init__(self, mb, wl, torch):
+        self.mb = mb
+        b, D, N = 256, 1536, 16
+        self.shape = dict(batch=b, D=D, N=N)
+        inp = wl.m1_decode()
+        f = torch.float32
+        self.x, self.dt, self.B, self.C = (_dev(inp[k], f) for k in ("x", "dt", "B", "C"))
+        self.A, self.D = _dev(inp["A"], f), _dev(inp["D"], f)
+        self.h = _dev(inp["h"], f)
+        self.y = torch.empty_like(self.x)
+        self.tokens = b
+        self.bytes, self.exps = m1_step_work(b, D, N)
+        self.flops = None
+
+    def run(self):
+        self.mb.mb_ssm_step(self.x, self.dt, self.A, self.B, self.C, self.D, self.h, y=self.y)
+
+
+class SSD(Workload):
+    kernel = "k_ssd_walk"
+    source = "selective_state_space_amd/csrc/ssd.hip"
+    bound = "mfma"
+
+    def __init__(self, mb, wl, torch, dtype):
+        self.mb = mb
+        self.name = "ssd_" + dtype
+        b, L, H, P, N, G = 4, 4096, 24, 64, 128, 1
+        self.shape = dict(batch=b, L=L, H=H, P=P, N=N, G=G)
+        inp = wl.ssd_block()
+        act = torch.bfloat16 if dtype == "bf16" else torch.float32
+        self.X, self.B, self.C = (_dev(inp[k], act) for k in ("X", "B", "C"))
+        self.ld = _dev(inp["logdecay"], torch.float32)
+        self.Y = torch.empty_like(self.X)
+        self.h = torch.empty((b, H, N, P), dtype=torch.float32, device="cuda")
+        self.ws = torch.empty(mb.mb_workspace_size(mb.MB_OP_SSD_CHUNKED, b, L, H, P, G, N, 1, 0),
+                              dtype=torch.uint8, device="cuda")
+        self.tokens = b * L
+        es = 2 if dtype == "bf16" else 4
+        self.bytes, self.flops = ssd_work(b, L, H, P, N, G, es)
+        self.exps = None
+        self.dtype = dtype
+        if dtype == "bf16":
+            self.bound = "hbm"
+
+    def run(self):
+        self.mb.mb_ssd_chunked(self.X, self.ld, self.B, self.C, None, Y=self.Y, h_out=self.h, ws=self.ws)
+
+
+class SISO(Workload):
+    name = "siso"
+    kernel = "k_trap_walk"
+    source = "selective_state_space_amd/csrc/ssd.hip"
+    bound = "mfma"
+
+    def __init__(self, mb, wl, torch):
+        self.mb = mb
+        b, L, H, P, N, G = 4, 4096, 24, 64, 128, 1
+        self.shape = dict(batch=b, L=L, H=H, P=P, N=N, G=G)
+        inp = wl.siso_block()
+        f = torch.float32
+        self.t = {k: _dev(inp[k], f) for k in ("X", "logdecay", "B", "C", "beta", "gamma", "theta")}
+        self.Y = torch.empty_like(self.t["X"])
+        self.h = torch.empty((b, H, N, P), dtype=f, device="cuda")
+        self.ws = torch.empty(mb.mb_workspace_size(mb.MB_OP_TRAP_SSD, b, L, H, P, G, N, 1, 0),
+                              dtype=torch.uint8, device="cuda")
+        self.tokens = b * L
+        self.bytes, self.flops = siso_work(b, L, H, P, N, G)
+        self.exps = None
+
+    def run(self):
+        t = self.t
+        self.mb.mb_trap_ssd(t["X"], t["logdecay"], t["B"], t["C"], t["beta"], t["gamma"], t["theta"], None,
+                            Y=self.Y, h_out=self.h, ws=self.ws)
+
+
+class MIMO(Workload):
+    name = "mimo"
+    kernel = "k_trap_walk"
+    source = "selective_state_space_amd/csrc/ssd.hip"
+    bound = "mfma"
+
+    def __init__(self, mb, wl, torch):
+        self.mb = mb
+        b, L, H, P, N, R = 2, 8192, 16, 64, 128, 4
+        self.shape = dict(batch=b, L=L, H=H, P=P, N=N, R=R)
+        inp = wl.mimo_block()
+        f = torch.float32
+        self.t = {k: _dev(inp[k], f) for k in ("X", "logdecay", "B", "C", "beta", "gamma", "theta")}
+        self.Y = torch.empty_like(self.t["X"])
+        self.h = torch.empty((b, H, N, P), dtype=f, device="cuda")
+        self.ws = torch.empty(mb.mb_workspace_size(mb.MB_OP_MIMO_SSD, b, L, H, P, 1, N, R, 0),
+                              dtype=torch.uint8, device="cuda")
+        self.tokens = b * L
+        self.bytes, self.flops = mimo_work(b, L, H, P, N, R)
+        self.exps = None
+
+    def run(self):
+        t = self.t
+        self.mb.mb_mimo_ssd(t["X"], t["logdecay"], t["B"], t["C"], t["beta"], t["gamma"], t["theta"], None,
+                            Y=self.Y, h_out=self.h, ws=self.ws)
+
+
+ALL = ["m1_scan", "m1_step", "ssd_f32", "ssd_bf16", "siso", "mimo"]
+
+
+def make(name, mb, wl, torch):
+    if name == "m1_scan":
+        return M1Scan(mb, wl, torch)
+    if name == "m1_step":
+        return M1Step(mb, wl, torch)
+    if name == "ssd_f32":
+        return SSD(mb, wl, torch, "f32")
+    if name == "ssd_bf16":
+        return SSD(mb, wl, torch, "bf16")
+    if name == "siso":
+        return SISO(mb, wl, torch)
+    if name == "mimo":
+        return MIMO(mb, wl, torch)
+    raise ValueError(name)
+
+
+def roofline_of(w, ms):
+    """Achieved fraction of the roofline that bounds workload w at ms per call."""
+    s = ms * 1e-3
+    if w.bound == "mfma":
+        peak = BF16_PEAK_TFLOPS if getattr(w, "dtype", "f32") == "bf16" else FP32_PEAK_TFLOPS
+        ach = w.flops / s / 1e12
+        return {"bound": "mfma", "achieved": ach, "peak": peak, "unit": "TFLOP/s", "frac": ach / peak}
+    ach = w.bytes / s / 1e9
+    return {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBS}
+
+
+def source_hash(path):
+    with open(os.path.join(ROOT, path), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_for(w):
+    """HBM bytes per call measured with rocprofv3 counters (profiles/traffic.json),
+    or None when no measurement exists for the current kernel source."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        rec = json.load(open(p)).get(w.name)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_sha") != source_hash(w.source):
+        return None
+    return rec.get("bytes_per_call")
+
+
+# ----------------------------------------------------------------------------
+# CPU baseline: the fp64 oracle on a bounded sample of each workload
+# ----------------------------------------------------------------------------
+def cpu_baseline(names):
+    import oracle
+    from selective_state_space_amd import workloads as wl
+    oracle.build()
+    threads = oracle.get_threads()
+    total_tok, total_s, parts = 0.0, 0.0, []
+    for n in names:
+        if n == "m1_scan":
+            inp = wl.m1_block(batch=1, L=512)
+            t0 = time.perf_counter(); oracle.m1_scan(**inp); dt = time.perf_counter() - t0
+            tok, desc = 512, "m1_scan batch 1 x L 512 of D 1536"
+        elif n == "m1_step":
+            inp = wl.m1_decode()
+            t0 = time.perf_counter()
+            oracle.m1_step(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["D"], inp["h"])
+            dt = time.perf_counter() - t0
+            tok, desc = 256, "m1_step full (256 sequences)"
+        elif n in ("ssd_f32", "ssd_bf16"):
+            inp = wl.ssd_block(batch=1, L=512)
+            t0 = time.perf_counter(); oracle.ssd(**inp); dt = time.perf_counter() - t0
+            tok, desc = 512, n + " batch 1 x L 512 of H 24"
+        elif n == "siso":
+            inp = wl.siso_block(batch=1, L=512)
+            t0 = time.perf_counter(); oracle.trap(**inp); dt = time.perf_counter() - t0
+            tok, desc = 512, "siso batch 1 x L 512 of H 24"
+        elif n == "mimo":
+            inp = wl.mimo_block(batch=1, L=256)
+            t0 = time.perf_counter(); oracle.mimo(**inp); dt = time.perf_counter() - t0
+            tok, desc = 256, "mimo batch 1 x L 256 of H 16"
+        else:
+            continue
+        total_tok += tok
+        total_s += dt
+        parts.append("%s (%.2f s)" % (desc, dt))
+    return {"value": total_tok / total_s if total_s else None, "unit": "scanned tokens/s",
+            "cores": threads, "kind": "oracle", "sample": "; ".join(parts)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--only", default="")
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU; this library has no multi-GPU path (run with --gpus 1)",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    import selective_state_space_amd as mb
+    from selective_state_space_amd import workloads as wl
+
+    if not torch.cuda.is_available():
+        print("no GPU available", file=sys.stderr)
+        return 2
+    mb.load_library()
+    names = [n for n in (args.only.split(",") if args.only else ALL) if n]
+    ws = []
+    for n in names:
+        print("# preparing %s" % n, file=sys.stderr, flush=True)
+        ws.append(make(n, mb, wl, torch))
+    torch.cuda.synchronize()
+
+    for _ in range(args.warmup):
+        for w in ws:
+            w.run()
+    torch.cuda.synchronize()
+
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in ws]
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        for i, w in enumerate(ws):
+            ev[k][i][0].record()
+            w.run()
+            ev[k][i][1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    per = []
+    for i, w in enumerate(ws):
+        ms = [ev[k][i][0].elapsed_time(ev[k][i][1]) for k in range(args.steps)]
+        per.append(float(np.mean(ms)))
+    ms_per_step = wall * 1e3 / args.steps
+    tokens = sum(w.tokens for w in ws)
+    kernels = []
+    for w, ms in zip(ws, per):
+        r = roofline_of(w, ms)
+        d = {"workload": w.name, "ms": round(ms, 5), "tokens_per_s": w.tokens / (ms * 1e-3),
+             "roofline": {k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}}
+        hbm = w.bytes / (ms * 1e-3) / 1e9
+        d["hbm_gbs"] = round(hbm, 1)
+        if w.exps:
+            d["exp_per_s"] = w.exps / (ms * 1e-3)
+        kernels.append(d)
+    dom = int(np.argmax(per))
+    w = ws[dom]
+    r = roofline_of(w, per[dom])
+    roof = {"bound": r["bound"], "achieved": round(r["achieved"], 3), "peak": r["peak"],
+            "unit": r["unit"], "frac": round(r["frac"], 4), "traffic": traffic_for(w),
+            "kernel": w.kernel, "workload": w.name}
+
+    out = {
+        "metric": "scanned tokens/sec, SSD fwd L=4096 + M1 scan; % MFMA / % HBM roofline",
+        "value": tokens / (ms_per_step * 1e-3),
+        "unit": "scanned tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32" if all(getattr(w, "dtype", "f32") == "f32" for w in ws) else "f32+bf16",
+        "data": "synthetic (seeded numpy inputs, recipes in selective_state_space_amd/workloads.py)",
+        "config": {"workload": "+".join(names), "tokens_per_step": tokens,
+                   "shapes": {w.name: w.shape for w in ws}},
+        "roofline": roof,
+        "kernels": kernels,
+    }
+    if not args.no_cpu:
+        print("# timing the oracle on the host", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(names)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

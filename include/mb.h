@@ -1,0 +1,191 @@
+/*
+ * mb.h -- C ABI of libmb, the MI355X (gfx950) selective state-space scan
+ * library.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every tensor pointer is a DEVICE pointer to contiguous row-major memory,
+ *   last-named axis fastest, owned by the caller.  The library never keeps a
+ *   pointer after the call returns and never allocates or frees memory.
+ * - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued on
+ *   it asynchronously; no entry point synchronises the host, so every call can
+ *   be captured into a HIP graph.
+ * - Arguments are validated before anything is enqueued.  On any error code
+ *   other than MB_ERR_HIP nothing has been launched and no output was touched.
+ *   MB_ERR_HIP reports a failed launch; mb_last_hip_error() gives its code.
+ * - `dtype` selects the element type of the "activation" tensors named in each
+ *   entry point (MB_F32 or MB_BF16).  Every other tensor is fp32.  Arithmetic is
+ *   fp32 with fp32 accumulation; states are always fp32; a bf16 output is
+ *   rounded to nearest-even.  (TorchMamba README, API notes: half-precision
+ *   inputs compute in fp32, outputs take the input dtype, states stay fp32.)
+ * - NaN or Inf inputs propagate to the outputs; they are not trapped.
+ * - Outputs must not overlap inputs, except where an entry point says so.
+ * - A length-zero sequence is valid: the final state is h0 (or zeros) and no
+ *   y is written.  A zero batch is a no-op.
+ * - The library is re-entrant; its only global state is a per-device cache of
+ *   the compute-unit count, filled once under a lock.
+ */
+#ifndef MB_H
+#define MB_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MB_OK = 0,
+    MB_ERR_NULL = 1,      /* a required pointer is NULL                         */
+    MB_ERR_SHAPE = 2,     /* a size is negative, inconsistent or unsupported    */
+    MB_ERR_DTYPE = 3,     /* dtype is not MB_F32 / MB_BF16                      */
+    MB_ERR_WORKSPACE = 4, /* workspace missing, too small or misaligned        */
+    MB_ERR_HIP = 5,       /* a HIP launch failed                               */
+    MB_ERR_ALIAS = 6      /* an output overlaps an input it may not overlap    */
+} mb_status;
+
+typedef enum { MB_F32 = 0, MB_BF16 = 1 } mb_dtype;
+
+typedef enum {
+    MB_OP_SELECTIVE_SCAN = 0,
+    MB_OP_SSM_STEP = 1,
+    MB_OP_SSD_CHUNKED = 2,
+    MB_OP_TRAP_SSD = 3,
+    MB_OP_MIMO_SSD = 4
+} mb_op;
+
+/*
+ * Mamba-1 selective scan (TorchMamba README, Models table row "Mamba-1 (S6)"
+ * and Math notes M1; burn_mamba `struct Mamba1` docs, `selective_scan`).
+ * For every batch b, channel c and state n, exponential-Euler discretisation:
+ *     h_t[c,n] = exp(dt_t[c] * A[c,n]) * h_{t-1}[c,n] + dt_t[c] * B_t[n] * x_t[c]
+ *     y_t[c]   = sum_n C_t[n] * h_t[c,n] + Dskip[c] * x_t[c]
+ * h_{-1} = h0.  B and C are per (b, t) and shared by all channels.
+ *   x, dt : (batch, L, D)     dtype     dt is the final positive step (no softplus)
+ *   A     : (D, N)            fp32      used as given (not A_log)
+ *   B, C  : (batch, L, N)     dtype
+ *   Dskip : (D)               fp32      NULL = no skip term
+ *   h0    : (batch, D, N)     fp32      NULL = zeros
+ *   y     : (batch, L, D)     dtype     written
+ *   h_out : (batch, D, N)     fp32      final state; NULL = not written; may equal h0
+ * Supported: 1 <= N <= 64 (MB_ERR_SHAPE otherwise); any D, L, batch >= 0.
+ */
+mb_status mb_selective_scan(const void* x, const void* dt, const float* A,
+                            const void* B, const void* C, const float* Dskip,
+                            const float* h0, void* y, float* h_out,
+                            int64_t batch, int64_t L, int64_t D, int64_t N,
+                            mb_dtype dtype, hipStream_t stream);
+
+/*
+ * Mamba-1 single-token decode step (burn_mamba `struct Mamba1` docs,
+ * `selective_scan_step`; mamba-rs Quick Start `mamba_step`).  One iteration
+ * of the recurrence above for a batch of independent sequences:
+ *     h[b,c,n] <- exp(dt[b,c] * A[c,n]) * h[b,c,n] + dt[b,c] * B[b,n] * x[b,c]
+ *     y[b,c]    = sum_n C[b,n] * h[b,c,n] + Dskip[c] * x[b,c]
+ *   x, dt : (batch, D)  dtype;   B, C : (batch, N)  dtype;   A : (D, N) fp32
+ *   Dskip : (D) fp32 or NULL;    h_in, h_out : (batch, D, N) fp32
+ *   y     : (batch, D)  dtype
+ * h_out == h_in (in-place update, the decode use) is allowed; any other
+ * overlap between h_out and h_in is MB_ERR_ALIAS.
+ */
+mb_status mb_ssm_step(const void* x, const void* dt, const float* A,
+                      const void* B, const void* C, const float* Dskip,
+                      const float* h_in, float* h_out, void* y,
+                      int64_t batch, int64_t D, int64_t N,
+                      mb_dtype dtype, hipStream_t stream);
+
+/*
+ * Mamba-2 scalar-decay SSD, chunkwise (TorchMamba README, Models table row
+ * "Mamba-2 (SSD)" and Math notes M2: the dual form Y = (L o C B^T) X, computed
+ * per chunk with the state carried between chunks).  Per batch b and head h,
+ * with group g = h / (H/G):
+ *     S_t = exp(logdecay_t[h]) * S_{t-1} + B_t[g] (outer) X_t[h]      (N x P)
+ *     Y_t[h] = S_t^T C_t[g]
+ * S_{-1} = h0.  Heads share B and C within a group (H % G == 0 required).
+ *   X, Y      : (batch, L, H, P)  dtype
+ *   logdecay  : (batch, L, H)     fp32   log of the per-step decay (<= 0 in use)
+ *   B, C      : (batch, L, G, N)  dtype
+ *   h0, h_out : (batch, H, N, P)  fp32   h0 NULL = zeros; h_out may equal h0
+ * chunk: 0 selects the library's chunk length; otherwise must be 64.
+ * ws / ws_bytes: device workspace of at least mb_workspace_size(MB_OP_SSD_CHUNKED, ...)
+ * bytes, 256-byte aligned; contents on entry are ignored.
+ * Supported: N <= 128 and N % 4 == 0, P % 16 == 0.
+ */
+mb_status mb_ssd_chunked(const void* X, const float* logdecay, const void* B,
+                         const void* C, const float* h0, void* Y, float* h_out,
+                         int64_t batch, int64_t L, int64_t H, int64_t P,
+                         int64_t G, int64_t N, int64_t chunk, mb_dtype dtype,
+                         void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Mamba-3 SISO exponential-trapezoidal SSD with data-dependent rotations
+ * (TorchMamba README, Models table row "Mamba-3 SISO" and Math notes M3 SISO;
+ * mamba3-minimal README, "Two-SSD Decomposition").  Per batch b, head h:
+ *     Theta_t = sum_{s<=t} theta_s                    (per pair k; restarts per call)
+ *     B~_t = R(Theta_t) B_t,  C~_t = R(Theta_t) C_t   (consecutive pairs 2k, 2k+1)
+ *     S_t = exp(logdecay_t) S_{t-1} + beta_t B~_{t-1} (x) X_{t-1} + gamma_t B~_t (x) X_t
+ *     Y_t = S_t^T C~_t
+ * with B~_{-1} = X_{-1} = 0.  R(phi) = [[cos, -sin], [sin, cos]].
+ *   X, Y                   : (batch, L, H, P)    dtype
+ *   logdecay, beta, gamma  : (batch, L, H)       fp32 (alpha = exp(logdecay))
+ *   B, C                   : (batch, L, G, N)    dtype
+ *   theta                  : (batch, L, H, N/2)  fp32, or NULL for no rotation
+ *   h0, h_out              : (batch, H, N, P)    fp32, in the PHYSICAL (unrotated)
+ *                            frame: h_out = R(-Theta_{L-1}) S_{L-1}
+ * N must be even when theta != NULL.  Other limits as mb_ssd_chunked.
+ */
+mb_status mb_trap_ssd(const void* X, const float* logdecay, const void* B,
+                      const void* C, const float* beta, const float* gamma,
+                      const float* theta, const float* h0, void* Y,
+                      float* h_out, int64_t batch, int64_t L, int64_t H,
+                      int64_t P, int64_t G, int64_t N, int64_t chunk,
+                      mb_dtype dtype, void* ws, size_t ws_bytes,
+                      hipStream_t stream);
+
+/*
+ * Mamba-3 MIMO rank-R SSD (TorchMamba README, Models table row "Mamba-3 MIMO"
+ * and Math notes MIMO: the rank-R update is a matrix product on one shared
+ * (N, P) state).  As mb_trap_ssd, with every rank r of step t rotated by the
+ * same Theta_t:
+ *     S_t = exp(ld_t) S_{t-1} + beta_t sum_r B~_{t-1,r} (x) X_{t-1,r}
+ *                             + gamma_t sum_r B~_{t,r} (x) X_{t,r}
+ *     Y_{t,r} = S_t^T C~_{t,r}
+ *   X, Y      : (batch, L, H, P, R)  dtype     (rank innermost)
+ *   B, C      : (batch, L, H, N, R)  dtype     (per head, rank innermost)
+ *   logdecay, beta, gamma, theta, h0, h_out : as mb_trap_ssd (state has no R axis)
+ * Supported: R in {1, 2, 4, 8, 16}; other limits as mb_trap_ssd.
+ */
+mb_status mb_mimo_ssd(const void* X, const float* logdecay, const void* B,
+                      const void* C, const float* beta, const float* gamma,
+                      const float* theta, const float* h0, void* Y,
+                      float* h_out, int64_t batch, int64_t L, int64_t H,
+                      int64_t P, int64_t N, int64_t R, int64_t chunk,
+                      mb_dtype dtype, void* ws, size_t ws_bytes,
+                      hipStream_t stream);
+
+/*
+ * Bytes of device workspace an entry point needs for the given sizes (0 if it
+ * needs none).  Unused sizes are ignored: G for MB_OP_TRAP_SSD / MIMO, R for
+ * the others.  Returns 0 for invalid sizes as well (the call itself reports
+ * the error).
+ */
+size_t mb_workspace_size(mb_op op, int64_t batch, int64_t L, int64_t H,
+                         int64_t P, int64_t G, int64_t N, int64_t R,
+                         int64_t chunk);
+
+/* Static, NUL-terminated description of a status code. */
+const char* mb_status_str(mb_status status);
+
+/* The hipError_t of the most recent MB_ERR_HIP in this thread (0 if none). */
+int mb_last_hip_error(void);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int mb_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MB_H */

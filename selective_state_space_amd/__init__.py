@@ -1,1 +1,280 @@
-"""MI355X-native selective state-space scans (placeholder; binding follows)."""
+"""MI355X-native selective state-space scans.
+
+Thin Python binding over the C ABI in ``include/mb.h`` (``libmb.so``, built by
+``python -m selective_state_space_amd._build``).  The functions carry the same
+names as the C entry points and do argument marshalling only: check that the
+torch tensors are contiguous CUDA tensors of the right dtype and shape, allocate
+missing outputs and workspace with torch, and call the library on the current
+stream.  Every step of every scan runs in the HIP kernels; there is no fallback.
+If the library is missing the first call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+__all__ = [
+    "mb_selective_scan", "mb_ssm_step", "mb_ssd_chunked", "mb_trap_ssd", "mb_mimo_ssd",
+    "mb_workspace_size", "mb_status_str", "lib_path", "load_library", "MBError",
+    "MB_OP_SELECTIVE_SCAN", "MB_OP_SSM_STEP", "MB_OP_SSD_CHUNKED", "MB_OP_TRAP_SSD",
+    "MB_OP_MIMO_SSD",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libmb.so")
+_lock = threading.Lock()
+_lib = None
+
+MB_F32, MB_BF16 = 0, 1
+(MB_OP_SELECTIVE_SCAN, MB_OP_SSM_STEP, MB_OP_SSD_CHUNKED, MB_OP_TRAP_SSD,
+ MB_OP_MIMO_SSD) = range(5)
+
+_vp = ctypes.c_void_p
+_i64 = ctypes.c_int64
+
+
+class MBError(ValueError):
+    """A libmb entry point returned a status other than MB_OK."""
+
+    def __init__(self, fn, status):
+        msg = "%s failed: %s (status %d)" % (fn, mb_status_str(status), status)
+        if status == 5:
+            msg += ", hipError %d" % load_library().mb_last_hip_error()
+        super().__init__(msg)
+        self.status = status
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libmb.so (raises if it has not been built)."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(_LIB_PATH):
+            raise ImportError("libmb.so not built: run `python -m selective_state_space_amd._build`")
+        lib = ctypes.CDLL(_LIB_PATH)
+        lib.mb_selective_scan.argtypes = [_vp] * 9 + [_i64] * 4 + [ctypes.c_int, _vp]
+        lib.mb_ssm_step.argtypes = [_vp] * 9 + [_i64] * 3 + [ctypes.c_int, _vp]
+        if hasattr(lib, "mb_ssd_chunked"):
+            lib.mb_ssd_chunked.argtypes = [_vp] * 7 + [_i64] * 7 + [ctypes.c_int, _vp, ctypes.c_size_t, _vp]
+            lib.mb_trap_ssd.argtypes = [_vp] * 10 + [_i64] * 7 + [ctypes.c_int, _vp, ctypes.c_size_t, _vp]
+            lib.mb_mimo_ssd.argtypes = [_vp] * 10 + [_i64] * 7 + [ctypes.c_int, _vp, ctypes.c_size_t, _vp]
+            lib.mb_workspace_size.argtypes = [ctypes.c_int] + [_i64] * 8
+            lib.mb_workspace_size.restype = ctypes.c_size_t
+            for f in ("mb_ssd_chunked", "mb_trap_ssd", "mb_mimo_ssd"):
+                getattr(lib, f).restype = ctypes.c_int
+        lib.mb_status_str.argtypes = [ctypes.c_int]
+        lib.mb_status_str.restype = ctypes.c_char_p
+        lib.mb_last_hip_error.restype = ctypes.c_int
+        lib.mb_version.restype = ctypes.c_int
+        for f in ("mb_selective_scan", "mb_ssm_step"):
+            getattr(lib, f).restype = ctypes.c_int
+        _lib = lib
+        return lib
+
+
+def mb_status_str(status: int) -> str:
+    return load_library().mb_status_str(int(status)).decode()
+
+
+def mb_workspace_size(op, batch, L, H, P, G, N, R=1, chunk=0) -> int:
+    return int(load_library().mb_workspace_size(int(op), batch, L, H, P, G, N, R, chunk))
+
+
+# ----------------------------------------------------------------------------
+# marshalling helpers
+# ----------------------------------------------------------------------------
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t, name):
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return MB_F32
+    if t.dtype == torch.bfloat16:
+        return MB_BF16
+    raise TypeError("%s must be float32 or bfloat16, got %s" % (name, t.dtype))
+
+
+def _check(t, name, shape, dtype, device):
+    if t is None:
+        return None
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+    if t.dtype != dtype:
+        raise TypeError("%s has dtype %s, expected %s" % (name, t.dtype, dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return t
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _call(fn, *args):
+    st = getattr(load_library(), fn)(*args)
+    if st != 0:
+        raise MBError(fn, st)
+
+
+def _device_of(t):
+    if not t.is_cuda:
+        raise ValueError("tensors must be on a CUDA (HIP) device, got %s" % t.device)
+    return t.device
+
+
+def _workspace(op, device, ws, dims):
+    torch = _torch()
+    need = mb_workspace_size(op, *dims)
+    if ws is None:
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
+    if ws.device != device or not ws.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on %s" % device)
+    return ws, ws.numel() * ws.element_size()
+
+
+# ----------------------------------------------------------------------------
+# entry points
+# ----------------------------------------------------------------------------
+def mb_selective_scan(x, dt, A, B, C, D=None, h0=None, *, y=None, h_out=None):
+    """Mamba-1 selective scan.  x, dt (batch, L, D) and B, C (batch, L, N) share
+    one dtype (float32 or bfloat16); A (D, N), D (D,), h0 (batch, D, N) float32.
+    Returns (y, h_out)."""
+    torch = _torch()
+    dev = _device_of(x)
+    dtype = x.dtype
+    code = _dtype_code(x, "x")
+    b, L, Dm = x.shape
+    N = A.shape[1]
+    _check(x, "x", (b, L, Dm), dtype, dev)
+    _check(dt, "dt", (b, L, Dm), dtype, dev)
+    _check(A, "A", (Dm, N), torch.float32, dev)
+    _check(B, "B", (b, L, N), dtype, dev)
+    _check(C, "C", (b, L, N), dtype, dev)
+    _check(D, "D", (Dm,), torch.float32, dev)
+    _check(h0, "h0", (b, Dm, N), torch.float32, dev)
+    y = torch.empty((b, L, Dm), dtype=dtype, device=dev) if y is None else _check(y, "y", (b, L, Dm), dtype, dev)
+    h_out = torch.empty((b, Dm, N), dtype=torch.float32, device=dev) if h_out is None else \
+        _check(h_out, "h_out", (b, Dm, N), torch.float32, dev)
+    _call("mb_selective_scan", _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(h0),
+          _ptr(y), _ptr(h_out), b, L, Dm, N, code, _stream(dev))
+    return y, h_out
+
+
+def mb_ssm_step(x, dt, A, B, C, D, h, *, y=None, h_out=None):
+    """Mamba-1 decode step.  x, dt (batch, D), B, C (batch, N) in one dtype; A
+    (D, N), D (D,) or None, h (batch, D, N) float32.  With h_out=None the state
+    is updated in place.  Returns (y, h_out)."""
+    torch = _torch()
+    dev = _device_of(x)
+    dtype = x.dtype
+    code = _dtype_code(x, "x")
+    b, Dm = x.shape
+    N = A.shape[1]
+    _check(dt, "dt", (b, Dm), dtype, dev)
+    _check(A, "A", (Dm, N), torch.float32, dev)
+    _check(B, "B", (b, N), dtype, dev)
+    _check(C, "C", (b, N), dtype, dev)
+    _check(D, "D", (Dm,), torch.float32, dev)
+    _check(h, "h", (b, Dm, N), torch.float32, dev)
+    h_out = h if h_out is None else _check(h_out, "h_out", (b, Dm, N), torch.float32, dev)
+    y = torch.empty((b, Dm), dtype=dtype, device=dev) if y is None else _check(y, "y", (b, Dm), dtype, dev)
+    _call("mb_ssm_step", _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(h), _ptr(h_out),
+          _ptr(y), b, Dm, N, code, _stream(dev))
+    return y, h_out
+
+
+def mb_ssd_chunked(X, logdecay, B, C, h0=None, *, chunk=0, Y=None, h_out=None, ws=None):
+    """Mamba-2 SSD.  X (batch, L, H, P), B, C (batch, L, G, N) in one dtype;
+    logdecay (batch, L, H), h0 (batch, H, N, P) float32.  Returns (Y, h_out)."""
+    torch = _torch()
+    dev = _device_of(X)
+    dtype = X.dtype
+    code = _dtype_code(X, "X")
+    b, L, H, P = X.shape
+    G, N = B.shape[2], B.shape[3]
+    _check(logdecay, "logdecay", (b, L, H), torch.float32, dev)
+    _check(B, "B", (b, L, G, N), dtype, dev)
+    _check(C, "C", (b, L, G, N), dtype, dev)
+    _check(h0, "h0", (b, H, N, P), torch.float32, dev)
+    Y = torch.empty((b, L, H, P), dtype=dtype, device=dev) if Y is None else _check(Y, "Y", (b, L, H, P), dtype, dev)
+    h_out = torch.empty((b, H, N, P), dtype=torch.float32, device=dev) if h_out is None else \
+        _check(h_out, "h_out", (b, H, N, P), torch.float32, dev)
+    ws, nws = _workspace(MB_OP_SSD_CHUNKED, dev, ws, (b, L, H, P, G, N, 1, chunk))
+    _call("mb_ssd_chunked", _ptr(X), _ptr(logdecay), _ptr(B), _ptr(C), _ptr(h0), _ptr(Y), _ptr(h_out),
+          b, L, H, P, G, N, chunk, code, _ptr(ws), nws, _stream(dev))
+    return Y, h_out
+
+
+def mb_trap_ssd(X, logdecay, B, C, beta, gamma, theta=None, h0=None, *, chunk=0, Y=None,
+                h_out=None, ws=None):
+    """Mamba-3 SISO.  X (batch, L, H, P), B, C (batch, L, G, N) in one dtype;
+    logdecay, beta, gamma (batch, L, H), theta (batch, L, H, N/2) or None, h0
+    (batch, H, N, P) float32 (physical frame).  Returns (Y, h_out)."""
+    torch = _torch()
+    dev = _device_of(X)
+    dtype = X.dtype
+    code = _dtype_code(X, "X")
+    b, L, H, P = X.shape
+    G, N = B.shape[2], B.shape[3]
+    f32 = torch.float32
+    for t, n in ((logdecay, "logdecay"), (beta, "beta"), (gamma, "gamma")):
+        _check(t, n, (b, L, H), f32, dev)
+    _check(B, "B", (b, L, G, N), dtype, dev)
+    _check(C, "C", (b, L, G, N), dtype, dev)
+    _check(theta, "theta", (b, L, H, N // 2), f32, dev)
+    _check(h0, "h0", (b, H, N, P), f32, dev)
+    Y = torch.empty((b, L, H, P), dtype=dtype, device=dev) if Y is None else _check(Y, "Y", (b, L, H, P), dtype, dev)
+    h_out = torch.empty((b, H, N, P), dtype=f32, device=dev) if h_out is None else \
+        _check(h_out, "h_out", (b, H, N, P), f32, dev)
+    ws, nws = _workspace(MB_OP_TRAP_SSD, dev, ws, (b, L, H, P, G, N, 1, chunk))
+    _call("mb_trap_ssd", _ptr(X), _ptr(logdecay), _ptr(B), _ptr(C), _ptr(beta), _ptr(gamma),
+          _ptr(theta), _ptr(h0), _ptr(Y), _ptr(h_out), b, L, H, P, G, N, chunk, code, _ptr(ws), nws,
+          _stream(dev))
+    return Y, h_out
+
+
+def mb_mimo_ssd(X, logdecay, B, C, beta, gamma, theta=None, h0=None, *, chunk=0, Y=None,
+                h_out=None, ws=None):
+    """Mamba-3 MIMO.  X (batch, L, H, P, R), B, C (batch, L, H, N, R) in one
+    dtype; the rest as mb_trap_ssd.  Returns (Y, h_out)."""
+    torch = _torch()
+    dev = _device_of(X)
+    dtype = X.dtype
+    code = _dtype_code(X, "X")
+    b, L, H, P, R = X.shape
+    N = B.shape[3]
+    f32 = torch.float32
+    for t, n in ((logdecay, "logdecay"), (beta, "beta"), (gamma, "gamma")):
+        _check(t, n, (b, L, H), f32, dev)
+    _check(B, "B", (b, L, H, N, R), dtype, dev)
+    _check(C, "C", (b, L, H, N, R), dtype, dev)
+    _check(theta, "theta", (b, L, H, N // 2), f32, dev)
+    _check(h0, "h0", (b, H, N, P), f32, dev)
+    Y = torch.empty((b, L, H, P, R), dtype=dtype, device=dev) if Y is None else \
+        _check(Y, "Y", (b, L, H, P, R), dtype, dev)
+    h_out = torch.empty((b, H, N, P), dtype=f32, device=dev) if h_out is None else \
+        _check(h_out, "h_out", (b, H, N, P), f32, dev)
+    ws, nws = _workspace(MB_OP_MIMO_SSD, dev, ws, (b, L, H, P, 1, N, R, chunk))
+    _call("mb_mimo_ssd", _ptr(X), _ptr(logdecay), _ptr(B), _ptr(C), _ptr(beta), _ptr(gamma),
+          _ptr(theta), _ptr(h0), _ptr(Y), _ptr(h_out), b, L, H, P, N, R, chunk, code, _ptr(ws), nws,
+          _stream(dev))
+    return Y, h_out

@@ -1,0 +1,47 @@
+"""Helpers for the GPU parity tests: move seeded numpy inputs to the device in
+the run dtype, hand the oracle exactly the values the device sees, and measure
+the error the way the tolerances are stated: max|gpu - ref| / max|ref|."""
+import numpy as np
+import pytest
+import torch
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+# Names of the "activation" tensors that take the run dtype; all others stay fp32.
+ACT = {"x", "dt", "B", "C", "X"}
+
+
+def require_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def prepare(inp, dtype):
+    """Return (device tensors, fp64 arrays the oracle should see)."""
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    dev, ref = {}, {}
+    for k, v in inp.items():
+        if v is None:
+            dev[k], ref[k] = None, None
+            continue
+        t = torch.from_numpy(np.ascontiguousarray(v))
+        t = t.to(tdt if k in ACT else torch.float32)
+        ref[k] = t.to(torch.float64).numpy()
+        dev[k] = t.cuda()
+    return dev, ref
+
+
+def rel_err(got, ref):
+    got = got.detach().to(torch.float64).cpu().numpy() if isinstance(got, torch.Tensor) else got
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    if not np.all(np.isfinite(got)):
+        return float("inf")
+    den = np.max(np.abs(ref)) if ref.size else 0.0
+    num = np.max(np.abs(got - ref)) if ref.size else 0.0
+    return float(num / den) if den > 0 else float(num)
+
+
+def assert_close(got, ref, dtype, what=""):
+    e = rel_err(got, ref)
+    assert e <= TOL[dtype], "%s: max|err|/max|ref| = %.3e > %.0e" % (what, e, TOL[dtype])
+    return e

@@ -1,0 +1,135 @@
+"""CPU checks of the C ABI: libmb.so loads, exports every entry point that
+include/mb.h declares, and rejects invalid arguments on the host before anything
+is enqueued (no GPU needed: every call here fails validation or is a no-op)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import selective_state_space_amd as mb
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mb.h")
+
+OK, E_NULL, E_SHAPE, E_DTYPE, E_WS, E_HIP, E_ALIAS = range(7)
+FAKE = 0x10000000          # never dereferenced: validation fails before any access
+F32, BF16 = 0, 1
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(mb.lib_path()):
+        from selective_state_space_amd import _build
+        _build.build()
+    return mb.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mb_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_exports_every_declared_function(lib):
+    names = declared_functions()
+    assert {"mb_selective_scan", "mb_ssm_step", "mb_ssd_chunked", "mb_trap_ssd", "mb_mimo_ssd",
+            "mb_workspace_size", "mb_status_str", "mb_last_hip_error", "mb_version"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), "libmb.so does not export " + n
+
+
+def test_status_strings(lib):
+    for s in range(7):
+        assert mb.mb_status_str(s)
+    assert mb.mb_status_str(99) == "unknown status"
+    assert lib.mb_version() >= 100
+    assert lib.mb_last_hip_error() == 0
+
+
+def P(x=FAKE):
+    return ctypes.c_void_p(x)
+
+
+def scan(lib, x=FAKE, dt=FAKE, A=FAKE, B=FAKE, C=FAKE, D=None, h0=None, y=FAKE + (1 << 24),
+         h_out=FAKE + (1 << 25), batch=2, L=8, Dm=16, N=16, dtype=F32):
+    return lib.mb_selective_scan(P(x) if x else None, P(dt) if dt else None, P(A) if A else None,
+                                 P(B) if B else None, P(C) if C else None, P(D) if D else None,
+                                 P(h0) if h0 else None, P(y) if y else None,
+                                 P(h_out) if h_out else None, batch, L, Dm, N, dtype, None)
+
+
+def test_scan_validation(lib):
+    base = dict(x=FAKE, dt=FAKE + 4096, A=FAKE + 8192, B=FAKE + 12288, C=FAKE + 16384)
+    assert scan(lib, **base, dtype=7) == E_DTYPE
+    assert scan(lib, **base, N=0) == E_SHAPE
+    assert scan(lib, **base, N=65) == E_SHAPE
+    assert scan(lib, **base, L=-1) == E_SHAPE
+    assert scan(lib, **dict(base, x=0)) == E_NULL
+    assert scan(lib, **dict(base, C=0)) == E_NULL
+    # y overlapping x
+    assert scan(lib, **base, y=FAKE + 16) == E_ALIAS
+    # h_out overlapping B
+    assert scan(lib, **base, h_out=FAKE + 12288) == E_ALIAS
+    # empty batch is a no-op that succeeds without touching the device
+    assert scan(lib, **base, batch=0) == OK
+
+
+def step(lib, h_in=FAKE + (1 << 26), h_out=FAKE + (1 << 26), y=FAKE + (1 << 27), **kw):
+    args = dict(x=FAKE, dt=FAKE + 4096, A=FAKE + 8192, B=FAKE + 12288, C=FAKE + 16384)
+    args.update(kw)
+    b, Dm, N = 4, 16, 16
+    return lib.mb_ssm_step(P(args["x"]), P(args["dt"]), P(args["A"]), P(args["B"]), P(args["C"]),
+                           None, P(h_in), P(h_out), P(y), b, Dm, N, args.get("dtype", F32), None)
+
+
+def test_step_validation(lib):
+    assert step(lib, dtype=3) == E_DTYPE
+    # partial overlap between h_out and h_in is rejected (exact aliasing is allowed)
+    assert step(lib, h_out=FAKE + (1 << 26) + 64) == E_ALIAS
+    assert step(lib, y=FAKE + 8) == E_ALIAS
+
+
+def ssd(lib, ws=FAKE + (1 << 28), ws_bytes=1 << 30, H=4, P_=64, G=1, N=128, L=100, chunk=0,
+        dtype=F32, Y=FAKE + (1 << 27), batch=2):
+    return lib.mb_ssd_chunked(P(FAKE), P(FAKE + (1 << 22)), P(FAKE + (1 << 23)), P(FAKE + (1 << 24)),
+                              None, P(Y), P(FAKE + (1 << 26)), batch, L, H, P_, G, N, chunk, dtype,
+                              P(ws) if ws else None, ws_bytes, None)
+
+
+def test_ssd_validation(lib):
+    assert ssd(lib, dtype=2) == E_DTYPE
+    assert ssd(lib, G=3) == E_SHAPE            # H % G != 0
+    assert ssd(lib, N=130) == E_SHAPE
+    assert ssd(lib, N=6) == E_SHAPE            # N % 4 != 0
+    assert ssd(lib, P_=40) == E_SHAPE          # P % 16 != 0
+    assert ssd(lib, chunk=32) == E_SHAPE
+    assert ssd(lib, ws=0) == E_WS
+    assert ssd(lib, ws_bytes=16) == E_WS
+    assert ssd(lib, ws=FAKE + (1 << 28) + 4) == E_WS   # misaligned
+    assert ssd(lib, Y=FAKE + 64) == E_ALIAS
+    assert ssd(lib, batch=0) == OK
+
+
+def test_trap_and_mimo_validation(lib):
+    args = [P(FAKE), P(FAKE + (1 << 22)), P(FAKE + (1 << 23)), P(FAKE + (1 << 24)),
+            P(FAKE + (1 << 25)), P(FAKE + (1 << 25) + (1 << 21)), P(FAKE + (1 << 29)), None,
+            P(FAKE + (1 << 27)), P(FAKE + (1 << 26))]
+    # odd N with rotation angles
+    assert lib.mb_trap_ssd(*args, 1, 10, 2, 16, 1, 6, 0, F32, P(FAKE + (1 << 28)), 1 << 30, None) == E_SHAPE
+    # beta missing
+    a2 = list(args)
+    a2[4] = None
+    assert lib.mb_trap_ssd(*a2, 1, 10, 2, 16, 1, 8, 0, F32, P(FAKE + (1 << 28)), 1 << 30, None) == E_NULL
+    # unsupported rank
+    assert lib.mb_mimo_ssd(*args, 1, 10, 2, 16, 8, 3, 0, F32, P(FAKE + (1 << 28)), 1 << 30, None) == E_SHAPE
+    assert lib.mb_mimo_ssd(*args, 0, 10, 2, 16, 8, 4, 0, F32, P(FAKE + (1 << 28)), 1 << 30, None) == OK
+
+
+def test_workspace_sizes(lib):
+    # scores: batch * chunks * (groups or heads) * 64 rows * columns * 4 bytes
+    assert mb.mb_workspace_size(mb.MB_OP_SELECTIVE_SCAN, 8, 2048, 1, 1, 1, 16) == 0
+    assert mb.mb_workspace_size(mb.MB_OP_SSD_CHUNKED, 4, 4096, 24, 64, 1, 128) == 4 * 64 * 1 * 64 * 64 * 4
+    assert mb.mb_workspace_size(mb.MB_OP_TRAP_SSD, 4, 4096, 24, 64, 1, 128) == 4 * 64 * 24 * 64 * 65 * 4
+    assert mb.mb_workspace_size(mb.MB_OP_MIMO_SSD, 2, 8192, 16, 64, 1, 128, 4) == 2 * 512 * 16 * 64 * 68 * 4
+    assert mb.mb_workspace_size(mb.MB_OP_SSD_CHUNKED, 4, 4096, 24, 64, 5, 128) == 0   # invalid G

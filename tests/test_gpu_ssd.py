@@ -1,0 +1,185 @@
+"""GPU parity of the chunkwise SSD family (Mamba-2 SSD, Mamba-3 SISO, Mamba-3
+MIMO) against the fp64 oracle, through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+import selective_state_space_amd as mb
+from selective_state_space_amd import workloads as wl
+from gpu_util import assert_close, prepare, require_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def _seed(*xs):
+    return int(abs(hash(tuple(xs)))) % (2 ** 32)
+
+
+# -------------------------------------------------------------------- SSD ----
+SSD_SHAPES = [  # batch, L, H, P, N, G
+    (1, 1, 1, 16, 4, 1), (2, 65, 2, 16, 8, 1), (1, 64, 3, 32, 16, 3), (2, 130, 4, 16, 128, 2),
+    (1, 200, 2, 64, 128, 1), (2, 333, 3, 48, 64, 1), (1, 129, 6, 16, 32, 2)]
+
+
+@pytest.mark.parametrize("shape", SSD_SHAPES, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_ssd_shapes(oracle_mod, shape, dtype):
+    b, L, H, P, N, G = shape
+    inp = wl.ssd_inputs(np.random.default_rng(_seed(shape, 1)), b, L, H, P, N, G=G, h0_sd=0.05)
+    dev, ref = prepare(inp, dtype)
+    Y, h = mb.mb_ssd_chunked(dev["X"], dev["logdecay"], dev["B"], dev["C"], dev["h0"])
+    Yr, hr = oracle_mod.ssd(**ref)
+    assert Y.dtype == dev["X"].dtype
+    assert_close(Y, Yr, dtype, "Y")
+    assert_close(h, hr, dtype, "h")
+
+
+def test_ssd_split_chaining(oracle_mod):
+    inp = wl.ssd_inputs(np.random.default_rng(3), 2, 300, 2, 32, 64, h0_sd=0.05)
+    dev, ref = prepare(inp, "f32")
+    s = 100
+    cut = lambda k, sl: dev[k][:, sl].contiguous()
+    Ya, ha = mb.mb_ssd_chunked(cut("X", slice(0, s)), cut("logdecay", slice(0, s)),
+                               cut("B", slice(0, s)), cut("C", slice(0, s)), dev["h0"])
+    Yb, hb = mb.mb_ssd_chunked(cut("X", slice(s, None)), cut("logdecay", slice(s, None)),
+                               cut("B", slice(s, None)), cut("C", slice(s, None)), ha)
+    Yr, hr = oracle_mod.ssd(**ref)
+    assert_close(torch.cat([Ya, Yb], 1), Yr, "f32", "Y")
+    assert_close(hb, hr, "f32", "h")
+
+
+def test_ssd_zero_length_and_in_place_state():
+    X = torch.empty(2, 0, 2, 16, device="cuda")
+    ld = torch.empty(2, 0, 2, device="cuda")
+    B = torch.empty(2, 0, 1, 8, device="cuda")
+    h0 = torch.randn(2, 2, 8, 16, device="cuda")
+    Y, h = mb.mb_ssd_chunked(X, ld, B, B, h0)
+    assert torch.equal(h, h0)
+    hh = h0.clone()
+    Y, h = mb.mb_ssd_chunked(X, ld, B, B, hh, h_out=hh)
+    assert torch.equal(hh, h0)
+
+
+def test_ssd_deterministic():
+    dev, _ = prepare(wl.ssd_inputs(np.random.default_rng(4), 2, 257, 3, 32, 128), "f32")
+    r1 = mb.mb_ssd_chunked(dev["X"], dev["logdecay"], dev["B"], dev["C"])
+    r2 = mb.mb_ssd_chunked(dev["X"], dev["logdecay"], dev["B"], dev["C"])
+    assert torch.equal(r1[0], r2[0]) and torch.equal(r1[1], r2[1])
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_ssd_block_workload_full(oracle_mod, dtype):
+    """batch 4, L 4096, H 24, P 64, N 128, G 1 -- the bench configuration."""
+    dev, ref = prepare(wl.ssd_block(), dtype)
+    Y, h = mb.mb_ssd_chunked(dev["X"], dev["logdecay"], dev["B"], dev["C"])
+    torch.cuda.synchronize()
+    Yr, hr = oracle_mod.ssd(**ref)
+    assert_close(Y, Yr, dtype, "Y")
+    assert_close(h, hr, dtype, "h")
+
+
+# ------------------------------------------------------------------- SISO ----
+TRAP_SHAPES = [  # batch, L, H, P, N, G
+    (1, 1, 1, 16, 4, 1), (2, 65, 2, 16, 8, 2), (1, 64, 3, 32, 16, 1), (2, 130, 4, 16, 128, 2),
+    (1, 333, 2, 64, 128, 1), (2, 97, 3, 32, 32, 3)]
+
+
+@pytest.mark.parametrize("shape", TRAP_SHAPES, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("rotate", [True, False])
+def test_siso_shapes(oracle_mod, shape, rotate):
+    b, L, H, P, N, G = shape
+    inp = wl.trap_inputs(np.random.default_rng(_seed(shape, rotate)), b, L, H, P, N, G=G,
+                         h0_sd=0.05, rotate=rotate)
+    dev, ref = prepare(inp, "f32")
+    Y, h = mb.mb_trap_ssd(dev["X"], dev["logdecay"], dev["B"], dev["C"], dev["beta"], dev["gamma"],
+                          dev["theta"], dev["h0"])
+    Yr, hr = oracle_mod.trap(**ref)
+    assert_close(Y, Yr, "f32", "Y")
+    assert_close(h, hr, "f32", "h")
+
+
+def test_siso_bf16(oracle_mod):
+    inp = wl.trap_inputs(np.random.default_rng(5), 2, 200, 3, 32, 64, h0_sd=0.05)
+    dev, ref = prepare(inp, "bf16")
+    Y, h = mb.mb_trap_ssd(dev["X"], dev["logdecay"], dev["B"], dev["C"], dev["beta"], dev["gamma"],
+                          dev["theta"], dev["h0"])
+    Yr, hr = oracle_mod.trap(**ref)
+    assert_close(Y, Yr, "bf16", "Y")
+    assert_close(h, hr, "bf16", "h")
+
+
+def test_siso_large_angles(oracle_mod):
+    """Accumulated angles of several hundred radians (long sequence, large theta):
+    the chunk-local angles keep fp32 accurate."""
+    inp = wl.trap_inputs(np.random.default_rng(6), 1, 2000, 2, 16, 32)
+    inp["theta"] = inp["theta"] * 8.0
+    dev, ref = prepare(inp, "f32")
+    Y, h = mb.mb_trap_ssd(dev["X"], dev["logdecay"], dev["B"], dev["C"], dev["beta"], dev["gamma"],
+                          dev["theta"], None)
+    Yr, hr = oracle_mod.trap(**ref)
+    assert np.max(np.cumsum(ref["theta"], axis=1)) > 300
+    assert_close(Y, Yr, "f32", "Y")
+    assert_close(h, hr, "f32", "h")
+
+
+@pytest.mark.slow
+def test_siso_block_workload_full(oracle_mod):
+    """batch 4, L 4096, H 24, P 64, N 128 with rotations -- the bench configuration."""
+    dev, ref = prepare(wl.siso_block(), "f32")
+    Y, h = mb.mb_trap_ssd(dev["X"], dev["logdecay"], dev["B"], dev["C"], dev["beta"], dev["gamma"],
+                          dev["theta"], None)
+    torch.cuda.synchronize()
+    Yr, hr = oracle_mod.trap(**ref)
+    assert_close(Y, Yr, "f32", "Y")
+    assert_close(h, hr, "f32", "h")
+
+
+# ------------------------------------------------------------------- MIMO ----
+MIMO_SHAPES = [  # batch, L, H, P, N, R
+    (1, 1, 1, 16, 4, 1), (2, 37, 2, 16, 8, 2), (1, 70, 2, 32, 16, 4), (2, 50, 2, 16, 128, 4),
+    (1, 33, 3, 16, 32, 8), (1, 21, 2, 16, 16, 16), (2, 130, 2, 32, 64, 1)]
+
+
+@pytest.mark.parametrize("shape", MIMO_SHAPES, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("rotate", [True, False])
+def test_mimo_shapes(oracle_mod, shape, rotate):
+    b, L, H, P, N, R = shape
+    inp = wl.mimo_inputs(np.random.default_rng(_seed(shape, rotate)), b, L, H, P, N, R,
+                         h0_sd=0.05, rotate=rotate)
+    dev, ref = prepare(inp, "f32")
+    Y, h = mb.mb_mimo_ssd(dev["X"], dev["logdecay"], dev["B"], dev["C"], dev["beta"], dev["gamma"],
+                          dev["theta"], dev["h0"])
+    Yr, hr = oracle_mod.mimo(**ref)
+    assert_close(Y, Yr, "f32", "Y")
+    assert_close(h, hr, "f32", "h")
+
+
+def test_mimo_rank_one_matches_siso():
+    """R = 1 MIMO equals SISO with one group per head (both on the GPU)."""
+    inp = wl.mimo_inputs(np.random.default_rng(7), 2, 100, 3, 32, 64, 1, h0_sd=0.05)
+    dev, _ = prepare(inp, "f32")
+    Ym, hm = mb.mb_mimo_ssd(dev["X"], dev["logdecay"], dev["B"], dev["C"], dev["beta"], dev["gamma"],
+                            dev["theta"], dev["h0"])
+    Ys, hs = mb.mb_trap_ssd(dev["X"][..., 0].contiguous(), dev["logdecay"], dev["B"][..., 0].contiguous(),
+                            dev["C"][..., 0].contiguous(), dev["beta"], dev["gamma"], dev["theta"], dev["h0"])
+    scale = torch.max(torch.abs(Ys)).item()
+    assert torch.max(torch.abs(Ym[..., 0] - Ys)).item() <= 1e-4 * scale
+    assert torch.max(torch.abs(hm - hs)).item() <= 1e-4 * torch.max(torch.abs(hs)).item()
+
+
+@pytest.mark.slow
+def test_mimo_block_workload_full(oracle_mod):
+    """batch 2, L 8192, H 16, P 64, N 128, R 4 -- the bench configuration."""
+    dev, ref = prepare(wl.mimo_block(), "f32")
+    Y, h = mb.mb_mimo_ssd(dev["X"], dev["logdecay"], dev["B"], dev["C"], dev["beta"], dev["gamma"],
+                          dev["theta"], None)
+    torch.cuda.synchronize()
+    Yr, hr = oracle_mod.mimo(**ref)
+    assert_close(Y, Yr, "f32", "Y")
+    assert_close(h, hr, "f32", "h")
