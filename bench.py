@@ -101,6 +101,7 @@ class M1Scan(Workload):
         b, L, D, N = 8, 2048, 1536, 16
         self.shape = dict(batch=b, L=L, D=D, N=N)
         inp = wl.m1_block()
+        self.inp = inp
         f = torch.float32
         self.x, self.dt, self.B, self.C = (_dev(inp[k], f) for k in ("x", "dt", "B", "C"))
         self.A, self.D = _dev(inp["A"], f), _dev(inp["D"], f)
@@ -124,6 +125,7 @@ class M1Step(Workload):
         b, D, N = 256, 1536, 16
         self.shape = dict(batch=b, D=D, N=N)
         inp = wl.m1_decode()
+        self.inp = inp
         f = torch.float32
         self.x, self.dt, self.B, self.C = (_dev(inp[k], f) for k in ("x", "dt", "B", "C"))
         self.A, self.D = _dev(inp["A"], f), _dev(inp["D"], f)
@@ -148,6 +150,7 @@ class SSD(Workload):
         b, L, H, P, N, G = 4, 4096, 24, 64, 128, 1
         self.shape = dict(batch=b, L=L, H=H, P=P, N=N, G=G)
         inp = wl.ssd_block()
+        self.inp = inp
         act = torch.bfloat16 if dtype == "bf16" else torch.float32
         self.X, self.B, self.C = (_dev(inp[k], act) for k in ("X", "B", "C"))
         self.ld = _dev(inp["logdecay"], torch.float32)
@@ -178,6 +181,7 @@ class SISO(Workload):
         b, L, H, P, N, G = 4, 4096, 24, 64, 128, 1
         self.shape = dict(batch=b, L=L, H=H, P=P, N=N, G=G)
         inp = wl.siso_block()
+        self.inp = inp
         f = torch.float32
         self.t = {k: _dev(inp[k], f) for k in ("X", "logdecay", "B", "C", "beta", "gamma", "theta")}
         self.Y = torch.empty_like(self.t["X"])
@@ -205,6 +209,7 @@ class MIMO(Workload):
         b, L, H, P, N, R = 2, 8192, 16, 64, 128, 4
         self.shape = dict(batch=b, L=L, H=H, P=P, N=N, R=R)
         inp = wl.mimo_block()
+        self.inp = inp
         f = torch.float32
         self.t = {k: _dev(inp[k], f) for k in ("X", "logdecay", "B", "C", "beta", "gamma", "theta")}
         self.Y = torch.empty_like(self.t["X"])
@@ -272,40 +277,30 @@ def traffic_for(w):
 # ----------------------------------------------------------------------------
 # CPU baseline: the fp64 oracle on a bounded sample of each workload
 # ----------------------------------------------------------------------------
-def cpu_baseline(names):
+def cpu_baseline(ws):
+    """Time the fp64 oracle on the host cores on the same inputs (bf16 inputs are
+    timed with their fp32 values: the oracle's cost does not depend on them)."""
     import oracle
-    from selective_state_space_amd import workloads as wl
     oracle.build()
     threads = oracle.get_threads()
-    total_tok, total_s, parts = 0.0, 0.0, []
-    for n in names:
-        if n == "m1_scan":
-            inp = wl.m1_block(batch=1, L=512)
-            t0 = time.perf_counter(); oracle.m1_scan(**inp); dt = time.perf_counter() - t0
-            tok, desc = 512, "m1_scan batch 1 x L 512 of D 1536"
-        elif n == "m1_step":
-            inp = wl.m1_decode()
-            t0 = time.perf_counter()
-            oracle.m1_step(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["D"], inp["h"])
-            dt = time.perf_counter() - t0
-            tok, desc = 256, "m1_step full (256 sequences)"
-        elif n in ("ssd_f32", "ssd_bf16"):
-            inp = wl.ssd_block(batch=1, L=512)
-            t0 = time.perf_counter(); oracle.ssd(**inp); dt = time.perf_counter() - t0
-            tok, desc = 512, n + " batch 1 x L 512 of H 24"
-        elif n == "siso":
-            inp = wl.siso_block(batch=1, L=512)
-            t0 = time.perf_counter(); oracle.trap(**inp); dt = time.perf_counter() - t0
-            tok, desc = 512, "siso batch 1 x L 512 of H 24"
-        elif n == "mimo":
-            inp = wl.mimo_block(batch=1, L=256)
-            t0 = time.perf_counter(); oracle.mimo(**inp); dt = time.perf_counter() - t0
-            tok, desc = 256, "mimo batch 1 x L 256 of H 16"
-        else:
-            continue
-        total_tok += tok
+    total_tok, total_s, parts = 0, 0.0, []
+    for w in ws:
+        i = w.inp
+        t0 = time.perf_counter()
+        if w.name == "m1_scan":
+            oracle.m1_scan(**i)
+        elif w.name == "m1_step":
+            oracle.m1_step(i["x"], i["dt"], i["A"], i["B"], i["C"], i["D"], i["h"])
+        elif w.name.startswith("ssd"):
+            oracle.ssd(**i)
+        elif w.name == "siso":
+            oracle.trap(**i)
+        elif w.name == "mimo":
+            oracle.mimo(**i)
+        dt = time.perf_counter() - t0
+        total_tok += w.tokens
         total_s += dt
-        parts.append("%s (%.2f s)" % (desc, dt))
+        parts.append("%s full (%d tokens, %.2f s)" % (w.name, w.tokens, dt))
     return {"value": total_tok / total_s if total_s else None, "unit": "scanned tokens/s",
             "cores": threads, "kind": "oracle", "sample": "; ".join(parts)}
 
@@ -394,7 +389,7 @@ def main():
     }
     if not args.no_cpu:
         print("# timing the oracle on the host", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(names)
+        out["cpu_baseline"] = cpu_baseline(ws)
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out))

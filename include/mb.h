@@ -20,6 +20,8 @@
  *   inputs compute in fp32, outputs take the input dtype, states stay fp32.)
  * - NaN or Inf inputs propagate to the outputs; they are not trapped.
  * - Outputs must not overlap inputs, except where an entry point says so.
+ * - The chunked SSD entry points read X, B, C and write Y with 16-byte vector
+ *   accesses: those four pointers must be 16-byte aligned (MB_ERR_ALIGN).
  * - A length-zero sequence is valid: the final state is h0 (or zeros) and no
  *   y is written.  A zero batch is a no-op.
  * - The library is re-entrant; its only global state is a per-device cache of
@@ -43,7 +45,8 @@ typedef enum {
     MB_ERR_DTYPE = 3,     /* dtype is not MB_F32 / MB_BF16                      */
     MB_ERR_WORKSPACE = 4, /* workspace missing, too small or misaligned        */
     MB_ERR_HIP = 5,       /* a HIP launch failed                               */
-    MB_ERR_ALIAS = 6      /* an output overlaps an input it may not overlap    */
+    MB_ERR_ALIAS = 6,     /* an output overlaps an input it may not overlap    */
+    MB_ERR_ALIGN = 7      /* a tensor pointer is not 16-byte aligned           */
 } mb_status;
 
 typedef enum { MB_F32 = 0, MB_BF16 = 1 } mb_dtype;

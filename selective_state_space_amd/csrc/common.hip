@@ -50,6 +50,7 @@ extern "C" const char* mb_status_str(mb_status s) {
         case MB_ERR_WORKSPACE: return "workspace missing, too small or misaligned";
         case MB_ERR_HIP: return "HIP launch failed (see mb_last_hip_error)";
         case MB_ERR_ALIAS: return "an output overlaps an input";
+        case MB_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
     }
     return "unknown status";
 }

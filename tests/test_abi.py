@@ -12,7 +12,7 @@ import selective_state_space_amd as mb
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "mb.h")
 
-OK, E_NULL, E_SHAPE, E_DTYPE, E_WS, E_HIP, E_ALIAS = range(7)
+OK, E_NULL, E_SHAPE, E_DTYPE, E_WS, E_HIP, E_ALIAS, E_ALIGN = range(8)
 FAKE = 0x10000000          # never dereferenced: validation fails before any access
 F32, BF16 = 0, 1
 
@@ -40,7 +40,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_status_strings(lib):
-    for s in range(7):
+    for s in range(8):
         assert mb.mb_status_str(s)
     assert mb.mb_status_str(99) == "unknown status"
     assert lib.mb_version() >= 100
@@ -108,6 +108,7 @@ def test_ssd_validation(lib):
     assert ssd(lib, ws_bytes=16) == E_WS
     assert ssd(lib, ws=FAKE + (1 << 28) + 4) == E_WS   # misaligned
     assert ssd(lib, Y=FAKE + 64) == E_ALIAS
+    assert ssd(lib, Y=FAKE + (1 << 27) + 8) == E_ALIGN
     assert ssd(lib, batch=0) == OK
 
 
@@ -130,6 +131,6 @@ def test_workspace_sizes(lib):
     # scores: batch * chunks * (groups or heads) * 64 rows * columns * 4 bytes
     assert mb.mb_workspace_size(mb.MB_OP_SELECTIVE_SCAN, 8, 2048, 1, 1, 1, 16) == 0
     assert mb.mb_workspace_size(mb.MB_OP_SSD_CHUNKED, 4, 4096, 24, 64, 1, 128) == 4 * 64 * 1 * 64 * 64 * 4
-    assert mb.mb_workspace_size(mb.MB_OP_TRAP_SSD, 4, 4096, 24, 64, 1, 128) == 4 * 64 * 24 * 64 * 65 * 4
+    assert mb.mb_workspace_size(mb.MB_OP_TRAP_SSD, 4, 4096, 24, 64, 1, 128) == 4 * 64 * 24 * 64 * 68 * 4
     assert mb.mb_workspace_size(mb.MB_OP_MIMO_SSD, 2, 8192, 16, 64, 1, 128, 4) == 2 * 512 * 16 * 64 * 68 * 4
     assert mb.mb_workspace_size(mb.MB_OP_SSD_CHUNKED, 4, 4096, 24, 64, 5, 128) == 0   # invalid G
