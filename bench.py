@@ -39,6 +39,9 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 FP32_PEAK_TFLOPS = 157.3       # MI355X dense fp32 (vector and MFMA)
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 VALU_F32_LANE_OPS = 256 * 2.4e9 * 64   # non-packed fp32 VALU lane-ops/s (256 CU x 2.4 GHz x 64 lanes)
+# Minimal VALU issue slots per Mamba-1 (t, c, n) element: dt*A (1), exp (2: the
+# transcendental unit runs at half rate), (dt*x)*B (1), a*h + u (1), y += C*h (1).
+M1_SLOTS_PER_ELEM = 6
 
 
 # ----------------------------------------------------------------------------
@@ -94,6 +97,7 @@ def _dev(a, dtype):
 class M1Scan(Workload):
     name = "m1_scan"
     kernel = "k_m1_scan"
+    bound = "alu"
     source = "selective_state_space_amd/csrc/m1.hip"
 
     def __init__(self, mb, wl, torch):
@@ -140,7 +144,7 @@ class M1Step(Workload):
 
 
 class SSD(Workload):
-    kernel = "k_ssd_walk"
+    kernel = "k_scores + k_walk"
     source = "selective_state_space_amd/csrc/ssd.hip"
     bound = "mfma"
 
@@ -172,7 +176,7 @@ class SSD(Workload):
 
 class SISO(Workload):
     name = "siso"
-    kernel = "k_trap_walk"
+    kernel = "k_scores + k_walk"
     source = "selective_state_space_amd/csrc/ssd.hip"
     bound = "mfma"
 
@@ -200,7 +204,7 @@ class SISO(Workload):
 
 class MIMO(Workload):
     name = "mimo"
-    kernel = "k_trap_walk"
+    kernel = "k_scores + k_walk"
     source = "selective_state_space_amd/csrc/ssd.hip"
     bound = "mfma"
 
@@ -245,10 +249,15 @@ def make(name, mb, wl, torch):
     raise ValueError(name)
 
 
-def roofline_of(w, ms):
+def roofline_of(w, ms, bound=None):
     """Achieved fraction of the roofline that bounds workload w at ms per call."""
     s = ms * 1e-3
-    if w.bound == "mfma":
+    bound = bound or w.bound
+    if bound == "alu":
+        ach = w.exps * M1_SLOTS_PER_ELEM / s / 1e9
+        peak = VALU_F32_LANE_OPS / 1e9
+        return {"bound": "alu", "achieved": ach, "peak": peak, "unit": "Gop/s", "frac": ach / peak}
+    if bound == "mfma":
         peak = BF16_PEAK_TFLOPS if getattr(w, "dtype", "f32") == "bf16" else FP32_PEAK_TFLOPS
         ach = w.flops / s / 1e12
         return {"bound": "mfma", "achieved": ach, "peak": peak, "unit": "TFLOP/s", "frac": ach / peak}
@@ -361,8 +370,9 @@ def main():
         r = roofline_of(w, ms)
         d = {"workload": w.name, "ms": round(ms, 5), "tokens_per_s": w.tokens / (ms * 1e-3),
              "roofline": {k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}}
-        hbm = w.bytes / (ms * 1e-3) / 1e9
-        d["hbm_gbs"] = round(hbm, 1)
+        hbm = roofline_of(w, ms, "hbm")
+        d["hbm_gbs"] = round(hbm["achieved"], 1)
+        d["hbm_frac"] = round(hbm["frac"], 4)
         if w.exps:
             d["exp_per_s"] = w.exps / (ms * 1e-3)
         kernels.append(d)
