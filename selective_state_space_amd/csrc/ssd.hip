@@ -14,27 +14,34 @@
 // decomposition; keeping both passes in one mask is the "1SS @ band" form, so
 // the scores C~ B~^T, the decay factors and the output contraction are shared.
 // Per chunk, with H the state entering the chunk (physical frame):
-//     Y   = (w o S) X + diag(e^{cum}) C~ H,      S = C~ B~^T (rows x (R + rows))
+//     Y   = (w o S) X + diag(e^{cum}) C~ H,      S = C~ B~^T (rows x (rows + R))
 //     H'  = e^{cum_last} H + B~^T diag(w(last, .)) X
 // Rotations use chunk-local angles Phi_t = sum_{u<=t in chunk} theta_u, so B~ of
 // the previous step is unrotated; the carried state is rotated back by
 // R(-Phi_last) at the end of every chunk, which keeps it in the physical frame
 // and keeps every angle small (no large accumulated angles in fp32).
 //
+// Sequence segments.  The state entering segment s of the sequence is
+//     H_in(s+1) = e^{sum ld over s} R(-sum theta over s) H_in(s) + H_loc(s),
+// where H_loc(s) is segment s walked from a zero state: the (decay, state) pair
+// composition of a linear recurrence.  A state-only pass computes H_loc, the
+// total log-decay and the total angle of every segment but the last; the full
+// pass then starts every segment from its combined entering state, so all
+// segments of a sequence run in parallel.
+//
 // Kernels
-//   k_scores  one workgroup per (batch, chunk, group-or-head): S = C~ B~^T on
-//             fp32 MFMA 16x16x4 from LDS-staged rows, written to the caller's
-//             workspace with a row stride padded to a multiple of 4.  Mamba-2
-//             shares S across the heads of a group and the walk applies each
-//             head's decay mask; for Mamba-3 (rotation per head) the trapezoid
-//             weights w are applied here and the walk reads w o S directly.
-//   k_walk    one workgroup (4 waves) per (batch, head, 16-column slice of P):
-//             walks the chunks in order with the N x 16 state slice held in
-//             MFMA accumulators.  Every wave loads the MFMA operands it needs
-//             (its 16 rows of w o S and of C~, its 32 state rows of B~) straight
-//             into registers one chunk ahead; only X, the weighted X, the state
-//             and the angles go through LDS (double-buffered by chunk parity,
-//             one barrier per chunk).  No chunk state is written to HBM.
+//   k_scores  (Mamba-2 only) one workgroup per (batch, chunk, group):
+//             S = C B^T on fp32 MFMA, shared by the heads of the group.
+//   k_walk    one workgroup (4 waves) per (batch, head, segment, 64 state
+//             columns), walking the segment's chunks in order.  Per chunk the
+//             workgroup stages B~ and C~ (rotated once, for all columns), X and
+//             the chunk-end-weighted X (transposed) and the masked score matrix
+//             in LDS; wave w owns state columns 16w..16w+15 for all N rows as
+//             MFMA accumulators.  For Mamba-3 the scores C~ B~^T are computed in
+//             the walk (they are per head).  The state rows are permuted inside
+//             the accumulator tiles so that the accumulators are directly the
+//             operand of the next chunk's C~ H product: the state never leaves
+//             registers.
 // All global reads go through buffer resources that cover one batch row of a
 // tensor, so reads before the first or after the last step return zero in
 // hardware and the hot loops carry no bounds branches.
@@ -47,10 +54,11 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef unsigned int uintx2 __attribute__((ext_vector_type(2)));
 typedef unsigned int uintx4 __attribute__((ext_vector_type(4)));
 
-constexpr int kRows = 64;    // rows per chunk (time steps x ranks)
-constexpr int kW = 16;       // state / output columns per walk workgroup
-constexpr int kNMax = 128;   // largest supported state size
+constexpr int kRows = 64;      // rows per chunk (time steps x ranks)
+constexpr int kPG = 64;        // state / output columns per walk workgroup
+constexpr int kNMax = 128;     // largest supported state size
 constexpr int kThreads = 256;
+constexpr int kTargetWG = 768; // segments are chosen to give about this many workgroups
 
 __device__ __forceinline__ floatx4 mfma4(float a, float b, floatx4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
@@ -66,6 +74,15 @@ __device__ __forceinline__ void sincos_rev(float phi, float* s, float* c) {
     r = r - rintf(r);
     *s = __builtin_amdgcn_sinf(r);
     *c = __builtin_amdgcn_cosf(r);
+}
+
+__device__ __forceinline__ float wave_incl_scan(float v, int lane) {
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        float o = __shfl_up(v, d, 64);
+        if (lane >= d) v += o;
+    }
+    return v;
 }
 
 // ---------------------------------------------------------------------------
@@ -109,15 +126,65 @@ __device__ __forceinline__ float4 bload4<bf16>(const Buf& b, int e) {
                        __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
 }
 
+
+// CNT contiguous elements starting at element e, widened to fp32.
+template <typename IO, int CNT>
+struct VecLoad;
+template <int CNT>
+struct VecLoad<float, CNT> {
+    static __device__ __forceinline__ void run(const Buf& b, int e, float* o) {
+        if constexpr (CNT == 1) {
+            o[0] = bload<float>(b, e);
+        } else if constexpr (CNT == 2) {
+            const uintx2 u = __builtin_amdgcn_raw_buffer_load_b64(b.r, e * 4, 0, 0);
+            o[0] = __uint_as_float(u.x);
+            o[1] = __uint_as_float(u.y);
+        } else {
+            static_assert(CNT % 4 == 0, "fp32 vector loads take 1, 2 or 4k elements");
+#pragma unroll
+            for (int q = 0; q < CNT; q += 4) {
+                const uintx4 u = __builtin_amdgcn_raw_buffer_load_b128(b.r, (e + q) * 4, 0, 0);
+                o[q] = __uint_as_float(u.x);
+                o[q + 1] = __uint_as_float(u.y);
+                o[q + 2] = __uint_as_float(u.z);
+                o[q + 3] = __uint_as_float(u.w);
+            }
+        }
+    }
+};
+template <int CNT>
+struct VecLoad<bf16, CNT> {
+    static __device__ __forceinline__ void run(const Buf& b, int e, float* o) {
+        if constexpr (CNT == 1) {
+            o[0] = bload<bf16>(b, e);
+        } else if constexpr (CNT == 2) {
+            const uint32_t u = __builtin_amdgcn_raw_buffer_load_b32(b.r, e * 2, 0, 0);
+            o[0] = __uint_as_float(u << 16);
+            o[1] = __uint_as_float(u & 0xffff0000u);
+        } else {
+            static_assert(CNT % 4 == 0, "bf16 vector loads take 1, 2 or 4k elements");
+#pragma unroll
+            for (int q = 0; q < CNT; q += 4) {
+                const uintx2 u = __builtin_amdgcn_raw_buffer_load_b64(b.r, (e + q) * 2, 0, 0);
+                o[q] = __uint_as_float(u.x << 16);
+                o[q + 1] = __uint_as_float(u.x & 0xffff0000u);
+                o[q + 2] = __uint_as_float(u.y << 16);
+                o[q + 3] = __uint_as_float(u.y & 0xffff0000u);
+            }
+        }
+    }
+};
+
 template <int R, bool TRAP>
 struct Geo {
-    static constexpr int QT = kRows / R;                 // time steps per chunk
-    static constexpr int EXTRA = TRAP ? R : 0;           // previous-step rows
-    static constexpr int KC = kRows + EXTRA;             // columns of S
-    static constexpr int KP = (KC + 3) / 4 * 4;          // padded to the MFMA K step (row stride of S)
-    static constexpr int KS = KP / 4;                    // MFMA K steps over the columns
-    static constexpr int KT = (KC + 15) / 16 * 16;       // padded to 16-wide tiles
-    static constexpr int QS = QT / 4;                    // steps per angle-prefix segment
+    static constexpr int QT = kRows / R;                  // time steps per chunk
+    static constexpr int QS = QT / 4;                     // steps per staging quarter
+    static constexpr int EXTRA = TRAP ? R : 0;            // previous-step rows j = 64 .. 64+EXTRA-1
+    static constexpr int JX = (EXTRA + 3) / 4;            // MFMA K steps over them
+    static constexpr int JC = kRows + 4 * JX;             // columns of X^T / M in use
+    static constexpr int JP = (JC % 8 == 0) ? JC + 4 : JC + 8;   // LDS row stride (4 mod 8)
+    static constexpr int BR = TRAP ? kRows + 16 : kRows;  // staged B~ rows (zero padded)
+    static constexpr int PR = (R + 3) / 4;                // previous-step ranks per staging thread
 };
 
 struct Args {
@@ -131,26 +198,12 @@ struct Args {
     const float* h0;
     void* Y;
     float* h_out;
-    float* S;        // workspace: scores (Mamba-2) or weighted scores (Mamba-3)
-    int L, H, P, G, N, nch;
+    float* S;        // Mamba-2 scores, (batch, chunk, group, 64, 64)
+    float* seg_h;    // local end states of segments 0..nseg-2, (batch, H, nseg-1, N, P)
+    float* seg_ld;   // their total log-decay, (batch, H, nseg-1)
+    float* seg_rev;  // their total angle per pair in revolutions mod 1, (batch, H, nseg-1, N/2)
+    int L, H, P, G, N, nch, nseg, cps, npg;
 };
-
-// Column j of a chunk's score matrix -> local time step s (-1 = previous step)
-// and rank r; false for padding columns.
-template <int R, bool TRAP>
-__device__ __forceinline__ bool col_of(int j, int* s, int* r) {
-    using G = Geo<R, TRAP>;
-    if (j >= G::KC) return false;
-    int jj = j - G::EXTRA;
-    if (jj < 0) {
-        *s = -1;
-        *r = jj + R;
-    } else {
-        *s = jj / R;
-        *r = jj % R;
-    }
-    return true;
-}
 
 // Per-batch-row views of the inputs.  B/C: element (step t, n, rank r) at
 //   t * bc_step + bc_head + n * R + r   with bc_step = G*N (grouped layout,
@@ -180,576 +233,690 @@ struct Views {
 };
 
 // ---------------------------------------------------------------------------
-// chunk-local rotation angles Phi[t][k] = sum_{u <= t} theta_u[k], t in [0, QT).
-// Thread (k = 16 * wave + lane / 4, seg = lane % 4) owns steps
-// [seg*QS, seg*QS + QS) of pair k: it prefix-sums them, takes the totals of the
-// earlier segments from its quad and writes complete prefixes.
+// Mamba-2 scores S = C B^T per (batch, chunk, group): 64 x 64, contraction over
+// the state.  Only the causal blocks (column block <= row block) are computed;
+// the walk never reads the others.
 // ---------------------------------------------------------------------------
-template <int QT, bool GROUPED_UNUSED = false>
-__device__ __forceinline__ void angles_load(const Buf& th, int K, int H, int h, int t0g, float* v) {
-    constexpr int QS = QT / 4;
-    const int lane = threadIdx.x % 64;
-    const int k = 16 * (threadIdx.x / 64) + lane / 4, seg = lane % 4;
-    const int kk = k < K ? k : 0;
-    const int base = ((t0g + seg * QS) * H + h) * K + kk;
-#pragma unroll
-    for (int i = 0; i < QS; ++i) {
-        float x = bload<float>(th, base + i * H * K);
-        v[i] = k < K ? x : 0.0f;
-    }
-}
-
-template <int QT>
-__device__ __forceinline__ void angles_store(const float* v, float* phi) {
-    constexpr int QS = QT / 4;
-    const int lane = threadIdx.x % 64;
-    const int k = 16 * (threadIdx.x / 64) + lane / 4, seg = lane % 4;
-    float acc[QS];
-    float run = 0.0f;
-#pragma unroll
-    for (int i = 0; i < QS; ++i) {
-        run += v[i];
-        acc[i] = run;
-    }
-    // exclusive prefix of the segment totals within the quad
-    const float t1 = __shfl_up(run, 1, 4);
-    const float s1 = seg >= 1 ? t1 : 0.0f;
-    const float incl1 = run + s1;                  // inclusive over 2
-    const float t2 = __shfl_up(incl1, 2, 4);
-    const float off = s1 + (seg >= 2 ? t2 : 0.0f);
-#pragma unroll
-    for (int i = 0; i < QS; ++i) phi[(seg * QS + i) * 64 + k] = acc[i] + off;
-}
-
-// ---------------------------------------------------------------------------
-// Stage B or C rows of local steps [first_s, first_s + NSTEPS) into
-// dst[((s - first_s) * R + r) * stride + n], rotated by the chunk-local angle of
-// step s (step -1 is never rotated), zero outside the sequence and for n >= N.
-// Work unit: U consecutive values of one step, holding whole rotation pairs
-// (n, n+1) for every rank.  All loads of a thread are issued before use.
-// ---------------------------------------------------------------------------
-template <int NP, int R, int NSTEPS, bool ROT, typename IO>
-__device__ __forceinline__ void stage_bc(const Buf& src, int bc_step, int bc_head, int N,
-                                         int t0g, int first_s, float* dst, int stride,
-                                         const float* phi) {
-    constexpr int U = (2 * R > 8) ? 2 * R : 8;
-    constexpr int UPS = NP * R / U;                  // units per step
-    constexpr int NU = NSTEPS * UPS;
-    constexpr int IT = (NU + kThreads - 1) / kThreads;
-    float v[IT][U];
-#pragma unroll
-    for (int it = 0; it < IT; ++it) {
-        const int u = threadIdx.x + it * kThreads;
-        const int uu = u < NU ? u : 0;
-        const int si = uu / UPS, f = (uu % UPS) * U;
-        const int e = (t0g + first_s + si) * bc_step + bc_head + f;
-        const bool okn = f / R < N && u < NU;
-#pragma unroll
-        for (int q = 0; q < U; q += 4) {
-            float4 w4 = bload4<IO>(src, e + q);
-            v[it][q] = okn ? w4.x : 0.0f;
-            v[it][q + 1] = okn ? w4.y : 0.0f;
-            v[it][q + 2] = okn ? w4.z : 0.0f;
-            v[it][q + 3] = okn ? w4.w : 0.0f;
-        }
-    }
-#pragma unroll
-    for (int it = 0; it < IT; ++it) {
-        const int u = threadIdx.x + it * kThreads;
-        if (u >= NU) continue;
-        const int si = u / UPS, f = (u % UPS) * U;
-        const int s = first_s + si;
-        if (ROT && s >= 0) {
-#pragma unroll
-            for (int q = 0; q < U; ++q) {
-                if (((q / R) & 1) == 0) {
-                    const int k = ((f + q) / R) >> 1;
-                    float sn, cs;
-                    sincos_rev(phi[s * 64 + k], &sn, &cs);
-                    const float v0 = v[it][q], v1 = v[it][q + R];
-                    v[it][q] = fmaf(-sn, v1, cs * v0);
-                    v[it][q + R] = fmaf(sn, v0, cs * v1);
-                }
-            }
-        }
-#pragma unroll
-        for (int q = 0; q < U; ++q) {
-            const int flat = f + q;
-            dst[(si * R + flat % R) * stride + flat / R] = v[it][q];
-        }
-    }
-}
-
-__device__ __forceinline__ float wave_incl_scan(float v, int lane) {
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        float o = __shfl_up(v, d, 64);
-        if (lane >= d) v += o;
-    }
-    return v;
-}
-
-// ---------------------------------------------------------------------------
-// Scores per (batch, chunk, group-or-head)
-// ---------------------------------------------------------------------------
-template <int NP, int R, bool TRAP, bool ROT, bool GROUPED, typename IO>
+template <int NP, typename IO>
 __global__ __launch_bounds__(kThreads) void k_scores(Args a) {
-    using Gm = Geo<R, TRAP>;
-    constexpr int QT = Gm::QT;
-    constexpr int SB = NP + 2;    // LDS row stride (= 2 mod 4: conflict-free MFMA reads)
-    __shared__ float sC[kRows * SB];
-    __shared__ float sB[Gm::KT * SB];
-    __shared__ float sPhi[ROT ? QT * 64 : 1];
-    __shared__ float s_cum[QT + 1];
-    __shared__ float s_gam[QT];
-    __shared__ float s_bet[QT + 1];
-
-    const int c = blockIdx.x, hs = blockIdx.y, b = blockIdx.z;
-    const int hg = (GROUPED && TRAP) ? hs / (a.H / a.G) : hs;
-    const int t0g = c * QT;
+    constexpr int SB = NP + 4;
+    constexpr int NQ = NP / 4;
+    __shared__ __attribute__((aligned(16))) float sC[kRows * SB];
+    __shared__ __attribute__((aligned(16))) float sB[kRows * SB];
+    const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    const int t0g = c * kRows;
     const int tid = threadIdx.x, lane = tid % 64;
-    const int wave = __builtin_amdgcn_readfirstlane(tid / 64);   // uniform per wave
-    const Views<R, GROUPED, IO> vw(a, b, hs, hg);
-    if (ROT) {
-        float th[Gm::QS];
-        angles_load<QT>(vw.th, a.N / 2, a.H, hs, t0g, th);
-        angles_store<QT>(th, sPhi);
-    }
-    if (TRAP && wave == 0) {
-        const int o = (t0g + lane) * a.H + hs;
-        const bool in = lane < QT;
-        const float ldv = in ? bload<float>(vw.ld, o) : 0.0f;
-        const float cum = wave_incl_scan(ldv, lane);
-        if (in) {
-            s_cum[lane + 1] = cum;
-            s_gam[lane] = bload<float>(vw.gam, o);
-            s_bet[lane] = bload<float>(vw.bet, o);
-        }
-        if (lane == 0) {
-            s_cum[0] = 0.0f;
-            s_bet[QT] = 0.0f;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
+    const Views<1, true, IO> vw(a, b, 0, g);
+    {
+        const int row = tid / 4, q = tid % 4;
+        float vb[NQ], vc[NQ];
+        const int e = (t0g + row) * vw.bc_step + vw.bc_head + q * NQ;
+        VecLoad<IO, NQ>::run(vw.B, e, vb);
+        VecLoad<IO, NQ>::run(vw.C, e, vc);
+#pragma unroll
+        for (int i = 0; i < NQ; i += 4) {
+            const bool ok = q * NQ + i < a.N;   // N is a multiple of 4
+            float4 fb = ok ? make_float4(vb[i], vb[i + 1], vb[i + 2], vb[i + 3]) : make_float4(0, 0, 0, 0);
+            float4 fc = ok ? make_float4(vc[i], vc[i + 1], vc[i + 2], vc[i + 3]) : make_float4(0, 0, 0, 0);
+            *(float4*)&sB[row * SB + q * NQ + i] = fb;
+            *(float4*)&sC[row * SB + q * NQ + i] = fc;
         }
     }
-    for (int e = tid; e < (Gm::KT - Gm::KC) * NP; e += kThreads)
-        sB[(Gm::KC + e / NP) * SB + e % NP] = 0.0f;
     __syncthreads();
-    stage_bc<NP, R, QT, ROT, IO>(vw.C, vw.bc_step, vw.bc_head, a.N, t0g, 0, sC, SB, sPhi);
-    stage_bc<NP, R, QT + (TRAP ? 1 : 0), ROT, IO>(vw.B, vw.bc_step, vw.bc_head, a.N, t0g,
-                                                   TRAP ? -1 : 0, sB, SB, sPhi);
-    __syncthreads();
-
     const int li = lane % 16, lk = lane / 16;
-    constexpr int CT = Gm::KT / 16;
-    float* Sout = a.S + (((size_t)b * a.nch + c) * gridDim.y + hs) * (size_t)(kRows * Gm::KP);
-    for (int tile = wave; tile < 4 * CT; tile += 4) {
-        const int rt = tile / CT, ct = tile % CT;
+    float* Sout = a.S + (((size_t)b * a.nch + c) * a.G + g) * (size_t)(kRows * kRows);
+    const int it = wave;
+    for (int jt = 0; jt <= it; ++jt) {
         floatx4 acc0 = {0.0f, 0.0f, 0.0f, 0.0f}, acc1 = {0.0f, 0.0f, 0.0f, 0.0f};
-        const float* pa = sC + (rt * 16 + li) * SB + lk;
-        const float* pb = sB + (ct * 16 + li) * SB + lk;
+        const float* pa = sC + (16 * it + li) * SB + NQ * lk;
+        const float* pb = sB + (16 * jt + li) * SB + NQ * lk;
 #pragma unroll
-        for (int n = 0; n < NP; n += 8) {
-            acc0 = mfma4(pa[n], pb[n], acc0);
-            acc1 = mfma4(pa[n + 4], pb[n + 4], acc1);
+        for (int q = 0; q < NQ; q += 4) {
+            const float4 av = *(const float4*)(pa + q);
+            const float4 bv = *(const float4*)(pb + q);
+            acc0 = mfma4(av.x, bv.x, acc0);
+            acc1 = mfma4(av.y, bv.y, acc1);
+            acc0 = mfma4(av.z, bv.z, acc0);
+            acc1 = mfma4(av.w, bv.w, acc1);
         }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int i = rt * 16 + lk * 4 + r, j = ct * 16 + li;
-            if (j >= Gm::KP) continue;
-            float v = 0.0f;
-            int s, rk;
-            if (col_of<R, TRAP>(j, &s, &rk)) {
-                v = acc0[r] + acc1[r];
-                if (TRAP) {
-                    const int tau = i / R;
-                    float w = 0.0f;
-                    if (s <= tau) {
-                        if (s >= 0) w = s_gam[s] * exp_e(s_cum[tau + 1] - s_cum[s + 1]);
-                        if (s < tau) w += s_bet[s + 1] * exp_e(s_cum[tau + 1] - s_cum[s + 2]);
-                    }
-                    v *= w;
-                }
-            }
-            Sout[i * Gm::KP + j] = v;
-        }
+        for (int r = 0; r < 4; ++r)
+            Sout[(16 * it + 4 * lk + r) * kRows + 16 * jt + li] = acc0[r] + acc1[r];
     }
 }
 
 // ---------------------------------------------------------------------------
-// Chunk walk
+// Chunk walk.  SO = state only (the segment pre-pass).
+//
+// State layout: wave w holds columns p = p0 + 16w + li of all NP state rows in
+// NT = NP/16 accumulator tiles; tile t, register r of lane (li, lk) is row
+//     n(t, r) = 64 (t / 4) + 16 lk + 4 r + t % 4,
+// i.e. lane group lk owns rows {16 lk .. 16 lk + 15} (+64).  Read as the A
+// operand of Y^T = H^T C~^T this is a K-slice of 16 (or 32) consecutive rows per
+// lane group, matching contiguous 16-byte reads of C~; rotation pairs (2k, 2k+1)
+// sit in tiles (t, t+1) of the same lane.
 // ---------------------------------------------------------------------------
-// Uniform part of the element offset of B row j = 4s + lk (lk < 4): the step of
-// row j, relative to the chunk's first step, times the step stride, plus the
-// rank where it does not depend on lk.
-template <int R, bool TRAP>
-__device__ __forceinline__ int brow_uniform(int s, int step) {
-    if (R == 1) return 4 * s * step;
-    if (R == 2) return 2 * s * step;
-    return (4 * s / R) * step + (4 * s) % R;
-}
-// Lane part of the same offset (everything that depends on lk and n).
-template <int R, bool TRAP>
-__device__ __forceinline__ int brow_lane(int lk, int n, int step, int head) {
-    constexpr int E = TRAP ? 1 : 0;   // previous-step rows are one step back
-    if (R == 1) return (lk - E) * step + head + n;
-    if (R == 2) return (lk / 2 - E) * step + head + 2 * n + lk % 2;
-    return -E * step + head + n * R + lk;
+template <int NP>
+__device__ __forceinline__ int state_row(int t, int r, int lk) {
+    return 64 * (t / 4) + 16 * lk + 4 * r + (t % 4);
 }
 
-template <int NP, int R, bool TRAP>
-struct WalkRegs {
-    static constexpr int KS = Geo<R, TRAP>::KS;
-    float m[KS];        // row 16w+li of (w o) S, columns 4s + lk
-    float bb[2][KS];    // B rows 4s + lk, state row n = 32w + 16tt + li
-    float cc[NP / 4];   // C row 16w + li, n = lk * NP/4 + s
-};
+// Score tiles (row block, column block) of the trapezoid per wave; column
+// block 4 holds the previous-step columns.  -1 ends a list.
+__constant__ int kTrapTiles[4][4] = {{0x30, 0x31, 0x32, 0x33},
+                                     {0x20, 0x21, 0x22, 0x00},
+                                     {0x10, 0x11, 0x34, -1},
+                                     {0x24, 0x14, 0x04, -1}};
 
-template <int NP, int R, bool TRAP, bool ROT, bool GROUPED, typename IO, bool FULLN>
+template <int NP, int R, bool TRAP, bool ROT, bool GROUPED, typename IO, bool SO>
 __global__ __launch_bounds__(kThreads) void k_walk(Args a) {
     using Gm = Geo<R, TRAP>;
-    constexpr int QT = Gm::QT;
-    constexpr int KP = Gm::KP;
-    constexpr int KS = Gm::KS;
-    constexpr int NQ = NP / 4;                    // state rows per lane quarter in C~ H
-    constexpr int SHP = NP * kW + 4 * kW;         // state slice + a 16-float skew per quarter
-    constexpr int XU = KP * 4;                    // float4 units of the staged X block
-    constexpr int XR = (XU + kThreads - 1) / kThreads;
+    constexpr int QT = Gm::QT, QS = Gm::QS, EXTRA = Gm::EXTRA, JX = Gm::JX;
+    constexpr int JC = Gm::JC, JP = Gm::JP, PR = Gm::PR;
+    constexpr int BS = NP + 4;     // LDS row stride of B~ / C~ (4 mod 32 floats)
+    constexpr int NT = NP / 16;    // state tiles per wave
+    constexpr int NH = NT / 4;     // halves of 64 rows
+    constexpr int KQ = NP / 4;     // contraction slice over the state per lane group (scores)
+    constexpr bool FULL = !SO;
 
-    __shared__ float sX[2][KP * kW];
-    __shared__ float sXd[2][KP * kW];
-    __shared__ float sH[2][SHP];
-    __shared__ float sPhi[2][ROT ? QT * 64 : 1];
-    __shared__ float s_cum[2][QT + 1];
+    __shared__ __attribute__((aligned(16))) float sB[Gm::BR * BS];
+    __shared__ __attribute__((aligned(16))) float sC[FULL ? kRows * BS : 4];
+    __shared__ __attribute__((aligned(16))) float sXT[FULL ? kPG * JP : 4];
+    __shared__ __attribute__((aligned(16))) float sXdT[kPG * JP];
+    __shared__ __attribute__((aligned(16))) float sM[FULL ? kRows * JP : 4];
+    __shared__ float s_cum[QT + 1];
+    __shared__ float s_gam[TRAP ? QT : 1];
+    __shared__ float s_bet[TRAP ? QT + 1 : 1];
+    __shared__ float s_dc[ROT ? NP / 2 : 1];
+    __shared__ float s_ds[ROT ? NP / 2 : 1];
 
-    const int p0 = blockIdx.x * kW, h = blockIdx.y, b = blockIdx.z;
+    // ---- workgroup -> (batch, segment, head, column group) ------------------
+    // Workgroups of one (batch, segment) share B and C; ids i, i+8, i+16, ... run
+    // on one XCD, so they are given the heads of one (batch, segment).
+    const int nsegL = SO ? a.nseg - 1 : a.nseg;
+    const int gsize = a.H * a.npg;
+    const int ngroups = (int)(gridDim.x / gsize);
+    const int id = blockIdx.x;
+    const int full = ngroups / 8 * 8 * gsize;
+    int grp, wi;
+    if (id < full) {
+        const int x = id % 8, k = id / 8;
+        grp = x + 8 * (k / gsize);
+        wi = k % gsize;
+    } else {
+        grp = id / gsize;
+        wi = id % gsize;
+    }
+    const int b = grp / nsegL, seg = grp % nsegL;
+    const int h = wi / a.npg, pg = wi % a.npg;
     const int hg = GROUPED ? h / (a.H / a.G) : h;
-    const int hs = TRAP ? h : hg;
-    const int nS = TRAP ? a.H : a.G;
+    const int p0 = pg * kPG;
+    const int c_begin = seg * a.cps;
+    const int c_end = min(a.nch, c_begin + a.cps);
+
     const int tid = threadIdx.x, lane = tid % 64;
-    const int wave = __builtin_amdgcn_readfirstlane(tid / 64);   // uniform per wave
+    const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
     const int li = lane % 16, lk = lane / 16;
-    const size_t sh_off = (size_t)(b * a.H + h) * a.N * a.P;
+    const int pw_n = (min(kPG, a.P - p0)) / 16;
+    const bool active = wave < pw_n;   // uniform
+    const int pcol = p0 + 16 * wave + li;
     const Views<R, GROUPED, IO> vw(a, b, h, hg);
-    constexpr bool fullN = FULLN;   // N == NP: no state rows to mask
+    const size_t sh_off = (size_t)(b * a.H + h) * a.N * a.P;
 
-    auto hidx = [](int n, int p) { return n * kW + p + (n / NQ) * kW; };
+    // staging roles: (sk, ssg) = rotation pair and step quarter for B / C /
+    // angles; (xpl, xtq) = state column and step quarter for X
+    const int sk = tid / 4, ssg = tid % 4;
+    const bool k_in = sk < NP / 2;
+    const bool k_ok = k_in && 2 * sk < a.N;
+    const int xpl = tid % 64, xtq = tid / 64;
+    const bool x_ok = p0 + xpl < a.P;
+    const int si = tid / 4, sq = tid % 4;   // Mamba-2 score staging: row, column quarter
 
-    // ---- lane constants of the operand loads ----------------------------------
-    // S (or w o S): row 16w + li, column 4s + lk of chunk c's block
-    const Buf Sbuf = make_buf(a.S + ((size_t)b * a.nch * nS + hs) * (size_t)(kRows * KP),
-                              (size_t)a.nch * nS * kRows * KP * 4);
-    const int s_lane = (16 * wave + li) * KP + lk;
-    const int s_chunk = nS * kRows * KP;
-    // B: two state rows per lane
-    int b_lane[2];
-    bool b_ok[2];
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-        const int n = 32 * wave + 16 * tt + li;
-        b_ok[tt] = n < a.N;
-        b_lane[tt] = brow_lane<R, TRAP>(lk, b_ok[tt] ? n : 0, vw.bc_step, vw.bc_head);
+    // ---- one-time zero fill of padding that staging never writes ------------
+    if constexpr (TRAP) {
+        for (int e = tid; e < (Gm::BR - kRows - EXTRA) * BS; e += kThreads)
+            sB[(kRows + EXTRA) * BS + e] = 0.0f;
     }
-    // C: row i = 16w + li (step i / R, rank i % R), state rows lk*NQ + s
-    const int c_row = 16 * wave + li;
-    const int c_lane = (c_row / R) * vw.bc_step + vw.bc_head + lk * NQ * R + c_row % R;
-    const int c_nlim = a.N - lk * NQ;    // valid s < c_nlim
-
-    // (w o) S rows and B~ columns of chunk c
-    auto load_mb = [&](int c, WalkRegs<NP, R, TRAP>& o) {
-        const int t0g = c * QT;
-        const int sb = c * s_chunk + s_lane;
-#pragma unroll
-        for (int s = 0; s < KS; ++s) o.m[s] = bload<float>(Sbuf, sb + 4 * s);
-        const int cb = t0g * vw.bc_step;
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-#pragma unroll
-            for (int s = 0; s < KS; ++s)
-                o.bb[tt][s] = bload<IO>(vw.B, cb + b_lane[tt] + brow_uniform<R, TRAP>(s, vw.bc_step));
+    if constexpr (JC > kRows + EXTRA) {
+        constexpr int PADC = JC > kRows + EXTRA ? JC - kRows - EXTRA : 1;
+        for (int e = tid; e < kPG * PADC; e += kThreads) {
+            const int row = e / PADC, col = kRows + EXTRA + e % PADC;
+            if constexpr (FULL) sXT[row * JP + col] = 0.0f;
+            sXdT[row * JP + col] = 0.0f;
         }
-        if (!fullN) {   // state rows past N (uniform, small N only)
+    }
+
+    // ---- prefetch registers -------------------------------------------------
+    struct Pre {
+        float b[QS][2 * R];          // B pair (2sk, 2sk+1) x ranks, steps ssg*QS + i
+        float bp[2 * PR];            // previous step, ranks ssg*PR + q
+        float c[FULL ? QS : 1][2 * R];
+        float th[ROT ? QS : 1];
+        float x[QS][R];              // X column p0 + xpl, steps xtq*QS + i
+        float xp[PR];                // previous step, ranks xtq*PR + q
+        float sc[(FULL && !TRAP) ? 16 : 1];   // Mamba-2 score row si, columns 16 sq ..
+        float ld, gam, bet;          // step lane of the chunk
+    };
+    const Buf Sbuf = (FULL && !TRAP)
+        ? make_buf(a.S + (size_t)b * a.nch * a.G * (kRows * kRows), (size_t)a.nch * a.G * kRows * kRows * 4)
+        : make_buf(a.ld, 0);
+
+    auto prefetch = [&](int c, Pre& p) {
+        const int t0g = c * QT;
+        if (k_ok) {
 #pragma unroll
-            for (int tt = 0; tt < 2; ++tt)
+            for (int i = 0; i < QS; ++i) {
+                const int e = (t0g + ssg * QS + i) * vw.bc_step + vw.bc_head + 2 * sk * R;
+                VecLoad<IO, 2 * R>::run(vw.B, e, p.b[i]);
+                if constexpr (FULL) VecLoad<IO, 2 * R>::run(vw.C, e, p.c[i]);
+            }
+            if constexpr (TRAP) if (ssg * PR < R) {
+                const int e = (t0g - 1) * vw.bc_step + vw.bc_head + 2 * sk * R + ssg * PR;
+                VecLoad<IO, PR>::run(vw.B, e, p.bp);
+                VecLoad<IO, PR>::run(vw.B, e + R, p.bp + PR);
+            }
+            if constexpr (ROT) {
 #pragma unroll
-                for (int s = 0; s < KS; ++s) o.bb[tt][s] = b_ok[tt] ? o.bb[tt][s] : 0.0f;
+                for (int i = 0; i < QS; ++i)
+                    p.th[i] = bload<float>(vw.th, ((t0g + ssg * QS + i) * a.H + h) * (a.N / 2) + sk);
+            }
+        }
+        if (x_ok) {
+#pragma unroll
+            for (int i = 0; i < QS; ++i)
+                VecLoad<IO, R>::run(vw.X, (t0g + xtq * QS + i) * vw.x_step + vw.x_head + (p0 + xpl) * R,
+                                    p.x[i]);
+            if constexpr (TRAP) if (xtq * PR < R)
+                VecLoad<IO, PR>::run(vw.X, (t0g - 1) * vw.x_step + vw.x_head + (p0 + xpl) * R + xtq * PR,
+                                     p.xp);
+        }
+        if constexpr (FULL && !TRAP) if (16 * sq <= si) {
+            const int e = (c * a.G + hg) * (kRows * kRows) + si * kRows + 16 * sq;
+            VecLoad<float, 16>::run(Sbuf, e, p.sc);
+        }
+        const int o = (t0g + lane) * a.H + h;
+        p.ld = lane < QT ? bload<float>(vw.ld, o) : 0.0f;
+        if constexpr (TRAP) {
+            p.gam = lane < QT ? bload<float>(vw.gam, o) : 0.0f;
+            p.bet = lane < QT ? bload<float>(vw.bet, o) : 0.0f;
         }
     };
-    // C~ row of chunk c
-    auto load_c = [&](int c, WalkRegs<NP, R, TRAP>& o) {
-        const int cb = c * QT * vw.bc_step;
-        if (R == 1) {
-#pragma unroll
-            for (int s = 0; s < NQ; s += 4) {
-                const float4 w4 = bload4<IO>(vw.C, cb + c_lane + s);
-                o.cc[s] = w4.x;
-                o.cc[s + 1] = w4.y;
-                o.cc[s + 2] = w4.z;
-                o.cc[s + 3] = w4.w;
-            }
+
+    float seg_acc = 0.0f;   // SO: total log-decay of the segment
+    float rev_acc = 0.0f;   // SO: total angle of pair sk (threads ssg == 3), revolutions mod 1
+    float cum_last = 0.0f;
+
+    // ---- staging of one chunk from the prefetch registers into LDS ----------
+    auto stage = [&](const Pre& p) {
+        const float cum = wave_incl_scan(p.ld, lane);   // lanes >= QT add zero
+        cum_last = __shfl(cum, QT - 1, 64);
+        const float cum_n = __shfl_down(cum, 1, 64);
+        float wl, wprev = 0.0f;   // chunk-end weights of step `lane` and of the previous step
+        if constexpr (TRAP) {
+            const float bet_n = __shfl_down(p.bet, 1, 64);
+            wl = p.gam * exp_e(cum_last - cum) + (lane + 1 < QT ? bet_n * exp_e(cum_last - cum_n) : 0.0f);
+            wprev = __shfl(p.bet, 0, 64) * exp_e(cum_last - __shfl(cum, 0, 64));
         } else {
-#pragma unroll
-            for (int s = 0; s < NQ; ++s) o.cc[s] = bload<IO>(vw.C, cb + c_lane + s * R);
+            wl = exp_e(cum_last - cum);
         }
-        if (!fullN) {
-#pragma unroll
-            for (int s = 0; s < NQ; ++s) o.cc[s] = s < c_nlim ? o.cc[s] : 0.0f;
-        }
-    };
-
-    // ---- X block, step scalars and angles of chunk c -> LDS buffer c & 1 ------
-    float4 xr[XR];
-    float th[ROT ? Gm::QS : 1];
-    float sc_ld, sc_gam, sc_bet;
-    auto load_stage = [&](int c) {
-        const int t0g = c * QT;
-#pragma unroll
-        for (int q = 0; q < XR; ++q) {
-            const int u = tid + q * kThreads;
-            const int si = u / (4 * R), f = (u % (4 * R)) * 4;
-            const int s = si - (TRAP ? 1 : 0);
-            const int j0 = Gm::EXTRA + s * R;
-            float4 v = bload4<IO>(vw.X, (t0g + s) * vw.x_step + vw.x_head + p0 * R + f);
-            const bool ok = u < XU && j0 + R <= Gm::KC;
-            xr[q] = ok ? v : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-        }
-        if (ROT) angles_load<QT>(vw.th, a.N / 2, a.H, h, t0g, th);
-        const bool in = lane < QT && t0g + lane < a.L;
-        const size_t o = ((size_t)b * a.L + (in ? t0g + lane : 0)) * a.H + h;
-        sc_ld = in ? a.ld[o] : 0.0f;
-        sc_gam = (TRAP && in) ? a.gamma[o] : 0.0f;
-        sc_bet = (TRAP && in) ? a.beta[o] : 0.0f;
-    };
-    auto store_stage = [&](int c) {
-        const int buf = c & 1;
-        const float cum = wave_incl_scan(sc_ld, lane);
-        const float cum_last = __shfl(cum, QT - 1, 64);
-        const float e = exp_e(cum_last - cum);
-        const float wg = TRAP ? sc_gam * e : e;
-        const float wb = TRAP ? sc_bet * e : 0.0f;
         if (wave == 0) {
-            if (lane < QT) s_cum[buf][lane + 1] = cum;
-            if (lane == 0) s_cum[buf][0] = 0.0f;
+            if (lane < QT) {
+                s_cum[lane + 1] = cum;
+                if constexpr (TRAP) {
+                    s_gam[lane] = p.gam;
+                    s_bet[lane] = p.bet;
+                }
+            }
+            if (lane == 0) {
+                s_cum[0] = 0.0f;
+                if constexpr (TRAP) s_bet[QT] = 0.0f;
+            }
         }
+        // angles: prefix over this thread's QS steps, then over the quad
+        float phi[ROT ? QS : 1];
+        if constexpr (ROT) {
+            float run = 0.0f;
 #pragma unroll
-        for (int q = 0; q < XR; ++q) {
-            const int u = tid + q * kThreads;
-            const int si = u / (4 * R), f = (u % (4 * R)) * 4;
-            const int s = si - (TRAP ? 1 : 0);
-            // weight of step s in the chunk-end state
-            const float w_g = __shfl(wg, s < 0 ? 0 : (s < 64 ? s : 63), 64);
-            const float w_b = __shfl(wb, s + 1 < 64 ? s + 1 : 63, 64);
-            const float w = (s >= 0 ? w_g : 0.0f) + (s + 1 < QT ? w_b : 0.0f);
-            if (u < XU) {
-                const float vv[4] = {xr[q].x, xr[q].y, xr[q].z, xr[q].w};
+            for (int i = 0; i < QS; ++i) {
+                run += k_ok ? p.th[i] : 0.0f;
+                phi[i] = run;
+            }
+            const float t1 = __shfl_up(run, 1, 4);
+            const float s1 = ssg >= 1 ? t1 : 0.0f;
+            const float t2 = __shfl_up(run + s1, 2, 4);
+            const float off = s1 + (ssg >= 2 ? t2 : 0.0f);
 #pragma unroll
-                for (int e4 = 0; e4 < 4; ++e4) {
-                    const int flat = f + e4;               // (p, r) with r innermost
-                    const int j = Gm::EXTRA + s * R + flat % R;
-                    const int p = flat / R;
-                    if (j < KP) {
-                        sX[buf][j * kW + p] = vv[e4];
-                        sXd[buf][j * kW + p] = vv[e4] * w;
+            for (int i = 0; i < QS; ++i) phi[i] += off;
+            if (ssg == 3 && k_in) {
+                float sn, cs;
+                sincos_rev(phi[QS - 1], &sn, &cs);
+                s_dc[sk] = k_ok ? cs : 1.0f;
+                s_ds[sk] = k_ok ? sn : 0.0f;
+                if constexpr (SO) {
+                    rev_acc += phi[QS - 1] * 0.15915494309189535f;
+                    rev_acc -= rintf(rev_acc);
+                }
+            }
+        }
+        // B~, C~ rows (t R + r), columns (2 sk, 2 sk + 1)
+        if (k_in) {
+#pragma unroll
+            for (int i = 0; i < QS; ++i) {
+                const int t = ssg * QS + i;
+                float cs = 1.0f, sn = 0.0f;
+                if constexpr (ROT) sincos_rev(phi[i], &sn, &cs);
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    const float b0 = p.b[i][r], b1 = p.b[i][R + r];
+                    float2 vb = make_float2(fmaf(-sn, b1, cs * b0), fmaf(sn, b0, cs * b1));
+                    if (!k_ok) vb = make_float2(0.0f, 0.0f);
+                    *(float2*)&sB[(t * R + r) * BS + 2 * sk] = vb;
+                    if constexpr (FULL) {
+                        const float c0 = p.c[i][r], c1 = p.c[i][R + r];
+                        float2 vc = make_float2(fmaf(-sn, c1, cs * c0), fmaf(sn, c0, cs * c1));
+                        if (!k_ok) vc = make_float2(0.0f, 0.0f);
+                        *(float2*)&sC[(t * R + r) * BS + 2 * sk] = vc;
+                    }
+                }
+            }
+            if constexpr (TRAP) if (ssg * PR < R) {
+#pragma unroll
+                for (int q = 0; q < PR; ++q) {
+                    const int r = ssg * PR + q;
+                    if (r < R) {
+                        float2 vb = make_float2(p.bp[q], p.bp[PR + q]);
+                        if (!k_ok) vb = make_float2(0.0f, 0.0f);
+                        *(float2*)&sB[(kRows + r) * BS + 2 * sk] = vb;
                     }
                 }
             }
         }
-        if (ROT) angles_store<QT>(th, sPhi[buf]);
+        // X^T and the chunk-end-weighted X^T: rows xpl, columns (t R + r)
+        {
+            float xv[QS * R], xd[QS * R];
+#pragma unroll
+            for (int i = 0; i < QS; ++i) {
+                const float w = __shfl(wl, xtq * QS + i, 64);
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    const float v = x_ok ? p.x[i][r] : 0.0f;
+                    xv[i * R + r] = v;
+                    xd[i * R + r] = v * w;
+                }
+            }
+            const int j0 = xtq * QS * R;   // = 16 xtq
+#pragma unroll
+            for (int q = 0; q < QS * R; q += 4) {
+                if constexpr (FULL) *(float4*)&sXT[xpl * JP + j0 + q] = make_float4(xv[q], xv[q + 1], xv[q + 2], xv[q + 3]);
+                *(float4*)&sXdT[xpl * JP + j0 + q] = make_float4(xd[q], xd[q + 1], xd[q + 2], xd[q + 3]);
+            }
+            if constexpr (TRAP) if (xtq * PR < R) {
+#pragma unroll
+                for (int q = 0; q < PR; ++q) {
+                    const int r = xtq * PR + q;
+                    if (r < R) {
+                        const float v = x_ok ? p.xp[q] : 0.0f;
+                        if constexpr (FULL) sXT[xpl * JP + kRows + r] = v;
+                        sXdT[xpl * JP + kRows + r] = v * wprev;
+                    }
+                }
+            }
+        }
+        // Mamba-2: masked scores M[i][j] = S[i][j] e^{cum_i - cum_j}, j <= i
+        if constexpr (FULL && !TRAP) {
+            const float cum_i = __shfl(cum, si, 64);
+            float mv[16];
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                const int j = 16 * sq + q;
+                const float cum_j = __shfl(cum, j, 64);
+                const bool ok = j <= si;
+                const float e = exp_e(ok ? cum_i - cum_j : 0.0f);
+                mv[q] = ok ? p.sc[q] * e : 0.0f;
+            }
+#pragma unroll
+            for (int q = 0; q < 16; q += 4)
+                *(float4*)&sM[si * JP + 16 * sq + q] = make_float4(mv[q], mv[q + 1], mv[q + 2], mv[q + 3]);
+        }
     };
 
-    // ---- state ------------------------------------------------------------
-    floatx4 acc_h[2];
+    // ---- state ----------------------------------------------------------------
+    floatx4 acc_h[NT];
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
+    for (int t = 0; t < NT; ++t) acc_h[t] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+    if constexpr (FULL) if (active) {
+        if (a.h0) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int n = 32 * wave + 16 * tt + 4 * lk + r;
-            acc_h[tt][r] = (a.h0 && n < a.N) ? a.h0[sh_off + (size_t)n * a.P + p0 + li] : 0.0f;
+            for (int t = 0; t < NT; ++t)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int n = state_row<NP>(t, r, lk);
+                    acc_h[t][r] = n < a.N ? a.h0[sh_off + (size_t)n * a.P + pcol] : 0.0f;
+                }
         }
-    for (int e = tid; e < NP * kW; e += kThreads) {
-        const int n = e / kW, p = e % kW;
-        sH[0][hidx(n, p)] = (a.h0 && n < a.N) ? a.h0[sh_off + (size_t)n * a.P + p0 + p] : 0.0f;
+        // entering state of this segment: compose the earlier segments
+        for (int s2 = 0; s2 < seg; ++s2) {
+            const size_t u = (size_t)(b * a.H + h) * (a.nseg - 1) + s2;
+            const float d = exp_e(a.seg_ld[u]);
+            if constexpr (ROT) {
+#pragma unroll
+                for (int t = 0; t < NT; t += 2)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int n = state_row<NP>(t, r, lk);
+                        const float rev = n < a.N ? a.seg_rev[u * (a.N / 2) + n / 2] : 0.0f;
+                        const float sn = __builtin_amdgcn_sinf(rev), cs = __builtin_amdgcn_cosf(rev);
+                        const float v0 = acc_h[t][r], v1 = acc_h[t + 1][r];
+                        acc_h[t][r] = fmaf(sn, v1, cs * v0);
+                        acc_h[t + 1][r] = fmaf(-sn, v0, cs * v1);
+                    }
+            }
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int n = state_row<NP>(t, r, lk);
+                    const float hl = n < a.N ? a.seg_h[(u * a.N + n) * a.P + pcol] : 0.0f;
+                    acc_h[t][r] = fmaf(d, acc_h[t][r], hl);
+                }
+        }
     }
 
-    WalkRegs<NP, R, TRAP> cur;
-    load_mb(0, cur);
-    load_c(0, cur);
-    load_stage(0);
-    store_stage(0);
+    Pre pre;
+    if (c_begin < c_end) prefetch(c_begin, pre);
 
-    for (int c = 0; c < a.nch; ++c) {
-        const int buf = c & 1;
+    for (int c = c_begin; c < c_end; ++c) {
         const int t0g = c * QT;
+        __syncthreads();                 // the previous chunk's LDS reads are done
+        stage(pre);
+        if (c + 1 < c_end) prefetch(c + 1, pre);
         __syncthreads();
-        const bool more = c + 1 < a.nch;
-        if (more) load_stage(c + 1);
-        const float* phi = sPhi[buf];
-        const float cum_last = s_cum[buf][QT];
-        const float tot = exp_e(cum_last);
+        if constexpr (SO) seg_acc += cum_last;
 
-        // ---- Y_intra = (w o S) X and H' = e^{cum_last} H + B~^T (w_end o X) ---------
-        floatx4 acc_y = {0.0f, 0.0f, 0.0f, 0.0f};
-        floatx4 hacc0 = acc_h[0] * tot, hacc1 = acc_h[1] * tot;
-        {
-            const int tau_row = (16 * wave + li) / R;      // this lane's row, for the Mamba-2 mask
-            const float cum_row = s_cum[buf][tau_row + 1];
-            const int kend = Gm::EXTRA + ((16 * wave + 15) / R + 1) * R;
-            const float* px = sX[buf] + lk * kW + li;
-            const float* pxd = sXd[buf] + lk * kW + li;
+        floatx4 acc_y[4];
+        if constexpr (FULL) {
+            // ---- Mamba-3: weighted scores M = w o (C~ B~^T) -> LDS ---------------
+            if constexpr (TRAP) {
 #pragma unroll
-            for (int s = 0; s < KS; ++s) {
-                if (4 * s < kend) {
-                    float av = cur.m[s];
-                    if (!TRAP) {
-                        // R == 1: column j is step j; causal decay mask, branch-free
-                        const int j = 4 * s + lk;
-                        const float dec = exp_e(fminf(cum_row - s_cum[buf][j + 1], 0.0f));
-                        av = (j <= tau_row) ? av * dec : 0.0f;
+                for (int q = 0; q < 4; ++q) {
+                    const int code = kTrapTiles[wave][q];
+                    if (code < 0) break;
+                    const int it = code >> 4, jt = code & 15;
+                    floatx4 s0 = {0.0f, 0.0f, 0.0f, 0.0f}, s1 = {0.0f, 0.0f, 0.0f, 0.0f};
+                    const float* pa = sC + (16 * it + li) * BS + KQ * lk;
+                    const float* pb = sB + (16 * jt + li) * BS + KQ * lk;
+#pragma unroll
+                    for (int n = 0; n < KQ; n += 4) {
+                        const float4 av = *(const float4*)(pa + n);
+                        const float4 bv = *(const float4*)(pb + n);
+                        s0 = mfma4(av.x, bv.x, s0);
+                        s1 = mfma4(av.y, bv.y, s1);
+                        s0 = mfma4(av.z, bv.z, s0);
+                        s1 = mfma4(av.w, bv.w, s1);
                     }
-                    acc_y = mfma4(av, px[4 * s * kW], acc_y);
-                }
-                const float xd = pxd[4 * s * kW];
+                    const int j = 16 * jt + li;
+                    const bool colv = jt < 4 || j - kRows < EXTRA;
+                    const int sj = jt < 4 ? j / R : -1;       // step of column j
+                    const float cum_s = s_cum[sj + 1];
+                    const float cum_s1 = s_cum[min(sj + 2, QT)];
+                    const float gam_s = s_gam[sj < 0 ? 0 : sj];
+                    const float bet_s1 = s_bet[sj + 1];
 #pragma unroll
-                for (int tt = 0; tt < 2; ++tt) {
-                    // state rows past N have zero B~ and stay zero
-                    float bv = cur.bb[tt][s];
-                    if (ROT) {
-                        const int n = 32 * wave + 16 * tt + li;
-                        int st = 0, rk;
-                        const bool col = col_of<R, TRAP>(4 * s + lk, &st, &rk);
-                        const float partner = __shfl_xor(bv, 1, 64);
-                        const bool rot = col && st >= 0;
-                        float sn, cs;
-                        sincos_rev(phi[(rot ? st : 0) * 64 + (n >> 1)], &sn, &cs);
-                        const float sgn = (n & 1) ? sn : -sn;
-                        const float rv = fmaf(sgn, partner, cs * bv);
-                        bv = rot ? rv : bv;
+                    for (int r = 0; r < 4; ++r) {
+                        const int i = 16 * it + 4 * lk + r;
+                        const int tau = i / R;
+                        const float cum_t = s_cum[tau + 1];
+                        const bool vg = colv && sj >= 0 && sj <= tau;
+                        const bool vb = colv && sj < tau;
+                        const float eg = exp_e(vg ? cum_t - cum_s : 0.0f);
+                        const float eb = exp_e(vb ? cum_t - cum_s1 : 0.0f);
+                        const float w = (vg ? gam_s * eg : 0.0f) + (vb ? bet_s1 * eb : 0.0f);
+                        if (j < JC) sM[i * JP + j] = (s0[r] + s1[r]) * w;
                     }
-                    if (tt == 0)
-                        hacc0 = mfma4(bv, xd, hacc0);
-                    else
-                        hacc1 = mfma4(bv, xd, hacc1);
+                }
+            }
+            // ---- Y^T = H^T C~^T, scaled by e^{cum} per output row ---------------
+            if (active) {
+#pragma unroll
+                for (int it = 0; it < 4; ++it) {
+                    floatx4 y0 = {0.0f, 0.0f, 0.0f, 0.0f}, y1 = {0.0f, 0.0f, 0.0f, 0.0f};
+                    const float* pc = sC + (16 * it + li) * BS + 16 * lk;
+#pragma unroll
+                    for (int hf = 0; hf < NH; ++hf)
+#pragma unroll
+                        for (int qq = 0; qq < 4; ++qq) {
+                            const float4 cv = *(const float4*)(pc + 64 * hf + 4 * qq);
+                            y0 = mfma4(acc_h[4 * hf + 0][qq], cv.x, y0);
+                            y1 = mfma4(acc_h[4 * hf + 1][qq], cv.y, y1);
+                            y0 = mfma4(acc_h[4 * hf + 2][qq], cv.z, y0);
+                            y1 = mfma4(acc_h[4 * hf + 3][qq], cv.w, y1);
+                        }
+                    const float ey = exp_e(s_cum[(16 * it + li) / R + 1]);
+                    acc_y[it] = (y0 + y1) * ey;
+                }
+            }
+            if constexpr (TRAP) __syncthreads();   // M complete
+            // ---- Y^T += X^T M^T (intra-chunk), then store Y ----------------------
+            if (active) {
+                const float* px = sXT + (16 * wave + li) * JP + 4 * lk;
+#pragma unroll
+                for (int jt = 0; jt < 4; ++jt) {
+                    const float4 xv = *(const float4*)(px + 16 * jt);
+#pragma unroll
+                    for (int it = jt; it < 4; ++it) {
+                        const float4 mv = *(const float4*)(sM + (16 * it + li) * JP + 16 * jt + 4 * lk);
+                        acc_y[it] = mfma4(xv.x, mv.x, acc_y[it]);
+                        acc_y[it] = mfma4(xv.y, mv.y, acc_y[it]);
+                        acc_y[it] = mfma4(xv.z, mv.z, acc_y[it]);
+                        acc_y[it] = mfma4(xv.w, mv.w, acc_y[it]);
+                    }
+                }
+#pragma unroll
+                for (int e = 0; e < JX; ++e) {
+                    const float xe = sXT[(16 * wave + li) * JP + kRows + 4 * e + lk];
+#pragma unroll
+                    for (int it = 0; it < 4; ++it)
+                        acc_y[it] = mfma4(xe, sM[(16 * it + li) * JP + kRows + 4 * e + lk], acc_y[it]);
+                }
+                // lane holds Y[i = 16 it + li][p = p0 + 16 w + 4 lk + r]
+#pragma unroll
+                for (int it = 0; it < 4; ++it) {
+                    const int i = 16 * it + li;
+                    const int tg = t0g + i / R;
+                    if (tg < a.L) {
+                        const int pp = p0 + 16 * wave + 4 * lk;
+                        IO* yrow = (IO*)a.Y + (((size_t)b * a.L + tg) * a.H + h) * (size_t)a.P * R;
+                        if (R == 1) {
+                            if constexpr (sizeof(IO) == 4) {
+                                *(float4*)((float*)yrow + pp) =
+                                    make_float4(acc_y[it][0], acc_y[it][1], acc_y[it][2], acc_y[it][3]);
+                            } else {
+                                const uint32_t u0 = f32_to_bf16(acc_y[it][0]) | ((uint32_t)f32_to_bf16(acc_y[it][1]) << 16);
+                                const uint32_t u1 = f32_to_bf16(acc_y[it][2]) | ((uint32_t)f32_to_bf16(acc_y[it][3]) << 16);
+                                *(uint2*)((bf16*)yrow + pp) = make_uint2(u0, u1);
+                            }
+                        } else {
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) store_out(&yrow[(size_t)(pp + r) * R + i % R], acc_y[it][r]);
+                        }
+                    }
                 }
             }
         }
-        acc_h[0] = hacc0;
-        acc_h[1] = hacc1;
-        // the next chunk's S and B~ go into the registers just freed; they have the
-        // C~ H product, the epilogue and the barrier to arrive
-        if (more) load_mb(c + 1, cur);
-        // ---- Y_state = C~ H  (H = state entering the chunk, from sH[buf]) ----------
-        floatx4 acc_s0 = {0.0f, 0.0f, 0.0f, 0.0f}, acc_s1 = {0.0f, 0.0f, 0.0f, 0.0f};
-        {
-            const int tau = c_row / R;
-            if (ROT) {
+
+        // ---- H' = e^{cum_last} H + B~^T Xd, then back to the physical frame -------
+        if (active) {
+            const float tot = exp_e(cum_last);
 #pragma unroll
-                for (int s = 0; s < NQ; s += 2) {
-                    const int k = (lk * NQ + s) >> 1;
-                    float sn, cs;
-                    sincos_rev(phi[tau * 64 + k], &sn, &cs);
-                    const float v0 = cur.cc[s], v1 = cur.cc[s + 1];
-                    cur.cc[s] = fmaf(-sn, v1, cs * v0);
-                    cur.cc[s + 1] = fmaf(sn, v0, cs * v1);
+            for (int t = 0; t < NT; ++t) acc_h[t] *= tot;
+            const float* pxd = sXdT + (16 * wave + li) * JP + 16 * lk;
+#pragma unroll
+            for (int sq4 = 0; sq4 < 4; ++sq4) {
+                const float4 xd = *(const float4*)(pxd + 4 * sq4);
+                const float xds[4] = {xd.x, xd.y, xd.z, xd.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int j = 16 * lk + 4 * sq4 + e;
+#pragma unroll
+                    for (int hf = 0; hf < NH; ++hf) {
+                        const float4 bv = *(const float4*)(sB + j * BS + 64 * hf + 4 * li);
+                        acc_h[4 * hf + 0] = mfma4(bv.x, xds[e], acc_h[4 * hf + 0]);
+                        acc_h[4 * hf + 1] = mfma4(bv.y, xds[e], acc_h[4 * hf + 1]);
+                        acc_h[4 * hf + 2] = mfma4(bv.z, xds[e], acc_h[4 * hf + 2]);
+                        acc_h[4 * hf + 3] = mfma4(bv.w, xds[e], acc_h[4 * hf + 3]);
+                    }
                 }
             }
-            const float* ph = sH[buf] + hidx(lk * NQ, li);
 #pragma unroll
-            for (int s = 0; s < NQ; s += 2) {
-                acc_s0 = mfma4(cur.cc[s], ph[s * kW], acc_s0);
-                acc_s1 = mfma4(cur.cc[s + 1], ph[(s + 1) * kW], acc_s1);
-            }
-        }
-        // the next chunk's C~ rows: needed only at its C~ H product
-        if (more) load_c(c + 1, cur);
-        // ---- write Y = Y_intra + e^{cum_tau} Y_state ---------------------------------
+            for (int e = 0; e < JX; ++e) {
+                const int j = kRows + 4 * e + lk;
+                const float xd = sXdT[(16 * wave + li) * JP + j];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int i = 16 * wave + 4 * lk + r;
-            const int tau = i / R;
-            const int tg = t0g + tau;
-            const float y = fmaf(exp_e(s_cum[buf][tau + 1]), acc_s0[r] + acc_s1[r], acc_y[r]);
-            if (tg < a.L)
-                store_out(&((IO*)a.Y)[(((size_t)b * a.L + tg) * a.H + h) * (size_t)a.P * R +
-                                      (size_t)(p0 + li) * R + i % R], y);
-        }
-        // ---- rotate the state back to the physical frame and publish it ----------
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-            const int n0 = 32 * wave + 16 * tt + 4 * lk;
-            if (ROT && n0 < a.N) {
-#pragma unroll
-                for (int pr = 0; pr < 2; ++pr) {
-                    float sn, cs;
-                    sincos_rev(phi[(QT - 1) * 64 + (n0 >> 1) + pr], &sn, &cs);
-                    const float v0 = acc_h[tt][2 * pr], v1 = acc_h[tt][2 * pr + 1];
-                    // R(-phi): (c v0 + s v1, -s v0 + c v1)
-                    acc_h[tt][2 * pr] = fmaf(sn, v1, cs * v0);
-                    acc_h[tt][2 * pr + 1] = fmaf(-sn, v0, cs * v1);
+                for (int hf = 0; hf < NH; ++hf) {
+                    const float4 bv = *(const float4*)(sB + j * BS + 64 * hf + 4 * li);
+                    acc_h[4 * hf + 0] = mfma4(bv.x, xd, acc_h[4 * hf + 0]);
+                    acc_h[4 * hf + 1] = mfma4(bv.y, xd, acc_h[4 * hf + 1]);
+                    acc_h[4 * hf + 2] = mfma4(bv.z, xd, acc_h[4 * hf + 2]);
+                    acc_h[4 * hf + 3] = mfma4(bv.w, xd, acc_h[4 * hf + 3]);
                 }
             }
-            if (n0 < NP) {
+            if constexpr (ROT) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) sH[buf ^ 1][hidx(n0 + r, li)] = acc_h[tt][r];
+                for (int t = 0; t < NT; t += 2)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int k = state_row<NP>(t, r, lk) >> 1;
+                        const float cs = s_dc[k], sn = s_ds[k];
+                        const float v0 = acc_h[t][r], v1 = acc_h[t + 1][r];
+                        // R(-phi): (c v0 + s v1, -s v0 + c v1)
+                        acc_h[t][r] = fmaf(sn, v1, cs * v0);
+                        acc_h[t + 1][r] = fmaf(-sn, v0, cs * v1);
+                    }
             }
         }
-        if (more) store_stage(c + 1);
     }
-    if (a.h_out) {
+
+    // ---- outputs of the walk ------------------------------------------------------
+    if constexpr (SO) {
+        const size_t u = (size_t)(b * a.H + h) * (a.nseg - 1) + seg;
+        if (active) {
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
+            for (int t = 0; t < NT; ++t)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int n = state_row<NP>(t, r, lk);
+                    if (n < a.N) a.seg_h[(u * a.N + n) * a.P + pcol] = acc_h[t][r];
+                }
+        }
+        if (pg == 0) {
+            if (tid == 0) a.seg_ld[u] = seg_acc;
+            if (ROT && ssg == 3 && k_ok) a.seg_rev[u * (a.N / 2) + sk] = rev_acc;
+        }
+    } else {
+        if (a.h_out && seg == a.nseg - 1 && active) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int n = 32 * wave + 16 * tt + 4 * lk + r;
-                if (n < a.N) a.h_out[sh_off + (size_t)n * a.P + p0 + li] = acc_h[tt][r];
+                const int n = state_row<NP>(t, r, lk);
+                if (n < a.N) a.h_out[sh_off + (size_t)n * a.P + pcol] = acc_h[t][r];
             }
+        }
     }
 }
 
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
-template <int R, bool TRAP>
-size_t scores_bytes(int64_t batch, int64_t L, int64_t nS) {
-    using Gm = Geo<R, TRAP>;
-    int64_t nch = (L + Gm::QT - 1) / Gm::QT;
-    return (size_t)(batch * nch * nS) * (size_t)(kRows * Gm::KP) * sizeof(float);
+struct Plan {
+    int64_t nch, nseg, cps, npg;
+    size_t off_seg_h, off_seg_ld, off_seg_rev, bytes;
+};
+
+inline size_t align256(size_t v) { return (v + 255) / 256 * 256; }
+
+// Chunks, segments and workspace for a problem (depends on the sizes only, so
+// mb_workspace_size agrees with the call).
+Plan make_plan(bool trap, int64_t R, int64_t batch, int64_t L, int64_t H, int64_t P, int64_t G,
+               int64_t N) {
+    Plan p{};
+    const int64_t QT = kRows / R;
+    p.nch = (L + QT - 1) / QT;
+    p.npg = (P + kPG - 1) / kPG;
+    const int64_t units = batch * H * p.npg;
+    int64_t want = units > 0 ? (kTargetWG + units - 1) / units : 1;
+    int64_t maxseg = p.nch / 4;
+    if (maxseg < 1) maxseg = 1;
+    int64_t ns = want < maxseg ? want : maxseg;
+    if (ns > 64) ns = 64;
+    if (ns < 1) ns = 1;
+    p.cps = p.nch > 0 ? (p.nch + ns - 1) / ns : 1;
+    p.nseg = p.nch > 0 ? (p.nch + p.cps - 1) / p.cps : 1;
+    size_t off = 0;
+    if (!trap) off = align256((size_t)(batch * p.nch * G) * kRows * kRows * 4);
+    p.off_seg_h = off;
+    const size_t nsg = (size_t)(batch * H * (p.nseg - 1));
+    off += align256(nsg * (size_t)(N * P) * 4);
+    p.off_seg_ld = off;
+    off += align256(nsg * 4);
+    p.off_seg_rev = off;
+    if (trap) off += align256(nsg * (size_t)(N / 2) * 4);
+    p.bytes = (p.nseg > 1 || !trap) ? off : 0;
+    return p;
 }
 
 template <int NP, int R, bool TRAP, bool ROT, bool GROUPED, typename IO>
-mb_status launch(Args a, int64_t batch, hipStream_t stream) {
-    using Gm = Geo<R, TRAP>;
-    a.nch = (a.L + Gm::QT - 1) / Gm::QT;
-    const int nS = TRAP ? a.H : a.G;
-    hipLaunchKernelGGL((k_scores<NP, R, TRAP, ROT, GROUPED, IO>), dim3(a.nch, nS, (unsigned)batch),
-                       dim3(kThreads), 0, stream, a);
-    mb_status st = check_launch();
-    if (st != MB_OK) return st;
-    if (a.N == NP)
+mb_status launch(Args a, int64_t batch, const Plan& pl, char* ws, hipStream_t stream) {
+    a.nch = (int)pl.nch;
+    a.nseg = (int)pl.nseg;
+    a.cps = (int)pl.cps;
+    a.npg = (int)pl.npg;
+    a.S = TRAP ? nullptr : (float*)ws;
+    a.seg_h = (float*)(ws + pl.off_seg_h);
+    a.seg_ld = (float*)(ws + pl.off_seg_ld);
+    a.seg_rev = (float*)(ws + pl.off_seg_rev);
+    if constexpr (!TRAP) {
+        hipLaunchKernelGGL((k_scores<NP, IO>), dim3(a.nch, a.G, (unsigned)batch), dim3(kThreads), 0,
+                           stream, a);
+        mb_status st = check_launch();
+        if (st != MB_OK) return st;
+    }
+    const int64_t per_seg = batch * a.H * a.npg;
+    if (a.nseg > 1) {
         hipLaunchKernelGGL((k_walk<NP, R, TRAP, ROT, GROUPED, IO, true>),
-                           dim3(a.P / kW, a.H, (unsigned)batch), dim3(kThreads), 0, stream, a);
-    else
-        hipLaunchKernelGGL((k_walk<NP, R, TRAP, ROT, GROUPED, IO, false>),
-                           dim3(a.P / kW, a.H, (unsigned)batch), dim3(kThreads), 0, stream, a);
+                           dim3((unsigned)(per_seg * (a.nseg - 1))), dim3(kThreads), 0, stream, a);
+        mb_status st = check_launch();
+        if (st != MB_OK) return st;
+    }
+    hipLaunchKernelGGL((k_walk<NP, R, TRAP, ROT, GROUPED, IO, false>),
+                       dim3((unsigned)(per_seg * a.nseg)), dim3(kThreads), 0, stream, a);
     return check_launch();
 }
 
 template <int R, bool TRAP, bool ROT, bool GROUPED, typename IO>
-mb_status launch_np(Args a, int64_t batch, hipStream_t stream) {
-    if (a.N <= 64) return launch<64, R, TRAP, ROT, GROUPED, IO>(a, batch, stream);
-    return launch<128, R, TRAP, ROT, GROUPED, IO>(a, batch, stream);
+mb_status launch_np(Args a, int64_t batch, const Plan& pl, char* ws, hipStream_t stream) {
+    if (a.N <= 64) return launch<64, R, TRAP, ROT, GROUPED, IO>(a, batch, pl, ws, stream);
+    return launch<128, R, TRAP, ROT, GROUPED, IO>(a, batch, pl, ws, stream);
 }
 
 template <int R, bool TRAP, bool GROUPED>
-mb_status dispatch(Args a, int64_t batch, mb_dtype dtype, hipStream_t stream) {
+mb_status dispatch(Args a, int64_t batch, const Plan& pl, char* ws, mb_dtype dtype, hipStream_t stream) {
     const bool rot = a.theta != nullptr;
+    if constexpr (!TRAP) {
+        return dtype == MB_F32 ? launch_np<R, false, false, GROUPED, float>(a, batch, pl, ws, stream)
+                               : launch_np<R, false, false, GROUPED, bf16>(a, batch, pl, ws, stream);
+    }
     if (dtype == MB_F32)
-        return rot ? launch_np<R, TRAP, true, GROUPED, float>(a, batch, stream)
-                   : launch_np<R, TRAP, false, GROUPED, float>(a, batch, stream);
-    return rot ? launch_np<R, TRAP, true, GROUPED, bf16>(a, batch, stream)
-               : launch_np<R, TRAP, false, GROUPED, bf16>(a, batch, stream);
+        return rot ? launch_np<R, TRAP, true, GROUPED, float>(a, batch, pl, ws, stream)
+                   : launch_np<R, TRAP, false, GROUPED, float>(a, batch, pl, ws, stream);
+    return rot ? launch_np<R, TRAP, true, GROUPED, bf16>(a, batch, pl, ws, stream)
+               : launch_np<R, TRAP, false, GROUPED, bf16>(a, batch, pl, ws, stream);
 }
 
 bool dims_ok(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N, int64_t R = 1) {
     if (batch < 0 || L < 0 || H < 1 || P < 1 || N < 1) return false;
-    if (N > kNMax || N % 4 != 0 || P % kW != 0) return false;
+    if (N > kNMax || N % 4 != 0 || P % 16 != 0) return false;
     if (batch > 65535 || H > 65535 || L > INT32_MAX / 2) return false;
     // one batch row of any tensor is addressed with 32-bit byte offsets
     const int64_t row = L * H * (P > N ? P : N) * R * 4;
@@ -757,21 +924,10 @@ bool dims_ok(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N, int64_t 
     return true;
 }
 
-size_t ws_needed(mb_op op, int64_t batch, int64_t L, int64_t H, int64_t G, int64_t R) {
-    switch (op) {
-        case MB_OP_SSD_CHUNKED: return scores_bytes<1, false>(batch, L, G);
-        case MB_OP_TRAP_SSD: return scores_bytes<1, true>(batch, L, H);
-        case MB_OP_MIMO_SSD:
-            switch (R) {
-                case 1: return scores_bytes<1, true>(batch, L, H);
-                case 2: return scores_bytes<2, true>(batch, L, H);
-                case 4: return scores_bytes<4, true>(batch, L, H);
-                case 8: return scores_bytes<8, true>(batch, L, H);
-                case 16: return scores_bytes<16, true>(batch, L, H);
-                default: return 0;
-            }
-        default: return 0;
-    }
+Plan plan_for(mb_op op, int64_t batch, int64_t L, int64_t H, int64_t P, int64_t G, int64_t N,
+              int64_t R) {
+    return make_plan(op != MB_OP_SSD_CHUNKED, op == MB_OP_MIMO_SSD ? R : 1, batch, L, H, P,
+                     op == MB_OP_SSD_CHUNKED ? G : H, N);
 }
 
 mb_status check_ws(void* ws, size_t ws_bytes, size_t need) {
@@ -791,7 +947,9 @@ extern "C" size_t mb_workspace_size(mb_op op, int64_t batch, int64_t L, int64_t 
     if (op == MB_OP_SELECTIVE_SCAN || op == MB_OP_SSM_STEP) return 0;
     if (!dims_ok(batch, L, H, P, N)) return 0;
     if (op == MB_OP_SSD_CHUNKED && (G < 1 || H % G)) return 0;
-    return ws_needed(op, batch, L, H, G, R);
+    if (op == MB_OP_MIMO_SSD && R != 1 && R != 2 && R != 4 && R != 8 && R != 16) return 0;
+    if (batch == 0 || L == 0) return 0;
+    return plan_for(op, batch, L, H, P, G, N, R).bytes;
 }
 
 static mb_status ssd_common_checks(const void* X, const float* logdecay, const void* B,
@@ -833,13 +991,13 @@ extern "C" mb_status mb_ssd_chunked(const void* X, const float* logdecay, const 
     mb_status st = ssd_common_checks(X, logdecay, B, C, h0, Y, h_out, nullptr, nullptr, nullptr,
                                      batch, L, H, P, G, N, 1, dtype, chunk, false);
     if (st != MB_OK) return st;
-    const size_t need = ws_needed(MB_OP_SSD_CHUNKED, batch, L, H, G, 1);
-    if (L > 0 && batch > 0 && (st = check_ws(ws, ws_bytes, need)) != MB_OK) return st;
     if (batch == 0) return MB_OK;
     if (L == 0) return copy_state(h0, h_out, batch * H * N * P, stream);
-    Args a{X, logdecay, B, C, nullptr, nullptr, nullptr, h0, Y, h_out, (float*)ws,
-           (int)L, (int)H, (int)P, (int)G, (int)N, 0};
-    return dispatch<1, false, true>(a, batch, dtype, stream);
+    const Plan pl = plan_for(MB_OP_SSD_CHUNKED, batch, L, H, P, G, N, 1);
+    if ((st = check_ws(ws, ws_bytes, pl.bytes)) != MB_OK) return st;
+    Args a{X, logdecay, B, C, nullptr, nullptr, nullptr, h0, Y, h_out, nullptr, nullptr, nullptr,
+           nullptr, (int)L, (int)H, (int)P, (int)G, (int)N, 0, 0, 0, 0};
+    return dispatch<1, false, true>(a, batch, pl, (char*)ws, dtype, stream);
 }
 
 extern "C" mb_status mb_trap_ssd(const void* X, const float* logdecay, const void* B,
@@ -852,13 +1010,13 @@ extern "C" mb_status mb_trap_ssd(const void* X, const float* logdecay, const voi
     mb_status st = ssd_common_checks(X, logdecay, B, C, h0, Y, h_out, beta, gamma, theta, batch,
                                      L, H, P, G, N, 1, dtype, chunk, true);
     if (st != MB_OK) return st;
-    const size_t need = ws_needed(MB_OP_TRAP_SSD, batch, L, H, G, 1);
-    if (L > 0 && batch > 0 && (st = check_ws(ws, ws_bytes, need)) != MB_OK) return st;
     if (batch == 0) return MB_OK;
     if (L == 0) return copy_state(h0, h_out, batch * H * N * P, stream);
-    Args a{X, logdecay, B, C, beta, gamma, theta, h0, Y, h_out, (float*)ws,
-           (int)L, (int)H, (int)P, (int)G, (int)N, 0};
-    return dispatch<1, true, true>(a, batch, dtype, stream);
+    const Plan pl = plan_for(MB_OP_TRAP_SSD, batch, L, H, P, G, N, 1);
+    if ((st = check_ws(ws, ws_bytes, pl.bytes)) != MB_OK) return st;
+    Args a{X, logdecay, B, C, beta, gamma, theta, h0, Y, h_out, nullptr, nullptr, nullptr, nullptr,
+           (int)L, (int)H, (int)P, (int)G, (int)N, 0, 0, 0, 0};
+    return dispatch<1, true, true>(a, batch, pl, (char*)ws, dtype, stream);
 }
 
 extern "C" mb_status mb_mimo_ssd(const void* X, const float* logdecay, const void* B,
@@ -871,17 +1029,18 @@ extern "C" mb_status mb_mimo_ssd(const void* X, const float* logdecay, const voi
     mb_status st = ssd_common_checks(X, logdecay, B, C, h0, Y, h_out, beta, gamma, theta, batch,
                                      L, H, P, H, N, R, dtype, chunk, true);
     if (st != MB_OK) return st;
-    const size_t need = ws_needed(MB_OP_MIMO_SSD, batch, L, H, 1, R);
-    if (L > 0 && batch > 0 && (st = check_ws(ws, ws_bytes, need)) != MB_OK) return st;
     if (batch == 0) return MB_OK;
     if (L == 0) return copy_state(h0, h_out, batch * H * N * P, stream);
-    Args a{X, logdecay, B, C, beta, gamma, theta, h0, Y, h_out, (float*)ws,
-           (int)L, (int)H, (int)P, (int)H, (int)N, 0};
+    const Plan pl = plan_for(MB_OP_MIMO_SSD, batch, L, H, P, 1, N, R);
+    if ((st = check_ws(ws, ws_bytes, pl.bytes)) != MB_OK) return st;
+    Args a{X, logdecay, B, C, beta, gamma, theta, h0, Y, h_out, nullptr, nullptr, nullptr, nullptr,
+           (int)L, (int)H, (int)P, (int)H, (int)N, 0, 0, 0, 0};
+    char* w = (char*)ws;
     switch (R) {
-        case 1: return dispatch<1, true, false>(a, batch, dtype, stream);
-        case 2: return dispatch<2, true, false>(a, batch, dtype, stream);
-        case 4: return dispatch<4, true, false>(a, batch, dtype, stream);
-        case 8: return dispatch<8, true, false>(a, batch, dtype, stream);
-        default: return dispatch<16, true, false>(a, batch, dtype, stream);
+        case 1: return dispatch<1, true, false>(a, batch, pl, w, dtype, stream);
+        case 2: return dispatch<2, true, false>(a, batch, pl, w, dtype, stream);
+        case 4: return dispatch<4, true, false>(a, batch, pl, w, dtype, stream);
+        case 8: return dispatch<8, true, false>(a, batch, pl, w, dtype, stream);
+        default: return dispatch<16, true, false>(a, batch, pl, w, dtype, stream);
     }
 }
