@@ -32,12 +32,12 @@
 // Kernels
 //   k_scores  (Mamba-2 only) one workgroup per (batch, chunk, group):
 //             S = C B^T on fp32 MFMA, shared by the heads of the group.
-//   k_walk    one workgroup (4 waves) per (batch, head, segment, 64 state
+//   k_walk    one workgroup (8 waves) per (batch, head, segment, 64 state
 //             columns), walking the segment's chunks in order.  Per chunk the
 //             workgroup stages B~ and C~ (rotated once, for all columns), X and
 //             the chunk-end-weighted X (transposed) and the masked score matrix
-//             in LDS; wave w owns state columns 16w..16w+15 for all N rows as
-//             MFMA accumulators.  For Mamba-3 the scores C~ B~^T are computed in
+//             in LDS; waves w and w+4 own state columns 16w..16w+15, each for
+//             half of the N rows, as MFMA accumulators.  For Mamba-3 the scores C~ B~^T are computed in
 //             the walk (they are per head).  The state rows are permuted inside
 //             the accumulator tiles so that the accumulators are directly the
 //             operand of the next chunk's C~ H product: the state never leaves
@@ -289,35 +289,43 @@ __global__ __launch_bounds__(kThreads) void k_scores(Args a) {
 // ---------------------------------------------------------------------------
 // Chunk walk.  SO = state only (the segment pre-pass).
 //
-// State layout: wave w holds columns p = p0 + 16w + li of all NP state rows in
-// NT = NP/16 accumulator tiles; tile t, register r of lane (li, lk) is row
-//     n(t, r) = 64 (t / 4) + 16 lk + 4 r + t % 4,
-// i.e. lane group lk owns rows {16 lk .. 16 lk + 15} (+64).  Read as the A
-// operand of Y^T = H^T C~^T this is a K-slice of 16 (or 32) consecutive rows per
-// lane group, matching contiguous 16-byte reads of C~; rotation pairs (2k, 2k+1)
-// sit in tiles (t, t+1) of the same lane.
+// Eight waves, two per SIMD.  Waves w and w + 4 own state columns
+// p = p0 + 16 (w % 4) + li; wave w holds state rows n < NP/2, wave w + 4 rows
+// n >= NP/2, each in NT2 = NP/32 accumulator tiles.  Tile t, register r of lane
+// (li, lk) of half nh is row
+//     n(t, r) = (NP/2) nh + (NP/8) lk + NT2 r + t,
+// i.e. lane group lk owns NP/8 consecutive rows.  Read as the A operand of
+// Y^T = H^T C~^T, the accumulators are a K-slice of consecutive rows per lane
+// group, matching contiguous 16-byte reads of C~: the state never leaves
+// registers.  Rotation pairs (2k, 2k + 1) sit in tiles (t, t + 1) of one lane.
+// The two halves' partial outputs are summed through LDS.
 // ---------------------------------------------------------------------------
+constexpr int kWalkThreads = 512;
+
 template <int NP>
-__device__ __forceinline__ int state_row(int t, int r, int lk) {
-    return 64 * (t / 4) + 16 * lk + 4 * r + (t % 4);
+__device__ __forceinline__ int state_row(int t, int r, int lk, int nh) {
+    return (NP / 2) * nh + (NP / 8) * lk + (NP / 32) * r + t;
 }
 
-// Score tiles (row block, column block) of the trapezoid per wave; column
-// block 4 holds the previous-step columns.  -1 ends a list.
-__constant__ int kTrapTiles[4][4] = {{0x30, 0x31, 0x32, 0x33},
-                                     {0x20, 0x21, 0x22, 0x00},
-                                     {0x10, 0x11, 0x34, -1},
-                                     {0x24, 0x14, 0x04, -1}};
+// Score tiles (row block << 4 | column block) of the trapezoid per wave;
+// column block 4 holds the previous-step columns; -1 ends a list.
+__constant__ int kTrapTiles[8][2] = {{0x11, 0x00}, {0x04, 0x14}, {0x24, -1}, {0x34, -1},
+                                     {0x30, 0x31}, {0x32, 0x33}, {0x20, 0x21}, {0x22, 0x10}};
 
 template <int NP, int R, bool TRAP, bool ROT, bool GROUPED, typename IO, bool SO>
-__global__ __launch_bounds__(kThreads) void k_walk(Args a) {
+__global__ __launch_bounds__(kWalkThreads) void k_walk(Args a) {
     using Gm = Geo<R, TRAP>;
-    constexpr int QT = Gm::QT, QS = Gm::QS, EXTRA = Gm::EXTRA, JX = Gm::JX;
-    constexpr int JC = Gm::JC, JP = Gm::JP, PR = Gm::PR;
-    constexpr int BS = NP + 4;     // LDS row stride of B~ / C~ (4 mod 32 floats)
-    constexpr int NT = NP / 16;    // state tiles per wave
-    constexpr int NH = NT / 4;     // halves of 64 rows
-    constexpr int KQ = NP / 4;     // contraction slice over the state per lane group (scores)
+    constexpr int QT = Gm::QT, EXTRA = Gm::EXTRA, JX = Gm::JX;
+    constexpr int JC = Gm::JC, JP = Gm::JP;
+    constexpr int BS = NP + 4;      // LDS row stride of B~ / C~ (4 mod 32 floats)
+    constexpr int NT2 = NP / 32;    // state tiles per wave
+    constexpr int KQ = NP / 4;      // contraction slice over the state per lane group (scores)
+    constexpr int NSG = QT < 8 ? QT : 8;       // step groups (one per wave) of the B / C / angle staging
+    constexpr int QSG = QT / NSG;              // steps per group
+    constexpr int PRG = (R + NSG - 1) / NSG;   // previous-step ranks per staging thread
+    constexpr int NXG = QT < 8 ? QT : 8;       // step groups of the X staging
+    constexpr int QXG = QT / NXG;
+    constexpr int PRX = (R + NXG - 1) / NXG;
     constexpr bool FULL = !SO;
 
     __shared__ __attribute__((aligned(16))) float sB[Gm::BR * BS];
@@ -325,11 +333,13 @@ __global__ __launch_bounds__(kThreads) void k_walk(Args a) {
     __shared__ __attribute__((aligned(16))) float sXT[FULL ? kPG * JP : 4];
     __shared__ __attribute__((aligned(16))) float sXdT[kPG * JP];
     __shared__ __attribute__((aligned(16))) float sM[FULL ? kRows * JP : 4];
+    __shared__ __attribute__((aligned(16))) float sYp[FULL ? 4 * 4 * 64 * 4 : 4];
     __shared__ float s_cum[QT + 1];
     __shared__ float s_gam[TRAP ? QT : 1];
     __shared__ float s_bet[TRAP ? QT + 1 : 1];
     __shared__ float s_dc[ROT ? NP / 2 : 1];
     __shared__ float s_ds[ROT ? NP / 2 : 1];
+    __shared__ float s_tht[ROT ? 8 * 64 : 1];   // per step group: chunk-local angle totals per pair
 
     // ---- workgroup -> (batch, segment, head, column group) ------------------
     // Workgroups of one (batch, segment) share B and C; ids i, i+8, i+16, ... run
@@ -357,30 +367,33 @@ __global__ __launch_bounds__(kThreads) void k_walk(Args a) {
 
     const int tid = threadIdx.x, lane = tid % 64;
     const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
+    const int pw = wave & 3, nh = wave >> 2;
     const int li = lane % 16, lk = lane / 16;
     const int pw_n = (min(kPG, a.P - p0)) / 16;
-    const bool active = wave < pw_n;   // uniform
-    const int pcol = p0 + 16 * wave + li;
+    const bool active = pw < pw_n;   // uniform
+    const int pcol = p0 + 16 * pw + li;
     const Views<R, GROUPED, IO> vw(a, b, h, hg);
     const size_t sh_off = (size_t)(b * a.H + h) * a.N * a.P;
 
-    // staging roles: (sk, ssg) = rotation pair and step quarter for B / C /
-    // angles; (xpl, xtq) = state column and step quarter for X
-    const int sk = tid / 4, ssg = tid % 4;
-    const bool k_in = sk < NP / 2;
+    // staging roles: (sk, ssg) = rotation pair (lane) and step group (wave) for
+    // B / C / angles; (xpl, xtq) = state column and step group for X.  Lanes run
+    // along the row, so loads are contiguous and LDS writes hit distinct banks.
+    const int sk = tid % 64, ssg = tid / 64;
+    const bool k_in = sk < NP / 2 && ssg < NSG;
     const bool k_ok = k_in && 2 * sk < a.N;
     const int xpl = tid % 64, xtq = tid / 64;
-    const bool x_ok = p0 + xpl < a.P;
-    const int si = tid / 4, sq = tid % 4;   // Mamba-2 score staging: row, column quarter
+    const bool x_in = xtq < NXG;
+    const bool x_ok = x_in && p0 + xpl < a.P;
+    const int si = tid / 8, sq = tid % 8;   // Mamba-2 score staging: row, 8-column block
 
     // ---- one-time zero fill of padding that staging never writes ------------
     if constexpr (TRAP) {
-        for (int e = tid; e < (Gm::BR - kRows - EXTRA) * BS; e += kThreads)
+        for (int e = tid; e < (Gm::BR - kRows - EXTRA) * BS; e += kWalkThreads)
             sB[(kRows + EXTRA) * BS + e] = 0.0f;
     }
     if constexpr (JC > kRows + EXTRA) {
         constexpr int PADC = JC > kRows + EXTRA ? JC - kRows - EXTRA : 1;
-        for (int e = tid; e < kPG * PADC; e += kThreads) {
+        for (int e = tid; e < kPG * PADC; e += kWalkThreads) {
             const int row = e / PADC, col = kRows + EXTRA + e % PADC;
             if constexpr (FULL) sXT[row * JP + col] = 0.0f;
             sXdT[row * JP + col] = 0.0f;
@@ -389,14 +402,14 @@ __global__ __launch_bounds__(kThreads) void k_walk(Args a) {
 
     // ---- prefetch registers -------------------------------------------------
     struct Pre {
-        float b[QS][2 * R];          // B pair (2sk, 2sk+1) x ranks, steps ssg*QS + i
-        float bp[2 * PR];            // previous step, ranks ssg*PR + q
-        float c[FULL ? QS : 1][2 * R];
-        float th[ROT ? QS : 1];
-        float x[QS][R];              // X column p0 + xpl, steps xtq*QS + i
-        float xp[PR];                // previous step, ranks xtq*PR + q
-        float sc[(FULL && !TRAP) ? 16 : 1];   // Mamba-2 score row si, columns 16 sq ..
-        float ld, gam, bet;          // step lane of the chunk
+        float b[QSG][2 * R];          // B pair (2sk, 2sk+1) x ranks, steps ssg*QSG + i
+        float bp[2 * PRG];            // previous step, ranks ssg*PRG + q
+        float c[FULL ? QSG : 1][2 * R];
+        float th[ROT ? QSG : 1];
+        float x[QXG][R];              // X column p0 + xpl, steps xtq*QXG + i
+        float xp[PRX];                // previous step, ranks xtq*PRX + q
+        float sc[(FULL && !TRAP) ? 8 : 1];   // Mamba-2 score row si, columns 8 sq ..
+        float ld, gam, bet;           // step `lane` of the chunk
     };
     const Buf Sbuf = (FULL && !TRAP)
         ? make_buf(a.S + (size_t)b * a.nch * a.G * (kRows * kRows), (size_t)a.nch * a.G * kRows * kRows * 4)
@@ -406,34 +419,34 @@ __global__ __launch_bounds__(kThreads) void k_walk(Args a) {
         const int t0g = c * QT;
         if (k_ok) {
 #pragma unroll
-            for (int i = 0; i < QS; ++i) {
-                const int e = (t0g + ssg * QS + i) * vw.bc_step + vw.bc_head + 2 * sk * R;
+            for (int i = 0; i < QSG; ++i) {
+                const int e = (t0g + ssg * QSG + i) * vw.bc_step + vw.bc_head + 2 * sk * R;
                 VecLoad<IO, 2 * R>::run(vw.B, e, p.b[i]);
                 if constexpr (FULL) VecLoad<IO, 2 * R>::run(vw.C, e, p.c[i]);
             }
-            if constexpr (TRAP) if (ssg * PR < R) {
-                const int e = (t0g - 1) * vw.bc_step + vw.bc_head + 2 * sk * R + ssg * PR;
-                VecLoad<IO, PR>::run(vw.B, e, p.bp);
-                VecLoad<IO, PR>::run(vw.B, e + R, p.bp + PR);
+            if constexpr (TRAP) if (ssg * PRG < R) {
+                const int e = (t0g - 1) * vw.bc_step + vw.bc_head + 2 * sk * R + ssg * PRG;
+                VecLoad<IO, PRG>::run(vw.B, e, p.bp);
+                VecLoad<IO, PRG>::run(vw.B, e + R, p.bp + PRG);
             }
             if constexpr (ROT) {
 #pragma unroll
-                for (int i = 0; i < QS; ++i)
-                    p.th[i] = bload<float>(vw.th, ((t0g + ssg * QS + i) * a.H + h) * (a.N / 2) + sk);
+                for (int i = 0; i < QSG; ++i)
+                    p.th[i] = bload<float>(vw.th, ((t0g + ssg * QSG + i) * a.H + h) * (a.N / 2) + sk);
             }
         }
         if (x_ok) {
 #pragma unroll
-            for (int i = 0; i < QS; ++i)
-                VecLoad<IO, R>::run(vw.X, (t0g + xtq * QS + i) * vw.x_step + vw.x_head + (p0 + xpl) * R,
+            for (int i = 0; i < QXG; ++i)
+                VecLoad<IO, R>::run(vw.X, (t0g + xtq * QXG + i) * vw.x_step + vw.x_head + (p0 + xpl) * R,
                                     p.x[i]);
-            if constexpr (TRAP) if (xtq * PR < R)
-                VecLoad<IO, PR>::run(vw.X, (t0g - 1) * vw.x_step + vw.x_head + (p0 + xpl) * R + xtq * PR,
-                                     p.xp);
+            if constexpr (TRAP) if (xtq * PRX < R)
+                VecLoad<IO, PRX>::run(vw.X, (t0g - 1) * vw.x_step + vw.x_head + (p0 + xpl) * R + xtq * PRX,
+                                      p.xp);
         }
-        if constexpr (FULL && !TRAP) if (16 * sq <= si) {
-            const int e = (c * a.G + hg) * (kRows * kRows) + si * kRows + 16 * sq;
-            VecLoad<float, 16>::run(Sbuf, e, p.sc);
+        if constexpr (FULL && !TRAP) if (8 * sq <= si) {
+            const int e = (c * a.G + hg) * (kRows * kRows) + si * kRows + 8 * sq;
+            VecLoad<float, 8>::run(Sbuf, e, p.sc);
         }
         const int o = (t0g + lane) * a.H + h;
         p.ld = lane < QT ? bload<float>(vw.ld, o) : 0.0f;
@@ -443,8 +456,22 @@ __global__ __launch_bounds__(kThreads) void k_walk(Args a) {
         }
     };
 
+    // chunk-local angle prefix within this thread's step group, and the group
+    // total for the other groups (read by the next stage, after a barrier)
+    auto angle_prefix = [&](Pre& p) {
+        if constexpr (ROT) {
+            float run = 0.0f;
+#pragma unroll
+            for (int i = 0; i < QSG; ++i) {
+                run += k_ok ? p.th[i] : 0.0f;
+                p.th[i] = run;
+            }
+            if (ssg < NSG) s_tht[ssg * 64 + sk] = run;
+        }
+    };
+
     float seg_acc = 0.0f;   // SO: total log-decay of the segment
-    float rev_acc = 0.0f;   // SO: total angle of pair sk (threads ssg == 3), revolutions mod 1
+    float rev_acc = 0.0f;   // SO: total angle of pair sk (last step group), revolutions mod 1
     float cum_last = 0.0f;
 
     // ---- staging of one chunk from the prefetch registers into LDS ----------
@@ -473,28 +500,21 @@ __global__ __launch_bounds__(kThreads) void k_walk(Args a) {
                 if constexpr (TRAP) s_bet[QT] = 0.0f;
             }
         }
-        // angles: prefix over this thread's QS steps, then over the quad
-        float phi[ROT ? QS : 1];
+        // angles: this thread's local prefix (made before the barrier) plus the
+        // totals of the earlier step groups
+        float phi[ROT ? QSG : 1];
         if constexpr (ROT) {
-            float run = 0.0f;
+            float off = 0.0f;
+            for (int g = 0; g < ssg && g < NSG; ++g) off += s_tht[g * 64 + sk];
 #pragma unroll
-            for (int i = 0; i < QS; ++i) {
-                run += k_ok ? p.th[i] : 0.0f;
-                phi[i] = run;
-            }
-            const float t1 = __shfl_up(run, 1, 4);
-            const float s1 = ssg >= 1 ? t1 : 0.0f;
-            const float t2 = __shfl_up(run + s1, 2, 4);
-            const float off = s1 + (ssg >= 2 ? t2 : 0.0f);
-#pragma unroll
-            for (int i = 0; i < QS; ++i) phi[i] += off;
-            if (ssg == 3 && k_in) {
+            for (int i = 0; i < QSG; ++i) phi[i] = p.th[i] + off;
+            if (ssg == NSG - 1 && k_in) {
                 float sn, cs;
-                sincos_rev(phi[QS - 1], &sn, &cs);
+                sincos_rev(phi[QSG - 1], &sn, &cs);
                 s_dc[sk] = k_ok ? cs : 1.0f;
                 s_ds[sk] = k_ok ? sn : 0.0f;
                 if constexpr (SO) {
-                    rev_acc += phi[QS - 1] * 0.15915494309189535f;
+                    rev_acc += phi[QSG - 1] * 0.15915494309189535f;
                     rev_acc -= rintf(rev_acc);
                 }
             }
@@ -502,8 +522,8 @@ __global__ __launch_bounds__(kThreads) void k_walk(Args a) {
         // B~, C~ rows (t R + r), columns (2 sk, 2 sk + 1)
         if (k_in) {
 #pragma unroll
-            for (int i = 0; i < QS; ++i) {
-                const int t = ssg * QS + i;
+            for (int i = 0; i < QSG; ++i) {
+                const int t = ssg * QSG + i;
                 float cs = 1.0f, sn = 0.0f;
                 if constexpr (ROT) sincos_rev(phi[i], &sn, &cs);
 #pragma unroll
@@ -520,12 +540,12 @@ __global__ __launch_bounds__(kThreads) void k_walk(Args a) {
                     }
                 }
             }
-            if constexpr (TRAP) if (ssg * PR < R) {
+            if constexpr (TRAP) if (ssg * PRG < R) {
 #pragma unroll
-                for (int q = 0; q < PR; ++q) {
-                    const int r = ssg * PR + q;
+                for (int q = 0; q < PRG; ++q) {
+                    const int r = ssg * PRG + q;
                     if (r < R) {
-                        float2 vb = make_float2(p.bp[q], p.bp[PR + q]);
+                        float2 vb = make_float2(p.bp[q], p.bp[PRG + q]);
                         if (!k_ok) vb = make_float2(0.0f, 0.0f);
                         *(float2*)&sB[(kRows + r) * BS + 2 * sk] = vb;
                     }
@@ -533,11 +553,11 @@ __global__ __launch_bounds__(kThreads) void k_walk(Args a) {
             }
         }
         // X^T and the chunk-end-weighted X^T: rows xpl, columns (t R + r)
-        {
-            float xv[QS * R], xd[QS * R];
+        if (x_in) {
+            float xv[QXG * R], xd[QXG * R];
 #pragma unroll
-            for (int i = 0; i < QS; ++i) {
-                const float w = __shfl(wl, xtq * QS + i, 64);
+            for (int i = 0; i < QXG; ++i) {
+                const float w = __shfl(wl, xtq * QXG + i, 64);
 #pragma unroll
                 for (int r = 0; r < R; ++r) {
                     const float v = x_ok ? p.x[i][r] : 0.0f;
@@ -545,16 +565,16 @@ __global__ __launch_bounds__(kThreads) void k_walk(Args a) {
                     xd[i * R + r] = v * w;
                 }
             }
-            const int j0 = xtq * QS * R;   // = 16 xtq
+            const int j0 = xtq * QXG * R;
 #pragma unroll
-            for (int q = 0; q < QS * R; q += 4) {
+            for (int q = 0; q < QXG * R; q += 4) {
                 if constexpr (FULL) *(float4*)&sXT[xpl * JP + j0 + q] = make_float4(xv[q], xv[q + 1], xv[q + 2], xv[q + 3]);
                 *(float4*)&sXdT[xpl * JP + j0 + q] = make_float4(xd[q], xd[q + 1], xd[q + 2], xd[q + 3]);
             }
-            if constexpr (TRAP) if (xtq * PR < R) {
+            if constexpr (TRAP) if (xtq * PRX < R) {
 #pragma unroll
-                for (int q = 0; q < PR; ++q) {
-                    const int r = xtq * PR + q;
+                for (int q = 0; q < PRX; ++q) {
+                    const int r = xtq * PRX + q;
                     if (r < R) {
                         const float v = x_ok ? p.xp[q] : 0.0f;
                         if constexpr (FULL) sXT[xpl * JP + kRows + r] = v;
@@ -566,32 +586,31 @@ __global__ __launch_bounds__(kThreads) void k_walk(Args a) {
         // Mamba-2: masked scores M[i][j] = S[i][j] e^{cum_i - cum_j}, j <= i
         if constexpr (FULL && !TRAP) {
             const float cum_i = __shfl(cum, si, 64);
-            float mv[16];
+            float mv[8];
 #pragma unroll
-            for (int q = 0; q < 16; ++q) {
-                const int j = 16 * sq + q;
+            for (int q = 0; q < 8; ++q) {
+                const int j = 8 * sq + q;
                 const float cum_j = __shfl(cum, j, 64);
                 const bool ok = j <= si;
                 const float e = exp_e(ok ? cum_i - cum_j : 0.0f);
                 mv[q] = ok ? p.sc[q] * e : 0.0f;
             }
-#pragma unroll
-            for (int q = 0; q < 16; q += 4)
-                *(float4*)&sM[si * JP + 16 * sq + q] = make_float4(mv[q], mv[q + 1], mv[q + 2], mv[q + 3]);
+            *(float4*)&sM[si * JP + 8 * sq] = make_float4(mv[0], mv[1], mv[2], mv[3]);
+            *(float4*)&sM[si * JP + 8 * sq + 4] = make_float4(mv[4], mv[5], mv[6], mv[7]);
         }
     };
 
     // ---- state ----------------------------------------------------------------
-    floatx4 acc_h[NT];
+    floatx4 acc_h[NT2];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) acc_h[t] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int t = 0; t < NT2; ++t) acc_h[t] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
     if constexpr (FULL) if (active) {
         if (a.h0) {
 #pragma unroll
-            for (int t = 0; t < NT; ++t)
+            for (int t = 0; t < NT2; ++t)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int n = state_row<NP>(t, r, lk);
+                    const int n = state_row<NP>(t, r, lk, nh);
                     acc_h[t][r] = n < a.N ? a.h0[sh_off + (size_t)n * a.P + pcol] : 0.0f;
                 }
         }
@@ -601,10 +620,10 @@ __global__ __launch_bounds__(kThreads) void k_walk(Args a) {
             const float d = exp_e(a.seg_ld[u]);
             if constexpr (ROT) {
 #pragma unroll
-                for (int t = 0; t < NT; t += 2)
+                for (int t = 0; t < NT2; t += 2)
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        const int n = state_row<NP>(t, r, lk);
+                        const int n = state_row<NP>(t, r, lk, nh);
                         const float rev = n < a.N ? a.seg_rev[u * (a.N / 2) + n / 2] : 0.0f;
                         const float sn = __builtin_amdgcn_sinf(rev), cs = __builtin_amdgcn_cosf(rev);
                         const float v0 = acc_h[t][r], v1 = acc_h[t + 1][r];
@@ -613,10 +632,10 @@ __global__ __launch_bounds__(kThreads) void k_walk(Args a) {
                     }
             }
 #pragma unroll
-            for (int t = 0; t < NT; ++t)
+            for (int t = 0; t < NT2; ++t)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int n = state_row<NP>(t, r, lk);
+                    const int n = state_row<NP>(t, r, lk, nh);
                     const float hl = n < a.N ? a.seg_h[(u * a.N + n) * a.P + pcol] : 0.0f;
                     acc_h[t][r] = fmaf(d, acc_h[t][r], hl);
                 }
@@ -624,22 +643,27 @@ __global__ __launch_bounds__(kThreads) void k_walk(Args a) {
     }
 
     Pre pre;
-    if (c_begin < c_end) prefetch(c_begin, pre);
+    if (c_begin < c_end) {
+        prefetch(c_begin, pre);
+        angle_prefix(pre);
+    }
 
     for (int c = c_begin; c < c_end; ++c) {
         const int t0g = c * QT;
         __syncthreads();                 // the previous chunk's LDS reads are done
         stage(pre);
-        if (c + 1 < c_end) prefetch(c + 1, pre);
+        if constexpr (SO) {
+            if (c + 1 < c_end) prefetch(c + 1, pre);
+        }
         __syncthreads();
         if constexpr (SO) seg_acc += cum_last;
 
-        floatx4 acc_y[4];
         if constexpr (FULL) {
+            floatx4 acc_y[4];
             // ---- Mamba-3: weighted scores M = w o (C~ B~^T) -> LDS ---------------
             if constexpr (TRAP) {
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
+                for (int q = 0; q < 2; ++q) {
                     const int code = kTrapTiles[wave][q];
                     if (code < 0) break;
                     const int it = code >> 4, jt = code & 15;
@@ -676,35 +700,44 @@ __global__ __launch_bounds__(kThreads) void k_walk(Args a) {
                     }
                 }
             }
-            // ---- Y^T = H^T C~^T, scaled by e^{cum} per output row ---------------
+            // ---- partial Y^T = H^T C~^T over this wave's state rows ---------------
             if (active) {
 #pragma unroll
                 for (int it = 0; it < 4; ++it) {
                     floatx4 y0 = {0.0f, 0.0f, 0.0f, 0.0f}, y1 = {0.0f, 0.0f, 0.0f, 0.0f};
-                    const float* pc = sC + (16 * it + li) * BS + 16 * lk;
+                    const float* pc = sC + (16 * it + li) * BS + (NP / 2) * nh + (NP / 8) * lk;
 #pragma unroll
-                    for (int hf = 0; hf < NH; ++hf)
+                    for (int q4 = 0; q4 < NP / 32; ++q4) {
+                        // columns 4 q4 .. 4 q4 + 3 of the lane group's slice: s = NT2 r + t
+                        const float4 cv = *(const float4*)(pc + 4 * q4);
+                        const float cvs[4] = {cv.x, cv.y, cv.z, cv.w};
 #pragma unroll
-                        for (int qq = 0; qq < 4; ++qq) {
-                            const float4 cv = *(const float4*)(pc + 64 * hf + 4 * qq);
-                            y0 = mfma4(acc_h[4 * hf + 0][qq], cv.x, y0);
-                            y1 = mfma4(acc_h[4 * hf + 1][qq], cv.y, y1);
-                            y0 = mfma4(acc_h[4 * hf + 2][qq], cv.z, y0);
-                            y1 = mfma4(acc_h[4 * hf + 3][qq], cv.w, y1);
+                        for (int e = 0; e < 4; ++e) {
+                            const int s = 4 * q4 + e;
+                            const int t = s % NT2, r = s / NT2;
+                            if (e % 2 == 0)
+                                y0 = mfma4(acc_h[t][r], cvs[e], y0);
+                            else
+                                y1 = mfma4(acc_h[t][r], cvs[e], y1);
                         }
-                    const float ey = exp_e(s_cum[(16 * it + li) / R + 1]);
-                    acc_y[it] = (y0 + y1) * ey;
+                    }
+                    // the state part carries the row decay e^{cum_i}; the intra part does not
+                    acc_y[it] = (y0 + y1) * exp_e(s_cum[(16 * it + li) / R + 1]);
                 }
             }
+            // the next chunk's operands load while the rest of this chunk computes
+            if (c + 1 < c_end) prefetch(c + 1, pre);
             if constexpr (TRAP) __syncthreads();   // M complete
-            // ---- Y^T += X^T M^T (intra-chunk), then store Y ----------------------
+            // ---- partial Y^T += X^T M^T over half of the column blocks ------------
             if (active) {
-                const float* px = sXT + (16 * wave + li) * JP + 4 * lk;
+                const float* px = sXT + (16 * pw + li) * JP + 4 * lk;
 #pragma unroll
-                for (int jt = 0; jt < 4; ++jt) {
+                for (int jh = 0; jh < 2; ++jh) {
+                    const int jt = 2 * nh + jh;
                     const float4 xv = *(const float4*)(px + 16 * jt);
 #pragma unroll
-                    for (int it = jt; it < 4; ++it) {
+                    for (int it = 0; it < 4; ++it) {
+                        if (it < jt) continue;
                         const float4 mv = *(const float4*)(sM + (16 * it + li) * JP + 16 * jt + 4 * lk);
                         acc_y[it] = mfma4(xv.x, mv.x, acc_y[it]);
                         acc_y[it] = mfma4(xv.y, mv.y, acc_y[it]);
@@ -712,45 +745,69 @@ __global__ __launch_bounds__(kThreads) void k_walk(Args a) {
                         acc_y[it] = mfma4(xv.w, mv.w, acc_y[it]);
                     }
                 }
+                if (nh == 1) {
 #pragma unroll
-                for (int e = 0; e < JX; ++e) {
-                    const float xe = sXT[(16 * wave + li) * JP + kRows + 4 * e + lk];
+                    for (int e = 0; e < JX; ++e) {
+                        const float xe = sXT[(16 * pw + li) * JP + kRows + 4 * e + lk];
+#pragma unroll
+                        for (int it = 0; it < 4; ++it)
+                            acc_y[it] = mfma4(xe, sM[(16 * it + li) * JP + kRows + 4 * e + lk], acc_y[it]);
+                    }
+                }
+            }
+            // ---- H' = e^{cum_last} H + B~^T Xd over this wave's rows ------------------
+            if (active) {
+                const float tot = exp_e(cum_last);
+#pragma unroll
+                for (int t = 0; t < NT2; ++t) acc_h[t] *= tot;
+            }
+            if (active) {
+                // exchange: the upper half writes its partial sums, the lower half adds them
+                if (nh == 1) {
 #pragma unroll
                     for (int it = 0; it < 4; ++it)
-                        acc_y[it] = mfma4(xe, sM[(16 * it + li) * JP + kRows + 4 * e + lk], acc_y[it]);
+                        *(floatx4*)&sYp[((pw * 4 + it) * 64 + lane) * 4] = acc_y[it];
                 }
-                // lane holds Y[i = 16 it + li][p = p0 + 16 w + 4 lk + r]
+            }
+            __syncthreads();
+            if (active && nh == 0) {
 #pragma unroll
                 for (int it = 0; it < 4; ++it) {
+                    const floatx4 o = *(const floatx4*)&sYp[((pw * 4 + it) * 64 + lane) * 4];
+                    const floatx4 y = acc_y[it] + o;
+                    // lane holds Y[i = 16 it + li][p = p0 + 16 pw + 4 lk + r]
                     const int i = 16 * it + li;
                     const int tg = t0g + i / R;
                     if (tg < a.L) {
-                        const int pp = p0 + 16 * wave + 4 * lk;
+                        const int pp = p0 + 16 * pw + 4 * lk;
                         IO* yrow = (IO*)a.Y + (((size_t)b * a.L + tg) * a.H + h) * (size_t)a.P * R;
                         if (R == 1) {
                             if constexpr (sizeof(IO) == 4) {
-                                *(float4*)((float*)yrow + pp) =
-                                    make_float4(acc_y[it][0], acc_y[it][1], acc_y[it][2], acc_y[it][3]);
+                                *(float4*)((float*)yrow + pp) = make_float4(y[0], y[1], y[2], y[3]);
                             } else {
-                                const uint32_t u0 = f32_to_bf16(acc_y[it][0]) | ((uint32_t)f32_to_bf16(acc_y[it][1]) << 16);
-                                const uint32_t u1 = f32_to_bf16(acc_y[it][2]) | ((uint32_t)f32_to_bf16(acc_y[it][3]) << 16);
+                                const uint32_t u0 = f32_to_bf16(y[0]) | ((uint32_t)f32_to_bf16(y[1]) << 16);
+                                const uint32_t u1 = f32_to_bf16(y[2]) | ((uint32_t)f32_to_bf16(y[3]) << 16);
                                 *(uint2*)((bf16*)yrow + pp) = make_uint2(u0, u1);
                             }
                         } else {
 #pragma unroll
-                            for (int r = 0; r < 4; ++r) store_out(&yrow[(size_t)(pp + r) * R + i % R], acc_y[it][r]);
+                            for (int r = 0; r < 4; ++r) store_out(&yrow[(size_t)(pp + r) * R + i % R], y[r]);
                         }
                     }
                 }
             }
+        } else {
+            if (active) {
+                const float tot = exp_e(cum_last);
+#pragma unroll
+                for (int t = 0; t < NT2; ++t) acc_h[t] *= tot;
+            }
         }
 
-        // ---- H' = e^{cum_last} H + B~^T Xd, then back to the physical frame -------
+        // ---- H' += B~^T Xd over this wave's rows, then back to the physical frame --
         if (active) {
-            const float tot = exp_e(cum_last);
-#pragma unroll
-            for (int t = 0; t < NT; ++t) acc_h[t] *= tot;
-            const float* pxd = sXdT + (16 * wave + li) * JP + 16 * lk;
+            const float* pxd = sXdT + (16 * pw + li) * JP + 16 * lk;
+            const float* pb = sB + (NP / 2) * nh + NT2 * li;
 #pragma unroll
             for (int sq4 = 0; sq4 < 4; ++sq4) {
                 const float4 xd = *(const float4*)(pxd + 4 * sq4);
@@ -758,35 +815,41 @@ __global__ __launch_bounds__(kThreads) void k_walk(Args a) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int j = 16 * lk + 4 * sq4 + e;
-#pragma unroll
-                    for (int hf = 0; hf < NH; ++hf) {
-                        const float4 bv = *(const float4*)(sB + j * BS + 64 * hf + 4 * li);
-                        acc_h[4 * hf + 0] = mfma4(bv.x, xds[e], acc_h[4 * hf + 0]);
-                        acc_h[4 * hf + 1] = mfma4(bv.y, xds[e], acc_h[4 * hf + 1]);
-                        acc_h[4 * hf + 2] = mfma4(bv.z, xds[e], acc_h[4 * hf + 2]);
-                        acc_h[4 * hf + 3] = mfma4(bv.w, xds[e], acc_h[4 * hf + 3]);
+                    if constexpr (NT2 == 4) {
+                        const float4 bv = *(const float4*)(pb + j * BS);
+                        acc_h[0] = mfma4(bv.x, xds[e], acc_h[0]);
+                        acc_h[1] = mfma4(bv.y, xds[e], acc_h[1]);
+                        acc_h[2] = mfma4(bv.z, xds[e], acc_h[2]);
+                        acc_h[3] = mfma4(bv.w, xds[e], acc_h[3]);
+                    } else {
+                        const float2 bv = *(const float2*)(pb + j * BS);
+                        acc_h[0] = mfma4(bv.x, xds[e], acc_h[0]);
+                        acc_h[1] = mfma4(bv.y, xds[e], acc_h[1]);
                     }
                 }
             }
 #pragma unroll
             for (int e = 0; e < JX; ++e) {
                 const int j = kRows + 4 * e + lk;
-                const float xd = sXdT[(16 * wave + li) * JP + j];
-#pragma unroll
-                for (int hf = 0; hf < NH; ++hf) {
-                    const float4 bv = *(const float4*)(sB + j * BS + 64 * hf + 4 * li);
-                    acc_h[4 * hf + 0] = mfma4(bv.x, xd, acc_h[4 * hf + 0]);
-                    acc_h[4 * hf + 1] = mfma4(bv.y, xd, acc_h[4 * hf + 1]);
-                    acc_h[4 * hf + 2] = mfma4(bv.z, xd, acc_h[4 * hf + 2]);
-                    acc_h[4 * hf + 3] = mfma4(bv.w, xd, acc_h[4 * hf + 3]);
+                const float xd = sXdT[(16 * pw + li) * JP + j];
+                if constexpr (NT2 == 4) {
+                    const float4 bv = *(const float4*)(pb + j * BS);
+                    acc_h[0] = mfma4(bv.x, xd, acc_h[0]);
+                    acc_h[1] = mfma4(bv.y, xd, acc_h[1]);
+                    acc_h[2] = mfma4(bv.z, xd, acc_h[2]);
+                    acc_h[3] = mfma4(bv.w, xd, acc_h[3]);
+                } else {
+                    const float2 bv = *(const float2*)(pb + j * BS);
+                    acc_h[0] = mfma4(bv.x, xd, acc_h[0]);
+                    acc_h[1] = mfma4(bv.y, xd, acc_h[1]);
                 }
             }
             if constexpr (ROT) {
 #pragma unroll
-                for (int t = 0; t < NT; t += 2)
+                for (int t = 0; t < NT2; t += 2)
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        const int k = state_row<NP>(t, r, lk) >> 1;
+                        const int k = state_row<NP>(t, r, lk, nh) >> 1;
                         const float cs = s_dc[k], sn = s_ds[k];
                         const float v0 = acc_h[t][r], v1 = acc_h[t + 1][r];
                         // R(-phi): (c v0 + s v1, -s v0 + c v1)
@@ -795,6 +858,7 @@ __global__ __launch_bounds__(kThreads) void k_walk(Args a) {
                     }
             }
         }
+        if (c + 1 < c_end) angle_prefix(pre);
     }
 
     // ---- outputs of the walk ------------------------------------------------------
@@ -802,26 +866,26 @@ __global__ __launch_bounds__(kThreads) void k_walk(Args a) {
         const size_t u = (size_t)(b * a.H + h) * (a.nseg - 1) + seg;
         if (active) {
 #pragma unroll
-            for (int t = 0; t < NT; ++t)
+            for (int t = 0; t < NT2; ++t)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int n = state_row<NP>(t, r, lk);
+                    const int n = state_row<NP>(t, r, lk, nh);
                     if (n < a.N) a.seg_h[(u * a.N + n) * a.P + pcol] = acc_h[t][r];
                 }
         }
         if (pg == 0) {
             if (tid == 0) a.seg_ld[u] = seg_acc;
-            if (ROT && ssg == 3 && k_ok) a.seg_rev[u * (a.N / 2) + sk] = rev_acc;
+            if (ROT && ssg == NSG - 1 && k_ok) a.seg_rev[u * (a.N / 2) + sk] = rev_acc;
         }
     } else {
         if (a.h_out && seg == a.nseg - 1 && active) {
 #pragma unroll
-        for (int t = 0; t < NT; ++t)
+            for (int t = 0; t < NT2; ++t)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int n = state_row<NP>(t, r, lk);
-                if (n < a.N) a.h_out[sh_off + (size_t)n * a.P + pcol] = acc_h[t][r];
-            }
+                for (int r = 0; r < 4; ++r) {
+                    const int n = state_row<NP>(t, r, lk, nh);
+                    if (n < a.N) a.h_out[sh_off + (size_t)n * a.P + pcol] = acc_h[t][r];
+                }
         }
     }
 }
@@ -885,12 +949,12 @@ mb_status launch(Args a, int64_t batch, const Plan& pl, char* ws, hipStream_t st
     const int64_t per_seg = batch * a.H * a.npg;
     if (a.nseg > 1) {
         hipLaunchKernelGGL((k_walk<NP, R, TRAP, ROT, GROUPED, IO, true>),
-                           dim3((unsigned)(per_seg * (a.nseg - 1))), dim3(kThreads), 0, stream, a);
+                           dim3((unsigned)(per_seg * (a.nseg - 1))), dim3(kWalkThreads), 0, stream, a);
         mb_status st = check_launch();
         if (st != MB_OK) return st;
     }
     hipLaunchKernelGGL((k_walk<NP, R, TRAP, ROT, GROUPED, IO, false>),
-                       dim3((unsigned)(per_seg * a.nseg)), dim3(kThreads), 0, stream, a);
+                       dim3((unsigned)(per_seg * a.nseg)), dim3(kWalkThreads), 0, stream, a);
     return check_launch();
 }
 
