@@ -66,6 +66,14 @@ __device__ __forceinline__ floatx4 mfma4(float a, float b, floatx4 c) {
 
 __device__ __forceinline__ float exp_e(float v) { return exp2_fast(v * kLog2e); }
 
+// Wait until at most N vector memory operations of this wave are outstanding
+// (s_waitcnt vmcnt(N), other counters unconstrained).
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+    static_assert(N >= 0 && N < 16, "vmcnt field");
+    __builtin_amdgcn_s_waitcnt(N | (7 << 4) | (15 << 8));
+}
+
 // sin / cos of an angle in radians through the hardware units, which take the
 // argument in revolutions; the fraction of a revolution is taken first so the
 // argument stays in [-0.5, 0.5].
@@ -317,7 +325,6 @@ __global__ __launch_bounds__(kWalkThreads) void k_walk(Args a) {
     using Gm = Geo<R, TRAP>;
     constexpr int QT = Gm::QT, EXTRA = Gm::EXTRA, JX = Gm::JX;
     constexpr int JC = Gm::JC, JP = Gm::JP;
-    constexpr int BS = NP + 4;      // LDS row stride of B~ / C~ (4 mod 32 floats)
     constexpr int NT2 = NP / 32;    // state tiles per wave
     constexpr int KQ = NP / 4;      // contraction slice over the state per lane group (scores)
     constexpr int NSG = QT < 8 ? QT : 8;       // step groups (one per wave) of the B / C / angle staging
@@ -327,8 +334,19 @@ __global__ __launch_bounds__(kWalkThreads) void k_walk(Args a) {
     constexpr int QXG = QT / NXG;
     constexpr int PRX = (R + NXG - 1) / NXG;
     constexpr bool FULL = !SO;
+    // Mamba-2 fp32: B and C rows need no rotation and are copied from global
+    // memory straight into LDS (asynchronous LDS DMA), unpadded, with the
+    // 16-byte column groups of row j XOR-swizzled by j % 8 so that the MFMA
+    // operand reads stay free of bank conflicts.
+    constexpr bool DMA = FULL && !TRAP && !ROT && sizeof(IO) == 4;
+    constexpr int BS = DMA ? NP : NP + 4;   // LDS row stride of B~ / C~
 
     __shared__ __attribute__((aligned(16))) float sB[Gm::BR * BS];
+    // float offset of element (row j, state n) of sB / sC
+    auto bcx = [](int j, int n) {
+        if constexpr (DMA) return j * NP + ((((n >> 2) ^ (j & 7))) << 2) + (n & 3);
+        else return j * BS + n;
+    };
     __shared__ __attribute__((aligned(16))) float sC[FULL ? kRows * BS : 4];
     __shared__ __attribute__((aligned(16))) float sXT[FULL ? kPG * JP : 4];
     __shared__ __attribute__((aligned(16))) float sXdT[kPG * JP];
@@ -415,9 +433,30 @@ __global__ __launch_bounds__(kWalkThreads) void k_walk(Args a) {
         ? make_buf(a.S + (size_t)b * a.nch * a.G * (kRows * kRows), (size_t)a.nch * a.G * kRows * kRows * 4)
         : make_buf(a.ld, 0);
 
+    // LDS DMA of the 64 rows of B or C of chunk c: 1 KB per wave instruction,
+    // lane l filling 16 bytes at dst + 256 q + 4 l (swizzled position) from the
+    // matching global column group; groups at or past N are left as zero.
+    constexpr int kDmaPerWave = DMA ? kRows * NP / 256 / 8 : 1;
+    auto dma_rows = [&](const Buf& src, float* dst, int c) {
+        if constexpr (DMA) {
+            const int t0g = c * QT;
+#pragma unroll
+            for (int m = 0; m < kDmaPerWave; ++m) {
+                const int q = wave + 8 * m;
+                const int f = 256 * q + 4 * lane;           // physical float offset
+                const int j = f / NP, gp = (f % NP) >> 2;   // row, physical group
+                const int g = gp ^ (j & 7);                 // global column group
+                const int e = (t0g + j) * vw.bc_step + vw.bc_head + 4 * g;
+                if (4 * g < a.N)
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                        src.r, (__attribute__((address_space(3))) void*)(dst + 256 * q), 16, e * 4, 0, 0, 0);
+            }
+        }
+    };
+
     auto prefetch = [&](int c, Pre& p) {
         const int t0g = c * QT;
-        if (k_ok) {
+        if (!DMA && k_ok) {
 #pragma unroll
             for (int i = 0; i < QSG; ++i) {
                 const int e = (t0g + ssg * QSG + i) * vw.bc_step + vw.bc_head + 2 * sk * R;
@@ -520,7 +559,7 @@ __global__ __launch_bounds__(kWalkThreads) void k_walk(Args a) {
             }
         }
         // B~, C~ rows (t R + r), columns (2 sk, 2 sk + 1)
-        if (k_in) {
+        if (!DMA && k_in) {
 #pragma unroll
             for (int i = 0; i < QSG; ++i) {
                 const int t = ssg * QSG + i;
@@ -642,19 +681,32 @@ __global__ __launch_bounds__(kWalkThreads) void k_walk(Args a) {
         }
     }
 
+    if constexpr (DMA) {
+        // column groups at or past N are never copied: keep them zero
+        if (a.N < NP) {
+            for (int e = tid; e < kRows * NP; e += kWalkThreads) {
+                sB[e] = 0.0f;
+                sC[e] = 0.0f;
+            }
+            __syncthreads();
+        }
+    }
     Pre pre;
     if (c_begin < c_end) {
         prefetch(c_begin, pre);
         angle_prefix(pre);
+        dma_rows(vw.C, sC, c_begin);
     }
 
     for (int c = c_begin; c < c_end; ++c) {
         const int t0g = c * QT;
         __syncthreads();                 // the previous chunk's LDS reads are done
+        dma_rows(vw.B, sB, c);           // B of this chunk: needed by the state update
         stage(pre);
         if constexpr (SO) {
             if (c + 1 < c_end) prefetch(c + 1, pre);
         }
+        if constexpr (DMA) vm_wait<kDmaPerWave>();   // C of this chunk has arrived
         __syncthreads();
         if constexpr (SO) seg_acc += cum_last;
 
@@ -705,11 +757,10 @@ __global__ __launch_bounds__(kWalkThreads) void k_walk(Args a) {
 #pragma unroll
                 for (int it = 0; it < 4; ++it) {
                     floatx4 y0 = {0.0f, 0.0f, 0.0f, 0.0f}, y1 = {0.0f, 0.0f, 0.0f, 0.0f};
-                    const float* pc = sC + (16 * it + li) * BS + (NP / 2) * nh + (NP / 8) * lk;
 #pragma unroll
                     for (int q4 = 0; q4 < NP / 32; ++q4) {
                         // columns 4 q4 .. 4 q4 + 3 of the lane group's slice: s = NT2 r + t
-                        const float4 cv = *(const float4*)(pc + 4 * q4);
+                        const float4 cv = *(const float4*)(sC + bcx(16 * it + li, (NP / 2) * nh + (NP / 8) * lk + 4 * q4));
                         const float cvs[4] = {cv.x, cv.y, cv.z, cv.w};
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
@@ -769,7 +820,10 @@ __global__ __launch_bounds__(kWalkThreads) void k_walk(Args a) {
                         *(floatx4*)&sYp[((pw * 4 + it) * 64 + lane) * 4] = acc_y[it];
                 }
             }
+            if constexpr (DMA) vm_wait<0>();   // B of this chunk has arrived
             __syncthreads();
+            // C~ of this chunk is no longer read: copy in the next chunk's
+            if (c + 1 < c_end) dma_rows(vw.C, sC, c + 1);
             if (active && nh == 0) {
 #pragma unroll
                 for (int it = 0; it < 4; ++it) {
@@ -807,7 +861,7 @@ __global__ __launch_bounds__(kWalkThreads) void k_walk(Args a) {
         // ---- H' += B~^T Xd over this wave's rows, then back to the physical frame --
         if (active) {
             const float* pxd = sXdT + (16 * pw + li) * JP + 16 * lk;
-            const float* pb = sB + (NP / 2) * nh + NT2 * li;
+            const int nb = (NP / 2) * nh + NT2 * li;   // first state row of this lane's tiles
 #pragma unroll
             for (int sq4 = 0; sq4 < 4; ++sq4) {
                 const float4 xd = *(const float4*)(pxd + 4 * sq4);
@@ -816,13 +870,13 @@ __global__ __launch_bounds__(kWalkThreads) void k_walk(Args a) {
                 for (int e = 0; e < 4; ++e) {
                     const int j = 16 * lk + 4 * sq4 + e;
                     if constexpr (NT2 == 4) {
-                        const float4 bv = *(const float4*)(pb + j * BS);
+                        const float4 bv = *(const float4*)(sB + bcx(j, nb));
                         acc_h[0] = mfma4(bv.x, xds[e], acc_h[0]);
                         acc_h[1] = mfma4(bv.y, xds[e], acc_h[1]);
                         acc_h[2] = mfma4(bv.z, xds[e], acc_h[2]);
                         acc_h[3] = mfma4(bv.w, xds[e], acc_h[3]);
                     } else {
-                        const float2 bv = *(const float2*)(pb + j * BS);
+                        const float2 bv = *(const float2*)(sB + bcx(j, nb));
                         acc_h[0] = mfma4(bv.x, xds[e], acc_h[0]);
                         acc_h[1] = mfma4(bv.y, xds[e], acc_h[1]);
                     }
@@ -833,13 +887,13 @@ __global__ __launch_bounds__(kWalkThreads) void k_walk(Args a) {
                 const int j = kRows + 4 * e + lk;
                 const float xd = sXdT[(16 * pw + li) * JP + j];
                 if constexpr (NT2 == 4) {
-                    const float4 bv = *(const float4*)(pb + j * BS);
+                    const float4 bv = *(const float4*)(sB + bcx(j, nb));
                     acc_h[0] = mfma4(bv.x, xd, acc_h[0]);
                     acc_h[1] = mfma4(bv.y, xd, acc_h[1]);
                     acc_h[2] = mfma4(bv.z, xd, acc_h[2]);
                     acc_h[3] = mfma4(bv.w, xd, acc_h[3]);
                 } else {
-                    const float2 bv = *(const float2*)(pb + j * BS);
+                    const float2 bv = *(const float2*)(sB + bcx(j, nb));
                     acc_h[0] = mfma4(bv.x, xd, acc_h[0]);
                     acc_h[1] = mfma4(bv.y, xd, acc_h[1]);
                 }
