@@ -243,7 +243,9 @@ struct Views {
 // ---------------------------------------------------------------------------
 // Mamba-2 scores S = C B^T per (batch, chunk, group): 64 x 64, contraction over
 // the state.  Only the causal blocks (column block <= row block) are computed;
-// the walk never reads the others.
+// the walk never reads the others.  Stored in blocks of 8 columns: element
+// (i, j) at (j / 8) * 512 + i * 8 + j % 8, so a row's 8 columns of one block
+// are 32 contiguous bytes.
 // ---------------------------------------------------------------------------
 template <int NP, typename IO>
 __global__ __launch_bounds__(kThreads) void k_scores(Args a) {
@@ -290,7 +292,7 @@ __global__ __launch_bounds__(kThreads) void k_scores(Args a) {
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-            Sout[(16 * it + 4 * lk + r) * kRows + 16 * jt + li] = acc0[r] + acc1[r];
+            Sout[((16 * jt + li) / 8) * (kRows * 8) + (16 * it + 4 * lk + r) * 8 + (li % 8)] = acc0[r] + acc1[r];
     }
 }
 
@@ -334,19 +336,11 @@ __global__ __launch_bounds__(kWalkThreads) void k_walk(Args a) {
     constexpr int QXG = QT / NXG;
     constexpr int PRX = (R + NXG - 1) / NXG;
     constexpr bool FULL = !SO;
-    // Mamba-2 fp32: B and C rows need no rotation and are copied from global
-    // memory straight into LDS (asynchronous LDS DMA), unpadded, with the
-    // 16-byte column groups of row j XOR-swizzled by j % 8 so that the MFMA
-    // operand reads stay free of bank conflicts.
-    constexpr bool DMA = FULL && !TRAP && !ROT && sizeof(IO) == 4;
-    constexpr int BS = DMA ? NP : NP + 4;   // LDS row stride of B~ / C~
+    constexpr int BS = NP + 4;      // LDS row stride of B~ / C~ (4 mod 32 floats)
 
     __shared__ __attribute__((aligned(16))) float sB[Gm::BR * BS];
     // float offset of element (row j, state n) of sB / sC
-    auto bcx = [](int j, int n) {
-        if constexpr (DMA) return j * NP + ((((n >> 2) ^ (j & 7))) << 2) + (n & 3);
-        else return j * BS + n;
-    };
+    auto bcx = [](int j, int n) { return j * BS + n; };
     __shared__ __attribute__((aligned(16))) float sC[FULL ? kRows * BS : 4];
     __shared__ __attribute__((aligned(16))) float sXT[FULL ? kPG * JP : 4];
     __shared__ __attribute__((aligned(16))) float sXdT[kPG * JP];
@@ -433,30 +427,9 @@ __global__ __launch_bounds__(kWalkThreads) void k_walk(Args a) {
         ? make_buf(a.S + (size_t)b * a.nch * a.G * (kRows * kRows), (size_t)a.nch * a.G * kRows * kRows * 4)
         : make_buf(a.ld, 0);
 
-    // LDS DMA of the 64 rows of B or C of chunk c: 1 KB per wave instruction,
-    // lane l filling 16 bytes at dst + 256 q + 4 l (swizzled position) from the
-    // matching global column group; groups at or past N are left as zero.
-    constexpr int kDmaPerWave = DMA ? kRows * NP / 256 / 8 : 1;
-    auto dma_rows = [&](const Buf& src, float* dst, int c) {
-        if constexpr (DMA) {
-            const int t0g = c * QT;
-#pragma unroll
-            for (int m = 0; m < kDmaPerWave; ++m) {
-                const int q = wave + 8 * m;
-                const int f = 256 * q + 4 * lane;           // physical float offset
-                const int j = f / NP, gp = (f % NP) >> 2;   // row, physical group
-                const int g = gp ^ (j & 7);                 // global column group
-                const int e = (t0g + j) * vw.bc_step + vw.bc_head + 4 * g;
-                if (4 * g < a.N)
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                        src.r, (__attribute__((address_space(3))) void*)(dst + 256 * q), 16, e * 4, 0, 0, 0);
-            }
-        }
-    };
-
     auto prefetch = [&](int c, Pre& p) {
         const int t0g = c * QT;
-        if (!DMA && k_ok) {
+        if (k_ok) {
 #pragma unroll
             for (int i = 0; i < QSG; ++i) {
                 const int e = (t0g + ssg * QSG + i) * vw.bc_step + vw.bc_head + 2 * sk * R;
@@ -484,7 +457,7 @@ __global__ __launch_bounds__(kWalkThreads) void k_walk(Args a) {
                                       p.xp);
         }
         if constexpr (FULL && !TRAP) if (8 * sq <= si) {
-            const int e = (c * a.G + hg) * (kRows * kRows) + si * kRows + 8 * sq;
+            const int e = (c * a.G + hg) * (kRows * kRows) + sq * (kRows * 8) + si * 8;
             VecLoad<float, 8>::run(Sbuf, e, p.sc);
         }
         const int o = (t0g + lane) * a.H + h;
@@ -559,7 +532,7 @@ __global__ __launch_bounds__(kWalkThreads) void k_walk(Args a) {
             }
         }
         // B~, C~ rows (t R + r), columns (2 sk, 2 sk + 1)
-        if (!DMA && k_in) {
+        if (k_in) {
 #pragma unroll
             for (int i = 0; i < QSG; ++i) {
                 const int t = ssg * QSG + i;
@@ -681,32 +654,19 @@ __global__ __launch_bounds__(kWalkThreads) void k_walk(Args a) {
         }
     }
 
-    if constexpr (DMA) {
-        // column groups at or past N are never copied: keep them zero
-        if (a.N < NP) {
-            for (int e = tid; e < kRows * NP; e += kWalkThreads) {
-                sB[e] = 0.0f;
-                sC[e] = 0.0f;
-            }
-            __syncthreads();
-        }
-    }
     Pre pre;
     if (c_begin < c_end) {
         prefetch(c_begin, pre);
         angle_prefix(pre);
-        dma_rows(vw.C, sC, c_begin);
     }
 
     for (int c = c_begin; c < c_end; ++c) {
         const int t0g = c * QT;
         __syncthreads();                 // the previous chunk's LDS reads are done
-        dma_rows(vw.B, sB, c);           // B of this chunk: needed by the state update
         stage(pre);
         if constexpr (SO) {
             if (c + 1 < c_end) prefetch(c + 1, pre);
         }
-        if constexpr (DMA) vm_wait<kDmaPerWave>();   // C of this chunk has arrived
         __syncthreads();
         if constexpr (SO) seg_acc += cum_last;
 
@@ -820,10 +780,7 @@ __global__ __launch_bounds__(kWalkThreads) void k_walk(Args a) {
                         *(floatx4*)&sYp[((pw * 4 + it) * 64 + lane) * 4] = acc_y[it];
                 }
             }
-            if constexpr (DMA) vm_wait<0>();   // B of this chunk has arrived
             __syncthreads();
-            // C~ of this chunk is no longer read: copy in the next chunk's
-            if (c + 1 < c_end) dma_rows(vw.C, sC, c + 1);
             if (active && nh == 0) {
 #pragma unroll
                 for (int it = 0; it < 4; ++it) {
@@ -945,6 +902,303 @@ __global__ __launch_bounds__(kWalkThreads) void k_walk(Args a) {
 }
 
 // ---------------------------------------------------------------------------
+// Mamba-2 fp32 walk (full pass).  Same decomposition and state layout as
+// k_walk, specialised for the case with no rotation and no trapezoid:
+//   - B and C go from global memory straight into LDS by LDS DMA (swizzled
+//     rows, see bcx below);
+//   - per chunk only X^T, the chunk-end-weighted X^T (double-buffered) and the
+//     masked scores are staged through registers, in a thread mapping where
+//     lane = time step, so every cross-lane value is a wave-uniform readlane
+//     and the decay prefix is a DPP scan;
+//   - the next chunk is staged right after the output exchange, while the
+//     other wave of the SIMD runs the state update, and each chunk needs two
+//     barriers.
+// Per chunk c (LDS holds C(c), X^T(c), Xd^T(c), M(c), cum(c) at the top):
+//   B DMA(c); prefetch registers (c+1); Y^T partial = H^T C^T (scaled), + X^T M^T;
+//   exchange partials; wait B(c); barrier; C DMA(c+1); store Y(c);
+//   stage (c+1); H = e^{cum_last} H + B^T Xd; wait C(c+1); barrier.
+// ---------------------------------------------------------------------------
+// inclusive prefix sum over the 64 lanes with DPP row shifts and broadcasts
+__device__ __forceinline__ float wave_scan_dpp(float v) {
+#define MB_DPP(ctrl, rmask) \
+    __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), ctrl, rmask, 0xf, false))
+    v += MB_DPP(0x111, 0xf);   // row_shr:1
+    v += MB_DPP(0x112, 0xf);   // row_shr:2
+    v += MB_DPP(0x114, 0xf);   // row_shr:4
+    v += MB_DPP(0x118, 0xf);   // row_shr:8
+    v += MB_DPP(0x142, 0xa);   // row_bcast:15 into rows 1 and 3
+    v += MB_DPP(0x143, 0xc);   // row_bcast:31 into rows 2 and 3
+#undef MB_DPP
+    return v;
+}
+
+__device__ __forceinline__ float readlane_f(float v, int l) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+
+template <int NP>
+__global__ __launch_bounds__(kWalkThreads) void k_walk_m2(Args a) {
+    constexpr int JP = kRows + 4;   // LDS row stride of X^T / Xd^T / M (4 mod 32)
+    constexpr int NT2 = NP / 32;    // state tiles per wave
+    constexpr int kDmaPerWave = kRows * NP / 256 / 8;
+
+    __shared__ __attribute__((aligned(16))) float sB[kRows * NP];
+    __shared__ __attribute__((aligned(16))) float sC[kRows * NP];
+    __shared__ __attribute__((aligned(16))) float sXT[kPG * JP];
+    __shared__ __attribute__((aligned(16))) float sXdT[2][kPG * JP];
+    __shared__ __attribute__((aligned(16))) float sM[kRows * JP];
+    __shared__ __attribute__((aligned(16))) float sYp[4 * 4 * 64 * 4];
+    __shared__ float s_cum[kRows + 1];
+
+    // float offset of element (row j, state n) of sB / sC: 16-byte column
+    // groups of row j XOR-swizzled by j % 8 (conflict-free operand reads)
+    auto bcx = [](int j, int n) { return j * NP + ((((n >> 2) ^ (j & 7))) << 2) + (n & 3); };
+
+    // ---- workgroup -> (batch, segment, head, column group), as k_walk ------------
+    const int gsize = a.H * a.npg;
+    const int ngroups = (int)(gridDim.x / gsize);
+    const int id = blockIdx.x;
+    const int full = ngroups / 8 * 8 * gsize;
+    int grp, wi;
+    if (id < full) {
+        const int x = id % 8, k = id / 8;
+        grp = x + 8 * (k / gsize);
+        wi = k % gsize;
+    } else {
+        grp = id / gsize;
+        wi = id % gsize;
+    }
+    const int b = grp / a.nseg, seg = grp % a.nseg;
+    const int h = wi / a.npg, pg = wi % a.npg;
+    const int hg = h / (a.H / a.G);
+    const int p0 = pg * kPG;
+    const int c_begin = seg * a.cps;
+    const int c_end = min(a.nch, c_begin + a.cps);
+
+    const int tid = threadIdx.x, lane = tid % 64;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
+    const int pw = wave & 3, nh = wave >> 2;
+    const int li = lane % 16, lk = lane / 16;
+    const int pw_n = (min(kPG, a.P - p0)) / 16;
+    const bool active = pw < pw_n;   // uniform
+    const int pcol = p0 + 16 * pw + li;
+    const Views<1, true, float> vw(a, b, h, hg);
+    const size_t sh_off = (size_t)(b * a.H + h) * a.N * a.P;
+    const bool x_ok = p0 + lane < a.P;   // staging: this lane's X column
+    const Buf Sbuf = make_buf(a.S + (size_t)b * a.nch * a.G * (kRows * kRows),
+                              (size_t)a.nch * a.G * kRows * kRows * 4);
+
+    // LDS DMA of the 64 rows of B or C of chunk c: 1 KB per wave instruction,
+    // lane l filling the 16 bytes at dst + 256 q + 4 l (a swizzled position)
+    // from the matching global column group; groups at or past N stay zero.
+    auto dma_rows = [&](const Buf& src, float* dst, int c) {
+        const int t0g = c * kRows;
+#pragma unroll
+        for (int m = 0; m < kDmaPerWave; ++m) {
+            const int q = wave + 8 * m;
+            const int f = 256 * q + 4 * lane;
+            const int j = f / NP, gp = (f % NP) >> 2;
+            const int g = gp ^ (j & 7);
+            const int e = (t0g + j) * vw.bc_step + vw.bc_head + 4 * g;
+            if (4 * g < a.N)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    src.r, (__attribute__((address_space(3))) void*)(dst + 256 * q), 16, e * 4, 0, 0, 0);
+        }
+    };
+
+    // staging registers: X column p0 + lane at steps 8 wave + i; scores row
+    // `lane`, columns 8 wave .. 8 wave + 7; log-decay of step `lane`
+    float px[8], psc[8], pld;
+    auto prefetch = [&](int c) {
+        const int t0g = c * kRows;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            px[i] = x_ok ? bload<float>(vw.X, (t0g + 8 * wave + i) * vw.x_step + vw.x_head + p0 + lane) : 0.0f;
+        if (8 * wave <= lane)
+            VecLoad<float, 8>::run(Sbuf, (c * a.G + hg) * (kRows * kRows) + wave * (kRows * 8) + lane * 8, psc);
+        pld = bload<float>(vw.ld, (t0g + lane) * a.H + h);
+    };
+    float cum_last = 0.0f;   // of the chunk staged last
+    auto stage = [&](int c) {
+        const float cum = wave_scan_dpp(pld);
+        cum_last = readlane_f(cum, kRows - 1);
+        const float wl = exp_e(cum_last - cum);   // chunk-end weight of step `lane`
+        if (wave == 0) {
+            s_cum[lane + 1] = cum;
+            if (lane == 0) s_cum[0] = 0.0f;
+        }
+        float* xd = sXdT[c & 1];
+        float xv[8], xw[8], mv[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int t = 8 * wave + i;
+            xv[i] = px[i];
+            xw[i] = px[i] * readlane_f(wl, t);
+            const float e = exp_e(t <= lane ? cum - readlane_f(cum, t) : 0.0f);
+            mv[i] = t <= lane ? psc[i] * e : 0.0f;
+        }
+        // X^T[p][t] for p = p0 + lane (rows of X^T are columns of X)
+#pragma unroll
+        for (int i = 0; i < 8; i += 4) {
+            *(float4*)&sXT[lane * JP + 8 * wave + i] = make_float4(xv[i], xv[i + 1], xv[i + 2], xv[i + 3]);
+            *(float4*)&xd[lane * JP + 8 * wave + i] = make_float4(xw[i], xw[i + 1], xw[i + 2], xw[i + 3]);
+            *(float4*)&sM[lane * JP + 8 * wave + i] = make_float4(mv[i], mv[i + 1], mv[i + 2], mv[i + 3]);
+        }
+    };
+
+    // ---- entering state (h0 and the earlier segments), as k_walk --------------
+    floatx4 acc_h[NT2];
+#pragma unroll
+    for (int t = 0; t < NT2; ++t) acc_h[t] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+    if (active) {
+        if (a.h0) {
+#pragma unroll
+            for (int t = 0; t < NT2; ++t)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int n = state_row<NP>(t, r, lk, nh);
+                    acc_h[t][r] = n < a.N ? a.h0[sh_off + (size_t)n * a.P + pcol] : 0.0f;
+                }
+        }
+        for (int s2 = 0; s2 < seg; ++s2) {
+            const size_t u = (size_t)(b * a.H + h) * (a.nseg - 1) + s2;
+            const float d = exp_e(a.seg_ld[u]);
+#pragma unroll
+            for (int t = 0; t < NT2; ++t)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int n = state_row<NP>(t, r, lk, nh);
+                    const float hl = n < a.N ? a.seg_h[(u * a.N + n) * a.P + pcol] : 0.0f;
+                    acc_h[t][r] = fmaf(d, acc_h[t][r], hl);
+                }
+        }
+    }
+
+    // ---- first chunk ------------------------------------------------------------
+    if (a.N < NP) {   // column groups at or past N are never copied: keep them zero
+        for (int e = tid; e < kRows * NP; e += kWalkThreads) {
+            sB[e] = 0.0f;
+            sC[e] = 0.0f;
+        }
+        __syncthreads();
+    }
+    if (c_begin < c_end) {
+        dma_rows(vw.C, sC, c_begin);
+        prefetch(c_begin);
+        stage(c_begin);
+    }
+    vm_wait<0>();
+    __syncthreads();
+
+    for (int c = c_begin; c < c_end; ++c) {
+        const int t0g = c * kRows;
+        const float tot = exp_e(cum_last);   // decay over this chunk
+        dma_rows(vw.B, sB, c);
+        if (c + 1 < c_end) prefetch(c + 1);
+
+        // ---- partial Y^T = H^T C^T over this wave's state rows, x e^{cum_i} ---------
+        floatx4 acc_y[4];
+        if (active) {
+#pragma unroll
+            for (int it = 0; it < 4; ++it) {
+                floatx4 y0 = {0.0f, 0.0f, 0.0f, 0.0f}, y1 = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int q4 = 0; q4 < NP / 32; ++q4) {
+                    const float4 cv = *(const float4*)(sC + bcx(16 * it + li, (NP / 2) * nh + (NP / 8) * lk + 4 * q4));
+                    const float cvs[4] = {cv.x, cv.y, cv.z, cv.w};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int s = 4 * q4 + e;
+                        const int t = s % NT2, r = s / NT2;
+                        if (e % 2 == 0)
+                            y0 = mfma4(acc_h[t][r], cvs[e], y0);
+                        else
+                            y1 = mfma4(acc_h[t][r], cvs[e], y1);
+                    }
+                }
+                acc_y[it] = (y0 + y1) * exp_e(s_cum[16 * it + li + 1]);
+            }
+            // ---- partial Y^T += X^T M^T over half of the column blocks --------------
+            const float* pxr = sXT + (16 * pw + li) * JP + 4 * lk;
+#pragma unroll
+            for (int jh = 0; jh < 2; ++jh) {
+                const int jt = 2 * nh + jh;
+                const float4 xv = *(const float4*)(pxr + 16 * jt);
+#pragma unroll
+                for (int it = 0; it < 4; ++it) {
+                    if (it < jt) continue;
+                    const float4 mv = *(const float4*)(sM + (16 * it + li) * JP + 16 * jt + 4 * lk);
+                    acc_y[it] = mfma4(xv.x, mv.x, acc_y[it]);
+                    acc_y[it] = mfma4(xv.y, mv.y, acc_y[it]);
+                    acc_y[it] = mfma4(xv.z, mv.z, acc_y[it]);
+                    acc_y[it] = mfma4(xv.w, mv.w, acc_y[it]);
+                }
+            }
+            if (nh == 1) {
+#pragma unroll
+                for (int it = 0; it < 4; ++it)
+                    *(floatx4*)&sYp[((pw * 4 + it) * 64 + lane) * 4] = acc_y[it];
+            }
+        }
+        vm_wait<0>();       // B of this chunk and the next chunk's registers have arrived
+        __syncthreads();
+        if (c + 1 < c_end) dma_rows(vw.C, sC, c + 1);   // C of this chunk is no longer read
+        if (active && nh == 0) {
+#pragma unroll
+            for (int it = 0; it < 4; ++it) {
+                const floatx4 y = acc_y[it] + *(const floatx4*)&sYp[((pw * 4 + it) * 64 + lane) * 4];
+                const int tg = t0g + 16 * it + li;
+                if (tg < a.L) {
+                    float* yrow = (float*)a.Y + (((size_t)b * a.L + tg) * a.H + h) * (size_t)a.P;
+                    *(float4*)(yrow + p0 + 16 * pw + 4 * lk) = make_float4(y[0], y[1], y[2], y[3]);
+                }
+            }
+        }
+        if (c + 1 < c_end) stage(c + 1);
+
+        // ---- H = e^{cum_last} H + B^T Xd over this wave's rows ---------------------
+        if (active) {
+#pragma unroll
+            for (int t = 0; t < NT2; ++t) acc_h[t] *= tot;
+            const float* pxd = sXdT[c & 1] + (16 * pw + li) * JP + 16 * lk;
+            const int nb = (NP / 2) * nh + NT2 * li;
+#pragma unroll
+            for (int sq4 = 0; sq4 < 4; ++sq4) {
+                const float4 xd = *(const float4*)(pxd + 4 * sq4);
+                const float xds[4] = {xd.x, xd.y, xd.z, xd.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int j = 16 * lk + 4 * sq4 + e;
+                    if constexpr (NT2 == 4) {
+                        const float4 bv = *(const float4*)(sB + bcx(j, nb));
+                        acc_h[0] = mfma4(bv.x, xds[e], acc_h[0]);
+                        acc_h[1] = mfma4(bv.y, xds[e], acc_h[1]);
+                        acc_h[2] = mfma4(bv.z, xds[e], acc_h[2]);
+                        acc_h[3] = mfma4(bv.w, xds[e], acc_h[3]);
+                    } else {
+                        const float2 bv = *(const float2*)(sB + bcx(j, nb));
+                        acc_h[0] = mfma4(bv.x, xds[e], acc_h[0]);
+                        acc_h[1] = mfma4(bv.y, xds[e], acc_h[1]);
+                    }
+                }
+            }
+        }
+        vm_wait<0>();       // C of the next chunk has arrived
+        __syncthreads();
+    }
+
+    if (a.h_out && seg == a.nseg - 1 && active) {
+#pragma unroll
+        for (int t = 0; t < NT2; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int n = state_row<NP>(t, r, lk, nh);
+                if (n < a.N) a.h_out[sh_off + (size_t)n * a.P + pcol] = acc_h[t][r];
+            }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
 struct Plan {
@@ -1007,8 +1261,12 @@ mb_status launch(Args a, int64_t batch, const Plan& pl, char* ws, hipStream_t st
         mb_status st = check_launch();
         if (st != MB_OK) return st;
     }
-    hipLaunchKernelGGL((k_walk<NP, R, TRAP, ROT, GROUPED, IO, false>),
-                       dim3((unsigned)(per_seg * a.nseg)), dim3(kWalkThreads), 0, stream, a);
+    if constexpr (!TRAP && !ROT && sizeof(IO) == 4)
+        hipLaunchKernelGGL((k_walk_m2<NP>), dim3((unsigned)(per_seg * a.nseg)), dim3(kWalkThreads), 0,
+                           stream, a);
+    else
+        hipLaunchKernelGGL((k_walk<NP, R, TRAP, ROT, GROUPED, IO, false>),
+                           dim3((unsigned)(per_seg * a.nseg)), dim3(kWalkThreads), 0, stream, a);
     return check_launch();
 }
 

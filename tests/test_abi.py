@@ -127,10 +127,45 @@ def test_trap_and_mimo_validation(lib):
     assert lib.mb_mimo_ssd(*args, 0, 10, 2, 16, 8, 4, 0, F32, P(FAKE + (1 << 28)), 1 << 30, None) == OK
 
 
+def _a256(v):
+    return (v + 255) // 256 * 256
+
+
+def _plan(batch, L, H, P, R):
+    """Chunks and sequence segments as the library chooses them: 64 rows per
+    chunk, about 768 workgroups of 64 state columns, at least 4 chunks and at
+    most 64 segments."""
+    nch = -(-L // (64 // R))
+    units = batch * H * (-(-P // 64))
+    nseg = max(1, min(-(-768 // units), max(1, nch // 4), 64))
+    cps = -(-nch // nseg)
+    return nch, -(-nch // cps)
+
+
+def _ws(op, batch, L, H, P, G, N, R=1):
+    nch, nseg = _plan(batch, L, H, P, R if op == mb.MB_OP_MIMO_SSD else 1)
+    trap = op != mb.MB_OP_SSD_CHUNKED
+    total = 0 if trap else _a256(batch * nch * G * 64 * 64 * 4)     # Mamba-2 scores
+    nsg = batch * H * (nseg - 1)
+    total += _a256(nsg * N * P * 4) + _a256(nsg * 4)                  # segment states, decays
+    if trap:
+        total += _a256(nsg * (N // 2) * 4)                            # segment angles
+    return total if (nseg > 1 or not trap) else 0
+
+
 def test_workspace_sizes(lib):
-    # scores: batch * chunks * (groups or heads) * 64 rows * columns * 4 bytes
     assert mb.mb_workspace_size(mb.MB_OP_SELECTIVE_SCAN, 8, 2048, 1, 1, 1, 16) == 0
-    assert mb.mb_workspace_size(mb.MB_OP_SSD_CHUNKED, 4, 4096, 24, 64, 1, 128) == 4 * 64 * 1 * 64 * 64 * 4
-    assert mb.mb_workspace_size(mb.MB_OP_TRAP_SSD, 4, 4096, 24, 64, 1, 128) == 4 * 64 * 24 * 64 * 68 * 4
-    assert mb.mb_workspace_size(mb.MB_OP_MIMO_SSD, 2, 8192, 16, 64, 1, 128, 4) == 2 * 512 * 16 * 64 * 68 * 4
+    # Mamba-2 block workload: 8 segments of 8 chunks; scores 4 MiB + 7 segment states
+    assert mb.mb_workspace_size(mb.MB_OP_SSD_CHUNKED, 4, 4096, 24, 64, 1, 128) == \
+        4 * 64 * 64 * 64 * 4 + 4 * 24 * 7 * 128 * 64 * 4 + 2816
+    for args in [(mb.MB_OP_SSD_CHUNKED, 4, 4096, 24, 64, 1, 128), (mb.MB_OP_TRAP_SSD, 4, 4096, 24, 64, 1, 128),
+                 (mb.MB_OP_SSD_CHUNKED, 2, 333, 3, 48, 1, 64), (mb.MB_OP_TRAP_SSD, 1, 2000, 2, 16, 1, 32),
+                 (mb.MB_OP_TRAP_SSD, 2, 130, 4, 16, 2, 128)]:
+        assert mb.mb_workspace_size(*args) == _ws(*args), args
+    for R in (1, 2, 4, 8, 16):
+        args = (mb.MB_OP_MIMO_SSD, 2, 8192, 16, 64, 1, 128, R)
+        assert mb.mb_workspace_size(*args) == _ws(*args), args
+    # short sequences need no segments; the trapezoid then needs no workspace
+    assert mb.mb_workspace_size(mb.MB_OP_TRAP_SSD, 1, 100, 2, 16, 1, 16) == 0
     assert mb.mb_workspace_size(mb.MB_OP_SSD_CHUNKED, 4, 4096, 24, 64, 5, 128) == 0   # invalid G
+    assert mb.mb_workspace_size(mb.MB_OP_MIMO_SSD, 2, 8192, 16, 64, 1, 128, 3) == 0   # invalid R
