@@ -5,158 +5,191 @@
 //     h_t[c,n] = exp(dt_t[c] A[c,n]) h_{t-1}[c,n] + dt_t[c] B_t[n] x_t[c]
 //     y_t[c]   = sum_n C_t[n] h_t[c,n] + Dskip[c] x_t[c]
 //
-// Scan layout.  One workgroup owns 16 channels of one batch row and walks the
-// whole sequence; each of its 16*NPAD lanes owns one (channel, state) chain, so
-// the recurrence needs no cross-lane traffic and 8 batches x 1536 channels fill
-// 768 workgroups (three per compute unit).  Per time tile the workgroup stages
-// dt, dt*x, x (16 channels) and B, C (shared by all channels) in LDS, prefetching
-// the next tile into registers while the current one is computed; each lane
-// writes C_t[n] h_t[c,n] into LDS and the sum over n is done by one thread per
-// (t, c) output.  One hardware exp2 per (t, c, n) element.
+// Scan layout (detailed at k_m1_scan): a workgroup of 64 x ceil(N/4) lanes owns
+// 64 channels of one batch row and walks the whole sequence; each lane keeps
+// four (channel, state) chains in registers.  One hardware exp2 per (t, c, n)
+// element.
 #include "mb_internal.h"
 
 namespace mb {
 namespace {
 
-constexpr int kCW = 16;  // channels per workgroup
+// Buffer resources over one batch row of a tensor: reads at or past the end
+// (including the steps past L of the last tile) return zero.
+struct Buf {
+    __amdgpu_buffer_rsrc_t r;
+};
+__device__ __forceinline__ Buf make_buf(const void* base, size_t bytes) {
+    Buf b;
+    b.r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+    return b;
+}
+__device__ __forceinline__ float bload(const Buf& b, int e, float) {
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(b.r, e * 4, 0, 0));
+}
+__device__ __forceinline__ float bload(const Buf& b, int e, bf16) {
+    return __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(b.r, e * 2, 0, 0) << 16);
+}
 
-template <int NPAD, typename IO>
-__global__ __launch_bounds__(kCW * NPAD) void k_m1_scan(
+// Scan layout.  A workgroup owns 64 channels of one batch row and walks the
+// whole sequence; lane l of wave w holds channel c0 + l and the four states
+// n = 4w .. 4w + 3, so the step's dt and dt*x serve four states and B_t, C_t
+// of the wave's states are the same for all its lanes (one broadcast LDS read
+// each).  Per tile of T steps the waves write their partial sums over their
+// four states to LDS and, after one barrier, sum them per (t, c).
+template <int NW, typename IO>
+__global__ __launch_bounds__(64 * NW) void k_m1_scan(
     const IO* __restrict__ x, const IO* __restrict__ dt, const float* __restrict__ A,
     const IO* __restrict__ Bm, const IO* __restrict__ Cm, const float* __restrict__ Dskip,
-    const float* h0, IO* __restrict__ y, float* h_out, int L, int D, int N, int n_cblk,
-    int n_wg)
+    const float* h0, IO* __restrict__ y, float* h_out, int L, int D, int N, int n_cg)
 {
-    constexpr int NT = kCW * NPAD;      // threads
-    constexpr int T = 256 / NPAD;       // time steps per tile
-    constexpr int XE = T * kCW;         // x / dt elements per tile
-    constexpr int BE = T * NPAD;        // B / C elements per tile
-    constexpr int RX = (XE + NT - 1) / NT;
-    constexpr int RB = (BE + NT - 1) / NT;
-    constexpr int PSTR = NPAD * kCW + kCW;   // s_p stride per time step (bank skew)
+    constexpr int T = 16;           // steps per tile
+    constexpr int NS = 4 * NW;      // states, padded to the waves
+    // B / C tiles [B, C][t][n], one array per buffer parity: separate objects,
+    // so a copy into one never orders the reads of the other
+    __shared__ __attribute__((aligned(16))) float sBC0[2][T][NS];
+    __shared__ __attribute__((aligned(16))) float sBC1[2][T][NS];
+    __shared__ float sY[2][NW][T][64];                                // partial sums over states
 
-    __shared__ float s_dt[2][T][kCW];
-    __shared__ float s_dtx[2][T][kCW];
-    __shared__ float s_x[2][T][kCW];
-    __shared__ float s_B[2][T][NPAD];
-    __shared__ float s_C[2][T][NPAD];
-    __shared__ float s_p[T * PSTR];
+    const int b = blockIdx.x / n_cg, c0 = (blockIdx.x % n_cg) * 64;
+    const int tid = threadIdx.x, lane = tid % 64;
+    const int w = __builtin_amdgcn_readfirstlane(tid / 64);
+    const int c = c0 + lane;
+    const bool cok = c < D;
+    const size_t row = (size_t)L * D;
+    const Buf bx = make_buf(x + (size_t)b * row, row * sizeof(IO));
+    const Buf bdt = make_buf(dt + (size_t)b * row, row * sizeof(IO));
+    const Buf bB = make_buf(Bm + (size_t)b * L * N, (size_t)L * N * sizeof(IO));
+    const Buf bC = make_buf(Cm + (size_t)b * L * N, (size_t)L * N * sizeof(IO));
 
-    // Workgroup -> (batch, channel block).  Workgroups i and i+8 land on the same
-    // XCD, so they take adjacent 16-channel blocks and share 128-byte lines in L2.
-    int wg = blockIdx.x;
-    int full = n_wg / 16 * 16;
-    int logical = wg;
-    if (wg < full) {
-        int g = wg / 16, r = wg % 16;
-        logical = g * 16 + (r % 8) * 2 + r / 8;
+    float A2[4], h[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int n = 4 * w + q;
+        const bool ok = cok && n < N;
+        A2[q] = ok ? A[(size_t)c * N + n] * kLog2e : 0.0f;   // states past N: a = 1, no input
+        h[q] = (ok && h0) ? h0[((size_t)b * D + c) * N + n] : 0.0f;
     }
-    const int b = logical / n_cblk;
-    const int c0 = (logical % n_cblk) * kCW;
+    const float Dv = (cok && Dskip) ? Dskip[c] : 0.0f;   // added by wave 0
 
-    const int tid = threadIdx.x;
-    const int cl = tid % kCW, n = tid / kCW;
-    const int c = c0 + cl;
-    const bool lane_ok = (c < D) && (n < N);
+    // B / C tile staging: thread tid holds element (t, n) = (tid / NS, tid % NS)
+    const int bt = tid / NS, bn = tid % NS;
+    const bool bok = bn < N;
 
-    const float A2 = lane_ok ? A[(size_t)c * N + n] * kLog2e : 0.0f;
-    float h = (lane_ok && h0) ? h0[((size_t)b * D + c) * N + n] : 0.0f;
-    const float Dv = (c < D && Dskip) ? Dskip[c] : 0.0f;
-
-    float px[RX], pdt[RX], pB[RB], pC[RB];
-
-    auto load = [&](int k) {
+    float dt_a[T], x_a[T], dt_b[T], x_b[T];
+    float nB = 0.0f, nC = 0.0f;
+    // fp32: the next tile's B / C go straight into LDS (LDS DMA, one dword per
+    // lane into the wave's 64 consecutive slots); bf16 goes through registers
+    constexpr bool DMA = sizeof(IO) == 4;
+    auto load_bc = [&](int k, float (*dst)[T][NS]) {
         const int t0 = k * T;
-#pragma unroll
-        for (int r = 0; r < RX; ++r) {
-            int e = tid + r * NT;
-            px[r] = 0.0f;
-            pdt[r] = 0.0f;
-            if (e < XE) {
-                int tt = t0 + e / kCW, cc = c0 + e % kCW;
-                if (tt < L && cc < D) {
-                    size_t off = ((size_t)b * L + tt) * D + cc;
-                    px[r] = to_f32(x[off]);
-                    pdt[r] = to_f32(dt[off]);
-                }
+        if constexpr (DMA) {
+            if (bok && t0 + bt < L) {
+                const size_t e = ((size_t)b * L + t0 + bt) * N + bn;
+                __builtin_amdgcn_global_load_lds((const void*)(Bm + e),
+                    (__attribute__((address_space(3))) void*)(&dst[0][0][0] + 64 * w), 4, 0, 0);
+                __builtin_amdgcn_global_load_lds((const void*)(Cm + e),
+                    (__attribute__((address_space(3))) void*)(&dst[1][0][0] + 64 * w), 4, 0, 0);
             }
-        }
-#pragma unroll
-        for (int r = 0; r < RB; ++r) {
-            int e = tid + r * NT;
-            pB[r] = 0.0f;
-            pC[r] = 0.0f;
-            if (e < BE) {
-                int tt = t0 + e / NPAD, nn = e % NPAD;
-                if (tt < L && nn < N) {
-                    size_t off = ((size_t)b * L + tt) * N + nn;
-                    pB[r] = to_f32(Bm[off]);
-                    pC[r] = to_f32(Cm[off]);
-                }
-            }
+        } else {
+            const float lb = bload(bB, (t0 + bt) * N + bn, IO{});
+            const float lc = bload(bC, (t0 + bt) * N + bn, IO{});
+            nB = bok ? lb : 0.0f;
+            nC = bok ? lc : 0.0f;
         }
     };
-    auto stash = [&](int buf) {
-#pragma unroll
-        for (int r = 0; r < RX; ++r) {
-            int e = tid + r * NT;
-            if (e < XE) {
-                int t = e / kCW, cc = e % kCW;
-                s_dt[buf][t][cc] = pdt[r];
-                s_dtx[buf][t][cc] = pdt[r] * px[r];
-                s_x[buf][t][cc] = px[r];
-            }
-        }
-#pragma unroll
-        for (int r = 0; r < RB; ++r) {
-            int e = tid + r * NT;
-            if (e < BE) {
-                int t = e / NPAD, nn = e % NPAD;
-                s_B[buf][t][nn] = pB[r];
-                s_C[buf][t][nn] = pC[r];
-            }
-        }
-    };
-
-    const int ntiles = (L + T - 1) / T;
-    if (ntiles > 0) {
-        load(0);
-        stash(0);
-    }
-    __syncthreads();
-    for (int k = 0; k < ntiles; ++k) {
-        const int buf = k & 1;
-        if (k + 1 < ntiles) load(k + 1);
-        // recurrence: one (channel, state) chain per lane
+    auto load = [&](int k, float* pd, float* px, float (*dst)[T][NS]) {
+        const int t0 = k * T;
+        load_bc(k, dst);
 #pragma unroll
         for (int t = 0; t < T; ++t) {
-            float a = exp2_fast(s_dt[buf][t][cl] * A2);
-            h = fmaf(a, h, s_dtx[buf][t][cl] * s_B[buf][t][n]);
-            s_p[t * PSTR + n * kCW + cl] = s_C[buf][t][n] * h;
+            pd[t] = bload(bdt, (t0 + t) * D + c, IO{});
+            px[t] = bload(bx, (t0 + t) * D + c, IO{});
         }
-        __syncthreads();
-        // y_t[c] = sum_n C h + D x, one output per thread per pass
-        const int t0 = k * T;
-#pragma unroll
-        for (int r = 0; r < (T * kCW + NT - 1) / NT; ++r) {
-            int o = tid + r * NT;
-            if (o < T * kCW) {
-                int t = o / kCW;   // o % kCW == cl because NT is a multiple of kCW
-                int tt = t0 + t;
-                if (tt < L && c < D) {
-                    const float* pp = s_p + t * PSTR + cl;
-                    float acc = 0.0f;
-#pragma unroll
-                    for (int nn = 0; nn < NPAD; ++nn) acc += pp[nn * kCW];
-                    acc = fmaf(Dv, s_x[buf][t][cl], acc);
-                    store_out(&y[((size_t)b * L + tt) * D + c], acc);
-                }
-            }
+    };
+    auto stash_bc = [&](float (*dst)[T][NS]) {
+        if constexpr (!DMA) {
+            dst[0][bt][bn] = nB;
+            dst[1][bt][bn] = nC;
         }
-        if (k + 1 < ntiles) stash(buf ^ 1);
+    };
+    // states at or past N are never copied: their slots stay zero
+    if constexpr (DMA) {
+        for (int e = tid; e < 2 * T * NS; e += 64 * NW) {
+            (&sBC0[0][0][0])[e] = 0.0f;
+            (&sBC1[0][0][0])[e] = 0.0f;
+        }
         __syncthreads();
     }
-    if (h_out && lane_ok) h_out[((size_t)b * D + c) * N + n] = h;
+    const int ntiles = (L + T - 1) / T;
+
+    // one tile: T recurrence steps on this lane's four states, partial sums to
+    // LDS, the next tile's B / C staged, one barrier, then the sums per (t, c)
+    auto tile = [&](int k, const float* pd, const float* px, float* nd, float* nx,
+                    float (*cur)[T][NS], float (*nxt)[T][NS]) {
+        const int buf = k & 1;
+        // unconditional (tiles past the end read zeros) and pinned here, so the
+        // next tile's loads stay a full tile ahead of their use
+        load(k + 1, nd, nx, nxt);
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("" ::: "memory");
+        // all of the tile's B / C for this wave's states first (broadcast reads),
+        // so the LDS latency is paid once per tile rather than once per step
+        float4 bqs[T], cqs[T];
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+            bqs[t] = *(const float4*)&cur[0][t][4 * w];
+            cqs[t] = *(const float4*)&cur[1][t][4 * w];
+        }
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+            const float4 bq = bqs[t];
+            const float4 cq = cqs[t];
+            const float dtv = pd[t];
+            const float dtx = dtv * px[t];
+            h[0] = fmaf(exp2_fast(dtv * A2[0]), h[0], dtx * bq.x);
+            h[1] = fmaf(exp2_fast(dtv * A2[1]), h[1], dtx * bq.y);
+            h[2] = fmaf(exp2_fast(dtv * A2[2]), h[2], dtx * bq.z);
+            h[3] = fmaf(exp2_fast(dtv * A2[3]), h[3], dtx * bq.w);
+            float p = fmaf(cq.x, h[0], fmaf(cq.y, h[1], fmaf(cq.z, h[2], cq.w * h[3])));
+            if (w == 0) p = fmaf(Dv, px[t], p);
+            sY[buf][w][t][lane] = p;
+        }
+        if (k + 1 < ntiles) stash_bc(nxt);
+        if constexpr (DMA) {
+            // the next tile's B / C copies were issued before its 2T dt / x loads
+            __builtin_amdgcn_s_waitcnt(((2 * T) & 15) | (((2 * T) >> 4) << 14) | (7 << 4) | (15 << 8));
+        }
+        __syncthreads();
+        const int t0 = k * T;
+#pragma unroll
+        for (int t = w; t < T; t += NW) {
+            float s = 0.0f;
+#pragma unroll
+            for (int v = 0; v < NW; ++v) s += sY[buf][v][t][lane];
+            if (cok && t0 + t < L) store_out(&y[((size_t)b * L + t0 + t) * D + c], s);
+        }
+    };
+
+    if (ntiles > 0) {
+        load(0, dt_a, x_a, sBC0);
+        stash_bc(sBC0);
+    }
+    // everything loaded so far (initial state, first tile) has arrived: the
+    // waits inside the loop then only cover the tile loads in flight
+    __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
+    __syncthreads();
+    for (int k = 0; k < ntiles; k += 2) {
+        tile(k, dt_a, x_a, dt_b, x_b, sBC0, sBC1);
+        if (k + 1 < ntiles) tile(k + 1, dt_b, x_b, dt_a, x_a, sBC1, sBC0);
+    }
+    if (h_out && cok) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int n = 4 * w + q;
+            if (n < N) h_out[((size_t)b * D + c) * N + n] = h[q];
+        }
+    }
 }
 
 // Decode step, N a multiple of 4 with N/4 dividing 64: one lane per
@@ -233,18 +266,22 @@ mb_status launch_scan(const void* x, const void* dt, const float* A, const void*
                       float* h_out, int64_t batch, int64_t L, int64_t D, int64_t N,
                       hipStream_t stream)
 {
-    const int n_cblk = (int)((D + kCW - 1) / kCW);
-    const int n_wg = (int)(batch * n_cblk);
-#define MB_SCAN_LAUNCH(NP)                                                                    \
-    hipLaunchKernelGGL((k_m1_scan<NP, IO>), dim3(n_wg), dim3(kCW * NP), 0, stream,            \
+    const int n_cg = (int)((D + 63) / 64);
+    const int n_wg = (int)(batch * n_cg);
+#define MB_SCAN_LAUNCH(NW)                                                                    \
+    hipLaunchKernelGGL((k_m1_scan<NW, IO>), dim3(n_wg), dim3(64 * NW), 0, stream,             \
                        (const IO*)x, (const IO*)dt, A, (const IO*)B, (const IO*)C, Dskip, h0, \
-                       (IO*)y, h_out, (int)L, (int)D, (int)N, n_cblk, n_wg)
-    if (N <= 16)
-        MB_SCAN_LAUNCH(16);
+                       (IO*)y, h_out, (int)L, (int)D, (int)N, n_cg)
+    if (N <= 4)
+        MB_SCAN_LAUNCH(1);
+    else if (N <= 8)
+        MB_SCAN_LAUNCH(2);
+    else if (N <= 16)
+        MB_SCAN_LAUNCH(4);
     else if (N <= 32)
-        MB_SCAN_LAUNCH(32);
+        MB_SCAN_LAUNCH(8);
     else
-        MB_SCAN_LAUNCH(64);
+        MB_SCAN_LAUNCH(16);
 #undef MB_SCAN_LAUNCH
     return check_launch();
 }
@@ -299,7 +336,9 @@ extern "C" mb_status mb_selective_scan(const void* x, const void* dt, const floa
     const size_t es = dtype_size(dtype);
     const size_t n_x = (size_t)(batch * L * D), n_b = (size_t)(batch * L * N);
     const size_t n_h = (size_t)(batch * D * N);
-    if (batch * ((D + kCW - 1) / kCW) > INT32_MAX) return MB_ERR_SHAPE;
+    if (batch * ((D + 63) / 64) > INT32_MAX) return MB_ERR_SHAPE;
+    // one batch row is addressed with 32-bit byte offsets (tile padding included)
+    if ((L + 16) * D * 4 >= ((int64_t)1 << 31) || (L + 16) * N * 4 >= ((int64_t)1 << 31)) return MB_ERR_SHAPE;
     if (n_x && (!x || !dt || !y)) return MB_ERR_NULL;
     if (n_b && (!B || !C)) return MB_ERR_NULL;
     if (D > 0 && !A) return MB_ERR_NULL;
