@@ -58,7 +58,7 @@ constexpr int kRows = 64;      // rows per chunk (time steps x ranks)
 constexpr int kPG = 64;        // state / output columns per walk workgroup
 constexpr int kNMax = 128;     // largest supported state size
 constexpr int kThreads = 256;
-constexpr int kTargetWG = 768; // segments are chosen to give about this many workgroups
+constexpr int kCUs = 256;       // compute units of an MI355X (segment planning only)
 
 __device__ __forceinline__ floatx4 mfma4(float a, float b, floatx4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
@@ -1217,13 +1217,26 @@ Plan make_plan(bool trap, int64_t R, int64_t batch, int64_t L, int64_t H, int64_
     p.nch = (L + QT - 1) / QT;
     p.npg = (P + kPG - 1) / kPG;
     const int64_t units = batch * H * p.npg;
-    int64_t want = units > 0 ? (kTargetWG + units - 1) / units : 1;
-    int64_t maxseg = p.nch / 4;
-    if (maxseg < 1) maxseg = 1;
-    int64_t ns = want < maxseg ? want : maxseg;
-    if (ns > 64) ns = 64;
-    if (ns < 1) ns = 1;
-    p.cps = p.nch > 0 ? (p.nch + ns - 1) / ns : 1;
+    // Segment count: minimise an estimate of the walk time on 256 compute units,
+    // with one full-pass workgroup and two state-only workgroups per unit, a
+    // state-only chunk costing about 0.45 of a full one and every workgroup a
+    // start-up of about two chunks; at least 4 chunks per segment.  Depends on
+    // the sizes only, so mb_workspace_size agrees.
+    int64_t best = 1;
+    double best_cost = -1.0;
+    for (int64_t ns = 1; ns <= 64; ++ns) {
+        if (ns > 1 && p.nch / ns < 4) break;
+        const int64_t cps = p.nch > 0 ? (p.nch + ns - 1) / ns : 1;
+        const int64_t nse = p.nch > 0 ? (p.nch + cps - 1) / cps : 1;
+        const double full_rounds = (double)((nse * units + kCUs - 1) / kCUs);
+        const double so_rounds = (double)(((nse - 1) * units + 2 * kCUs - 1) / (2 * kCUs));
+        const double cost = (full_rounds + 0.45 * so_rounds) * (double)(cps + 2);
+        if (best_cost < 0.0 || cost < best_cost - 1e-9) {
+            best_cost = cost;
+            best = ns;
+        }
+    }
+    p.cps = p.nch > 0 ? (p.nch + best - 1) / best : 1;
     p.nseg = p.nch > 0 ? (p.nch + p.cps - 1) / p.cps : 1;
     size_t off = 0;
     if (!trap) off = align256((size_t)(batch * p.nch * G) * kRows * kRows * 4);

@@ -133,12 +133,21 @@ def _a256(v):
 
 def _plan(batch, L, H, P, R):
     """Chunks and sequence segments as the library chooses them: 64 rows per
-    chunk, about 768 workgroups of 64 state columns, at least 4 chunks and at
-    most 64 segments."""
+    chunk; the segment count minimises (full-pass rounds + 0.45 state-only
+    rounds) x (chunks per segment + 2) on 256 compute units, with at least 4
+    chunks per segment and at most 64 segments."""
     nch = -(-L // (64 // R))
     units = batch * H * (-(-P // 64))
-    nseg = max(1, min(-(-768 // units), max(1, nch // 4), 64))
-    cps = -(-nch // nseg)
+    best, best_cost = 1, None
+    for ns in range(1, 65):
+        if ns > 1 and nch // ns < 4:
+            break
+        cps = -(-nch // ns)
+        nse = -(-nch // cps)
+        cost = (-(-(nse * units) // 256) + 0.45 * (-(-((nse - 1) * units) // 512))) * (cps + 2)
+        if best_cost is None or cost < best_cost - 1e-9:
+            best, best_cost = ns, cost
+    cps = -(-nch // best)
     return nch, -(-nch // cps)
 
 
