@@ -164,9 +164,9 @@ def _ws(op, batch, L, H, P, G, N, R=1):
 
 def test_workspace_sizes(lib):
     assert mb.mb_workspace_size(mb.MB_OP_SELECTIVE_SCAN, 8, 2048, 1, 1, 1, 16) == 0
-    # Mamba-2 block workload: 8 segments of 8 chunks; scores 4 MiB + 7 segment states
+    # Mamba-2 block workload: 5 segments of 13 chunks; scores 4 MiB + 4 segment states
     assert mb.mb_workspace_size(mb.MB_OP_SSD_CHUNKED, 4, 4096, 24, 64, 1, 128) == \
-        4 * 64 * 64 * 64 * 4 + 4 * 24 * 7 * 128 * 64 * 4 + 2816
+        4 * 64 * 64 * 64 * 4 + 4 * 24 * 4 * 128 * 64 * 4 + 1536
     for args in [(mb.MB_OP_SSD_CHUNKED, 4, 4096, 24, 64, 1, 128), (mb.MB_OP_TRAP_SSD, 4, 4096, 24, 64, 1, 128),
                  (mb.MB_OP_SSD_CHUNKED, 2, 333, 3, 48, 1, 64), (mb.MB_OP_TRAP_SSD, 1, 2000, 2, 16, 1, 32),
                  (mb.MB_OP_TRAP_SSD, 2, 130, 4, 16, 2, 128)]:
