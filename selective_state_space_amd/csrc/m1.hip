@@ -193,45 +193,80 @@ __global__ __launch_bounds__(64 * NW) void k_m1_scan(
 }
 
 // Decode step, N a multiple of 4 with N/4 dividing 64: one lane per
-// (batch, channel, group of 4 states); 16-byte state loads, so consecutive lanes
-// read consecutive 16-byte pieces of the state.  The sum over n is a butterfly
-// over the N/4 lanes of a channel.
-template <int NQ, typename IO>
+// (channel, group of 4 states) of one batch row (grid y = batch, so no
+// division by D); 16-byte state loads and stores, streamed past the caches,
+// so consecutive lanes move consecutive 16-byte pieces of the state.  The sum
+// over n is a butterfly over the N/4 lanes of a channel (DPP within quads).
+typedef float f4v __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float xor_lanes(float v, int m) {
+    if (m == 1) return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));
+    if (m == 2) return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true));
+    return __shfl_xor(v, m, 64);
+}
+
+// Each thread handles K (channel, state-quad) items 256 apart, all loads first,
+// so a wave keeps K 16-byte state loads in flight (h_out may alias h_in).
+template <int NQ, typename IO, bool VEC_BC, int K>
 __global__ __launch_bounds__(256) void k_m1_step_q(
     const IO* __restrict__ x, const IO* __restrict__ dt, const float* __restrict__ A,
     const IO* __restrict__ Bm, const IO* __restrict__ Cm, const float* __restrict__ Dskip,
-    const float* h_in, float* h_out, IO* __restrict__ y, int64_t total, int D)
+    const float* h_in, float* h_out, IO* __restrict__ y, int D)
 {
     constexpr int N = NQ * 4;
-    int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (gid >= total) return;
-    const int q = (int)(gid % NQ);
-    const int64_t bc = gid / NQ;
-    const int64_t b = bc / D;
-    const int c = (int)(bc % D);
-    const float xv = to_f32(x[bc]);
-    const float dtv = to_f32(dt[bc]);
-    const float4 hv = *reinterpret_cast<const float4*>(h_in + bc * N + 4 * q);
-    const float4 av = *reinterpret_cast<const float4*>(A + (size_t)c * N + 4 * q);
+    const int b = blockIdx.y;
+    int c[K], q[K];
+    bool ok[K];
+    size_t bc[K];
+    float xv[K], dtv[K];
+    f4v hv[K];
+    float4 av[K];
     float bv[4], cv[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        bv[i] = to_f32(Bm[b * N + 4 * q + i]);
-        cv[i] = to_f32(Cm[b * N + 4 * q + i]);
+    for (int k = 0; k < K; ++k) {
+        const int idx = (blockIdx.x * K + k) * 256 + threadIdx.x;
+        c[k] = idx / NQ;
+        q[k] = idx % NQ;
+        ok[k] = c[k] < D;                 // lanes past D compute on channel 0, store nothing
+        const int cc = ok[k] ? c[k] : 0;
+        bc[k] = (size_t)b * D + cc;
+        xv[k] = to_f32(x[bc[k]]);
+        dtv[k] = to_f32(dt[bc[k]]);
+        hv[k] = __builtin_nontemporal_load(reinterpret_cast<const f4v*>(h_in + bc[k] * N + 4 * q[k]));
+        av[k] = *reinterpret_cast<const float4*>(A + (size_t)cc * N + 4 * q[k]);
     }
-    const float dtx = dtv * xv;
-    float4 hn;
-    hn.x = fmaf(exp2_fast(dtv * av.x * kLog2e), hv.x, dtx * bv[0]);
-    hn.y = fmaf(exp2_fast(dtv * av.y * kLog2e), hv.y, dtx * bv[1]);
-    hn.z = fmaf(exp2_fast(dtv * av.z * kLog2e), hv.z, dtx * bv[2]);
-    hn.w = fmaf(exp2_fast(dtv * av.w * kLog2e), hv.w, dtx * bv[3]);
-    float p = cv[0] * hn.x + cv[1] * hn.y + cv[2] * hn.z + cv[3] * hn.w;
+    // B and C of this batch row: the state quad of item k is q[k] = threadIdx.x % NQ for all k
+    const int qq = threadIdx.x % NQ;
+    if constexpr (VEC_BC) {
+        const float4 b4 = *reinterpret_cast<const float4*>((const float*)Bm + (size_t)b * N + 4 * qq);
+        const float4 c4 = *reinterpret_cast<const float4*>((const float*)Cm + (size_t)b * N + 4 * qq);
+        bv[0] = b4.x; bv[1] = b4.y; bv[2] = b4.z; bv[3] = b4.w;
+        cv[0] = c4.x; cv[1] = c4.y; cv[2] = c4.z; cv[3] = c4.w;
+    } else {
 #pragma unroll
-    for (int m = 1; m < NQ; m <<= 1) p += __shfl_xor(p, m, 64);
-    *reinterpret_cast<float4*>(h_out + bc * N + 4 * q) = hn;
-    if (q == 0) {
-        float dv = Dskip ? Dskip[c] : 0.0f;
-        store_out(&y[bc], fmaf(dv, xv, p));
+        for (int i = 0; i < 4; ++i) {
+            bv[i] = to_f32(Bm[(size_t)b * N + 4 * qq + i]);
+            cv[i] = to_f32(Cm[(size_t)b * N + 4 * qq + i]);
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        const float dtx = dtv[k] * xv[k];
+        f4v hn;
+        hn.x = fmaf(exp2_fast(dtv[k] * av[k].x * kLog2e), hv[k].x, dtx * bv[0]);
+        hn.y = fmaf(exp2_fast(dtv[k] * av[k].y * kLog2e), hv[k].y, dtx * bv[1]);
+        hn.z = fmaf(exp2_fast(dtv[k] * av[k].z * kLog2e), hv[k].z, dtx * bv[2]);
+        hn.w = fmaf(exp2_fast(dtv[k] * av[k].w * kLog2e), hv[k].w, dtx * bv[3]);
+        float p = cv[0] * hn.x + cv[1] * hn.y + cv[2] * hn.z + cv[3] * hn.w;
+#pragma unroll
+        for (int m = 1; m < NQ; m <<= 1) p += xor_lanes(p, m);   // all lanes take part
+        if (ok[k]) {
+            __builtin_nontemporal_store(hn, reinterpret_cast<f4v*>(h_out + bc[k] * N + 4 * q[k]));
+            if (q[k] == 0) {
+                const float dv = Dskip ? Dskip[c[k]] : 0.0f;
+                store_out(&y[bc[k]], fmaf(dv, xv[k], p));
+            }
+        }
     }
 }
 
@@ -293,23 +328,28 @@ mb_status launch_step(const void* x, const void* dt, const float* A, const void*
 {
     const int64_t bcs = batch * D;
     const bool aligned = (((uintptr_t)h_in | (uintptr_t)h_out | (uintptr_t)A) & 15) == 0;
+    const bool vec_bc = sizeof(IO) == 4 && ((((uintptr_t)B | (uintptr_t)C) & 15) == 0);
 #define MB_STEP_Q(NQ)                                                                         \
     do {                                                                                     \
-        int64_t total = bcs * NQ;                                                            \
-        hipLaunchKernelGGL((k_m1_step_q<NQ, IO>), dim3((unsigned)((total + 255) / 256)),      \
-                           dim3(256), 0, stream, (const IO*)x, (const IO*)dt, A,             \
-                           (const IO*)B, (const IO*)C, Dskip, h_in, h_out, (IO*)y, total,    \
-                           (int)D);                                                          \
+        const dim3 grid((unsigned)((D * NQ + 511) / 512), (unsigned)batch);                  \
+        if (vec_bc)                                                                          \
+            hipLaunchKernelGGL((k_m1_step_q<NQ, IO, true, 2>), grid, dim3(256), 0, stream,   \
+                               (const IO*)x, (const IO*)dt, A, (const IO*)B, (const IO*)C,   \
+                               Dskip, h_in, h_out, (IO*)y, (int)D);                          \
+        else                                                                                 \
+            hipLaunchKernelGGL((k_m1_step_q<NQ, IO, false, 2>), grid, dim3(256), 0, stream,  \
+                               (const IO*)x, (const IO*)dt, A, (const IO*)B, (const IO*)C,   \
+                               Dskip, h_in, h_out, (IO*)y, (int)D);                          \
     } while (0)
-    if (aligned && N == 16)
+    if (aligned && N == 16 && batch <= 65535)
         MB_STEP_Q(4);
-    else if (aligned && N == 8)
+    else if (aligned && N == 8 && batch <= 65535)
         MB_STEP_Q(2);
-    else if (aligned && N == 4)
+    else if (aligned && N == 4 && batch <= 65535)
         MB_STEP_Q(1);
-    else if (aligned && N == 32)
+    else if (aligned && N == 32 && batch <= 65535)
         MB_STEP_Q(8);
-    else if (aligned && N == 64)
+    else if (aligned && N == 64 && batch <= 65535)
         MB_STEP_Q(16);
     else
         hipLaunchKernelGGL((k_m1_step_any<IO>), dim3((unsigned)((bcs + 255) / 256)), dim3(256),
