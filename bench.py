@@ -314,6 +314,42 @@ def cpu_baseline(ws):
             "cores": threads, "kind": "oracle", "sample": "; ".join(parts)}
 
 
+_FLUSH = []
+
+
+def cold_ms(torch, w, reps=5):
+    """Median time of one call of workload w after overwriting a 512 MiB buffer,
+    which evicts the 256 MB last-level cache: every input comes from HBM."""
+    if not _FLUSH:
+        _FLUSH.append(torch.empty(128 << 20, dtype=torch.float32, device="cuda"))
+    buf = _FLUSH[0]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ms = []
+    for r in range(reps):
+        buf.fill_(float(r))
+        e0.record()
+        w.run()
+        e1.record()
+        torch.cuda.synchronize()
+        ms.append(e0.elapsed_time(e1))
+    return float(np.median(ms))
+
+
+def copy_calibration(torch, reps=5):
+    """A plain device-to-device copy of 256 MiB, repeated: the reference that the
+    rocprofv3 FETCH_SIZE / WRITE_SIZE counters are scaled by."""
+    n = 64 << 20
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read_per_call": n * 4, "copy_bytes_written_per_call": n * 4,
+                      "calls": reps}))
+    return 0
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -321,6 +357,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--only", default="")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-cold", action="store_true",
+                    help="skip the per-workload timings after a last-level-cache flush")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 256 MiB device copy (reference for rocprofv3 byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU; this library has no multi-GPU path (run with --gpus 1)",
@@ -334,6 +374,8 @@ def main():
     if not torch.cuda.is_available():
         print("no GPU available", file=sys.stderr)
         return 2
+    if args.copy_calibration:
+        return copy_calibration(torch)
     mb.load_library()
     names = [n for n in (args.only.split(",") if args.only else ALL) if n]
     ws = []
@@ -382,6 +424,13 @@ def main():
     roof = {"bound": r["bound"], "achieved": round(r["achieved"], 3), "peak": r["peak"],
             "unit": r["unit"], "frac": round(r["frac"], 4), "traffic": traffic_for(w),
             "kernel": w.kernel, "workload": w.name}
+
+    if not args.no_cold:
+        print("# cold timings (last-level cache flushed before each call)", file=sys.stderr, flush=True)
+        for w, d in zip(ws, kernels):
+            cms = cold_ms(torch, w)
+            d["cold_ms"] = round(cms, 5)
+            d["cold_hbm_frac"] = round(w.bytes / (cms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
 
     out = {
         "metric": "scanned tokens/sec, SSD fwd L=4096 + M1 scan; % MFMA / % HBM roofline",
