@@ -144,7 +144,7 @@ class M1Step(Workload):
 
 
 class SSD(Workload):
-    kernel = "k_scores + k_walk"
+    kernel = "k_scores + k_walk (state-only pass) + k_walk_m2 (full pass)"
     source = "selective_state_space_amd/csrc/ssd.hip"
     bound = "mfma"
 
@@ -169,6 +169,7 @@ class SSD(Workload):
         self.dtype = dtype
         if dtype == "bf16":
             self.bound = "hbm"
+            self.kernel = "k_scores + k_walk (state-only pass) + k_walk (full pass)"
 
     def run(self):
         self.mb.mb_ssd_chunked(self.X, self.ld, self.B, self.C, None, Y=self.Y, h_out=self.h, ws=self.ws)
@@ -176,7 +177,7 @@ class SSD(Workload):
 
 class SISO(Workload):
     name = "siso"
-    kernel = "k_scores + k_walk"
+    kernel = "k_walk (state-only pass) + k_walk (full pass)"
     source = "selective_state_space_amd/csrc/ssd.hip"
     bound = "mfma"
 
@@ -204,7 +205,7 @@ class SISO(Workload):
 
 class MIMO(Workload):
     name = "mimo"
-    kernel = "k_scores + k_walk"
+    kernel = "k_walk (state-only pass) + k_walk (full pass)"
     source = "selective_state_space_amd/csrc/ssd.hip"
     bound = "mfma"
 
