@@ -192,6 +192,230 @@ __global__ __launch_bounds__(64 * NW) void k_m1_scan(
     }
 }
 
+// Scan layout for fp32 with N = 4 S, S in {1, 2, 4, 8}: one wave per (batch,
+// 16 channels), nothing shared between waves and no barriers; a workgroup is
+// four such waves (64 channels), so that its waves sit on the four SIMDs of one
+// compute unit.  Lane l
+// holds channel c0 + l / 4 and the S states n = S (l % 4) + s.  Tiles of T
+// steps of dt and x (the wave's 16 channels) and of B and C (all N states) go
+// global -> LDS by LDS DMA one tile ahead, into two separate buffers.  Per step
+// a lane updates its S chains and sums C.h over them; the four lanes of a
+// channel are summed per group of four steps by a two-stage exchange inside
+// the quad, after which lane q holds step 4i + q, so one store writes four
+// steps of the wave's 16 channels.  Every store is issued by the whole wave
+// (lanes past D store to an offset that the buffer range check drops), so the
+// number of memory operations issued after a tile's DMA is fixed and the wait
+// for that DMA is exact.
+constexpr int kScanT = 32;   // steps per tile
+
+// one tile in LDS: dt[T][16], x[T][16], B[T][N], C[T][N]
+template <int S>
+struct ScanTile {
+    float v[kScanT * (32 + 8 * S)];
+};
+
+// s_waitcnt vmcnt(N), other counters unconstrained
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+    static_assert(N >= 0 && N < 64, "vmcnt field");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+typedef __attribute__((address_space(3))) float lds_f;
+typedef __attribute__((address_space(3))) const float lds_cf;
+typedef float fv2 __attribute__((ext_vector_type(2)));
+typedef float fv4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) const fv2 lds_cf2;
+typedef __attribute__((address_space(3))) const fv4 lds_cf4;
+
+template <int S>
+__device__ __forceinline__ void lds_row(lds_cf* p, float* o) {
+    if constexpr (S == 1) {
+        o[0] = p[0];
+    } else if constexpr (S == 2) {
+        const fv2 v = *(lds_cf2*)p;
+        o[0] = v.x;
+        o[1] = v.y;
+    } else {
+#pragma unroll
+        for (int i = 0; i < S; i += 4) {
+            const fv4 v = *(lds_cf4*)(p + i);
+            o[i] = v.x;
+            o[i + 1] = v.y;
+            o[i + 2] = v.z;
+            o[i + 3] = v.w;
+        }
+    }
+}
+
+template <int CTRL>
+__device__ __forceinline__ float quad_swap(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+
+// LDS DMA of W bytes per lane: lane l's piece lands at dst + W l bytes
+template <int W>
+__device__ __forceinline__ void dma_lds(const Buf& src, lds_f* dst, uint32_t off) {
+    static_assert(W == 4 || W == 16, "copy width");
+    if constexpr (W == 16)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(src.r, (__attribute__((address_space(3))) void*)dst, 16, off, 0, 0, 0);
+    else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(src.r, (__attribute__((address_space(3))) void*)dst, 4, off, 0, 0, 0);
+}
+
+template <int S, bool V16>
+__global__ __launch_bounds__(256) void k_m1_scan_w(
+    const float* __restrict__ x, const float* __restrict__ dt, const float* __restrict__ A,
+    const float* __restrict__ Bm, const float* __restrict__ Cm, const float* __restrict__ Dskip,
+    const float* h0, float* y, float* h_out, int L, int D, int n_cg)
+{
+    constexpr int T = kScanT;
+    constexpr int N = 4 * S;
+    constexpr int NG = T / 4;                   // groups of four steps per tile
+    constexpr bool BC16 = (T * N) % 256 == 0;   // 16-byte copies for the B / C tile
+    constexpr int XW = V16 ? 16 : 4;            // bytes per lane of a dt / x copy
+    constexpr int BW = BC16 ? 16 : 4;
+    constexpr int NDX = T * 16 * 4 / (64 * XW); // copies per dt / x tile
+    constexpr int NDB = T * N * 4 / (64 * BW);  // copies per B / C tile
+    constexpr int NDMA = 2 * NDX + 2 * NDB;     // copies per tile
+    constexpr int OX = T * 16, OB = 2 * T * 16, OC = 2 * T * 16 + T * N;   // offsets in a tile
+    // three tile buffers, separate objects so that a copy into one never orders
+    // the reads of another
+    __shared__ __attribute__((aligned(16))) ScanTile<S> tb0[4];
+    __shared__ __attribute__((aligned(16))) ScanTile<S> tb1[4];
+    __shared__ __attribute__((aligned(16))) ScanTile<S> tb2[4];
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
+    lds_f* const p0 = (lds_f*)tb0[w].v;
+    lds_f* const p1 = (lds_f*)tb1[w].v;
+    lds_f* const p2 = (lds_f*)tb2[w].v;
+
+    const int b = blockIdx.x / n_cg, c0 = (blockIdx.x % n_cg) * 64 + 16 * w;
+    const int lane = threadIdx.x % 64;
+    const int cl = lane >> 2, q = lane & 3;
+    const int c = c0 + cl;
+    const bool cok = c < D;
+    const size_t row = (size_t)L * D;
+    const Buf bx = make_buf(x + (size_t)b * row, row * 4);
+    const Buf bdt = make_buf(dt + (size_t)b * row, row * 4);
+    const Buf bB = make_buf(Bm + (size_t)b * L * N, (size_t)L * N * 4);
+    const Buf bC = make_buf(Cm + (size_t)b * L * N, (size_t)L * N * 4);
+    const Buf by = make_buf(y + (size_t)b * row, row * 4);
+
+    // byte offset of this lane's piece of a tile copy, relative to the tile's first
+    // step.  Tiles at or past the end read zeros (offsets past the buffer).
+    const uint32_t xo = V16 ? (uint32_t)(((lane >> 2) * D + c0 + 4 * (lane & 3)) * 4)
+                            : (uint32_t)(((lane >> 4) * D + c0 + (lane & 15)) * 4);
+    const uint32_t bo = (uint32_t)(BW * lane);
+    auto dma = [&](int k, lds_f* dst) __attribute__((always_inline)) {
+        const int t0 = k * T;
+#pragma unroll
+        for (int m = 0; m < NDX; ++m) {
+            const uint32_t off = xo + (uint32_t)((t0 + XW * m) * D) * 4u;   // XW steps per copy
+            dma_lds<XW>(bdt, dst + 16 * XW * m, off);
+            dma_lds<XW>(bx, dst + OX + 16 * XW * m, off);
+        }
+#pragma unroll
+        for (int m = 0; m < NDB; ++m) {
+            const uint32_t off = bo + (uint32_t)(t0 * N + 16 * BW * m) * 4u;
+            dma_lds<BW>(bB, dst + OB + 16 * BW * m, off);
+            dma_lds<BW>(bC, dst + OC + 16 * BW * m, off);
+        }
+    };
+
+    // the operands of four steps, read from LDS one group ahead of their use
+    struct Grp {
+        float dt[4], x[4], b[4][S], c[4][S];
+        float xs;   // x of step 4i + q (skip term)
+    };
+    auto read_grp = [&](lds_cf* cur, int i, Grp& g) __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int t = 4 * i + j;
+            g.dt[j] = cur[t * 16 + cl];
+            g.x[j] = cur[OX + t * 16 + cl];
+            lds_row<S>(cur + OB + t * N + S * q, g.b[j]);
+            lds_row<S>(cur + OC + t * N + S * q, g.c[j]);
+        }
+        g.xs = cur[OX + (4 * i + q) * 16 + cl];
+    };
+
+    float A2[S], h[S];
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+        const int n = S * q + s;
+        A2[s] = cok ? A[(size_t)c * N + n] * kLog2e : 0.0f;
+        h[s] = (cok && h0) ? h0[((size_t)b * D + c) * N + n] : 0.0f;
+    }
+    const float Dv = (cok && Dskip) ? Dskip[c] : 0.0f;
+    const bool lo = (q & 2) == 0, ev = (q & 1) == 0;
+
+    const int ntiles = (L + T - 1) / T;
+    Grp g;
+    dma(0, p0);
+    vm_wait<0>();         // tile 0 (and the initial state) has arrived
+    asm volatile("" ::: "memory");
+    dma(1, p1);
+    read_grp(p0, 0, g);
+
+    // tile k: copies of tile k + 2 go out first; the operands of its groups are
+    // read one group ahead, the last group reading the first of tile k + 1
+    auto tile = [&](int k, lds_cf* cur, lds_f* nxt, lds_f* nxt2) __attribute__((always_inline)) {
+        dma(k + 2, nxt2);
+        const int t0 = k * T;
+#pragma unroll
+        for (int i = 0; i < NG; ++i) {
+            Grp gn;
+            if (i + 1 < NG) {
+                read_grp(cur, i + 1, gn);
+            } else {
+                // tile k + 1's copies were followed by at most the previous
+                // tile's stores, tile k + 2's copies and this tile's first NG - 1
+                // stores
+                vm_wait<NDMA + NG - 1>();
+                asm volatile("" ::: "memory");
+                read_grp(nxt, 0, gn);
+            }
+            // keep the reads here, a whole group ahead of their use
+            __builtin_amdgcn_sched_barrier(0);
+            float ps[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float dtv = g.dt[j];
+                const float dtx = dtv * g.x[j];
+                float p = 0.0f;
+#pragma unroll
+                for (int s = 0; s < S; ++s) {
+                    h[s] = fmaf(exp2_fast(dtv * A2[s]), h[s], dtx * g.b[j][s]);
+                    p = fmaf(g.c[j][s], h[s], p);
+                }
+                ps[j] = p;
+            }
+            // sum over the quad: after the exchange lane q holds step 4i + q
+            float k0 = lo ? ps[0] : ps[2], s0 = lo ? ps[2] : ps[0];
+            float k1 = lo ? ps[1] : ps[3], s1 = lo ? ps[3] : ps[1];
+            k0 += quad_swap<0x4E>(s0);
+            k1 += quad_swap<0x4E>(s1);
+            float kk = ev ? k0 : k1;
+            const float ss = ev ? k1 : k0;
+            kk += quad_swap<0xB1>(ss);
+            kk = fmaf(Dv, g.xs, kk);
+            const uint32_t off = cok ? (uint32_t)((t0 + 4 * i + q) * D + c) * 4u : 0x80000000u;
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(kk), by.r, off, 0, 0);
+            g = gn;
+        }
+    };
+    for (int k = 0; k < ntiles; k += 3) {
+        tile(k, p0, p1, p2);
+        if (k + 1 < ntiles) tile(k + 1, p1, p2, p0);
+        if (k + 2 < ntiles) tile(k + 2, p2, p0, p1);
+    }
+    vm_wait<0>();   // no copy into LDS may be in flight when the wave ends
+    if (h_out && cok) {
+#pragma unroll
+        for (int s = 0; s < S; ++s) h_out[((size_t)b * D + c) * N + S * q + s] = h[s];
+    }
+}
+
 // Decode step, N a multiple of 4 with N/4 dividing 64: one lane per
 // (channel, group of 4 states) of one batch row (grid y = batch, so no
 // division by D); 16-byte state loads and stores, streamed past the caches,
@@ -301,6 +525,34 @@ mb_status launch_scan(const void* x, const void* dt, const float* A, const void*
                       float* h_out, int64_t batch, int64_t L, int64_t D, int64_t N,
                       hipStream_t stream)
 {
+    if constexpr (sizeof(IO) == 4) {
+        if (N == 4 || N == 8 || N == 16 || N == 32) {
+            const int n_cg = (int)((D + 63) / 64);
+            const int n_wg = (int)(batch * n_cg);
+            const bool v16 = D % 4 == 0;
+#define MB_SCAN_W(S)                                                                          \
+    do {                                                                                     \
+        if (v16)                                                                             \
+            hipLaunchKernelGGL((k_m1_scan_w<S, true>), dim3(n_wg), dim3(256), 0, stream,       \
+                               (const float*)x, (const float*)dt, A, (const float*)B,        \
+                               (const float*)C, Dskip, h0, (float*)y, h_out, (int)L, (int)D, \
+                               n_cg);                                                        \
+        else                                                                                 \
+            hipLaunchKernelGGL((k_m1_scan_w<S, false>), dim3(n_wg), dim3(256), 0, stream,     \
+                               (const float*)x, (const float*)dt, A, (const float*)B,        \
+                               (const float*)C, Dskip, h0, (float*)y, h_out, (int)L, (int)D, \
+                               n_cg);                                                        \
+    } while (0)
+            switch (N) {
+            case 4: MB_SCAN_W(1); break;
+            case 8: MB_SCAN_W(2); break;
+            case 16: MB_SCAN_W(4); break;
+            default: MB_SCAN_W(8); break;
+            }
+#undef MB_SCAN_W
+            return check_launch();
+        }
+    }
     const int n_cg = (int)((D + 63) / 64);
     const int n_wg = (int)(batch * n_cg);
 #define MB_SCAN_LAUNCH(NW)                                                                    \
@@ -378,7 +630,7 @@ extern "C" mb_status mb_selective_scan(const void* x, const void* dt, const floa
     const size_t n_h = (size_t)(batch * D * N);
     if (batch * ((D + 63) / 64) > INT32_MAX) return MB_ERR_SHAPE;
     // one batch row is addressed with 32-bit byte offsets (tile padding included)
-    if ((L + 16) * D * 4 >= ((int64_t)1 << 31) || (L + 16) * N * 4 >= ((int64_t)1 << 31)) return MB_ERR_SHAPE;
+    if ((L + 64) * D * 4 >= ((int64_t)1 << 31) || (L + 64) * N * 4 >= ((int64_t)1 << 31)) return MB_ERR_SHAPE;
     if (n_x && (!x || !dt || !y)) return MB_ERR_NULL;
     if (n_b && (!B || !C)) return MB_ERR_NULL;
     if (D > 0 && !A) return MB_ERR_NULL;

@@ -30,7 +30,8 @@ def test_tiny_workload(oracle_mod):
 
 
 SHAPES = [(1, 1, 1, 1), (2, 17, 5, 3), (1, 64, 16, 4), (2, 130, 33, 16), (3, 77, 40, 17),
-          (1, 50, 20, 33), (2, 40, 18, 64), (1, 300, 64, 16), (2, 1000, 48, 16)]
+          (1, 50, 20, 33), (2, 40, 18, 64), (1, 300, 64, 16), (2, 1000, 48, 16),
+          (2, 97, 30, 8), (1, 161, 52, 32), (1, 95, 7, 4), (2, 33, 16, 16)]
 
 
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
