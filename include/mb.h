@@ -73,7 +73,9 @@ typedef enum {
  *   h0    : (batch, D, N)     fp32      NULL = zeros
  *   y     : (batch, L, D)     dtype     written
  *   h_out : (batch, D, N)     fp32      final state; NULL = not written; may equal h0
- * Supported: 1 <= N <= 64 (MB_ERR_SHAPE otherwise); any D, L, batch >= 0.
+ * Supported: 1 <= N <= 64, and one batch row of x and of B addressed in
+ * 32-bit offsets: (L + 64) * D * 4 < 2^31 and (L + 64) * N * 4 < 2^31
+ * (MB_ERR_SHAPE otherwise); any batch >= 0.
  */
 mb_status mb_selective_scan(const void* x, const void* dt, const float* A,
                             const void* B, const void* C, const float* Dskip,

@@ -73,6 +73,10 @@ def test_scan_validation(lib):
     assert scan(lib, **base, h_out=FAKE + 12288) == E_ALIAS
     # empty batch is a no-op that succeeds without touching the device
     assert scan(lib, **base, batch=0) == OK
+    # one batch row must be addressable in 32-bit byte offsets, tile padding included
+    L_max = (1 << 31) // (4 * 512) - 64        # (L + 64) * D * 4 == 2^31 at D = 512
+    assert scan(lib, **base, L=L_max, Dm=512) == E_SHAPE
+    assert scan(lib, **dict(base, x=0), L=L_max - 1, Dm=512) == E_NULL
 
 
 def step(lib, h_in=FAKE + (1 << 26), h_out=FAKE + (1 << 26), y=FAKE + (1 << 27), **kw):
