@@ -84,13 +84,22 @@ __device__ __forceinline__ void sincos_rev(float phi, float* s, float* c) {
     *c = __builtin_amdgcn_cosf(r);
 }
 
-__device__ __forceinline__ float wave_incl_scan(float v, int lane) {
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        float o = __shfl_up(v, d, 64);
-        if (lane >= d) v += o;
-    }
+// inclusive prefix sum over the 64 lanes with DPP row shifts and broadcasts
+__device__ __forceinline__ float wave_scan_dpp(float v) {
+#define MB_DPP(ctrl, rmask) \
+    __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), ctrl, rmask, 0xf, false))
+    v += MB_DPP(0x111, 0xf);   // row_shr:1
+    v += MB_DPP(0x112, 0xf);   // row_shr:2
+    v += MB_DPP(0x114, 0xf);   // row_shr:4
+    v += MB_DPP(0x118, 0xf);   // row_shr:8
+    v += MB_DPP(0x142, 0xa);   // row_bcast:15 into rows 1 and 3
+    v += MB_DPP(0x143, 0xc);   // row_bcast:31 into rows 2 and 3
+#undef MB_DPP
     return v;
+}
+
+__device__ __forceinline__ float readlane_f(float v, int l) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
 }
 
 // ---------------------------------------------------------------------------
@@ -422,6 +431,7 @@ __global__ __launch_bounds__(kWalkThreads) void k_walk(Args a) {
         float xp[PRX];                // previous step, ranks xtq*PRX + q
         float sc[(FULL && !TRAP) ? 8 : 1];   // Mamba-2 score row si, columns 8 sq ..
         float ld, gam, bet;           // step `lane` of the chunk
+        float ldn, betn;              // step `lane` + 1 (trapezoid only)
     };
     const Buf Sbuf = (FULL && !TRAP)
         ? make_buf(a.S + (size_t)b * a.nch * a.G * (kRows * kRows), (size_t)a.nch * a.G * kRows * kRows * 4)
@@ -465,6 +475,8 @@ __global__ __launch_bounds__(kWalkThreads) void k_walk(Args a) {
         if constexpr (TRAP) {
             p.gam = lane < QT ? bload<float>(vw.gam, o) : 0.0f;
             p.bet = lane < QT ? bload<float>(vw.bet, o) : 0.0f;
+            p.ldn = lane + 1 < QT ? bload<float>(vw.ld, o + a.H) : 0.0f;
+            p.betn = lane + 1 < QT ? bload<float>(vw.bet, o + a.H) : 0.0f;
         }
     };
 
@@ -488,14 +500,13 @@ __global__ __launch_bounds__(kWalkThreads) void k_walk(Args a) {
 
     // ---- staging of one chunk from the prefetch registers into LDS ----------
     auto stage = [&](const Pre& p) {
-        const float cum = wave_incl_scan(p.ld, lane);   // lanes >= QT add zero
-        cum_last = __shfl(cum, QT - 1, 64);
-        const float cum_n = __shfl_down(cum, 1, 64);
+        const float cum = wave_scan_dpp(p.ld);   // lanes >= QT add zero
+        cum_last = readlane_f(cum, QT - 1);
         float wl, wprev = 0.0f;   // chunk-end weights of step `lane` and of the previous step
         if constexpr (TRAP) {
-            const float bet_n = __shfl_down(p.bet, 1, 64);
-            wl = p.gam * exp_e(cum_last - cum) + (lane + 1 < QT ? bet_n * exp_e(cum_last - cum_n) : 0.0f);
-            wprev = __shfl(p.bet, 0, 64) * exp_e(cum_last - __shfl(cum, 0, 64));
+            const float cum_n = cum + p.ldn;       // cumulative log-decay of step `lane` + 1
+            wl = p.gam * exp_e(cum_last - cum) + (lane + 1 < QT ? p.betn * exp_e(cum_last - cum_n) : 0.0f);
+            wprev = readlane_f(p.bet, 0) * exp_e(cum_last - readlane_f(cum, 0));
         } else {
             wl = exp_e(cum_last - cum);
         }
@@ -569,7 +580,7 @@ __global__ __launch_bounds__(kWalkThreads) void k_walk(Args a) {
             float xv[QXG * R], xd[QXG * R];
 #pragma unroll
             for (int i = 0; i < QXG; ++i) {
-                const float w = __shfl(wl, xtq * QXG + i, 64);
+                const float w = readlane_f(wl, xtq * QXG + i);   // xtq is the wave index
 #pragma unroll
                 for (int r = 0; r < R; ++r) {
                     const float v = x_ok ? p.x[i][r] : 0.0f;
@@ -918,24 +929,6 @@ __global__ __launch_bounds__(kWalkThreads) void k_walk(Args a) {
 //   exchange partials; wait B(c); barrier; C DMA(c+1); store Y(c);
 //   stage (c+1); H = e^{cum_last} H + B^T Xd; wait C(c+1); barrier.
 // ---------------------------------------------------------------------------
-// inclusive prefix sum over the 64 lanes with DPP row shifts and broadcasts
-__device__ __forceinline__ float wave_scan_dpp(float v) {
-#define MB_DPP(ctrl, rmask) \
-    __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), ctrl, rmask, 0xf, false))
-    v += MB_DPP(0x111, 0xf);   // row_shr:1
-    v += MB_DPP(0x112, 0xf);   // row_shr:2
-    v += MB_DPP(0x114, 0xf);   // row_shr:4
-    v += MB_DPP(0x118, 0xf);   // row_shr:8
-    v += MB_DPP(0x142, 0xa);   // row_bcast:15 into rows 1 and 3
-    v += MB_DPP(0x143, 0xc);   // row_bcast:31 into rows 2 and 3
-#undef MB_DPP
-    return v;
-}
-
-__device__ __forceinline__ float readlane_f(float v, int l) {
-    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
-}
-
 template <int NP>
 __global__ __launch_bounds__(kWalkThreads) void k_walk_m2(Args a) {
     constexpr int JP = kRows + 4;   // LDS row stride of X^T / Xd^T / M (4 mod 32)
