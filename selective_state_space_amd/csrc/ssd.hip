@@ -683,69 +683,84 @@ __global__ __launch_bounds__(kWalkThreads) void k_walk(Args a) {
 
         if constexpr (FULL) {
             floatx4 acc_y[4];
-            // ---- Mamba-3: weighted scores M = w o (C~ B~^T) -> LDS ---------------
-            if constexpr (TRAP) {
+            // The two waves of a SIMD (same column group, other state half) take the
+            // score tiles and the state part in opposite orders, so that one
+            // wave's vector work on the score weights meets the other's matrix
+            // instructions.
+            auto score_tiles = [&]() __attribute__((always_inline)) {
+                // ---- Mamba-3: weighted scores M = w o (C~ B~^T) -> LDS ---------------
+                if constexpr (TRAP) {
 #pragma unroll
-                for (int q = 0; q < 2; ++q) {
-                    const int code = kTrapTiles[wave][q];
-                    if (code < 0) break;
-                    const int it = code >> 4, jt = code & 15;
-                    floatx4 s0 = {0.0f, 0.0f, 0.0f, 0.0f}, s1 = {0.0f, 0.0f, 0.0f, 0.0f};
-                    const float* pa = sC + (16 * it + li) * BS + KQ * lk;
-                    const float* pb = sB + (16 * jt + li) * BS + KQ * lk;
+                    for (int q = 0; q < 2; ++q) {
+                        const int code = kTrapTiles[wave][q];
+                        if (code < 0) break;
+                        const int it = code >> 4, jt = code & 15;
+                        floatx4 s0 = {0.0f, 0.0f, 0.0f, 0.0f}, s1 = {0.0f, 0.0f, 0.0f, 0.0f};
+                        const float* pa = sC + (16 * it + li) * BS + KQ * lk;
+                        const float* pb = sB + (16 * jt + li) * BS + KQ * lk;
 #pragma unroll
-                    for (int n = 0; n < KQ; n += 4) {
-                        const float4 av = *(const float4*)(pa + n);
-                        const float4 bv = *(const float4*)(pb + n);
-                        s0 = mfma4(av.x, bv.x, s0);
-                        s1 = mfma4(av.y, bv.y, s1);
-                        s0 = mfma4(av.z, bv.z, s0);
-                        s1 = mfma4(av.w, bv.w, s1);
-                    }
-                    const int j = 16 * jt + li;
-                    const bool colv = jt < 4 || j - kRows < EXTRA;
-                    const int sj = jt < 4 ? j / R : -1;       // step of column j
-                    const float cum_s = s_cum[sj + 1];
-                    const float cum_s1 = s_cum[min(sj + 2, QT)];
-                    const float gam_s = s_gam[sj < 0 ? 0 : sj];
-                    const float bet_s1 = s_bet[sj + 1];
+                        for (int n = 0; n < KQ; n += 4) {
+                            const float4 av = *(const float4*)(pa + n);
+                            const float4 bv = *(const float4*)(pb + n);
+                            s0 = mfma4(av.x, bv.x, s0);
+                            s1 = mfma4(av.y, bv.y, s1);
+                            s0 = mfma4(av.z, bv.z, s0);
+                            s1 = mfma4(av.w, bv.w, s1);
+                        }
+                        const int j = 16 * jt + li;
+                        const bool colv = jt < 4 || j - kRows < EXTRA;
+                        const int sj = jt < 4 ? j / R : -1;       // step of column j
+                        const float cum_s = s_cum[sj + 1];
+                        const float cum_s1 = s_cum[min(sj + 2, QT)];
+                        const float gam_s = s_gam[sj < 0 ? 0 : sj];
+                        const float bet_s1 = s_bet[sj + 1];
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int i = 16 * it + 4 * lk + r;
-                        const int tau = i / R;
-                        const float cum_t = s_cum[tau + 1];
-                        const bool vg = colv && sj >= 0 && sj <= tau;
-                        const bool vb = colv && sj < tau;
-                        const float eg = exp_e(vg ? cum_t - cum_s : 0.0f);
-                        const float eb = exp_e(vb ? cum_t - cum_s1 : 0.0f);
-                        const float w = (vg ? gam_s * eg : 0.0f) + (vb ? bet_s1 * eb : 0.0f);
-                        if (j < JC) sM[i * JP + j] = (s0[r] + s1[r]) * w;
-                    }
-                }
-            }
-            // ---- partial Y^T = H^T C~^T over this wave's state rows ---------------
-            if (active) {
-#pragma unroll
-                for (int it = 0; it < 4; ++it) {
-                    floatx4 y0 = {0.0f, 0.0f, 0.0f, 0.0f}, y1 = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-                    for (int q4 = 0; q4 < NP / 32; ++q4) {
-                        // columns 4 q4 .. 4 q4 + 3 of the lane group's slice: s = NT2 r + t
-                        const float4 cv = *(const float4*)(sC + bcx(16 * it + li, (NP / 2) * nh + (NP / 8) * lk + 4 * q4));
-                        const float cvs[4] = {cv.x, cv.y, cv.z, cv.w};
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const int s = 4 * q4 + e;
-                            const int t = s % NT2, r = s / NT2;
-                            if (e % 2 == 0)
-                                y0 = mfma4(acc_h[t][r], cvs[e], y0);
-                            else
-                                y1 = mfma4(acc_h[t][r], cvs[e], y1);
+                        for (int r = 0; r < 4; ++r) {
+                            const int i = 16 * it + 4 * lk + r;
+                            const int tau = i / R;
+                            const float cum_t = s_cum[tau + 1];
+                            const bool vg = colv && sj >= 0 && sj <= tau;
+                            const bool vb = colv && sj < tau;
+                            const float eg = exp_e(vg ? cum_t - cum_s : 0.0f);
+                            const float eb = exp_e(vb ? cum_t - cum_s1 : 0.0f);
+                            const float w = (vg ? gam_s * eg : 0.0f) + (vb ? bet_s1 * eb : 0.0f);
+                            if (j < JC) sM[i * JP + j] = (s0[r] + s1[r]) * w;
                         }
                     }
-                    // the state part carries the row decay e^{cum_i}; the intra part does not
-                    acc_y[it] = (y0 + y1) * exp_e(s_cum[(16 * it + li) / R + 1]);
                 }
+            };
+            auto state_part = [&]() __attribute__((always_inline)) {
+                // ---- partial Y^T = H^T C~^T over this wave's state rows ---------------
+                if (active) {
+#pragma unroll
+                    for (int it = 0; it < 4; ++it) {
+                        floatx4 y0 = {0.0f, 0.0f, 0.0f, 0.0f}, y1 = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                        for (int q4 = 0; q4 < NP / 32; ++q4) {
+                            // columns 4 q4 .. 4 q4 + 3 of the lane group's slice: s = NT2 r + t
+                            const float4 cv = *(const float4*)(sC + bcx(16 * it + li, (NP / 2) * nh + (NP / 8) * lk + 4 * q4));
+                            const float cvs[4] = {cv.x, cv.y, cv.z, cv.w};
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                const int s = 4 * q4 + e;
+                                const int t = s % NT2, r = s / NT2;
+                                if (e % 2 == 0)
+                                    y0 = mfma4(acc_h[t][r], cvs[e], y0);
+                                else
+                                    y1 = mfma4(acc_h[t][r], cvs[e], y1);
+                            }
+                        }
+                        // the state part carries the row decay e^{cum_i}; the intra part does not
+                        acc_y[it] = (y0 + y1) * exp_e(s_cum[(16 * it + li) / R + 1]);
+                    }
+                }
+            };
+            if (nh == 0) {
+                state_part();
+                score_tiles();
+            } else {
+                score_tiles();
+                state_part();
             }
             // the next chunk's operands load while the rest of this chunk computes
             if (c + 1 < c_end) prefetch(c + 1, pre);
