@@ -16,6 +16,10 @@
 // Per chunk, with H the state entering the chunk (physical frame):
 //     Y   = (w o S) X + diag(e^{cum}) C~ H,      S = C~ B~^T (rows x (rows + R))
 //     H'  = e^{cum_last} H + B~^T diag(w(last, .)) X
+// The full pass of the trapezoid folds the previous step's term into the state
+// first, H+ = alpha_0 H + beta_0 B_{-1}^T x_{-1}, after which it decays with the
+// chunk like the state: Y = (w o S) X + diag(e^{cum - cum_0}) C~ H+ with S only
+// over the chunk's own rows, and H' = e^{cum_last - cum_0} H+ + B~^T diag(w) X.
 // Rotations use chunk-local angles Phi_t = sum_{u<=t in chunk} theta_u, so B~ of
 // the previous step is unrotated; the carried state is rotated back by
 // R(-Phi_last) at the end of every chunk, which keeps it in the physical frame
@@ -326,10 +330,11 @@ __device__ __forceinline__ int state_row(int t, int r, int lk, int nh) {
     return (NP / 2) * nh + (NP / 8) * lk + (NP / 32) * r + t;
 }
 
-// Score tiles (row block << 4 | column block) of the trapezoid per wave;
-// column block 4 holds the previous-step columns; -1 ends a list.
-__constant__ int kTrapTiles[8][2] = {{0x11, 0x00}, {0x04, 0x14}, {0x24, -1}, {0x34, -1},
-                                     {0x30, 0x31}, {0x32, 0x33}, {0x20, 0x21}, {0x22, 0x10}};
+// Causal score tiles (row block << 4 | column block) of the trapezoid per wave,
+// three per SIMD on SIMDs 0 and 1 and two on SIMDs 2 and 3 (waves w and w + 4
+// share SIMD w); -1 ends a list.
+__constant__ int kTrapTiles[8][2] = {{0x33, 0x00}, {0x32, 0x11}, {0x22, -1}, {0x20, -1},
+                                     {0x30, -1}, {0x31, -1}, {0x21, -1}, {0x10, -1}};
 
 template <int NP, int R, bool TRAP, bool ROT, bool GROUPED, typename IO, bool SO>
 __global__ __launch_bounds__(kWalkThreads) void k_walk(Args a) {
@@ -497,22 +502,27 @@ __global__ __launch_bounds__(kWalkThreads) void k_walk(Args a) {
     float seg_acc = 0.0f;   // SO: total log-decay of the segment
     float rev_acc = 0.0f;   // SO: total angle of pair sk (last step group), revolutions mod 1
     float cum_last = 0.0f;
+    float cum0 = 0.0f;      // trapezoid: log-decay of the chunk's first step
 
     // ---- staging of one chunk from the prefetch registers into LDS ----------
     auto stage = [&](const Pre& p) {
         const float cum = wave_scan_dpp(p.ld);   // lanes >= QT add zero
         cum_last = readlane_f(cum, QT - 1);
-        float wl, wprev = 0.0f;   // chunk-end weights of step `lane` and of the previous step
+        // chunk-end weights of step `lane` and of the previous step (the full
+        // pass adds the previous step's term to the state at the start of the
+        // chunk, with weight beta_0; the state-only pass at the end, decayed)
+        float wl, wprev = 0.0f;
         if constexpr (TRAP) {
             const float cum_n = cum + p.ldn;       // cumulative log-decay of step `lane` + 1
             wl = p.gam * exp_e(cum_last - cum) + (lane + 1 < QT ? p.betn * exp_e(cum_last - cum_n) : 0.0f);
-            wprev = readlane_f(p.bet, 0) * exp_e(cum_last - readlane_f(cum, 0));
+            cum0 = readlane_f(cum, 0);
+            wprev = readlane_f(p.bet, 0) * (SO ? exp_e(cum_last - cum0) : 1.0f);
         } else {
             wl = exp_e(cum_last - cum);
         }
         if (wave == 0) {
             if (lane < QT) {
-                s_cum[lane + 1] = cum;
+                s_cum[lane + 1] = TRAP ? cum - cum0 : cum;   // trapezoid: relative to step 0
                 if constexpr (TRAP) {
                     s_gam[lane] = p.gam;
                     s_bet[lane] = p.bet;
@@ -681,6 +691,31 @@ __global__ __launch_bounds__(kWalkThreads) void k_walk(Args a) {
         __syncthreads();
         if constexpr (SO) seg_acc += cum_last;
 
+        // ---- trapezoid: H+ = alpha_0 H + beta_0 B_{-1}^T x_{-1} (the previous
+        // step's beta term, which then decays with the chunk like the state) -----
+        if constexpr (TRAP && FULL) if (active) {
+            const float a0 = exp_e(cum0);
+#pragma unroll
+            for (int t = 0; t < NT2; ++t) acc_h[t] *= a0;
+            const int nb = (NP / 2) * nh + NT2 * li;   // first state row of this lane's tiles
+#pragma unroll
+            for (int e = 0; e < JX; ++e) {
+                const int j = kRows + 4 * e + lk;
+                const float xd = sXdT[(16 * pw + li) * JP + j];
+                if constexpr (NT2 == 4) {
+                    const float4 bv = *(const float4*)(sB + bcx(j, nb));
+                    acc_h[0] = mfma4(bv.x, xd, acc_h[0]);
+                    acc_h[1] = mfma4(bv.y, xd, acc_h[1]);
+                    acc_h[2] = mfma4(bv.z, xd, acc_h[2]);
+                    acc_h[3] = mfma4(bv.w, xd, acc_h[3]);
+                } else {
+                    const float2 bv = *(const float2*)(sB + bcx(j, nb));
+                    acc_h[0] = mfma4(bv.x, xd, acc_h[0]);
+                    acc_h[1] = mfma4(bv.y, xd, acc_h[1]);
+                }
+            }
+        }
+
         if constexpr (FULL) {
             floatx4 acc_y[4];
             // The two waves of a SIMD (same column group, other state half) take the
@@ -782,19 +817,11 @@ __global__ __launch_bounds__(kWalkThreads) void k_walk(Args a) {
                         acc_y[it] = mfma4(xv.w, mv.w, acc_y[it]);
                     }
                 }
-                if (nh == 1) {
-#pragma unroll
-                    for (int e = 0; e < JX; ++e) {
-                        const float xe = sXT[(16 * pw + li) * JP + kRows + 4 * e + lk];
-#pragma unroll
-                        for (int it = 0; it < 4; ++it)
-                            acc_y[it] = mfma4(xe, sM[(16 * it + li) * JP + kRows + 4 * e + lk], acc_y[it]);
-                    }
-                }
             }
             // ---- H' = e^{cum_last} H + B~^T Xd over this wave's rows ------------------
+            // (trapezoid: H is already H+, decayed through step 0)
             if (active) {
-                const float tot = exp_e(cum_last);
+                const float tot = exp_e(cum_last - cum0);
 #pragma unroll
                 for (int t = 0; t < NT2; ++t) acc_h[t] *= tot;
             }
@@ -865,20 +892,23 @@ __global__ __launch_bounds__(kWalkThreads) void k_walk(Args a) {
                     }
                 }
             }
+            // state-only pass: the previous step's beta term, decayed to the chunk end
+            if constexpr (SO) {
 #pragma unroll
-            for (int e = 0; e < JX; ++e) {
-                const int j = kRows + 4 * e + lk;
-                const float xd = sXdT[(16 * pw + li) * JP + j];
-                if constexpr (NT2 == 4) {
-                    const float4 bv = *(const float4*)(sB + bcx(j, nb));
-                    acc_h[0] = mfma4(bv.x, xd, acc_h[0]);
-                    acc_h[1] = mfma4(bv.y, xd, acc_h[1]);
-                    acc_h[2] = mfma4(bv.z, xd, acc_h[2]);
-                    acc_h[3] = mfma4(bv.w, xd, acc_h[3]);
-                } else {
-                    const float2 bv = *(const float2*)(sB + bcx(j, nb));
-                    acc_h[0] = mfma4(bv.x, xd, acc_h[0]);
-                    acc_h[1] = mfma4(bv.y, xd, acc_h[1]);
+                for (int e = 0; e < JX; ++e) {
+                    const int j = kRows + 4 * e + lk;
+                    const float xd = sXdT[(16 * pw + li) * JP + j];
+                    if constexpr (NT2 == 4) {
+                        const float4 bv = *(const float4*)(sB + bcx(j, nb));
+                        acc_h[0] = mfma4(bv.x, xd, acc_h[0]);
+                        acc_h[1] = mfma4(bv.y, xd, acc_h[1]);
+                        acc_h[2] = mfma4(bv.z, xd, acc_h[2]);
+                        acc_h[3] = mfma4(bv.w, xd, acc_h[3]);
+                    } else {
+                        const float2 bv = *(const float2*)(sB + bcx(j, nb));
+                        acc_h[0] = mfma4(bv.x, xd, acc_h[0]);
+                        acc_h[1] = mfma4(bv.y, xd, acc_h[1]);
+                    }
                 }
             }
             if constexpr (ROT) {
