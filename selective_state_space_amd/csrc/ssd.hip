@@ -351,6 +351,10 @@ __global__ __launch_bounds__(kWalkThreads) void k_walk(Args a) {
     constexpr int PRX = (R + NXG - 1) / NXG;
     constexpr bool FULL = !SO;
     constexpr int BS = NP + 4;      // LDS row stride of B~ / C~ (4 mod 32 floats)
+    // R >= 4: output tiles are computed as Y = C~ H (a lane holds four rows of one
+    // column: the four ranks of a step, stored as one 16-byte piece); otherwise as
+    // Y^T = H^T C~^T (a lane holds four columns of one row)
+    constexpr bool YROW = R >= 4;
 
     __shared__ __attribute__((aligned(16))) float sB[Gm::BR * BS];
     // float offset of element (row j, state n) of sB / sC
@@ -780,13 +784,13 @@ __global__ __launch_bounds__(kWalkThreads) void k_walk(Args a) {
                                 const int s = 4 * q4 + e;
                                 const int t = s % NT2, r = s / NT2;
                                 if (e % 2 == 0)
-                                    y0 = mfma4(acc_h[t][r], cvs[e], y0);
+                                    y0 = YROW ? mfma4(cvs[e], acc_h[t][r], y0) : mfma4(acc_h[t][r], cvs[e], y0);
                                 else
-                                    y1 = mfma4(acc_h[t][r], cvs[e], y1);
+                                    y1 = YROW ? mfma4(cvs[e], acc_h[t][r], y1) : mfma4(acc_h[t][r], cvs[e], y1);
                             }
                         }
                         // the state part carries the row decay e^{cum_i}; the intra part does not
-                        acc_y[it] = (y0 + y1) * exp_e(s_cum[(16 * it + li) / R + 1]);
+                        acc_y[it] = (y0 + y1) * exp_e(s_cum[(16 * it + (YROW ? 4 * lk : li)) / R + 1]);
                     }
                 }
             };
@@ -811,10 +815,17 @@ __global__ __launch_bounds__(kWalkThreads) void k_walk(Args a) {
                     for (int it = 0; it < 4; ++it) {
                         if (it < jt) continue;
                         const float4 mv = *(const float4*)(sM + (16 * it + li) * JP + 16 * jt + 4 * lk);
-                        acc_y[it] = mfma4(xv.x, mv.x, acc_y[it]);
-                        acc_y[it] = mfma4(xv.y, mv.y, acc_y[it]);
-                        acc_y[it] = mfma4(xv.z, mv.z, acc_y[it]);
-                        acc_y[it] = mfma4(xv.w, mv.w, acc_y[it]);
+                        if constexpr (YROW) {
+                            acc_y[it] = mfma4(mv.x, xv.x, acc_y[it]);
+                            acc_y[it] = mfma4(mv.y, xv.y, acc_y[it]);
+                            acc_y[it] = mfma4(mv.z, xv.z, acc_y[it]);
+                            acc_y[it] = mfma4(mv.w, xv.w, acc_y[it]);
+                        } else {
+                            acc_y[it] = mfma4(xv.x, mv.x, acc_y[it]);
+                            acc_y[it] = mfma4(xv.y, mv.y, acc_y[it]);
+                            acc_y[it] = mfma4(xv.z, mv.z, acc_y[it]);
+                            acc_y[it] = mfma4(xv.w, mv.w, acc_y[it]);
+                        }
                     }
                 }
             }
@@ -839,6 +850,24 @@ __global__ __launch_bounds__(kWalkThreads) void k_walk(Args a) {
                 for (int it = 0; it < 4; ++it) {
                     const floatx4 o = *(const floatx4*)&sYp[((pw * 4 + it) * 64 + lane) * 4];
                     const floatx4 y = acc_y[it] + o;
+                    if constexpr (YROW) {
+                        // lane holds Y[i = 16 it + 4 lk + r][p = p0 + 16 pw + li]: ranks
+                        // rk .. rk + 3 of step tg
+                        const int i0 = 16 * it + 4 * lk;
+                        const int tg = t0g + i0 / R, rk = i0 % R;
+                        if (tg < a.L) {
+                            IO* yrow = (IO*)a.Y + (((size_t)b * a.L + tg) * a.H + h) * (size_t)a.P * R;
+                            const size_t e = (size_t)(p0 + 16 * pw + li) * R + rk;
+                            if constexpr (sizeof(IO) == 4) {
+                                *(float4*)((float*)yrow + e) = make_float4(y[0], y[1], y[2], y[3]);
+                            } else {
+                                const uint32_t u0 = f32_to_bf16(y[0]) | ((uint32_t)f32_to_bf16(y[1]) << 16);
+                                const uint32_t u1 = f32_to_bf16(y[2]) | ((uint32_t)f32_to_bf16(y[3]) << 16);
+                                *(uint2*)((bf16*)yrow + e) = make_uint2(u0, u1);
+                            }
+                        }
+                        continue;
+                    }
                     // lane holds Y[i = 16 it + li][p = p0 + 16 pw + 4 lk + r]
                     const int i = 16 * it + li;
                     const int tg = t0g + i / R;
