@@ -36,6 +36,10 @@
 // Kernels
 //   k_scores  (Mamba-2 only) one workgroup per (batch, chunk, group):
 //             S = C B^T on fp32 MFMA, shared by the heads of the group.
+//   k_walk_m2s  (Mamba-2, fp32 full pass) the same walk with the roles split:
+//             four matrix waves hold the state and do every product, four
+//             staging waves copy B and C into LDS and stage X and the masked
+//             scores of the next chunk.
 //   k_walk    one workgroup (8 waves) per (batch, head, segment, 64 state
 //             columns), walking the segment's chunks in order.  Per chunk the
 //             workgroup stages B~ and C~ (rotated once, for all columns), X and
@@ -987,35 +991,36 @@ __global__ __launch_bounds__(kWalkThreads) void k_walk(Args a) {
 }
 
 // ---------------------------------------------------------------------------
-// Mamba-2 fp32 walk (full pass).  Same decomposition and state layout as
-// k_walk, specialised for the case with no rotation and no trapezoid:
-//   - B and C go from global memory straight into LDS by LDS DMA (swizzled
-//     rows, see bcx below);
-//   - per chunk only X^T, the chunk-end-weighted X^T (double-buffered) and the
-//     masked scores are staged through registers, in a thread mapping where
-//     lane = time step, so every cross-lane value is a wave-uniform readlane
-//     and the decay prefix is a DPP scan;
-//   - the next chunk is staged right after the output exchange, while the
-//     other wave of the SIMD runs the state update, and each chunk needs two
-//     barriers.
-// Per chunk c (LDS holds C(c), X^T(c), Xd^T(c), M(c), cum(c) at the top):
-//   B DMA(c); prefetch registers (c+1); Y^T partial = H^T C^T (scaled), + X^T M^T;
-//   exchange partials; wait B(c); barrier; C DMA(c+1); store Y(c);
-//   stage (c+1); H = e^{cum_last} H + B^T Xd; wait C(c+1); barrier.
+// Mamba-2 fp32 walk (full pass), wave-specialised.  Waves 0-3 (one per SIMD)
+// are the matrix waves: wave w owns state columns p0 + 16 w .. + 15 for all NP
+// state rows (NT = NP/16 accumulator tiles; tile t, register r of lane
+// (li, lk) is row (NP/4) lk + (NP/16) r + t) and does every matrix product of
+// the chunk for those columns, so the output needs no exchange.  Waves 4-7 are
+// the staging waves: they copy B and C into LDS by LDS DMA, load X, the scores
+// and the log-decay of the next chunk into registers and stage X^T, the
+// chunk-end-weighted X^T and the masked scores.  Per chunk c, three phases
+// separated by workgroup barriers:
+//   1. matrix: Y^T = H^T C^T x e^{cum}      staging: B(c) -> LDS; loads for c+1
+//   2. matrix: Y^T += X^T M^T, store Y(c)   staging: C(c+1) -> LDS
+//   3. matrix: H = e^{cum_last} H + B^T Xd  staging: X^T, Xd^T, M, cum of c+1
+// Each buffer is written in the phase after its last reader, so single LDS
+// buffers suffice (Xd^T and cum, read in phase 3, are double-buffered).  Every
+// copy and load of the staging waves is issued unconditionally (offsets past a
+// buffer read zeros), so their vmcnt waits are exact.
 // ---------------------------------------------------------------------------
 template <int NP>
-__global__ __launch_bounds__(kWalkThreads) void k_walk_m2(Args a) {
+__global__ __launch_bounds__(kWalkThreads) void k_walk_m2s(Args a) {
     constexpr int JP = kRows + 4;   // LDS row stride of X^T / Xd^T / M (4 mod 32)
-    constexpr int NT2 = NP / 32;    // state tiles per wave
-    constexpr int kDmaPerWave = kRows * NP / 256 / 8;
+    constexpr int NT = NP / 16;     // state tiles per matrix wave
+    constexpr int NDMA = kRows * NP / 256 / 4;   // 16-byte copies per staging wave for B or C
+    constexpr uint32_t kOut = 0x80000000u;       // byte offset past any buffer: reads zero
 
     __shared__ __attribute__((aligned(16))) float sB[kRows * NP];
     __shared__ __attribute__((aligned(16))) float sC[kRows * NP];
     __shared__ __attribute__((aligned(16))) float sXT[kPG * JP];
     __shared__ __attribute__((aligned(16))) float sXdT[2][kPG * JP];
     __shared__ __attribute__((aligned(16))) float sM[kRows * JP];
-    __shared__ __attribute__((aligned(16))) float sYp[4 * 4 * 64 * 4];
-    __shared__ float s_cum[kRows + 1];
+    __shared__ float s_cum[2][kRows + 1];
 
     // float offset of element (row j, state n) of sB / sC: 16-byte column
     // groups of row j XOR-swizzled by j % 8 (conflict-free operand reads)
@@ -1044,86 +1049,104 @@ __global__ __launch_bounds__(kWalkThreads) void k_walk_m2(Args a) {
 
     const int tid = threadIdx.x, lane = tid % 64;
     const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
-    const int pw = wave & 3, nh = wave >> 2;
+    const bool mma = wave < 4;         // uniform
+    const int pw = wave & 3;           // matrix wave: column block; staging wave: step block
     const int li = lane % 16, lk = lane / 16;
     const int pw_n = (min(kPG, a.P - p0)) / 16;
-    const bool active = pw < pw_n;   // uniform
+    const bool active = mma && pw < pw_n;   // uniform
     const int pcol = p0 + 16 * pw + li;
     const Views<1, true, float> vw(a, b, h, hg);
     const size_t sh_off = (size_t)(b * a.H + h) * a.N * a.P;
-    const bool x_ok = p0 + lane < a.P;   // staging: this lane's X column
     const Buf Sbuf = make_buf(a.S + (size_t)b * a.nch * a.G * (kRows * kRows),
                               (size_t)a.nch * a.G * kRows * kRows * 4);
+    auto srow = [](int t, int r, int lk_) { return (NP / 4) * lk_ + (NP / 16) * r + t; };
 
-    // LDS DMA of the 64 rows of B or C of chunk c: 1 KB per wave instruction,
-    // lane l filling the 16 bytes at dst + 256 q + 4 l (a swizzled position)
-    // from the matching global column group; groups at or past N stay zero.
+    // ---- staging waves -----------------------------------------------------------
+    // LDS DMA of the 64 rows of B or C of chunk c: staging wave pw moves 1 KB per
+    // instruction, lane l filling the 16 bytes at dst + 256 q + 4 l (a swizzled
+    // position) from the matching global column group; groups at or past N read
+    // zero.
     auto dma_rows = [&](const Buf& src, float* dst, int c) {
         const int t0g = c * kRows;
 #pragma unroll
-        for (int m = 0; m < kDmaPerWave; ++m) {
-            const int q = wave + 8 * m;
+        for (int m = 0; m < NDMA; ++m) {
+            const int q = pw + 4 * m;
             const int f = 256 * q + 4 * lane;
             const int j = f / NP, gp = (f % NP) >> 2;
             const int g = gp ^ (j & 7);
-            const int e = (t0g + j) * vw.bc_step + vw.bc_head + 4 * g;
-            if (4 * g < a.N)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    src.r, (__attribute__((address_space(3))) void*)(dst + 256 * q), 16, e * 4, 0, 0, 0);
+            const uint32_t off = (uint32_t)(((t0g + j) * vw.bc_step + vw.bc_head + 4 * g) * 4) | (4 * g < a.N ? 0u : kOut);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                src.r, (__attribute__((address_space(3))) void*)(dst + 256 * q), 16, off, 0, 0, 0);
         }
     };
-
-    // staging registers: X column p0 + lane at steps 8 wave + i; scores row
-    // `lane`, columns 8 wave .. 8 wave + 7; log-decay of step `lane`
-    float px[8], psc[8], pld;
+    // registers of the next chunk: X column p0 + lane at steps 16 pw + i; score row
+    // `lane`, columns 16 pw .. 16 pw + 15; log-decay of step `lane`
+    float px[16], psc[16], pld = 0.0f;
+    // offsets of lanes without a value get the top bit set (past any buffer);
+    // kept as arithmetic so that the loads stay one straight block
+    const uint32_t xbad = p0 + lane < a.P ? 0u : kOut;
+    const uint32_t sbad = 16 * pw <= lane ? 0u : kOut;   // score rows before the block: masked
     auto prefetch = [&](int c) {
         const int t0g = c * kRows;
+        const uint32_t xo = (uint32_t)(((t0g + 16 * pw) * vw.x_step + vw.x_head + p0 + lane) * 4);
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-            px[i] = x_ok ? bload<float>(vw.X, (t0g + 8 * wave + i) * vw.x_step + vw.x_head + p0 + lane) : 0.0f;
-        if (8 * wave <= lane)
-            VecLoad<float, 8>::run(Sbuf, (c * a.G + hg) * (kRows * kRows) + wave * (kRows * 8) + lane * 8, psc);
-        pld = bload<float>(vw.ld, (t0g + lane) * a.H + h);
+        for (int i = 0; i < 16; ++i)
+            px[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                vw.X.r, (xo + (uint32_t)(i * vw.x_step * 4)) | xbad, 0, 0));
+        // blocked score layout: columns 8 (2 pw + q) .. + 7 of row `lane`
+        const uint32_t so = (uint32_t)(((c * a.G + hg) * (kRows * kRows) + (2 * pw) * (kRows * 8) + lane * 8) * 4);
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+            for (int v = 0; v < 2; ++v) {
+                const uintx4 u = __builtin_amdgcn_raw_buffer_load_b128(
+                    Sbuf.r, (so + (uint32_t)(q * kRows * 8 * 4 + v * 16)) | sbad, 0, 0);
+                psc[8 * q + 4 * v] = __uint_as_float(u.x);
+                psc[8 * q + 4 * v + 1] = __uint_as_float(u.y);
+                psc[8 * q + 4 * v + 2] = __uint_as_float(u.z);
+                psc[8 * q + 4 * v + 3] = __uint_as_float(u.w);
+            }
+        pld = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+            vw.ld.r, (uint32_t)(((t0g + lane) * a.H + h) * 4), 0, 0));
     };
-    float cum_last = 0.0f;   // of the chunk staged last
     auto stage = [&](int c) {
         const float cum = wave_scan_dpp(pld);
-        cum_last = readlane_f(cum, kRows - 1);
+        const float cum_last = readlane_f(cum, kRows - 1);
         const float wl = exp_e(cum_last - cum);   // chunk-end weight of step `lane`
-        if (wave == 0) {
-            s_cum[lane + 1] = cum;
-            if (lane == 0) s_cum[0] = 0.0f;
+        if (pw == 0) {
+            s_cum[c & 1][lane + 1] = cum;
+            if (lane == 0) s_cum[c & 1][0] = 0.0f;
         }
         float* xd = sXdT[c & 1];
-        float xv[8], xw[8], mv[8];
+        float xv[16], xw[16], mv[16];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int t = 8 * wave + i;
+        for (int i = 0; i < 16; ++i) {
+            const int t = 16 * pw + i;
             xv[i] = px[i];
             xw[i] = px[i] * readlane_f(wl, t);
             const float e = exp_e(t <= lane ? cum - readlane_f(cum, t) : 0.0f);
             mv[i] = t <= lane ? psc[i] * e : 0.0f;
         }
-        // X^T[p][t] for p = p0 + lane (rows of X^T are columns of X)
+        // X^T[p][t] for p = p0 + lane (rows of X^T are columns of X); M[lane][t]
 #pragma unroll
-        for (int i = 0; i < 8; i += 4) {
-            *(float4*)&sXT[lane * JP + 8 * wave + i] = make_float4(xv[i], xv[i + 1], xv[i + 2], xv[i + 3]);
-            *(float4*)&xd[lane * JP + 8 * wave + i] = make_float4(xw[i], xw[i + 1], xw[i + 2], xw[i + 3]);
-            *(float4*)&sM[lane * JP + 8 * wave + i] = make_float4(mv[i], mv[i + 1], mv[i + 2], mv[i + 3]);
+        for (int i = 0; i < 16; i += 4) {
+            *(float4*)&sXT[lane * JP + 16 * pw + i] = make_float4(xv[i], xv[i + 1], xv[i + 2], xv[i + 3]);
+            *(float4*)&xd[lane * JP + 16 * pw + i] = make_float4(xw[i], xw[i + 1], xw[i + 2], xw[i + 3]);
+            *(float4*)&sM[lane * JP + 16 * pw + i] = make_float4(mv[i], mv[i + 1], mv[i + 2], mv[i + 3]);
         }
     };
 
-    // ---- entering state (h0 and the earlier segments), as k_walk --------------
-    floatx4 acc_h[NT2];
+    // ---- matrix waves: entering state (h0 and the earlier segments) -----------------
+    floatx4 acc_h[NT];
 #pragma unroll
-    for (int t = 0; t < NT2; ++t) acc_h[t] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int t = 0; t < NT; ++t) acc_h[t] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
     if (active) {
         if (a.h0) {
 #pragma unroll
-            for (int t = 0; t < NT2; ++t)
+            for (int t = 0; t < NT; ++t)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int n = state_row<NP>(t, r, lk, nh);
+                    const int n = srow(t, r, lk);
                     acc_h[t][r] = n < a.N ? a.h0[sh_off + (size_t)n * a.P + pcol] : 0.0f;
                 }
         }
@@ -1131,10 +1154,10 @@ __global__ __launch_bounds__(kWalkThreads) void k_walk_m2(Args a) {
             const size_t u = (size_t)(b * a.H + h) * (a.nseg - 1) + s2;
             const float d = exp_e(a.seg_ld[u]);
 #pragma unroll
-            for (int t = 0; t < NT2; ++t)
+            for (int t = 0; t < NT; ++t)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int n = state_row<NP>(t, r, lk, nh);
+                    const int n = srow(t, r, lk);
                     const float hl = n < a.N ? a.seg_h[(u * a.N + n) * a.P + pcol] : 0.0f;
                     acc_h[t][r] = fmaf(d, acc_h[t][r], hl);
                 }
@@ -1142,124 +1165,120 @@ __global__ __launch_bounds__(kWalkThreads) void k_walk_m2(Args a) {
     }
 
     // ---- first chunk ------------------------------------------------------------
-    if (a.N < NP) {   // column groups at or past N are never copied: keep them zero
-        for (int e = tid; e < kRows * NP; e += kWalkThreads) {
-            sB[e] = 0.0f;
-            sC[e] = 0.0f;
-        }
-        __syncthreads();
-    }
-    if (c_begin < c_end) {
+    if (!mma && c_begin < c_end) {
         dma_rows(vw.C, sC, c_begin);
         prefetch(c_begin);
+        vm_wait<0>();
         stage(c_begin);
     }
-    vm_wait<0>();
     __syncthreads();
 
-    for (int c = c_begin; c < c_end; ++c) {
-        const int t0g = c * kRows;
-        const float tot = exp_e(cum_last);   // decay over this chunk
-        dma_rows(vw.B, sB, c);
-        if (c + 1 < c_end) prefetch(c + 1);
-
-        // ---- partial Y^T = H^T C^T over this wave's state rows, x e^{cum_i} ---------
-        floatx4 acc_y[4];
-        if (active) {
-#pragma unroll
-            for (int it = 0; it < 4; ++it) {
-                floatx4 y0 = {0.0f, 0.0f, 0.0f, 0.0f}, y1 = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-                for (int q4 = 0; q4 < NP / 32; ++q4) {
-                    const float4 cv = *(const float4*)(sC + bcx(16 * it + li, (NP / 2) * nh + (NP / 8) * lk + 4 * q4));
-                    const float cvs[4] = {cv.x, cv.y, cv.z, cv.w};
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int s = 4 * q4 + e;
-                        const int t = s % NT2, r = s / NT2;
-                        if (e % 2 == 0)
-                            y0 = mfma4(acc_h[t][r], cvs[e], y0);
-                        else
-                            y1 = mfma4(acc_h[t][r], cvs[e], y1);
-                    }
-                }
-                acc_y[it] = (y0 + y1) * exp_e(s_cum[16 * it + li + 1]);
-            }
-            // ---- partial Y^T += X^T M^T over half of the column blocks --------------
-            const float* pxr = sXT + (16 * pw + li) * JP + 4 * lk;
-#pragma unroll
-            for (int jh = 0; jh < 2; ++jh) {
-                const int jt = 2 * nh + jh;
-                const float4 xv = *(const float4*)(pxr + 16 * jt);
+    // The two roles run separate loops with the same three barriers per chunk.
+    if (mma) {
+        for (int c = c_begin; c < c_end; ++c) {
+            const int t0g = c * kRows;
+            // ---- phase 1: Y^T = H^T C^T, scaled by e^{cum} per row ------------------------
+            floatx4 acc_y[4];
+            if (active) {
 #pragma unroll
                 for (int it = 0; it < 4; ++it) {
-                    if (it < jt) continue;
-                    const float4 mv = *(const float4*)(sM + (16 * it + li) * JP + 16 * jt + 4 * lk);
-                    acc_y[it] = mfma4(xv.x, mv.x, acc_y[it]);
-                    acc_y[it] = mfma4(xv.y, mv.y, acc_y[it]);
-                    acc_y[it] = mfma4(xv.z, mv.z, acc_y[it]);
-                    acc_y[it] = mfma4(xv.w, mv.w, acc_y[it]);
+                    floatx4 y4[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) y4[e] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                    for (int q4 = 0; q4 < NP / 16; ++q4) {
+                        // state rows (NP/4) lk + 4 q4 .. + 3 of this lane group: s = NT r + t
+                        const float4 cv = *(const float4*)(sC + bcx(16 * it + li, (NP / 4) * lk + 4 * q4));
+                        const float cvs[4] = {cv.x, cv.y, cv.z, cv.w};
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int s = 4 * q4 + e;
+                            const int t = s % NT, r = s / NT;
+                            y4[e] = mfma4(acc_h[t][r], cvs[e], y4[e]);
+                        }
+                    }
+                    acc_y[it] = ((y4[0] + y4[1]) + (y4[2] + y4[3])) * exp_e(s_cum[c & 1][16 * it + li + 1]);
                 }
             }
-            if (nh == 1) {
+            __syncthreads();
+            // ---- phase 2: Y^T += X^T M^T; store Y(c) -----------------------------------------
+            if (active) {
+                const float* pxr = sXT + (16 * pw + li) * JP + 4 * lk;
 #pragma unroll
-                for (int it = 0; it < 4; ++it)
-                    *(floatx4*)&sYp[((pw * 4 + it) * 64 + lane) * 4] = acc_y[it];
-            }
-        }
-        vm_wait<0>();       // B of this chunk and the next chunk's registers have arrived
-        __syncthreads();
-        if (c + 1 < c_end) dma_rows(vw.C, sC, c + 1);   // C of this chunk is no longer read
-        if (active && nh == 0) {
+                for (int jt = 0; jt < 4; ++jt) {
+                    const float4 xv = *(const float4*)(pxr + 16 * jt);
 #pragma unroll
-            for (int it = 0; it < 4; ++it) {
-                const floatx4 y = acc_y[it] + *(const floatx4*)&sYp[((pw * 4 + it) * 64 + lane) * 4];
-                const int tg = t0g + 16 * it + li;
-                if (tg < a.L) {
-                    float* yrow = (float*)a.Y + (((size_t)b * a.L + tg) * a.H + h) * (size_t)a.P;
-                    *(float4*)(yrow + p0 + 16 * pw + 4 * lk) = make_float4(y[0], y[1], y[2], y[3]);
+                    for (int it = 0; it < 4; ++it) {
+                        if (it < jt) continue;
+                        const float4 mv = *(const float4*)(sM + (16 * it + li) * JP + 16 * jt + 4 * lk);
+                        acc_y[it] = mfma4(xv.x, mv.x, acc_y[it]);
+                        acc_y[it] = mfma4(xv.y, mv.y, acc_y[it]);
+                        acc_y[it] = mfma4(xv.z, mv.z, acc_y[it]);
+                        acc_y[it] = mfma4(xv.w, mv.w, acc_y[it]);
+                    }
                 }
-            }
-        }
-        if (c + 1 < c_end) stage(c + 1);
-
-        // ---- H = e^{cum_last} H + B^T Xd over this wave's rows ---------------------
-        if (active) {
 #pragma unroll
-            for (int t = 0; t < NT2; ++t) acc_h[t] *= tot;
-            const float* pxd = sXdT[c & 1] + (16 * pw + li) * JP + 16 * lk;
-            const int nb = (NP / 2) * nh + NT2 * li;
-#pragma unroll
-            for (int sq4 = 0; sq4 < 4; ++sq4) {
-                const float4 xd = *(const float4*)(pxd + 4 * sq4);
-                const float xds[4] = {xd.x, xd.y, xd.z, xd.w};
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int j = 16 * lk + 4 * sq4 + e;
-                    if constexpr (NT2 == 4) {
-                        const float4 bv = *(const float4*)(sB + bcx(j, nb));
-                        acc_h[0] = mfma4(bv.x, xds[e], acc_h[0]);
-                        acc_h[1] = mfma4(bv.y, xds[e], acc_h[1]);
-                        acc_h[2] = mfma4(bv.z, xds[e], acc_h[2]);
-                        acc_h[3] = mfma4(bv.w, xds[e], acc_h[3]);
-                    } else {
-                        const float2 bv = *(const float2*)(sB + bcx(j, nb));
-                        acc_h[0] = mfma4(bv.x, xds[e], acc_h[0]);
-                        acc_h[1] = mfma4(bv.y, xds[e], acc_h[1]);
+                for (int it = 0; it < 4; ++it) {
+                    // lane holds Y[i = 16 it + li][p = p0 + 16 pw + 4 lk + r]
+                    const int tg = t0g + 16 * it + li;
+                    if (tg < a.L) {
+                        float* yrow = (float*)a.Y + (((size_t)b * a.L + tg) * a.H + h) * (size_t)a.P;
+                        *(float4*)(yrow + p0 + 16 * pw + 4 * lk) =
+                            make_float4(acc_y[it][0], acc_y[it][1], acc_y[it][2], acc_y[it][3]);
                     }
                 }
             }
+            __syncthreads();
+            // ---- phase 3: H = e^{cum_last} H + B^T Xd ------------------------------------------
+            if (active) {
+                const float tot = exp_e(s_cum[c & 1][kRows]);   // decay over this chunk
+#pragma unroll
+                for (int t = 0; t < NT; ++t) acc_h[t] *= tot;
+                const float* pxd = sXdT[c & 1] + (16 * pw + li) * JP + 16 * lk;
+                const int nb = (NP / 4) * (li / 4) + (NP / 16) * (li % 4);   // this lane's first row
+#pragma unroll
+                for (int sq4 = 0; sq4 < 4; ++sq4) {
+                    const float4 xd = *(const float4*)(pxd + 4 * sq4);
+                    const float xds[4] = {xd.x, xd.y, xd.z, xd.w};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int j = 16 * lk + 4 * sq4 + e;
+#pragma unroll
+                        for (int g4 = 0; g4 < NT / 4; ++g4) {
+                            const float4 bv = *(const float4*)(sB + bcx(j, nb + 4 * g4));
+                            acc_h[4 * g4 + 0] = mfma4(bv.x, xds[e], acc_h[4 * g4 + 0]);
+                            acc_h[4 * g4 + 1] = mfma4(bv.y, xds[e], acc_h[4 * g4 + 1]);
+                            acc_h[4 * g4 + 2] = mfma4(bv.z, xds[e], acc_h[4 * g4 + 2]);
+                            acc_h[4 * g4 + 3] = mfma4(bv.w, xds[e], acc_h[4 * g4 + 3]);
+                        }
+                    }
+                }
+            }
+            __syncthreads();
         }
-        vm_wait<0>();       // C of the next chunk has arrived
-        __syncthreads();
+    } else {
+        for (int c = c_begin; c < c_end; ++c) {
+            // phase 1: B(c) -> LDS (read in phase 3); the registers of chunk c + 1
+            // (past the segment: unused; past the sequence: zeros)
+            dma_rows(vw.B, sB, c);
+            prefetch(c + 1);
+            __syncthreads();
+            // phase 2: nothing to stage
+            __syncthreads();
+            // phase 3: C(c + 1) -> LDS (C(c) was last read in phase 1); stage c + 1
+            dma_rows(vw.C, sC, c + 1);
+            if (c + 1 < c_end) stage(c + 1);
+            vm_wait<0>();
+            __syncthreads();
+        }
     }
 
     if (a.h_out && seg == a.nseg - 1 && active) {
 #pragma unroll
-        for (int t = 0; t < NT2; ++t)
+        for (int t = 0; t < NT; ++t)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int n = state_row<NP>(t, r, lk, nh);
+                const int n = srow(t, r, lk);
                 if (n < a.N) a.h_out[sh_off + (size_t)n * a.P + pcol] = acc_h[t][r];
             }
     }
@@ -1342,7 +1361,7 @@ mb_status launch(Args a, int64_t batch, const Plan& pl, char* ws, hipStream_t st
         if (st != MB_OK) return st;
     }
     if constexpr (!TRAP && !ROT && sizeof(IO) == 4)
-        hipLaunchKernelGGL((k_walk_m2<NP>), dim3((unsigned)(per_seg * a.nseg)), dim3(kWalkThreads), 0,
+        hipLaunchKernelGGL((k_walk_m2s<NP>), dim3((unsigned)(per_seg * a.nseg)), dim3(kWalkThreads), 0,
                            stream, a);
     else
         hipLaunchKernelGGL((k_walk<NP, R, TRAP, ROT, GROUPED, IO, false>),
