@@ -23,7 +23,8 @@ def _seed(*xs):
 # -------------------------------------------------------------------- SSD ----
 SSD_SHAPES = [  # batch, L, H, P, N, G
     (1, 1, 1, 16, 4, 1), (2, 65, 2, 16, 8, 1), (1, 64, 3, 32, 16, 3), (2, 130, 4, 16, 128, 2),
-    (1, 200, 2, 64, 128, 1), (2, 333, 3, 48, 64, 1), (1, 129, 6, 16, 32, 2)]
+    (1, 200, 2, 64, 128, 1), (2, 333, 3, 48, 64, 1), (1, 129, 6, 16, 32, 2),
+    (1, 700, 2, 128, 64, 1)]   # two column groups, two sequence segments
 
 
 @pytest.mark.parametrize("shape", SSD_SHAPES, ids=lambda s: "x".join(map(str, s)))
@@ -87,7 +88,8 @@ def test_ssd_block_workload_full(oracle_mod, dtype):
 # ------------------------------------------------------------------- SISO ----
 TRAP_SHAPES = [  # batch, L, H, P, N, G
     (1, 1, 1, 16, 4, 1), (2, 65, 2, 16, 8, 2), (1, 64, 3, 32, 16, 1), (2, 130, 4, 16, 128, 2),
-    (1, 333, 2, 64, 128, 1), (2, 97, 3, 32, 32, 3)]
+    (1, 333, 2, 64, 128, 1), (2, 97, 3, 32, 32, 3),
+    (1, 700, 2, 128, 64, 1)]   # two column groups, two sequence segments
 
 
 @pytest.mark.parametrize("shape", TRAP_SHAPES, ids=lambda s: "x".join(map(str, s)))
