@@ -144,7 +144,7 @@ class M1Step(Workload):
 
 
 class SSD(Workload):
-    kernel = "k_scores + k_walk (state-only pass) + k_walk_m2 (full pass)"
+    kernel = "k_scores + k_walk (state-only pass) + k_walk_m2s (full pass)"
     source = "selective_state_space_amd/csrc/ssd.hip"
     bound = "mfma"
 

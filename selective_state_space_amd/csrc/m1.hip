@@ -5,10 +5,13 @@
 //     h_t[c,n] = exp(dt_t[c] A[c,n]) h_{t-1}[c,n] + dt_t[c] B_t[n] x_t[c]
 //     y_t[c]   = sum_n C_t[n] h_t[c,n] + Dskip[c] x_t[c]
 //
-// Scan layout (detailed at k_m1_scan): a workgroup of 64 x ceil(N/4) lanes owns
-// 64 channels of one batch row and walks the whole sequence; each lane keeps
-// four (channel, state) chains in registers.  One hardware exp2 per (t, c, n)
-// element.
+// Scans (layouts detailed at the kernels): every lane keeps several (channel,
+// state) chains in registers and walks the whole sequence; one hardware exp2
+// per (t, c, n) element.
+//   k_m1_scan_w  fp32, N in {4, 8, 16, 32}: independent waves of 16 channels,
+//                tiles copied into LDS by DMA, no barriers.
+//   k_m1_scan    any other case: workgroups of 64 channels x ceil(N/4) waves,
+//                partial sums over states reduced through LDS once per tile.
 #include "mb_internal.h"
 
 namespace mb {
