@@ -529,7 +529,9 @@ mb_status launch_scan(const void* x, const void* dt, const float* A, const void*
                       hipStream_t stream)
 {
     if constexpr (sizeof(IO) == 4) {
-        if (N == 4 || N == 8 || N == 16 || N == 32) {
+        // 16-byte LDS copies need 16-byte aligned rows
+        const bool aligned = ((((uintptr_t)x | (uintptr_t)dt | (uintptr_t)B | (uintptr_t)C) & 15) == 0);
+        if (aligned && (N == 4 || N == 8 || N == 16 || N == 32)) {
             const int n_cg = (int)((D + 63) / 64);
             const int n_wg = (int)(batch * n_cg);
             const bool v16 = D % 4 == 0;

@@ -49,6 +49,25 @@ def test_scan_shapes(oracle_mod, shape, dtype):
     assert_close(h, hr, dtype, "h")
 
 
+def test_scan_unaligned_inputs(oracle_mod):
+    """x, dt, B, C at 4-byte (not 16-byte) aligned addresses take the general scan."""
+    b, L, D, N = 2, 90, 24, 16
+    inp = wl.m1_inputs(np.random.default_rng(11), b, L, D, N, h0_sd=0.1)
+    dev, ref = prepare(inp, "f32")
+    shifted = {}
+    for k in ("x", "dt", "B", "C"):
+        t = dev[k]
+        buf = torch.empty(t.numel() + 1, dtype=t.dtype, device=t.device)
+        v = buf[1:].view(t.shape)
+        v.copy_(t)
+        shifted[k] = v
+    y, h = mb.mb_selective_scan(shifted["x"], shifted["dt"], dev["A"], shifted["B"], shifted["C"],
+                                dev.get("D"), dev.get("h0"))
+    yr, hr = oracle_mod.m1_scan(**ref)
+    assert_close(y, yr, "f32", "y")
+    assert_close(h, hr, "f32", "h")
+
+
 def test_scan_without_skip_and_state(oracle_mod):
     rng = np.random.default_rng(5)
     inp = wl.m1_inputs(rng, 2, 45, 24, 16, with_D=False)
