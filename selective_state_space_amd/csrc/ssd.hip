@@ -1021,6 +1021,7 @@ __global__ __launch_bounds__(kWalkThreads) void k_walk_m2s(Args a) {
     __shared__ __attribute__((aligned(16))) float sXdT[2][kPG * JP];
     __shared__ __attribute__((aligned(16))) float sM[kRows * JP];
     __shared__ float s_cum[2][kRows + 1];
+    __shared__ __attribute__((aligned(16))) float s_bc[4][2][kRows];   // per staging wave: cum, wl
 
     // float offset of element (row j, state n) of sB / sC: 16-byte column
     // groups of row j XOR-swizzled by j % 8 (conflict-free operand reads)
@@ -1117,14 +1118,26 @@ __global__ __launch_bounds__(kWalkThreads) void k_walk_m2s(Args a) {
             s_cum[c & 1][lane + 1] = cum;
             if (lane == 0) s_cum[c & 1][0] = 0.0f;
         }
+        // the 16 steps of this wave's block, broadcast through the wave's own LDS
+        // slots (cheaper than one readlane per value)
+        s_bc[pw][0][lane] = cum;
+        s_bc[pw][1][lane] = wl;
+        float cumv[16], wlv[16];
+#pragma unroll
+        for (int q = 0; q < 16; q += 4) {
+            const float4 u = *(const float4*)&s_bc[pw][0][16 * pw + q];
+            const float4 v = *(const float4*)&s_bc[pw][1][16 * pw + q];
+            cumv[q] = u.x; cumv[q + 1] = u.y; cumv[q + 2] = u.z; cumv[q + 3] = u.w;
+            wlv[q] = v.x; wlv[q + 1] = v.y; wlv[q + 2] = v.z; wlv[q + 3] = v.w;
+        }
         float* xd = sXdT[c & 1];
         float xv[16], xw[16], mv[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const int t = 16 * pw + i;
             xv[i] = px[i];
-            xw[i] = px[i] * readlane_f(wl, t);
-            const float e = exp_e(t <= lane ? cum - readlane_f(cum, t) : 0.0f);
+            xw[i] = px[i] * wlv[i];
+            const float e = exp_e(t <= lane ? cum - cumv[i] : 0.0f);
             mv[i] = t <= lane ? psc[i] * e : 0.0f;
         }
         // X^T[p][t] for p = p0 + lane (rows of X^T are columns of X); M[lane][t]
