@@ -74,6 +74,24 @@ __device__ __forceinline__ floatx4 mfma4(float a, float b, floatx4 c) {
 
 __device__ __forceinline__ float exp_e(float v) { return exp2_fast(v * kLog2e); }
 
+// bf16 matrix instruction: 16 x 16 x 32, fp32 accumulation.  Lane l supplies
+// A[l % 16][8 (l / 16) + q] and B[8 (l / 16) + q][l % 16], q = 0..7, as four
+// registers of bf16 pairs; the accumulator layout is that of the fp32 16 x 16
+// instruction.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float floatx2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ floatx4 mfma_bf(uintx4 a, uintx4 b, floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// two fp32 values rounded to nearest-even bf16, packed (lo in the low half)
+__device__ __forceinline__ uint32_t pack_bf(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((floatx2){lo, hi}, bf16x2));
+}
+
 // Wait until at most N vector memory operations of this wave are outstanding
 // (s_waitcnt vmcnt(N), other counters unconstrained).
 template <int N>
@@ -224,6 +242,7 @@ struct Args {
     void* Y;
     float* h_out;
     float* S;        // Mamba-2 scores, (batch, chunk, group, 64, 64)
+    bf16* BT;        // Mamba-2 with bf16 inputs: B^T per chunk, (batch, chunk, group, NP, 64)
     float* seg_h;    // local end states of segments 0..nseg-2, (batch, H, nseg-1, N, P)
     float* seg_ld;   // their total log-decay, (batch, H, nseg-1)
     float* seg_rev;  // their total angle per pair in revolutions mod 1, (batch, H, nseg-1, N/2)
@@ -291,6 +310,19 @@ __global__ __launch_bounds__(kThreads) void k_scores(Args a) {
         }
     }
     __syncthreads();
+    if constexpr (sizeof(IO) == 2) {
+        // bf16 inputs: also store this chunk's B transposed, rows n (zero at n >= N),
+        // 64 steps each, for the walk's state update
+        bf16* bt = a.BT + (((size_t)b * a.nch + c) * a.G + g) * (size_t)(NP * kRows);
+        for (int e = tid; e < NP * 8; e += kThreads) {
+            const int n = e % NP, blk = e / NP;
+            uint32_t u[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                u[q] = pack_bf(sB[(8 * blk + 2 * q) * SB + n], sB[(8 * blk + 2 * q + 1) * SB + n]);
+            *(uint4*)(bt + n * kRows + 8 * blk) = make_uint4(u[0], u[1], u[2], u[3]);
+        }
+    }
     const int li = lane % 16, lk = lane / 16;
     float* Sout = a.S + (((size_t)b * a.nch + c) * a.G + g) * (size_t)(kRows * kRows);
     const int it = wave;
@@ -1298,11 +1330,363 @@ __global__ __launch_bounds__(kWalkThreads) void k_walk_m2s(Args a) {
 }
 
 // ---------------------------------------------------------------------------
+// Mamba-2 walk with bf16 inputs on the bf16 matrix instruction (SO = state-only
+// pre-pass).  Four waves, one workgroup per (batch, segment, head, 64 columns);
+// wave w owns state columns p0 + 16 w .. + 15 for all NP state rows in NT =
+// NP/16 fp32 accumulator tiles, and computes the output for those columns.
+// The state stays fp32 and is rounded to bf16 only as an operand of the output
+// product.  Tile t, register r of lane (li, lk) holds state row
+//     n = 32 (t / 2) + 8 lk + 4 (t % 2) + r,
+// so that tiles 2k and 2k + 1 are directly the eight consecutive rows 32 k +
+// 8 lk .. + 7 that lane group lk supplies to the output product.  Per chunk:
+//   Y^T = H^T C^T x e^{cum} + X^T M^T        (M: masked scores, bf16)
+//   H   = e^{cum_last} H + B^T Xd            (Xd = X weighted to the chunk end)
+// C and B^T (a transposed copy that k_scores writes) come into double-buffered
+// LDS by LDS DMA; X is loaded straight into operand registers (the eight steps
+// of a lane group per register quad), and the masked scores are built once per
+// chunk in LDS by all waves.  One workgroup barrier per chunk: every buffer a
+// chunk reads is written before that chunk's barrier and rewritten only after
+// the next one.
+// ---------------------------------------------------------------------------
+constexpr int kBfThreads = 256;
+
+// XOR swizzles of the 16-byte pieces of an LDS row, chosen so that the operand
+// reads (16 rows, one piece each, per lane group) hit distinct banks
+template <int NP>
+__device__ __forceinline__ int swz_c(int i) {   // C: rows i of NP/8 pieces
+    return NP == 128 ? (i & 15) : ((i & 7) ^ ((i >> 3) & 1));
+}
+__device__ __forceinline__ int swz_m(int i) { return (i & 7) ^ ((i >> 3) & 1); }   // M: 8 pieces
+__device__ __forceinline__ int swz_bt(int n) {   // B^T: rows n of 8 pieces, read as 16 state rows
+    return ((n & 3) | (((n >> 3) & 1) << 2)) ^ ((n >> 4) & 1);
+}
+
+template <int NP, bool SO>
+__global__ __launch_bounds__(kBfThreads, 2) void k_walk_bf(Args a) {
+    constexpr bool FULL = !SO;
+    constexpr int NT = NP / 16;      // state tiles per wave
+    constexpr int KB = NP / 32;      // 32-row blocks of the state contraction
+    constexpr int GPR = NP / 8;      // 16-byte pieces per row of C
+    constexpr int NDMA = NP / 32;    // 1 KB copies per wave for C or B^T
+    constexpr int CB = kRows * NP;   // bf16 elements of one C or B^T buffer
+    constexpr int MB = kRows * kRows;
+    constexpr uint32_t kOut = 0x80000000u;   // byte offset past any buffer: reads zero
+
+    __shared__ __attribute__((aligned(16))) bf16 sBT[2 * CB];
+    __shared__ __attribute__((aligned(16))) bf16 sC[FULL ? 2 * CB : 8];
+    __shared__ __attribute__((aligned(16))) bf16 sM[FULL ? 2 * MB : 8];
+
+    // ---- workgroup -> (batch, segment, head, column group), as k_walk ------------
+    const int nsegL = SO ? a.nseg - 1 : a.nseg;
+    const int gsize = a.H * a.npg;
+    const int ngroups = (int)(gridDim.x / gsize);
+    const int id = blockIdx.x;
+    const int full = ngroups / 8 * 8 * gsize;
+    int grp, wi;
+    if (id < full) {
+        const int x = id % 8, k = id / 8;
+        grp = x + 8 * (k / gsize);
+        wi = k % gsize;
+    } else {
+        grp = id / gsize;
+        wi = id % gsize;
+    }
+    const int b = grp / nsegL, seg = grp % nsegL;
+    const int h = wi / a.npg, pg = wi % a.npg;
+    const int hg = h / (a.H / a.G);
+    const int p0 = pg * kPG;
+    const int c_begin = seg * a.cps;
+    const int c_end = min(a.nch, c_begin + a.cps);
+
+    const int tid = threadIdx.x, lane = tid % 64;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
+    const int li = lane % 16, lk = lane / 16;
+    const bool active = 16 * wave < a.P - p0;   // uniform (P is a multiple of 16)
+    const int pcol = p0 + 16 * wave + li;
+    const Views<1, true, bf16> vw(a, b, h, hg);
+    const size_t sh_off = (size_t)(b * a.H + h) * a.N * a.P;
+    const size_t bt_rows = (size_t)a.nch * a.G * (NP * kRows);
+    const Buf BTbuf = make_buf(a.BT + (size_t)b * bt_rows, bt_rows * 2);
+    const Buf Sbuf = FULL ? make_buf(a.S + (size_t)b * a.nch * a.G * MB, (size_t)a.nch * a.G * MB * 4)
+                          : make_buf(a.ld, 0);
+    // state row of tile t, row rho of the tile (rho = 4 lk + r in the accumulators)
+    auto srow = [](int t, int rho) { return 32 * (t >> 1) + 8 * (rho >> 2) + 4 * (t & 1) + (rho & 3); };
+
+    // ---- LDS DMA of C and B^T of chunk c: wave w moves pieces 64 (w + 4 m) + lane --
+    auto dma_c = [&](int c) {
+        const int t0g = c * kRows;
+        bf16* dst = sC + (c & 1) * CB;
+#pragma unroll
+        for (int m = 0; m < NDMA; ++m) {
+            const int q = wave + 4 * m;
+            const int gi = 64 * q + lane;
+            const int i = gi / GPR, g = (gi % GPR) ^ swz_c<NP>(i);
+            const uint32_t off = (uint32_t)(((t0g + i) * vw.bc_step + vw.bc_head + 8 * g) * 2) |
+                                 (8 * g < a.N ? 0u : kOut);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                vw.C.r, (__attribute__((address_space(3))) void*)(dst + 512 * q), 16, off, 0, 0, 0);
+        }
+    };
+    auto dma_bt = [&](int c) {
+        bf16* dst = sBT + (c & 1) * CB;
+#pragma unroll
+        for (int m = 0; m < NDMA; ++m) {
+            const int q = wave + 4 * m;
+            const int gi = 64 * q + lane;
+            const int n = gi / 8, g = (gi % 8) ^ swz_bt(n);
+            const uint32_t off = (uint32_t)((((c * a.G + hg) * NP + n) * kRows + 8 * g) * 2);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                BTbuf.r, (__attribute__((address_space(3))) void*)(dst + 512 * q), 16, off, 0, 0, 0);
+        }
+    };
+
+    // ---- masked-score items of this thread: causal (row, 8-column block) pairs,
+    // numbered row block by row block; 288 of them, so thread t takes item t and
+    // threads 0..31 also item 256 + t ------------------------------------------
+    int mi[2], mj[2];
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+        const int k = m == 0 ? tid : min(256 + tid, 287);
+        int r = 0;
+        while (r < 7 && 4 * (r + 1) * (r + 2) <= k) ++r;
+        const int loc = k - 4 * r * (r + 1);
+        mi[m] = 8 * r + loc / (r + 1);
+        mj[m] = loc % (r + 1);
+    }
+    const bool m2 = tid < 32;
+
+    // ---- prefetch registers -------------------------------------------------------
+    uint32_t px[16];     // X[32 k + 8 lk + q][pcol] (k = q / 8): raw bf16 bits
+    float ps[2][8];      // scores of the items
+    float pld = 0.0f;    // log-decay of step `lane`
+    const uint32_t xlane = (uint32_t)(((8 * lk) * vw.x_step + vw.x_head + pcol) * 2);
+    auto prefetch = [&](int c) {
+        const int t0g = c * kRows;
+        if (active) {
+            // the whole offset goes in the vector operand: the range check that
+            // turns steps past the sequence into zeros does not see the scalar one
+            const uint32_t xo = (uint32_t)(t0g * vw.x_step * 2) + xlane;
+#pragma unroll
+            for (int q = 0; q < 16; ++q)
+                px[q] = __builtin_amdgcn_raw_buffer_load_b16(
+                    vw.X.r, xo + (uint32_t)((32 * (q / 8) + q % 8) * vw.x_step * 2), 0, 0);
+        }
+        if constexpr (FULL) {
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+                if (m == 1 && !m2) continue;
+                const uint32_t so = (uint32_t)(((c * a.G + hg) * MB + mj[m] * (kRows * 8) + mi[m] * 8) * 4);
+                const uintx4 u0 = __builtin_amdgcn_raw_buffer_load_b128(Sbuf.r, so, 0, 0);
+                const uintx4 u1 = __builtin_amdgcn_raw_buffer_load_b128(Sbuf.r, so + 16, 0, 0);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    ps[m][e] = __uint_as_float(u0[e]);
+                    ps[m][4 + e] = __uint_as_float(u1[e]);
+                }
+            }
+        }
+        pld = bload<float>(vw.ld, (t0g + lane) * a.H + h);
+    };
+
+    // ---- state: h0 and the earlier segments --------------------------------------
+    floatx4 acc_h[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc_h[t] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+    if constexpr (FULL) if (active) {
+        if (a.h0) {
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int n = srow(t, 4 * lk + r);
+                    acc_h[t][r] = n < a.N ? a.h0[sh_off + (size_t)n * a.P + pcol] : 0.0f;
+                }
+        }
+        for (int s2 = 0; s2 < seg; ++s2) {
+            const size_t u = (size_t)(b * a.H + h) * (a.nseg - 1) + s2;
+            const float d = exp_e(a.seg_ld[u]);
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int n = srow(t, 4 * lk + r);
+                    const float hl = n < a.N ? a.seg_h[(u * a.N + n) * a.P + pcol] : 0.0f;
+                    acc_h[t][r] = fmaf(d, acc_h[t][r], hl);
+                }
+        }
+    }
+
+    // the score blocks above the diagonal stay zero in both buffers
+    if constexpr (FULL) {
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            const int e = tid + 256 * m;
+            const int i = e / 8, jb = e % 8;
+            if (8 * jb > i) {
+                *(uint4*)&sM[i * kRows + 8 * (jb ^ swz_m(i))] = make_uint4(0, 0, 0, 0);
+                *(uint4*)&sM[MB + i * kRows + 8 * (jb ^ swz_m(i))] = make_uint4(0, 0, 0, 0);
+            }
+        }
+    }
+
+    if (c_begin < c_end) {
+        if constexpr (FULL) dma_c(c_begin);
+        dma_bt(c_begin);
+        prefetch(c_begin);
+    }
+    float seg_acc = 0.0f;   // state-only pass: total log-decay of the segment
+
+    for (int c = c_begin; c < c_end; ++c) {
+        const int t0g = c * kRows;
+        vm_wait<0>();   // this wave's copies and loads of chunk c
+        const float cum = wave_scan_dpp(pld);
+        const float cum_last = readlane_f(cum, kRows - 1);
+        if constexpr (SO) seg_acc += cum_last;
+        const float wl = exp_e(cum_last - cum);   // chunk-end weight of step `lane`
+        // X operands: xo = X, xd = X weighted to the chunk end (steps 32 k + 8 lk + q)
+        uintx4 xo[2], xd[2];
+#pragma unroll
+        for (int k = 0; k < 2; ++k)
+#pragma unroll
+            for (int q2 = 0; q2 < 4; ++q2) {
+                const uint32_t lo = px[8 * k + 2 * q2] & 0xffffu, hi = px[8 * k + 2 * q2 + 1] & 0xffffu;
+                xo[k][q2] = lo | (hi << 16);
+                const int t = 32 * k + 8 * lk + 2 * q2;
+                const float w0 = __shfl(wl, t, 64), w1 = __shfl(wl, t + 1, 64);
+                xd[k][q2] = pack_bf(__uint_as_float(lo << 16) * w0, __uint_as_float(hi << 16) * w1);
+            }
+        float ey[4];
+        if constexpr (FULL) {
+            // masked scores M[i][j] = S[i][j] e^{cum_i - cum_j}, j <= i, into sM[c & 1]
+            bf16* mb = sM + (c & 1) * MB;
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+                // the lane reads run with all lanes on (a read from a lane that is
+                // off returns zero)
+                const int i = mi[m], jb = mj[m];
+                const float ci = __shfl(cum, i, 64);
+                float cjs[8];
+#pragma unroll
+                for (int q = 0; q < 8; ++q) cjs[q] = __shfl(cum, 8 * jb + q, 64);
+                if (m == 1 && !m2) continue;
+                float mv[8];
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                    const int j = 8 * jb + q;
+                    const float cj = cjs[q];
+                    const bool ok = j <= i;
+                    const float e = exp_e(ok ? ci - cj : 0.0f);
+                    mv[q] = ok ? ps[m][q] * e : 0.0f;
+                }
+                *(uint4*)&mb[i * kRows + 8 * (jb ^ swz_m(i))] =
+                    make_uint4(pack_bf(mv[0], mv[1]), pack_bf(mv[2], mv[3]), pack_bf(mv[4], mv[5]),
+                               pack_bf(mv[6], mv[7]));
+            }
+            // decay of the entering state at the output rows 16 it + li
+#pragma unroll
+            for (int it = 0; it < 4; ++it) ey[it] = exp_e(__shfl(cum, 16 * it + li, 64));
+        }
+        __syncthreads();
+        if (c + 1 < c_end) {
+            if constexpr (FULL) dma_c(c + 1);
+            dma_bt(c + 1);
+            prefetch(c + 1);
+        }
+        if (active) {
+            if constexpr (FULL) {
+                const bf16* cb = sC + (c & 1) * CB;
+                const bf16* mb = sM + (c & 1) * MB;
+                // H^T as bf16 operand: rows 32 k + 8 lk .. + 7 from tiles 2k, 2k + 1
+                uintx4 hb[KB];
+#pragma unroll
+                for (int k = 0; k < KB; ++k)
+                    hb[k] = uintx4{pack_bf(acc_h[2 * k][0], acc_h[2 * k][1]), pack_bf(acc_h[2 * k][2], acc_h[2 * k][3]),
+                                   pack_bf(acc_h[2 * k + 1][0], acc_h[2 * k + 1][1]),
+                                   pack_bf(acc_h[2 * k + 1][2], acc_h[2 * k + 1][3])};
+                floatx4 acc_y[4];
+#pragma unroll
+                for (int it = 0; it < 4; ++it) {
+                    const int i = 16 * it + li;
+                    floatx4 y0 = {0.0f, 0.0f, 0.0f, 0.0f}, y1 = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                    for (int k = 0; k < KB; ++k) {
+                        const uintx4 cv = *(const uintx4*)&cb[i * NP + 8 * ((4 * k + lk) ^ swz_c<NP>(i))];
+                        if (k % 2 == 0) y0 = mfma_bf(hb[k], cv, y0);
+                        else y1 = mfma_bf(hb[k], cv, y1);
+                    }
+                    acc_y[it] = (y0 + y1) * ey[it];
+                }
+#pragma unroll
+                for (int it = 0; it < 4; ++it) {
+                    const int i = 16 * it + li;
+#pragma unroll
+                    for (int k = 0; k < 2; ++k) {
+                        if (32 * k > 16 * it + 15) continue;   // above the diagonal
+                        const uintx4 mv = *(const uintx4*)&mb[i * kRows + 8 * ((4 * k + lk) ^ swz_m(i))];
+                        acc_y[it] = mfma_bf(xo[k], mv, acc_y[it]);
+                    }
+                }
+                // lane holds Y[t0 + 16 it + li][p0 + 16 w + 4 lk + r]
+#pragma unroll
+                for (int it = 0; it < 4; ++it) {
+                    const int tg = t0g + 16 * it + li;
+                    if (tg < a.L) {
+                        bf16* yrow = (bf16*)a.Y + (((size_t)b * a.L + tg) * a.H + h) * (size_t)a.P;
+                        *(uint2*)(yrow + p0 + 16 * wave + 4 * lk) =
+                            make_uint2(pack_bf(acc_y[it][0], acc_y[it][1]), pack_bf(acc_y[it][2], acc_y[it][3]));
+                    }
+                }
+            }
+            // H = e^{cum_last} H + B^T Xd
+            const bf16* btb = sBT + (c & 1) * CB;
+            const float tot = exp_e(cum_last);
+#pragma unroll
+            for (int t = 0; t < NT; ++t) acc_h[t] *= tot;
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                const int n = srow(t, li);
+#pragma unroll
+                for (int k = 0; k < 2; ++k) {
+                    const uintx4 bv = *(const uintx4*)&btb[n * kRows + 8 * ((4 * k + lk) ^ swz_bt(n))];
+                    acc_h[t] = mfma_bf(bv, xd[k], acc_h[t]);
+                }
+            }
+        }
+    }
+    vm_wait<0>();
+
+    // ---- outputs of the walk --------------------------------------------------------
+    if constexpr (SO) {
+        const size_t u = (size_t)(b * a.H + h) * (a.nseg - 1) + seg;
+        if (active) {
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int n = srow(t, 4 * lk + r);
+                    if (n < a.N) a.seg_h[(u * a.N + n) * a.P + pcol] = acc_h[t][r];
+                }
+        }
+        if (pg == 0 && tid == 0) a.seg_ld[u] = seg_acc;
+    } else {
+        if (a.h_out && seg == a.nseg - 1 && active) {
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int n = srow(t, 4 * lk + r);
+                    if (n < a.N) a.h_out[sh_off + (size_t)n * a.P + pcol] = acc_h[t][r];
+                }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
 struct Plan {
     int64_t nch, nseg, cps, npg;
-    size_t off_seg_h, off_seg_ld, off_seg_rev, bytes;
+    size_t off_bt, off_seg_h, off_seg_ld, off_seg_rev, bytes;
 };
 
 inline size_t align256(size_t v) { return (v + 255) / 256 * 256; }
@@ -1338,7 +1722,12 @@ Plan make_plan(bool trap, int64_t R, int64_t batch, int64_t L, int64_t H, int64_
     p.cps = p.nch > 0 ? (p.nch + best - 1) / best : 1;
     p.nseg = p.nch > 0 ? (p.nch + p.cps - 1) / p.cps : 1;
     size_t off = 0;
-    if (!trap) off = align256((size_t)(batch * p.nch * G) * kRows * kRows * 4);
+    if (!trap) {
+        // Mamba-2: scores, then the transposed B that the bf16 walk reads
+        off = align256((size_t)(batch * p.nch * G) * kRows * kRows * 4);
+        p.off_bt = off;
+        off += align256((size_t)(batch * p.nch * G) * (N <= 64 ? 64 : 128) * kRows * 2);
+    }
     p.off_seg_h = off;
     const size_t nsg = (size_t)(batch * H * (p.nseg - 1));
     off += align256(nsg * (size_t)(N * P) * 4);
@@ -1357,6 +1746,7 @@ mb_status launch(Args a, int64_t batch, const Plan& pl, char* ws, hipStream_t st
     a.cps = (int)pl.cps;
     a.npg = (int)pl.npg;
     a.S = TRAP ? nullptr : (float*)ws;
+    a.BT = TRAP ? nullptr : (bf16*)(ws + pl.off_bt);
     a.seg_h = (float*)(ws + pl.off_seg_h);
     a.seg_ld = (float*)(ws + pl.off_seg_ld);
     a.seg_rev = (float*)(ws + pl.off_seg_rev);
@@ -1367,6 +1757,21 @@ mb_status launch(Args a, int64_t batch, const Plan& pl, char* ws, hipStream_t st
         if (st != MB_OK) return st;
     }
     const int64_t per_seg = batch * a.H * a.npg;
+    if constexpr (!TRAP && !ROT && sizeof(IO) == 2) {
+        // bf16 inputs: the walk on the bf16 matrix instruction (16-byte copies of
+        // C rows need N to be a multiple of 8)
+        if (a.N % 8 == 0) {
+            if (a.nseg > 1) {
+                hipLaunchKernelGGL((k_walk_bf<NP, true>), dim3((unsigned)(per_seg * (a.nseg - 1))),
+                                   dim3(kBfThreads), 0, stream, a);
+                mb_status st = check_launch();
+                if (st != MB_OK) return st;
+            }
+            hipLaunchKernelGGL((k_walk_bf<NP, false>), dim3((unsigned)(per_seg * a.nseg)), dim3(kBfThreads),
+                               0, stream, a);
+            return check_launch();
+        }
+    }
     if (a.nseg > 1) {
         hipLaunchKernelGGL((k_walk<NP, R, TRAP, ROT, GROUPED, IO, true>),
                            dim3((unsigned)(per_seg * (a.nseg - 1))), dim3(kWalkThreads), 0, stream, a);
@@ -1484,7 +1889,7 @@ extern "C" mb_status mb_ssd_chunked(const void* X, const float* logdecay, const 
     const Plan pl = plan_for(MB_OP_SSD_CHUNKED, batch, L, H, P, G, N, 1);
     if ((st = check_ws(ws, ws_bytes, pl.bytes)) != MB_OK) return st;
     Args a{X, logdecay, B, C, nullptr, nullptr, nullptr, h0, Y, h_out, nullptr, nullptr, nullptr,
-           nullptr, (int)L, (int)H, (int)P, (int)G, (int)N, 0, 0, 0, 0};
+           nullptr, nullptr, (int)L, (int)H, (int)P, (int)G, (int)N, 0, 0, 0, 0};
     return dispatch<1, false, true>(a, batch, pl, (char*)ws, dtype, stream);
 }
 
@@ -1503,7 +1908,7 @@ extern "C" mb_status mb_trap_ssd(const void* X, const float* logdecay, const voi
     const Plan pl = plan_for(MB_OP_TRAP_SSD, batch, L, H, P, G, N, 1);
     if ((st = check_ws(ws, ws_bytes, pl.bytes)) != MB_OK) return st;
     Args a{X, logdecay, B, C, beta, gamma, theta, h0, Y, h_out, nullptr, nullptr, nullptr, nullptr,
-           (int)L, (int)H, (int)P, (int)G, (int)N, 0, 0, 0, 0};
+           nullptr, (int)L, (int)H, (int)P, (int)G, (int)N, 0, 0, 0, 0};
     return dispatch<1, true, true>(a, batch, pl, (char*)ws, dtype, stream);
 }
 
@@ -1522,7 +1927,7 @@ extern "C" mb_status mb_mimo_ssd(const void* X, const float* logdecay, const voi
     const Plan pl = plan_for(MB_OP_MIMO_SSD, batch, L, H, P, 1, N, R);
     if ((st = check_ws(ws, ws_bytes, pl.bytes)) != MB_OK) return st;
     Args a{X, logdecay, B, C, beta, gamma, theta, h0, Y, h_out, nullptr, nullptr, nullptr, nullptr,
-           (int)L, (int)H, (int)P, (int)H, (int)N, 0, 0, 0, 0};
+           nullptr, (int)L, (int)H, (int)P, (int)H, (int)N, 0, 0, 0, 0};
     char* w = (char*)ws;
     switch (R) {
         case 1: return dispatch<1, true, false>(a, batch, pl, w, dtype, stream);

@@ -159,6 +159,8 @@ def _ws(op, batch, L, H, P, G, N, R=1):
     nch, nseg = _plan(batch, L, H, P, R if op == mb.MB_OP_MIMO_SSD else 1)
     trap = op != mb.MB_OP_SSD_CHUNKED
     total = 0 if trap else _a256(batch * nch * G * 64 * 64 * 4)     # Mamba-2 scores
+    if not trap:                                                    # Mamba-2 B^T (bf16)
+        total += _a256(batch * nch * G * (64 if N <= 64 else 128) * 64 * 2)
     nsg = batch * H * (nseg - 1)
     total += _a256(nsg * N * P * 4) + _a256(nsg * 4)                  # segment states, decays
     if trap:
@@ -168,9 +170,10 @@ def _ws(op, batch, L, H, P, G, N, R=1):
 
 def test_workspace_sizes(lib):
     assert mb.mb_workspace_size(mb.MB_OP_SELECTIVE_SCAN, 8, 2048, 1, 1, 1, 16) == 0
-    # Mamba-2 block workload: 5 segments of 13 chunks; scores 4 MiB + 4 segment states
+    # Mamba-2 block workload: 5 segments of 13 chunks; scores 4 MiB + B^T 4 MiB + 4
+    # segment states
     assert mb.mb_workspace_size(mb.MB_OP_SSD_CHUNKED, 4, 4096, 24, 64, 1, 128) == \
-        4 * 64 * 64 * 64 * 4 + 4 * 24 * 4 * 128 * 64 * 4 + 1536
+        4 * 64 * 64 * 64 * 4 + 4 * 64 * 128 * 64 * 2 + 4 * 24 * 4 * 128 * 64 * 4 + 1536
     for args in [(mb.MB_OP_SSD_CHUNKED, 4, 4096, 24, 64, 1, 128), (mb.MB_OP_TRAP_SSD, 4, 4096, 24, 64, 1, 128),
                  (mb.MB_OP_SSD_CHUNKED, 2, 333, 3, 48, 1, 64), (mb.MB_OP_TRAP_SSD, 1, 2000, 2, 16, 1, 32),
                  (mb.MB_OP_TRAP_SSD, 2, 130, 4, 16, 2, 128)]:

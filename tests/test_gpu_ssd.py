@@ -24,7 +24,9 @@ def _seed(*xs):
 SSD_SHAPES = [  # batch, L, H, P, N, G
     (1, 1, 1, 16, 4, 1), (2, 65, 2, 16, 8, 1), (1, 64, 3, 32, 16, 3), (2, 130, 4, 16, 128, 2),
     (1, 200, 2, 64, 128, 1), (2, 333, 3, 48, 64, 1), (1, 129, 6, 16, 32, 2),
-    (1, 700, 2, 128, 64, 1)]   # two column groups, two sequence segments
+    (1, 700, 2, 128, 64, 1),   # two column groups, two sequence segments
+    (1, 150, 2, 32, 96, 1),    # state rows padded to 128
+    (1, 90, 2, 16, 12, 1)]     # N not a multiple of 8
 
 
 @pytest.mark.parametrize("shape", SSD_SHAPES, ids=lambda s: "x".join(map(str, s)))
