@@ -1350,6 +1350,18 @@ __global__ __launch_bounds__(kWalkThreads) void k_walk_m2s(Args a) {
 // ---------------------------------------------------------------------------
 constexpr int kBfThreads = 256;
 
+template <int V>
+struct Par {
+    static constexpr int value = V;
+};
+
+// A value the compiler cannot see through: per-load offsets built from it by
+// uniform adds are not hoisted out of the chunk loop as one register each.
+__device__ __forceinline__ uint32_t opaque(uint32_t v) {
+    asm volatile("" : "+v"(v));
+    return v;
+}
+
 // XOR swizzles of the 16-byte pieces of an LDS row, chosen so that the operand
 // reads (16 rows, one piece each, per lane group) hit distinct banks
 template <int NP>
@@ -1372,9 +1384,16 @@ __global__ __launch_bounds__(kBfThreads, 2) void k_walk_bf(Args a) {
     constexpr int MB = kRows * kRows;
     constexpr uint32_t kOut = 0x80000000u;   // byte offset past any buffer: reads zero
 
-    __shared__ __attribute__((aligned(16))) bf16 sBT[2 * CB];
-    __shared__ __attribute__((aligned(16))) bf16 sC[FULL ? 2 * CB : 8];
-    __shared__ __attribute__((aligned(16))) bf16 sM[FULL ? 2 * MB : 8];
+    // Double buffers as separate objects, and the chunk loop unrolled by two so
+    // that every access names its buffer at compile time: the compiler then sees
+    // that a copy into one buffer cannot alias reads of the other, and does not
+    // wait for the copies of the next chunk before reading this one.
+    __shared__ __attribute__((aligned(16))) bf16 sBT0[CB];
+    __shared__ __attribute__((aligned(16))) bf16 sBT1[CB];
+    __shared__ __attribute__((aligned(16))) bf16 sC0[FULL ? CB : 8];
+    __shared__ __attribute__((aligned(16))) bf16 sC1[FULL ? CB : 8];
+    __shared__ __attribute__((aligned(16))) bf16 sM0[FULL ? MB : 8];
+    __shared__ __attribute__((aligned(16))) bf16 sM1[FULL ? MB : 8];
 
     // ---- workgroup -> (batch, segment, head, column group), as k_walk ------------
     const int nsegL = SO ? a.nseg - 1 : a.nseg;
@@ -1412,31 +1431,42 @@ __global__ __launch_bounds__(kBfThreads, 2) void k_walk_bf(Args a) {
     // state row of tile t, row rho of the tile (rho = 4 lk + r in the accumulators)
     auto srow = [](int t, int rho) { return 32 * (t >> 1) + 8 * (rho >> 2) + 4 * (t & 1) + (rho & 3); };
 
-    // ---- LDS DMA of C and B^T of chunk c: wave w moves pieces 64 (w + 4 m) + lane --
-    auto dma_c = [&](int c) {
+    // ---- LDS DMA of C and B^T of chunk c into buffer PB: wave w moves pieces
+    // 64 (w + 4 m) + lane ------------------------------------------------------------
+    auto dma_c = [&](int c, auto par) {
+        constexpr int PB = decltype(par)::value;
         const int t0g = c * kRows;
-        bf16* dst = sC + (c & 1) * CB;
+        bf16* dst;
+        if constexpr (PB) dst = sC1;
+        else dst = sC0;
+        // piece m is row i0 + (4 m)(64 / GPR) of the same swizzled column group
+        const int gi0 = 64 * wave + lane;
+        const int i0 = gi0 / GPR, g = (gi0 % GPR) ^ swz_c<NP>(i0);
+        const uint32_t base = opaque((uint32_t)(((t0g + i0) * vw.bc_step + vw.bc_head + 8 * g) * 2) |
+                                     (8 * g < a.N ? 0u : kOut));
 #pragma unroll
         for (int m = 0; m < NDMA; ++m) {
             const int q = wave + 4 * m;
-            const int gi = 64 * q + lane;
-            const int i = gi / GPR, g = (gi % GPR) ^ swz_c<NP>(i);
-            const uint32_t off = (uint32_t)(((t0g + i) * vw.bc_step + vw.bc_head + 8 * g) * 2) |
-                                 (8 * g < a.N ? 0u : kOut);
+            const uint32_t off = base + (uint32_t)(m * (256 / GPR) * vw.bc_step * 2);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 vw.C.r, (__attribute__((address_space(3))) void*)(dst + 512 * q), 16, off, 0, 0, 0);
         }
     };
-    auto dma_bt = [&](int c) {
-        bf16* dst = sBT + (c & 1) * CB;
+    auto dma_bt = [&](int c, auto par) {
+        constexpr int PB = decltype(par)::value;
+        bf16* dst;
+        if constexpr (PB) dst = sBT1;
+        else dst = sBT0;
+        // piece m is row n0 + 32 m of the same swizzled column group
+        const int gi0 = 64 * wave + lane;
+        const int n0 = gi0 / 8, g = (gi0 % 8) ^ swz_bt(n0);
+        const uint32_t base = opaque((uint32_t)((((c * a.G + hg) * NP + n0) * kRows + 8 * g) * 2));
 #pragma unroll
         for (int m = 0; m < NDMA; ++m) {
             const int q = wave + 4 * m;
-            const int gi = 64 * q + lane;
-            const int n = gi / 8, g = (gi % 8) ^ swz_bt(n);
-            const uint32_t off = (uint32_t)((((c * a.G + hg) * NP + n) * kRows + 8 * g) * 2);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                BTbuf.r, (__attribute__((address_space(3))) void*)(dst + 512 * q), 16, off, 0, 0, 0);
+                BTbuf.r, (__attribute__((address_space(3))) void*)(dst + 512 * q), 16,
+                base + (uint32_t)(m * 32 * kRows * 2), 0, 0, 0);
         }
     };
 
@@ -1465,7 +1495,7 @@ __global__ __launch_bounds__(kBfThreads, 2) void k_walk_bf(Args a) {
         if (active) {
             // the whole offset goes in the vector operand: the range check that
             // turns steps past the sequence into zeros does not see the scalar one
-            const uint32_t xo = (uint32_t)(t0g * vw.x_step * 2) + xlane;
+            const uint32_t xo = opaque((uint32_t)(t0g * vw.x_step * 2) + xlane);
 #pragma unroll
             for (int q = 0; q < 16; ++q)
                 px[q] = __builtin_amdgcn_raw_buffer_load_b16(
@@ -1523,20 +1553,22 @@ __global__ __launch_bounds__(kBfThreads, 2) void k_walk_bf(Args a) {
             const int e = tid + 256 * m;
             const int i = e / 8, jb = e % 8;
             if (8 * jb > i) {
-                *(uint4*)&sM[i * kRows + 8 * (jb ^ swz_m(i))] = make_uint4(0, 0, 0, 0);
-                *(uint4*)&sM[MB + i * kRows + 8 * (jb ^ swz_m(i))] = make_uint4(0, 0, 0, 0);
+                *(uint4*)&sM0[i * kRows + 8 * (jb ^ swz_m(i))] = make_uint4(0, 0, 0, 0);
+                *(uint4*)&sM1[i * kRows + 8 * (jb ^ swz_m(i))] = make_uint4(0, 0, 0, 0);
             }
         }
     }
 
     if (c_begin < c_end) {
-        if constexpr (FULL) dma_c(c_begin);
-        dma_bt(c_begin);
+        if constexpr (FULL) dma_c(c_begin, Par<0>{});
+        dma_bt(c_begin, Par<0>{});
         prefetch(c_begin);
     }
     float seg_acc = 0.0f;   // state-only pass: total log-decay of the segment
 
-    for (int c = c_begin; c < c_end; ++c) {
+    // one chunk; its operands sit in buffer PB, the next chunk's go to 1 - PB
+    auto chunk = [&](int c, auto par) __attribute__((always_inline)) {
+        constexpr int PB = decltype(par)::value;
         const int t0g = c * kRows;
         vm_wait<0>();   // this wave's copies and loads of chunk c
         const float cum = wave_scan_dpp(pld);
@@ -1557,8 +1589,10 @@ __global__ __launch_bounds__(kBfThreads, 2) void k_walk_bf(Args a) {
             }
         float ey[4];
         if constexpr (FULL) {
-            // masked scores M[i][j] = S[i][j] e^{cum_i - cum_j}, j <= i, into sM[c & 1]
-            bf16* mb = sM + (c & 1) * MB;
+            // masked scores M[i][j] = S[i][j] e^{cum_i - cum_j}, j <= i, into buffer PB
+            bf16* mb;
+            if constexpr (PB) mb = sM1;
+            else mb = sM0;
 #pragma unroll
             for (int m = 0; m < 2; ++m) {
                 // the lane reads run with all lanes on (a read from a lane that is
@@ -1588,14 +1622,21 @@ __global__ __launch_bounds__(kBfThreads, 2) void k_walk_bf(Args a) {
         }
         __syncthreads();
         if (c + 1 < c_end) {
-            if constexpr (FULL) dma_c(c + 1);
-            dma_bt(c + 1);
+            if constexpr (FULL) dma_c(c + 1, Par<1 - PB>{});
+            dma_bt(c + 1, Par<1 - PB>{});
             prefetch(c + 1);
         }
         if (active) {
             if constexpr (FULL) {
-                const bf16* cb = sC + (c & 1) * CB;
-                const bf16* mb = sM + (c & 1) * MB;
+                const bf16* cb;
+                const bf16* mb;
+                if constexpr (PB) {
+                    cb = sC1;
+                    mb = sM1;
+                } else {
+                    cb = sC0;
+                    mb = sM0;
+                }
                 // H^T as bf16 operand: rows 32 k + 8 lk .. + 7 from tiles 2k, 2k + 1
                 uintx4 hb[KB];
 #pragma unroll
@@ -1638,7 +1679,9 @@ __global__ __launch_bounds__(kBfThreads, 2) void k_walk_bf(Args a) {
                 }
             }
             // H = e^{cum_last} H + B^T Xd
-            const bf16* btb = sBT + (c & 1) * CB;
+            const bf16* btb;
+            if constexpr (PB) btb = sBT1;
+            else btb = sBT0;
             const float tot = exp_e(cum_last);
 #pragma unroll
             for (int t = 0; t < NT; ++t) acc_h[t] *= tot;
@@ -1652,6 +1695,10 @@ __global__ __launch_bounds__(kBfThreads, 2) void k_walk_bf(Args a) {
                 }
             }
         }
+    };
+    for (int c = c_begin; c < c_end; c += 2) {
+        chunk(c, Par<0>{});
+        if (c + 1 < c_end) chunk(c + 1, Par<1>{});
     }
     vm_wait<0>();
 
