@@ -7,7 +7,8 @@ already resident in HBM:
   m1_scan    Mamba-1 selective scan, batch 8, L 2048, D 1536, N 16, fp32
   m1_step    Mamba-1 decode step, 256 sequences, D 1536, N 16, fp32, in place
   ssd_f32    Mamba-2 SSD, batch 4, L 4096, H 24, P 64, N 128, G 1, fp32
-  ssd_bf16   the same with bf16 X/B/C/Y (fp32 accumulation and state)
+  ssd_bf16   the same with bf16 X/B/C/Y (bf16 matrix operands, fp32
+             accumulation and state)
   siso       Mamba-3 SISO trapezoid + rotations, shapes of ssd_f32, fp32
   mimo       Mamba-3 MIMO rank 4, batch 2, L 8192, H 16, P 64, N 128, fp32
 
@@ -169,7 +170,7 @@ class SSD(Workload):
         self.dtype = dtype
         if dtype == "bf16":
             self.bound = "hbm"
-            self.kernel = "k_scores + k_walk (state-only pass) + k_walk (full pass)"
+            self.kernel = "k_scores + k_walk_bf (state-only pass) + k_walk_bf (full pass)"
 
     def run(self):
         self.mb.mb_ssd_chunked(self.X, self.ld, self.B, self.C, None, Y=self.Y, h_out=self.h, ws=self.ws)

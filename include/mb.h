@@ -18,6 +18,10 @@
  *   fp32 with fp32 accumulation; states are always fp32; a bf16 output is
  *   rounded to nearest-even.  (TorchMamba README, API notes: half-precision
  *   inputs compute in fp32, outputs take the input dtype, states stay fp32.)
+ *   One exception: mb_ssd_chunked with MB_BF16 and N a multiple of 8 runs its
+ *   matrix products on bf16 operands with fp32 accumulation.  The operands are
+ *   the inputs and three rounded intermediates: a copy of the state (the
+ *   carried state stays fp32), the masked scores and the chunk-end-weighted X.
  * - NaN or Inf inputs propagate to the outputs; they are not trapped.
  * - Outputs must not overlap inputs, except where an entry point says so.
  * - The chunked SSD entry points read X, B, C and write Y with 16-byte vector
@@ -117,6 +121,8 @@ mb_status mb_ssm_step(const void* x, const void* dt, const float* A,
  * ws / ws_bytes: device workspace of at least mb_workspace_size(MB_OP_SSD_CHUNKED, ...)
  * bytes, 256-byte aligned; contents on entry are ignored.
  * Supported: N <= 128 and N % 4 == 0, P % 16 == 0.
+ * With MB_BF16 and N % 8 == 0 the products take bf16 operands (fp32
+ * accumulation, fp32 state; see the dtype note at the top).
  */
 mb_status mb_ssd_chunked(const void* X, const float* logdecay, const void* B,
                          const void* C, const float* h0, void* Y, float* h_out,
