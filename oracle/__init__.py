@@ -17,6 +17,8 @@ Which passage each loop follows is cited at the loop in ``oracle.c``:
   trap               - TorchMamba README (Math notes M3 SISO);
                        mamba3-minimal README (Two-SSD Decomposition)
   mimo               - TorchMamba README (Math notes MIMO)
+  ssd_step           - the same recurrences one token at a time, state in the
+                       physical frame (Math notes M2, M3 SISO, MIMO)
 """
 from __future__ import annotations
 
@@ -62,6 +64,7 @@ def _load():
         lib.oracle_ssd.argtypes = [_D] * 7 + [_I] * 6
         lib.oracle_trap.argtypes = [_D] * 10 + [_I] * 6
         lib.oracle_mimo.argtypes = [_D] * 10 + [_I] * 6
+        lib.oracle_ssd_step.argtypes = [_D] * 12 + [_I] * 6
         lib.oracle_set_threads.argtypes = [ctypes.c_int]
         lib.oracle_get_threads.restype = ctypes.c_int
         _lib = lib
@@ -204,3 +207,45 @@ def mimo(X, logdecay, B, C, beta, gamma, theta=None, h0=None):
     _load().oracle_mimo(_p(X), _p(logdecay), _p(B), _p(C), _p(beta), _p(gamma),
                         _p(theta), _p(h0), _p(Y), _p(h), b, L, H, P, N, R)
     return Y, h
+
+
+def ssd_step(X, logdecay, B, C, h=None, beta=None, gamma=None, theta=None, X_prev=None, B_prev=None):
+    """One decode token of the SSD family, physical-frame state.
+    X, X_prev (b, H, P[, R]); B, C, B_prev (b, G, N[, R]); logdecay, beta,
+    gamma (b, H); theta (b, H, N/2); h (b, H, N, P).  Without the R axis, R = 1.
+    beta None = 0, gamma None = 1, theta None = no rotation, X_prev / B_prev /
+    h None = 0.  Returns (Y, h_out) with Y shaped like X."""
+    X = _f64(X)
+    squeeze = X.ndim == 3
+    if squeeze:
+        X = X[..., None]
+    b, H, P, R = X.shape
+    B = _f64(B)
+    if B.ndim == 3:
+        B = B[..., None]
+    G, N = B.shape[1], B.shape[2]
+    if G <= 0 or H % G:
+        raise ValueError("H must be a multiple of G")
+    if theta is not None and N % 2:
+        raise ValueError("rotation needs an even N")
+
+    def r4(a, shape, name):
+        if a is None:
+            return None
+        a = _f64(a)
+        return _chk(a[..., None] if a.ndim == len(shape) - 1 else a, shape, name)
+
+    B = _chk(B, (b, G, N, R), "B")
+    C = r4(C, (b, G, N, R), "C")
+    B_prev = r4(B_prev, (b, G, N, R), "B_prev")
+    X_prev = r4(X_prev, (b, H, P, R), "X_prev")
+    logdecay = _chk(logdecay, (b, H), "logdecay")
+    beta = _opt(beta, (b, H))
+    gamma = _opt(gamma, (b, H))
+    theta = _opt(theta, (b, H, N // 2))
+    h = _opt(h, (b, H, N, P))
+    Y = np.empty((b, H, P, R))
+    hout = np.empty((b, H, N, P))
+    _load().oracle_ssd_step(_p(X), _p(logdecay), _p(B), _p(C), _p(beta), _p(gamma), _p(theta),
+                            _p(X_prev), _p(B_prev), _p(h), _p(Y), _p(hout), b, H, P, G, N, R)
+    return (Y[..., 0] if squeeze else Y), hout

@@ -330,3 +330,79 @@ void oracle_mimo(const double *X, const double *logdecay, const double *B,
         free(S); free(Theta); free(Bt); free(Ct); free(Bprev); free(Xprev);
     }
 }
+
+/*
+ * Decode step of the SSD family, one token per (b, h), state in the physical
+ * (unrotated) frame.  The rotated-frame state of oracle_trap / oracle_mimo is
+ * S~_t = R(Theta_t) S_t (pairwise along N); since plane rotations compose
+ * additively, R(-Theta_t) R(Theta_{t-1}) = R(-theta_t), and the recurrence
+ * needs only this step's angle increment and the unrotated B, C:
+ *     S_t = R(-theta_t) (exp(ld_t) S_{t-1} + beta_t sum_r Bp_r (x) Xp_r)
+ *           + gamma_t sum_r B_r (x) X_r
+ *     Y_r = S_t^T C_r
+ * where Bp, Xp are the previous token's B and X (TorchMamba README, Math notes
+ * M3 SISO and MIMO; Mamba-2, Math notes M2, is beta = 0, gamma = 1, no
+ * rotation).  Layouts: X, X_prev, Y (batch, H, P, R); B, C, B_prev
+ * (batch, G, N, R), head h reading group h / (H/G); logdecay, beta, gamma
+ * (batch, H); theta (batch, H, N/2); h_in, h_out (batch, H, N, P).
+ * beta NULL = 0, gamma NULL = 1, theta NULL = no rotation, X_prev / B_prev
+ * NULL = 0, h_in NULL = 0.
+ */
+void oracle_ssd_step(const double *X, const double *logdecay, const double *B,
+                     const double *C, const double *beta, const double *gamma,
+                     const double *theta, const double *X_prev,
+                     const double *B_prev, const double *h_in, double *Y,
+                     double *h_out, int64_t batch, int64_t H, int64_t P,
+                     int64_t G, int64_t N, int64_t R)
+{
+    int64_t units = batch * H;
+    int64_t hpg = H / G;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t u = 0; u < units; ++u) {
+        int64_t b = u / H, h = u % H, g = h / hpg;
+        size_t np = (size_t)(N * P > 0 ? N * P : 1);
+        double *T = (double *)malloc(sizeof(double) * np);
+        double *S = (double *)malloc(sizeof(double) * np);
+        const double *Bt = B + (b * G + g) * N * R;      /* [n][r] */
+        const double *Ct = C + (b * G + g) * N * R;
+        const double *Xt = X + (b * H + h) * P * R;      /* [p][r] */
+        const double *Bp = B_prev ? B_prev + (b * G + g) * N * R : NULL;
+        const double *Xp = X_prev ? X_prev + (b * H + h) * P * R : NULL;
+        double a = exp(logdecay[b * H + h]);
+        double be = beta ? beta[b * H + h] : 0.0;
+        double ga = gamma ? gamma[b * H + h] : 1.0;
+        /* T = exp(ld) S + beta sum_r Bp_r (x) Xp_r */
+        for (int64_t n = 0; n < N; ++n)
+            for (int64_t p = 0; p < P; ++p) {
+                double prev = 0.0;
+                if (Bp && Xp)
+                    for (int64_t r = 0; r < R; ++r) prev += Bp[n * R + r] * Xp[p * R + r];
+                double s0 = h_in ? h_in[(b * H + h) * N * P + n * P + p] : 0.0;
+                T[n * P + p] = a * s0 + be * prev;
+            }
+        /* rotate every column by -theta: the new token's frame */
+        if (theta) {
+            for (int64_t p = 0; p < P; ++p)
+                rotate_pairs(S + p, T + p, theta + (b * H + h) * (N / 2), N, P, -1.0);
+        } else {
+            memcpy(S, T, sizeof(double) * (size_t)(N * P));
+        }
+        /* + gamma sum_r B_r (x) X_r */
+        for (int64_t n = 0; n < N; ++n)
+            for (int64_t p = 0; p < P; ++p) {
+                double cur = 0.0;
+                for (int64_t r = 0; r < R; ++r) cur += Bt[n * R + r] * Xt[p * R + r];
+                S[n * P + p] += ga * cur;
+            }
+        double *Yt = Y + (b * H + h) * P * R;
+        for (int64_t p = 0; p < P; ++p)
+            for (int64_t r = 0; r < R; ++r) {
+                double acc = 0.0;
+                for (int64_t n = 0; n < N; ++n) acc += S[n * P + p] * Ct[n * R + r];
+                Yt[p * R + r] = acc;
+            }
+        if (h_out)
+            memcpy(h_out + (b * H + h) * N * P, S, sizeof(double) * (size_t)(N * P));
+        free(T); free(S);
+    }
+}

@@ -37,6 +37,11 @@ MUTATIONS = {
     "mimo_rank_index": ("cur += Bt[n * R + r] * Xt[p * R + r];", "cur += Bt[n * R + r] * Xt[p * R];"),
     "mimo_output_rank": ("acc += S[n * P + p] * Ct[n * R + r];", "acc += S[n * P + p] * Ct[n * R];"),
     "decay_halved": ("double a = exp(logdecay[bth]);", "double a = exp(0.5 * logdecay[bth]);"),
+    "step_beta_uses_current_B": ("prev += Bp[n * R + r] * Xp[p * R + r];", "prev += Bt[n * R + r] * Xp[p * R + r];"),
+    "step_rotation_sign": ("rotate_pairs(S + p, T + p, theta + (b * H + h) * (N / 2), N, P, -1.0);",
+                           "rotate_pairs(S + p, T + p, theta + (b * H + h) * (N / 2), N, P, 1.0);"),
+    "step_gamma_rotated": ("S[n * P + p] += ga * cur;", "S[n * P + p] += ga * cur * (theta ? 0.5 : 1.0);"),
+    "step_decay_dropped": ("T[n * P + p] = a * s0 + be * prev;", "T[n * P + p] = s0 + be * prev;"),
 }
 
 
@@ -78,6 +83,17 @@ def _battery(o):
     Yp, hp = forms.mimo_physical_step_loop(**inp)
     if not (np.allclose(Y, Yp, rtol=1e-9, atol=1e-11) and np.allclose(h, hp, rtol=1e-9, atol=1e-11)):
         failed.append("mimo_physical_step")
+
+    inp = wl.trap_inputs(rng, 1, 9, 2, 3, 6, G=1, h0_sd=0.5)
+    Y, h = o.trap(**inp)
+    hs, ys = inp["h0"], []
+    for t in range(9):
+        yt, hs = o.ssd_step(inp["X"][:, t], inp["logdecay"][:, t], inp["B"][:, t], inp["C"][:, t], hs,
+                            inp["beta"][:, t], inp["gamma"][:, t], inp["theta"][:, t],
+                            inp["X"][:, t - 1] if t else None, inp["B"][:, t - 1] if t else None)
+        ys.append(yt)
+    if not (np.allclose(np.stack(ys, 1), Y, rtol=1e-9, atol=1e-11) and np.allclose(hs, h, rtol=1e-9, atol=1e-11)):
+        failed.append("trap_steps_vs_forward")
     return failed
 
 
