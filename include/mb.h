@@ -177,6 +177,36 @@ mb_status mb_mimo_ssd(const void* X, const float* logdecay, const void* B,
                       hipStream_t stream);
 
 /*
+ * Decode step of the SSD family: one token per sequence, state in the physical
+ * (unrotated) frame (TorchMamba README, Math notes M3 SISO and MIMO: plane
+ * rotations compose additively, so the rotated-frame recurrence needs only the
+ * token's angle increment and the unrotated B, C; Mamba-2, Math notes M2, is
+ * beta = gamma = theta = NULL).  Per batch b and head h, group g = h / (H/G):
+ *     S' = R(-theta) (exp(logdecay) S + beta sum_r Bp_r (outer) Xp_r)
+ *          + gamma sum_r B_r (outer) X_r
+ *     Y_r = S'^T C_r
+ * R(phi) rotates consecutive state-row pairs (2k, 2k+1) by phi[k]; Bp, Xp are
+ * the previous token's B and X.  The final state of mb_ssd_chunked,
+ * mb_trap_ssd or mb_mimo_ssd (physical frame) continues exactly with this step,
+ * passing that call's last B and X as B_prev, X_prev.
+ *   X, X_prev, Y : (batch, H, P, R)   dtype   (R = 1: (batch, H, P))
+ *   B, C, B_prev : (batch, G, N, R)   dtype   (MIMO: G = H, per head)
+ *   logdecay, beta, gamma : (batch, H) fp32; beta NULL = 0, gamma NULL = 1
+ *   theta        : (batch, H, N/2)  fp32 angle increments, or NULL (no rotation)
+ *   h_in, h_out  : (batch, H, N, P) fp32, 16-byte aligned; h_in NULL = zeros;
+ *                  h_out == h_in (in place) is allowed
+ * X_prev and B_prev are both given or both NULL (NULL: zeros, the first token
+ * of a sequence).  Supported: H % G == 0, P % 4 == 0 and P <= 1024, N even,
+ * R in {1, 2, 4, 8, 16}.  No workspace.
+ */
+mb_status mb_ssd_step(const void* X, const float* logdecay, const void* B,
+                      const void* C, const float* beta, const float* gamma,
+                      const float* theta, const void* X_prev, const void* B_prev,
+                      const float* h_in, float* h_out, void* Y, int64_t batch,
+                      int64_t H, int64_t P, int64_t G, int64_t N, int64_t R,
+                      mb_dtype dtype, hipStream_t stream);
+
+/*
  * Bytes of device workspace an entry point needs for the given sizes (0 if it
  * needs none).  Unused sizes are ignored: G for MB_OP_TRAP_SSD / MIMO, R for
  * the others.  Returns 0 for invalid sizes as well (the call itself reports

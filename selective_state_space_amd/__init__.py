@@ -16,7 +16,7 @@ import threading
 
 __all__ = [
     "mb_selective_scan", "mb_ssm_step", "mb_ssd_chunked", "mb_trap_ssd", "mb_mimo_ssd",
-    "mb_workspace_size", "mb_status_str", "lib_path", "load_library", "MBError",
+    "mb_ssd_step", "mb_workspace_size", "mb_status_str", "lib_path", "load_library", "MBError",
     "MB_OP_SELECTIVE_SCAN", "MB_OP_SSM_STEP", "MB_OP_SSD_CHUNKED", "MB_OP_TRAP_SSD",
     "MB_OP_MIMO_SSD",
 ]
@@ -68,6 +68,9 @@ def load_library():
             lib.mb_workspace_size.restype = ctypes.c_size_t
             for f in ("mb_ssd_chunked", "mb_trap_ssd", "mb_mimo_ssd"):
                 getattr(lib, f).restype = ctypes.c_int
+        if hasattr(lib, "mb_ssd_step"):
+            lib.mb_ssd_step.argtypes = [_vp] * 12 + [_i64] * 6 + [ctypes.c_int, _vp]
+            lib.mb_ssd_step.restype = ctypes.c_int
         lib.mb_status_str.argtypes = [ctypes.c_int]
         lib.mb_status_str.restype = ctypes.c_char_p
         lib.mb_last_hip_error.restype = ctypes.c_int
@@ -277,4 +280,38 @@ def mb_mimo_ssd(X, logdecay, B, C, beta, gamma, theta=None, h0=None, *, chunk=0,
     _call("mb_mimo_ssd", _ptr(X), _ptr(logdecay), _ptr(B), _ptr(C), _ptr(beta), _ptr(gamma),
           _ptr(theta), _ptr(h0), _ptr(Y), _ptr(h_out), b, L, H, P, N, R, chunk, code, _ptr(ws), nws,
           _stream(dev))
+    return Y, h_out
+
+
+def mb_ssd_step(X, logdecay, B, C, h, *, beta=None, gamma=None, theta=None, X_prev=None, B_prev=None,
+                Y=None, h_out=None):
+    """Decode step of the SSD family (one token per sequence), state in the
+    physical frame.  X, X_prev (batch, H, P[, R]); B, C, B_prev (batch, G, N[, R])
+    in one dtype; logdecay, beta, gamma (batch, H), theta (batch, H, N/2) and
+    h (batch, H, N, P) float32.  Mamba-2: beta, gamma, theta None.  With
+    h_out=None the state is updated in place.  Returns (Y, h_out), Y shaped
+    like X."""
+    torch = _torch()
+    dev = _device_of(X)
+    dtype = X.dtype
+    code = _dtype_code(X, "X")
+    ranked = X.dim() == 4
+    b, H, P = X.shape[:3]
+    R = X.shape[3] if ranked else 1
+    G, N = B.shape[1], B.shape[2]
+    xs = (b, H, P, R) if ranked else (b, H, P)
+    bs = (b, G, N, R) if ranked else (b, G, N)
+    f32 = torch.float32
+    _check(B, "B", bs, dtype, dev)
+    _check(C, "C", bs, dtype, dev)
+    _check(X_prev, "X_prev", xs, dtype, dev)
+    _check(B_prev, "B_prev", bs, dtype, dev)
+    for t, n in ((logdecay, "logdecay"), (beta, "beta"), (gamma, "gamma")):
+        _check(t, n, (b, H), f32, dev)
+    _check(theta, "theta", (b, H, N // 2), f32, dev)
+    _check(h, "h", (b, H, N, P), f32, dev)
+    h_out = h if h_out is None else _check(h_out, "h_out", (b, H, N, P), f32, dev)
+    Y = torch.empty(xs, dtype=dtype, device=dev) if Y is None else _check(Y, "Y", xs, dtype, dev)
+    _call("mb_ssd_step", _ptr(X), _ptr(logdecay), _ptr(B), _ptr(C), _ptr(beta), _ptr(gamma), _ptr(theta),
+          _ptr(X_prev), _ptr(B_prev), _ptr(h), _ptr(h_out), _ptr(Y), b, H, P, G, N, R, code, _stream(dev))
     return Y, h_out

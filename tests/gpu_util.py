@@ -7,7 +7,7 @@ import torch
 
 TOL = {"f32": 1e-4, "bf16": 2e-2}
 # Names of the "activation" tensors that take the run dtype; all others stay fp32.
-ACT = {"x", "dt", "B", "C", "X"}
+ACT = {"x", "dt", "B", "C", "X", "X_prev", "B_prev"}
 
 
 def require_gpu():

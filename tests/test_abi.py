@@ -34,7 +34,7 @@ def declared_functions():
 def test_exports_every_declared_function(lib):
     names = declared_functions()
     assert {"mb_selective_scan", "mb_ssm_step", "mb_ssd_chunked", "mb_trap_ssd", "mb_mimo_ssd",
-            "mb_workspace_size", "mb_status_str", "mb_last_hip_error", "mb_version"} <= set(names)
+            "mb_ssd_step", "mb_workspace_size", "mb_status_str", "mb_last_hip_error", "mb_version"} <= set(names)
     for n in names:
         assert hasattr(lib, n), "libmb.so does not export " + n
 
@@ -92,6 +92,30 @@ def test_step_validation(lib):
     # partial overlap between h_out and h_in is rejected (exact aliasing is allowed)
     assert step(lib, h_out=FAKE + (1 << 26) + 64) == E_ALIAS
     assert step(lib, y=FAKE + 8) == E_ALIAS
+
+
+def ssd_step(lib, X=FAKE, B=FAKE + (1 << 22), Bp=None, Xp=None, h_in=FAKE + (1 << 26), h_out=FAKE + (1 << 26),
+             Y=FAKE + (1 << 27), theta=None, batch=2, H=4, P_=64, G=1, N=128, R=1, dtype=F32):
+    q = lambda v: P(v) if v else None
+    return lib.mb_ssd_step(q(X), P(FAKE + (1 << 21)), q(B), P(FAKE + (1 << 23)), None, None, q(theta), q(Xp), q(Bp),
+                           q(h_in), q(h_out), q(Y), batch, H, P_, G, N, R, dtype, None)
+
+
+def test_ssd_step_validation(lib):
+    assert ssd_step(lib, dtype=2) == E_DTYPE
+    assert ssd_step(lib, G=3) == E_SHAPE            # H % G != 0
+    assert ssd_step(lib, N=7) == E_SHAPE            # odd N
+    assert ssd_step(lib, P_=6) == E_SHAPE           # P % 4 != 0
+    assert ssd_step(lib, P_=1028) == E_SHAPE        # P > 1024
+    assert ssd_step(lib, R=3) == E_SHAPE
+    assert ssd_step(lib, X=0) == E_NULL
+    assert ssd_step(lib, Y=0) == E_NULL
+    assert ssd_step(lib, Bp=FAKE + (1 << 24)) == E_NULL   # B_prev without X_prev
+    assert ssd_step(lib, h_out=FAKE + (1 << 26) + 8) == E_ALIGN
+    assert ssd_step(lib, h_out=FAKE + (1 << 26) + 256) == E_ALIAS   # partial overlap with h_in
+    assert ssd_step(lib, Y=FAKE + 64) == E_ALIAS      # Y over X
+    assert ssd_step(lib, h_in=None, h_out=FAKE + (1 << 22)) == E_ALIAS   # h_out over B
+    assert ssd_step(lib, batch=0) == OK
 
 
 def ssd(lib, ws=FAKE + (1 << 28), ws_bytes=1 << 30, H=4, P_=64, G=1, N=128, L=100, chunk=0,
