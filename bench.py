@@ -18,9 +18,11 @@ sequences).  Per-workload times come from HIP events recorded on the stream the
 kernels run on, over the same timed steps.  The `roofline` object is for the
 workload whose kernels take the largest share of the step; `kernels` lists
 every workload.  `cpu_baseline` times the fp64 oracle on a bounded sample of the
-same workloads on the host cores.
+same workloads on the host cores.  `next` times, beside the step and outside its
+token count, the decode steps of the SSD family (one token for 256 sequences:
+Mamba-2, SISO and MIMO on the block shapes; bound by HBM).
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--only a,b] [--no-cpu]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--only a,b] [--no-cpu] [--no-next]
 """
 from __future__ import annotations
 
@@ -76,6 +78,17 @@ def mimo_work(b, L, H, P, N, R, Q=64):
     nbytes = 4 * (2 * b * L * H * P * R + 2 * b * L * H * N * R + 3 * b * L * H + b * L * H * N // 2 + b * H * N * P)
     flops = b * L * H * (4 * N * P * R + R * R * (Qt + 1) * (N + P))
     return nbytes, flops
+
+
+def ssd_step_work(b, H, P, N, G, R, trap, rot, es=4):
+    """One decode token: the fp32 state read and written once, plus the token's
+    inputs and output."""
+    nbytes = 4 * 2 * b * H * N * P + es * (2 * b * H * P * R + 2 * b * G * N * R) + 4 * b * H
+    if trap:
+        nbytes += es * (b * H * P * R + b * G * N * R) + 4 * 2 * b * H
+    if rot:
+        nbytes += 4 * b * H * (N // 2)
+    return nbytes
 
 
 # ----------------------------------------------------------------------------
@@ -232,7 +245,38 @@ class MIMO(Workload):
                             Y=self.Y, h_out=self.h, ws=self.ws)
 
 
+class SSDDecode(Workload):
+    """Decode step of the SSD family (outside the timed step: measured next to it)."""
+    kernel = "k_ssd_step"
+    source = "selective_state_space_amd/csrc/ssd_step.hip"
+
+    def __init__(self, mb, wl, torch, model):
+        self.mb = mb
+        self.name = model + "_decode"
+        inp = wl.ssd_decode(model)
+        self.inp = inp
+        f = torch.float32
+        self.t = {k: (_dev(v, f) if v is not None else None) for k, v in inp.items()}
+        X, B = inp["X"], inp["B"]
+        b, H, P = X.shape[:3]
+        R = X.shape[3] if X.ndim == 4 else 1
+        G, N = B.shape[1], B.shape[2]
+        self.shape = dict(batch=b, H=H, P=P, N=N, G=G, R=R, trapezoid=model != "m2", rotation=model != "m2")
+        self.tokens = b
+        self.bytes = ssd_step_work(b, H, P, N, G, R, model != "m2", model != "m2")
+        self.flops = self.exps = None
+        self.Y = torch.empty_like(self.t["X"])
+
+    def run(self):
+        t = self.t
+        self.mb.mb_ssd_step(t["X"], t["logdecay"], t["B"], t["C"], t["h"], beta=t.get("beta"),
+                            gamma=t.get("gamma"), theta=t.get("theta"), X_prev=t.get("X_prev"),
+                            B_prev=t.get("B_prev"), Y=self.Y)
+
+
 ALL = ["m1_scan", "m1_step", "ssd_f32", "ssd_bf16", "siso", "mimo"]
+# measured beside the step, not part of it: the decode steps of the SSD family
+NEXT = ["m2_decode", "siso_decode", "mimo_decode"]
 
 
 def make(name, mb, wl, torch):
@@ -248,6 +292,8 @@ def make(name, mb, wl, torch):
         return SISO(mb, wl, torch)
     if name == "mimo":
         return MIMO(mb, wl, torch)
+    if name.endswith("_decode"):
+        return SSDDecode(mb, wl, torch, name[:-len("_decode")])
     raise ValueError(name)
 
 
@@ -337,6 +383,32 @@ def cold_ms(torch, w, reps=5):
     return float(np.median(ms))
 
 
+def time_next(args, mb, wl, torch):
+    """Decode steps of the SSD family, timed with HIP events on the stream they
+    run on, outside the step (they are not part of its token count)."""
+    res = []
+    for n in NEXT:
+        print("# preparing %s" % n, file=sys.stderr, flush=True)
+        w = make(n, mb, wl, torch)
+        for _ in range(args.warmup):
+            w.run()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+        for e0, e1 in ev:
+            e0.record()
+            w.run()
+            e1.record()
+        torch.cuda.synchronize()
+        ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev]))
+        r = roofline_of(w, ms)
+        res.append({"workload": w.name, "kernel": w.kernel, "shape": w.shape, "ms": round(ms, 5),
+                    "tokens_per_s": w.tokens / (ms * 1e-3),
+                    "roofline": {k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}})
+        del w
+    return res
+
+
 def copy_calibration(torch, reps=5):
     """A plain device-to-device copy of 256 MiB, repeated: the reference that the
     rocprofv3 FETCH_SIZE / WRITE_SIZE counters are scaled by."""
@@ -361,6 +433,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-cold", action="store_true",
                     help="skip the per-workload timings after a last-level-cache flush")
+    ap.add_argument("--no-next", action="store_true",
+                    help="skip the decode steps of the SSD family measured beside the step")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy (reference for rocprofv3 byte counters)")
     args = ap.parse_args()
@@ -448,6 +522,8 @@ def main():
         "roofline": roof,
         "kernels": kernels,
     }
+    if not args.no_next and not args.only:
+        out["next"] = time_next(args, mb, wl, torch)
     if not args.no_cpu:
         print("# timing the oracle on the host", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(ws)

@@ -193,8 +193,10 @@ mb_status mb_mimo_ssd(const void* X, const float* logdecay, const void* B,
  *   B, C, B_prev : (batch, G, N, R)   dtype   (MIMO: G = H, per head)
  *   logdecay, beta, gamma : (batch, H) fp32; beta NULL = 0, gamma NULL = 1
  *   theta        : (batch, H, N/2)  fp32 angle increments, or NULL (no rotation)
- *   h_in, h_out  : (batch, H, N, P) fp32, 16-byte aligned; h_in NULL = zeros;
- *                  h_out == h_in (in place) is allowed
+ *   h_in, h_out  : (batch, H, N, P) fp32; h_in NULL = zeros; h_out == h_in (in
+ *                  place) is allowed
+ * Every tensor pointer except logdecay, beta, gamma and theta must be 16-byte
+ * aligned (MB_ERR_ALIGN): rows are read and written with 16-byte accesses.
  * X_prev and B_prev are both given or both NULL (NULL: zeros, the first token
  * of a sequence).  Supported: H % G == 0, P % 4 == 0 and P <= 1024, N even,
  * R in {1, 2, 4, 8, 16}.  No workspace.

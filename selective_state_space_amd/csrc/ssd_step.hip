@@ -24,8 +24,48 @@ namespace {
 
 constexpr int kStepThreads = 256;
 
-template <typename T>
-__device__ __forceinline__ float ld_act(const T* p, size_t i) { return to_f32(p[i]); }
+// The R ranks of one row, elements e .. e + R - 1 (e a multiple of R, the base
+// 16-byte aligned), widened to fp32, with the widest loads the alignment allows.
+template <int R, typename IO>
+__device__ __forceinline__ void ld_ranks(const IO* p, size_t e, float* o) {
+    if constexpr (sizeof(IO) == 4) {
+        if constexpr (R >= 4) {
+#pragma unroll
+            for (int i = 0; i < R; i += 4) {
+                const float4 v = *(const float4*)((const float*)p + e + i);
+                o[i] = v.x; o[i + 1] = v.y; o[i + 2] = v.z; o[i + 3] = v.w;
+            }
+        } else if constexpr (R == 2) {
+            const float2 v = *(const float2*)((const float*)p + e);
+            o[0] = v.x; o[1] = v.y;
+        } else {
+            o[0] = ((const float*)p)[e];
+        }
+    } else {
+        const bf16* q = (const bf16*)p + e;
+        if constexpr (R >= 8) {
+#pragma unroll
+            for (int i = 0; i < R; i += 8) {
+                const uint4 v = *(const uint4*)(q + i);
+                const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    o[i + 2 * k] = __uint_as_float(w[k] << 16);
+                    o[i + 2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
+                }
+            }
+        } else if constexpr (R == 4) {
+            const uint2 v = *(const uint2*)q;
+            o[0] = __uint_as_float(v.x << 16); o[1] = __uint_as_float(v.x & 0xffff0000u);
+            o[2] = __uint_as_float(v.y << 16); o[3] = __uint_as_float(v.y & 0xffff0000u);
+        } else if constexpr (R == 2) {
+            const uint32_t v = *(const uint32_t*)q;
+            o[0] = __uint_as_float(v << 16); o[1] = __uint_as_float(v & 0xffff0000u);
+        } else {
+            o[0] = to_f32(q[0]);
+        }
+    }
+}
 
 // sin / cos of an angle in radians through the hardware units, which take the
 // argument in revolutions; the whole turns are removed first
@@ -60,68 +100,85 @@ __global__ __launch_bounds__(kStepThreads) void k_ssd_step(
     const size_t bo = ((size_t)b * G + g) * (size_t)N * R;
     float xv[4][R], xp[4][R], y[4][R];
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 4; ++j) {
+        const size_t e = xo + (size_t)(4 * q + j) * R;
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            const size_t e = xo + (size_t)(4 * q + j) * R + r;
-            xv[j][r] = on ? ld_act(X, e) : 0.0f;
-            xp[j][r] = (on && prev) ? ld_act(X_prev, e) : 0.0f;
+            xv[j][r] = 0.0f;
+            xp[j][r] = 0.0f;
             y[j][r] = 0.0f;
         }
+        if (on) ld_ranks<R>(X, e, xv[j]);
+        if (on && prev) ld_ranks<R>(X_prev, e, xp[j]);
+    }
 
     const size_t so = (size_t)bh * N * P;
     if (on) {
-        for (int k = rg; 2 * k < N; k += RG) {
-            const int n0 = 2 * k, n1 = 2 * k + 1;
-            float4 s0 = make_float4(0.0f, 0.0f, 0.0f, 0.0f), s1 = s0;
-            if (h_in) {
-                s0 = *(const float4*)(h_in + so + (size_t)n0 * P + 4 * q);
-                s1 = *(const float4*)(h_in + so + (size_t)n1 * P + 4 * q);
-            }
-            float t0[4] = {a * s0.x, a * s0.y, a * s0.z, a * s0.w};
-            float t1[4] = {a * s1.x, a * s1.y, a * s1.z, a * s1.w};
-            if (prev) {
+        // row pairs k0, k0 + RG, ... in batches of KU: the batch's state loads are
+        // all issued before its first store (in place, a later load may not pass
+        // an earlier store, so without batching one pair would be in flight)
+        constexpr int KU = 4;
+        for (int k0 = rg; 2 * k0 < N; k0 += KU * RG) {
+            float4 s0[KU], s1[KU];
 #pragma unroll
-                for (int r = 0; r < R; ++r) {
-                    const float bp0 = be * ld_act(B_prev, bo + (size_t)n0 * R + r);
-                    const float bp1 = be * ld_act(B_prev, bo + (size_t)n1 * R + r);
+            for (int u = 0; u < KU; ++u) {
+                const int k = k0 + u * RG;
+                s0[u] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+                s1[u] = s0[u];
+                if (h_in && 2 * k < N) {
+                    s0[u] = *(const float4*)(h_in + so + (size_t)(2 * k) * P + 4 * q);
+                    s1[u] = *(const float4*)(h_in + so + (size_t)(2 * k + 1) * P + 4 * q);
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < KU; ++u) {
+                const int k = k0 + u * RG;
+                if (2 * k >= N) break;
+                const int n0 = 2 * k, n1 = 2 * k + 1;
+                float t0[4] = {a * s0[u].x, a * s0[u].y, a * s0[u].z, a * s0[u].w};
+                float t1[4] = {a * s1[u].x, a * s1[u].y, a * s1[u].z, a * s1[u].w};
+                if (prev) {
+                    float bp0[R], bp1[R];
+                    ld_ranks<R>(B_prev, bo + (size_t)n0 * R, bp0);
+                    ld_ranks<R>(B_prev, bo + (size_t)n1 * R, bp1);
+#pragma unroll
+                    for (int r = 0; r < R; ++r)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            t0[j] = fmaf(be * bp0[r], xp[j][r], t0[j]);
+                            t1[j] = fmaf(be * bp1[r], xp[j][r], t1[j]);
+                        }
+                }
+                if constexpr (ROT) {
+                    // R(-theta) on the pair (n0, n1): (c v0 + s v1, -s v0 + c v1)
+                    float sn, cs;
+                    sincos_turns(theta[(size_t)bh * (N / 2) + k], &sn, &cs);
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
-                        t0[j] = fmaf(bp0, xp[j][r], t0[j]);
-                        t1[j] = fmaf(bp1, xp[j][r], t1[j]);
+                        const float v0 = t0[j], v1 = t1[j];
+                        t0[j] = fmaf(cs, v0, sn * v1);
+                        t1[j] = fmaf(cs, v1, -sn * v0);
                     }
                 }
+                float b0[R], b1[R], c0[R], c1[R];
+                ld_ranks<R>(B, bo + (size_t)n0 * R, b0);
+                ld_ranks<R>(B, bo + (size_t)n1 * R, b1);
+                ld_ranks<R>(C, bo + (size_t)n0 * R, c0);
+                ld_ranks<R>(C, bo + (size_t)n1 * R, c1);
+#pragma unroll
+                for (int r = 0; r < R; ++r)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        t0[j] = fmaf(ga * b0[r], xv[j][r], t0[j]);
+                        t1[j] = fmaf(ga * b1[r], xv[j][r], t1[j]);
+                    }
+                *(float4*)(h_out + so + (size_t)n0 * P + 4 * q) = make_float4(t0[0], t0[1], t0[2], t0[3]);
+                *(float4*)(h_out + so + (size_t)n1 * P + 4 * q) = make_float4(t1[0], t1[1], t1[2], t1[3]);
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+#pragma unroll
+                    for (int r = 0; r < R; ++r) y[j][r] = fmaf(t0[j], c0[r], fmaf(t1[j], c1[r], y[j][r]));
             }
-            if constexpr (ROT) {
-                // R(-theta) on the pair (n0, n1): (c v0 + s v1, -s v0 + c v1)
-                float sn, cs;
-                sincos_turns(theta[(size_t)bh * (N / 2) + k], &sn, &cs);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const float v0 = t0[j], v1 = t1[j];
-                    t0[j] = fmaf(cs, v0, sn * v1);
-                    t1[j] = fmaf(cs, v1, -sn * v0);
-                }
-            }
-            float c0[R], c1[R];
-#pragma unroll
-            for (int r = 0; r < R; ++r) {
-                const float b0 = ga * ld_act(B, bo + (size_t)n0 * R + r);
-                const float b1 = ga * ld_act(B, bo + (size_t)n1 * R + r);
-                c0[r] = ld_act(C, bo + (size_t)n0 * R + r);
-                c1[r] = ld_act(C, bo + (size_t)n1 * R + r);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    t0[j] = fmaf(b0, xv[j][r], t0[j]);
-                    t1[j] = fmaf(b1, xv[j][r], t1[j]);
-                }
-            }
-            *(float4*)(h_out + so + (size_t)n0 * P + 4 * q) = make_float4(t0[0], t0[1], t0[2], t0[3]);
-            *(float4*)(h_out + so + (size_t)n1 * P + 4 * q) = make_float4(t1[0], t1[1], t1[2], t1[3]);
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-#pragma unroll
-                for (int r = 0; r < R; ++r) y[j][r] = fmaf(t0[j], c0[r], fmaf(t1[j], c1[r], y[j][r]));
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j)
@@ -187,7 +244,9 @@ extern "C" mb_status mb_ssd_step(const void* X, const float* logdecay, const voi
     if (batch == 0) return MB_OK;
     if (!X || !logdecay || !B || !C || !h_out || !Y) return MB_ERR_NULL;
     if ((X_prev == nullptr) != (B_prev == nullptr)) return MB_ERR_NULL;
-    if (((uintptr_t)h_in | (uintptr_t)h_out) & 15) return MB_ERR_ALIGN;
+    if (((uintptr_t)h_in | (uintptr_t)h_out | (uintptr_t)X | (uintptr_t)X_prev | (uintptr_t)B |
+         (uintptr_t)B_prev | (uintptr_t)C | (uintptr_t)Y) & 15)
+        return MB_ERR_ALIGN;
     const size_t es = dtype_size(dtype);
     const size_t n_x = (size_t)(batch * H * P * R), n_bc = (size_t)(batch * G * N * R);
     const size_t n_s = (size_t)(batch * H), n_h = (size_t)(batch * H * N * P);

@@ -16,6 +16,8 @@ expand 2 for Mamba-1, d_head 64 / d_state 128 for the SSD family):
 * ssd_block   seed 103: batch 4, L 4096, H 24, P 64, N 128, G 1.
 * siso_block  seed 104: as ssd_block, with trapezoid mix and rotary angles.
 * mimo_block  seed 105: batch 2, L 8192, H 16, P 64, N 128, R 4.
+* ssd_decode  seeds 107 (Mamba-2), 108 (SISO), 109 (MIMO): one token for 256
+              sequences on the block shapes, state ~ N(0, 0.1).
 """
 from __future__ import annotations
 
@@ -159,3 +161,47 @@ def mimo_inputs(rng, batch, L, H, P, N, R, h0_sd=0.0, rotate=True):
 
 def mimo_block(seed=105, batch=2, L=8192, H=16, P=64, N=128, R=4):
     return mimo_inputs(np.random.default_rng(seed), batch, L, H, P, N, R)
+
+
+def ssd_step_inputs(rng, batch, H, P, G, N, R, kind, h_sd=0.1):
+    """One decode token of the SSD family.  kind "m2": X, B, C, logdecay and the
+    state; "trap": also beta, gamma and the previous token's X, B; "rot": also
+    the angle increments theta.  X, B, C ~ N(0,1)/sqrt(N R); dt = softplus(N(-3,1)),
+    A_h = -U(1,16), logdecay = dt A_h; lambda = sigmoid(N(0,1)), beta = (1-lambda)
+    dt alpha, gamma = lambda dt; theta = U(0, pi) dt; state ~ N(0, h_sd).
+    Order: X, B, C, dt, A_h, state, then lambda, X_prev, B_prev, theta.  With
+    R = 1 the rank axis is dropped."""
+    s = 1.0 / np.sqrt(N * R)
+    shp_x, shp_b = (batch, H, P, R), (batch, G, N, R)
+    d = dict(X=rng.standard_normal(shp_x) * s, B=rng.standard_normal(shp_b) * s,
+             C=rng.standard_normal(shp_b) * s)
+    dt = _softplus(rng.normal(-3.0, 1.0, (batch, H)))
+    ld = dt * -rng.uniform(1.0, 16.0, H)
+    d["logdecay"] = ld
+    d["h"] = rng.normal(0.0, h_sd, (batch, H, N, P))
+    if kind != "m2":
+        lam = _sigmoid(rng.standard_normal((batch, H)))
+        d["beta"] = (1.0 - lam) * dt * np.exp(ld)
+        d["gamma"] = lam * dt
+        d["X_prev"] = rng.standard_normal(shp_x) * s
+        d["B_prev"] = rng.standard_normal(shp_b) * s
+        if kind == "rot":
+            d["theta"] = rng.uniform(0.0, np.pi, (batch, H, N // 2)) * dt[..., None]
+    if R == 1:
+        for k in ("X", "B", "C", "X_prev", "B_prev"):
+            if k in d:
+                d[k] = d[k][..., 0]
+    return d
+
+
+def ssd_decode(model):
+    """The decode workloads: 256 sequences on the block shapes.  "m2": H 24,
+    P 64, N 128, G 1; "siso": the same with trapezoid and rotation; "mimo": H 16,
+    P 64, N 128, R 4, with trapezoid and rotation."""
+    if model == "m2":
+        return ssd_step_inputs(np.random.default_rng(107), 256, 24, 64, 1, 128, 1, "m2")
+    if model == "siso":
+        return ssd_step_inputs(np.random.default_rng(108), 256, 24, 64, 1, 128, 1, "rot")
+    if model == "mimo":
+        return ssd_step_inputs(np.random.default_rng(109), 256, 16, 64, 16, 128, 4, "rot")
+    raise ValueError(model)

@@ -112,6 +112,8 @@ def test_ssd_step_validation(lib):
     assert ssd_step(lib, Y=0) == E_NULL
     assert ssd_step(lib, Bp=FAKE + (1 << 24)) == E_NULL   # B_prev without X_prev
     assert ssd_step(lib, h_out=FAKE + (1 << 26) + 8) == E_ALIGN
+    assert ssd_step(lib, X=FAKE + 4) == E_ALIGN
+    assert ssd_step(lib, B=FAKE + (1 << 22) + 8) == E_ALIGN
     assert ssd_step(lib, h_out=FAKE + (1 << 26) + 256) == E_ALIAS   # partial overlap with h_in
     assert ssd_step(lib, Y=FAKE + 64) == E_ALIAS      # Y over X
     assert ssd_step(lib, h_in=None, h_out=FAKE + (1 << 22)) == E_ALIAS   # h_out over B

@@ -21,31 +21,7 @@ def _gpu():
 
 
 def _step_inputs(rng, b, H, P, G, N, R, kind, h_sd=0.3):
-    """One token: X, B, C ~ N(0,1)/sqrt(N R); the previous token's X, B; the
-    decay and trapezoid coefficients and angle increments as the SISO workload
-    (dt = softplus(N(-3,1)), A_h = -U(1,16), lambda = sigmoid(N(0,1)), theta =
-    U(0, pi) dt); state ~ N(0, h_sd)."""
-    s = 1.0 / np.sqrt(N * R)
-    shp_x, shp_b = (b, H, P, R), (b, G, N, R)
-    d = dict(X=rng.standard_normal(shp_x) * s, B=rng.standard_normal(shp_b) * s,
-             C=rng.standard_normal(shp_b) * s)
-    dt = np.log1p(np.exp(rng.normal(-3.0, 1.0, (b, H))))
-    ld = dt * -rng.uniform(1.0, 16.0, H)
-    d["logdecay"] = ld
-    d["h"] = rng.normal(0.0, h_sd, (b, H, N, P))
-    if kind != "m2":
-        lam = 1.0 / (1.0 + np.exp(-rng.standard_normal((b, H))))
-        d["beta"] = (1.0 - lam) * dt * np.exp(ld)
-        d["gamma"] = lam * dt
-        d["X_prev"] = rng.standard_normal(shp_x) * s
-        d["B_prev"] = rng.standard_normal(shp_b) * s
-        if kind == "rot":
-            d["theta"] = rng.uniform(0.0, np.pi, (b, H, N // 2)) * dt[..., None]
-    if R == 1:
-        for k in ("X", "B", "C", "X_prev", "B_prev"):
-            if k in d:
-                d[k] = d[k][..., 0]
-    return d
+    return wl.ssd_step_inputs(rng, b, H, P, G, N, R, kind, h_sd=h_sd)
 
 
 def _run(dev):
@@ -131,11 +107,10 @@ def test_decode_after_chunked_prefill(oracle_mod, model):
     assert_close(h, hr, "f32", "h")
 
 
-def test_ssd_step_block_workload(oracle_mod):
-    """256 sequences, H 24, P 64, N 128, with rotation and the previous token:
-    the configuration the step is measured on."""
-    inp = _step_inputs(np.random.default_rng(31), 256, 24, 64, 1, 128, 1, "rot", h_sd=0.1)
-    dev, ref = prepare(inp, "f32")
+@pytest.mark.parametrize("model", ["m2", "siso", "mimo"])
+def test_ssd_step_decode_workloads(oracle_mod, model):
+    """The measured decode workloads: 256 sequences on the block shapes."""
+    dev, ref = prepare(wl.ssd_decode(model), "f32")
     Y, h = _run(dev)
     torch.cuda.synchronize()
     Yr, hr = oracle_mod.ssd_step(**ref)
