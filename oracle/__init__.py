@@ -62,8 +62,8 @@ def _load():
         lib.oracle_m1_scan.argtypes = [_D] * 9 + [_I] * 4
         lib.oracle_m1_step.argtypes = [_D] * 9 + [_I] * 3
         lib.oracle_ssd.argtypes = [_D] * 7 + [_I] * 6
-        lib.oracle_trap.argtypes = [_D] * 10 + [_I] * 6
-        lib.oracle_mimo.argtypes = [_D] * 10 + [_I] * 6
+        lib.oracle_trap.argtypes = [_D] * 12 + [_I] * 6
+        lib.oracle_mimo.argtypes = [_D] * 12 + [_I] * 6
         lib.oracle_ssd_step.argtypes = [_D] * 12 + [_I] * 6
         lib.oracle_set_threads.argtypes = [ctypes.c_int]
         lib.oracle_get_threads.restype = ctypes.c_int
@@ -161,9 +161,10 @@ def ssd(X, logdecay, B, C, h0=None):
     return Y, h
 
 
-def trap(X, logdecay, B, C, beta, gamma, theta=None, h0=None):
+def trap(X, logdecay, B, C, beta, gamma, theta=None, h0=None, X_prev=None, B_prev=None):
     """Mamba-3 SISO.  X (b, L, H, P); logdecay, beta, gamma (b, L, H);
-    B, C (b, L, G, N); theta (b, L, H, N/2) or None."""
+    B, C (b, L, G, N); theta (b, L, H, N/2) or None; X_prev (b, H, P) and
+    B_prev (b, G, N): the token before the call, or None (zeros)."""
     X = _f64(X)
     b, L, H, P = X.shape
     B = _f64(B)
@@ -179,16 +180,19 @@ def trap(X, logdecay, B, C, beta, gamma, theta=None, h0=None):
     C = _chk(C, (b, L, G, N), "C")
     theta = _opt(theta, (b, L, H, N // 2))
     h0 = _opt(h0, (b, H, N, P))
+    X_prev = _opt(X_prev, (b, H, P))
+    B_prev = _opt(B_prev, (b, G, N))
     Y = np.empty((b, L, H, P))
     h = np.empty((b, H, N, P))
     _load().oracle_trap(_p(X), _p(logdecay), _p(B), _p(C), _p(beta), _p(gamma),
-                        _p(theta), _p(h0), _p(Y), _p(h), b, L, H, P, G, N)
+                        _p(theta), _p(h0), _p(X_prev), _p(B_prev), _p(Y), _p(h), b, L, H, P, G, N)
     return Y, h
 
 
-def mimo(X, logdecay, B, C, beta, gamma, theta=None, h0=None):
+def mimo(X, logdecay, B, C, beta, gamma, theta=None, h0=None, X_prev=None, B_prev=None):
     """Mamba-3 MIMO.  X (b, L, H, P, R); B, C (b, L, H, N, R);
-    logdecay, beta, gamma (b, L, H); theta (b, L, H, N/2) or None."""
+    logdecay, beta, gamma (b, L, H); theta (b, L, H, N/2) or None; X_prev
+    (b, H, P, R) and B_prev (b, H, N, R): the token before the call, or None."""
     X = _f64(X)
     b, L, H, P, R = X.shape
     B = _f64(B)
@@ -202,10 +206,12 @@ def mimo(X, logdecay, B, C, beta, gamma, theta=None, h0=None):
     C = _chk(C, (b, L, H, N, R), "C")
     theta = _opt(theta, (b, L, H, N // 2))
     h0 = _opt(h0, (b, H, N, P))
+    X_prev = _opt(X_prev, (b, H, P, R))
+    B_prev = _opt(B_prev, (b, H, N, R))
     Y = np.empty((b, L, H, P, R))
     h = np.empty((b, H, N, P))
     _load().oracle_mimo(_p(X), _p(logdecay), _p(B), _p(C), _p(beta), _p(gamma),
-                        _p(theta), _p(h0), _p(Y), _p(h), b, L, H, P, N, R)
+                        _p(theta), _p(h0), _p(X_prev), _p(B_prev), _p(Y), _p(h), b, L, H, P, N, R)
     return Y, h
 
 

@@ -183,16 +183,19 @@ static void rotate_pairs(double *dst, const double *src, const double *phi,
  *     Bt_t = R(Theta_t) B_t,  Ct_t = R(Theta_t) C_t     (pairs 2k, 2k+1)
  *     S_t = exp(ld_t) S_{t-1} + beta_t Bt_{t-1} (x) X_{t-1} + gamma_t Bt_t (x) X_t
  *     Y_t = S_t^T Ct_t
- * with Bt_{-1} = X_{-1} = 0.  h0 is given in the physical (unrotated) frame,
- * which equals the rotated frame at Theta = 0, and h_out is returned in the
- * physical frame: h_out = R(-Theta_{L-1}) S_{L-1}.  theta == NULL means no
- * rotation (the real-valued path).
+ * with Bt_{-1} = X_{-1} given by B_prev0 (batch, G, N) and X_prev0 (batch, H, P),
+ * the token before the call, or 0 when NULL.  Theta restarts at 0 each call, so
+ * Bt_{-1} = B_{-1}: the physical frame.  h0 is given in the physical
+ * (unrotated) frame, which equals the rotated frame at Theta = 0, and h_out is
+ * returned in the physical frame: h_out = R(-Theta_{L-1}) S_{L-1}.
+ * theta == NULL means no rotation (the real-valued path).
  */
 void oracle_trap(const double *X, const double *logdecay, const double *B,
                  const double *C, const double *beta, const double *gamma,
-                 const double *theta, const double *h0, double *Y,
-                 double *h_out, int64_t batch, int64_t L, int64_t H, int64_t P,
-                 int64_t G, int64_t N)
+                 const double *theta, const double *h0, const double *X_prev0,
+                 const double *B_prev0, double *Y, double *h_out,
+                 int64_t batch, int64_t L, int64_t H, int64_t P, int64_t G,
+                 int64_t N)
 {
     int64_t units = batch * H;
     int64_t hpg = H / G;
@@ -207,6 +210,8 @@ void oracle_trap(const double *X, const double *logdecay, const double *B,
         double *Ct = (double *)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1));
         double *Bprev = (double *)calloc((size_t)(N > 0 ? N : 1), sizeof(double));
         double *Xprev = (double *)calloc((size_t)(P > 0 ? P : 1), sizeof(double));
+        if (B_prev0) memcpy(Bprev, B_prev0 + (b * G + g) * N, sizeof(double) * (size_t)N);
+        if (X_prev0) memcpy(Xprev, X_prev0 + (b * H + h) * P, sizeof(double) * (size_t)P);
         for (int64_t i = 0; i < N * P; ++i)
             S[i] = h0 ? h0[(b * H + h) * N * P + i] : 0.0;
         for (int64_t t = 0; t < L; ++t) {
@@ -258,13 +263,15 @@ void oracle_trap(const double *X, const double *logdecay, const double *B,
  *                              + gamma_t sum_r Bt_{t,r} (x) X_{t,r}
  *     Y_{t,r} = S_t^T Ct_{t,r}
  * where every rank r of step t is rotated by the same per-head Theta_t as in
- * the SISO loop above.  h0 / h_out in the physical frame.
+ * the SISO loop above.  h0 / h_out in the physical frame; the token before the
+ * call is B_prev0 (batch, H, N, R) and X_prev0 (batch, H, P, R), or 0 when NULL.
  */
 void oracle_mimo(const double *X, const double *logdecay, const double *B,
                  const double *C, const double *beta, const double *gamma,
-                 const double *theta, const double *h0, double *Y,
-                 double *h_out, int64_t batch, int64_t L, int64_t H, int64_t P,
-                 int64_t N, int64_t R)
+                 const double *theta, const double *h0, const double *X_prev0,
+                 const double *B_prev0, double *Y, double *h_out,
+                 int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N,
+                 int64_t R)
 {
     int64_t units = batch * H;
     int64_t K = N / 2;
@@ -280,6 +287,8 @@ void oracle_mimo(const double *X, const double *logdecay, const double *B,
         double *Ct = (double *)malloc(sizeof(double) * nr);
         double *Bprev = (double *)calloc(nr, sizeof(double));
         double *Xprev = (double *)calloc(pr, sizeof(double));
+        if (B_prev0) memcpy(Bprev, B_prev0 + (b * H + h) * N * R, sizeof(double) * (size_t)(N * R));
+        if (X_prev0) memcpy(Xprev, X_prev0 + (b * H + h) * P * R, sizeof(double) * (size_t)(P * R));
         for (int64_t i = 0; i < N * P; ++i)
             S[i] = h0 ? h0[(b * H + h) * N * P + i] : 0.0;
         for (int64_t t = 0; t < L; ++t) {

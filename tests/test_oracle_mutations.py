@@ -42,6 +42,9 @@ MUTATIONS = {
                            "rotate_pairs(S + p, T + p, theta + (b * H + h) * (N / 2), N, P, 1.0);"),
     "step_gamma_rotated": ("S[n * P + p] += ga * cur;", "S[n * P + p] += ga * cur * (theta ? 0.5 : 1.0);"),
     "step_decay_dropped": ("T[n * P + p] = a * s0 + be * prev;", "T[n * P + p] = s0 + be * prev;"),
+    "trap_prev0_ignored": ("if (B_prev0) memcpy(Bprev, B_prev0 + (b * G + g) * N, sizeof(double) * (size_t)N);", ""),
+    "mimo_prev0_wrong_head": ("if (X_prev0) memcpy(Xprev, X_prev0 + (b * H + h) * P * R, sizeof(double) * (size_t)(P * R));",
+                              "if (X_prev0) memcpy(Xprev, X_prev0 + b * H * P * R, sizeof(double) * (size_t)(P * R));"),
 }
 
 
@@ -94,6 +97,18 @@ def _battery(o):
         ys.append(yt)
     if not (np.allclose(np.stack(ys, 1), Y, rtol=1e-9, atol=1e-11) and np.allclose(hs, h, rtol=1e-9, atol=1e-11)):
         failed.append("trap_steps_vs_forward")
+
+    for fn, mk in (("trap", lambda: wl.trap_inputs(rng, 2, 20, 2, 3, 6, G=1, h0_sd=0.5)),
+                   ("mimo", lambda: wl.mimo_inputs(rng, 1, 20, 2, 3, 6, 2, h0_sd=0.5))):
+        inp = mk()
+        Y, h = getattr(o, fn)(**inp)
+        cut = lambda sl: {k: (v[:, sl] if k != "h0" and v is not None else v) for k, v in inp.items()}
+        _, ha = getattr(o, fn)(**cut(slice(0, 8)))
+        rest = cut(slice(8, None))
+        rest["h0"] = ha
+        Yb, hb = getattr(o, fn)(**rest, X_prev=inp["X"][:, 7], B_prev=inp["B"][:, 7])
+        if not (np.allclose(Yb, Y[:, 8:], rtol=1e-9, atol=1e-11) and np.allclose(hb, h, rtol=1e-9, atol=1e-11)):
+            failed.append(fn + "_split_with_previous_token")
     return failed
 
 

@@ -131,6 +131,41 @@ def test_siso_split_chaining(oracle_mod):
 
 
 @pytest.mark.parametrize("rotate", [False, True])
+def test_siso_split_chaining_with_previous_token(oracle_mod, rotate):
+    """With the token before the split passed as X_prev, B_prev, two calls chain
+    exactly whatever the cross-boundary weight."""
+    rng = np.random.default_rng(4650 + rotate)
+    inp = wl.trap_inputs(rng, 2, 90, 3, 4, 6, G=3, h0_sd=0.5, rotate=rotate)
+    assert np.all(inp["beta"] > 0)
+    Y, h = oracle_mod.trap(**inp)
+    s = 41
+    cut = lambda sl: {k: (v[:, sl] if k not in ("h0",) and v is not None else v) for k, v in inp.items()}
+    Ya, ha = oracle_mod.trap(**cut(slice(0, s)))
+    b = cut(slice(s, None))
+    b["h0"] = ha
+    Yb, hb = oracle_mod.trap(**b, X_prev=inp["X"][:, s - 1], B_prev=inp["B"][:, s - 1])
+    close(np.concatenate([Ya, Yb], 1), Y, rtol=1e-9, atol=1e-11)
+    close(hb, h, rtol=1e-9, atol=1e-11)
+    # without the previous token the second part differs
+    Yc, _ = oracle_mod.trap(**b)
+    assert np.max(np.abs(Yc - Y[:, s:])) > 1e-6
+
+
+def test_mimo_split_chaining_with_previous_token(oracle_mod):
+    rng = np.random.default_rng(4660)
+    inp = wl.mimo_inputs(rng, 2, 70, 2, 5, 8, 3, h0_sd=0.5)
+    Y, h = oracle_mod.mimo(**inp)
+    s = 29
+    cut = lambda sl: {k: (v[:, sl] if k not in ("h0",) and v is not None else v) for k, v in inp.items()}
+    Ya, ha = oracle_mod.mimo(**cut(slice(0, s)))
+    b = cut(slice(s, None))
+    b["h0"] = ha
+    Yb, hb = oracle_mod.mimo(**b, X_prev=inp["X"][:, s - 1], B_prev=inp["B"][:, s - 1])
+    close(np.concatenate([Ya, Yb], 1), Y, rtol=1e-9, atol=1e-11)
+    close(hb, h, rtol=1e-9, atol=1e-11)
+
+
+@pytest.mark.parametrize("rotate", [False, True])
 def test_mimo_as_r2_siso_calls(oracle_mod, rotate):
     """MIMO equals R^2 SISO calls (TorchMamba README, Math notes MIMO):
     Y_r = sum_r' SISO(X_r', B_r', C_r), with h0 entered in one term only."""
