@@ -138,21 +138,28 @@ mb_status mb_ssd_chunked(const void* X, const float* logdecay, const void* B,
  *     B~_t = R(Theta_t) B_t,  C~_t = R(Theta_t) C_t   (consecutive pairs 2k, 2k+1)
  *     S_t = exp(logdecay_t) S_{t-1} + beta_t B~_{t-1} (x) X_{t-1} + gamma_t B~_t (x) X_t
  *     Y_t = S_t^T C~_t
- * with B~_{-1} = X_{-1} = 0.  R(phi) = [[cos, -sin], [sin, cos]].
+ * with B~_{-1} = B_prev and X_{-1} = X_prev, the token before the call (zeros
+ * when both are NULL; Theta restarts at 0 per call, so B~_{-1} is B_prev
+ * unrotated).  R(phi) = [[cos, -sin], [sin, cos]].  A sequence split across
+ * calls chains exactly when each call after the first gets h0 = the previous
+ * call's h_out and X_prev, B_prev = the previous call's last X and B.
  *   X, Y                   : (batch, L, H, P)    dtype
  *   logdecay, beta, gamma  : (batch, L, H)       fp32 (alpha = exp(logdecay))
  *   B, C                   : (batch, L, G, N)    dtype
  *   theta                  : (batch, L, H, N/2)  fp32, or NULL for no rotation
  *   h0, h_out              : (batch, H, N, P)    fp32, in the PHYSICAL (unrotated)
  *                            frame: h_out = R(-Theta_{L-1}) S_{L-1}
+ *   X_prev                 : (batch, H, P)       dtype, or NULL
+ *   B_prev                 : (batch, G, N)       dtype, or NULL (with X_prev)
+ * X_prev and B_prev are both given or both NULL; 16-byte aligned like X, B.
  * N must be even when theta != NULL.  Other limits as mb_ssd_chunked.
  */
 mb_status mb_trap_ssd(const void* X, const float* logdecay, const void* B,
                       const void* C, const float* beta, const float* gamma,
-                      const float* theta, const float* h0, void* Y,
-                      float* h_out, int64_t batch, int64_t L, int64_t H,
-                      int64_t P, int64_t G, int64_t N, int64_t chunk,
-                      mb_dtype dtype, void* ws, size_t ws_bytes,
+                      const float* theta, const float* h0, const void* X_prev,
+                      const void* B_prev, void* Y, float* h_out, int64_t batch,
+                      int64_t L, int64_t H, int64_t P, int64_t G, int64_t N,
+                      int64_t chunk, mb_dtype dtype, void* ws, size_t ws_bytes,
                       hipStream_t stream);
 
 /*
@@ -166,14 +173,16 @@ mb_status mb_trap_ssd(const void* X, const float* logdecay, const void* B,
  *   X, Y      : (batch, L, H, P, R)  dtype     (rank innermost)
  *   B, C      : (batch, L, H, N, R)  dtype     (per head, rank innermost)
  *   logdecay, beta, gamma, theta, h0, h_out : as mb_trap_ssd (state has no R axis)
+ *   X_prev    : (batch, H, P, R)     dtype, or NULL   (the token before the call,
+ *   B_prev    : (batch, H, N, R)     dtype, or NULL    as mb_trap_ssd)
  * Supported: R in {1, 2, 4, 8, 16}; other limits as mb_trap_ssd.
  */
 mb_status mb_mimo_ssd(const void* X, const float* logdecay, const void* B,
                       const void* C, const float* beta, const float* gamma,
-                      const float* theta, const float* h0, void* Y,
-                      float* h_out, int64_t batch, int64_t L, int64_t H,
-                      int64_t P, int64_t N, int64_t R, int64_t chunk,
-                      mb_dtype dtype, void* ws, size_t ws_bytes,
+                      const float* theta, const float* h0, const void* X_prev,
+                      const void* B_prev, void* Y, float* h_out, int64_t batch,
+                      int64_t L, int64_t H, int64_t P, int64_t N, int64_t R,
+                      int64_t chunk, mb_dtype dtype, void* ws, size_t ws_bytes,
                       hipStream_t stream);
 
 /*

@@ -62,8 +62,8 @@ def load_library():
         lib.mb_ssm_step.argtypes = [_vp] * 9 + [_i64] * 3 + [ctypes.c_int, _vp]
         if hasattr(lib, "mb_ssd_chunked"):
             lib.mb_ssd_chunked.argtypes = [_vp] * 7 + [_i64] * 7 + [ctypes.c_int, _vp, ctypes.c_size_t, _vp]
-            lib.mb_trap_ssd.argtypes = [_vp] * 10 + [_i64] * 7 + [ctypes.c_int, _vp, ctypes.c_size_t, _vp]
-            lib.mb_mimo_ssd.argtypes = [_vp] * 10 + [_i64] * 7 + [ctypes.c_int, _vp, ctypes.c_size_t, _vp]
+            lib.mb_trap_ssd.argtypes = [_vp] * 12 + [_i64] * 7 + [ctypes.c_int, _vp, ctypes.c_size_t, _vp]
+            lib.mb_mimo_ssd.argtypes = [_vp] * 12 + [_i64] * 7 + [ctypes.c_int, _vp, ctypes.c_size_t, _vp]
             lib.mb_workspace_size.argtypes = [ctypes.c_int] + [_i64] * 8
             lib.mb_workspace_size.restype = ctypes.c_size_t
             for f in ("mb_ssd_chunked", "mb_trap_ssd", "mb_mimo_ssd"):
@@ -227,11 +227,12 @@ def mb_ssd_chunked(X, logdecay, B, C, h0=None, *, chunk=0, Y=None, h_out=None, w
     return Y, h_out
 
 
-def mb_trap_ssd(X, logdecay, B, C, beta, gamma, theta=None, h0=None, *, chunk=0, Y=None,
-                h_out=None, ws=None):
+def mb_trap_ssd(X, logdecay, B, C, beta, gamma, theta=None, h0=None, *, X_prev=None, B_prev=None,
+                chunk=0, Y=None, h_out=None, ws=None):
     """Mamba-3 SISO.  X (batch, L, H, P), B, C (batch, L, G, N) in one dtype;
     logdecay, beta, gamma (batch, L, H), theta (batch, L, H, N/2) or None, h0
-    (batch, H, N, P) float32 (physical frame).  Returns (Y, h_out)."""
+    (batch, H, N, P) float32 (physical frame); X_prev (batch, H, P) and B_prev
+    (batch, G, N): the token before the call, or None.  Returns (Y, h_out)."""
     torch = _torch()
     dev = _device_of(X)
     dtype = X.dtype
@@ -245,20 +246,23 @@ def mb_trap_ssd(X, logdecay, B, C, beta, gamma, theta=None, h0=None, *, chunk=0,
     _check(C, "C", (b, L, G, N), dtype, dev)
     _check(theta, "theta", (b, L, H, N // 2), f32, dev)
     _check(h0, "h0", (b, H, N, P), f32, dev)
+    _check(X_prev, "X_prev", (b, H, P), dtype, dev)
+    _check(B_prev, "B_prev", (b, G, N), dtype, dev)
     Y = torch.empty((b, L, H, P), dtype=dtype, device=dev) if Y is None else _check(Y, "Y", (b, L, H, P), dtype, dev)
     h_out = torch.empty((b, H, N, P), dtype=f32, device=dev) if h_out is None else \
         _check(h_out, "h_out", (b, H, N, P), f32, dev)
     ws, nws = _workspace(MB_OP_TRAP_SSD, dev, ws, (b, L, H, P, G, N, 1, chunk))
     _call("mb_trap_ssd", _ptr(X), _ptr(logdecay), _ptr(B), _ptr(C), _ptr(beta), _ptr(gamma),
-          _ptr(theta), _ptr(h0), _ptr(Y), _ptr(h_out), b, L, H, P, G, N, chunk, code, _ptr(ws), nws,
-          _stream(dev))
+          _ptr(theta), _ptr(h0), _ptr(X_prev), _ptr(B_prev), _ptr(Y), _ptr(h_out), b, L, H, P, G, N, chunk,
+          code, _ptr(ws), nws, _stream(dev))
     return Y, h_out
 
 
-def mb_mimo_ssd(X, logdecay, B, C, beta, gamma, theta=None, h0=None, *, chunk=0, Y=None,
-                h_out=None, ws=None):
+def mb_mimo_ssd(X, logdecay, B, C, beta, gamma, theta=None, h0=None, *, X_prev=None, B_prev=None,
+                chunk=0, Y=None, h_out=None, ws=None):
     """Mamba-3 MIMO.  X (batch, L, H, P, R), B, C (batch, L, H, N, R) in one
-    dtype; the rest as mb_trap_ssd.  Returns (Y, h_out)."""
+    dtype; X_prev (batch, H, P, R), B_prev (batch, H, N, R) or None; the rest
+    as mb_trap_ssd.  Returns (Y, h_out)."""
     torch = _torch()
     dev = _device_of(X)
     dtype = X.dtype
@@ -272,14 +276,16 @@ def mb_mimo_ssd(X, logdecay, B, C, beta, gamma, theta=None, h0=None, *, chunk=0,
     _check(C, "C", (b, L, H, N, R), dtype, dev)
     _check(theta, "theta", (b, L, H, N // 2), f32, dev)
     _check(h0, "h0", (b, H, N, P), f32, dev)
+    _check(X_prev, "X_prev", (b, H, P, R), dtype, dev)
+    _check(B_prev, "B_prev", (b, H, N, R), dtype, dev)
     Y = torch.empty((b, L, H, P, R), dtype=dtype, device=dev) if Y is None else \
         _check(Y, "Y", (b, L, H, P, R), dtype, dev)
     h_out = torch.empty((b, H, N, P), dtype=f32, device=dev) if h_out is None else \
         _check(h_out, "h_out", (b, H, N, P), f32, dev)
     ws, nws = _workspace(MB_OP_MIMO_SSD, dev, ws, (b, L, H, P, 1, N, R, chunk))
     _call("mb_mimo_ssd", _ptr(X), _ptr(logdecay), _ptr(B), _ptr(C), _ptr(beta), _ptr(gamma),
-          _ptr(theta), _ptr(h0), _ptr(Y), _ptr(h_out), b, L, H, P, N, R, chunk, code, _ptr(ws), nws,
-          _stream(dev))
+          _ptr(theta), _ptr(h0), _ptr(X_prev), _ptr(B_prev), _ptr(Y), _ptr(h_out), b, L, H, P, N, R, chunk,
+          code, _ptr(ws), nws, _stream(dev))
     return Y, h_out
 
 

@@ -239,6 +239,8 @@ struct Args {
     const float* gamma;
     const float* theta;
     const float* h0;
+    const void* X_prev;   // trapezoid: the token before the call (NULL: zeros)
+    const void* B_prev;
     void* Y;
     float* h_out;
     float* S;        // Mamba-2 scores, (batch, chunk, group, 64, 64)
@@ -255,8 +257,9 @@ struct Args {
 // X/Y: element (step t, p, r) at t * x_step + h*P*R + p*R + r, x_step = H*P*R.
 template <int R, bool GROUPED, typename IO>
 struct Views {
-    Buf B, C, X, ld, gam, bet, th;
+    Buf B, C, X, ld, gam, bet, th, Bp, Xp;
     int bc_step, bc_head, x_step, x_head;
+    bool has_prev;
     __device__ Views(const Args& a, int b, int h, int hg) {
         bc_step = GROUPED ? a.G * a.N : a.H * a.N * R;
         bc_head = GROUPED ? hg * a.N : hg * a.N * R;
@@ -267,6 +270,13 @@ struct Views {
         C = make_buf((const IO*)a.C + (size_t)b * nbc, nbc * sizeof(IO));
         const size_t nx = (size_t)a.L * x_step;
         X = make_buf((const IO*)a.X + (size_t)b * nx, nx * sizeof(IO));
+        // the token before the call: one step of B and X, same element offsets
+        // as a row of B / X without the step term
+        has_prev = a.B_prev != nullptr;
+        Bp = make_buf(has_prev ? (const IO*)a.B_prev + (size_t)b * bc_step : (const IO*)a.B,
+                      has_prev ? (size_t)bc_step * sizeof(IO) : 0);
+        Xp = make_buf(has_prev ? (const IO*)a.X_prev + (size_t)b * x_step : (const IO*)a.X,
+                      has_prev ? (size_t)x_step * sizeof(IO) : 0);
         const size_t ns = (size_t)a.L * a.H;
         ld = make_buf(a.ld + (size_t)b * ns, ns * 4);
         gam = make_buf(a.gamma ? a.gamma + (size_t)b * ns : a.ld, a.gamma ? ns * 4 : 0);
@@ -492,9 +502,12 @@ __global__ __launch_bounds__(kWalkThreads) void k_walk(Args a) {
                 if constexpr (FULL) VecLoad<IO, 2 * R>::run(vw.C, e, p.c[i]);
             }
             if constexpr (TRAP) if (ssg * PRG < R) {
-                const int e = (t0g - 1) * vw.bc_step + vw.bc_head + 2 * sk * R + ssg * PRG;
-                VecLoad<IO, PRG>::run(vw.B, e, p.bp);
-                VecLoad<IO, PRG>::run(vw.B, e + R, p.bp + PRG);
+                // the previous step; before the call's first step it is the given
+                // previous token (or zeros: a negative offset reads zero)
+                const bool first = t0g == 0 && vw.has_prev;
+                const int e = (first ? 0 : (t0g - 1) * vw.bc_step) + vw.bc_head + 2 * sk * R + ssg * PRG;
+                VecLoad<IO, PRG>::run(first ? vw.Bp : vw.B, e, p.bp);
+                VecLoad<IO, PRG>::run(first ? vw.Bp : vw.B, e + R, p.bp + PRG);
             }
             if constexpr (ROT) {
 #pragma unroll
@@ -507,9 +520,12 @@ __global__ __launch_bounds__(kWalkThreads) void k_walk(Args a) {
             for (int i = 0; i < QXG; ++i)
                 VecLoad<IO, R>::run(vw.X, (t0g + xtq * QXG + i) * vw.x_step + vw.x_head + (p0 + xpl) * R,
                                     p.x[i]);
-            if constexpr (TRAP) if (xtq * PRX < R)
-                VecLoad<IO, PRX>::run(vw.X, (t0g - 1) * vw.x_step + vw.x_head + (p0 + xpl) * R + xtq * PRX,
+            if constexpr (TRAP) if (xtq * PRX < R) {
+                const bool first = t0g == 0 && vw.has_prev;
+                VecLoad<IO, PRX>::run(first ? vw.Xp : vw.X,
+                                      (first ? 0 : (t0g - 1) * vw.x_step) + vw.x_head + (p0 + xpl) * R + xtq * PRX,
                                       p.xp);
+            }
         }
         if constexpr (FULL && !TRAP) if (8 * sq <= si) {
             const int e = (c * a.G + hg) * (kRows * kRows) + sq * (kRows * 8) + si * 8;
@@ -1895,6 +1911,7 @@ extern "C" size_t mb_workspace_size(mb_op op, int64_t batch, int64_t L, int64_t 
 static mb_status ssd_common_checks(const void* X, const float* logdecay, const void* B,
                                    const void* C, const float* h0, void* Y, float* h_out,
                                    const float* beta, const float* gamma, const float* theta,
+                                   const void* X_prev, const void* B_prev,
                                    int64_t batch, int64_t L, int64_t H, int64_t P, int64_t nBC,
                                    int64_t N, int64_t R, mb_dtype dtype, int64_t chunk,
                                    bool trap) {
@@ -1908,14 +1925,20 @@ static mb_status ssd_common_checks(const void* X, const float* logdecay, const v
     const size_t n_s = (size_t)(batch * L * H);
     const size_t n_h = (size_t)(batch * H * N * P);
     if (n_x && (!X || !Y || !logdecay || !B || !C)) return MB_ERR_NULL;
-    if (((uintptr_t)X | (uintptr_t)Y | (uintptr_t)B | (uintptr_t)C) & 15) return MB_ERR_ALIGN;
+    if ((X_prev == nullptr) != (B_prev == nullptr)) return MB_ERR_NULL;
+    if (((uintptr_t)X | (uintptr_t)Y | (uintptr_t)B | (uintptr_t)C | (uintptr_t)X_prev |
+         (uintptr_t)B_prev) & 15)
+        return MB_ERR_ALIGN;
     if (trap && n_x && (!beta || !gamma)) return MB_ERR_NULL;
+    const size_t n_xp = (size_t)(batch * H * P * R), n_bp = (size_t)(batch * nBC * N * R);
     const Span ins[] = {{X, n_x * es}, {B, n_bc * es}, {C, n_bc * es}, {logdecay, n_s * 4},
                         {beta, trap && beta ? n_s * 4 : 0}, {gamma, trap && gamma ? n_s * 4 : 0},
-                        {theta, theta ? n_s * (size_t)(N / 2) * 4 : 0}, {h0, h0 ? n_h * 4 : 0}};
-    if (overlaps_any(Y, n_x * es, ins, 8)) return MB_ERR_ALIAS;
+                        {theta, theta ? n_s * (size_t)(N / 2) * 4 : 0},
+                        {X_prev, X_prev ? n_xp * es : 0}, {B_prev, B_prev ? n_bp * es : 0},
+                        {h0, h0 ? n_h * 4 : 0}};
+    if (overlaps_any(Y, n_x * es, ins, 10)) return MB_ERR_ALIAS;
     if (h_out) {
-        if (overlaps_any(h_out, n_h * 4, ins, 7)) return MB_ERR_ALIAS;
+        if (overlaps_any(h_out, n_h * 4, ins, 9)) return MB_ERR_ALIAS;
         if (h0 && h0 != h_out && overlaps(h_out, n_h * 4, h0, n_h * 4)) return MB_ERR_ALIAS;
         if (overlaps(h_out, n_h * 4, Y, n_x * es)) return MB_ERR_ALIAS;
     }
@@ -1929,52 +1952,54 @@ extern "C" mb_status mb_ssd_chunked(const void* X, const float* logdecay, const 
                                     size_t ws_bytes, hipStream_t stream) {
     if (G < 1 || H < 1 || H % G) return MB_ERR_SHAPE;
     mb_status st = ssd_common_checks(X, logdecay, B, C, h0, Y, h_out, nullptr, nullptr, nullptr,
-                                     batch, L, H, P, G, N, 1, dtype, chunk, false);
+                                     nullptr, nullptr, batch, L, H, P, G, N, 1, dtype, chunk, false);
     if (st != MB_OK) return st;
     if (batch == 0) return MB_OK;
     if (L == 0) return copy_state(h0, h_out, batch * H * N * P, stream);
     const Plan pl = plan_for(MB_OP_SSD_CHUNKED, batch, L, H, P, G, N, 1);
     if ((st = check_ws(ws, ws_bytes, pl.bytes)) != MB_OK) return st;
-    Args a{X, logdecay, B, C, nullptr, nullptr, nullptr, h0, Y, h_out, nullptr, nullptr, nullptr,
-           nullptr, nullptr, (int)L, (int)H, (int)P, (int)G, (int)N, 0, 0, 0, 0};
+    Args a{X, logdecay, B, C, nullptr, nullptr, nullptr, h0, nullptr, nullptr, Y, h_out, nullptr,
+           nullptr, nullptr, nullptr, nullptr, (int)L, (int)H, (int)P, (int)G, (int)N, 0, 0, 0, 0};
     return dispatch<1, false, true>(a, batch, pl, (char*)ws, dtype, stream);
 }
 
 extern "C" mb_status mb_trap_ssd(const void* X, const float* logdecay, const void* B,
                                  const void* C, const float* beta, const float* gamma,
-                                 const float* theta, const float* h0, void* Y, float* h_out,
-                                 int64_t batch, int64_t L, int64_t H, int64_t P, int64_t G,
-                                 int64_t N, int64_t chunk, mb_dtype dtype, void* ws,
-                                 size_t ws_bytes, hipStream_t stream) {
+                                 const float* theta, const float* h0, const void* X_prev,
+                                 const void* B_prev, void* Y, float* h_out, int64_t batch,
+                                 int64_t L, int64_t H, int64_t P, int64_t G, int64_t N,
+                                 int64_t chunk, mb_dtype dtype, void* ws, size_t ws_bytes,
+                                 hipStream_t stream) {
     if (G < 1 || H < 1 || H % G) return MB_ERR_SHAPE;
-    mb_status st = ssd_common_checks(X, logdecay, B, C, h0, Y, h_out, beta, gamma, theta, batch,
-                                     L, H, P, G, N, 1, dtype, chunk, true);
+    mb_status st = ssd_common_checks(X, logdecay, B, C, h0, Y, h_out, beta, gamma, theta, X_prev,
+                                     B_prev, batch, L, H, P, G, N, 1, dtype, chunk, true);
     if (st != MB_OK) return st;
     if (batch == 0) return MB_OK;
     if (L == 0) return copy_state(h0, h_out, batch * H * N * P, stream);
     const Plan pl = plan_for(MB_OP_TRAP_SSD, batch, L, H, P, G, N, 1);
     if ((st = check_ws(ws, ws_bytes, pl.bytes)) != MB_OK) return st;
-    Args a{X, logdecay, B, C, beta, gamma, theta, h0, Y, h_out, nullptr, nullptr, nullptr, nullptr,
-           nullptr, (int)L, (int)H, (int)P, (int)G, (int)N, 0, 0, 0, 0};
+    Args a{X, logdecay, B, C, beta, gamma, theta, h0, X_prev, B_prev, Y, h_out, nullptr, nullptr,
+           nullptr, nullptr, nullptr, (int)L, (int)H, (int)P, (int)G, (int)N, 0, 0, 0, 0};
     return dispatch<1, true, true>(a, batch, pl, (char*)ws, dtype, stream);
 }
 
 extern "C" mb_status mb_mimo_ssd(const void* X, const float* logdecay, const void* B,
                                  const void* C, const float* beta, const float* gamma,
-                                 const float* theta, const float* h0, void* Y, float* h_out,
-                                 int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N,
-                                 int64_t R, int64_t chunk, mb_dtype dtype, void* ws,
-                                 size_t ws_bytes, hipStream_t stream) {
+                                 const float* theta, const float* h0, const void* X_prev,
+                                 const void* B_prev, void* Y, float* h_out, int64_t batch,
+                                 int64_t L, int64_t H, int64_t P, int64_t N, int64_t R,
+                                 int64_t chunk, mb_dtype dtype, void* ws, size_t ws_bytes,
+                                 hipStream_t stream) {
     if (R != 1 && R != 2 && R != 4 && R != 8 && R != 16) return MB_ERR_SHAPE;
-    mb_status st = ssd_common_checks(X, logdecay, B, C, h0, Y, h_out, beta, gamma, theta, batch,
-                                     L, H, P, H, N, R, dtype, chunk, true);
+    mb_status st = ssd_common_checks(X, logdecay, B, C, h0, Y, h_out, beta, gamma, theta, X_prev,
+                                     B_prev, batch, L, H, P, H, N, R, dtype, chunk, true);
     if (st != MB_OK) return st;
     if (batch == 0) return MB_OK;
     if (L == 0) return copy_state(h0, h_out, batch * H * N * P, stream);
     const Plan pl = plan_for(MB_OP_MIMO_SSD, batch, L, H, P, 1, N, R);
     if ((st = check_ws(ws, ws_bytes, pl.bytes)) != MB_OK) return st;
-    Args a{X, logdecay, B, C, beta, gamma, theta, h0, Y, h_out, nullptr, nullptr, nullptr, nullptr,
-           nullptr, (int)L, (int)H, (int)P, (int)H, (int)N, 0, 0, 0, 0};
+    Args a{X, logdecay, B, C, beta, gamma, theta, h0, X_prev, B_prev, Y, h_out, nullptr, nullptr,
+           nullptr, nullptr, nullptr, (int)L, (int)H, (int)P, (int)H, (int)N, 0, 0, 0, 0};
     char* w = (char*)ws;
     switch (R) {
         case 1: return dispatch<1, true, false>(a, batch, pl, w, dtype, stream);

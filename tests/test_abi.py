@@ -144,7 +144,7 @@ def test_ssd_validation(lib):
 
 def test_trap_and_mimo_validation(lib):
     args = [P(FAKE), P(FAKE + (1 << 22)), P(FAKE + (1 << 23)), P(FAKE + (1 << 24)),
-            P(FAKE + (1 << 25)), P(FAKE + (1 << 25) + (1 << 21)), P(FAKE + (1 << 29)), None,
+            P(FAKE + (1 << 25)), P(FAKE + (1 << 25) + (1 << 21)), P(FAKE + (1 << 29)), None, None, None,
             P(FAKE + (1 << 27)), P(FAKE + (1 << 26))]
     # odd N with rotation angles
     assert lib.mb_trap_ssd(*args, 1, 10, 2, 16, 1, 6, 0, F32, P(FAKE + (1 << 28)), 1 << 30, None) == E_SHAPE
@@ -152,6 +152,14 @@ def test_trap_and_mimo_validation(lib):
     a2 = list(args)
     a2[4] = None
     assert lib.mb_trap_ssd(*a2, 1, 10, 2, 16, 1, 8, 0, F32, P(FAKE + (1 << 28)), 1 << 30, None) == E_NULL
+    # the previous token: X_prev and B_prev together, 16-byte aligned, not under an output
+    a3 = list(args)
+    a3[8] = P(FAKE + (1 << 30))
+    assert lib.mb_trap_ssd(*a3, 1, 10, 2, 16, 1, 8, 0, F32, P(FAKE + (1 << 28)), 1 << 30, None) == E_NULL
+    a3[9] = P(FAKE + (1 << 30) + (1 << 20) + 4)
+    assert lib.mb_trap_ssd(*a3, 1, 10, 2, 16, 1, 8, 0, F32, P(FAKE + (1 << 28)), 1 << 30, None) == E_ALIGN
+    a3[9] = P(FAKE + (1 << 27))    # under Y
+    assert lib.mb_trap_ssd(*a3, 1, 10, 2, 16, 1, 8, 0, F32, P(FAKE + (1 << 28)), 1 << 30, None) == E_ALIAS
     # unsupported rank
     assert lib.mb_mimo_ssd(*args, 1, 10, 2, 16, 8, 3, 0, F32, P(FAKE + (1 << 28)), 1 << 30, None) == E_SHAPE
     assert lib.mb_mimo_ssd(*args, 0, 10, 2, 16, 8, 4, 0, F32, P(FAKE + (1 << 28)), 1 << 30, None) == OK

@@ -118,6 +118,41 @@ def test_siso_bf16(oracle_mod):
     assert_close(h, hr, "bf16", "h")
 
 
+def _split_call(fn, dev, s, **kw):
+    """Two chunked calls split at step s; the second gets the first's final state
+    and the token before the split."""
+    cut = lambda sl: {k: (v[:, sl].contiguous() if k != "h0" and v is not None else v) for k, v in dev.items()}
+    a, b = cut(slice(0, s)), cut(slice(s, None))
+    args = lambda d: (d["X"], d["logdecay"], d["B"], d["C"], d["beta"], d["gamma"], d["theta"])
+    Ya, ha = fn(*args(a), dev["h0"])
+    Yb, hb = fn(*args(b), ha, X_prev=dev["X"][:, s - 1].contiguous(), B_prev=dev["B"][:, s - 1].contiguous())
+    return torch.cat([Ya, Yb], 1), hb
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("rotate", [True, False])
+def test_siso_split_with_previous_token(oracle_mod, dtype, rotate):
+    """A sequence split at a step that is not a chunk boundary, with a nonzero
+    cross-boundary weight, chains exactly through h0 and (X_prev, B_prev); the
+    second part is long enough for several sequence segments."""
+    inp = wl.trap_inputs(np.random.default_rng(41 + rotate), 2, 900, 3, 32, 64, G=1, h0_sd=0.05, rotate=rotate)
+    dev, ref = prepare(inp, dtype)
+    Yr, hr = oracle_mod.trap(**ref)
+    Y, h = _split_call(mb.mb_trap_ssd, dev, 301)
+    assert_close(Y, Yr, dtype, "Y")
+    assert_close(h, hr, dtype, "h")
+
+
+@pytest.mark.parametrize("R", [2, 4])
+def test_mimo_split_with_previous_token(oracle_mod, R):
+    inp = wl.mimo_inputs(np.random.default_rng(43 + R), 1, 600, 2, 32, 64, R, h0_sd=0.05)
+    dev, ref = prepare(inp, "f32")
+    Yr, hr = oracle_mod.mimo(**ref)
+    Y, h = _split_call(mb.mb_mimo_ssd, dev, 133)
+    assert_close(Y, Yr, "f32", "Y")
+    assert_close(h, hr, "f32", "h")
+
+
 def test_siso_large_angles(oracle_mod):
     """Accumulated angles of several hundred radians (long sequence, large theta):
     the chunk-local angles keep fp32 accurate."""
