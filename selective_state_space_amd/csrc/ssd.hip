@@ -74,6 +74,12 @@ __device__ __forceinline__ floatx4 mfma4(float a, float b, floatx4 c) {
 
 __device__ __forceinline__ float exp_e(float v) { return exp2_fast(v * kLog2e); }
 
+// a compile-time int carried by a lambda argument
+template <int V>
+struct Par {
+    static constexpr int value = V;
+};
+
 // bf16 matrix instruction: 16 x 16 x 32, fp32 accumulation.  Lane l supplies
 // A[l % 16][8 (l / 16) + q] and B[8 (l / 16) + q][l % 16], q = 0..7, as four
 // registers of bf16 pairs; the accumulator layout is that of the fp32 16 x 16
@@ -492,7 +498,11 @@ __global__ __launch_bounds__(kWalkThreads) void k_walk(Args a) {
         ? make_buf(a.S + (size_t)b * a.nch * a.G * (kRows * kRows), (size_t)a.nch * a.G * kRows * kRows * 4)
         : make_buf(a.ld, 0);
 
-    auto prefetch = [&](int c, Pre& p) {
+    // FIRST: the chunk may be the call's first, whose previous step is the given
+    // previous token (only the prefetch before the loop; the loop's prefetches
+    // never are, and stay free of the selection)
+    auto prefetch = [&](int c, Pre& p, auto first_tag) {
+        constexpr bool FIRST = decltype(first_tag)::value != 0;
         const int t0g = c * QT;
         if (k_ok) {
 #pragma unroll
@@ -504,7 +514,7 @@ __global__ __launch_bounds__(kWalkThreads) void k_walk(Args a) {
             if constexpr (TRAP) if (ssg * PRG < R) {
                 // the previous step; before the call's first step it is the given
                 // previous token (or zeros: a negative offset reads zero)
-                const bool first = t0g == 0 && vw.has_prev;
+                const bool first = FIRST && t0g == 0 && vw.has_prev;
                 const int e = (first ? 0 : (t0g - 1) * vw.bc_step) + vw.bc_head + 2 * sk * R + ssg * PRG;
                 VecLoad<IO, PRG>::run(first ? vw.Bp : vw.B, e, p.bp);
                 VecLoad<IO, PRG>::run(first ? vw.Bp : vw.B, e + R, p.bp + PRG);
@@ -521,7 +531,7 @@ __global__ __launch_bounds__(kWalkThreads) void k_walk(Args a) {
                 VecLoad<IO, R>::run(vw.X, (t0g + xtq * QXG + i) * vw.x_step + vw.x_head + (p0 + xpl) * R,
                                     p.x[i]);
             if constexpr (TRAP) if (xtq * PRX < R) {
-                const bool first = t0g == 0 && vw.has_prev;
+                const bool first = FIRST && t0g == 0 && vw.has_prev;
                 VecLoad<IO, PRX>::run(first ? vw.Xp : vw.X,
                                       (first ? 0 : (t0g - 1) * vw.x_step) + vw.x_head + (p0 + xpl) * R + xtq * PRX,
                                       p.xp);
@@ -733,7 +743,7 @@ __global__ __launch_bounds__(kWalkThreads) void k_walk(Args a) {
 
     Pre pre;
     if (c_begin < c_end) {
-        prefetch(c_begin, pre);
+        prefetch(c_begin, pre, Par<1>{});
         angle_prefix(pre);
     }
 
@@ -742,7 +752,7 @@ __global__ __launch_bounds__(kWalkThreads) void k_walk(Args a) {
         __syncthreads();                 // the previous chunk's LDS reads are done
         stage(pre);
         if constexpr (SO) {
-            if (c + 1 < c_end) prefetch(c + 1, pre);
+            if (c + 1 < c_end) prefetch(c + 1, pre, Par<0>{});
         }
         __syncthreads();
         if constexpr (SO) seg_acc += cum_last;
@@ -854,7 +864,7 @@ __global__ __launch_bounds__(kWalkThreads) void k_walk(Args a) {
                 state_part();
             }
             // the next chunk's operands load while the rest of this chunk computes
-            if (c + 1 < c_end) prefetch(c + 1, pre);
+            if (c + 1 < c_end) prefetch(c + 1, pre, Par<0>{});
             if constexpr (TRAP) __syncthreads();   // M complete
             // ---- partial Y^T += X^T M^T over half of the column blocks ------------
             if (active) {
@@ -1365,11 +1375,6 @@ __global__ __launch_bounds__(kWalkThreads) void k_walk_m2s(Args a) {
 // the next one.
 // ---------------------------------------------------------------------------
 constexpr int kBfThreads = 256;
-
-template <int V>
-struct Par {
-    static constexpr int value = V;
-};
 
 // A value the compiler cannot see through: per-load offsets built from it by
 // uniform adds are not hoisted out of the chunk loop as one register each.
