@@ -402,9 +402,10 @@ def time_next(args, mb, wl, torch):
         torch.cuda.synchronize()
         ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev]))
         r = roofline_of(w, ms)
+        roof = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}
+        roof["traffic"] = traffic_for(w)
         res.append({"workload": w.name, "kernel": w.kernel, "shape": w.shape, "ms": round(ms, 5),
-                    "tokens_per_s": w.tokens / (ms * 1e-3),
-                    "roofline": {k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}})
+                    "tokens_per_s": w.tokens / (ms * 1e-3), "roofline": roof})
         del w
     return res
 
