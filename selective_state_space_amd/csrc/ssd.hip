@@ -389,7 +389,7 @@ __constant__ int kTrapTiles[8][2] = {{0x33, 0x00}, {0x32, 0x11}, {0x22, -1}, {0x
                                      {0x30, -1}, {0x31, -1}, {0x21, -1}, {0x10, -1}};
 
 template <int NP, int R, bool TRAP, bool ROT, bool GROUPED, typename IO, bool SO>
-__global__ __launch_bounds__(kWalkThreads) void k_walk(Args a) {
+__global__ __launch_bounds__(kWalkThreads, SO ? 4 : 2) void k_walk(Args a) {
     using Gm = Geo<R, TRAP>;
     constexpr int QT = Gm::QT, EXTRA = Gm::EXTRA, JX = Gm::JX;
     constexpr int JC = Gm::JC, JP = Gm::JP;
