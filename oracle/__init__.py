@@ -13,6 +13,8 @@ widened, so that the oracle sees the values the GPU sees).
 Which passage each loop follows is cited at the loop in ``oracle.c``:
   m1_scan / m1_step  - TorchMamba README (Models table, Math notes M1);
                        burn_mamba Mamba1 docs (selective_scan, selective_scan_step)
+  m1_block           - the same scan with the block's causal conv1d + SiLU,
+                       softplus(dt + bias) and SiLU(z) gate around it
   ssd                - TorchMamba README (Models table, Math notes M2)
   trap               - TorchMamba README (Math notes M3 SISO);
                        mamba3-minimal README (Two-SSD Decomposition)
@@ -65,6 +67,7 @@ def _load():
         lib.oracle_trap.argtypes = [_D] * 12 + [_I] * 6
         lib.oracle_mimo.argtypes = [_D] * 12 + [_I] * 6
         lib.oracle_ssd_step.argtypes = [_D] * 12 + [_I] * 6
+        lib.oracle_m1_block.argtypes = [_D] * 14 + [_I] * 5
         lib.oracle_set_threads.argtypes = [ctypes.c_int]
         lib.oracle_get_threads.restype = ctypes.c_int
         _lib = lib
@@ -255,3 +258,31 @@ def ssd_step(X, logdecay, B, C, h=None, beta=None, gamma=None, theta=None, X_pre
     _load().oracle_ssd_step(_p(X), _p(logdecay), _p(B), _p(C), _p(beta), _p(gamma), _p(theta),
                             _p(X_prev), _p(B_prev), _p(h), _p(Y), _p(hout), b, H, P, G, N, R)
     return (Y[..., 0] if squeeze else Y), hout
+
+
+def m1_block(x, conv_w, dt, A, B, C, D=None, h0=None, conv_b=None, dt_bias=None, z=None, x_hist=None):
+    """Mamba-1 scan with the block prologue and epilogue.  x, dt, z (b, L, D);
+    conv_w (D, K); conv_b, dt_bias, D (D,); A (D, N); B, C (b, L, N); h0
+    (b, D, N); x_hist (b, K-1, D).  Returns (y, h_out)."""
+    x = _f64(x)
+    b, L, Dm = x.shape
+    conv_w = _f64(conv_w)
+    K = conv_w.shape[1]
+    A = _f64(A)
+    N = A.shape[1]
+    conv_w = _chk(conv_w, (Dm, K), "conv_w")
+    dt = _chk(dt, (b, L, Dm), "dt")
+    A = _chk(A, (Dm, N), "A")
+    B = _chk(B, (b, L, N), "B")
+    C = _chk(C, (b, L, N), "C")
+    D = _opt(D, (Dm,))
+    h0 = _opt(h0, (b, Dm, N))
+    conv_b = _opt(conv_b, (Dm,))
+    dt_bias = _opt(dt_bias, (Dm,))
+    z = _opt(z, (b, L, Dm))
+    x_hist = _opt(x_hist, (b, K - 1, Dm)) if K > 1 else None
+    y = np.empty((b, L, Dm))
+    h = np.empty((b, Dm, N))
+    _load().oracle_m1_block(_p(x), _p(x_hist), _p(conv_w), _p(conv_b), _p(dt), _p(dt_bias), _p(A), _p(B),
+                            _p(C), _p(D), _p(z), _p(h0), _p(y), _p(h), b, L, Dm, N, K)
+    return y, h

@@ -415,3 +415,65 @@ void oracle_ssd_step(const double *X, const double *logdecay, const double *B,
         free(T); free(S);
     }
 }
+
+/*
+ * Mamba-1 selective scan with the block's prologue and epilogue around it
+ * (TorchMamba README, Models table row Mamba-1 "conv1d + sequential selective
+ * scan" and Math notes M1; mamba-rs page, Mamba block).  Per (b, c):
+ *     xc_t  = SiLU(conv_b[c] + sum_{k<K} conv_w[c,k] * x_{t-K+1+k}[c])
+ *             (causal: x_{-j} = x_hist[K-1-j] when given, else 0)
+ *     dt'_t = softplus(dt_t[c] + dt_bias[c])
+ *     h_t   = exp(dt'_t A[c,n]) h_{t-1} + dt'_t B_t[n] xc_t     (per n)
+ *     y_t   = (sum_n C_t[n] h_t[n] + Dskip[c] xc_t) * SiLU(z_t[c])
+ * SiLU(v) = v / (1 + e^{-v}), softplus(v) = log(1 + e^v).  conv_b, dt_bias,
+ * Dskip, z and x_hist may be NULL (0, 0, 0, no gate, zero history).
+ * x_hist is (batch, K-1, D): the K-1 raw inputs before the call.
+ */
+static double silu(double v) { return v / (1.0 + exp(-v)); }
+static double softplus(double v) { return v > 30.0 ? v : log1p(exp(v)); }
+
+void oracle_m1_block(const double *x, const double *x_hist, const double *conv_w,
+                     const double *conv_b, const double *dt, const double *dt_bias,
+                     const double *A, const double *B, const double *C,
+                     const double *Dskip, const double *z, const double *h0,
+                     double *y, double *h_out, int64_t batch, int64_t L,
+                     int64_t D, int64_t N, int64_t K)
+{
+    int64_t units = batch * D;
+#pragma omp parallel for schedule(static)
+    for (int64_t u = 0; u < units; ++u) {
+        int64_t b = u / D, c = u % D;
+        double *h = (double *)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1));
+        for (int64_t n = 0; n < N; ++n)
+            h[n] = h0 ? h0[(b * D + c) * N + n] : 0.0;
+        for (int64_t t = 0; t < L; ++t) {
+            /* causal convolution over the raw inputs, then SiLU */
+            double pre = conv_b ? conv_b[c] : 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                int64_t s = t - (K - 1) + k;       /* input step of tap k */
+                double xs;
+                if (s >= 0)
+                    xs = x[(b * L + s) * D + c];
+                else
+                    xs = x_hist ? x_hist[(b * (K - 1) + (K - 1 + s)) * D + c] : 0.0;
+                pre += conv_w[c * K + k] * xs;
+            }
+            double xc = silu(pre);
+            double dtv = softplus(dt[(b * L + t) * D + c] + (dt_bias ? dt_bias[c] : 0.0));
+            const double *Bt = B + (b * L + t) * N;
+            const double *Ct = C + (b * L + t) * N;
+            double acc = 0.0;
+            for (int64_t n = 0; n < N; ++n) {
+                double a = exp(dtv * A[c * N + n]);
+                h[n] = a * h[n] + (dtv * Bt[n]) * xc;
+                acc += Ct[n] * h[n];
+            }
+            double yv = acc + (Dskip ? Dskip[c] * xc : 0.0);
+            if (z) yv *= silu(z[(b * L + t) * D + c]);
+            y[(b * L + t) * D + c] = yv;
+        }
+        if (h_out)
+            for (int64_t n = 0; n < N; ++n) h_out[(b * D + c) * N + n] = h[n];
+        free(h);
+    }
+}

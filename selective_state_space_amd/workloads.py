@@ -18,6 +18,8 @@ expand 2 for Mamba-1, d_head 64 / d_state 128 for the SSD family):
 * mimo_block  seed 105: batch 2, L 8192, H 16, P 64, N 128, R 4.
 * ssd_decode  seeds 107 (Mamba-2), 108 (SISO), 109 (MIMO): one token for 256
               sequences on the block shapes, state ~ N(0, 0.1).
+* m1_fused    seed 110: the Mamba-1 block shapes with the block's prologue and
+              epilogue inputs (conv1d width 4, dt bias, gate z).
 """
 from __future__ import annotations
 
@@ -205,3 +207,32 @@ def ssd_decode(model):
     if model == "mimo":
         return ssd_step_inputs(np.random.default_rng(109), 256, 16, 64, 16, 128, 4, "rot")
     raise ValueError(model)
+
+
+def m1_block_inputs(rng, batch, L, D, N, K=4, h0_sd=0.0, hist=False):
+    """Inputs of the Mamba-1 scan with the block prologue and epilogue: raw x ~
+    N(0,1); conv_w ~ N(0, 1/K) (D, K); conv_b ~ N(0, 0.1); raw dt ~ N(0, 0.5) with
+    dt_bias = softplus^-1(U(0.001, 0.1)) (so softplus(dt + bias) starts near the
+    usual step sizes); B, C ~ N(0,1); D ~ N(0,1); gate z ~ N(0,1); A = -(n+1).
+    Order: x, conv_w, conv_b, dt, dt_bias, B, C, D, z, (h0), (x_hist)."""
+    x = rng.standard_normal((batch, L, D))
+    conv_w = rng.normal(0.0, 1.0 / np.sqrt(K), (D, K))
+    conv_b = rng.normal(0.0, 0.1, D)
+    dt = rng.normal(0.0, 0.5, (batch, L, D))
+    u = rng.uniform(0.001, 0.1, D)
+    dt_bias = np.log(np.expm1(u))
+    B = rng.standard_normal((batch, L, N))
+    C = rng.standard_normal((batch, L, N))
+    Dskip = rng.standard_normal(D)
+    z = rng.standard_normal((batch, L, D))
+    d = dict(x=x, conv_w=conv_w, conv_b=conv_b, dt=dt, dt_bias=dt_bias, A=s4d_real_A(D, N), B=B, C=C,
+             D=Dskip, z=z, h0=None, x_hist=None)
+    if h0_sd > 0:
+        d["h0"] = rng.normal(0.0, h0_sd, (batch, D, N))
+    if hist and K > 1:
+        d["x_hist"] = rng.standard_normal((batch, K - 1, D))
+    return d
+
+
+def m1_fused(seed=110, batch=8, L=2048, D=1536, N=16, K=4):
+    return m1_block_inputs(np.random.default_rng(seed), batch, L, D, N, K)

@@ -42,6 +42,13 @@ MUTATIONS = {
                            "rotate_pairs(S + p, T + p, theta + (b * H + h) * (N / 2), N, P, 1.0);"),
     "step_gamma_rotated": ("S[n * P + p] += ga * cur;", "S[n * P + p] += ga * cur * (theta ? 0.5 : 1.0);"),
     "step_decay_dropped": ("T[n * P + p] = a * s0 + be * prev;", "T[n * P + p] = s0 + be * prev;"),
+    "block_conv_shift": ("int64_t s = t - (K - 1) + k;", "int64_t s = t - K + k;"),
+    "block_dt_bias_dropped": ("softplus(dt[(b * L + t) * D + c] + (dt_bias ? dt_bias[c] : 0.0))",
+                              "softplus(dt[(b * L + t) * D + c])"),
+    "block_skip_uses_raw_x": ("(Dskip ? Dskip[c] * xc : 0.0)", "(Dskip ? Dskip[c] * x[(b * L + t) * D + c] : 0.0)"),
+    "block_gate_sigmoid_only": ("if (z) yv *= silu(z[(b * L + t) * D + c]);",
+                                "if (z) yv *= 1.0 / (1.0 + exp(-z[(b * L + t) * D + c]));"),
+    "block_history_reversed": ("x_hist[(b * (K - 1) + (K - 1 + s)) * D + c]", "x_hist[(b * (K - 1) + (-1 - s)) * D + c]"),
     "trap_prev0_ignored": ("if (B_prev0) memcpy(Bprev, B_prev0 + (b * G + g) * N, sizeof(double) * (size_t)N);", ""),
     "mimo_prev0_wrong_head": ("if (X_prev0) memcpy(Xprev, X_prev0 + (b * H + h) * P * R, sizeof(double) * (size_t)(P * R));",
                               "if (X_prev0) memcpy(Xprev, X_prev0 + b * H * P * R, sizeof(double) * (size_t)(P * R));"),
@@ -109,7 +116,27 @@ def _battery(o):
         Yb, hb = getattr(o, fn)(**rest, X_prev=inp["X"][:, 7], B_prev=inp["B"][:, 7])
         if not (np.allclose(Yb, Y[:, 8:], rtol=1e-9, atol=1e-11) and np.allclose(hb, h, rtol=1e-9, atol=1e-11)):
             failed.append(fn + "_split_with_previous_token")
+
+    inp = wl.m1_block_inputs(rng, 2, 15, 3, 4, K=4, h0_sd=0.3, hist=True)
+    y, h = o.m1_block(**inp)
+    yr, hr = _block_reference(o, inp)
+    if not (ok(y, yr) and ok(h, hr)):
+        failed.append("m1_block_composition")
     return failed
+
+
+def _block_reference(o, inp):
+    from scipy.signal import lfilter
+    from scipy.special import expit
+    x, w = inp["x"], inp["conv_w"]
+    b, L, D = x.shape
+    K = w.shape[1]
+    ext = np.concatenate([inp["x_hist"], x], axis=1)
+    pre = np.stack([lfilter(w[c, ::-1], [1.0], ext[:, :, c], axis=1)[:, K - 1:] for c in range(D)], -1) + inp["conv_b"]
+    xc = pre * expit(pre)
+    y, h = o.m1_scan(xc, np.logaddexp(0.0, inp["dt"] + inp["dt_bias"]), inp["A"], inp["B"], inp["C"], inp["D"],
+                     inp["h0"])
+    return y * inp["z"] * expit(inp["z"]), h
 
 
 def _load_variant(tmp_path, src_text, tag):
