@@ -133,6 +133,39 @@ class M1Scan(Workload):
         self.mb.mb_selective_scan(self.x, self.dt, self.A, self.B, self.C, self.D, None, y=self.y, h_out=self.h)
 
 
+class M1Fused(Workload):
+    """The Mamba-1 scan with the block prologue and epilogue in the same kernel
+    (conv1d + SiLU, softplus of dt plus bias, SiLU gate); outside the step,
+    measured beside it.  Its ALU count is the scan's alone (the prologue adds a
+    few operations per (t, c), not per state), so the fraction is a lower bound."""
+    name = "m1_fused"
+    kernel = "k_m1_scan_w"
+    bound = "alu"
+    source = "selective_state_space_amd/csrc/m1.hip"
+
+    def __init__(self, mb, wl, torch):
+        self.mb = mb
+        inp = wl.m1_fused()
+        self.inp = inp
+        b, L, D = inp["x"].shape
+        N, K = inp["A"].shape[1], inp["conv_w"].shape[1]
+        self.shape = dict(batch=b, L=L, D=D, N=N, K=K)
+        f = torch.float32
+        self.t = {k: (_dev(v, f) if v is not None else None) for k, v in inp.items()}
+        self.y = torch.empty_like(self.t["x"])
+        self.h = torch.empty((b, D, N), dtype=f, device="cuda")
+        self.tokens = b * L
+        nbytes, self.exps = m1_scan_work(b, L, D, N)
+        self.bytes = nbytes + 4 * (b * L * D + D * (K + 2))   # the gate z, conv_w, conv_b, dt_bias
+        self.flops = None
+
+    def run(self):
+        t = self.t
+        self.mb.mb_selective_scan_fused(t["x"], t["conv_w"], t["dt"], t["A"], t["B"], t["C"], t["D"], None,
+                                        conv_b=t["conv_b"], dt_bias=t["dt_bias"], z=t["z"], y=self.y,
+                                        h_out=self.h)
+
+
 class M1Step(Workload):
     name = "m1_step"
     kernel = "k_m1_step_q"
@@ -275,8 +308,9 @@ class SSDDecode(Workload):
 
 
 ALL = ["m1_scan", "m1_step", "ssd_f32", "ssd_bf16", "siso", "mimo"]
-# measured beside the step, not part of it: the decode steps of the SSD family
-NEXT = ["m2_decode", "siso_decode", "mimo_decode"]
+# measured beside the step, not part of it: the decode steps of the SSD family and
+# the Mamba-1 scan with the block prologue and epilogue fused
+NEXT = ["m2_decode", "siso_decode", "mimo_decode", "m1_fused"]
 
 
 def make(name, mb, wl, torch):
@@ -284,6 +318,8 @@ def make(name, mb, wl, torch):
         return M1Scan(mb, wl, torch)
     if name == "m1_step":
         return M1Step(mb, wl, torch)
+    if name == "m1_fused":
+        return M1Fused(mb, wl, torch)
     if name == "ssd_f32":
         return SSD(mb, wl, torch, "f32")
     if name == "ssd_bf16":
@@ -384,8 +420,9 @@ def cold_ms(torch, w, reps=5):
 
 
 def time_next(args, mb, wl, torch):
-    """Decode steps of the SSD family, timed with HIP events on the stream they
-    run on, outside the step (they are not part of its token count)."""
+    """Decode steps of the SSD family and the fused Mamba-1 block scan, timed with
+    HIP events on the stream they run on, outside the step (they are not part of
+    its token count)."""
     res = []
     for n in NEXT:
         print("# preparing %s" % n, file=sys.stderr, flush=True)

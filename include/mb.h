@@ -106,6 +106,33 @@ mb_status mb_ssm_step(const void* x, const void* dt, const float* A,
                       mb_dtype dtype, hipStream_t stream);
 
 /*
+ * Mamba-1 selective scan with the block's prologue and epilogue fused around it
+ * (TorchMamba README, Models table row Mamba-1, "conv1d + sequential selective
+ * scan"; the Mamba block takes the softplus of dt plus a bias and gates the
+ * output with SiLU(z)).  Per batch b, channel c, state n:
+ *     xc_t  = SiLU(conv_b[c] + sum_{k<K} conv_w[c,k] * x_{t-K+1+k}[c])
+ *     dt'_t = softplus(dt_t[c] + dt_bias[c])
+ *     h_t   = exp(dt'_t * A[c,n]) * h_{t-1} + dt'_t * B_t[n] * xc_t
+ *     y_t   = (sum_n C_t[n] h_t[n] + Dskip[c] * xc_t) * SiLU(z_t[c])
+ * with SiLU(v) = v / (1 + e^-v), softplus(v) = log(1 + e^v); the inputs x_{-j}
+ * before the call are x_hist (zeros when NULL), so a sequence split across
+ * calls chains exactly with h0 = the previous h_out and x_hist = the previous
+ * call's last K-1 raw inputs.
+ *   x, dt, z, y : (batch, L, D) fp32   (raw x and dt; z NULL = no gate)
+ *   conv_w      : (D, K) fp32, K in 1..4;   conv_b, dt_bias, Dskip : (D) or NULL
+ *   x_hist      : (batch, K-1, D) fp32 or NULL
+ *   A (D, N), B, C (batch, L, N), h0, h_out (batch, D, N): as mb_selective_scan
+ * Supported: dtype MB_F32 (MB_ERR_DTYPE otherwise), N in {4, 8, 16}; x, dt, B, C
+ * and z 16-byte aligned (MB_ERR_ALIGN).  No workspace.
+ */
+mb_status mb_selective_scan_fused(const float* x, const float* conv_w, const float* conv_b,
+                                  const float* x_hist, const float* dt, const float* dt_bias,
+                                  const float* A, const float* B, const float* C,
+                                  const float* Dskip, const float* z, const float* h0, float* y,
+                                  float* h_out, int64_t batch, int64_t L, int64_t D, int64_t N,
+                                  int64_t K, mb_dtype dtype, hipStream_t stream);
+
+/*
  * Mamba-2 scalar-decay SSD, chunkwise (TorchMamba README, Models table row
  * "Mamba-2 (SSD)" and Math notes M2: the dual form Y = (L o C B^T) X, computed
  * per chunk with the state carried between chunks).  Per batch b and head h,

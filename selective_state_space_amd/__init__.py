@@ -16,7 +16,7 @@ import threading
 
 __all__ = [
     "mb_selective_scan", "mb_ssm_step", "mb_ssd_chunked", "mb_trap_ssd", "mb_mimo_ssd",
-    "mb_ssd_step", "mb_workspace_size", "mb_status_str", "lib_path", "load_library", "MBError",
+    "mb_ssd_step", "mb_selective_scan_fused", "mb_workspace_size", "mb_status_str", "lib_path", "load_library", "MBError",
     "MB_OP_SELECTIVE_SCAN", "MB_OP_SSM_STEP", "MB_OP_SSD_CHUNKED", "MB_OP_TRAP_SSD",
     "MB_OP_MIMO_SSD",
 ]
@@ -68,6 +68,9 @@ def load_library():
             lib.mb_workspace_size.restype = ctypes.c_size_t
             for f in ("mb_ssd_chunked", "mb_trap_ssd", "mb_mimo_ssd"):
                 getattr(lib, f).restype = ctypes.c_int
+        if hasattr(lib, "mb_selective_scan_fused"):
+            lib.mb_selective_scan_fused.argtypes = [_vp] * 14 + [_i64] * 5 + [ctypes.c_int, _vp]
+            lib.mb_selective_scan_fused.restype = ctypes.c_int
         if hasattr(lib, "mb_ssd_step"):
             lib.mb_ssd_step.argtypes = [_vp] * 12 + [_i64] * 6 + [ctypes.c_int, _vp]
             lib.mb_ssd_step.restype = ctypes.c_int
@@ -321,3 +324,35 @@ def mb_ssd_step(X, logdecay, B, C, h, *, beta=None, gamma=None, theta=None, X_pr
     _call("mb_ssd_step", _ptr(X), _ptr(logdecay), _ptr(B), _ptr(C), _ptr(beta), _ptr(gamma), _ptr(theta),
           _ptr(X_prev), _ptr(B_prev), _ptr(h), _ptr(h_out), _ptr(Y), b, H, P, G, N, R, code, _stream(dev))
     return Y, h_out
+
+
+def mb_selective_scan_fused(x, conv_w, dt, A, B, C, D=None, h0=None, *, conv_b=None, dt_bias=None, z=None,
+                            x_hist=None, y=None, h_out=None):
+    """Mamba-1 scan with the block prologue and epilogue: causal conv1d + SiLU on
+    x, softplus(dt + dt_bias), and the output gated by SiLU(z).  x, dt, z (batch,
+    L, D), conv_w (D, K), conv_b, dt_bias, D (D,), A (D, N), B, C (batch, L, N),
+    h0 (batch, D, N), x_hist (batch, K-1, D), all float32.  Returns (y, h_out)."""
+    torch = _torch()
+    dev = _device_of(x)
+    f32 = torch.float32
+    b, L, Dm = x.shape
+    K = conv_w.shape[1]
+    N = A.shape[1]
+    _check(x, "x", (b, L, Dm), f32, dev)
+    _check(conv_w, "conv_w", (Dm, K), f32, dev)
+    for t, n in ((conv_b, "conv_b"), (dt_bias, "dt_bias"), (D, "D")):
+        _check(t, n, (Dm,), f32, dev)
+    _check(x_hist, "x_hist", (b, K - 1, Dm), f32, dev)
+    _check(dt, "dt", (b, L, Dm), f32, dev)
+    _check(z, "z", (b, L, Dm), f32, dev)
+    _check(A, "A", (Dm, N), f32, dev)
+    _check(B, "B", (b, L, N), f32, dev)
+    _check(C, "C", (b, L, N), f32, dev)
+    _check(h0, "h0", (b, Dm, N), f32, dev)
+    y = torch.empty((b, L, Dm), dtype=f32, device=dev) if y is None else _check(y, "y", (b, L, Dm), f32, dev)
+    h_out = torch.empty((b, Dm, N), dtype=f32, device=dev) if h_out is None else \
+        _check(h_out, "h_out", (b, Dm, N), f32, dev)
+    _call("mb_selective_scan_fused", _ptr(x), _ptr(conv_w), _ptr(conv_b), _ptr(x_hist), _ptr(dt), _ptr(dt_bias),
+          _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0), _ptr(y), _ptr(h_out), b, L, Dm, N, K, MB_F32,
+          _stream(dev))
+    return y, h_out

@@ -211,11 +211,44 @@ __global__ __launch_bounds__(64 * NW) void k_m1_scan(
 // for that DMA is exact.
 constexpr int kScanT = 32;   // steps per tile
 
-// one tile in LDS: dt[T][16], x[T][16], B[T][N], C[T][N]
-template <int S>
+// one tile in LDS: dt[T][16], x[T][16], B[T][N], C[T][N], and with the block
+// prologue / epilogue the gate z[T][16]
+template <int S, bool Z = false>
 struct ScanTile {
-    float v[kScanT * (32 + 8 * S)];
+    float v[kScanT * (32 + 8 * S + (Z ? 16 : 0))];
 };
+
+// The block prologue / epilogue of the fused scan (its extra inputs).
+struct Fuse {
+    const float* conv_w;    // (D, K), K <= 4
+    const float* conv_b;    // (D) or NULL
+    const float* x_hist;    // (batch, K-1, D) raw inputs before the call, or NULL
+    const float* dt_bias;   // (D) or NULL
+    const float* z;         // (batch, L, D) gate, or NULL
+    int K;
+};
+
+// lane j's value of a quad, to every lane of the quad
+template <int J>
+__device__ __forceinline__ float quad_bcast(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), J * 0x55, 0xF, 0xF, true));
+}
+
+// SiLU and softplus through the hardware exp2 / log2 / reciprocal
+__device__ __forceinline__ float silu_f(float v) {
+    return v * __builtin_amdgcn_rcpf(1.0f + exp2_fast(-v * kLog2e));
+}
+__device__ __forceinline__ float softplus_f(float v) {
+    // max(v, 0) + log(1 + e^-|v|); below 1/16 the log1p series to u^5 (its
+    // truncation is under 2e-7 relative), since forming 1 + u there would lose
+    // the low bits of u
+    // Both branches are computed and one is selected: no divergent branch.
+    const float u = exp2_fast(-fabsf(v) * kLog2e);
+    const float ser = u * (1.0f - u * (0.5f - u * (1.0f / 3.0f - u * (0.25f - 0.2f * u))));
+    const float lg = __builtin_amdgcn_logf(1.0f + u) * 0.6931471805599453f;
+    const float l = u < 0.0625f ? ser : lg;
+    return fmaxf(v, 0.0f) + l;
+}
 
 // s_waitcnt vmcnt(N), other counters unconstrained
 template <int N>
@@ -266,11 +299,11 @@ __device__ __forceinline__ void dma_lds(const Buf& src, lds_f* dst, uint32_t off
         __builtin_amdgcn_raw_ptr_buffer_load_lds(src.r, (__attribute__((address_space(3))) void*)dst, 4, off, 0, 0, 0);
 }
 
-template <int S, bool V16>
+template <int S, bool V16, bool FUSED = false>
 __global__ __launch_bounds__(256) void k_m1_scan_w(
     const float* __restrict__ x, const float* __restrict__ dt, const float* __restrict__ A,
     const float* __restrict__ Bm, const float* __restrict__ Cm, const float* __restrict__ Dskip,
-    const float* h0, float* y, float* h_out, int L, int D, int n_cg)
+    const float* h0, float* y, float* h_out, int L, int D, int n_cg, Fuse fz = Fuse{})
 {
     constexpr int T = kScanT;
     constexpr int N = 4 * S;
@@ -280,13 +313,14 @@ __global__ __launch_bounds__(256) void k_m1_scan_w(
     constexpr int BW = BC16 ? 16 : 4;
     constexpr int NDX = T * 16 * 4 / (64 * XW); // copies per dt / x tile
     constexpr int NDB = T * N * 4 / (64 * BW);  // copies per B / C tile
-    constexpr int NDMA = 2 * NDX + 2 * NDB;     // copies per tile
+    constexpr int NDMA = (FUSED ? 3 : 2) * NDX + 2 * NDB;   // copies per tile
     constexpr int OX = T * 16, OB = 2 * T * 16, OC = 2 * T * 16 + T * N;   // offsets in a tile
+    constexpr int OZ = OC + T * N;
     // three tile buffers, separate objects so that a copy into one never orders
     // the reads of another
-    __shared__ __attribute__((aligned(16))) ScanTile<S> tb0[4];
-    __shared__ __attribute__((aligned(16))) ScanTile<S> tb1[4];
-    __shared__ __attribute__((aligned(16))) ScanTile<S> tb2[4];
+    __shared__ __attribute__((aligned(16))) ScanTile<S, FUSED> tb0[4];
+    __shared__ __attribute__((aligned(16))) ScanTile<S, FUSED> tb1[4];
+    __shared__ __attribute__((aligned(16))) ScanTile<S, FUSED> tb2[4];
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
     lds_f* const p0 = (lds_f*)tb0[w].v;
     lds_f* const p1 = (lds_f*)tb1[w].v;
@@ -303,6 +337,8 @@ __global__ __launch_bounds__(256) void k_m1_scan_w(
     const Buf bB = make_buf(Bm + (size_t)b * L * N, (size_t)L * N * 4);
     const Buf bC = make_buf(Cm + (size_t)b * L * N, (size_t)L * N * 4);
     const Buf by = make_buf(y + (size_t)b * row, row * 4);
+    // the gate: without one, its copies read zeros (the copy count stays fixed)
+    const Buf bz = make_buf(FUSED && fz.z ? fz.z + (size_t)b * row : x, FUSED && fz.z ? row * 4 : 0);
 
     // byte offset of this lane's piece of a tile copy, relative to the tile's first
     // step.  Tiles at or past the end read zeros (offsets past the buffer).
@@ -316,6 +352,7 @@ __global__ __launch_bounds__(256) void k_m1_scan_w(
             const uint32_t off = xo + (uint32_t)((t0 + XW * m) * D) * 4u;   // XW steps per copy
             dma_lds<XW>(bdt, dst + 16 * XW * m, off);
             dma_lds<XW>(bx, dst + OX + 16 * XW * m, off);
+            if constexpr (FUSED) dma_lds<XW>(bz, dst + OZ + 16 * XW * m, off);
         }
 #pragma unroll
         for (int m = 0; m < NDB; ++m) {
@@ -328,7 +365,8 @@ __global__ __launch_bounds__(256) void k_m1_scan_w(
     // the operands of four steps, read from LDS one group ahead of their use
     struct Grp {
         float dt[4], x[4], b[4][S], c[4][S];
-        float xs;   // x of step 4i + q (skip term)
+        float xs;     // x of step 4i + q (skip term); fused: the gate z of that step
+        float gate;   // fused: SiLU of the gate of step 4i + q (1 without a gate)
     };
     auto read_grp = [&](lds_cf* cur, int i, Grp& g) __attribute__((always_inline)) {
 #pragma unroll
@@ -339,7 +377,7 @@ __global__ __launch_bounds__(256) void k_m1_scan_w(
             lds_row<S>(cur + OB + t * N + S * q, g.b[j]);
             lds_row<S>(cur + OC + t * N + S * q, g.c[j]);
         }
-        g.xs = cur[OX + (4 * i + q) * 16 + cl];
+        g.xs = cur[(FUSED ? OZ : OX) + (4 * i + q) * 16 + cl];
     };
 
     float A2[S], h[S];
@@ -352,6 +390,55 @@ __global__ __launch_bounds__(256) void k_m1_scan_w(
     const float Dv = (cok && Dskip) ? Dskip[c] : 0.0f;
     const bool lo = (q & 2) == 0, ev = (q & 1) == 0;
 
+    // fused: the convolution taps (right-aligned to four), the biases and the
+    // raw inputs of the three steps before the current group
+    float cw[4] = {0.0f, 0.0f, 0.0f, 0.0f}, cbv = 0.0f, dtb = 0.0f, xw[3] = {0.0f, 0.0f, 0.0f};
+    if constexpr (FUSED) {
+        const int cc = cok ? c : 0;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const int k = kk - (4 - fz.K);
+            cw[kk] = k >= 0 ? fz.conv_w[(size_t)cc * fz.K + k] : 0.0f;
+        }
+        cbv = fz.conv_b ? fz.conv_b[cc] : 0.0f;
+        dtb = fz.dt_bias ? fz.dt_bias[cc] : 0.0f;
+#pragma unroll
+        for (int j = 0; j < 3; ++j) {
+            const int hk = j - 3 + (fz.K - 1);   // x_hist holds steps -(K-1) .. -1
+            xw[j] = (fz.x_hist && hk >= 0 && cok) ? fz.x_hist[((size_t)b * (fz.K - 1) + hk) * D + c] : 0.0f;
+        }
+    }
+
+    // fused: replace a group's raw x and dt by the convolved, activated input
+    // and the step size; every lane forms the four convolution sums, applies
+    // SiLU and softplus to its own step tg + q only and shares the results
+    // within the quad.  xs becomes the activated input of step tg + q (skip
+    // term) and gate SiLU(z) of that step.
+    auto prologue = [&](Grp& g, int tg) __attribute__((always_inline)) {
+        const float win[7] = {xw[0], xw[1], xw[2], g.x[0], g.x[1], g.x[2], g.x[3]};
+        float pre[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            pre[j] = fmaf(cw[3], win[j + 3], fmaf(cw[2], win[j + 2], fmaf(cw[1], win[j + 1], fmaf(cw[0], win[j], cbv))));
+        // element q of four, by two selects on the bits of q (a chained select on
+        // q would be lowered to an indexed private array)
+        auto own = [&](const float* v) __attribute__((always_inline)) {
+            const float a = ev ? v[0] : v[1], bb = ev ? v[2] : v[3];
+            return lo ? a : bb;
+        };
+        const float xq = silu_f(own(pre));
+        // steps past the sequence keep the state: step size zero (a factor,
+        // not a branch)
+        const float dq = softplus_f(own(g.dt) + dtb) * (tg + q < L ? 1.0f : 0.0f);
+        g.gate = fz.z ? silu_f(g.xs) : 1.0f;
+        g.xs = xq;
+        xw[0] = g.x[1]; xw[1] = g.x[2]; xw[2] = g.x[3];
+        g.x[0] = quad_bcast<0>(xq); g.x[1] = quad_bcast<1>(xq);
+        g.x[2] = quad_bcast<2>(xq); g.x[3] = quad_bcast<3>(xq);
+        g.dt[0] = quad_bcast<0>(dq); g.dt[1] = quad_bcast<1>(dq);
+        g.dt[2] = quad_bcast<2>(dq); g.dt[3] = quad_bcast<3>(dq);
+    };
+
     const int ntiles = (L + T - 1) / T;
     Grp g;
     dma(0, p0);
@@ -359,6 +446,7 @@ __global__ __launch_bounds__(256) void k_m1_scan_w(
     asm volatile("" ::: "memory");
     dma(1, p1);
     read_grp(p0, 0, g);
+    if constexpr (FUSED) prologue(g, 0);
 
     // tile k: copies of tile k + 2 go out first; the operands of its groups are
     // read one group ahead, the last group reading the first of tile k + 1
@@ -380,11 +468,17 @@ __global__ __launch_bounds__(256) void k_m1_scan_w(
             }
             // keep the reads here, a whole group ahead of their use
             __builtin_amdgcn_sched_barrier(0);
+            float xcv[4], dtev[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                xcv[j] = g.x[j];
+                dtev[j] = g.dt[j];
+            }
             float ps[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const float dtv = g.dt[j];
-                const float dtx = dtv * g.x[j];
+                const float dtv = dtev[j];
+                const float dtx = dtv * xcv[j];
                 float p = 0.0f;
 #pragma unroll
                 for (int s = 0; s < S; ++s) {
@@ -401,9 +495,15 @@ __global__ __launch_bounds__(256) void k_m1_scan_w(
             float kk = ev ? k0 : k1;
             const float ss = ev ? k1 : k0;
             kk += quad_swap<0xB1>(ss);
-            kk = fmaf(Dv, g.xs, kk);
+            if constexpr (FUSED)
+                kk = fmaf(Dv, g.xs, kk) * g.gate;
+            else
+                kk = fmaf(Dv, g.xs, kk);
             const uint32_t off = cok ? (uint32_t)((t0 + 4 * i + q) * D + c) * 4u : 0x80000000u;
             __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(kk), by.r, off, 0, 0);
+            // fused: the next group's prologue, a group ahead of its use, so that
+            // its dependent chain overlaps this group's recurrence
+            if constexpr (FUSED) prologue(gn, t0 + 4 * i + 4);
             g = gn;
         }
     };
@@ -653,6 +753,62 @@ extern "C" mb_status mb_selective_scan(const void* x, const void* dt, const floa
     if (dtype == MB_F32)
         return launch_scan<float>(x, dt, A, B, C, Dskip, h0, y, h_out, batch, L, D, N, stream);
     return launch_scan<bf16>(x, dt, A, B, C, Dskip, h0, y, h_out, batch, L, D, N, stream);
+}
+
+extern "C" mb_status mb_selective_scan_fused(const float* x, const float* conv_w, const float* conv_b,
+                                             const float* x_hist, const float* dt, const float* dt_bias,
+                                             const float* A, const float* B, const float* C,
+                                             const float* Dskip, const float* z, const float* h0, float* y,
+                                             float* h_out, int64_t batch, int64_t L, int64_t D, int64_t N,
+                                             int64_t K, mb_dtype dtype, hipStream_t stream)
+{
+    if (dtype != MB_F32) return MB_ERR_DTYPE;
+    if (batch < 0 || L < 0 || D < 0 || K < 1 || K > 4) return MB_ERR_SHAPE;
+    // three tiles of dt, x, z, B and C per wave fit the LDS up to N = 16
+    if (N != 4 && N != 8 && N != 16) return MB_ERR_SHAPE;
+    if (batch > INT32_MAX || L > INT32_MAX || D > INT32_MAX) return MB_ERR_SHAPE;
+    const size_t n_x = (size_t)(batch * L * D), n_b = (size_t)(batch * L * N);
+    const size_t n_h = (size_t)(batch * D * N);
+    if (batch * ((D + 63) / 64) > INT32_MAX) return MB_ERR_SHAPE;
+    if ((L + 64) * D * 4 >= ((int64_t)1 << 31) || (L + 64) * N * 4 >= ((int64_t)1 << 31)) return MB_ERR_SHAPE;
+    if (n_x && (!x || !dt || !y)) return MB_ERR_NULL;
+    if (n_b && (!B || !C)) return MB_ERR_NULL;
+    if (D > 0 && (!A || !conv_w)) return MB_ERR_NULL;
+    // the tiles are copied with 16-byte pieces of rows
+    if (((uintptr_t)x | (uintptr_t)dt | (uintptr_t)B | (uintptr_t)C | (uintptr_t)z) & 15) return MB_ERR_ALIGN;
+    const Span ins[] = {{x, n_x * 4}, {dt, n_x * 4}, {B, n_b * 4}, {C, n_b * 4},
+                        {A, (size_t)(D * N) * 4}, {Dskip, Dskip ? (size_t)D * 4 : 0},
+                        {conv_w, (size_t)(D * K) * 4}, {conv_b, conv_b ? (size_t)D * 4 : 0},
+                        {dt_bias, dt_bias ? (size_t)D * 4 : 0}, {z, z ? n_x * 4 : 0},
+                        {x_hist, x_hist ? (size_t)(batch * (K - 1) * D) * 4 : 0}, {h0, h0 ? n_h * 4 : 0}};
+    if (overlaps_any(y, n_x * 4, ins, 12)) return MB_ERR_ALIAS;
+    if (h_out) {
+        if (overlaps_any(h_out, n_h * 4, ins, 11)) return MB_ERR_ALIAS;
+        if (h0 && h0 != h_out && overlaps(h_out, n_h * 4, h0, n_h * 4)) return MB_ERR_ALIAS;
+        if (overlaps(h_out, n_h * 4, y, n_x * 4)) return MB_ERR_ALIAS;
+    }
+    if (batch == 0 || D == 0) return MB_OK;
+    if (L == 0) return copy_state(h0, h_out, (int64_t)n_h, stream);
+    const Fuse fz{conv_w, conv_b, K > 1 ? x_hist : nullptr, dt_bias, z, (int)K};
+    const int n_cg = (int)((D + 63) / 64);
+    const int n_wg = (int)(batch * n_cg);
+    const bool v16 = D % 4 == 0;
+#define MB_SCAN_F(S)                                                                          \
+    do {                                                                                     \
+        if (v16)                                                                             \
+            hipLaunchKernelGGL((k_m1_scan_w<S, true, true>), dim3(n_wg), dim3(256), 0, stream, \
+                               x, dt, A, B, C, Dskip, h0, y, h_out, (int)L, (int)D, n_cg, fz);  \
+        else                                                                                 \
+            hipLaunchKernelGGL((k_m1_scan_w<S, false, true>), dim3(n_wg), dim3(256), 0, stream, \
+                               x, dt, A, B, C, Dskip, h0, y, h_out, (int)L, (int)D, n_cg, fz);  \
+    } while (0)
+    switch (N) {
+    case 4: MB_SCAN_F(1); break;
+    case 8: MB_SCAN_F(2); break;
+    default: MB_SCAN_F(4); break;
+    }
+#undef MB_SCAN_F
+    return check_launch();
 }
 
 extern "C" mb_status mb_ssm_step(const void* x, const void* dt, const float* A, const void* B,

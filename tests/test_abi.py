@@ -34,7 +34,7 @@ def declared_functions():
 def test_exports_every_declared_function(lib):
     names = declared_functions()
     assert {"mb_selective_scan", "mb_ssm_step", "mb_ssd_chunked", "mb_trap_ssd", "mb_mimo_ssd",
-            "mb_ssd_step", "mb_workspace_size", "mb_status_str", "mb_last_hip_error", "mb_version"} <= set(names)
+            "mb_ssd_step", "mb_selective_scan_fused", "mb_workspace_size", "mb_status_str", "mb_last_hip_error", "mb_version"} <= set(names)
     for n in names:
         assert hasattr(lib, n), "libmb.so does not export " + n
 
@@ -92,6 +92,27 @@ def test_step_validation(lib):
     # partial overlap between h_out and h_in is rejected (exact aliasing is allowed)
     assert step(lib, h_out=FAKE + (1 << 26) + 64) == E_ALIAS
     assert step(lib, y=FAKE + 8) == E_ALIAS
+
+
+def fused(lib, x=FAKE, dt=FAKE + (1 << 22), z=None, y=FAKE + (1 << 24), h_out=FAKE + (1 << 25), conv_w=FAKE + (1 << 26),
+          N=16, K=4, dtype=F32, batch=2):
+    q = lambda v: P(v) if v else None
+    return lib.mb_selective_scan_fused(q(x), q(conv_w), None, None, q(dt), None, P(FAKE + (1 << 23)),
+                                       P(FAKE + (1 << 23) + (1 << 20)), P(FAKE + (1 << 23) + (1 << 21)), None,
+                                       q(z), None, q(y), q(h_out), batch, 8, 16, N, K, dtype, None)
+
+
+def test_fused_scan_validation(lib):
+    assert fused(lib, dtype=BF16) == E_DTYPE
+    assert fused(lib, N=32) == E_SHAPE
+    assert fused(lib, K=5) == E_SHAPE
+    assert fused(lib, K=0) == E_SHAPE
+    assert fused(lib, conv_w=0) == E_NULL
+    assert fused(lib, x=FAKE + 4) == E_ALIGN
+    assert fused(lib, z=FAKE + (1 << 27) + 8) == E_ALIGN
+    assert fused(lib, y=FAKE + 64) == E_ALIAS          # y over x
+    assert fused(lib, z=FAKE + (1 << 24)) == E_ALIAS   # y over z
+    assert fused(lib, batch=0) == OK
 
 
 def ssd_step(lib, X=FAKE, B=FAKE + (1 << 22), Bp=None, Xp=None, h_in=FAKE + (1 << 26), h_out=FAKE + (1 << 26),
