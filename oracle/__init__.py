@@ -64,6 +64,7 @@ def _load():
         lib.oracle_m1_scan.argtypes = [_D] * 9 + [_I] * 4
         lib.oracle_m1_step.argtypes = [_D] * 9 + [_I] * 3
         lib.oracle_ssd.argtypes = [_D] * 7 + [_I] * 6
+        lib.oracle_ssd_bwd.argtypes = [_D] * 12 + [_I] * 6
         lib.oracle_trap.argtypes = [_D] * 12 + [_I] * 6
         lib.oracle_mimo.argtypes = [_D] * 12 + [_I] * 6
         lib.oracle_ssd_step.argtypes = [_D] * 12 + [_I] * 6
@@ -162,6 +163,32 @@ def ssd(X, logdecay, B, C, h0=None):
     _load().oracle_ssd(_p(X), _p(logdecay), _p(B), _p(C), _p(h0), _p(Y), _p(h),
                        b, L, H, P, G, N)
     return Y, h
+
+
+def ssd_bwd(X, logdecay, B, C, dY, h0=None, dh_out=None):
+    """Backward of the Mamba-2 SSD: the gradients of sum dY . Y + sum dh_out .
+    h_out with respect to X, logdecay, B, C, h0.  Shapes as ssd(); dY like X,
+    dh_out like h0.  Returns (dX, dlogdecay, dB, dC, dh0)."""
+    X = _f64(X)
+    b, L, H, P = X.shape
+    B = _f64(B)
+    G, N = B.shape[2], B.shape[3]
+    if G <= 0 or H % G:
+        raise ValueError("H must be a multiple of G")
+    logdecay = _chk(logdecay, (b, L, H), "logdecay")
+    B = _chk(B, (b, L, G, N), "B")
+    C = _chk(C, (b, L, G, N), "C")
+    dY = _chk(dY, (b, L, H, P), "dY")
+    h0 = _opt(h0, (b, H, N, P))
+    dh_out = _opt(dh_out, (b, H, N, P))
+    dX = np.empty((b, L, H, P))
+    dld = np.empty((b, L, H))
+    dB = np.empty((b, L, G, N))
+    dC = np.empty((b, L, G, N))
+    dh0 = np.empty((b, H, N, P))
+    _load().oracle_ssd_bwd(_p(X), _p(logdecay), _p(B), _p(C), _p(h0), _p(dY), _p(dh_out), _p(dX), _p(dld),
+                           _p(dB), _p(dC), _p(dh0), b, L, H, P, G, N)
+    return dX, dld, dB, dC, dh0
 
 
 def trap(X, logdecay, B, C, beta, gamma, theta=None, h0=None, X_prev=None, B_prev=None):

@@ -160,6 +160,94 @@ void oracle_ssd(const double *X, const double *logdecay, const double *B,
     }
 }
 
+/*
+ * Backward (vector-Jacobian product) of the Mamba-2 SSD above: back-propagation
+ * through time of its recurrence (TorchMamba README, Math notes M2 for the
+ * recurrence; the mamba-rs page lists training by back-propagation through
+ * time).  Given dY (b, L, H, P) and dh_out (b, H, N, P) or NULL, it returns the
+ * gradients of  sum dY . Y + sum dh_out . h_out  with respect to X, logdecay,
+ * B, C and h0.  With h_t the state after step t (h_{-1} = h0) and G the
+ * adjoint of the state, walking t = L-1 .. 0 from G = dh_out:
+ *     G     += C_t dY_t^T                         (now d/dh_t)
+ *     dC_t  += h_t dY_t          dB_t += G X_t     (summed over the heads of a group)
+ *     dX_t   = G^T B_t
+ *     dld_t  = e^{ld_t} <G, h_{t-1}>
+ *     G      = e^{ld_t} G                         (now d/dh_{t-1})
+ * and dh0 = G at the end.  The forward states are kept for every step.
+ */
+void oracle_ssd_bwd(const double *X, const double *logdecay, const double *B,
+                    const double *C, const double *h0, const double *dY,
+                    const double *dh_out, double *dX, double *dld, double *dB,
+                    double *dC, double *dh0, int64_t batch, int64_t L, int64_t H,
+                    int64_t P, int64_t G, int64_t N)
+{
+    int64_t hpg = H / G;
+    int64_t units = batch * G;
+    int64_t NP = N * P;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t u = 0; u < units; ++u) {
+        int64_t b = u / G, g = u % G;
+        for (int64_t t = 0; t < L; ++t)
+            for (int64_t n = 0; n < N; ++n) {
+                dB[((b * L + t) * G + g) * N + n] = 0.0;
+                dC[((b * L + t) * G + g) * N + n] = 0.0;
+            }
+        double *hs = (double *)malloc(sizeof(double) * (size_t)((L + 1) * NP > 0 ? (L + 1) * NP : 1));
+        double *A = (double *)malloc(sizeof(double) * (size_t)(NP > 0 ? NP : 1));
+        for (int64_t h = g * hpg; h < (g + 1) * hpg; ++h) {
+            /* forward: hs[t + 1] = state after step t, hs[0] = h0 */
+            for (int64_t i = 0; i < NP; ++i) hs[i] = h0 ? h0[(b * H + h) * NP + i] : 0.0;
+            for (int64_t t = 0; t < L; ++t) {
+                double a = exp(logdecay[(b * L + t) * H + h]);
+                const double *Bt = B + ((b * L + t) * G + g) * N;
+                const double *Xt = X + ((b * L + t) * H + h) * P;
+                const double *prev = hs + t * NP;
+                double *cur = hs + (t + 1) * NP;
+                for (int64_t n = 0; n < N; ++n)
+                    for (int64_t p = 0; p < P; ++p)
+                        cur[n * P + p] = a * prev[n * P + p] + Bt[n] * Xt[p];
+            }
+            /* reverse */
+            for (int64_t i = 0; i < NP; ++i) A[i] = dh_out ? dh_out[(b * H + h) * NP + i] : 0.0;
+            for (int64_t t = L - 1; t >= 0; --t) {
+                double a = exp(logdecay[(b * L + t) * H + h]);
+                const double *Bt = B + ((b * L + t) * G + g) * N;
+                const double *Ct = C + ((b * L + t) * G + g) * N;
+                const double *Xt = X + ((b * L + t) * H + h) * P;
+                const double *dYt = dY + ((b * L + t) * H + h) * P;
+                const double *ht = hs + (t + 1) * NP, *hp = hs + t * NP;
+                double *dBt = dB + ((b * L + t) * G + g) * N;
+                double *dCt = dC + ((b * L + t) * G + g) * N;
+                double *dXt = dX + ((b * L + t) * H + h) * P;
+                for (int64_t n = 0; n < N; ++n)
+                    for (int64_t p = 0; p < P; ++p) A[n * P + p] += Ct[n] * dYt[p];
+                for (int64_t n = 0; n < N; ++n) {
+                    double sc = 0.0, sb = 0.0;
+                    for (int64_t p = 0; p < P; ++p) {
+                        sc += ht[n * P + p] * dYt[p];
+                        sb += A[n * P + p] * Xt[p];
+                    }
+                    dCt[n] += sc;
+                    dBt[n] += sb;
+                }
+                for (int64_t p = 0; p < P; ++p) {
+                    double sx = 0.0;
+                    for (int64_t n = 0; n < N; ++n) sx += Bt[n] * A[n * P + p];
+                    dXt[p] = sx;
+                }
+                double sl = 0.0;
+                for (int64_t i = 0; i < NP; ++i) sl += A[i] * hp[i];
+                dld[(b * L + t) * H + h] = a * sl;
+                for (int64_t i = 0; i < NP; ++i) A[i] *= a;
+            }
+            if (dh0)
+                for (int64_t i = 0; i < NP; ++i) dh0[(b * H + h) * NP + i] = A[i];
+        }
+        free(hs);
+        free(A);
+    }
+}
+
 /* Rotate consecutive pairs (2k, 2k+1) of v[0..N) by angle phi[k]:
  * (v0, v1) -> (cos*v0 - sin*v1, sin*v0 + cos*v1).  `stride` is the distance in
  * elements between v[n] and v[n+1]. */

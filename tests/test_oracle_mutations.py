@@ -52,6 +52,13 @@ MUTATIONS = {
     "trap_prev0_ignored": ("if (B_prev0) memcpy(Bprev, B_prev0 + (b * G + g) * N, sizeof(double) * (size_t)N);", ""),
     "mimo_prev0_wrong_head": ("if (X_prev0) memcpy(Xprev, X_prev0 + (b * H + h) * P * R, sizeof(double) * (size_t)(P * R));",
                               "if (X_prev0) memcpy(Xprev, X_prev0 + b * H * P * R, sizeof(double) * (size_t)(P * R));"),
+    "bwd_dld_uses_new_state": ("for (int64_t i = 0; i < NP; ++i) sl += A[i] * hp[i];",
+                               "for (int64_t i = 0; i < NP; ++i) sl += A[i] * ht[i];"),
+    "bwd_adjoint_not_decayed": ("for (int64_t i = 0; i < NP; ++i) A[i] *= a;", ""),
+    "bwd_dX_uses_C": ("for (int64_t n = 0; n < N; ++n) sx += Bt[n] * A[n * P + p];",
+                      "for (int64_t n = 0; n < N; ++n) sx += Ct[n] * A[n * P + p];"),
+    "bwd_dC_uses_previous_state": ("sc += ht[n * P + p] * dYt[p];", "sc += hp[n * P + p] * dYt[p];"),
+    "bwd_final_state_gradient_dropped": ("A[i] = dh_out ? dh_out[(b * H + h) * NP + i] : 0.0;", "A[i] = 0.0;"),
 }
 
 
@@ -116,6 +123,21 @@ def _battery(o):
         Yb, hb = getattr(o, fn)(**rest, X_prev=inp["X"][:, 7], B_prev=inp["B"][:, 7])
         if not (np.allclose(Yb, Y[:, 8:], rtol=1e-9, atol=1e-11) and np.allclose(hb, h, rtol=1e-9, atol=1e-11)):
             failed.append(fn + "_split_with_previous_token")
+
+    # backward of the SSD: directional derivatives of the forward loss
+    inp = wl.ssd_inputs(rng, 1, 12, 2, 3, 4, G=1, h0_sd=0.5)
+    dY = rng.standard_normal(inp["X"].shape)
+    dh = rng.standard_normal(inp["h0"].shape)
+
+    def lossf(d):
+        Yf, hf = o.ssd(**d)
+        return float(np.sum(Yf * dY) + np.sum(hf * dh))
+    gr = o.ssd_bwd(inp["X"], inp["logdecay"], inp["B"], inp["C"], dY, inp["h0"], dh)
+    for k, gk in zip(("X", "logdecay", "B", "C", "h0"), gr):
+        v = rng.standard_normal(inp[k].shape)
+        fd = (lossf(dict(inp, **{k: inp[k] + 1e-6 * v})) - lossf(dict(inp, **{k: inp[k] - 1e-6 * v}))) / 2e-6
+        if abs(fd - float(np.sum(gk * v))) > 1e-6 * max(1.0, abs(fd)):
+            failed.append("ssd_bwd_directional_" + k)
 
     inp = wl.m1_block_inputs(rng, 2, 15, 3, 4, K=4, h0_sd=0.3, hist=True)
     y, h = o.m1_block(**inp)
