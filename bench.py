@@ -80,6 +80,17 @@ def mimo_work(b, L, H, P, N, R, Q=64):
     return nbytes, flops
 
 
+def ssd_bwd_work(b, L, H, P, N, G, Q=64):
+    """Backward of the Mamba-2 SSD: inputs X, dY, logdecay, B, C, dh_out read and
+    dX, dlogdecay, dB, dC, dh0 written once; flops of the chunkwise form at
+    Q = 64 (causal halves): the chunk-local states U and V (4NP), the state
+    products dY H^T, B G, X G^T (6NP), dY X^T and its two uses (2P(Q+1) + 2N(Q+1)
+    less the shared C B^T, N(Q+1) G/H)."""
+    nbytes = 4 * (2 * 2 * b * L * H * P + 2 * 2 * b * L * G * N + 2 * b * L * H + 2 * b * H * N * P)
+    flops = b * L * H * (10 * N * P + 2 * P * (Q + 1) + 2 * N * (Q + 1) + N * (Q + 1) * G / H)
+    return nbytes, flops
+
+
 def ssd_step_work(b, H, P, N, G, R, trap, rot, es=4):
     """One decode token: the fp32 state read and written once, plus the token's
     inputs and output."""
@@ -222,6 +233,36 @@ class SSD(Workload):
         self.mb.mb_ssd_chunked(self.X, self.ld, self.B, self.C, None, Y=self.Y, h_out=self.h, ws=self.ws)
 
 
+class SSDBwd(Workload):
+    """Backward of the Mamba-2 SSD at the block shape (outside the step, measured
+    beside it)."""
+    name = "ssd_bwd"
+    kernel = "k_bwd_local + k_bwd_pass + k_bwd_grad + k_bwd_ld"
+    source = "selective_state_space_amd/csrc/ssd_bwd.hip"
+    bound = "mfma"
+
+    def __init__(self, mb, wl, torch):
+        self.mb = mb
+        b, L, H, P, N, G = 4, 4096, 24, 64, 128, 1
+        self.shape = dict(batch=b, L=L, H=H, P=P, N=N, G=G)
+        inp = wl.ssd_bwd_block()
+        self.inp = inp
+        self.t = {k: _dev(v, torch.float32) for k, v in inp.items() if v is not None}
+        self.ws = torch.empty(mb.mb_workspace_size(mb.MB_OP_SSD_CHUNKED_BWD, b, L, H, P, G, N),
+                              dtype=torch.uint8, device="cuda")
+        t = self.t
+        self.out = dict(dX=torch.empty_like(t["X"]), dlogdecay=torch.empty_like(t["logdecay"]),
+                        dB=torch.empty_like(t["B"]), dC=torch.empty_like(t["C"]), dh0=torch.empty_like(t["dh_out"]))
+        self.tokens = b * L
+        self.bytes, self.flops = ssd_bwd_work(b, L, H, P, N, G)
+        self.exps = None
+
+    def run(self):
+        t = self.t
+        self.mb.mb_ssd_chunked_bwd(t["X"], t["logdecay"], t["B"], t["C"], t["dY"], None, t["dh_out"], ws=self.ws,
+                                   **self.out)
+
+
 class SISO(Workload):
     name = "siso"
     kernel = "k_walk (state-only pass) + k_walk (full pass)"
@@ -308,9 +349,10 @@ class SSDDecode(Workload):
 
 
 ALL = ["m1_scan", "m1_step", "ssd_f32", "ssd_bf16", "siso", "mimo"]
-# measured beside the step, not part of it: the decode steps of the SSD family and
-# the Mamba-1 scan with the block prologue and epilogue fused
-NEXT = ["m2_decode", "siso_decode", "mimo_decode", "m1_fused"]
+# measured beside the step, not part of it: the decode steps of the SSD family, the
+# Mamba-1 scan with the block prologue and epilogue fused, and the backward of the
+# Mamba-2 SSD
+NEXT = ["m2_decode", "siso_decode", "mimo_decode", "m1_fused", "ssd_bwd"]
 
 
 def make(name, mb, wl, torch):
@@ -320,6 +362,8 @@ def make(name, mb, wl, torch):
         return M1Step(mb, wl, torch)
     if name == "m1_fused":
         return M1Fused(mb, wl, torch)
+    if name == "ssd_bwd":
+        return SSDBwd(mb, wl, torch)
     if name == "ssd_f32":
         return SSD(mb, wl, torch, "f32")
     if name == "ssd_bf16":
@@ -420,7 +464,8 @@ def cold_ms(torch, w, reps=5):
 
 
 def time_next(args, mb, wl, torch):
-    """Decode steps of the SSD family and the fused Mamba-1 block scan, timed with
+    """Decode steps of the SSD family, the fused Mamba-1 block scan and the SSD
+    backward, timed with
     HIP events on the stream they run on, outside the step (they are not part of
     its token count)."""
     res = []

@@ -60,7 +60,8 @@ typedef enum {
     MB_OP_SSM_STEP = 1,
     MB_OP_SSD_CHUNKED = 2,
     MB_OP_TRAP_SSD = 3,
-    MB_OP_MIMO_SSD = 4
+    MB_OP_MIMO_SSD = 4,
+    MB_OP_SSD_CHUNKED_BWD = 5
 } mb_op;
 
 /*
@@ -243,6 +244,37 @@ mb_status mb_ssd_step(const void* X, const float* logdecay, const void* B,
                       const float* h_in, float* h_out, void* Y, int64_t batch,
                       int64_t H, int64_t P, int64_t G, int64_t N, int64_t R,
                       mb_dtype dtype, hipStream_t stream);
+
+/*
+ * Backward of mb_ssd_chunked (fp32): the vector-Jacobian product of the Mamba-2
+ * SSD (TorchMamba README, Math notes M2; trained by back-propagation through
+ * time, as the mamba-rs page lists).  Given dY (gradient of the loss with
+ * respect to Y) and dh_out (with respect to h_out; NULL = zero), returns the
+ * gradients of  sum dY . Y + sum dh_out . h_out  with respect to X, logdecay,
+ * B, C and h0.  With h_t the forward state after step t and G_t its adjoint
+ * (G_{L-1} = C_{L-1} dY_{L-1}^T + dh_out, G_{t-1} = e^{ld_t} G_t + C_{t-1} dY_{t-1}^T):
+ *     dX_t = G_t^T B_t,  dB_t = sum_h G_t X_t,  dC_t = sum_h h_t dY_t,
+ *     dlogdecay_t = e^{ld_t} <G_t, h_{t-1}>,  dh0 = e^{ld_0} G_0
+ * (sums over the heads h of the group).  The forward states are recomputed
+ * chunkwise; nothing of the forward call is needed.
+ *   X, dY, dX           : (batch, L, H, P)  fp32
+ *   logdecay, dlogdecay : (batch, L, H)     fp32
+ *   B, C, dB, dC        : (batch, L, G, N)  fp32
+ *   h0, dh_out, dh0     : (batch, H, N, P)  fp32; h0, dh_out NULL = zeros; dh0 NULL = not wanted
+ * ws / ws_bytes: device workspace of at least
+ * mb_workspace_size(MB_OP_SSD_CHUNKED_BWD, ...) bytes, 256-byte aligned (two
+ * N x P states per (batch, head, 64-step chunk), plus small buffers).
+ * Supported: dtype MB_F32 (MB_ERR_DTYPE otherwise); N in {64, 128}, P in
+ * {32, 64} (MB_ERR_SHAPE otherwise); X, B, C, dY, dX, dB, dC 16-byte aligned
+ * (MB_ERR_ALIGN).  No output may overlap an input, another output or the
+ * workspace (MB_ERR_ALIAS).
+ */
+mb_status mb_ssd_chunked_bwd(const float* X, const float* logdecay, const float* B,
+                             const float* C, const float* h0, const float* dY,
+                             const float* dh_out, float* dX, float* dlogdecay, float* dB,
+                             float* dC, float* dh0, int64_t batch, int64_t L, int64_t H,
+                             int64_t P, int64_t G, int64_t N, mb_dtype dtype, void* ws,
+                             size_t ws_bytes, hipStream_t stream);
 
 /*
  * Bytes of device workspace an entry point needs for the given sizes (0 if it

@@ -16,9 +16,9 @@ import threading
 
 __all__ = [
     "mb_selective_scan", "mb_ssm_step", "mb_ssd_chunked", "mb_trap_ssd", "mb_mimo_ssd",
-    "mb_ssd_step", "mb_selective_scan_fused", "mb_workspace_size", "mb_status_str", "lib_path", "load_library", "MBError",
+    "mb_ssd_step", "mb_selective_scan_fused", "mb_ssd_chunked_bwd", "mb_workspace_size", "mb_status_str", "lib_path", "load_library", "MBError",
     "MB_OP_SELECTIVE_SCAN", "MB_OP_SSM_STEP", "MB_OP_SSD_CHUNKED", "MB_OP_TRAP_SSD",
-    "MB_OP_MIMO_SSD",
+    "MB_OP_MIMO_SSD", "MB_OP_SSD_CHUNKED_BWD",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -28,7 +28,7 @@ _lib = None
 
 MB_F32, MB_BF16 = 0, 1
 (MB_OP_SELECTIVE_SCAN, MB_OP_SSM_STEP, MB_OP_SSD_CHUNKED, MB_OP_TRAP_SSD,
- MB_OP_MIMO_SSD) = range(5)
+ MB_OP_MIMO_SSD, MB_OP_SSD_CHUNKED_BWD) = range(6)
 
 _vp = ctypes.c_void_p
 _i64 = ctypes.c_int64
@@ -68,6 +68,9 @@ def load_library():
             lib.mb_workspace_size.restype = ctypes.c_size_t
             for f in ("mb_ssd_chunked", "mb_trap_ssd", "mb_mimo_ssd"):
                 getattr(lib, f).restype = ctypes.c_int
+        if hasattr(lib, "mb_ssd_chunked_bwd"):
+            lib.mb_ssd_chunked_bwd.argtypes = [_vp] * 12 + [_i64] * 6 + [ctypes.c_int, _vp, ctypes.c_size_t, _vp]
+            lib.mb_ssd_chunked_bwd.restype = ctypes.c_int
         if hasattr(lib, "mb_selective_scan_fused"):
             lib.mb_selective_scan_fused.argtypes = [_vp] * 14 + [_i64] * 5 + [ctypes.c_int, _vp]
             lib.mb_selective_scan_fused.restype = ctypes.c_int
@@ -228,6 +231,34 @@ def mb_ssd_chunked(X, logdecay, B, C, h0=None, *, chunk=0, Y=None, h_out=None, w
     _call("mb_ssd_chunked", _ptr(X), _ptr(logdecay), _ptr(B), _ptr(C), _ptr(h0), _ptr(Y), _ptr(h_out),
           b, L, H, P, G, N, chunk, code, _ptr(ws), nws, _stream(dev))
     return Y, h_out
+
+
+def mb_ssd_chunked_bwd(X, logdecay, B, C, dY, h0=None, dh_out=None, *, dX=None, dlogdecay=None, dB=None,
+                       dC=None, dh0=None, ws=None):
+    """Backward of the Mamba-2 SSD (float32): the gradients of sum dY . Y + sum
+    dh_out . h_out with respect to X, logdecay, B, C and h0.  Shapes as
+    mb_ssd_chunked; dY like X, dh_out like h0 (None: zero).  Returns (dX,
+    dlogdecay, dB, dC, dh0)."""
+    torch = _torch()
+    dev = _device_of(X)
+    f32 = torch.float32
+    b, L, H, P = X.shape
+    G, N = B.shape[2], B.shape[3]
+    _check(X, "X", (b, L, H, P), f32, dev)
+    _check(logdecay, "logdecay", (b, L, H), f32, dev)
+    _check(B, "B", (b, L, G, N), f32, dev)
+    _check(C, "C", (b, L, G, N), f32, dev)
+    _check(dY, "dY", (b, L, H, P), f32, dev)
+    _check(h0, "h0", (b, H, N, P), f32, dev)
+    _check(dh_out, "dh_out", (b, H, N, P), f32, dev)
+    out = []
+    for t, n, shp in ((dX, "dX", (b, L, H, P)), (dlogdecay, "dlogdecay", (b, L, H)), (dB, "dB", (b, L, G, N)),
+                      (dC, "dC", (b, L, G, N)), (dh0, "dh0", (b, H, N, P))):
+        out.append(torch.empty(shp, dtype=f32, device=dev) if t is None else _check(t, n, shp, f32, dev))
+    ws, nws = _workspace(MB_OP_SSD_CHUNKED_BWD, dev, ws, (b, L, H, P, G, N, 1, 0))
+    _call("mb_ssd_chunked_bwd", _ptr(X), _ptr(logdecay), _ptr(B), _ptr(C), _ptr(h0), _ptr(dY), _ptr(dh_out),
+          *[_ptr(t) for t in out], b, L, H, P, G, N, MB_F32, _ptr(ws), nws, _stream(dev))
+    return tuple(out)
 
 
 def mb_trap_ssd(X, logdecay, B, C, beta, gamma, theta=None, h0=None, *, X_prev=None, B_prev=None,

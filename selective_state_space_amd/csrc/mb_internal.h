@@ -49,6 +49,9 @@ inline bool dtype_ok(mb_dtype d) { return d == MB_F32 || d == MB_BF16; }
 // Number of compute units of the current device (cached per device).
 int device_cu_count();
 
+// Workspace bytes of the Mamba-2 SSD backward (0 for unsupported sizes).
+size_t ssd_bwd_workspace(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t G, int64_t N);
+
 // Copy h0 (or zeros) into h_out; used for zero-length sequences.
 mb_status copy_state(const float* h0, float* h_out, int64_t n, hipStream_t stream);
 

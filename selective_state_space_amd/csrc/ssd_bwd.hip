@@ -1,0 +1,697 @@
+// ssd_bwd.hip -- backward of the Mamba-2 scalar-decay SSD (fp32) for gfx950.
+//
+// The forward recurrence (TorchMamba README, Math notes M2), per batch b and
+// head h with group g:
+//     h_t = e^{ld_t} h_{t-1} + B_t X_t^T      (N x P),   Y_t = h_t^T C_t.
+// Its vector-Jacobian product for dY and dh_out (back-propagation through time,
+// the training mode listed on the mamba-rs page) is computed chunkwise.  A chunk
+// holds Q = 64 steps; cum_j is the chunk-local inclusive sum of ld, Lam = cum_63.
+// With Hc the state entering chunk c and Gc the adjoint of the state at its end
+// (the gradient arriving from every later step and dh_out):
+//     H_{c+1} = e^{Lam_c} H_c + U_c,     U_c = sum_j e^{Lam - cum_j} B_j X_j^T
+//     G_{c-1} = e^{Lam_c} G_c + V_c,     V_c = sum_j e^{cum_j} C_j dY_j^T
+// with H_0 = h0, G_last = dh_out and dh0 = G_{-1}.  Inside a chunk, with the
+// causal decay mask W[i][j] = e^{cum_i - cum_j} [j <= i]:
+//     dC = (dY X^T o W) B + diag(e^{cum}) dY H^T
+//     dX = (C B^T o W)^T dY + diag(e^{Lam - cum}) B G
+//     dB = (dY X^T o W)^T C + diag(e^{Lam - cum}) X G^T
+// (dB and dC summed over the heads of a group).  The log-decay gradient follows
+// from the same quantities: with dl_t = C_t . dC_t - X_t . dX_t (per head),
+//     dlogdecay_t = sum_{tau >= t} dl_tau + <dh_out, h_out>,
+// since <G_t, h_t> telescopes along the sequence.
+//
+// Kernels
+//   k_bwd_local  (batch, chunk, group), heads in turn: U_c, V_c and Lam_c on
+//                fp32 MFMA into the workspace.
+//   k_bwd_pass   one thread per (batch, head, state element): the two chunk
+//                recurrences, elementwise, in place (U_c -> H_c, V_c -> G_c), dh0,
+//                and the partial sums of <dh_out, h_out>.
+//   k_bwd_grad   (batch, chunk, group), heads in turn: dX, the per-step dl, and
+//                dB, dC accumulated over the group's heads, on fp32 MFMA.
+//   k_bwd_ld     one wave per (batch, head): the suffix sums of dl.
+#include "mb_internal.h"
+
+namespace mb {
+namespace {
+
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+constexpr int kQ = 64;          // steps per chunk
+constexpr int kBwdThreads = 256;
+constexpr int kLQ = kQ + 4;     // LDS row stride of the 64 x 64 score tiles
+
+__device__ __forceinline__ floatx4 mfma4(float a, float b, floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float exp_e(float v) { return exp2_fast(v * kLog2e); }
+
+struct BwdArgs {
+    const float* X;         // (batch, L, H, P)
+    const float* ld;        // (batch, L, H)
+    const float* B;         // (batch, L, G, N)
+    const float* C;
+    const float* h0;        // (batch, H, N, P) or NULL
+    const float* dY;        // (batch, L, H, P)
+    const float* dh_out;    // (batch, H, N, P) or NULL
+    float* dX;
+    float* dld;             // (batch, L, H)
+    float* dB;              // (batch, L, G, N)
+    float* dC;
+    float* dh0;             // (batch, H, N, P) or NULL
+    float* st;              // workspace: per (b, h, c) two N x P slots (H_c, G_c)
+    float* lam;             // workspace: per (b, h, c) total log-decay of the chunk
+    float* dl;              // workspace: (batch, L, H) per-step dl
+    float* fin;             // workspace: per (b, h) partial sums of <dh_out, h_out>
+    int L, H, G, N, P, nch, nfin;
+};
+
+// Row stride (floats) of an LDS array of rows `w` wide: w + 4, so that rows
+// four apart fall sixteen banks apart (column reads of four rows per lane group).
+template <int W>
+struct Ld {
+    static constexpr int v = W + 4;
+};
+
+// Rows t0 .. t0 + 63 of a tensor with rows of W floats (row pitch `pitch`),
+// held in registers between a load and an LDS store: float4 f = tid + T k of
+// the 64 x W / 4, rows at or past L read as zero.  Loading one head's rows
+// while the previous head computes hides the global latency.
+template <int W, int T>
+struct RowPref {
+    static constexpr int V = W / 4;
+    static constexpr int F = (kQ * V + T - 1) / T;
+    float4 v[F];
+    __device__ __forceinline__ void load(const float* src, size_t pitch, int t0, int L) {
+#pragma unroll
+        for (int k = 0; k < F; ++k) {
+            const int f = threadIdx.x + T * k;
+            const int j = f / V, v4 = f % V;
+            v[k] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            if (f < kQ * V && t0 + j < L) v[k] = *(const float4*)(src + (size_t)(t0 + j) * pitch + 4 * v4);
+        }
+    }
+    // to LDS rows of stride LDW, each row scaled by scale[j] when given
+    __device__ __forceinline__ void store(float* dst, int LDW, const float* scale) const {
+#pragma unroll
+        for (int k = 0; k < F; ++k) {
+            const int f = threadIdx.x + T * k;
+            if (f >= kQ * V) continue;
+            const int j = f / V, v4 = f % V;
+            float4 x = v[k];
+            if (scale) {
+                const float s = scale[j];
+                x.x *= s; x.y *= s; x.z *= s; x.w *= s;
+            }
+            *(float4*)(dst + j * LDW + 4 * v4) = x;
+        }
+    }
+};
+
+// Chunk-local cumulative log-decay by one wave from its lanes' log-decays (lane
+// j: step t0 + j): s_cum[j], e^{Lam - cum_j} (s_we), e^{cum_j} (s_ws); returns Lam.
+__device__ __forceinline__ float chunk_weights(float v, float* s_cum, float* s_we, float* s_ws) {
+    const int lane = threadIdx.x % 64;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const float u = __shfl_up(v, d, 64);
+        if (lane >= d) v += u;
+    }
+    const float lam = __shfl(v, 63, 64);
+    if (s_cum) s_cum[lane] = v;
+    s_we[lane] = exp_e(lam - v);
+    s_ws[lane] = exp_e(v);
+    return lam;
+}
+
+constexpr int kMma = 512;   // threads of the two matrix kernels: 8 waves, two per SIMD
+
+// ---------------------------------------------------------------------------
+// k_bwd_local: U_c = B^T diag(e^{Lam - cum}) X and V_c = C^T diag(e^{cum}) dY for
+// every head of the group, and Lam_c.  Wave w owns the state row blocks
+// w, w + 8, ... (16 rows each) of both, for all P columns.
+// ---------------------------------------------------------------------------
+template <int NN, int PP>
+__global__ __launch_bounds__(kMma) void k_bwd_local(BwdArgs a) {
+    constexpr int LB = Ld<NN>::v, LX = Ld<PP>::v;
+    constexpr int NB = NN / 16, PB = PP / 16;
+    constexpr int NBW = (NB + 7) / 8;        // row blocks per wave
+    __shared__ __attribute__((aligned(16))) float sB[kQ * LB];
+    __shared__ __attribute__((aligned(16))) float sC[kQ * LB];
+    __shared__ __attribute__((aligned(16))) float sX[kQ * LX];
+    __shared__ __attribute__((aligned(16))) float sD[kQ * LX];
+    __shared__ float s_we[kQ], s_ws[kQ];
+
+    const int g = blockIdx.x % a.G;
+    const int c = (blockIdx.x / a.G) % a.nch;
+    const int b = blockIdx.x / (a.G * a.nch);
+    const int t0 = c * kQ;
+    const int hpg = a.H / a.G;
+    const int lane = threadIdx.x % 64, wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
+    const int li = lane % 16, q = lane / 16;
+    const size_t bc_pitch = (size_t)a.G * NN, x_pitch = (size_t)a.H * PP;
+    const size_t NP = (size_t)NN * PP;
+    {
+        RowPref<NN, kMma> r;
+        r.load(a.B + ((size_t)b * a.L * a.G + g) * NN, bc_pitch, t0, a.L);
+        r.store(sB, LB, nullptr);
+        r.load(a.C + ((size_t)b * a.L * a.G + g) * NN, bc_pitch, t0, a.L);
+        r.store(sC, LB, nullptr);
+    }
+    RowPref<PP, kMma> px, pd;
+    float ldv = 0.0f;
+    auto prefetch = [&](int h) {
+        px.load(a.X + ((size_t)b * a.L * a.H + h) * PP, x_pitch, t0, a.L);
+        pd.load(a.dY + ((size_t)b * a.L * a.H + h) * PP, x_pitch, t0, a.L);
+        if (wave == 0) ldv = t0 + lane < a.L ? a.ld[((size_t)b * a.L + t0 + lane) * a.H + h] : 0.0f;
+    };
+    prefetch(g * hpg);
+
+    for (int hh = 0; hh < hpg; ++hh) {
+        const int h = g * hpg + hh;
+        if (wave == 0) {
+            const float lam = chunk_weights(ldv, nullptr, s_we, s_ws);
+            if (lane == 0) a.lam[((size_t)b * a.H + h) * a.nch + c] = lam;
+        }
+        __syncthreads();   // weights ready; the previous head's reads of sX / sD done
+        px.store(sX, LX, s_we);
+        pd.store(sD, LX, s_ws);
+        __syncthreads();
+        if (hh + 1 < hpg) prefetch(h + 1);
+
+        floatx4 accu[NBW][PB], accv[NBW][PB];
+#pragma unroll
+        for (int m = 0; m < NBW; ++m)
+#pragma unroll
+            for (int pb = 0; pb < PB; ++pb) {
+                accu[m][pb] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+                accv[m][pb] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+            }
+#pragma unroll
+        for (int kg = 0; kg < kQ / 16; ++kg) {
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const int j = 16 * kg + 4 * q + s;     // the step this lane supplies
+                float xb[PB], db[PB];
+#pragma unroll
+                for (int pb = 0; pb < PB; ++pb) {
+                    xb[pb] = sX[j * LX + 16 * pb + li];
+                    db[pb] = sD[j * LX + 16 * pb + li];
+                }
+#pragma unroll
+                for (int m = 0; m < NBW; ++m) {
+                    const int nb = wave + 8 * m;
+                    if (nb >= NB) continue;
+                    const float bv = sB[j * LB + 16 * nb + li];
+                    const float cv = sC[j * LB + 16 * nb + li];
+#pragma unroll
+                    for (int pb = 0; pb < PB; ++pb) {
+                        accu[m][pb] = mfma4(bv, xb[pb], accu[m][pb]);
+                        accv[m][pb] = mfma4(cv, db[pb], accv[m][pb]);
+                    }
+                }
+            }
+        }
+        float* slot = a.st + (((size_t)b * a.H + h) * a.nch + c) * 2 * NP;
+#pragma unroll
+        for (int m = 0; m < NBW; ++m) {
+            const int nb = wave + 8 * m;
+            if (nb >= NB) continue;
+#pragma unroll
+            for (int pb = 0; pb < PB; ++pb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const size_t e = (size_t)(16 * nb + 4 * q + r) * PP + 16 * pb + li;
+                    slot[e] = accu[m][pb][r];
+                    slot[NP + e] = accv[m][pb][r];
+                }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// k_bwd_pass: the chunk recurrences, elementwise.  Thread e of (b, h) holds
+// state element e = n P + p.  Forward: slot 0 of chunk c becomes H_c (read
+// U_c first); reverse: slot 1 becomes G_c.  Eight chunks are loaded ahead of
+// their use.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kBwdThreads) void k_bwd_pass(BwdArgs a) {
+    const int bh = blockIdx.y;
+    const size_t NP = (size_t)a.N * a.P;
+    const int e = blockIdx.x * kBwdThreads + threadIdx.x;
+    const bool ok = e < (int)NP;
+    const int ee = ok ? e : 0;
+    float* base = a.st + (size_t)bh * a.nch * 2 * NP;
+    const float* lam = a.lam + (size_t)bh * a.nch;
+    constexpr int KU = 8;
+
+    float hs = (ok && a.h0) ? a.h0[(size_t)bh * NP + ee] : 0.0f;
+    for (int c0 = 0; c0 < a.nch; c0 += KU) {
+        float u[KU], d[KU];
+#pragma unroll
+        for (int k = 0; k < KU; ++k) {
+            const int c = c0 + k;
+            u[k] = (ok && c < a.nch) ? base[(size_t)c * 2 * NP + ee] : 0.0f;
+            d[k] = c < a.nch ? exp_e(lam[c]) : 1.0f;
+        }
+#pragma unroll
+        for (int k = 0; k < KU; ++k) {
+            const int c = c0 + k;
+            if (ok && c < a.nch) base[(size_t)c * 2 * NP + ee] = hs;
+            hs = fmaf(d[k], hs, u[k]);
+        }
+    }
+    const float dh = (ok && a.dh_out) ? a.dh_out[(size_t)bh * NP + ee] : 0.0f;
+    // partial sum of <dh_out, h_out> over this block
+    {
+        float v = dh * hs;
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+        __shared__ float s_part[kBwdThreads / 64];
+        if (threadIdx.x % 64 == 0) s_part[threadIdx.x / 64] = v;
+        __syncthreads();
+        if (threadIdx.x == 0)
+            a.fin[(size_t)bh * a.nfin + blockIdx.x] = (s_part[0] + s_part[1]) + (s_part[2] + s_part[3]);
+    }
+    float gs = dh;
+    for (int c1 = a.nch - 1; c1 >= 0; c1 -= KU) {
+        float v[KU], d[KU];
+#pragma unroll
+        for (int k = 0; k < KU; ++k) {
+            const int c = c1 - k;
+            v[k] = (ok && c >= 0) ? base[((size_t)c * 2 + 1) * NP + ee] : 0.0f;
+            d[k] = c >= 0 ? exp_e(lam[c]) : 1.0f;
+        }
+#pragma unroll
+        for (int k = 0; k < KU; ++k) {
+            const int c = c1 - k;
+            if (ok && c >= 0) base[((size_t)c * 2 + 1) * NP + ee] = gs;
+            gs = fmaf(d[k], gs, v[k]);
+        }
+    }
+    if (ok && a.dh0) a.dh0[(size_t)bh * NP + ee] = gs;
+}
+
+// ---------------------------------------------------------------------------
+// k_bwd_grad: per chunk and group, heads in turn.  Waves w and w + 4 own the 16
+// steps 16 w .. 16 w + 15 of the chunk for every output (dC, dX, dB rows), each
+// for half of the output columns, so the causal parts balance across row
+// blocks: dC sums over the earlier steps, dX and dB over the later ones.
+//   once per chunk:  S = C B^T (lower block triangle) -> sS
+//   per head:        W2 = (dY X^T) o W -> sW;  M = S o W -> sM
+//                    dC_h = diag(e^{cum}) dY H^T + W2 B
+//                    dX   = diag(e^{Lam - cum}) B G + M^T dY      (stored)
+//                    dB  += diag(e^{Lam - cum}) X G^T + W2^T C
+//                    dl   = rows of C . dC_h - X . dX              (stored)
+//                    dC  += dC_h
+// MFMA operands whose contraction index runs along an LDS row are read four at
+// a time; the others (contraction down a column) one row each.  The next
+// head's X, dY and log-decay load into registers during the products.
+// ---------------------------------------------------------------------------
+template <int NN, int PP>
+__global__ __launch_bounds__(kMma) void k_bwd_grad(BwdArgs a) {
+    constexpr int LB = Ld<NN>::v, LX = Ld<PP>::v;
+    constexpr int NB = NN / 16, PB = PP / 16;
+    constexpr int NBH = NB / 2, PBH = PB / 2;    // column tiles per half
+    static_assert(NB % 2 == 0 && PB % 2 == 0, "column tiles split in halves");
+    __shared__ __attribute__((aligned(16))) float sB[kQ * LB];
+    __shared__ __attribute__((aligned(16))) float sC[kQ * LB];
+    __shared__ __attribute__((aligned(16))) float sX[kQ * LX];
+    __shared__ __attribute__((aligned(16))) float sD[kQ * LX];
+    __shared__ __attribute__((aligned(16))) float sS[kQ * kLQ];
+    __shared__ __attribute__((aligned(16))) float sW[kQ * kLQ];
+    __shared__ __attribute__((aligned(16))) float sM[kQ * kLQ];
+    __shared__ float s_cum[kQ], s_we[kQ], s_ws[kQ], s_dl[2][kQ];
+
+    const int g = blockIdx.x % a.G;
+    const int c = (blockIdx.x / a.G) % a.nch;
+    const int b = blockIdx.x / (a.G * a.nch);
+    const int t0 = c * kQ;
+    const int hpg = a.H / a.G;
+    const int lane = threadIdx.x % 64, wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
+    const int rb = wave & 3, half = wave >> 2;
+    const int li = lane % 16, q = lane / 16;
+    const size_t bc_pitch = (size_t)a.G * NN, x_pitch = (size_t)a.H * PP;
+    const size_t NP = (size_t)NN * PP;
+    const int jrow = 16 * rb + 4 * q;            // first of the four rows of this lane's accumulators
+    const int nb0 = half * NBH, pb0 = half * PBH;
+
+    {
+        RowPref<NN, kMma> r;
+        r.load(a.B + ((size_t)b * a.L * a.G + g) * NN, bc_pitch, t0, a.L);
+        r.store(sB, LB, nullptr);
+        r.load(a.C + ((size_t)b * a.L * a.G + g) * NN, bc_pitch, t0, a.L);
+        r.store(sC, LB, nullptr);
+    }
+    RowPref<PP, kMma> px, pd;
+    float ldv = 0.0f;
+    auto prefetch = [&](int h) {
+        px.load(a.X + ((size_t)b * a.L * a.H + h) * PP, x_pitch, t0, a.L);
+        pd.load(a.dY + ((size_t)b * a.L * a.H + h) * PP, x_pitch, t0, a.L);
+        if (wave == 0) ldv = t0 + lane < a.L ? a.ld[((size_t)b * a.L + t0 + lane) * a.H + h] : 0.0f;
+    };
+    prefetch(g * hpg);
+    __syncthreads();
+    // S = C B^T, tiles (rb, jb <= rb), alternate tiles to the two halves
+    for (int jb = half; jb <= rb; jb += 2) {
+        floatx4 acc = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int kg = 0; kg < NB; ++kg) {
+            const float4 av = *(const float4*)(sC + (16 * rb + li) * LB + 16 * kg + 4 * q);
+            const float4 bv = *(const float4*)(sB + (16 * jb + li) * LB + 16 * kg + 4 * q);
+            acc = mfma4(av.x, bv.x, acc);
+            acc = mfma4(av.y, bv.y, acc);
+            acc = mfma4(av.z, bv.z, acc);
+            acc = mfma4(av.w, bv.w, acc);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sS[(jrow + r) * kLQ + 16 * jb + li] = acc[r];
+    }
+
+    floatx4 dBs[NBH], dCs[NBH];
+#pragma unroll
+    for (int k = 0; k < NBH; ++k) {
+        dBs[k] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+        dCs[k] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+    // the two halves' partial dl of a head's rows, summed and stored by wave 0
+    auto store_dl = [&](int h) {
+        const int t = t0 + lane;
+        if (t < a.L) a.dl[((size_t)b * a.L + t) * a.H + h] = s_dl[0][lane] + s_dl[1][lane];
+    };
+
+    for (int hh = 0; hh < hpg; ++hh) {
+        const int h = g * hpg + hh;
+        __syncthreads();   // A: the previous head's reads of sX, sD, sW, sM, weights done
+        if (wave == 0) {
+            if (hh > 0) store_dl(h - 1);
+            chunk_weights(ldv, s_cum, s_we, s_ws);
+        }
+        px.store(sX, LX, nullptr);
+        pd.store(sD, LX, nullptr);
+        __syncthreads();   // B
+        if (hh + 1 < hpg) prefetch(h + 1);
+
+        // ---- W2 = (dY X^T) o W and M = S o W, tiles (rb, jb <= rb) ----------------
+        float cum_r[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) cum_r[r] = s_cum[jrow + r];
+        for (int jb = half; jb <= rb; jb += 2) {
+            floatx4 acc = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int kg = 0; kg < PB; ++kg) {
+                const float4 av = *(const float4*)(sD + (16 * rb + li) * LX + 16 * kg + 4 * q);
+                const float4 bv = *(const float4*)(sX + (16 * jb + li) * LX + 16 * kg + 4 * q);
+                acc = mfma4(av.x, bv.x, acc);
+                acc = mfma4(av.y, bv.y, acc);
+                acc = mfma4(av.z, bv.z, acc);
+                acc = mfma4(av.w, bv.w, acc);
+            }
+            const int jc = 16 * jb + li;
+            const float cj = s_cum[jc];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = jrow + r;
+                const float w = jc <= i ? exp_e(cum_r[r] - cj) : 0.0f;
+                sW[i * kLQ + jc] = acc[r] * w;
+                sM[i * kLQ + jc] = sS[i * kLQ + jc] * w;
+            }
+        }
+        __syncthreads();   // C
+
+        const float* Hs = a.st + (((size_t)b * a.H + h) * a.nch + c) * 2 * NP;
+        const float* Gs = Hs + NP;
+        float we_r[4], ws_r[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            we_r[r] = s_we[jrow + r];
+            ws_r[r] = s_ws[jrow + r];
+        }
+
+        // ---- dC_h = diag(e^{cum}) dY H^T + W2 B ------------------------------------
+        floatx4 dCh[NBH];
+#pragma unroll
+        for (int k = 0; k < NBH; ++k) {
+            const int nb = nb0 + k;
+            floatx4 acc = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int kg = 0; kg < PB; ++kg) {
+                const float4 av = *(const float4*)(sD + (16 * rb + li) * LX + 16 * kg + 4 * q);
+                const float4 bv = *(const float4*)(Hs + (size_t)(16 * nb + li) * PP + 16 * kg + 4 * q);
+                acc = mfma4(av.x, bv.x, acc);
+                acc = mfma4(av.y, bv.y, acc);
+                acc = mfma4(av.z, bv.z, acc);
+                acc = mfma4(av.w, bv.w, acc);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[r] *= ws_r[r];
+            dCh[k] = acc;
+        }
+        for (int kg = 0; kg <= rb; ++kg) {
+            const float4 av = *(const float4*)(sW + (16 * rb + li) * kLQ + 16 * kg + 4 * q);
+            const float avs[4] = {av.x, av.y, av.z, av.w};
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const int i = 16 * kg + 4 * q + s;
+#pragma unroll
+                for (int k = 0; k < NBH; ++k) dCh[k] = mfma4(avs[s], sB[i * LB + 16 * (nb0 + k) + li], dCh[k]);
+            }
+        }
+
+        // ---- dX = diag(e^{Lam - cum}) B G + M^T dY ---------------------------------
+        floatx4 dXa[PBH];
+#pragma unroll
+        for (int k = 0; k < PBH; ++k) {
+            const int pb = pb0 + k;
+            floatx4 acc = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int kg = 0; kg < NB; ++kg) {
+                // G is read down its columns: four rows of 16 consecutive columns
+                // per instruction
+                const float4 av = *(const float4*)(sB + (16 * rb + li) * LB + 16 * kg + 4 * q);
+                const float* gc = Gs + (size_t)(16 * kg + 4 * q) * PP + 16 * pb + li;
+                acc = mfma4(av.x, gc[0], acc);
+                acc = mfma4(av.y, gc[PP], acc);
+                acc = mfma4(av.z, gc[2 * PP], acc);
+                acc = mfma4(av.w, gc[3 * PP], acc);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[r] *= we_r[r];
+            dXa[k] = acc;
+        }
+        for (int kg = rb; kg < 4; ++kg) {
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const int i = 16 * kg + 4 * q + s;
+                const float mv = sM[i * kLQ + 16 * rb + li];
+#pragma unroll
+                for (int k = 0; k < PBH; ++k) dXa[k] = mfma4(mv, sD[i * LX + 16 * (pb0 + k) + li], dXa[k]);
+            }
+        }
+
+        // ---- dB += diag(e^{Lam - cum}) X G^T + W2^T C --------------------------------
+        {
+            floatx4 dBh[NBH];
+#pragma unroll
+            for (int k = 0; k < NBH; ++k) {
+                const int nb = nb0 + k;
+                floatx4 acc = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int kg = 0; kg < PB; ++kg) {
+                    const float4 av = *(const float4*)(sX + (16 * rb + li) * LX + 16 * kg + 4 * q);
+                    const float4 bv = *(const float4*)(Gs + (size_t)(16 * nb + li) * PP + 16 * kg + 4 * q);
+                    acc = mfma4(av.x, bv.x, acc);
+                    acc = mfma4(av.y, bv.y, acc);
+                    acc = mfma4(av.z, bv.z, acc);
+                    acc = mfma4(av.w, bv.w, acc);
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[r] *= we_r[r];
+                dBh[k] = acc;
+            }
+            for (int kg = rb; kg < 4; ++kg) {
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    const int i = 16 * kg + 4 * q + s;
+                    const float wv = sW[i * kLQ + 16 * rb + li];
+#pragma unroll
+                    for (int k = 0; k < NBH; ++k) dBh[k] = mfma4(wv, sC[i * LB + 16 * (nb0 + k) + li], dBh[k]);
+                }
+            }
+#pragma unroll
+            for (int k = 0; k < NBH; ++k) dBs[k] += dBh[k];
+        }
+
+        // ---- partial dl = C . dC_h - X . dX over this half's columns; store dX -------
+        float part[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int k = 0; k < NBH; ++k)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                part[r] = fmaf(sC[(jrow + r) * LB + 16 * (nb0 + k) + li], dCh[k][r], part[r]);
+#pragma unroll
+        for (int k = 0; k < PBH; ++k)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                part[r] = fmaf(-sX[(jrow + r) * LX + 16 * (pb0 + k) + li], dXa[k][r], part[r]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+#pragma unroll
+            for (int off = 8; off >= 1; off >>= 1) part[r] += __shfl_xor(part[r], off, 16);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int t = t0 + jrow + r;
+            if (li == 0) s_dl[half][jrow + r] = part[r];
+            if (t < a.L) {
+                float* dxr = a.dX + (((size_t)b * a.L + t) * a.H + h) * PP;
+#pragma unroll
+                for (int k = 0; k < PBH; ++k) dxr[16 * (pb0 + k) + li] = dXa[k][r];
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < NBH; ++k) dCs[k] += dCh[k];
+    }
+    __syncthreads();
+    if (wave == 0 && hpg > 0) store_dl(g * hpg + hpg - 1);
+
+    // ---- the group's dB, dC, this half's columns --------------------------------------
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int t = t0 + jrow + r;
+        if (t >= a.L) continue;
+        float* dbr = a.dB + (((size_t)b * a.L + t) * a.G + g) * NN;
+        float* dcr = a.dC + (((size_t)b * a.L + t) * a.G + g) * NN;
+#pragma unroll
+        for (int k = 0; k < NBH; ++k) {
+            dbr[16 * (nb0 + k) + li] = dBs[k][r];
+            dcr[16 * (nb0 + k) + li] = dCs[k][r];
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// k_bwd_ld: dlogdecay_t = sum_{tau >= t} dl_tau + <dh_out, h_out>, one wave per
+// (batch, head), 64 steps at a time from the end (lane l takes step 63 - l of
+// the block, so a prefix sum over lanes is a suffix sum over steps).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(64) void k_bwd_ld(BwdArgs a) {
+    const int bh = blockIdx.x;
+    const int b = bh / a.H, h = bh % a.H;
+    const int lane = threadIdx.x;
+    float run = 0.0f;
+    for (int k = lane; k < a.nfin; k += 64) run += a.fin[(size_t)bh * a.nfin + k];
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) run += __shfl_xor(run, off, 64);
+    const int nblk = (a.L + 63) / 64;
+    for (int blk = nblk - 1; blk >= 0; --blk) {
+        const int t = 64 * blk + 63 - lane;
+        float v = t < a.L ? a.dl[((size_t)b * a.L + t) * a.H + h] : 0.0f;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const float u = __shfl_up(v, d, 64);
+            if (lane >= d) v += u;
+        }
+        if (t < a.L) a.dld[((size_t)b * a.L + t) * a.H + h] = v + run;
+        run += __shfl(v, 63, 64);
+    }
+}
+
+struct BwdPlan {
+    int64_t nch, nfin;
+    size_t off_lam, off_dl, off_fin, bytes;
+};
+
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+BwdPlan bwd_plan(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N) {
+    BwdPlan p{};
+    p.nch = (L + kQ - 1) / kQ;
+    p.nfin = (N * P + kBwdThreads - 1) / kBwdThreads;
+    size_t off = align256((size_t)(batch * H * p.nch) * 2 * (size_t)(N * P) * 4);
+    p.off_lam = off;
+    off += align256((size_t)(batch * H * p.nch) * 4);
+    p.off_dl = off;
+    off += align256((size_t)(batch * L * H) * 4);
+    p.off_fin = off;
+    off += align256((size_t)(batch * H * p.nfin) * 4);
+    p.bytes = off;
+    return p;
+}
+
+bool bwd_dims_ok(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t G, int64_t N) {
+    if (batch < 0 || L < 0 || H < 1 || G < 1 || H % G) return false;
+    if (N != 64 && N != 128) return false;
+    if (P != 32 && P != 64) return false;
+    if (batch > INT32_MAX || L > INT32_MAX || H > 65535) return false;
+    if (batch * H > 65535) return false;                     // grid y of the pass
+    if (batch * ((L + kQ - 1) / kQ) * G > INT32_MAX) return false;
+    return true;
+}
+
+template <int NN, int PP>
+mb_status bwd_launch(const BwdArgs& a, int64_t batch, hipStream_t stream) {
+    const unsigned nwg = (unsigned)(batch * a.nch * a.G);
+    hipLaunchKernelGGL((k_bwd_local<NN, PP>), dim3(nwg), dim3(kMma), 0, stream, a);
+    hipLaunchKernelGGL(k_bwd_pass, dim3((unsigned)a.nfin, (unsigned)(batch * a.H)), dim3(kBwdThreads), 0,
+                       stream, a);
+    hipLaunchKernelGGL((k_bwd_grad<NN, PP>), dim3(nwg), dim3(kMma), 0, stream, a);
+    hipLaunchKernelGGL(k_bwd_ld, dim3((unsigned)(batch * a.H)), dim3(64), 0, stream, a);
+    return check_launch();
+}
+
+}  // namespace
+
+size_t ssd_bwd_workspace(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t G, int64_t N) {
+    if (!bwd_dims_ok(batch, L, H, P, G, N) || batch == 0 || L == 0) return 0;
+    return bwd_plan(batch, L, H, P, N).bytes;
+}
+
+}  // namespace mb
+
+using namespace mb;
+
+extern "C" mb_status mb_ssd_chunked_bwd(const float* X, const float* logdecay, const float* B,
+                                        const float* C, const float* h0, const float* dY,
+                                        const float* dh_out, float* dX, float* dlogdecay, float* dB,
+                                        float* dC, float* dh0, int64_t batch, int64_t L, int64_t H,
+                                        int64_t P, int64_t G, int64_t N, mb_dtype dtype, void* ws,
+                                        size_t ws_bytes, hipStream_t stream)
+{
+    if (dtype != MB_F32) return MB_ERR_DTYPE;
+    if (!bwd_dims_ok(batch, L, H, P, G, N)) return MB_ERR_SHAPE;
+    const size_t n_x = (size_t)(batch * L * H * P), n_b = (size_t)(batch * L * G * N);
+    const size_t n_l = (size_t)(batch * L * H), n_h = (size_t)(batch * H * N * P);
+    if (n_x && (!X || !dY || !dX || !logdecay || !dlogdecay)) return MB_ERR_NULL;
+    if (n_b && (!B || !C || !dB || !dC)) return MB_ERR_NULL;
+    if ((((uintptr_t)X | (uintptr_t)B | (uintptr_t)C | (uintptr_t)dY | (uintptr_t)dX | (uintptr_t)dB |
+          (uintptr_t)dC) & 15))
+        return MB_ERR_ALIGN;
+    const Span ins[] = {{X, n_x * 4}, {logdecay, n_l * 4}, {B, n_b * 4}, {C, n_b * 4},
+                        {h0, h0 ? n_h * 4 : 0}, {dY, n_x * 4}, {dh_out, dh_out ? n_h * 4 : 0}};
+    const Span outs[] = {{dX, n_x * 4}, {dlogdecay, n_l * 4}, {dB, n_b * 4}, {dC, n_b * 4},
+                         {dh0, dh0 ? n_h * 4 : 0}};
+    for (int i = 0; i < 5; ++i) {
+        if (overlaps_any(outs[i].p, outs[i].bytes, ins, 7)) return MB_ERR_ALIAS;
+        for (int j = i + 1; j < 5; ++j)
+            if (overlaps(outs[i].p, outs[i].bytes, outs[j].p, outs[j].bytes)) return MB_ERR_ALIAS;
+    }
+    if (batch == 0) return MB_OK;
+    if (L == 0) return dh0 ? copy_state(dh_out, dh0, (int64_t)n_h, stream) : MB_OK;   // dh0 = dh_out
+    const BwdPlan pl = bwd_plan(batch, L, H, P, N);
+    if (!ws || ws_bytes < pl.bytes || ((uintptr_t)ws & 255)) return MB_ERR_WORKSPACE;
+    if (overlaps_any(ws, pl.bytes, ins, 7) || overlaps_any(ws, pl.bytes, outs, 5)) return MB_ERR_ALIAS;
+    char* w = (char*)ws;
+    BwdArgs a{};
+    a.X = X; a.ld = logdecay; a.B = B; a.C = C; a.h0 = h0; a.dY = dY; a.dh_out = dh_out;
+    a.dX = dX; a.dld = dlogdecay; a.dB = dB; a.dC = dC; a.dh0 = dh0;
+    a.st = (float*)w;
+    a.lam = (float*)(w + pl.off_lam);
+    a.dl = (float*)(w + pl.off_dl);
+    a.fin = (float*)(w + pl.off_fin);
+    a.L = (int)L; a.H = (int)H; a.G = (int)G; a.N = (int)N; a.P = (int)P;
+    a.nch = (int)pl.nch; a.nfin = (int)pl.nfin;
+    if (N == 128)
+        return P == 64 ? bwd_launch<128, 64>(a, batch, stream) : bwd_launch<128, 32>(a, batch, stream);
+    return P == 64 ? bwd_launch<64, 64>(a, batch, stream) : bwd_launch<64, 32>(a, batch, stream);
+}

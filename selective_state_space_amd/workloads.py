@@ -116,6 +116,16 @@ def ssd_block(seed=103, batch=4, L=4096, H=24, P=64, N=128, G=1):
     return ssd_inputs(np.random.default_rng(seed), batch, L, H, P, N, G)
 
 
+def ssd_bwd_block(seed=111, batch=4, L=4096, H=24, P=64, N=128, G=1):
+    """The Mamba-2 block inputs (seed 103) with the incoming gradients of the
+    backward: dY ~ N(0,1) like X and dh_out ~ N(0,1) like the state."""
+    d = ssd_block(batch=batch, L=L, H=H, P=P, N=N, G=G)
+    rng = np.random.default_rng(seed)
+    d["dY"] = rng.standard_normal((batch, L, H, P))
+    d["dh_out"] = rng.standard_normal((batch, H, N, P))
+    return d
+
+
 def _trap_coeffs(rng, batch, L, H, N):
     """dt = softplus(N(-3,1)); A_h = -U(1,16); alpha = exp(dt*A_h);
     lambda = sigmoid(N(0,1)); gamma = lambda*dt; beta = (1-lambda)*dt*alpha;

@@ -34,7 +34,7 @@ def declared_functions():
 def test_exports_every_declared_function(lib):
     names = declared_functions()
     assert {"mb_selective_scan", "mb_ssm_step", "mb_ssd_chunked", "mb_trap_ssd", "mb_mimo_ssd",
-            "mb_ssd_step", "mb_selective_scan_fused", "mb_workspace_size", "mb_status_str", "mb_last_hip_error", "mb_version"} <= set(names)
+            "mb_ssd_step", "mb_selective_scan_fused", "mb_ssd_chunked_bwd", "mb_workspace_size", "mb_status_str", "mb_last_hip_error", "mb_version"} <= set(names)
     for n in names:
         assert hasattr(lib, n), "libmb.so does not export " + n
 
@@ -161,6 +161,36 @@ def test_ssd_validation(lib):
     assert ssd(lib, Y=FAKE + 64) == E_ALIAS
     assert ssd(lib, Y=FAKE + (1 << 27) + 8) == E_ALIGN
     assert ssd(lib, batch=0) == OK
+
+
+def ssd_bwd(lib, X=FAKE, dY=FAKE + (1 << 24), dX=FAKE + (1 << 25), dB=FAKE + (1 << 26), dh0=FAKE + (1 << 27),
+            ws=FAKE + (1 << 28), ws_bytes=1 << 30, H=4, P_=64, G=1, N=128, L=100, batch=2, dtype=F32):
+    q = lambda v: P(v) if v else None
+    return lib.mb_ssd_chunked_bwd(q(X), P(FAKE + (1 << 22)), P(FAKE + (1 << 23)), P(FAKE + (1 << 23) + (1 << 21)),
+                                  None, q(dY), None, q(dX), P(FAKE + (1 << 25) + (1 << 21)), q(dB),
+                                  P(FAKE + (1 << 26) + (1 << 21)), q(dh0), batch, L, H, P_, G, N, dtype, q(ws),
+                                  ws_bytes, None)
+
+
+def test_ssd_bwd_validation(lib):
+    assert ssd_bwd(lib, dtype=BF16) == E_DTYPE
+    assert ssd_bwd(lib, N=32) == E_SHAPE
+    assert ssd_bwd(lib, P_=48) == E_SHAPE
+    assert ssd_bwd(lib, G=3) == E_SHAPE
+    assert ssd_bwd(lib, X=0) == E_NULL
+    assert ssd_bwd(lib, dB=0) == E_NULL
+    assert ssd_bwd(lib, dX=FAKE + (1 << 25) + 4) == E_ALIGN
+    assert ssd_bwd(lib, dX=FAKE + 256) == E_ALIAS          # dX over X
+    assert ssd_bwd(lib, dB=FAKE + (1 << 25) + 1024) == E_ALIAS   # dB over dX
+    assert ssd_bwd(lib, dh0=FAKE + (1 << 28)) == E_ALIAS   # dh0 over the workspace
+    assert ssd_bwd(lib, ws=0) == E_WS
+    assert ssd_bwd(lib, ws_bytes=4096) == E_WS
+    assert ssd_bwd(lib, ws=FAKE + (1 << 28) + 16) == E_WS
+    assert ssd_bwd(lib, batch=0) == OK
+    need = mb.mb_workspace_size(mb.MB_OP_SSD_CHUNKED_BWD, 2, 100, 4, 64, 1, 128)
+    assert need >= 2 * 4 * 2 * 2 * 128 * 64 * 4
+    assert mb.mb_workspace_size(mb.MB_OP_SSD_CHUNKED_BWD, 2, 100, 4, 48, 1, 128) == 0
+    assert mb.mb_workspace_size(mb.MB_OP_SSD_CHUNKED_BWD, 2, 0, 4, 64, 1, 128) == 0
 
 
 def test_trap_and_mimo_validation(lib):
