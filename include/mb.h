@@ -265,8 +265,8 @@ mb_status mb_ssd_step(const void* X, const float* logdecay, const void* B,
  * mb_workspace_size(MB_OP_SSD_CHUNKED_BWD, ...) bytes, 256-byte aligned (two
  * N x P states per (batch, head, 64-step chunk), plus small buffers).
  * Supported: dtype MB_F32 (MB_ERR_DTYPE otherwise); N in {64, 128}, P in
- * {32, 64} (MB_ERR_SHAPE otherwise); X, B, C, dY, dX, dB, dC 16-byte aligned
- * (MB_ERR_ALIGN).  No output may overlap an input, another output or the
+ * {32, 64} (MB_ERR_SHAPE otherwise); X, B, C, dY, dX, dB, dC, h0, dh_out, dh0
+ * 16-byte aligned (MB_ERR_ALIGN).  No output may overlap an input, another output or the
  * workspace (MB_ERR_ALIAS).
  */
 mb_status mb_ssd_chunked_bwd(const float* X, const float* logdecay, const float* B,

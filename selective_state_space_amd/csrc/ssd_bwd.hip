@@ -26,9 +26,11 @@
 //   k_bwd_pass   one thread per (batch, head, state element): the two chunk
 //                recurrences, elementwise, in place (U_c -> H_c, V_c -> G_c), dh0,
 //                and the partial sums of <dh_out, h_out>.
-//   k_bwd_grad   (batch, chunk, group), heads in turn: dX, the per-step dl, and
-//                dB, dC accumulated over the group's heads, on fp32 MFMA.
-//   k_bwd_ld     one wave per (batch, head): the suffix sums of dl.
+//   k_bwd_grad   (batch, chunk, group), heads in turn: dX, the suffix sums of
+//                dl inside the chunk and the chunk's total, and dB, dC
+//                accumulated over the group's heads, on fp32 MFMA.
+//   k_bwd_ld     one wave per (batch, head, chunk): adds the later chunks' totals
+//                and <dh_out, h_out>.
 #include "mb_internal.h"
 
 namespace mb {
@@ -61,7 +63,7 @@ struct BwdArgs {
     float* dh0;             // (batch, H, N, P) or NULL
     float* st;              // workspace: per (b, h, c) two N x P slots (H_c, G_c)
     float* lam;             // workspace: per (b, h, c) total log-decay of the chunk
-    float* dl;              // workspace: (batch, L, H) per-step dl
+    float* tot;             // workspace: per (b, h, c) the sum of dl over the chunk
     float* fin;             // workspace: per (b, h) partial sums of <dh_out, h_out>
     int L, H, G, N, P, nch, nfin;
 };
@@ -231,40 +233,45 @@ __global__ __launch_bounds__(kMma) void k_bwd_local(BwdArgs a) {
 
 // ---------------------------------------------------------------------------
 // k_bwd_pass: the chunk recurrences, elementwise.  Thread e of (b, h) holds
-// state element e = n P + p.  Forward: slot 0 of chunk c becomes H_c (read
-// U_c first); reverse: slot 1 becomes G_c.  Eight chunks are loaded ahead of
-// their use.
+// the four state elements 4 e .. 4 e + 3 (n P + p order).  Forward: slot 0 of
+// chunk c becomes H_c (read U_c first); reverse: slot 1 becomes G_c.  Eight
+// chunks are loaded ahead of their use.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kBwdThreads) void k_bwd_pass(BwdArgs a) {
     const int bh = blockIdx.y;
     const size_t NP = (size_t)a.N * a.P;
     const int e = blockIdx.x * kBwdThreads + threadIdx.x;
-    const bool ok = e < (int)NP;
-    const int ee = ok ? e : 0;
+    const bool ok = 4 * (size_t)e < NP;
+    const size_t ee = ok ? 4 * (size_t)e : 0;
     float* base = a.st + (size_t)bh * a.nch * 2 * NP;
     const float* lam = a.lam + (size_t)bh * a.nch;
     constexpr int KU = 8;
+    const float4 z4 = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
 
-    float hs = (ok && a.h0) ? a.h0[(size_t)bh * NP + ee] : 0.0f;
+    float4 hs = (ok && a.h0) ? *(const float4*)(a.h0 + (size_t)bh * NP + ee) : z4;
     for (int c0 = 0; c0 < a.nch; c0 += KU) {
-        float u[KU], d[KU];
+        float4 u[KU];
+        float d[KU];
 #pragma unroll
         for (int k = 0; k < KU; ++k) {
             const int c = c0 + k;
-            u[k] = (ok && c < a.nch) ? base[(size_t)c * 2 * NP + ee] : 0.0f;
+            u[k] = (ok && c < a.nch) ? *(const float4*)(base + (size_t)c * 2 * NP + ee) : z4;
             d[k] = c < a.nch ? exp_e(lam[c]) : 1.0f;
         }
 #pragma unroll
         for (int k = 0; k < KU; ++k) {
             const int c = c0 + k;
-            if (ok && c < a.nch) base[(size_t)c * 2 * NP + ee] = hs;
-            hs = fmaf(d[k], hs, u[k]);
+            if (ok && c < a.nch) *(float4*)(base + (size_t)c * 2 * NP + ee) = hs;
+            hs.x = fmaf(d[k], hs.x, u[k].x);
+            hs.y = fmaf(d[k], hs.y, u[k].y);
+            hs.z = fmaf(d[k], hs.z, u[k].z);
+            hs.w = fmaf(d[k], hs.w, u[k].w);
         }
     }
-    const float dh = (ok && a.dh_out) ? a.dh_out[(size_t)bh * NP + ee] : 0.0f;
+    const float4 dh = (ok && a.dh_out) ? *(const float4*)(a.dh_out + (size_t)bh * NP + ee) : z4;
     // partial sum of <dh_out, h_out> over this block
     {
-        float v = dh * hs;
+        float v = (dh.x * hs.x + dh.y * hs.y) + (dh.z * hs.z + dh.w * hs.w);
 #pragma unroll
         for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
         __shared__ float s_part[kBwdThreads / 64];
@@ -273,23 +280,27 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_pass(BwdArgs a) {
         if (threadIdx.x == 0)
             a.fin[(size_t)bh * a.nfin + blockIdx.x] = (s_part[0] + s_part[1]) + (s_part[2] + s_part[3]);
     }
-    float gs = dh;
+    float4 gs = dh;
     for (int c1 = a.nch - 1; c1 >= 0; c1 -= KU) {
-        float v[KU], d[KU];
+        float4 v[KU];
+        float d[KU];
 #pragma unroll
         for (int k = 0; k < KU; ++k) {
             const int c = c1 - k;
-            v[k] = (ok && c >= 0) ? base[((size_t)c * 2 + 1) * NP + ee] : 0.0f;
+            v[k] = (ok && c >= 0) ? *(const float4*)(base + ((size_t)c * 2 + 1) * NP + ee) : z4;
             d[k] = c >= 0 ? exp_e(lam[c]) : 1.0f;
         }
 #pragma unroll
         for (int k = 0; k < KU; ++k) {
             const int c = c1 - k;
-            if (ok && c >= 0) base[((size_t)c * 2 + 1) * NP + ee] = gs;
-            gs = fmaf(d[k], gs, v[k]);
+            if (ok && c >= 0) *(float4*)(base + ((size_t)c * 2 + 1) * NP + ee) = gs;
+            gs.x = fmaf(d[k], gs.x, v[k].x);
+            gs.y = fmaf(d[k], gs.y, v[k].y);
+            gs.z = fmaf(d[k], gs.z, v[k].z);
+            gs.w = fmaf(d[k], gs.w, v[k].w);
         }
     }
-    if (ok && a.dh0) a.dh0[(size_t)bh * NP + ee] = gs;
+    if (ok && a.dh0) *(float4*)(a.dh0 + (size_t)bh * NP + ee) = gs;
 }
 
 // ---------------------------------------------------------------------------
@@ -374,10 +385,20 @@ __global__ __launch_bounds__(kMma) void k_bwd_grad(BwdArgs a) {
         dBs[k] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
         dCs[k] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
     }
-    // the two halves' partial dl of a head's rows, summed and stored by wave 0
+    // by wave 0: the two halves' partial dl of a head's rows summed, the suffix
+    // sums inside the chunk stored as dlogdecay (k_bwd_ld adds the rest) and the
+    // chunk's total kept (lane l takes row 63 - l: a prefix over lanes is a
+    // suffix over steps)
     auto store_dl = [&](int h) {
-        const int t = t0 + lane;
-        if (t < a.L) a.dl[((size_t)b * a.L + t) * a.H + h] = s_dl[0][lane] + s_dl[1][lane];
+        const int j = 63 - lane, t = t0 + j;
+        float v = t < a.L ? s_dl[0][j] + s_dl[1][j] : 0.0f;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const float u = __shfl_up(v, d, 64);
+            if (lane >= d) v += u;
+        }
+        if (t < a.L) a.dld[((size_t)b * a.L + t) * a.H + h] = v;
+        if (lane == 63) a.tot[((size_t)b * a.H + h) * a.nch + c] = v;
     };
 
     for (int hh = 0; hh < hpg; ++hh) {
@@ -571,35 +592,26 @@ __global__ __launch_bounds__(kMma) void k_bwd_grad(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// k_bwd_ld: dlogdecay_t = sum_{tau >= t} dl_tau + <dh_out, h_out>, one wave per
-// (batch, head), 64 steps at a time from the end (lane l takes step 63 - l of
-// the block, so a prefix sum over lanes is a suffix sum over steps).
+// k_bwd_ld: one wave per (batch, head, chunk) adds to the chunk's in-chunk
+// suffix sums the totals of every later chunk and <dh_out, h_out>.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(64) void k_bwd_ld(BwdArgs a) {
-    const int bh = blockIdx.x;
+    const int c = blockIdx.x % a.nch;
+    const int bh = blockIdx.x / a.nch;
     const int b = bh / a.H, h = bh % a.H;
     const int lane = threadIdx.x;
-    float run = 0.0f;
-    for (int k = lane; k < a.nfin; k += 64) run += a.fin[(size_t)bh * a.nfin + k];
+    float off = 0.0f;
+    for (int k = lane; k < a.nfin; k += 64) off += a.fin[(size_t)bh * a.nfin + k];
+    for (int k = c + 1 + lane; k < a.nch; k += 64) off += a.tot[(size_t)bh * a.nch + k];
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) run += __shfl_xor(run, off, 64);
-    const int nblk = (a.L + 63) / 64;
-    for (int blk = nblk - 1; blk >= 0; --blk) {
-        const int t = 64 * blk + 63 - lane;
-        float v = t < a.L ? a.dl[((size_t)b * a.L + t) * a.H + h] : 0.0f;
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-            const float u = __shfl_up(v, d, 64);
-            if (lane >= d) v += u;
-        }
-        if (t < a.L) a.dld[((size_t)b * a.L + t) * a.H + h] = v + run;
-        run += __shfl(v, 63, 64);
-    }
+    for (int d = 32; d >= 1; d >>= 1) off += __shfl_xor(off, d, 64);
+    const int t = c * kQ + lane;
+    if (t < a.L) a.dld[((size_t)b * a.L + t) * a.H + h] += off;
 }
 
 struct BwdPlan {
     int64_t nch, nfin;
-    size_t off_lam, off_dl, off_fin, bytes;
+    size_t off_lam, off_tot, off_fin, bytes;
 };
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -607,12 +619,12 @@ size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 BwdPlan bwd_plan(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N) {
     BwdPlan p{};
     p.nch = (L + kQ - 1) / kQ;
-    p.nfin = (N * P + kBwdThreads - 1) / kBwdThreads;
+    p.nfin = (N * P / 4 + kBwdThreads - 1) / kBwdThreads;   // blocks of k_bwd_pass per (b, h)
     size_t off = align256((size_t)(batch * H * p.nch) * 2 * (size_t)(N * P) * 4);
     p.off_lam = off;
     off += align256((size_t)(batch * H * p.nch) * 4);
-    p.off_dl = off;
-    off += align256((size_t)(batch * L * H) * 4);
+    p.off_tot = off;
+    off += align256((size_t)(batch * H * p.nch) * 4);
     p.off_fin = off;
     off += align256((size_t)(batch * H * p.nfin) * 4);
     p.bytes = off;
@@ -626,6 +638,7 @@ bool bwd_dims_ok(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t G, int6
     if (batch > INT32_MAX || L > INT32_MAX || H > 65535) return false;
     if (batch * H > 65535) return false;                     // grid y of the pass
     if (batch * ((L + kQ - 1) / kQ) * G > INT32_MAX) return false;
+    if (batch * H * ((L + kQ - 1) / kQ) > INT32_MAX) return false;   // grid of k_bwd_ld
     return true;
 }
 
@@ -636,7 +649,7 @@ mb_status bwd_launch(const BwdArgs& a, int64_t batch, hipStream_t stream) {
     hipLaunchKernelGGL(k_bwd_pass, dim3((unsigned)a.nfin, (unsigned)(batch * a.H)), dim3(kBwdThreads), 0,
                        stream, a);
     hipLaunchKernelGGL((k_bwd_grad<NN, PP>), dim3(nwg), dim3(kMma), 0, stream, a);
-    hipLaunchKernelGGL(k_bwd_ld, dim3((unsigned)(batch * a.H)), dim3(64), 0, stream, a);
+    hipLaunchKernelGGL(k_bwd_ld, dim3((unsigned)(batch * a.H * a.nch)), dim3(64), 0, stream, a);
     return check_launch();
 }
 
@@ -665,7 +678,7 @@ extern "C" mb_status mb_ssd_chunked_bwd(const float* X, const float* logdecay, c
     if (n_x && (!X || !dY || !dX || !logdecay || !dlogdecay)) return MB_ERR_NULL;
     if (n_b && (!B || !C || !dB || !dC)) return MB_ERR_NULL;
     if ((((uintptr_t)X | (uintptr_t)B | (uintptr_t)C | (uintptr_t)dY | (uintptr_t)dX | (uintptr_t)dB |
-          (uintptr_t)dC) & 15))
+          (uintptr_t)dC | (uintptr_t)h0 | (uintptr_t)dh_out | (uintptr_t)dh0) & 15))
         return MB_ERR_ALIGN;
     const Span ins[] = {{X, n_x * 4}, {logdecay, n_l * 4}, {B, n_b * 4}, {C, n_b * 4},
                         {h0, h0 ? n_h * 4 : 0}, {dY, n_x * 4}, {dh_out, dh_out ? n_h * 4 : 0}};
@@ -687,7 +700,7 @@ extern "C" mb_status mb_ssd_chunked_bwd(const float* X, const float* logdecay, c
     a.dX = dX; a.dld = dlogdecay; a.dB = dB; a.dC = dC; a.dh0 = dh0;
     a.st = (float*)w;
     a.lam = (float*)(w + pl.off_lam);
-    a.dl = (float*)(w + pl.off_dl);
+    a.tot = (float*)(w + pl.off_tot);
     a.fin = (float*)(w + pl.off_fin);
     a.L = (int)L; a.H = (int)H; a.G = (int)G; a.N = (int)N; a.P = (int)P;
     a.nch = (int)pl.nch; a.nfin = (int)pl.nfin;

@@ -180,6 +180,7 @@ def test_ssd_bwd_validation(lib):
     assert ssd_bwd(lib, X=0) == E_NULL
     assert ssd_bwd(lib, dB=0) == E_NULL
     assert ssd_bwd(lib, dX=FAKE + (1 << 25) + 4) == E_ALIGN
+    assert ssd_bwd(lib, dh0=FAKE + (1 << 27) + 8) == E_ALIGN
     assert ssd_bwd(lib, dX=FAKE + 256) == E_ALIAS          # dX over X
     assert ssd_bwd(lib, dB=FAKE + (1 << 25) + 1024) == E_ALIAS   # dB over dX
     assert ssd_bwd(lib, dh0=FAKE + (1 << 28)) == E_ALIAS   # dh0 over the workspace
