@@ -63,6 +63,7 @@ def _load():
         lib = ctypes.CDLL(_LIB_PATH)
         lib.oracle_m1_scan.argtypes = [_D] * 9 + [_I] * 4
         lib.oracle_m1_step.argtypes = [_D] * 9 + [_I] * 3
+        lib.oracle_m1_scan_bwd.argtypes = [_D] * 16 + [_I] * 4
         lib.oracle_ssd.argtypes = [_D] * 7 + [_I] * 6
         lib.oracle_ssd_bwd.argtypes = [_D] * 12 + [_I] * 6
         lib.oracle_trap.argtypes = [_D] * 12 + [_I] * 6
@@ -126,6 +127,32 @@ def m1_scan(x, dt, A, B, C, D=None, h0=None):
     _load().oracle_m1_scan(_p(x), _p(dt), _p(A), _p(B), _p(C), _p(D), _p(h0),
                            _p(y), _p(h), b, L, Dm, N)
     return y, h
+
+
+def m1_scan_bwd(x, dt, A, B, C, dy, D=None, h0=None, dh_out=None):
+    """Backward of the Mamba-1 scan: the gradients of sum dy . y + sum dh_out .
+    h_out with respect to x, dt, A, B, C, D and h0.  Shapes as m1_scan(); dy
+    like x, dh_out like h0.  Returns (dx, ddt, dA, dB, dC, dD, dh0)."""
+    x = _f64(x)
+    b, L, Dm = x.shape
+    A = _f64(A)
+    N = A.shape[1]
+    dt = _chk(dt, (b, L, Dm), "dt")
+    A = _chk(A, (Dm, N), "A")
+    B = _chk(B, (b, L, N), "B")
+    C = _chk(C, (b, L, N), "C")
+    dy = _chk(dy, (b, L, Dm), "dy")
+    D = _opt(D, (Dm,))
+    h0 = _opt(h0, (b, Dm, N))
+    dh_out = _opt(dh_out, (b, Dm, N))
+    dx, ddt = np.empty((b, L, Dm)), np.empty((b, L, Dm))
+    dA = np.empty((Dm, N))
+    dB, dC = np.empty((b, L, N)), np.empty((b, L, N))
+    dD = np.empty(Dm)
+    dh0 = np.empty((b, Dm, N))
+    _load().oracle_m1_scan_bwd(_p(x), _p(dt), _p(A), _p(B), _p(C), _p(D), _p(h0), _p(dy), _p(dh_out), _p(dx),
+                               _p(ddt), _p(dA), _p(dB), _p(dC), _p(dD), _p(dh0), b, L, Dm, N)
+    return dx, ddt, dA, dB, dC, dD, dh0
 
 
 def m1_step(x, dt, A, B, C, D, h):

@@ -92,6 +92,90 @@ void oracle_m1_scan(const double *x, const double *dt, const double *A,
 }
 
 /*
+ * Backward (vector-Jacobian product) of the Mamba-1 scan above: back-propagation
+ * through time of its recurrence (TorchMamba README, Math notes M1; the mamba-rs
+ * page lists training by back-propagation through time).  Given dy (b, L, D)
+ * and dh_out (b, D, N) or NULL, it returns the gradients of
+ * sum dy . y + sum dh_out . h_out with respect to x, dt, A, B, C, Dskip and h0.
+ * With a_t = exp(dt_t A) and G the adjoint of the state of one (b, c), walking
+ * t = L-1 .. 0 from G = dh_out:
+ *     G     += C_t dy_t                            (now d/dh_t)
+ *     dC_t  += h_t dy_t,     dB_t += G dt_t x_t    (summed over channels)
+ *     dx_t   = sum_n G dt_t B_t + Dskip dy_t
+ *     ddt_t  = sum_n G (B_t x_t + A a_t h_{t-1})
+ *     dA    += G dt_t a_t h_{t-1}                   (summed over batch and time)
+ *     G      = a_t G                               (now d/dh_{t-1})
+ * dDskip = sum over batch and time of dy x; dh0 = G at the end.  The forward
+ * states are kept for every step.  One thread per batch row; dA and dDskip are
+ * summed over the rows in order at the end.
+ */
+void oracle_m1_scan_bwd(const double *x, const double *dt, const double *A,
+                        const double *B, const double *C, const double *Dskip,
+                        const double *h0, const double *dy, const double *dh_out,
+                        double *dx, double *ddt, double *dA, double *dB, double *dC,
+                        double *dD, double *dh0, int64_t batch, int64_t L, int64_t D,
+                        int64_t N)
+{
+    double *dA_b = (double *)calloc((size_t)(batch * D * N > 0 ? batch * D * N : 1), sizeof(double));
+    double *dD_b = (double *)calloc((size_t)(batch * D > 0 ? batch * D : 1), sizeof(double));
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t b = 0; b < batch; ++b) {
+        for (int64_t i = 0; i < L * N; ++i) {
+            dB[b * L * N + i] = 0.0;
+            dC[b * L * N + i] = 0.0;
+        }
+        double *hs = (double *)malloc(sizeof(double) * (size_t)((L + 1) * N > 0 ? (L + 1) * N : 1));
+        double *G = (double *)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1));
+        for (int64_t c = 0; c < D; ++c) {
+            for (int64_t n = 0; n < N; ++n) hs[n] = h0 ? h0[(b * D + c) * N + n] : 0.0;
+            for (int64_t t = 0; t < L; ++t) {
+                double xv = x[(b * L + t) * D + c], dtv = dt[(b * L + t) * D + c];
+                for (int64_t n = 0; n < N; ++n)
+                    hs[(t + 1) * N + n] = exp(dtv * A[c * N + n]) * hs[t * N + n] +
+                                          (dtv * B[(b * L + t) * N + n]) * xv;
+            }
+            for (int64_t n = 0; n < N; ++n) G[n] = dh_out ? dh_out[(b * D + c) * N + n] : 0.0;
+            for (int64_t t = L - 1; t >= 0; --t) {
+                double xv = x[(b * L + t) * D + c], dtv = dt[(b * L + t) * D + c];
+                double dyv = dy[(b * L + t) * D + c];
+                const double *Bt = B + (b * L + t) * N, *Ct = C + (b * L + t) * N;
+                const double *ht = hs + (t + 1) * N, *hp = hs + t * N;
+                double sx = 0.0, sdt = 0.0;
+                for (int64_t n = 0; n < N; ++n) {
+                    double a = exp(dtv * A[c * N + n]);
+                    G[n] += Ct[n] * dyv;
+                    dC[(b * L + t) * N + n] += ht[n] * dyv;
+                    dB[(b * L + t) * N + n] += G[n] * dtv * xv;
+                    sx += G[n] * dtv * Bt[n];
+                    sdt += G[n] * (Bt[n] * xv + A[c * N + n] * a * hp[n]);
+                    dA_b[(b * D + c) * N + n] += G[n] * dtv * a * hp[n];
+                    G[n] *= a;
+                }
+                dx[(b * L + t) * D + c] = sx + (Dskip ? Dskip[c] * dyv : 0.0);
+                ddt[(b * L + t) * D + c] = sdt;
+                dD_b[b * D + c] += dyv * xv;
+            }
+            if (dh0)
+                for (int64_t n = 0; n < N; ++n) dh0[(b * D + c) * N + n] = G[n];
+        }
+        free(hs);
+        free(G);
+    }
+    for (int64_t i = 0; i < D * N; ++i) {
+        double s = 0.0;
+        for (int64_t b = 0; b < batch; ++b) s += dA_b[b * D * N + i];
+        dA[i] = s;
+    }
+    for (int64_t c = 0; c < D; ++c) {
+        double s = 0.0;
+        for (int64_t b = 0; b < batch; ++b) s += dD_b[b * D + c];
+        dD[c] = s;
+    }
+    free(dA_b);
+    free(dD_b);
+}
+
+/*
  * Mamba-1 single-token step (burn_mamba `struct Mamba1` docs,
  * `selective_scan_step`; mamba-rs "Quick Start" step call).  One iteration of
  * the loop above on a state of shape (batch, D, N):

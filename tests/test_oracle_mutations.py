@@ -59,6 +59,12 @@ MUTATIONS = {
                       "for (int64_t n = 0; n < N; ++n) sx += Ct[n] * A[n * P + p];"),
     "bwd_dC_uses_previous_state": ("sc += ht[n * P + p] * dYt[p];", "sc += hp[n * P + p] * dYt[p];"),
     "bwd_final_state_gradient_dropped": ("A[i] = dh_out ? dh_out[(b * H + h) * NP + i] : 0.0;", "A[i] = 0.0;"),
+    "m1bwd_dt_uses_new_state": ("sdt += G[n] * (Bt[n] * xv + A[c * N + n] * a * hp[n]);",
+                                "sdt += G[n] * (Bt[n] * xv + A[c * N + n] * a * ht[n]);"),
+    "m1bwd_dx_drops_dt": ("sx += G[n] * dtv * Bt[n];", "sx += G[n] * Bt[n];"),
+    "m1bwd_adjoint_not_decayed": ("                    G[n] *= a;\n", ""),
+    "m1bwd_dB_before_adjoint_update": ("                    G[n] += Ct[n] * dyv;\n                    dC[(b * L + t) * N + n] += ht[n] * dyv;\n                    dB[(b * L + t) * N + n] += G[n] * dtv * xv;",
+                                       "                    dB[(b * L + t) * N + n] += G[n] * dtv * xv;\n                    G[n] += Ct[n] * dyv;\n                    dC[(b * L + t) * N + n] += ht[n] * dyv;"),
 }
 
 
@@ -138,6 +144,21 @@ def _battery(o):
         fd = (lossf(dict(inp, **{k: inp[k] + 1e-6 * v})) - lossf(dict(inp, **{k: inp[k] - 1e-6 * v}))) / 2e-6
         if abs(fd - float(np.sum(gk * v))) > 1e-6 * max(1.0, abs(fd)):
             failed.append("ssd_bwd_directional_" + k)
+
+    # backward of the Mamba-1 scan: directional derivatives of the forward loss
+    inp = wl.m1_inputs(rng, 2, 10, 3, 4, dt_mu=-1.0, h0_sd=0.4, A=-rng.uniform(0.1, 2.0, (3, 4)))
+    dy = rng.standard_normal(inp["x"].shape)
+    dh = rng.standard_normal(inp["h0"].shape)
+
+    def lossm(d):
+        yf, hf = o.m1_scan(**d)
+        return float(np.sum(yf * dy) + np.sum(hf * dh))
+    gr = o.m1_scan_bwd(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], dy, inp["D"], inp["h0"], dh)
+    for k, gk in zip(("x", "dt", "A", "B", "C", "D", "h0"), gr):
+        v = rng.standard_normal(inp[k].shape)
+        fd = (lossm(dict(inp, **{k: inp[k] + 1e-6 * v})) - lossm(dict(inp, **{k: inp[k] - 1e-6 * v}))) / 2e-6
+        if abs(fd - float(np.sum(gk * v))) > 1e-6 * max(1.0, abs(fd)):
+            failed.append("m1_bwd_directional_" + k)
 
     inp = wl.m1_block_inputs(rng, 2, 15, 3, 4, K=4, h0_sd=0.3, hist=True)
     y, h = o.m1_block(**inp)
