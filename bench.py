@@ -56,6 +56,20 @@ def m1_scan_work(b, L, D, N, es=4):
     return nbytes, b * L * D * N      # (bytes, exp count)
 
 
+# Minimal VALU issue slots per (t, c, n) element of the Mamba-1 backward: the
+# recomputed forward (6) and the adjoint step: G += C dy, dB and dC products,
+# U += G B, exp (2) and its argument, G a h_prev (2), V += A w, dA += dt w,
+# G *= a (12).
+M1_BWD_SLOTS_PER_ELEM = 18
+
+
+def m1_bwd_work(b, L, D, N):
+    """x, dt, dy, B, C, A, Dskip, dh_out read and dx, ddt, dB, dC, dA, dDskip, dh0
+    written once; (bytes, elements)."""
+    nbytes = 4 * (5 * b * L * D + 4 * b * L * N + 2 * b * D * N + 2 * D * N + 2 * D)
+    return nbytes, b * L * D * N
+
+
 def m1_step_work(b, D, N, es=4):
     nbytes = 4 * (2 * b * D * N) + es * (3 * b * D + 2 * b * N) + 4 * (D * N + D)
     return nbytes, b * D * N
@@ -233,6 +247,39 @@ class SSD(Workload):
         self.mb.mb_ssd_chunked(self.X, self.ld, self.B, self.C, None, Y=self.Y, h_out=self.h, ws=self.ws)
 
 
+class M1Bwd(Workload):
+    """Backward of the Mamba-1 scan at the block shape (outside the step,
+    measured beside it)."""
+    name = "m1_bwd"
+    kernel = "k_m1_scan_w (checkpoints) + k_m1_bwd + k_m1_bwd_reduce"
+    source = "selective_state_space_amd/csrc/m1.hip"
+    bound = "alu"
+    slots = M1_BWD_SLOTS_PER_ELEM
+
+    def __init__(self, mb, wl, torch):
+        self.mb = mb
+        inp = wl.m1_bwd_block()
+        self.inp = inp
+        b, L, D = inp["x"].shape
+        N = inp["A"].shape[1]
+        self.shape = dict(batch=b, L=L, D=D, N=N)
+        self.t = {k: _dev(v, torch.float32) for k, v in inp.items() if v is not None}
+        self.ws = torch.empty(mb.mb_workspace_size(mb.MB_OP_SELECTIVE_SCAN_BWD, b, L, D, 1, 1, N),
+                              dtype=torch.uint8, device="cuda")
+        t = self.t
+        self.out = dict(dx=torch.empty_like(t["x"]), ddt=torch.empty_like(t["x"]), dA=torch.empty_like(t["A"]),
+                        dB=torch.empty_like(t["B"]), dC=torch.empty_like(t["C"]), dD=torch.empty_like(t["D"]),
+                        dh0=torch.empty_like(t["dh_out"]))
+        self.tokens = b * L
+        self.bytes, self.exps = m1_bwd_work(b, L, D, N)
+        self.flops = None
+
+    def run(self):
+        t = self.t
+        self.mb.mb_selective_scan_bwd(t["x"], t["dt"], t["A"], t["B"], t["C"], t["dy"], t["D"], None, t["dh_out"],
+                                      ws=self.ws, **self.out)
+
+
 class SSDBwd(Workload):
     """Backward of the Mamba-2 SSD at the block shape (outside the step, measured
     beside it)."""
@@ -350,9 +397,9 @@ class SSDDecode(Workload):
 
 ALL = ["m1_scan", "m1_step", "ssd_f32", "ssd_bf16", "siso", "mimo"]
 # measured beside the step, not part of it: the decode steps of the SSD family, the
-# Mamba-1 scan with the block prologue and epilogue fused, and the backward of the
-# Mamba-2 SSD
-NEXT = ["m2_decode", "siso_decode", "mimo_decode", "m1_fused", "ssd_bwd"]
+# Mamba-1 scan with the block prologue and epilogue fused, and the backwards of the
+# Mamba-2 SSD and the Mamba-1 scan
+NEXT = ["m2_decode", "siso_decode", "mimo_decode", "m1_fused", "ssd_bwd", "m1_bwd"]
 
 
 def make(name, mb, wl, torch):
@@ -364,6 +411,8 @@ def make(name, mb, wl, torch):
         return M1Fused(mb, wl, torch)
     if name == "ssd_bwd":
         return SSDBwd(mb, wl, torch)
+    if name == "m1_bwd":
+        return M1Bwd(mb, wl, torch)
     if name == "ssd_f32":
         return SSD(mb, wl, torch, "f32")
     if name == "ssd_bf16":
@@ -382,7 +431,7 @@ def roofline_of(w, ms, bound=None):
     s = ms * 1e-3
     bound = bound or w.bound
     if bound == "alu":
-        ach = w.exps * M1_SLOTS_PER_ELEM / s / 1e9
+        ach = w.exps * getattr(w, "slots", M1_SLOTS_PER_ELEM) / s / 1e9
         peak = VALU_F32_LANE_OPS / 1e9
         return {"bound": "alu", "achieved": ach, "peak": peak, "unit": "Gop/s", "frac": ach / peak}
     if bound == "mfma":
@@ -464,8 +513,8 @@ def cold_ms(torch, w, reps=5):
 
 
 def time_next(args, mb, wl, torch):
-    """Decode steps of the SSD family, the fused Mamba-1 block scan and the SSD
-    backward, timed with
+    """Decode steps of the SSD family, the fused Mamba-1 block scan and the two
+    backwards, timed with
     HIP events on the stream they run on, outside the step (they are not part of
     its token count)."""
     res = []

@@ -61,7 +61,8 @@ typedef enum {
     MB_OP_SSD_CHUNKED = 2,
     MB_OP_TRAP_SSD = 3,
     MB_OP_MIMO_SSD = 4,
-    MB_OP_SSD_CHUNKED_BWD = 5
+    MB_OP_SSD_CHUNKED_BWD = 5,
+    MB_OP_SELECTIVE_SCAN_BWD = 6
 } mb_op;
 
 /*
@@ -244,6 +245,39 @@ mb_status mb_ssd_step(const void* X, const float* logdecay, const void* B,
                       const float* h_in, float* h_out, void* Y, int64_t batch,
                       int64_t H, int64_t P, int64_t G, int64_t N, int64_t R,
                       mb_dtype dtype, hipStream_t stream);
+
+/*
+ * Backward of mb_selective_scan (fp32): the vector-Jacobian product of the
+ * Mamba-1 scan (TorchMamba README, Math notes M1; trained by back-propagation
+ * through time, as the mamba-rs page lists).  Given dy (gradient of the loss
+ * with respect to y) and dh_out (with respect to h_out; NULL = zero), returns
+ * the gradients of  sum dy . y + sum dh_out . h_out  with respect to x, dt, A,
+ * B, C, Dskip and h0.  With a_t = exp(dt_t A) and G the adjoint of one
+ * channel's state (G = dh_out, then per step from the last: G += C_t dy_t, ...,
+ * G = a_t G):
+ *     dx_t = dt_t sum_n G B_t + Dskip dy_t,  ddt_t = sum_n G (B_t x_t + A a_t h_{t-1}),
+ *     dB_t = sum_c G dt_t x_t,  dC_t = sum_c h_t dy_t,
+ *     dA = sum_{b,t} G dt_t a_t h_{t-1},  dDskip = sum_{b,t} dy_t x_t,  dh0 = G at the end.
+ * The forward states are recomputed from per-32-step checkpoints in the
+ * workspace; nothing of the forward call is needed.  Deterministic.
+ *   x, dt, dy, dx, ddt : (batch, L, D)  fp32
+ *   A, dA              : (D, N)         fp32
+ *   B, C, dB, dC       : (batch, L, N)  fp32
+ *   Dskip, dD          : (D)            fp32; Dskip NULL = no skip term; dD NULL = not wanted
+ *   h0, dh_out, dh0    : (batch, D, N)  fp32; h0, dh_out NULL = zeros; dh0 NULL = not wanted
+ * ws / ws_bytes: device workspace of at least
+ * mb_workspace_size(MB_OP_SELECTIVE_SCAN_BWD, batch, L, D, <P ignored>, <G
+ * ignored>, N, ...) bytes (D in the H argument), 256-byte aligned.
+ * Supported: dtype MB_F32 (MB_ERR_DTYPE otherwise); N in {4, 8, 16}
+ * (MB_ERR_SHAPE otherwise); x, dt, B, C, dy 16-byte aligned (MB_ERR_ALIGN).  No
+ * output may overlap an input, another output or the workspace (MB_ERR_ALIAS).
+ */
+mb_status mb_selective_scan_bwd(const float* x, const float* dt, const float* A, const float* B,
+                                const float* C, const float* Dskip, const float* h0,
+                                const float* dy, const float* dh_out, float* dx, float* ddt,
+                                float* dA, float* dB, float* dC, float* dD, float* dh0,
+                                int64_t batch, int64_t L, int64_t D, int64_t N, mb_dtype dtype,
+                                void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * Backward of mb_ssd_chunked (fp32): the vector-Jacobian product of the Mamba-2

@@ -16,9 +16,9 @@ import threading
 
 __all__ = [
     "mb_selective_scan", "mb_ssm_step", "mb_ssd_chunked", "mb_trap_ssd", "mb_mimo_ssd",
-    "mb_ssd_step", "mb_selective_scan_fused", "mb_ssd_chunked_bwd", "mb_workspace_size", "mb_status_str", "lib_path", "load_library", "MBError",
+    "mb_ssd_step", "mb_selective_scan_fused", "mb_ssd_chunked_bwd", "mb_selective_scan_bwd", "mb_workspace_size", "mb_status_str", "lib_path", "load_library", "MBError",
     "MB_OP_SELECTIVE_SCAN", "MB_OP_SSM_STEP", "MB_OP_SSD_CHUNKED", "MB_OP_TRAP_SSD",
-    "MB_OP_MIMO_SSD", "MB_OP_SSD_CHUNKED_BWD",
+    "MB_OP_MIMO_SSD", "MB_OP_SSD_CHUNKED_BWD", "MB_OP_SELECTIVE_SCAN_BWD",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -28,7 +28,7 @@ _lib = None
 
 MB_F32, MB_BF16 = 0, 1
 (MB_OP_SELECTIVE_SCAN, MB_OP_SSM_STEP, MB_OP_SSD_CHUNKED, MB_OP_TRAP_SSD,
- MB_OP_MIMO_SSD, MB_OP_SSD_CHUNKED_BWD) = range(6)
+ MB_OP_MIMO_SSD, MB_OP_SSD_CHUNKED_BWD, MB_OP_SELECTIVE_SCAN_BWD) = range(7)
 
 _vp = ctypes.c_void_p
 _i64 = ctypes.c_int64
@@ -68,6 +68,9 @@ def load_library():
             lib.mb_workspace_size.restype = ctypes.c_size_t
             for f in ("mb_ssd_chunked", "mb_trap_ssd", "mb_mimo_ssd"):
                 getattr(lib, f).restype = ctypes.c_int
+        if hasattr(lib, "mb_selective_scan_bwd"):
+            lib.mb_selective_scan_bwd.argtypes = [_vp] * 16 + [_i64] * 4 + [ctypes.c_int, _vp, ctypes.c_size_t, _vp]
+            lib.mb_selective_scan_bwd.restype = ctypes.c_int
         if hasattr(lib, "mb_ssd_chunked_bwd"):
             lib.mb_ssd_chunked_bwd.argtypes = [_vp] * 12 + [_i64] * 6 + [ctypes.c_int, _vp, ctypes.c_size_t, _vp]
             lib.mb_ssd_chunked_bwd.restype = ctypes.c_int
@@ -231,6 +234,36 @@ def mb_ssd_chunked(X, logdecay, B, C, h0=None, *, chunk=0, Y=None, h_out=None, w
     _call("mb_ssd_chunked", _ptr(X), _ptr(logdecay), _ptr(B), _ptr(C), _ptr(h0), _ptr(Y), _ptr(h_out),
           b, L, H, P, G, N, chunk, code, _ptr(ws), nws, _stream(dev))
     return Y, h_out
+
+
+def mb_selective_scan_bwd(x, dt, A, B, C, dy, D=None, h0=None, dh_out=None, *, dx=None, ddt=None, dA=None,
+                          dB=None, dC=None, dD=None, dh0=None, ws=None):
+    """Backward of the Mamba-1 scan (float32): the gradients of sum dy . y + sum
+    dh_out . h_out with respect to x, dt, A, B, C, D and h0.  Shapes as
+    mb_selective_scan; dy like x, dh_out like h0 (None: zero).  Returns (dx, ddt,
+    dA, dB, dC, dD, dh0)."""
+    torch = _torch()
+    dev = _device_of(x)
+    f32 = torch.float32
+    b, L, Dm = x.shape
+    N = A.shape[1]
+    _check(x, "x", (b, L, Dm), f32, dev)
+    _check(dt, "dt", (b, L, Dm), f32, dev)
+    _check(A, "A", (Dm, N), f32, dev)
+    _check(B, "B", (b, L, N), f32, dev)
+    _check(C, "C", (b, L, N), f32, dev)
+    _check(dy, "dy", (b, L, Dm), f32, dev)
+    _check(D, "D", (Dm,), f32, dev)
+    _check(h0, "h0", (b, Dm, N), f32, dev)
+    _check(dh_out, "dh_out", (b, Dm, N), f32, dev)
+    out = []
+    for t, n, shp in ((dx, "dx", (b, L, Dm)), (ddt, "ddt", (b, L, Dm)), (dA, "dA", (Dm, N)), (dB, "dB", (b, L, N)),
+                      (dC, "dC", (b, L, N)), (dD, "dD", (Dm,)), (dh0, "dh0", (b, Dm, N))):
+        out.append(torch.empty(shp, dtype=f32, device=dev) if t is None else _check(t, n, shp, f32, dev))
+    ws, nws = _workspace(MB_OP_SELECTIVE_SCAN_BWD, dev, ws, (b, L, Dm, 1, 1, N, 1, 0))
+    _call("mb_selective_scan_bwd", _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(h0), _ptr(dy),
+          _ptr(dh_out), *[_ptr(t) for t in out], b, L, Dm, N, MB_F32, _ptr(ws), nws, _stream(dev))
+    return tuple(out)
 
 
 def mb_ssd_chunked_bwd(X, logdecay, B, C, dY, h0=None, dh_out=None, *, dX=None, dlogdecay=None, dB=None,

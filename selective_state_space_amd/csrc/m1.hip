@@ -226,6 +226,7 @@ struct Fuse {
     const float* dt_bias;   // (D) or NULL
     const float* z;         // (batch, L, D) gate, or NULL
     int K;
+    float* ck;              // checkpoint mode: (batch, ntiles, D, N) state entering every tile
 };
 
 // lane j's value of a quad, to every lane of the quad
@@ -299,7 +300,7 @@ __device__ __forceinline__ void dma_lds(const Buf& src, lds_f* dst, uint32_t off
         __builtin_amdgcn_raw_ptr_buffer_load_lds(src.r, (__attribute__((address_space(3))) void*)dst, 4, off, 0, 0, 0);
 }
 
-template <int S, bool V16, bool FUSED = false>
+template <int S, bool V16, bool FUSED = false, bool CK = false>
 __global__ __launch_bounds__(256) void k_m1_scan_w(
     const float* __restrict__ x, const float* __restrict__ dt, const float* __restrict__ A,
     const float* __restrict__ Bm, const float* __restrict__ Cm, const float* __restrict__ Dskip,
@@ -336,7 +337,8 @@ __global__ __launch_bounds__(256) void k_m1_scan_w(
     const Buf bdt = make_buf(dt + (size_t)b * row, row * 4);
     const Buf bB = make_buf(Bm + (size_t)b * L * N, (size_t)L * N * 4);
     const Buf bC = make_buf(Cm + (size_t)b * L * N, (size_t)L * N * 4);
-    const Buf by = make_buf(y + (size_t)b * row, row * 4);
+    // without y (checkpoint mode) the stores fall outside a zero-size buffer
+    const Buf by = make_buf(y ? y + (size_t)b * row : x, y ? row * 4 : 0);
     // the gate: without one, its copies read zeros (the copy count stays fixed)
     const Buf bz = make_buf(FUSED && fz.z ? fz.z + (size_t)b * row : x, FUSED && fz.z ? row * 4 : 0);
 
@@ -451,6 +453,15 @@ __global__ __launch_bounds__(256) void k_m1_scan_w(
     // tile k: copies of tile k + 2 go out first; the operands of its groups are
     // read one group ahead, the last group reading the first of tile k + 1
     auto tile = [&](int k, lds_cf* cur, lds_f* nxt, lds_f* nxt2) __attribute__((always_inline)) {
+        if constexpr (CK) {
+            // the state entering tile k (issued before the copies of tile k + 2:
+            // the waits below stay exact or conservative)
+            if (cok) {
+                float* dst = fz.ck + (((size_t)b * ntiles + k) * D + c) * N + S * q;
+#pragma unroll
+                for (int s = 0; s < S; ++s) dst[s] = h[s];
+            }
+        }
         dma(k + 2, nxt2);
         const int t0 = k * T;
 #pragma unroll
@@ -594,6 +605,305 @@ __global__ __launch_bounds__(256) void k_m1_step_q(
                 store_out(&y[bc[k]], fmaf(dv, xv[k], p));
             }
         }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Backward of the Mamba-1 scan (fp32, N in {4, 8, 16}), the vector-Jacobian
+// product of (y, h_out) for (dy, dh_out).  The lane layout of k_m1_scan_w: a
+// wave holds 16 channels x 4 lanes, lane (cl, q) the states n = S q + s.  Tiles
+// of 32 steps are walked last to first; each starts from the checkpointed state
+// entering it (k_m1_scan_w in checkpoint mode), recomputes its 32 states in
+// registers and runs the adjoint G back through them, with a_t = e^{dt_t A}:
+//     G += C_t dy_t;   dB_t += G dt x;   dC_t += h_t dy_t;   U = sum_n G B_t
+//     w = G a_t h_{t-1};   V = sum_n A w;   dA += dt w;   G *= a_t
+//     dx_t = dt U + Dskip dy_t,   ddt_t = x U + V,   dDskip += dy x.
+// U and V are summed over the quad by the forward's exchange (lane q then holds
+// step 4i + q); dB and dC of four steps are summed over the wave's 16 channels
+// by a halving butterfly (each exchange halves the values a lane keeps), over the
+// workgroup's four waves in LDS once per tile, and over the workgroups by
+// k_m1_bwd_reduce, in a fixed order (deterministic).
+// ---------------------------------------------------------------------------
+// a where the mask is all ones, b where it is zero (bitwise, so that a choice
+// between two elements of a register array is never turned into an index)
+__device__ __forceinline__ float bsel(uint32_t m, float a, float b) {
+    return __uint_as_float((__float_as_uint(a) & m) | (__float_as_uint(b) & ~m));
+}
+
+struct M1Bwd {
+    const float *x, *dt, *A, *B, *C, *Dskip, *dy, *dh_out, *ck;
+    float *dx, *ddt, *dh0;
+    float* pBC;   // (2, batch, n_cg, L, N) per-workgroup partial dB (0) and dC (1)
+    float* pA;    // (batch, D, N) per-batch dA
+    float* pD;    // (batch, D) per-batch dDskip
+    int L, D, n_cg;
+};
+
+template <int S, bool V16>
+__global__ __launch_bounds__(256) void k_m1_bwd(M1Bwd a) {
+    constexpr int T = kScanT;
+    constexpr int N = 4 * S;
+    constexpr int NG = T / 4;
+    constexpr bool BC16 = (T * N) % 256 == 0;
+    constexpr int XW = V16 ? 16 : 4;
+    constexpr int BW = BC16 ? 16 : 4;
+    constexpr int NDX = T * 16 * 4 / (64 * XW);
+    constexpr int NDB = T * N * 4 / (64 * BW);
+    constexpr int OX = T * 16, OB = 2 * T * 16, OC = 2 * T * 16 + T * N, OZ = OC + T * N;
+    constexpr int NV = 8 * S;                    // dB, dC values of four steps per lane
+    __shared__ __attribute__((aligned(16))) ScanTile<S, true> tb0[4];
+    __shared__ __attribute__((aligned(16))) ScanTile<S, true> tb1[4];
+    __shared__ float sAcc[2][4][2][T][N];        // per tile parity and wave: dB, dC of the tile's steps
+    constexpr int NFL = 2 * T * N / 256;         // flush stores per thread and tile
+
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
+    lds_f* const p0 = (lds_f*)tb0[w].v;
+    lds_f* const p1 = (lds_f*)tb1[w].v;
+    const int L = a.L, D = a.D;
+    const int batch = gridDim.x / a.n_cg;
+    const int b = blockIdx.x / a.n_cg, cg = blockIdx.x % a.n_cg, c0 = cg * 64 + 16 * w;
+    const int lane = threadIdx.x % 64;
+    const int cl = lane >> 2, q = lane & 3;
+    const int c = c0 + cl;
+    const bool cok = c < D;
+    const size_t row = (size_t)L * D;
+    const Buf bx = make_buf(a.x + (size_t)b * row, row * 4);
+    const Buf bdt = make_buf(a.dt + (size_t)b * row, row * 4);
+    const Buf bdy = make_buf(a.dy + (size_t)b * row, row * 4);
+    const Buf bB = make_buf(a.B + (size_t)b * L * N, (size_t)L * N * 4);
+    const Buf bC = make_buf(a.C + (size_t)b * L * N, (size_t)L * N * 4);
+    const Buf bdx = make_buf(a.dx + (size_t)b * row, row * 4);
+    const Buf bddt = make_buf(a.ddt + (size_t)b * row, row * 4);
+
+    // tile copies as in k_m1_scan_w, with dy in the third stream
+    const uint32_t xo = V16 ? (uint32_t)(((lane >> 2) * D + c0 + 4 * (lane & 3)) * 4)
+                            : (uint32_t)(((lane >> 4) * D + c0 + (lane & 15)) * 4);
+    const uint32_t bo = (uint32_t)(BW * lane);
+    auto dma = [&](int k, lds_f* dst) __attribute__((always_inline)) {
+        const int t0 = k * T;
+#pragma unroll
+        for (int m = 0; m < NDX; ++m) {
+            const uint32_t off = xo + (uint32_t)((t0 + XW * m) * D) * 4u;
+            dma_lds<XW>(bdt, dst + 16 * XW * m, off);
+            dma_lds<XW>(bx, dst + OX + 16 * XW * m, off);
+            dma_lds<XW>(bdy, dst + OZ + 16 * XW * m, off);
+        }
+#pragma unroll
+        for (int m = 0; m < NDB; ++m) {
+            const uint32_t off = bo + (uint32_t)(t0 * N + 16 * BW * m) * 4u;
+            dma_lds<BW>(bB, dst + OB + 16 * BW * m, off);
+            dma_lds<BW>(bC, dst + OC + 16 * BW * m, off);
+        }
+    };
+
+    float A2[S], Ar[S], G[S], dA[S];
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+        const int n = S * q + s;
+        Ar[s] = cok ? a.A[(size_t)c * N + n] : 0.0f;
+        A2[s] = Ar[s] * kLog2e;
+        G[s] = (cok && a.dh_out) ? a.dh_out[((size_t)b * D + c) * N + n] : 0.0f;
+        dA[s] = 0.0f;
+    }
+    const float Dv = (cok && a.Dskip) ? a.Dskip[c] : 0.0f;
+    float dDacc = 0.0f;
+    const uint32_t mlo = (q & 2) == 0 ? ~0u : 0u, mev = (q & 1) == 0 ? ~0u : 0u;
+    const int ntiles = (L + T - 1) / T;
+    const float* ckb = a.ck + ((size_t)b * ntiles * D + (cok ? c : 0)) * N + S * q;
+    float ckr[S];
+    // one vector load (S consecutive floats)
+    auto ld_ck = [&](int k) __attribute__((always_inline)) {
+        const float* p = ckb + (size_t)k * D * N;
+        if constexpr (S == 4) {
+            const float4 v = *(const float4*)p;
+            ckr[0] = v.x; ckr[1] = v.y; ckr[2] = v.z; ckr[3] = v.w;
+        } else if constexpr (S == 2) {
+            const float2 v = *(const float2*)p;
+            ckr[0] = v.x; ckr[1] = v.y;
+        } else {
+            ckr[0] = p[0];
+        }
+    };
+
+    auto tile = [&](int k, lds_cf* cur, lds_f* nxt, int par) __attribute__((always_inline)) {
+        // tile k's copies were followed by at most one checkpoint load, the
+        // previous tile's 2 NG stores of dx and ddt and its NFL partial-sum stores
+        vm_wait<1 + 2 * NG + NFL>();
+        asm volatile("" ::: "memory");
+        float hst[S];
+#pragma unroll
+        for (int s = 0; s < S; ++s) hst[s] = ckr[s];
+        if (k > 0) {
+            dma(k - 1, nxt);
+            ld_ck(k - 1);
+        }
+        const int t0 = k * T;
+        // the tile's states, recomputed from the checkpoint
+        float hs[T][S];
+        {
+            float h[S];
+#pragma unroll
+            for (int s = 0; s < S; ++s) h[s] = hst[s];
+#pragma unroll
+            for (int t = 0; t < T; ++t) {
+                const float dtv = cur[t * 16 + cl];
+                const float dtx = dtv * cur[OX + t * 16 + cl];
+                float bb[S];
+                lds_row<S>(cur + OB + t * N + S * q, bb);
+#pragma unroll
+                for (int s = 0; s < S; ++s) {
+                    h[s] = fmaf(exp2_fast(dtv * A2[s]), h[s], dtx * bb[s]);
+                    hs[t][s] = h[s];
+                }
+            }
+        }
+        // the adjoint, back through the tile, four steps at a time
+#pragma unroll
+        for (int i = NG - 1; i >= 0; --i) {
+            float U[4], V[4], vals[NV];
+#pragma unroll
+            for (int j = 3; j >= 0; --j) {
+                const int t = 4 * i + j;
+                const float dtv = cur[t * 16 + cl];
+                const float xv = cur[OX + t * 16 + cl];
+                // lanes past the last channel read the next row's values: their dy
+                // is zeroed so that they add nothing to the channel sums of dB, dC
+                const float dyv = cok ? cur[OZ + t * 16 + cl] : 0.0f;
+                const float dtx = dtv * xv;
+                float bb[S], cc[S];
+                lds_row<S>(cur + OB + t * N + S * q, bb);
+                lds_row<S>(cur + OC + t * N + S * q, cc);
+                float u = 0.0f, v = 0.0f;
+#pragma unroll
+                for (int s = 0; s < S; ++s) {
+                    G[s] = fmaf(cc[s], dyv, G[s]);
+                    vals[(j * S + s) * 2 + 0] = G[s] * dtx;
+                    vals[(j * S + s) * 2 + 1] = hs[t][s] * dyv;
+                    u = fmaf(G[s], bb[s], u);
+                    const float av = exp2_fast(dtv * A2[s]);
+                    const float hp = t > 0 ? hs[t > 0 ? t - 1 : 0][s] : hst[s];
+                    const float wv = G[s] * av * hp;
+                    v = fmaf(Ar[s], wv, v);
+                    dA[s] = fmaf(dtv, wv, dA[s]);
+                    G[s] *= av;
+                }
+                U[j] = u;
+                V[j] = v;
+            }
+            // sums over the quad: lane q then holds step 4i + q
+            auto quad_sum = [&](float p0, float p1, float p2, float p3) __attribute__((always_inline)) {
+                float k0 = bsel(mlo, p0, p2), s0 = bsel(mlo, p2, p0);
+                float k1 = bsel(mlo, p1, p3), s1 = bsel(mlo, p3, p1);
+                k0 += quad_swap<0x4E>(s0);
+                k1 += quad_swap<0x4E>(s1);
+                const float kk = bsel(mev, k0, k1), ss = bsel(mev, k1, k0);
+                return kk + quad_swap<0xB1>(ss);
+            };
+            const float Uq = quad_sum(U[0], U[1], U[2], U[3]), Vq = quad_sum(V[0], V[1], V[2], V[3]);
+            const int tq = 4 * i + q;
+            const float dtq = cur[tq * 16 + cl], xq = cur[OX + tq * 16 + cl], dyq = cur[OZ + tq * 16 + cl];
+            dDacc = fmaf(dyq, xq, dDacc);
+            const uint32_t off = cok ? (uint32_t)((t0 + tq) * D + c) * 4u : 0x80000000u;
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(fmaf(dtq, Uq, Dv * dyq)), bdx.r, off, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(fmaf(xq, Uq, Vq)), bddt.r, off, 0, 0);
+            // dB, dC summed over the wave's 16 channels (lane bits 2..5)
+            int base = 0;
+#pragma unroll
+            for (int st = 0; st < 4; ++st) {
+                const int m = 4 << st;
+                const uint32_t up = (lane & m) != 0 ? ~0u : 0u;
+                const int half = (NV >> st) / 2;          // values kept after this exchange
+                if constexpr (true) {
+                    if (half >= 1) {
+#pragma unroll
+                        for (int e = 0; e < NV / 2; ++e) {
+                            if (e < half) {
+                                const float send = bsel(up, vals[e], vals[e + half]);
+                                const float keep = bsel(up, vals[e + half], vals[e]);
+                                vals[e] = keep + __shfl_xor(send, m, 64);
+                            }
+                        }
+                        base += (lane & m) != 0 ? half : 0;
+                    } else {
+                        vals[0] += __shfl_xor(vals[0], m, 64);
+                    }
+                }
+            }
+            // the lane keeps cnt values, original indices base .. base + cnt - 1
+            // (after a final plain exchange the lanes with bit 5 set hold copies)
+            if (NV >= 16 || (lane & 32) == 0) {
+#pragma unroll
+                for (int e = 0; e < NV / 16 + (NV < 16 ? 1 : 0); ++e) {
+                    const int idx = base + e;
+                    const int kind = idx & 1, js = idx >> 1;
+                    const int j = js / S, sidx = js % S;
+                    sAcc[par][w][kind][4 * i + j][S * q + sidx] = vals[e];
+                }
+            }
+        }
+        // the tile's per-wave sums are in LDS; the other parity's were read
+        // out by every wave before this barrier, so the next tile may write them
+        __syncthreads();
+#pragma unroll
+        for (int f = 0; f < NFL; ++f) {
+            const int e = threadIdx.x + 256 * f;
+            const int kind = e / (T * N), t = (e / N) % T, n = e % N;
+            if (t0 + t < L) {
+                const float v = (sAcc[par][0][kind][t][n] + sAcc[par][1][kind][t][n]) +
+                                (sAcc[par][2][kind][t][n] + sAcc[par][3][kind][t][n]);
+                a.pBC[((((size_t)kind * batch + b) * a.n_cg + cg) * L + t0 + t) * N + n] = v;
+            }
+        }
+    };
+
+    ld_ck(ntiles - 1);
+    dma(ntiles - 1, p0);
+    vm_wait<0>();   // the first tile and its checkpoint
+    for (int k = ntiles - 1; k >= 0; k -= 2) {
+        tile(k, p0, p1, 0);
+        if (k - 1 >= 0) tile(k - 1, p1, p0, 1);
+    }
+    vm_wait<0>();   // no copy into LDS may be in flight when the wave ends
+    dDacc += __shfl_xor(dDacc, 1, 64);
+    dDacc += __shfl_xor(dDacc, 2, 64);
+    if (cok) {
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+            const size_t e = ((size_t)b * D + c) * N + S * q + s;
+            if (a.dh0) a.dh0[e] = G[s];
+            a.pA[e] = dA[s];
+        }
+        if (q == 0) a.pD[(size_t)b * D + c] = dDacc;
+    }
+}
+
+// Sums of the backward's partials in a fixed order: dB, dC over the channel
+// groups (job 0), dA over the batch (job 1), dDskip over the batch (job 2).
+__global__ __launch_bounds__(256) void k_m1_bwd_reduce(M1Bwd a, float* dB, float* dC, float* dA, float* dD,
+                                                      int batch, int N) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int job = blockIdx.y;
+    if (job == 0) {
+        const int64_t per = (int64_t)batch * a.L * N;
+        if (i >= 2 * per) return;
+        const int kind = (int)(i / per);
+        const int64_t r = i % per;
+        const int64_t b = r / ((int64_t)a.L * N), tn = r % ((int64_t)a.L * N);
+        const float* src = a.pBC + (((size_t)kind * batch + b) * a.n_cg) * a.L * N + tn;
+        float v = 0.0f;
+        for (int g = 0; g < a.n_cg; ++g) v += src[(size_t)g * a.L * N];
+        (kind ? dC : dB)[r] = v;
+    } else if (job == 1) {
+        const int64_t dn = (int64_t)a.D * N;
+        if (i >= dn) return;
+        float v = 0.0f;
+        for (int b = 0; b < batch; ++b) v += a.pA[(size_t)b * dn + i];
+        dA[i] = v;
+    } else {
+        if (i >= a.D || !dD) return;
+        float v = 0.0f;
+        for (int b = 0; b < batch; ++b) v += a.pD[(size_t)b * a.D + i];
+        dD[i] = v;
     }
 }
 
@@ -808,6 +1118,116 @@ extern "C" mb_status mb_selective_scan_fused(const float* x, const float* conv_w
     default: MB_SCAN_F(4); break;
     }
 #undef MB_SCAN_F
+    return check_launch();
+}
+
+namespace mb {
+namespace {
+struct M1BwdPlan {
+    size_t off_pbc, off_pa, off_pd, bytes;
+};
+M1BwdPlan m1_bwd_plan(int64_t batch, int64_t L, int64_t D, int64_t N) {
+    M1BwdPlan p{};
+    const int64_t ntiles = (L + kScanT - 1) / kScanT, n_cg = (D + 63) / 64;
+    auto al = [](size_t v) { return (v + 255) & ~(size_t)255; };
+    size_t off = al((size_t)(batch * ntiles * D * N) * 4);                 // checkpoints
+    p.off_pbc = off;
+    off += al((size_t)(2 * batch * n_cg * L * N) * 4);
+    p.off_pa = off;
+    off += al((size_t)(batch * D * N) * 4);
+    p.off_pd = off;
+    off += al((size_t)(batch * D) * 4);
+    p.bytes = off;
+    return p;
+}
+bool m1_bwd_dims_ok(int64_t batch, int64_t L, int64_t D, int64_t N) {
+    if (batch < 0 || L < 0 || D < 0) return false;
+    if (N != 4 && N != 8 && N != 16) return false;
+    if (batch > INT32_MAX || L > INT32_MAX || D > INT32_MAX) return false;
+    if (batch * ((D + 63) / 64) > INT32_MAX) return false;
+    if ((L + 64) * D * 4 >= ((int64_t)1 << 31) || (L + 64) * N * 4 >= ((int64_t)1 << 31)) return false;
+    return true;
+}
+}  // namespace
+
+size_t m1_bwd_workspace(int64_t batch, int64_t L, int64_t D, int64_t N) {
+    if (!m1_bwd_dims_ok(batch, L, D, N) || batch == 0 || L == 0 || D == 0) return 0;
+    return m1_bwd_plan(batch, L, D, N).bytes;
+}
+}  // namespace mb
+
+extern "C" mb_status mb_selective_scan_bwd(const float* x, const float* dt, const float* A, const float* B,
+                                           const float* C, const float* Dskip, const float* h0,
+                                           const float* dy, const float* dh_out, float* dx, float* ddt,
+                                           float* dA, float* dB, float* dC, float* dD, float* dh0,
+                                           int64_t batch, int64_t L, int64_t D, int64_t N, mb_dtype dtype,
+                                           void* ws, size_t ws_bytes, hipStream_t stream)
+{
+    if (dtype != MB_F32) return MB_ERR_DTYPE;
+    if (!m1_bwd_dims_ok(batch, L, D, N)) return MB_ERR_SHAPE;
+    const size_t n_x = (size_t)(batch * L * D), n_b = (size_t)(batch * L * N);
+    const size_t n_h = (size_t)(batch * D * N), n_a = (size_t)(D * N);
+    if (n_x && (!x || !dt || !dy || !dx || !ddt)) return MB_ERR_NULL;
+    if (n_b && (!B || !C || !dB || !dC)) return MB_ERR_NULL;
+    if (D > 0 && (!A || !dA)) return MB_ERR_NULL;
+    // the tiles are copied with 16-byte pieces of rows
+    if (((uintptr_t)x | (uintptr_t)dt | (uintptr_t)B | (uintptr_t)C | (uintptr_t)dy) & 15) return MB_ERR_ALIGN;
+    const Span ins[] = {{x, n_x * 4}, {dt, n_x * 4}, {A, n_a * 4}, {B, n_b * 4}, {C, n_b * 4},
+                        {Dskip, Dskip ? (size_t)D * 4 : 0}, {h0, h0 ? n_h * 4 : 0}, {dy, n_x * 4},
+                        {dh_out, dh_out ? n_h * 4 : 0}};
+    const Span outs[] = {{dx, n_x * 4}, {ddt, n_x * 4}, {dA, n_a * 4}, {dB, n_b * 4}, {dC, n_b * 4},
+                         {dD, dD ? (size_t)D * 4 : 0}, {dh0, dh0 ? n_h * 4 : 0}};
+    for (int i = 0; i < 7; ++i) {
+        if (overlaps_any(outs[i].p, outs[i].bytes, ins, 9)) return MB_ERR_ALIAS;
+        for (int j = i + 1; j < 7; ++j)
+            if (overlaps(outs[i].p, outs[i].bytes, outs[j].p, outs[j].bytes)) return MB_ERR_ALIAS;
+    }
+    if (D == 0) return MB_OK;
+    if (batch == 0 || L == 0) {
+        // no steps: dA = dDskip = 0, dh0 = dh_out
+        mb_status st = copy_state(nullptr, dA, (int64_t)n_a, stream);
+        if (st == MB_OK && dD) st = copy_state(nullptr, dD, D, stream);
+        if (st == MB_OK && dh0 && batch > 0) st = copy_state(dh_out, dh0, (int64_t)n_h, stream);
+        return st;
+    }
+    const M1BwdPlan pl = m1_bwd_plan(batch, L, D, N);
+    if (!ws || ws_bytes < pl.bytes || ((uintptr_t)ws & 255)) return MB_ERR_WORKSPACE;
+    if (overlaps_any(ws, pl.bytes, ins, 9) || overlaps_any(ws, pl.bytes, outs, 7)) return MB_ERR_ALIAS;
+    char* w = (char*)ws;
+    const int n_cg = (int)((D + 63) / 64);
+    const int n_wg = (int)(batch * n_cg);
+    M1Bwd a{};
+    a.x = x; a.dt = dt; a.A = A; a.B = B; a.C = C; a.Dskip = Dskip; a.dy = dy; a.dh_out = dh_out;
+    a.ck = (const float*)w;
+    a.dx = dx; a.ddt = ddt; a.dh0 = dh0;
+    a.pBC = (float*)(w + pl.off_pbc);
+    a.pA = (float*)(w + pl.off_pa);
+    a.pD = (float*)(w + pl.off_pd);
+    a.L = (int)L; a.D = (int)D; a.n_cg = n_cg;
+    Fuse ckf{};
+    ckf.ck = (float*)w;
+    const bool v16 = D % 4 == 0;
+#define MB_M1_BWD(S)                                                                                   \
+    do {                                                                                              \
+        if (v16) {                                                                                    \
+            hipLaunchKernelGGL((k_m1_scan_w<S, true, false, true>), dim3(n_wg), dim3(256), 0, stream, \
+                               x, dt, A, B, C, nullptr, h0, nullptr, nullptr, (int)L, (int)D, n_cg, ckf); \
+            hipLaunchKernelGGL((k_m1_bwd<S, true>), dim3(n_wg), dim3(256), 0, stream, a);             \
+        } else {                                                                                      \
+            hipLaunchKernelGGL((k_m1_scan_w<S, false, false, true>), dim3(n_wg), dim3(256), 0, stream,\
+                               x, dt, A, B, C, nullptr, h0, nullptr, nullptr, (int)L, (int)D, n_cg, ckf); \
+            hipLaunchKernelGGL((k_m1_bwd<S, false>), dim3(n_wg), dim3(256), 0, stream, a);            \
+        }                                                                                             \
+    } while (0)
+    switch (N) {
+    case 4: MB_M1_BWD(1); break;
+    case 8: MB_M1_BWD(2); break;
+    default: MB_M1_BWD(4); break;
+    }
+#undef MB_M1_BWD
+    const int64_t most = std::max<int64_t>(2 * batch * L * N, D * N);
+    hipLaunchKernelGGL(k_m1_bwd_reduce, dim3((unsigned)((most + 255) / 256), 3), dim3(256), 0, stream, a, dB, dC,
+                       dA, dD, (int)batch, (int)N);
     return check_launch();
 }
 

@@ -244,5 +244,17 @@ def m1_block_inputs(rng, batch, L, D, N, K=4, h0_sd=0.0, hist=False):
     return d
 
 
+def m1_bwd_block(seed=112):
+    """The Mamba-1 block inputs (seed 102) with the incoming gradients of the
+    backward: dy ~ N(0,1) like x and dh_out ~ N(0,1) like the state."""
+    d = m1_block()
+    rng = np.random.default_rng(seed)
+    b, L, D = d["x"].shape
+    N = d["A"].shape[1]
+    d["dy"] = rng.standard_normal((b, L, D))
+    d["dh_out"] = rng.standard_normal((b, D, N))
+    return d
+
+
 def m1_fused(seed=110, batch=8, L=2048, D=1536, N=16, K=4):
     return m1_block_inputs(np.random.default_rng(seed), batch, L, D, N, K)

@@ -34,7 +34,7 @@ def declared_functions():
 def test_exports_every_declared_function(lib):
     names = declared_functions()
     assert {"mb_selective_scan", "mb_ssm_step", "mb_ssd_chunked", "mb_trap_ssd", "mb_mimo_ssd",
-            "mb_ssd_step", "mb_selective_scan_fused", "mb_ssd_chunked_bwd", "mb_workspace_size", "mb_status_str", "mb_last_hip_error", "mb_version"} <= set(names)
+            "mb_ssd_step", "mb_selective_scan_fused", "mb_ssd_chunked_bwd", "mb_selective_scan_bwd", "mb_workspace_size", "mb_status_str", "mb_last_hip_error", "mb_version"} <= set(names)
     for n in names:
         assert hasattr(lib, n), "libmb.so does not export " + n
 
@@ -192,6 +192,33 @@ def test_ssd_bwd_validation(lib):
     assert need >= 2 * 4 * 2 * 2 * 128 * 64 * 4
     assert mb.mb_workspace_size(mb.MB_OP_SSD_CHUNKED_BWD, 2, 100, 4, 48, 1, 128) == 0
     assert mb.mb_workspace_size(mb.MB_OP_SSD_CHUNKED_BWD, 2, 0, 4, 64, 1, 128) == 0
+
+
+def m1_bwd(lib, x=FAKE, dy=FAKE + (1 << 24), dx=FAKE + (1 << 25), dB=FAKE + (1 << 26), dh0=None,
+           ws=FAKE + (1 << 28), ws_bytes=1 << 30, L=100, Dm=64, N=16, batch=2, dtype=F32):
+    q = lambda v: P(v) if v else None
+    return lib.mb_selective_scan_bwd(q(x), P(FAKE + (1 << 22)), P(FAKE + (1 << 23)), P(FAKE + (1 << 23) + (1 << 20)),
+                                     P(FAKE + (1 << 23) + (1 << 21)), None, None, q(dy), None, q(dx),
+                                     P(FAKE + (1 << 25) + (1 << 21)), P(FAKE + (1 << 27)), q(dB),
+                                     P(FAKE + (1 << 26) + (1 << 21)), None, q(dh0), batch, L, Dm, N, dtype, q(ws),
+                                     ws_bytes, None)
+
+
+def test_m1_bwd_validation(lib):
+    assert m1_bwd(lib, dtype=BF16) == E_DTYPE
+    assert m1_bwd(lib, N=32) == E_SHAPE
+    assert m1_bwd(lib, N=6) == E_SHAPE
+    assert m1_bwd(lib, x=0) == E_NULL
+    assert m1_bwd(lib, dB=0) == E_NULL
+    assert m1_bwd(lib, dy=FAKE + (1 << 24) + 4) == E_ALIGN
+    assert m1_bwd(lib, dx=FAKE + 64) == E_ALIAS                       # dx over x
+    assert m1_bwd(lib, dh0=FAKE + (1 << 25) + 512) == E_ALIAS          # dh0 over dx
+    assert m1_bwd(lib, ws=0) == E_WS
+    assert m1_bwd(lib, ws_bytes=4096) == E_WS
+    assert m1_bwd(lib, ws=FAKE + (1 << 28) + 64) == E_WS
+    need = mb.mb_workspace_size(mb.MB_OP_SELECTIVE_SCAN_BWD, 2, 100, 64, 1, 1, 16)
+    assert need >= 2 * 4 * 64 * 16 * 4
+    assert mb.mb_workspace_size(mb.MB_OP_SELECTIVE_SCAN_BWD, 2, 100, 64, 1, 1, 32) == 0
 
 
 def test_trap_and_mimo_validation(lib):
