@@ -428,6 +428,193 @@ void oracle_trap(const double *X, const double *logdecay, const double *B,
 }
 
 /*
+ * Backward (vector-Jacobian product) of the Mamba-3 SISO recurrence above, by
+ * back-propagation through time in the rotated frame (the mamba-rs page lists
+ * training by back-propagation through time).  Given dY (b, L, H, P) and dh_out
+ * (b, H, N, P) or NULL, it returns the gradients of sum dY . Y + sum dh_out . h_out
+ * with respect to X, logdecay, B, C, beta, gamma, theta, h0, X_prev0, B_prev0.
+ * With A the adjoint of the rotated state, starting from R(Theta_{L-1}) dh_out
+ * (h_out = R(-Theta_{L-1}) S_{L-1}) and walking t = L-1 .. 0:
+ *     A += Ct_t dY_t^T                                   (now d/dS_t)
+ *     dCt_t = S_t dY_t
+ *     dgamma_t = X_t . (A^T Bt_t),   dX_t += gamma_t A^T Bt_t,   dBt_t += gamma_t A X_t
+ *     dbeta_t = X_{t-1} . (A^T Bt_{t-1}),  dX_{t-1} += beta_t A^T Bt_{t-1},
+ *                                          dBt_{t-1} += beta_t A X_{t-1}
+ *     dld_t = e^{ld_t} <A, S_{t-1}>,   A = e^{ld_t} A    (now d/dS_{t-1})
+ * and dh0 = A.  The rotated gradients return to the physical frame, dB_t =
+ * R(-Theta_t) dBt_t (likewise C), and give the angle gradient: per pair k,
+ * dTheta_t = (Bt0 dBt1 - Bt1 dBt0) + (Ct0 dCt1 - Ct1 dCt0), plus at t = L-1 the
+ * rotation of h_out, sum_p (dh_out0 h_out1 - dh_out1 h_out0); dtheta_t is the sum
+ * of dTheta over steps >= t.  Step -1 (X_prev0, B_prev0) is unrotated.  dB, dC
+ * and dB_prev0 sum over the heads of a group.  Forward states are kept for every
+ * step.  theta == NULL: no rotation (dtheta untouched).
+ */
+void oracle_trap_bwd(const double *X, const double *logdecay, const double *B,
+                     const double *C, const double *beta, const double *gamma,
+                     const double *theta, const double *h0, const double *X_prev0,
+                     const double *B_prev0, const double *dY, const double *dh_out,
+                     double *dX, double *dld, double *dB, double *dC, double *dbeta,
+                     double *dgamma, double *dtheta, double *dh0, double *dX_prev0,
+                     double *dB_prev0, int64_t batch, int64_t L, int64_t H, int64_t P,
+                     int64_t G, int64_t N)
+{
+    int64_t hpg = H / G;
+    int64_t K = N / 2;
+    int64_t NP = N * P;
+    int64_t units = batch * G;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t u = 0; u < units; ++u) {
+        int64_t b = u / G, g = u % G;
+        for (int64_t t = 0; t < L; ++t)
+            for (int64_t n = 0; n < N; ++n) {
+                dB[((b * L + t) * G + g) * N + n] = 0.0;
+                dC[((b * L + t) * G + g) * N + n] = 0.0;
+            }
+        if (dB_prev0)
+            for (int64_t n = 0; n < N; ++n) dB_prev0[(b * G + g) * N + n] = 0.0;
+        double *S = (double *)malloc(sizeof(double) * (size_t)((L + 1) * NP > 0 ? (L + 1) * NP : 1));
+        double *Bt = (double *)malloc(sizeof(double) * (size_t)((L + 1) * N > 0 ? (L + 1) * N : 1));
+        double *Ct = (double *)malloc(sizeof(double) * (size_t)(L * N > 0 ? L * N : 1));
+        double *Th = (double *)calloc((size_t)(L * K > 0 ? L * K : 1), sizeof(double));
+        double *A = (double *)malloc(sizeof(double) * (size_t)(NP > 0 ? NP : 1));
+        double *dBt = (double *)malloc(sizeof(double) * (size_t)((L + 1) * N > 0 ? (L + 1) * N : 1));
+        double *dCt = (double *)malloc(sizeof(double) * (size_t)(L * N > 0 ? L * N : 1));
+        double *Xp = (double *)calloc((size_t)(P > 0 ? P : 1), sizeof(double));
+        double *dXp = (double *)malloc(sizeof(double) * (size_t)(P > 0 ? P : 1));
+        double *dTh = (double *)malloc(sizeof(double) * (size_t)(L * K > 0 ? L * K : 1));
+        for (int64_t h = g * hpg; h < (g + 1) * hpg; ++h) {
+            /* rotated B (Bt + N: step t at Bt[(t + 1) N], step -1 at Bt[0]) and C */
+            for (int64_t n = 0; n < N; ++n) Bt[n] = B_prev0 ? B_prev0[(b * G + g) * N + n] : 0.0;
+            for (int64_t t = 0; t < L; ++t) {
+                int64_t bth = (b * L + t) * H + h;
+                for (int64_t k = 0; k < K; ++k)
+                    Th[t * K + k] = (t ? Th[(t - 1) * K + k] : 0.0) + (theta ? theta[bth * K + k] : 0.0);
+                const double *Bs = B + ((b * L + t) * G + g) * N, *Cs = C + ((b * L + t) * G + g) * N;
+                if (theta) {
+                    rotate_pairs(Bt + (t + 1) * N, Bs, Th + t * K, N, 1, 1.0);
+                    rotate_pairs(Ct + t * N, Cs, Th + t * K, N, 1, 1.0);
+                } else {
+                    memcpy(Bt + (t + 1) * N, Bs, sizeof(double) * (size_t)N);
+                    memcpy(Ct + t * N, Cs, sizeof(double) * (size_t)N);
+                }
+            }
+            for (int64_t p = 0; p < P; ++p) Xp[p] = X_prev0 ? X_prev0[(b * H + h) * P + p] : 0.0;
+            /* forward states: S + (t + 1) NP = S_t, S = S_{-1} = h0 */
+            for (int64_t i = 0; i < NP; ++i) S[i] = h0 ? h0[(b * H + h) * NP + i] : 0.0;
+            for (int64_t t = 0; t < L; ++t) {
+                int64_t bth = (b * L + t) * H + h;
+                double a = exp(logdecay[bth]), be = beta[bth], ga = gamma[bth];
+                const double *Xt = X + bth * P, *Xq = t ? X + (bth - H) * P : Xp;
+                const double *Bc = Bt + (t + 1) * N, *Bq = Bt + t * N;
+                const double *Sp = S + t * NP;
+                double *Sc = S + (t + 1) * NP;
+                for (int64_t n = 0; n < N; ++n)
+                    for (int64_t p = 0; p < P; ++p)
+                        Sc[n * P + p] = a * Sp[n * P + p] + be * Bq[n] * Xq[p] + ga * Bc[n] * Xt[p];
+            }
+            /* adjoint start: A = R(Theta_{L-1}) dh_out; rotation term of h_out */
+            for (int64_t i = 0; i < L * K; ++i) dTh[i] = 0.0;
+            for (int64_t i = 0; i < (L + 1) * N; ++i) dBt[i] = 0.0;
+            for (int64_t p = 0; p < P; ++p) dXp[p] = 0.0;
+            for (int64_t i = 0; i < NP; ++i) A[i] = dh_out ? dh_out[(b * H + h) * NP + i] : 0.0;
+            if (theta && L > 0 && dh_out) {
+                const double *dh = dh_out + (b * H + h) * NP, *Sl = S + L * NP;
+                const double *thl = Th + (L - 1) * K;
+                for (int64_t k = 0; k < K; ++k) {
+                    double cs = cos(thl[k]), sn = sin(thl[k]), acc = 0.0;
+                    for (int64_t p = 0; p < P; ++p) {
+                        double s0 = Sl[(2 * k) * P + p], s1 = Sl[(2 * k + 1) * P + p];
+                        double o0 = cs * s0 + sn * s1, o1 = -sn * s0 + cs * s1;   /* h_out */
+                        acc += dh[(2 * k) * P + p] * o1 - dh[(2 * k + 1) * P + p] * o0;
+                    }
+                    dTh[(L - 1) * K + k] += acc;
+                }
+                for (int64_t p = 0; p < P; ++p) rotate_pairs(A + p, dh + p, thl, N, P, 1.0);
+            }
+            for (int64_t t = L - 1; t >= 0; --t) {
+                int64_t bth = (b * L + t) * H + h;
+                double a = exp(logdecay[bth]), be = beta[bth], ga = gamma[bth];
+                const double *Xt = X + bth * P, *Xq = t ? X + (bth - H) * P : Xp;
+                const double *Bc = Bt + (t + 1) * N, *Bq = Bt + t * N, *Cc = Ct + t * N;
+                const double *dYt = dY + bth * P;
+                const double *Sc = S + (t + 1) * NP, *Sp = S + t * NP;
+                double *dXq = t ? dX + (bth - H) * P : dXp;
+                for (int64_t n = 0; n < N; ++n)
+                    for (int64_t p = 0; p < P; ++p) A[n * P + p] += Cc[n] * dYt[p];
+                for (int64_t n = 0; n < N; ++n) {
+                    double s = 0.0;
+                    for (int64_t p = 0; p < P; ++p) s += Sc[n * P + p] * dYt[p];
+                    dCt[t * N + n] = s;
+                }
+                double sg = 0.0, sb = 0.0;
+                if (t == L - 1)
+                    for (int64_t p = 0; p < P; ++p) dX[bth * P + p] = 0.0;
+                for (int64_t p = 0; p < P; ++p) {
+                    double vc = 0.0, vq = 0.0;
+                    for (int64_t n = 0; n < N; ++n) {
+                        vc += A[n * P + p] * Bc[n];
+                        vq += A[n * P + p] * Bq[n];
+                    }
+                    sg += Xt[p] * vc;
+                    sb += Xq[p] * vq;
+                    dX[bth * P + p] += ga * vc;
+                    /* step t - 1's slot is first written here (walking down) */
+                    dXq[p] = be * vq;
+                }
+                for (int64_t n = 0; n < N; ++n) {
+                    double vc = 0.0, vq = 0.0;
+                    for (int64_t p = 0; p < P; ++p) {
+                        vc += A[n * P + p] * Xt[p];
+                        vq += A[n * P + p] * Xq[p];
+                    }
+                    dBt[(t + 1) * N + n] += ga * vc;
+                    dBt[t * N + n] += be * vq;
+                }
+                dgamma[bth] = sg;
+                dbeta[bth] = sb;
+                double sl = 0.0;
+                for (int64_t i = 0; i < NP; ++i) sl += A[i] * Sp[i];
+                dld[bth] = a * sl;
+                for (int64_t i = 0; i < NP; ++i) A[i] *= a;
+            }
+            /* back to the physical frame; the angle gradient */
+            for (int64_t t = 0; t < L; ++t) {
+                const double *bt = Bt + (t + 1) * N, *dbt = dBt + (t + 1) * N;
+                const double *ct = Ct + t * N, *dct = dCt + t * N;
+                double pb[2], pc[2];
+                for (int64_t k = 0; k < K; ++k) {
+                    if (theta)
+                        dTh[t * K + k] += (bt[2 * k] * dbt[2 * k + 1] - bt[2 * k + 1] * dbt[2 * k]) +
+                                          (ct[2 * k] * dct[2 * k + 1] - ct[2 * k + 1] * dct[2 * k]);
+                    double phi = theta ? -Th[t * K + k] : 0.0;
+                    rotate_pairs(pb, dbt + 2 * k, &phi, 2, 1, 1.0);
+                    rotate_pairs(pc, dct + 2 * k, &phi, 2, 1, 1.0);
+                    dB[((b * L + t) * G + g) * N + 2 * k] += pb[0];
+                    dB[((b * L + t) * G + g) * N + 2 * k + 1] += pb[1];
+                    dC[((b * L + t) * G + g) * N + 2 * k] += pc[0];
+                    dC[((b * L + t) * G + g) * N + 2 * k + 1] += pc[1];
+                }
+            }
+            if (theta)
+                for (int64_t k = 0; k < K; ++k) {
+                    double acc = 0.0;
+                    for (int64_t t = L - 1; t >= 0; --t) {
+                        acc += dTh[t * K + k];
+                        dtheta[((b * L + t) * H + h) * K + k] = acc;
+                    }
+                }
+            if (dh0)
+                for (int64_t i = 0; i < NP; ++i) dh0[(b * H + h) * NP + i] = A[i];
+            if (dX_prev0)
+                for (int64_t p = 0; p < P; ++p) dX_prev0[(b * H + h) * P + p] = L ? dXp[p] : 0.0;
+            if (dB_prev0)
+                for (int64_t n = 0; n < N; ++n) dB_prev0[(b * G + g) * N + n] += dBt[n];
+        }
+        free(S); free(Bt); free(Ct); free(Th); free(A); free(dBt); free(dCt); free(Xp); free(dXp); free(dTh);
+    }
+}
+
+/*
  * Mamba-3 MIMO rank-R recurrence (TorchMamba README, "Models" table row
  * Mamba-3 MIMO and "Math notes" MIMO bullet: the outer product B x^T becomes a
  * rank-R matrix product on one shared (N, P) state).  Per (b, h):

@@ -65,6 +65,11 @@ MUTATIONS = {
     "m1bwd_adjoint_not_decayed": ("                    G[n] *= a;\n", ""),
     "m1bwd_dB_before_adjoint_update": ("                    G[n] += Ct[n] * dyv;\n                    dC[(b * L + t) * N + n] += ht[n] * dyv;\n                    dB[(b * L + t) * N + n] += G[n] * dtv * xv;",
                                        "                    dB[(b * L + t) * N + n] += G[n] * dtv * xv;\n                    G[n] += Ct[n] * dyv;\n                    dC[(b * L + t) * N + n] += ht[n] * dyv;"),
+    "trapbwd_dbeta_uses_current_x": ("sb += Xq[p] * vq;", "sb += Xt[p] * vq;"),
+    "trapbwd_angle_sign": ("(bt[2 * k] * dbt[2 * k + 1] - bt[2 * k + 1] * dbt[2 * k])",
+                           "(bt[2 * k + 1] * dbt[2 * k] - bt[2 * k] * dbt[2 * k + 1])"),
+    "trapbwd_no_hout_rotation_term": ("dTh[(L - 1) * K + k] += acc;", ""),
+    "trapbwd_unrotate_wrong_way": ("double phi = theta ? -Th[t * K + k] : 0.0;", "double phi = theta ? Th[t * K + k] : 0.0;"),
 }
 
 
@@ -159,6 +164,24 @@ def _battery(o):
         fd = (lossm(dict(inp, **{k: inp[k] + 1e-6 * v})) - lossm(dict(inp, **{k: inp[k] - 1e-6 * v}))) / 2e-6
         if abs(fd - float(np.sum(gk * v))) > 1e-6 * max(1.0, abs(fd)):
             failed.append("m1_bwd_directional_" + k)
+
+    # backward of the SISO recurrence: directional derivatives of the forward loss
+    inp = wl.trap_inputs(rng, 1, 9, 2, 3, 4, G=1, h0_sd=0.4)
+    inp["X_prev"] = rng.standard_normal((1, 2, 3))
+    inp["B_prev"] = rng.standard_normal((1, 1, 4))
+    dY = rng.standard_normal(inp["X"].shape)
+    dh = rng.standard_normal(inp["h0"].shape)
+
+    def losst(d):
+        Yf, hf = o.trap(**d)
+        return float(np.sum(Yf * dY) + np.sum(hf * dh))
+    gr = o.trap_bwd(inp["X"], inp["logdecay"], inp["B"], inp["C"], inp["beta"], inp["gamma"], dY, inp["theta"],
+                    inp["h0"], dh, inp["X_prev"], inp["B_prev"])
+    for k, gk in zip(("X", "logdecay", "B", "C", "beta", "gamma", "theta", "h0", "X_prev", "B_prev"), gr):
+        v = rng.standard_normal(inp[k].shape)
+        fd = (losst(dict(inp, **{k: inp[k] + 1e-6 * v})) - losst(dict(inp, **{k: inp[k] - 1e-6 * v}))) / 2e-6
+        if abs(fd - float(np.sum(gk * v))) > 1e-6 * max(1.0, abs(fd)):
+            failed.append("trap_bwd_directional_" + k)
 
     inp = wl.m1_block_inputs(rng, 2, 15, 3, 4, K=4, h0_sd=0.3, hist=True)
     y, h = o.m1_block(**inp)
