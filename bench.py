@@ -105,6 +105,18 @@ def ssd_bwd_work(b, L, H, P, N, G, Q=64):
     return nbytes, flops
 
 
+def siso_bwd_work(b, L, H, P, N, G, Q=64):
+    """Backward of the Mamba-3 SISO recurrence: inputs X, dY, B, C, logdecay,
+    beta, gamma, theta, dh_out read and their gradients written once; flops of
+    the chunkwise form of the two-term (trapezoid) SSD at Q = 64: local states
+    (6NP), the state products for both terms (10NP), the scores and masked
+    products of both terms (4P(Q+1) + 6N(Q+1)).  The library runs it as a
+    one-term SSD over 2L interleaved steps (about 17% more flops)."""
+    nbytes = 4 * (4 * b * L * H * P + 4 * b * L * G * N + 6 * b * L * H + b * L * H * N + 2 * b * H * N * P)
+    flops = b * L * H * (16 * N * P + 4 * P * (Q + 1) + 6 * N * (Q + 1))
+    return nbytes, flops
+
+
 def ssd_step_work(b, H, P, N, G, R, trap, rot, es=4):
     """One decode token: the fp32 state read and written once, plus the token's
     inputs and output."""
@@ -310,6 +322,33 @@ class SSDBwd(Workload):
                                    **self.out)
 
 
+class SISOBwd(Workload):
+    """Backward of the Mamba-3 SISO recurrence at the block shape (outside the
+    step, measured beside it)."""
+    name = "siso_bwd"
+    kernel = "angle and interleave kernels + the SSD backward over 2L steps + the mapping back"
+    source = "selective_state_space_amd/csrc/ssd_bwd.hip"
+    bound = "mfma"
+
+    def __init__(self, mb, wl, torch):
+        self.mb = mb
+        b, L, H, P, N, G = 4, 4096, 24, 64, 128, 1
+        self.shape = dict(batch=b, L=L, H=H, P=P, N=N, G=G, trapezoid=True, rotation=True)
+        inp = wl.siso_bwd_block()
+        self.inp = inp
+        self.t = {k: _dev(v, torch.float32) for k, v in inp.items() if v is not None}
+        self.ws = torch.empty(mb.mb_workspace_size(mb.MB_OP_TRAP_SSD_BWD, b, L, H, P, G, N),
+                              dtype=torch.uint8, device="cuda")
+        self.tokens = b * L
+        self.bytes, self.flops = siso_bwd_work(b, L, H, P, N, G)
+        self.exps = None
+
+    def run(self):
+        t = self.t
+        self.mb.mb_trap_ssd_bwd(t["X"], t["logdecay"], t["B"], t["C"], t["beta"], t["gamma"], t["dY"], t["theta"],
+                                None, t["dh_out"], ws=self.ws)
+
+
 class SISO(Workload):
     name = "siso"
     kernel = "k_walk (state-only pass) + k_walk (full pass)"
@@ -398,8 +437,8 @@ class SSDDecode(Workload):
 ALL = ["m1_scan", "m1_step", "ssd_f32", "ssd_bf16", "siso", "mimo"]
 # measured beside the step, not part of it: the decode steps of the SSD family, the
 # Mamba-1 scan with the block prologue and epilogue fused, and the backwards of the
-# Mamba-2 SSD and the Mamba-1 scan
-NEXT = ["m2_decode", "siso_decode", "mimo_decode", "m1_fused", "ssd_bwd", "m1_bwd"]
+# Mamba-2 SSD, the Mamba-1 scan and Mamba-3 SISO
+NEXT = ["m2_decode", "siso_decode", "mimo_decode", "m1_fused", "ssd_bwd", "m1_bwd", "siso_bwd"]
 
 
 def make(name, mb, wl, torch):
@@ -413,6 +452,8 @@ def make(name, mb, wl, torch):
         return SSDBwd(mb, wl, torch)
     if name == "m1_bwd":
         return M1Bwd(mb, wl, torch)
+    if name == "siso_bwd":
+        return SISOBwd(mb, wl, torch)
     if name == "ssd_f32":
         return SSD(mb, wl, torch, "f32")
     if name == "ssd_bf16":
@@ -513,7 +554,7 @@ def cold_ms(torch, w, reps=5):
 
 
 def time_next(args, mb, wl, torch):
-    """Decode steps of the SSD family, the fused Mamba-1 block scan and the two
+    """Decode steps of the SSD family, the fused Mamba-1 block scan and the
     backwards, timed with
     HIP events on the stream they run on, outside the step (they are not part of
     its token count)."""

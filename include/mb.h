@@ -62,7 +62,8 @@ typedef enum {
     MB_OP_TRAP_SSD = 3,
     MB_OP_MIMO_SSD = 4,
     MB_OP_SSD_CHUNKED_BWD = 5,
-    MB_OP_SELECTIVE_SCAN_BWD = 6
+    MB_OP_SELECTIVE_SCAN_BWD = 6,
+    MB_OP_TRAP_SSD_BWD = 7
 } mb_op;
 
 /*
@@ -278,6 +279,38 @@ mb_status mb_selective_scan_bwd(const float* x, const float* dt, const float* A,
                                 float* dA, float* dB, float* dC, float* dD, float* dh0,
                                 int64_t batch, int64_t L, int64_t D, int64_t N, mb_dtype dtype,
                                 void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Backward of mb_trap_ssd (fp32): the vector-Jacobian product of the Mamba-3
+ * SISO recurrence (TorchMamba README, Math notes M3 SISO; trained by
+ * back-propagation through time, as the mamba-rs page lists).  Given dY and
+ * dh_out (NULL = zero), returns the gradients of  sum dY . Y + sum dh_out . h_out
+ * with respect to X, logdecay, B, C, beta, gamma, theta, h0 and the previous
+ * token X_prev, B_prev.  In the rotated frame, with A the adjoint of the state
+ * (A = R(Theta_{L-1}) dh_out at the end, since h_out = R(-Theta_{L-1}) S_{L-1}):
+ *     A += Ct_t dY_t^T;  dgamma_t = X_t . A^T Bt_t;  dbeta_t = X_{t-1} . A^T Bt_{t-1};
+ *     dX, dBt, dCt from both trapezoid terms;  dlogdecay_t = e^{ld_t} <A, S_{t-1}>;
+ *     A = e^{ld_t} A
+ * then dB_t = R(-Theta_t) dBt_t (likewise C, summed over the group's heads), and
+ * dtheta_t = sum over steps >= t of the angle gradient of the rotations (and of
+ * h_out at the last step).  dh0 is the adjoint before the first step.
+ * Arguments as mb_trap_ssd, gradients shaped like their inputs; theta NULL = no
+ * rotation (dtheta not written); X_prev, B_prev both given or both NULL;
+ * dh0, dX_prev, dB_prev NULL = not wanted.
+ * ws / ws_bytes: device workspace of at least
+ * mb_workspace_size(MB_OP_TRAP_SSD_BWD, ...) bytes, 256-byte aligned.
+ * Supported: dtype MB_F32 (MB_ERR_DTYPE otherwise); N in {64, 128}, P in
+ * {32, 64} (MB_ERR_SHAPE otherwise); X, B, C, dY, dX, dB, dC, h0, dh_out, dh0,
+ * X_prev, B_prev, dB_prev 16-byte aligned (MB_ERR_ALIGN).  No output may overlap
+ * an input, another output or the workspace (MB_ERR_ALIAS).
+ */
+mb_status mb_trap_ssd_bwd(const float* X, const float* logdecay, const float* B, const float* C,
+                          const float* beta, const float* gamma, const float* theta, const float* h0,
+                          const float* X_prev, const float* B_prev, const float* dY,
+                          const float* dh_out, float* dX, float* dlogdecay, float* dB, float* dC,
+                          float* dbeta, float* dgamma, float* dtheta, float* dh0, float* dX_prev,
+                          float* dB_prev, int64_t batch, int64_t L, int64_t H, int64_t P, int64_t G,
+                          int64_t N, mb_dtype dtype, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * Backward of mb_ssd_chunked (fp32): the vector-Jacobian product of the Mamba-2

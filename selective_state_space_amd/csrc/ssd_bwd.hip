@@ -65,6 +65,7 @@ struct BwdArgs {
     float* lam;             // workspace: per (b, h, c) total log-decay of the chunk
     float* tot;             // workspace: per (b, h, c) the sum of dl over the chunk
     float* fin;             // workspace: per (b, h) partial sums of <dh_out, h_out>
+    float* h_final;         // optional output: (batch, H, N, P) the final state
     int L, H, G, N, P, nch, nfin;
 };
 
@@ -268,6 +269,7 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_pass(BwdArgs a) {
             hs.w = fmaf(d[k], hs.w, u[k].w);
         }
     }
+    if (ok && a.h_final) *(float4*)(a.h_final + (size_t)bh * NP + ee) = hs;
     const float4 dh = (ok && a.dh_out) ? *(const float4*)(a.dh_out + (size_t)bh * NP + ee) : z4;
     // partial sum of <dh_out, h_out> over this block
     {
@@ -707,4 +709,378 @@ extern "C" mb_status mb_ssd_chunked_bwd(const float* X, const float* logdecay, c
     if (N == 128)
         return P == 64 ? bwd_launch<128, 64>(a, batch, stream) : bwd_launch<128, 32>(a, batch, stream);
     return P == 64 ? bwd_launch<64, 64>(a, batch, stream) : bwd_launch<64, 32>(a, batch, stream);
+}
+
+// ===========================================================================
+// Backward of the Mamba-3 SISO recurrence (mb_trap_ssd_bwd), through the SSD
+// backward above.  In the rotated frame the trapezoid step
+//     S_t = e^{ld_t} S_{t-1} + beta_t Bt_{t-1} X_{t-1}^T + gamma_t Bt_t X_t^T
+// is two SSD steps: pseudo-step 2t decays by e^{ld_t} and adds
+// Bt_{t-1} (beta_t X_{t-1})^T with no output, pseudo-step 2t + 1 does not decay
+// and adds Bt_t (gamma_t X_t)^T with the output Y_t = S^T Ct_t.  The SSD
+// backward runs on that interleaved sequence (2L steps, every head its own
+// group, per-head rotated B and C) from the rotated dh_out, and these kernels
+// map its gradients back: dX, dbeta, dgamma from the two pseudo-steps, dB and dC
+// rotated back to the physical frame and summed over the group's heads, and the
+// angle gradient per pair (Bt0 dBt1 - Bt1 dBt0 + Ct0 dCt1 - Ct1 dCt0, plus the
+// rotation of h_out at the last step) summed over later steps.
+// ===========================================================================
+namespace mb {
+namespace {
+
+struct TrapBwd {
+    const float *X, *ld, *B, *C, *beta, *gamma, *theta, *Xp, *Bp, *dY, *dh_out;
+    float *dX, *dld, *dB, *dC, *dbeta, *dgamma, *dtheta, *dXp, *dBp;
+    // workspace
+    float *X2, *dY2, *B2, *C2, *ld2;          // the interleaved inputs (2L steps)
+    float *dX2, *dld2, *dB2, *dC2;            // their gradients
+    float *Th, *dTh;                          // (batch, L, H, K) angles (as the fraction of a
+                                              // revolution) and angle gradients
+    float *seg, *hterm, *dh2, *hfin;          // segment sums, h_out term, rotated dh_out, final state
+    int L, H, G, N, P, nseg;
+};
+
+constexpr int kSeg = 64;   // steps per segment of the angle sums
+
+// sin and cos of an angle given as the fraction of a revolution (|f| <= 0.5)
+__device__ __forceinline__ void sincos_frac(float f, float* sn, float* cs) {
+    *sn = __builtin_amdgcn_sinf(f);
+    *cs = __builtin_amdgcn_cosf(f);
+}
+
+// sum of theta over each 64-step segment: one wave per (batch, head, segment),
+// lane k = pair
+__global__ __launch_bounds__(64) void k_tb_segsum(TrapBwd a, const float* v, float* out) {
+    const int sg = blockIdx.x % a.nseg, bh = blockIdx.x / a.nseg;
+    const int b = bh / a.H, h = bh % a.H, K = a.N / 2, k = threadIdx.x;
+    if (k >= K) return;
+    float s = 0.0f;
+    const int t1 = min(a.L, (sg + 1) * kSeg);
+    for (int t = sg * kSeg; t < t1; ++t) s += v[(((size_t)b * a.L + t) * a.H + h) * K + k];
+    out[((size_t)bh * a.nseg + sg) * K + k] = s;
+}
+
+// angles Theta_t (prefix sums of theta), the per-head rotated B and C of both
+// pseudo-steps, and the angles for the mapping back
+__global__ __launch_bounds__(64) void k_tb_prep_bc(TrapBwd a) {
+    const int sg = blockIdx.x % a.nseg, bh = blockIdx.x / a.nseg;
+    const int b = bh / a.H, h = bh % a.H, g = h / (a.H / a.G), K = a.N / 2, k = threadIdx.x;
+    if (k >= K) return;
+    // the cumulative angle reaches hundreds of radians: it is summed in fp64 and
+    // kept as the fraction of a revolution
+    double th = 0.0;
+    if (a.theta)
+        for (int s2 = 0; s2 < sg; ++s2) th += (double)a.seg[((size_t)bh * a.nseg + s2) * K + k];
+    const size_t L2 = 2 * (size_t)a.L;
+    auto row = [&](float* base, size_t t2) { return base + (((size_t)b * L2 + t2) * a.H + h) * a.N + 2 * k; };
+    if (sg == 0) {
+        // pseudo-step 0: the previous token, unrotated; no output
+        const float2 bp = a.Bp ? *(const float2*)(a.Bp + ((size_t)b * a.G + g) * a.N + 2 * k) : make_float2(0.0f, 0.0f);
+        *(float2*)row(a.B2, 0) = bp;
+        *(float2*)row(a.C2, 0) = make_float2(0.0f, 0.0f);
+    }
+    const int t1 = min(a.L, (sg + 1) * kSeg);
+    for (int t = sg * kSeg; t < t1; ++t) {
+        const size_t bth = ((size_t)b * a.L + t) * a.H + h;
+        if (a.theta) th += (double)a.theta[bth * K + k];
+        const double r = th * 0.15915494309189535;
+        const float f = (float)(r - rint(r));
+        a.Th[bth * K + k] = f;
+        float sn, cs;
+        sincos_frac(f, &sn, &cs);
+        const float2 bv = *(const float2*)(a.B + (((size_t)b * a.L + t) * a.G + g) * a.N + 2 * k);
+        const float2 cv = *(const float2*)(a.C + (((size_t)b * a.L + t) * a.G + g) * a.N + 2 * k);
+        const float2 br = make_float2(cs * bv.x - sn * bv.y, sn * bv.x + cs * bv.y);
+        const float2 cr = make_float2(cs * cv.x - sn * cv.y, sn * cv.x + cs * cv.y);
+        *(float2*)row(a.B2, 2 * (size_t)t + 1) = br;
+        *(float2*)row(a.C2, 2 * (size_t)t + 1) = cr;
+        if (t + 1 < a.L) {
+            *(float2*)row(a.B2, 2 * (size_t)t + 2) = br;
+            *(float2*)row(a.C2, 2 * (size_t)t + 2) = make_float2(0.0f, 0.0f);
+        }
+    }
+}
+
+// the interleaved X, dY and log-decay: one thread per (batch, step, head, 4 columns)
+__global__ __launch_bounds__(256) void k_tb_prep_x(TrapBwd a) {
+    const int P4 = a.P / 4;
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int b = blockIdx.y;
+    if (i >= (int64_t)a.L * a.H * P4) return;
+    const int p4 = (int)(i % P4);
+    const int64_t th = i / P4;              // t * H + h
+    const int h = (int)(th % a.H), t = (int)(th / a.H);
+    const size_t bth = (size_t)b * a.L * a.H + th;
+    const float4 z4 = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    const float4 xt = *(const float4*)(a.X + bth * a.P + 4 * p4);
+    const float4 xq = t > 0 ? *(const float4*)(a.X + (bth - a.H) * a.P + 4 * p4)
+                            : (a.Xp ? *(const float4*)(a.Xp + ((size_t)b * a.H + h) * a.P + 4 * p4) : z4);
+    const float be = a.beta[bth], ga = a.gamma[bth];
+    const size_t r0 = ((size_t)b * 2 * a.L + 2 * (size_t)t) * a.H + h, r1 = r0 + a.H;
+    *(float4*)(a.X2 + r0 * a.P + 4 * p4) = make_float4(be * xq.x, be * xq.y, be * xq.z, be * xq.w);
+    *(float4*)(a.X2 + r1 * a.P + 4 * p4) = make_float4(ga * xt.x, ga * xt.y, ga * xt.z, ga * xt.w);
+    *(float4*)(a.dY2 + r0 * a.P + 4 * p4) = z4;
+    *(float4*)(a.dY2 + r1 * a.P + 4 * p4) = *(const float4*)(a.dY + bth * a.P + 4 * p4);
+    if (p4 == 0) {
+        a.ld2[r0] = a.ld[bth];
+        a.ld2[r1] = 0.0f;
+    }
+}
+
+// dh_out in the rotated frame, R(Theta_{L-1}) dh_out: one thread per (b, h, pair, column)
+__global__ __launch_bounds__(256) void k_tb_rot_dh(TrapBwd a) {
+    const int K = a.N / 2;
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t per = (int64_t)K * a.P;
+    const int bh = blockIdx.y;
+    if (i >= per) return;
+    const int k = (int)(i / a.P), p = (int)(i % a.P);
+    const int b = bh / a.H, h = bh % a.H;
+    const float th = a.theta ? a.Th[(((size_t)b * a.L + a.L - 1) * a.H + h) * K + k] : 0.0f;
+    float sn, cs;
+    sincos_frac(th, &sn, &cs);
+    const float* src = a.dh_out + (size_t)bh * a.N * a.P;
+    float* dst = a.dh2 + (size_t)bh * a.N * a.P;
+    const float v0 = src[(2 * k) * a.P + p], v1 = src[(2 * k + 1) * a.P + p];
+    dst[(2 * k) * a.P + p] = cs * v0 - sn * v1;
+    dst[(2 * k + 1) * a.P + p] = sn * v0 + cs * v1;
+}
+
+// dX, dgamma, dbeta, dlogdecay: one wave per (batch, step, head), lane = column
+__global__ __launch_bounds__(64) void k_tb_post_x(TrapBwd a) {
+    const int64_t bth = blockIdx.x;
+    const int h = (int)(bth % a.H);
+    const int t = (int)((bth / a.H) % a.L), b = (int)(bth / ((int64_t)a.H * a.L));
+    const int p = threadIdx.x;
+    const bool ok = p < a.P;
+    const size_t r0 = ((size_t)b * 2 * a.L + 2 * (size_t)t) * a.H + h, r1 = r0 + a.H, r2 = r1 + a.H;
+    const float d1 = ok ? a.dX2[r1 * a.P + p] : 0.0f;          // d(gamma_t X_t)
+    const float d0 = ok ? a.dX2[r0 * a.P + p] : 0.0f;          // d(beta_t X_{t-1})
+    const float xt = ok ? a.X[bth * a.P + p] : 0.0f;
+    const float xq = !ok ? 0.0f : t > 0 ? a.X[(bth - a.H) * a.P + p] : (a.Xp ? a.Xp[((size_t)b * a.H + h) * a.P + p] : 0.0f);
+    const float be_next = t + 1 < a.L ? a.beta[bth + a.H] : 0.0f;
+    const float dnext = (ok && t + 1 < a.L) ? a.dX2[r2 * a.P + p] : 0.0f;   // d(beta_{t+1} X_t)
+    if (ok) a.dX[bth * a.P + p] = fmaf(a.gamma[bth], d1, be_next * dnext);
+    if (ok && t == 0 && a.dXp) a.dXp[((size_t)b * a.H + h) * a.P + p] = a.beta[bth] * d0;
+    float sg = xt * d1, sb = xq * d0;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        sg += __shfl_xor(sg, off, 64);
+        sb += __shfl_xor(sb, off, 64);
+    }
+    if (p == 0) {
+        a.dgamma[bth] = sg;
+        a.dbeta[bth] = sb;
+        a.dld[bth] = a.dld2[r0];
+    }
+}
+
+// dB, dC in the physical frame summed over the group's heads, the per-head angle
+// gradient, and dB_prev: one wave per (batch, step, group), lane = pair
+__global__ __launch_bounds__(64) void k_tb_post_bc(TrapBwd a) {
+    const int64_t btg = blockIdx.x;
+    const int g = (int)(btg % a.G);
+    const int t = (int)((btg / a.G) % a.L), b = (int)(btg / ((int64_t)a.G * a.L));
+    const int K = a.N / 2, k = threadIdx.x;
+    if (k >= K) return;
+    const int hpg = a.H / a.G;
+    float2 db = make_float2(0.0f, 0.0f), dc = make_float2(0.0f, 0.0f), dbp = make_float2(0.0f, 0.0f);
+    for (int h = g * hpg; h < (g + 1) * hpg; ++h) {
+        const size_t r0 = ((size_t)b * 2 * a.L + 2 * (size_t)t) * a.H + h, r1 = r0 + a.H, r2 = r1 + a.H;
+        auto ld2 = [&](const float* base, size_t r) { return *(const float2*)(base + r * a.N + 2 * k); };
+        float2 dbr = ld2(a.dB2, r1);
+        if (t + 1 < a.L) {
+            const float2 u = ld2(a.dB2, r2);
+            dbr.x += u.x;
+            dbr.y += u.y;
+        }
+        const float2 dcr = ld2(a.dC2, r1), br = ld2(a.B2, r1), cr = ld2(a.C2, r1);
+        const size_t bth = ((size_t)b * a.L + t) * a.H + h;
+        if (a.theta) {
+            a.dTh[bth * K + k] = (br.x * dbr.y - br.y * dbr.x) + (cr.x * dcr.y - cr.y * dcr.x);
+        }
+        const float th = a.theta ? a.Th[bth * K + k] : 0.0f;
+        float sn, cs;
+        sincos_frac(th, &sn, &cs);
+        // R(-Theta): (cs v0 + sn v1, -sn v0 + cs v1)
+        db.x += cs * dbr.x + sn * dbr.y;
+        db.y += -sn * dbr.x + cs * dbr.y;
+        dc.x += cs * dcr.x + sn * dcr.y;
+        dc.y += -sn * dcr.x + cs * dcr.y;
+        if (t == 0) {
+            const float2 u = ld2(a.dB2, r0);   // step -1 is unrotated
+            dbp.x += u.x;
+            dbp.y += u.y;
+        }
+    }
+    const size_t o = (((size_t)b * a.L + t) * a.G + g) * a.N + 2 * k;
+    *(float2*)(a.dB + o) = db;
+    *(float2*)(a.dC + o) = dc;
+    if (t == 0 && a.dBp) *(float2*)(a.dBp + ((size_t)b * a.G + g) * a.N + 2 * k) = dbp;
+}
+
+// the rotation of h_out = R(-Theta_{L-1}) S: per (b, h, pair) sum over columns of
+// dh_out0 o1 - dh_out1 o0; one wave per (batch, head), lane = pair
+__global__ __launch_bounds__(64) void k_tb_hterm(TrapBwd a) {
+    const int bh = blockIdx.x, K = a.N / 2, k = threadIdx.x;
+    if (k >= K) return;
+    const int b = bh / a.H, h = bh % a.H;
+    const float th = a.Th[(((size_t)b * a.L + a.L - 1) * a.H + h) * K + k];
+    float sn, cs;
+    sincos_frac(th, &sn, &cs);
+    const float* S = a.hfin + (size_t)bh * a.N * a.P;
+    const float* dh = a.dh_out + (size_t)bh * a.N * a.P;
+    float acc = 0.0f;
+    for (int p = 0; p < a.P; ++p) {
+        const float s0 = S[(2 * k) * a.P + p], s1 = S[(2 * k + 1) * a.P + p];
+        const float o0 = cs * s0 + sn * s1, o1 = -sn * s0 + cs * s1;
+        acc += dh[(2 * k) * a.P + p] * o1 - dh[(2 * k + 1) * a.P + p] * o0;
+    }
+    a.hterm[(size_t)bh * K + k] = acc;
+}
+
+// dtheta_t = sum_{tau >= t} dTheta_tau (+ the h_out term): one wave per (batch,
+// head, segment), the later segments' sums added first
+__global__ __launch_bounds__(64) void k_tb_theta(TrapBwd a) {
+    const int sg = blockIdx.x % a.nseg, bh = blockIdx.x / a.nseg;
+    const int b = bh / a.H, h = bh % a.H, K = a.N / 2, k = threadIdx.x;
+    if (k >= K) return;
+    float acc = a.dh_out ? a.hterm[(size_t)bh * K + k] : 0.0f;
+    for (int s2 = sg + 1; s2 < a.nseg; ++s2) acc += a.seg[((size_t)bh * a.nseg + s2) * K + k];
+    const int t1 = min(a.L, (sg + 1) * kSeg);
+    for (int t = t1 - 1; t >= sg * kSeg; --t) {
+        const size_t i = (((size_t)b * a.L + t) * a.H + h) * K + k;
+        acc += a.dTh[i];
+        a.dtheta[i] = acc;
+    }
+}
+
+struct TrapBwdPlan {
+    BwdPlan ssd;
+    size_t off_x2, off_dy2, off_b2, off_c2, off_ld2, off_dx2, off_dld2, off_db2, off_dc2, off_th, off_dth, off_seg,
+        off_hterm, off_dh2, off_hfin, bytes;
+};
+
+TrapBwdPlan trap_bwd_plan(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N) {
+    TrapBwdPlan p{};
+    p.ssd = bwd_plan(batch, 2 * L, H, P, N);
+    size_t off = p.ssd.bytes;
+    const size_t nx = (size_t)(batch * 2 * L * H * P) * 4, nb = (size_t)(batch * 2 * L * H * N) * 4;
+    const size_t nl = (size_t)(batch * 2 * L * H) * 4, nth = (size_t)(batch * L * H * (N / 2)) * 4;
+    const size_t nseg = (size_t)((L + kSeg - 1) / kSeg), nh = (size_t)(batch * H * N * P) * 4;
+    auto take = [&](size_t bytes) { const size_t o = off; off += align256(bytes); return o; };
+    p.off_x2 = take(nx); p.off_dy2 = take(nx); p.off_b2 = take(nb); p.off_c2 = take(nb); p.off_ld2 = take(nl);
+    p.off_dx2 = take(nx); p.off_dld2 = take(nl); p.off_db2 = take(nb); p.off_dc2 = take(nb);
+    p.off_th = take(nth); p.off_dth = take(nth);
+    p.off_seg = take((size_t)(batch * H) * nseg * (N / 2) * 4);
+    p.off_hterm = take((size_t)(batch * H * (N / 2)) * 4);
+    p.off_dh2 = take(nh); p.off_hfin = take(nh);
+    p.bytes = off;
+    return p;
+}
+
+}  // namespace
+
+size_t trap_bwd_workspace(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t G, int64_t N) {
+    if (!bwd_dims_ok(batch, 2 * L, H, P, H, N) || G < 1 || H % G || batch == 0 || L == 0) return 0;
+    return trap_bwd_plan(batch, L, H, P, N).bytes;
+}
+
+}  // namespace mb
+
+extern "C" mb_status mb_trap_ssd_bwd(const float* X, const float* logdecay, const float* B, const float* C,
+                                     const float* beta, const float* gamma, const float* theta, const float* h0,
+                                     const float* X_prev, const float* B_prev, const float* dY,
+                                     const float* dh_out, float* dX, float* dlogdecay, float* dB, float* dC,
+                                     float* dbeta, float* dgamma, float* dtheta, float* dh0, float* dX_prev,
+                                     float* dB_prev, int64_t batch, int64_t L, int64_t H, int64_t P, int64_t G,
+                                     int64_t N, mb_dtype dtype, void* ws, size_t ws_bytes, hipStream_t stream)
+{
+    if (dtype != MB_F32) return MB_ERR_DTYPE;
+    if (G < 1 || H % G || !bwd_dims_ok(batch, 2 * L, H, P, H, N)) return MB_ERR_SHAPE;
+    if (batch * L * H > INT32_MAX || batch * L * G > INT32_MAX) return MB_ERR_SHAPE;
+    const size_t n_x = (size_t)(batch * L * H * P), n_b = (size_t)(batch * L * G * N);
+    const size_t n_l = (size_t)(batch * L * H), n_h = (size_t)(batch * H * N * P);
+    const size_t n_th = (size_t)(batch * L * H * (N / 2));
+    const size_t n_xp = (size_t)(batch * H * P), n_bp = (size_t)(batch * G * N);
+    if (n_x && (!X || !dY || !dX || !logdecay || !dlogdecay || !beta || !gamma || !dbeta || !dgamma))
+        return MB_ERR_NULL;
+    if (n_b && (!B || !C || !dB || !dC)) return MB_ERR_NULL;
+    if (theta && n_th && !dtheta) return MB_ERR_NULL;
+    if ((X_prev == nullptr) != (B_prev == nullptr)) return MB_ERR_NULL;
+    if (((uintptr_t)X | (uintptr_t)B | (uintptr_t)C | (uintptr_t)dY | (uintptr_t)dX | (uintptr_t)dB |
+         (uintptr_t)dC | (uintptr_t)h0 | (uintptr_t)dh_out | (uintptr_t)dh0 | (uintptr_t)X_prev |
+         (uintptr_t)B_prev | (uintptr_t)dB_prev) & 15)
+        return MB_ERR_ALIGN;
+    const Span ins[] = {{X, n_x * 4}, {logdecay, n_l * 4}, {B, n_b * 4}, {C, n_b * 4}, {beta, n_l * 4},
+                        {gamma, n_l * 4}, {theta, theta ? n_th * 4 : 0}, {h0, h0 ? n_h * 4 : 0},
+                        {X_prev, X_prev ? n_xp * 4 : 0}, {B_prev, B_prev ? n_bp * 4 : 0}, {dY, n_x * 4},
+                        {dh_out, dh_out ? n_h * 4 : 0}};
+    const Span outs[] = {{dX, n_x * 4}, {dlogdecay, n_l * 4}, {dB, n_b * 4}, {dC, n_b * 4}, {dbeta, n_l * 4},
+                         {dgamma, n_l * 4}, {dtheta, theta && dtheta ? n_th * 4 : 0}, {dh0, dh0 ? n_h * 4 : 0},
+                         {dX_prev, dX_prev ? n_xp * 4 : 0}, {dB_prev, dB_prev ? n_bp * 4 : 0}};
+    for (int i = 0; i < 10; ++i) {
+        if (overlaps_any(outs[i].p, outs[i].bytes, ins, 12)) return MB_ERR_ALIAS;
+        for (int j = i + 1; j < 10; ++j)
+            if (overlaps(outs[i].p, outs[i].bytes, outs[j].p, outs[j].bytes)) return MB_ERR_ALIAS;
+    }
+    if (batch == 0) return MB_OK;
+    if (L == 0) {
+        // no steps: dh0 = dh_out; the previous token gets nothing
+        mb_status st = dh0 ? copy_state(dh_out, dh0, (int64_t)n_h, stream) : MB_OK;
+        if (st == MB_OK && dX_prev) st = copy_state(nullptr, dX_prev, (int64_t)n_xp, stream);
+        if (st == MB_OK && dB_prev) st = copy_state(nullptr, dB_prev, (int64_t)n_bp, stream);
+        return st;
+    }
+    const TrapBwdPlan pl = trap_bwd_plan(batch, L, H, P, N);
+    if (!ws || ws_bytes < pl.bytes || ((uintptr_t)ws & 255)) return MB_ERR_WORKSPACE;
+    if (overlaps_any(ws, pl.bytes, ins, 12) || overlaps_any(ws, pl.bytes, outs, 10)) return MB_ERR_ALIAS;
+    char* w = (char*)ws;
+    TrapBwd t{};
+    t.X = X; t.ld = logdecay; t.B = B; t.C = C; t.beta = beta; t.gamma = gamma; t.theta = theta;
+    t.Xp = X_prev; t.Bp = B_prev; t.dY = dY; t.dh_out = dh_out;
+    t.dX = dX; t.dld = dlogdecay; t.dB = dB; t.dC = dC; t.dbeta = dbeta; t.dgamma = dgamma; t.dtheta = dtheta;
+    t.dXp = dX_prev; t.dBp = dB_prev;
+    t.X2 = (float*)(w + pl.off_x2); t.dY2 = (float*)(w + pl.off_dy2); t.B2 = (float*)(w + pl.off_b2);
+    t.C2 = (float*)(w + pl.off_c2); t.ld2 = (float*)(w + pl.off_ld2); t.dX2 = (float*)(w + pl.off_dx2);
+    t.dld2 = (float*)(w + pl.off_dld2); t.dB2 = (float*)(w + pl.off_db2); t.dC2 = (float*)(w + pl.off_dc2);
+    t.Th = (float*)(w + pl.off_th); t.dTh = (float*)(w + pl.off_dth); t.seg = (float*)(w + pl.off_seg);
+    t.hterm = (float*)(w + pl.off_hterm); t.dh2 = (float*)(w + pl.off_dh2); t.hfin = (float*)(w + pl.off_hfin);
+    t.L = (int)L; t.H = (int)H; t.G = (int)G; t.N = (int)N; t.P = (int)P;
+    t.nseg = (int)((L + kSeg - 1) / kSeg);
+    const unsigned nseg_all = (unsigned)(batch * H * t.nseg);
+    // 1. angles, rotated and interleaved inputs
+    if (theta) hipLaunchKernelGGL(k_tb_segsum, dim3(nseg_all), dim3(64), 0, stream, t, theta, t.seg);
+    hipLaunchKernelGGL(k_tb_prep_bc, dim3(nseg_all), dim3(64), 0, stream, t);
+    hipLaunchKernelGGL(k_tb_prep_x, dim3((unsigned)((L * H * (P / 4) + 255) / 256), (unsigned)batch), dim3(256), 0,
+                       stream, t);
+    if (dh_out)
+        hipLaunchKernelGGL(k_tb_rot_dh, dim3((unsigned)(((N / 2) * P + 255) / 256), (unsigned)(batch * H)),
+                           dim3(256), 0, stream, t);
+    // 2. the SSD backward over the 2L pseudo-steps, every head its own group
+    BwdArgs a{};
+    a.X = t.X2; a.ld = t.ld2; a.B = t.B2; a.C = t.C2; a.h0 = h0; a.dY = t.dY2; a.dh_out = dh_out ? t.dh2 : nullptr;
+    a.dX = t.dX2; a.dld = t.dld2; a.dB = t.dB2; a.dC = t.dC2; a.dh0 = dh0;
+    a.st = (float*)w;
+    a.lam = (float*)(w + pl.ssd.off_lam);
+    a.tot = (float*)(w + pl.ssd.off_tot);
+    a.fin = (float*)(w + pl.ssd.off_fin);
+    a.h_final = t.hfin;
+    a.L = (int)(2 * L); a.H = (int)H; a.G = (int)H; a.N = (int)N; a.P = (int)P;
+    a.nch = (int)pl.ssd.nch; a.nfin = (int)pl.ssd.nfin;
+    mb_status st;
+    if (N == 128)
+        st = P == 64 ? bwd_launch<128, 64>(a, batch, stream) : bwd_launch<128, 32>(a, batch, stream);
+    else
+        st = P == 64 ? bwd_launch<64, 64>(a, batch, stream) : bwd_launch<64, 32>(a, batch, stream);
+    if (st != MB_OK) return st;
+    // 3. back to the inputs
+    hipLaunchKernelGGL(k_tb_post_x, dim3((unsigned)(batch * L * H)), dim3(64), 0, stream, t);
+    hipLaunchKernelGGL(k_tb_post_bc, dim3((unsigned)(batch * L * G)), dim3(64), 0, stream, t);
+    if (theta) {
+        if (dh_out) hipLaunchKernelGGL(k_tb_hterm, dim3((unsigned)(batch * H)), dim3(64), 0, stream, t);
+        hipLaunchKernelGGL(k_tb_segsum, dim3(nseg_all), dim3(64), 0, stream, t, (const float*)t.dTh, t.seg);
+        hipLaunchKernelGGL(k_tb_theta, dim3(nseg_all), dim3(64), 0, stream, t);
+    }
+    return check_launch();
 }

@@ -244,6 +244,18 @@ def m1_block_inputs(rng, batch, L, D, N, K=4, h0_sd=0.0, hist=False):
     return d
 
 
+def siso_bwd_block(seed=113):
+    """The Mamba-3 SISO block inputs (seed 104) with the incoming gradients of
+    the backward: dY ~ N(0,1) like X and dh_out ~ N(0,1) like the state."""
+    d = siso_block()
+    rng = np.random.default_rng(seed)
+    b, L, H, P = d["X"].shape
+    N = d["B"].shape[3]
+    d["dY"] = rng.standard_normal((b, L, H, P))
+    d["dh_out"] = rng.standard_normal((b, H, N, P))
+    return d
+
+
 def m1_bwd_block(seed=112):
     """The Mamba-1 block inputs (seed 102) with the incoming gradients of the
     backward: dy ~ N(0,1) like x and dh_out ~ N(0,1) like the state."""

@@ -34,7 +34,7 @@ def declared_functions():
 def test_exports_every_declared_function(lib):
     names = declared_functions()
     assert {"mb_selective_scan", "mb_ssm_step", "mb_ssd_chunked", "mb_trap_ssd", "mb_mimo_ssd",
-            "mb_ssd_step", "mb_selective_scan_fused", "mb_ssd_chunked_bwd", "mb_selective_scan_bwd", "mb_workspace_size", "mb_status_str", "mb_last_hip_error", "mb_version"} <= set(names)
+            "mb_ssd_step", "mb_selective_scan_fused", "mb_ssd_chunked_bwd", "mb_selective_scan_bwd", "mb_trap_ssd_bwd", "mb_workspace_size", "mb_status_str", "mb_last_hip_error", "mb_version"} <= set(names)
     for n in names:
         assert hasattr(lib, n), "libmb.so does not export " + n
 
@@ -219,6 +219,33 @@ def test_m1_bwd_validation(lib):
     need = mb.mb_workspace_size(mb.MB_OP_SELECTIVE_SCAN_BWD, 2, 100, 64, 1, 1, 16)
     assert need >= 2 * 4 * 64 * 16 * 4
     assert mb.mb_workspace_size(mb.MB_OP_SELECTIVE_SCAN_BWD, 2, 100, 64, 1, 1, 32) == 0
+
+
+def trap_bwd(lib, X=FAKE, dX=FAKE + (1 << 25), theta=FAKE + (1 << 24) + (1 << 22), dtheta=FAKE + (1 << 27),
+             Xp=None, Bp=None, N=128, P_=64, G=1, dtype=F32, ws=FAKE + (1 << 28), ws_bytes=1 << 33):
+    q = lambda v: P(v) if v else None
+    return lib.mb_trap_ssd_bwd(q(X), P(FAKE + (1 << 22)), P(FAKE + (1 << 23)), P(FAKE + (1 << 23) + (1 << 21)),
+                               P(FAKE + (1 << 22) + (1 << 20)), P(FAKE + (1 << 22) + (1 << 21)), q(theta), None,
+                               q(Xp), q(Bp), P(FAKE + (1 << 24)), None, q(dX), P(FAKE + (1 << 25) + (1 << 23)),
+                               P(FAKE + (1 << 26)), P(FAKE + (1 << 26) + (1 << 21)), P(FAKE + (1 << 26) + (1 << 22)),
+                               P(FAKE + (1 << 26) + (1 << 23)), q(dtheta), None, None, None, 2, 50, 4, P_, G, N,
+                               dtype, q(ws), ws_bytes, None)
+
+
+def test_trap_bwd_validation(lib):
+    assert trap_bwd(lib, dtype=BF16) == E_DTYPE
+    assert trap_bwd(lib, N=32) == E_SHAPE
+    assert trap_bwd(lib, P_=16) == E_SHAPE
+    assert trap_bwd(lib, G=3) == E_SHAPE
+    assert trap_bwd(lib, X=0) == E_NULL
+    assert trap_bwd(lib, dtheta=0) == E_NULL                      # theta given, dtheta missing
+    assert trap_bwd(lib, Xp=FAKE + (1 << 29)) == E_NULL             # X_prev without B_prev
+    assert trap_bwd(lib, dX=FAKE + (1 << 25) + 4) == E_ALIGN
+    assert trap_bwd(lib, dX=FAKE + 128) == E_ALIAS                  # dX over X
+    assert trap_bwd(lib, ws=0) == E_WS
+    assert trap_bwd(lib, ws_bytes=1 << 12) == E_WS
+    assert mb.mb_workspace_size(mb.MB_OP_TRAP_SSD_BWD, 2, 50, 4, 64, 1, 128) > 0
+    assert mb.mb_workspace_size(mb.MB_OP_TRAP_SSD_BWD, 2, 50, 4, 48, 1, 128) == 0
 
 
 def test_trap_and_mimo_validation(lib):
