@@ -737,7 +737,7 @@ struct TrapBwd {
     float *Th, *dTh;                          // (batch, L, H, K) angles (as the fraction of a
                                               // revolution) and angle gradients
     float *seg, *hterm, *dh2, *hfin;          // segment sums, h_out term, rotated dh_out, final state
-    int L, H, G, N, P, nseg;
+    int L, H, G, N, P, nseg, batch;
 };
 
 constexpr int kSeg = 64;   // steps per segment of the angle sums
@@ -780,16 +780,22 @@ __global__ __launch_bounds__(64) void k_tb_prep_bc(TrapBwd a) {
         *(float2*)row(a.C2, 0) = make_float2(0.0f, 0.0f);
     }
     const int t1 = min(a.L, (sg + 1) * kSeg);
+    // the inputs are never written here: loads may run ahead of the stores
+    const float* __restrict__ thv = a.theta;
+    const float* __restrict__ Bv = a.B;
+    const float* __restrict__ Cv = a.C;
+    float* __restrict__ Tho = a.Th;
+#pragma unroll 8
     for (int t = sg * kSeg; t < t1; ++t) {
         const size_t bth = ((size_t)b * a.L + t) * a.H + h;
-        if (a.theta) th += (double)a.theta[bth * K + k];
+        if (thv) th += (double)thv[bth * K + k];
         const double r = th * 0.15915494309189535;
         const float f = (float)(r - rint(r));
-        a.Th[bth * K + k] = f;
+        Tho[bth * K + k] = f;
         float sn, cs;
         sincos_frac(f, &sn, &cs);
-        const float2 bv = *(const float2*)(a.B + (((size_t)b * a.L + t) * a.G + g) * a.N + 2 * k);
-        const float2 cv = *(const float2*)(a.C + (((size_t)b * a.L + t) * a.G + g) * a.N + 2 * k);
+        const float2 bv = *(const float2*)(Bv + (((size_t)b * a.L + t) * a.G + g) * a.N + 2 * k);
+        const float2 cv = *(const float2*)(Cv + (((size_t)b * a.L + t) * a.G + g) * a.N + 2 * k);
         const float2 br = make_float2(cs * bv.x - sn * bv.y, sn * bv.x + cs * bv.y);
         const float2 cr = make_float2(cs * cv.x - sn * cv.y, sn * cv.x + cs * cv.y);
         *(float2*)row(a.B2, 2 * (size_t)t + 1) = br;
@@ -846,32 +852,47 @@ __global__ __launch_bounds__(256) void k_tb_rot_dh(TrapBwd a) {
     dst[(2 * k + 1) * a.P + p] = sn * v0 + cs * v1;
 }
 
-// dX, dgamma, dbeta, dlogdecay: one wave per (batch, step, head), lane = column
+// dX, dgamma, dbeta, dlogdecay: one wave per four (batch, step, head) rows,
+// 16 lanes per row, four columns per lane (P <= 64)
 __global__ __launch_bounds__(64) void k_tb_post_x(TrapBwd a) {
-    const int64_t bth = blockIdx.x;
-    const int h = (int)(bth % a.H);
-    const int t = (int)((bth / a.H) % a.L), b = (int)(bth / ((int64_t)a.H * a.L));
-    const int p = threadIdx.x;
-    const bool ok = p < a.P;
+    const int64_t rows = (int64_t)a.batch * a.L * a.H;
+    const int64_t bth = (int64_t)blockIdx.x * 4 + threadIdx.x / 16;
+    const int c4 = threadIdx.x % 16;
+    const bool rok = bth < rows;
+    const int64_t bthc = rok ? bth : 0;
+    const int h = (int)(bthc % a.H);
+    const int t = (int)((bthc / a.H) % a.L), b = (int)(bthc / ((int64_t)a.H * a.L));
+    const bool ok = rok && 4 * c4 < a.P;
+    const int p = 4 * c4;
     const size_t r0 = ((size_t)b * 2 * a.L + 2 * (size_t)t) * a.H + h, r1 = r0 + a.H, r2 = r1 + a.H;
-    const float d1 = ok ? a.dX2[r1 * a.P + p] : 0.0f;          // d(gamma_t X_t)
-    const float d0 = ok ? a.dX2[r0 * a.P + p] : 0.0f;          // d(beta_t X_{t-1})
-    const float xt = ok ? a.X[bth * a.P + p] : 0.0f;
-    const float xq = !ok ? 0.0f : t > 0 ? a.X[(bth - a.H) * a.P + p] : (a.Xp ? a.Xp[((size_t)b * a.H + h) * a.P + p] : 0.0f);
-    const float be_next = t + 1 < a.L ? a.beta[bth + a.H] : 0.0f;
-    const float dnext = (ok && t + 1 < a.L) ? a.dX2[r2 * a.P + p] : 0.0f;   // d(beta_{t+1} X_t)
-    if (ok) a.dX[bth * a.P + p] = fmaf(a.gamma[bth], d1, be_next * dnext);
-    if (ok && t == 0 && a.dXp) a.dXp[((size_t)b * a.H + h) * a.P + p] = a.beta[bth] * d0;
-    float sg = xt * d1, sb = xq * d0;
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        sg += __shfl_xor(sg, off, 64);
-        sb += __shfl_xor(sb, off, 64);
+    const float4 z4 = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    auto ld4 = [&](const float* base, size_t r, bool c) { return c ? *(const float4*)(base + r * a.P + p) : z4; };
+    const float4 d1 = ld4(a.dX2, r1, ok);                        // d(gamma_t X_t)
+    const float4 d0 = ld4(a.dX2, r0, ok);                        // d(beta_t X_{t-1})
+    const float4 dn = ld4(a.dX2, r2, ok && t + 1 < a.L);          // d(beta_{t+1} X_t)
+    const float4 xt = ld4(a.X, (size_t)bthc, ok);
+    const float4 xq = t > 0 ? ld4(a.X, (size_t)bthc - a.H, ok)
+                            : (a.Xp ? ld4(a.Xp, (size_t)b * a.H + h, ok) : z4);
+    const float ga = rok ? a.gamma[bthc] : 0.0f, be = rok ? a.beta[bthc] : 0.0f;
+    const float bn = (rok && t + 1 < a.L) ? a.beta[bthc + a.H] : 0.0f;
+    if (ok) {
+        *(float4*)(a.dX + (size_t)bthc * a.P + p) =
+            make_float4(fmaf(ga, d1.x, bn * dn.x), fmaf(ga, d1.y, bn * dn.y), fmaf(ga, d1.z, bn * dn.z),
+                        fmaf(ga, d1.w, bn * dn.w));
+        if (t == 0 && a.dXp)
+            *(float4*)(a.dXp + ((size_t)b * a.H + h) * a.P + p) = make_float4(be * d0.x, be * d0.y, be * d0.z, be * d0.w);
     }
-    if (p == 0) {
-        a.dgamma[bth] = sg;
-        a.dbeta[bth] = sb;
-        a.dld[bth] = a.dld2[r0];
+    float sg = (xt.x * d1.x + xt.y * d1.y) + (xt.z * d1.z + xt.w * d1.w);
+    float sb = (xq.x * d0.x + xq.y * d0.y) + (xq.z * d0.z + xq.w * d0.w);
+#pragma unroll
+    for (int off = 8; off >= 1; off >>= 1) {
+        sg += __shfl_xor(sg, off, 16);
+        sb += __shfl_xor(sb, off, 16);
+    }
+    if (rok && c4 == 0) {
+        a.dgamma[bthc] = sg;
+        a.dbeta[bthc] = sb;
+        a.dld[bthc] = a.dld2[r0];
     }
 }
 
@@ -885,23 +906,33 @@ __global__ __launch_bounds__(64) void k_tb_post_bc(TrapBwd a) {
     if (k >= K) return;
     const int hpg = a.H / a.G;
     float2 db = make_float2(0.0f, 0.0f), dc = make_float2(0.0f, 0.0f), dbp = make_float2(0.0f, 0.0f);
+    // the physical B, C of the step (shared by the group's heads); the rotated
+    // ones are recomputed per head from the angle
+    const size_t o = (((size_t)b * a.L + t) * a.G + g) * a.N + 2 * k;
+    const float2 bp = *(const float2*)(a.B + o), cp = *(const float2*)(a.C + o);
+    const float* __restrict__ dB2 = a.dB2;
+    const float* __restrict__ dC2 = a.dC2;
+    const float* __restrict__ Thv = a.Th;
+#pragma unroll 4
     for (int h = g * hpg; h < (g + 1) * hpg; ++h) {
         const size_t r0 = ((size_t)b * 2 * a.L + 2 * (size_t)t) * a.H + h, r1 = r0 + a.H, r2 = r1 + a.H;
         auto ld2 = [&](const float* base, size_t r) { return *(const float2*)(base + r * a.N + 2 * k); };
-        float2 dbr = ld2(a.dB2, r1);
+        float2 dbr = ld2(dB2, r1);
         if (t + 1 < a.L) {
-            const float2 u = ld2(a.dB2, r2);
+            const float2 u = ld2(dB2, r2);
             dbr.x += u.x;
             dbr.y += u.y;
         }
-        const float2 dcr = ld2(a.dC2, r1), br = ld2(a.B2, r1), cr = ld2(a.C2, r1);
+        const float2 dcr = ld2(dC2, r1);
         const size_t bth = ((size_t)b * a.L + t) * a.H + h;
-        if (a.theta) {
-            a.dTh[bth * K + k] = (br.x * dbr.y - br.y * dbr.x) + (cr.x * dcr.y - cr.y * dcr.x);
-        }
-        const float th = a.theta ? a.Th[bth * K + k] : 0.0f;
+        const float th = a.theta ? Thv[bth * K + k] : 0.0f;
         float sn, cs;
         sincos_frac(th, &sn, &cs);
+        if (a.theta) {
+            const float2 br = make_float2(cs * bp.x - sn * bp.y, sn * bp.x + cs * bp.y);
+            const float2 cr = make_float2(cs * cp.x - sn * cp.y, sn * cp.x + cs * cp.y);
+            a.dTh[bth * K + k] = (br.x * dbr.y - br.y * dbr.x) + (cr.x * dcr.y - cr.y * dcr.x);
+        }
         // R(-Theta): (cs v0 + sn v1, -sn v0 + cs v1)
         db.x += cs * dbr.x + sn * dbr.y;
         db.y += -sn * dbr.x + cs * dbr.y;
@@ -913,7 +944,6 @@ __global__ __launch_bounds__(64) void k_tb_post_bc(TrapBwd a) {
             dbp.y += u.y;
         }
     }
-    const size_t o = (((size_t)b * a.L + t) * a.G + g) * a.N + 2 * k;
     *(float2*)(a.dB + o) = db;
     *(float2*)(a.dC + o) = dc;
     if (t == 0 && a.dBp) *(float2*)(a.dBp + ((size_t)b * a.G + g) * a.N + 2 * k) = dbp;
@@ -1048,6 +1078,7 @@ extern "C" mb_status mb_trap_ssd_bwd(const float* X, const float* logdecay, cons
     t.hterm = (float*)(w + pl.off_hterm); t.dh2 = (float*)(w + pl.off_dh2); t.hfin = (float*)(w + pl.off_hfin);
     t.L = (int)L; t.H = (int)H; t.G = (int)G; t.N = (int)N; t.P = (int)P;
     t.nseg = (int)((L + kSeg - 1) / kSeg);
+    t.batch = (int)batch;
     const unsigned nseg_all = (unsigned)(batch * H * t.nseg);
     // 1. angles, rotated and interleaved inputs
     if (theta) hipLaunchKernelGGL(k_tb_segsum, dim3(nseg_all), dim3(64), 0, stream, t, theta, t.seg);
@@ -1075,7 +1106,7 @@ extern "C" mb_status mb_trap_ssd_bwd(const float* X, const float* logdecay, cons
         st = P == 64 ? bwd_launch<64, 64>(a, batch, stream) : bwd_launch<64, 32>(a, batch, stream);
     if (st != MB_OK) return st;
     // 3. back to the inputs
-    hipLaunchKernelGGL(k_tb_post_x, dim3((unsigned)(batch * L * H)), dim3(64), 0, stream, t);
+    hipLaunchKernelGGL(k_tb_post_x, dim3((unsigned)((batch * L * H + 3) / 4)), dim3(64), 0, stream, t);
     hipLaunchKernelGGL(k_tb_post_bc, dim3((unsigned)(batch * L * G)), dim3(64), 0, stream, t);
     if (theta) {
         if (dh_out) hipLaunchKernelGGL(k_tb_hterm, dim3((unsigned)(batch * H)), dim3(64), 0, stream, t);
