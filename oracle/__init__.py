@@ -68,6 +68,7 @@ def _load():
         lib.oracle_ssd_bwd.argtypes = [_D] * 12 + [_I] * 6
         lib.oracle_trap.argtypes = [_D] * 12 + [_I] * 6
         lib.oracle_trap_bwd.argtypes = [_D] * 22 + [_I] * 6
+        lib.oracle_mimo_bwd.argtypes = [_D] * 22 + [_I] * 6
         lib.oracle_mimo.argtypes = [_D] * 12 + [_I] * 6
         lib.oracle_ssd_step.argtypes = [_D] * 12 + [_I] * 6
         lib.oracle_m1_block.argtypes = [_D] * 14 + [_I] * 5
@@ -305,6 +306,38 @@ def mimo(X, logdecay, B, C, beta, gamma, theta=None, h0=None, X_prev=None, B_pre
     _load().oracle_mimo(_p(X), _p(logdecay), _p(B), _p(C), _p(beta), _p(gamma),
                         _p(theta), _p(h0), _p(X_prev), _p(B_prev), _p(Y), _p(h), b, L, H, P, N, R)
     return Y, h
+
+
+def mimo_bwd(X, logdecay, B, C, beta, gamma, dY, theta=None, h0=None, dh_out=None, X_prev=None, B_prev=None):
+    """Backward of the Mamba-3 MIMO recurrence: the gradients of sum dY . Y + sum
+    dh_out . h_out with respect to X, logdecay, B, C, beta, gamma, theta, h0,
+    X_prev, B_prev.  Shapes as mimo(); dY like X, dh_out like h0.  Returns (dX,
+    dlogdecay, dB, dC, dbeta, dgamma, dtheta or None, dh0, dX_prev, dB_prev)."""
+    X = _f64(X)
+    b, L, H, P, R = X.shape
+    B = _f64(B)
+    N = B.shape[3]
+    logdecay = _chk(logdecay, (b, L, H), "logdecay")
+    beta = _chk(beta, (b, L, H), "beta")
+    gamma = _chk(gamma, (b, L, H), "gamma")
+    B = _chk(B, (b, L, H, N, R), "B")
+    C = _chk(C, (b, L, H, N, R), "C")
+    dY = _chk(dY, (b, L, H, P, R), "dY")
+    theta = _opt(theta, (b, L, H, N // 2))
+    h0 = _opt(h0, (b, H, N, P))
+    dh_out = _opt(dh_out, (b, H, N, P))
+    X_prev = _opt(X_prev, (b, H, P, R))
+    B_prev = _opt(B_prev, (b, H, N, R))
+    out = dict(dX=np.empty((b, L, H, P, R)), dld=np.empty((b, L, H)), dB=np.empty((b, L, H, N, R)),
+               dC=np.empty((b, L, H, N, R)), dbeta=np.empty((b, L, H)), dgamma=np.empty((b, L, H)),
+               dtheta=np.empty((b, L, H, N // 2)) if theta is not None else None, dh0=np.empty((b, H, N, P)),
+               dX_prev=np.empty((b, H, P, R)), dB_prev=np.empty((b, H, N, R)))
+    _load().oracle_mimo_bwd(_p(X), _p(logdecay), _p(B), _p(C), _p(beta), _p(gamma), _p(theta), _p(h0), _p(X_prev),
+                            _p(B_prev), _p(dY), _p(dh_out), _p(out["dX"]), _p(out["dld"]), _p(out["dB"]),
+                            _p(out["dC"]), _p(out["dbeta"]), _p(out["dgamma"]), _p(out["dtheta"]), _p(out["dh0"]),
+                            _p(out["dX_prev"]), _p(out["dB_prev"]), b, L, H, P, N, R)
+    return (out["dX"], out["dld"], out["dB"], out["dC"], out["dbeta"], out["dgamma"], out["dtheta"], out["dh0"],
+            out["dX_prev"], out["dB_prev"])
 
 
 def ssd_step(X, logdecay, B, C, h=None, beta=None, gamma=None, theta=None, X_prev=None, B_prev=None):

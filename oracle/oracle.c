@@ -700,6 +700,183 @@ void oracle_mimo(const double *X, const double *logdecay, const double *B,
 }
 
 /*
+ * Backward (vector-Jacobian product) of the MIMO recurrence above, by
+ * back-propagation through time in the rotated frame, as oracle_trap_bwd with R
+ * ranks per step: the adjoint A (from R(Theta_{L-1}) dh_out) takes
+ * sum_r Ct_{t,r} dY_{t,r}^T at step t; dCt_{t,r} = S_t dY_{t,r}; for every rank
+ * the gamma term gives dX_{t,r} += gamma_t A^T Bt_{t,r}, dBt_{t,r} += gamma_t A X_{t,r},
+ * dgamma_t += X_{t,r} . A^T Bt_{t,r}, and the beta term the same with step t - 1
+ * and beta_t; dld_t = e^{ld_t} <A, S_{t-1}>; A = e^{ld_t} A.  Rotated gradients
+ * return by R(-Theta_t); the angle gradient sums over the ranks of B and C and
+ * adds the rotation of h_out at the last step; dtheta is its suffix sum.
+ * Layouts as oracle_mimo ([p][r] and [n][r] innermost); the previous token's
+ * gradients dX_prev0 (b, H, P, R), dB_prev0 (b, H, N, R).
+ */
+void oracle_mimo_bwd(const double *X, const double *logdecay, const double *B,
+                     const double *C, const double *beta, const double *gamma,
+                     const double *theta, const double *h0, const double *X_prev0,
+                     const double *B_prev0, const double *dY, const double *dh_out,
+                     double *dX, double *dld, double *dB, double *dC, double *dbeta,
+                     double *dgamma, double *dtheta, double *dh0, double *dX_prev0,
+                     double *dB_prev0, int64_t batch, int64_t L, int64_t H, int64_t P,
+                     int64_t N, int64_t R)
+{
+    int64_t K = N / 2;
+    int64_t NP = N * P, NR = N * R, PR = P * R;
+    int64_t units = batch * H;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t u = 0; u < units; ++u) {
+        int64_t b = u / H, h = u % H;
+        double *S = (double *)malloc(sizeof(double) * (size_t)((L + 1) * NP > 0 ? (L + 1) * NP : 1));
+        double *Bt = (double *)malloc(sizeof(double) * (size_t)((L + 1) * NR > 0 ? (L + 1) * NR : 1));
+        double *Ct = (double *)malloc(sizeof(double) * (size_t)(L * NR > 0 ? L * NR : 1));
+        double *Th = (double *)calloc((size_t)(L * K > 0 ? L * K : 1), sizeof(double));
+        double *A = (double *)malloc(sizeof(double) * (size_t)(NP > 0 ? NP : 1));
+        double *dBt = (double *)calloc((size_t)((L + 1) * NR > 0 ? (L + 1) * NR : 1), sizeof(double));
+        double *dCt = (double *)malloc(sizeof(double) * (size_t)(L * NR > 0 ? L * NR : 1));
+        double *Xp = (double *)calloc((size_t)(PR > 0 ? PR : 1), sizeof(double));
+        double *dXp = (double *)calloc((size_t)(PR > 0 ? PR : 1), sizeof(double));
+        double *dTh = (double *)calloc((size_t)(L * K > 0 ? L * K : 1), sizeof(double));
+        double *v = (double *)malloc(sizeof(double) * (size_t)(P > 0 ? P : 1));
+        /* rotated B (step t at Bt + (t + 1) NR, step -1 at Bt) and C */
+        for (int64_t i = 0; i < NR; ++i) Bt[i] = B_prev0 ? B_prev0[(b * H + h) * NR + i] : 0.0;
+        for (int64_t i = 0; i < PR; ++i) Xp[i] = X_prev0 ? X_prev0[(b * H + h) * PR + i] : 0.0;
+        for (int64_t t = 0; t < L; ++t) {
+            int64_t bth = (b * L + t) * H + h;
+            for (int64_t k = 0; k < K; ++k)
+                Th[t * K + k] = (t ? Th[(t - 1) * K + k] : 0.0) + (theta ? theta[bth * K + k] : 0.0);
+            for (int64_t r = 0; r < R; ++r) {
+                if (theta) {
+                    rotate_pairs(Bt + (t + 1) * NR + r, B + bth * NR + r, Th + t * K, N, R, 1.0);
+                    rotate_pairs(Ct + t * NR + r, C + bth * NR + r, Th + t * K, N, R, 1.0);
+                } else {
+                    for (int64_t n = 0; n < N; ++n) {
+                        Bt[(t + 1) * NR + n * R + r] = B[bth * NR + n * R + r];
+                        Ct[t * NR + n * R + r] = C[bth * NR + n * R + r];
+                    }
+                }
+            }
+        }
+        for (int64_t i = 0; i < NP; ++i) S[i] = h0 ? h0[(b * H + h) * NP + i] : 0.0;
+        for (int64_t t = 0; t < L; ++t) {
+            int64_t bth = (b * L + t) * H + h;
+            double a = exp(logdecay[bth]), be = beta[bth], ga = gamma[bth];
+            const double *Xt = X + bth * PR, *Xq = t ? X + (bth - H) * PR : Xp;
+            const double *Bc = Bt + (t + 1) * NR, *Bq = Bt + t * NR;
+            for (int64_t n = 0; n < N; ++n)
+                for (int64_t p = 0; p < P; ++p) {
+                    double prev = 0.0, cur = 0.0;
+                    for (int64_t r = 0; r < R; ++r) {
+                        prev += Bq[n * R + r] * Xq[p * R + r];
+                        cur += Bc[n * R + r] * Xt[p * R + r];
+                    }
+                    S[(t + 1) * NP + n * P + p] = a * S[t * NP + n * P + p] + be * prev + ga * cur;
+                }
+        }
+        for (int64_t i = 0; i < NP; ++i) A[i] = dh_out ? dh_out[(b * H + h) * NP + i] : 0.0;
+        if (theta && L > 0 && dh_out) {
+            const double *dh = dh_out + (b * H + h) * NP, *Sl = S + L * NP, *thl = Th + (L - 1) * K;
+            for (int64_t k = 0; k < K; ++k) {
+                double cs = cos(thl[k]), sn = sin(thl[k]), acc = 0.0;
+                for (int64_t p = 0; p < P; ++p) {
+                    double s0 = Sl[(2 * k) * P + p], s1 = Sl[(2 * k + 1) * P + p];
+                    double o0 = cs * s0 + sn * s1, o1 = -sn * s0 + cs * s1;
+                    acc += dh[(2 * k) * P + p] * o1 - dh[(2 * k + 1) * P + p] * o0;
+                }
+                dTh[(L - 1) * K + k] += acc;
+            }
+            for (int64_t p = 0; p < P; ++p) rotate_pairs(A + p, dh + p, thl, N, P, 1.0);
+        }
+        for (int64_t i = 0; i < L * PR; ++i) dX[((b * L + i / PR) * H + h) * PR + i % PR] = 0.0;
+        for (int64_t t = L - 1; t >= 0; --t) {
+            int64_t bth = (b * L + t) * H + h;
+            double a = exp(logdecay[bth]), be = beta[bth], ga = gamma[bth];
+            const double *Xt = X + bth * PR, *Xq = t ? X + (bth - H) * PR : Xp;
+            const double *Bc = Bt + (t + 1) * NR, *Bq = Bt + t * NR, *Cc = Ct + t * NR;
+            const double *dYt = dY + bth * PR;
+            const double *Sc = S + (t + 1) * NP, *Sp = S + t * NP;
+            double *dXq = t ? dX + (bth - H) * PR : dXp;
+            for (int64_t n = 0; n < N; ++n)
+                for (int64_t p = 0; p < P; ++p) {
+                    double acc = 0.0;
+                    for (int64_t r = 0; r < R; ++r) acc += Cc[n * R + r] * dYt[p * R + r];
+                    A[n * P + p] += acc;
+                }
+            for (int64_t n = 0; n < N; ++n)
+                for (int64_t r = 0; r < R; ++r) {
+                    double sacc = 0.0;
+                    for (int64_t p = 0; p < P; ++p) sacc += Sc[n * P + p] * dYt[p * R + r];
+                    dCt[t * NR + n * R + r] = sacc;
+                }
+            double sg = 0.0, sb = 0.0;
+            for (int64_t r = 0; r < R; ++r) {
+                for (int64_t p = 0; p < P; ++p) {          /* gamma term */
+                    double acc = 0.0;
+                    for (int64_t n = 0; n < N; ++n) acc += A[n * P + p] * Bc[n * R + r];
+                    v[p] = acc;
+                    sg += Xt[p * R + r] * acc;
+                    dX[bth * PR + p * R + r] += ga * acc;
+                }
+                for (int64_t p = 0; p < P; ++p) {          /* beta term */
+                    double acc = 0.0;
+                    for (int64_t n = 0; n < N; ++n) acc += A[n * P + p] * Bq[n * R + r];
+                    sb += Xq[p * R + r] * acc;
+                    dXq[p * R + r] += be * acc;
+                }
+                for (int64_t n = 0; n < N; ++n) {
+                    double vc = 0.0, vq = 0.0;
+                    for (int64_t p = 0; p < P; ++p) {
+                        vc += A[n * P + p] * Xt[p * R + r];
+                        vq += A[n * P + p] * Xq[p * R + r];
+                    }
+                    dBt[(t + 1) * NR + n * R + r] += ga * vc;
+                    dBt[t * NR + n * R + r] += be * vq;
+                }
+            }
+            dgamma[bth] = sg;
+            dbeta[bth] = sb;
+            double sl = 0.0;
+            for (int64_t i = 0; i < NP; ++i) sl += A[i] * Sp[i];
+            dld[bth] = a * sl;
+            for (int64_t i = 0; i < NP; ++i) A[i] *= a;
+        }
+        for (int64_t t = 0; t < L; ++t) {
+            int64_t bth = (b * L + t) * H + h;
+            for (int64_t r = 0; r < R; ++r) {
+                const double *bt = Bt + (t + 1) * NR + r, *dbt = dBt + (t + 1) * NR + r;
+                const double *ct = Ct + t * NR + r, *dct = dCt + t * NR + r;
+                for (int64_t k = 0; k < K; ++k) {
+                    double b0 = bt[(2 * k) * R], b1 = bt[(2 * k + 1) * R], db0 = dbt[(2 * k) * R], db1 = dbt[(2 * k + 1) * R];
+                    double c0 = ct[(2 * k) * R], c1 = ct[(2 * k + 1) * R], dc0 = dct[(2 * k) * R], dc1 = dct[(2 * k + 1) * R];
+                    if (theta) dTh[t * K + k] += (b0 * db1 - b1 * db0) + (c0 * dc1 - c1 * dc0);
+                    double phi = theta ? Th[t * K + k] : 0.0, cs = cos(phi), sn = sin(phi);
+                    /* R(-phi) */
+                    dB[bth * NR + (2 * k) * R + r] = cs * db0 + sn * db1;
+                    dB[bth * NR + (2 * k + 1) * R + r] = -sn * db0 + cs * db1;
+                    dC[bth * NR + (2 * k) * R + r] = cs * dc0 + sn * dc1;
+                    dC[bth * NR + (2 * k + 1) * R + r] = -sn * dc0 + cs * dc1;
+                }
+            }
+        }
+        if (theta)
+            for (int64_t k = 0; k < K; ++k) {
+                double acc = 0.0;
+                for (int64_t t = L - 1; t >= 0; --t) {
+                    acc += dTh[t * K + k];
+                    dtheta[((b * L + t) * H + h) * K + k] = acc;
+                }
+            }
+        if (dh0)
+            for (int64_t i = 0; i < NP; ++i) dh0[(b * H + h) * NP + i] = A[i];
+        if (dX_prev0)
+            for (int64_t i = 0; i < PR; ++i) dX_prev0[(b * H + h) * PR + i] = dXp[i];
+        if (dB_prev0)
+            for (int64_t i = 0; i < NR; ++i) dB_prev0[(b * H + h) * NR + i] = dBt[i];
+        free(S); free(Bt); free(Ct); free(Th); free(A); free(dBt); free(dCt); free(Xp); free(dXp); free(dTh); free(v);
+    }
+}
+
+/*
  * Decode step of the SSD family, one token per (b, h), state in the physical
  * (unrotated) frame.  The rotated-frame state of oracle_trap / oracle_mimo is
  * S~_t = R(Theta_t) S_t (pairwise along N); since plane rotations compose

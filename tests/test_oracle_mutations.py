@@ -70,6 +70,11 @@ MUTATIONS = {
                            "(bt[2 * k + 1] * dbt[2 * k] - bt[2 * k] * dbt[2 * k + 1])"),
     "trapbwd_no_hout_rotation_term": ("dTh[(L - 1) * K + k] += acc;", ""),
     "trapbwd_unrotate_wrong_way": ("double phi = theta ? -Th[t * K + k] : 0.0;", "double phi = theta ? Th[t * K + k] : 0.0;"),
+    "mimobwd_beta_term_uses_current_rank_row": ("dBt[t * NR + n * R + r] += be * vq;", "dBt[t * NR + n * R + r] += be * vc;"),
+    "mimobwd_dC_drops_rank": ("for (int64_t p = 0; p < P; ++p) sacc += Sc[n * P + p] * dYt[p * R + r];",
+                               "for (int64_t p = 0; p < P; ++p) sacc += Sc[n * P + p] * dYt[p * R];"),
+    "mimobwd_no_angle_from_C": ("if (theta) dTh[t * K + k] += (b0 * db1 - b1 * db0) + (c0 * dc1 - c1 * dc0);",
+                                "if (theta) dTh[t * K + k] += (b0 * db1 - b1 * db0);"),
 }
 
 
@@ -182,6 +187,24 @@ def _battery(o):
         fd = (losst(dict(inp, **{k: inp[k] + 1e-6 * v})) - losst(dict(inp, **{k: inp[k] - 1e-6 * v}))) / 2e-6
         if abs(fd - float(np.sum(gk * v))) > 1e-6 * max(1.0, abs(fd)):
             failed.append("trap_bwd_directional_" + k)
+
+    # backward of the MIMO recurrence: directional derivatives of the forward loss
+    inp = wl.mimo_inputs(rng, 1, 7, 2, 3, 4, 2, h0_sd=0.4)
+    inp["X_prev"] = rng.standard_normal((1, 2, 3, 2))
+    inp["B_prev"] = rng.standard_normal((1, 2, 4, 2))
+    dY = rng.standard_normal(inp["X"].shape)
+    dh = rng.standard_normal(inp["h0"].shape)
+
+    def lossq(d):
+        Yf, hf = o.mimo(**d)
+        return float(np.sum(Yf * dY) + np.sum(hf * dh))
+    gr = o.mimo_bwd(inp["X"], inp["logdecay"], inp["B"], inp["C"], inp["beta"], inp["gamma"], dY, inp["theta"],
+                    inp["h0"], dh, inp["X_prev"], inp["B_prev"])
+    for k, gk in zip(("X", "logdecay", "B", "C", "beta", "gamma", "theta", "h0", "X_prev", "B_prev"), gr):
+        v = rng.standard_normal(inp[k].shape)
+        fd = (lossq(dict(inp, **{k: inp[k] + 1e-6 * v})) - lossq(dict(inp, **{k: inp[k] - 1e-6 * v}))) / 2e-6
+        if abs(fd - float(np.sum(gk * v))) > 1e-6 * max(1.0, abs(fd)):
+            failed.append("mimo_bwd_directional_" + k)
 
     inp = wl.m1_block_inputs(rng, 2, 15, 3, 4, K=4, h0_sd=0.3, hist=True)
     y, h = o.m1_block(**inp)
