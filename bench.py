@@ -117,6 +117,18 @@ def siso_bwd_work(b, L, H, P, N, G, Q=64):
     return nbytes, flops
 
 
+def mimo_bwd_work(b, L, H, P, N, R, Q=64):
+    """Backward of the Mamba-3 MIMO recurrence: inputs and their gradients moved
+    once; flops of the chunkwise two-term rank-R form (Q rows, Q/R steps per
+    chunk): 16NPR for the local states and the state products, R^2 (Q/R + 1)
+    (4P + 6N) for the scores and masked products.  With R = 1 this is the SISO
+    count.  The library runs it as a one-term SSD over (3R - 1) L rows."""
+    Qt = Q // R
+    nbytes = 4 * (3 * b * L * H * P * R + 4 * b * L * H * N * R + 6 * b * L * H + b * L * H * N + 2 * b * H * N * P)
+    flops = b * L * H * (16 * N * P * R + R * R * (Qt + 1) * (4 * P + 6 * N))
+    return nbytes, flops
+
+
 def ssd_step_work(b, H, P, N, G, R, trap, rot, es=4):
     """One decode token: the fp32 state read and written once, plus the token's
     inputs and output."""
@@ -349,6 +361,33 @@ class SISOBwd(Workload):
                                 None, t["dh_out"], ws=self.ws)
 
 
+class MIMOBwd(Workload):
+    """Backward of the Mamba-3 MIMO recurrence at the block shape (outside the
+    step, measured beside it)."""
+    name = "mimo_bwd"
+    kernel = "angle and row kernels + the SSD backward over (3R - 1) L rows + the mapping back"
+    source = "selective_state_space_amd/csrc/ssd_bwd.hip"
+    bound = "mfma"
+
+    def __init__(self, mb, wl, torch):
+        self.mb = mb
+        b, L, H, P, N, R = 2, 8192, 16, 64, 128, 4
+        self.shape = dict(batch=b, L=L, H=H, P=P, N=N, R=R, trapezoid=True, rotation=True)
+        inp = wl.mimo_bwd_block()
+        self.inp = inp
+        self.t = {k: _dev(v, torch.float32) for k, v in inp.items() if v is not None}
+        self.ws = torch.empty(mb.mb_workspace_size(mb.MB_OP_MIMO_SSD_BWD, b, L, H, P, 1, N, R),
+                              dtype=torch.uint8, device="cuda")
+        self.tokens = b * L
+        self.bytes, self.flops = mimo_bwd_work(b, L, H, P, N, R)
+        self.exps = None
+
+    def run(self):
+        t = self.t
+        self.mb.mb_mimo_ssd_bwd(t["X"], t["logdecay"], t["B"], t["C"], t["beta"], t["gamma"], t["dY"], t["theta"],
+                                None, t["dh_out"], ws=self.ws)
+
+
 class SISO(Workload):
     name = "siso"
     kernel = "k_walk (state-only pass) + k_walk (full pass)"
@@ -437,8 +476,8 @@ class SSDDecode(Workload):
 ALL = ["m1_scan", "m1_step", "ssd_f32", "ssd_bf16", "siso", "mimo"]
 # measured beside the step, not part of it: the decode steps of the SSD family, the
 # Mamba-1 scan with the block prologue and epilogue fused, and the backwards of the
-# Mamba-2 SSD, the Mamba-1 scan and Mamba-3 SISO
-NEXT = ["m2_decode", "siso_decode", "mimo_decode", "m1_fused", "ssd_bwd", "m1_bwd", "siso_bwd"]
+# Mamba-2 SSD, the Mamba-1 scan, Mamba-3 SISO and MIMO
+NEXT = ["m2_decode", "siso_decode", "mimo_decode", "m1_fused", "ssd_bwd", "m1_bwd", "siso_bwd", "mimo_bwd"]
 
 
 def make(name, mb, wl, torch):
@@ -454,6 +493,8 @@ def make(name, mb, wl, torch):
         return M1Bwd(mb, wl, torch)
     if name == "siso_bwd":
         return SISOBwd(mb, wl, torch)
+    if name == "mimo_bwd":
+        return MIMOBwd(mb, wl, torch)
     if name == "ssd_f32":
         return SSD(mb, wl, torch, "f32")
     if name == "ssd_bf16":

@@ -63,7 +63,8 @@ typedef enum {
     MB_OP_MIMO_SSD = 4,
     MB_OP_SSD_CHUNKED_BWD = 5,
     MB_OP_SELECTIVE_SCAN_BWD = 6,
-    MB_OP_TRAP_SSD_BWD = 7
+    MB_OP_TRAP_SSD_BWD = 7,
+    MB_OP_MIMO_SSD_BWD = 8
 } mb_op;
 
 /*
@@ -279,6 +280,36 @@ mb_status mb_selective_scan_bwd(const float* x, const float* dt, const float* A,
                                 float* dA, float* dB, float* dC, float* dD, float* dh0,
                                 int64_t batch, int64_t L, int64_t D, int64_t N, mb_dtype dtype,
                                 void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Backward of mb_mimo_ssd (fp32): the vector-Jacobian product of the Mamba-3
+ * MIMO recurrence (TorchMamba README, Math notes MIMO; trained by
+ * back-propagation through time, as the mamba-rs page lists): the gradients of
+ * sum dY . Y + sum dh_out . h_out  with respect to X, logdecay, B, C, beta,
+ * gamma, theta, h0 and the previous token, as mb_trap_ssd_bwd with R ranks per
+ * step (the adjoint takes the R output ranks; every rank has both trapezoid
+ * terms; the angle gradient sums over the ranks of B and C).
+ * Arguments as mb_mimo_ssd (X, dY, dX (batch, L, H, P, R); B, C, dB, dC
+ * (batch, L, H, N, R); X_prev, dX_prev (batch, H, P, R); B_prev, dB_prev
+ * (batch, H, N, R)), gradients shaped like their inputs; theta NULL = no
+ * rotation (dtheta not written); X_prev, B_prev both given or both NULL; dh0,
+ * dX_prev, dB_prev NULL = not wanted.
+ * ws / ws_bytes: device workspace of at least
+ * mb_workspace_size(MB_OP_MIMO_SSD_BWD, batch, L, H, P, <G ignored>, N, R, 0)
+ * bytes, 256-byte aligned; it holds the sequence as (3R - 1) L rows of a plain
+ * SSD (about 11 GB at batch 2, L 8192, H 16, P 64, N 128, R 4).
+ * Supported: dtype MB_F32 (MB_ERR_DTYPE otherwise); N in {64, 128}, P in {32,
+ * 64}, R in {1, 2, 4, 8, 16} (MB_ERR_SHAPE otherwise); h0, dh_out, dh0 16-byte aligned
+ * (MB_ERR_ALIGN).  No output may overlap an input, another output or the
+ * workspace (MB_ERR_ALIAS).
+ */
+mb_status mb_mimo_ssd_bwd(const float* X, const float* logdecay, const float* B, const float* C,
+                          const float* beta, const float* gamma, const float* theta, const float* h0,
+                          const float* X_prev, const float* B_prev, const float* dY,
+                          const float* dh_out, float* dX, float* dlogdecay, float* dB, float* dC,
+                          float* dbeta, float* dgamma, float* dtheta, float* dh0, float* dX_prev,
+                          float* dB_prev, int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N,
+                          int64_t R, mb_dtype dtype, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * Backward of mb_trap_ssd (fp32): the vector-Jacobian product of the Mamba-3

@@ -16,9 +16,10 @@ import threading
 
 __all__ = [
     "mb_selective_scan", "mb_ssm_step", "mb_ssd_chunked", "mb_trap_ssd", "mb_mimo_ssd",
-    "mb_ssd_step", "mb_selective_scan_fused", "mb_ssd_chunked_bwd", "mb_selective_scan_bwd", "mb_trap_ssd_bwd", "mb_workspace_size", "mb_status_str", "lib_path", "load_library", "MBError",
+    "mb_ssd_step", "mb_selective_scan_fused", "mb_ssd_chunked_bwd", "mb_selective_scan_bwd", "mb_trap_ssd_bwd", "mb_mimo_ssd_bwd", "mb_workspace_size", "mb_status_str", "lib_path", "load_library", "MBError",
     "MB_OP_SELECTIVE_SCAN", "MB_OP_SSM_STEP", "MB_OP_SSD_CHUNKED", "MB_OP_TRAP_SSD",
     "MB_OP_MIMO_SSD", "MB_OP_SSD_CHUNKED_BWD", "MB_OP_SELECTIVE_SCAN_BWD", "MB_OP_TRAP_SSD_BWD",
+    "MB_OP_MIMO_SSD_BWD",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -28,7 +29,8 @@ _lib = None
 
 MB_F32, MB_BF16 = 0, 1
 (MB_OP_SELECTIVE_SCAN, MB_OP_SSM_STEP, MB_OP_SSD_CHUNKED, MB_OP_TRAP_SSD,
- MB_OP_MIMO_SSD, MB_OP_SSD_CHUNKED_BWD, MB_OP_SELECTIVE_SCAN_BWD, MB_OP_TRAP_SSD_BWD) = range(8)
+ MB_OP_MIMO_SSD, MB_OP_SSD_CHUNKED_BWD, MB_OP_SELECTIVE_SCAN_BWD, MB_OP_TRAP_SSD_BWD,
+ MB_OP_MIMO_SSD_BWD) = range(9)
 
 _vp = ctypes.c_void_p
 _i64 = ctypes.c_int64
@@ -68,6 +70,9 @@ def load_library():
             lib.mb_workspace_size.restype = ctypes.c_size_t
             for f in ("mb_ssd_chunked", "mb_trap_ssd", "mb_mimo_ssd"):
                 getattr(lib, f).restype = ctypes.c_int
+        if hasattr(lib, "mb_mimo_ssd_bwd"):
+            lib.mb_mimo_ssd_bwd.argtypes = [_vp] * 22 + [_i64] * 6 + [ctypes.c_int, _vp, ctypes.c_size_t, _vp]
+            lib.mb_mimo_ssd_bwd.restype = ctypes.c_int
         if hasattr(lib, "mb_trap_ssd_bwd"):
             lib.mb_trap_ssd_bwd.argtypes = [_vp] * 22 + [_i64] * 6 + [ctypes.c_int, _vp, ctypes.c_size_t, _vp]
             lib.mb_trap_ssd_bwd.restype = ctypes.c_int
@@ -301,6 +306,41 @@ def mb_trap_ssd_bwd(X, logdecay, B, C, beta, gamma, dY, theta=None, h0=None, dh_
     _call("mb_trap_ssd_bwd", _ptr(X), _ptr(logdecay), _ptr(B), _ptr(C), _ptr(beta), _ptr(gamma), _ptr(theta),
           _ptr(h0), _ptr(X_prev), _ptr(B_prev), _ptr(dY), _ptr(dh_out), _ptr(dX), _ptr(dld), _ptr(dB), _ptr(dC),
           _ptr(dbeta), _ptr(dgamma), _ptr(dtheta), _ptr(dh0), _ptr(dXp), _ptr(dBp), b, L, H, P, G, N, MB_F32,
+          _ptr(ws), nws, _stream(dev))
+    return dX, dld, dB, dC, dbeta, dgamma, dtheta, dh0, dXp, dBp
+
+
+def mb_mimo_ssd_bwd(X, logdecay, B, C, beta, gamma, dY, theta=None, h0=None, dh_out=None, *, X_prev=None,
+                    B_prev=None, ws=None):
+    """Backward of the Mamba-3 MIMO recurrence (float32).  Shapes as mb_mimo_ssd;
+    dY like X, dh_out like h0.  Returns (dX, dlogdecay, dB, dC, dbeta, dgamma,
+    dtheta or None, dh0, dX_prev or None, dB_prev or None)."""
+    torch = _torch()
+    dev = _device_of(X)
+    f32 = torch.float32
+    b, L, H, P, R = X.shape
+    N = B.shape[3]
+    _check(X, "X", (b, L, H, P, R), f32, dev)
+    for t, n in ((logdecay, "logdecay"), (beta, "beta"), (gamma, "gamma")):
+        _check(t, n, (b, L, H), f32, dev)
+    _check(B, "B", (b, L, H, N, R), f32, dev)
+    _check(C, "C", (b, L, H, N, R), f32, dev)
+    _check(dY, "dY", (b, L, H, P, R), f32, dev)
+    _check(theta, "theta", (b, L, H, N // 2), f32, dev)
+    _check(h0, "h0", (b, H, N, P), f32, dev)
+    _check(dh_out, "dh_out", (b, H, N, P), f32, dev)
+    _check(X_prev, "X_prev", (b, H, P, R), f32, dev)
+    _check(B_prev, "B_prev", (b, H, N, R), f32, dev)
+    e = lambda shp: torch.empty(shp, dtype=f32, device=dev)
+    dX, dld, dB, dC = e((b, L, H, P, R)), e((b, L, H)), e((b, L, H, N, R)), e((b, L, H, N, R))
+    dbeta, dgamma, dh0 = e((b, L, H)), e((b, L, H)), e((b, H, N, P))
+    dtheta = e((b, L, H, N // 2)) if theta is not None else None
+    dXp = e((b, H, P, R)) if X_prev is not None else None
+    dBp = e((b, H, N, R)) if B_prev is not None else None
+    ws, nws = _workspace(MB_OP_MIMO_SSD_BWD, dev, ws, (b, L, H, P, 1, N, R, 0))
+    _call("mb_mimo_ssd_bwd", _ptr(X), _ptr(logdecay), _ptr(B), _ptr(C), _ptr(beta), _ptr(gamma), _ptr(theta),
+          _ptr(h0), _ptr(X_prev), _ptr(B_prev), _ptr(dY), _ptr(dh_out), _ptr(dX), _ptr(dld), _ptr(dB), _ptr(dC),
+          _ptr(dbeta), _ptr(dgamma), _ptr(dtheta), _ptr(dh0), _ptr(dXp), _ptr(dBp), b, L, H, P, N, R, MB_F32,
           _ptr(ws), nws, _stream(dev))
     return dX, dld, dB, dC, dbeta, dgamma, dtheta, dh0, dXp, dBp
 

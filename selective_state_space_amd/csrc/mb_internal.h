@@ -52,6 +52,9 @@ int device_cu_count();
 // Workspace bytes of the Mamba-1 scan backward (0 for unsupported sizes).
 size_t m1_bwd_workspace(int64_t batch, int64_t L, int64_t D, int64_t N);
 
+// Workspace bytes of the Mamba-3 MIMO backward (0 for unsupported sizes).
+size_t mimo_bwd_workspace(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N, int64_t R);
+
 // Workspace bytes of the Mamba-3 SISO backward (0 for unsupported sizes).
 size_t trap_bwd_workspace(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t G, int64_t N);
 

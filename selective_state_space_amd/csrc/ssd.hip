@@ -1908,6 +1908,7 @@ extern "C" size_t mb_workspace_size(mb_op op, int64_t batch, int64_t L, int64_t 
     if (op == MB_OP_SELECTIVE_SCAN || op == MB_OP_SSM_STEP) return 0;
     if (op == MB_OP_SSD_CHUNKED_BWD) return ssd_bwd_workspace(batch, L, H, P, G, N);
     if (op == MB_OP_TRAP_SSD_BWD) return trap_bwd_workspace(batch, L, H, P, G, N);
+    if (op == MB_OP_MIMO_SSD_BWD) return mimo_bwd_workspace(batch, L, H, P, N, R);
     // Mamba-1 backward: the sizes (batch, L, D, N) travel as (batch, L, H, N)
     if (op == MB_OP_SELECTIVE_SCAN_BWD) return m1_bwd_workspace(batch, L, H, N);
     if (!dims_ok(batch, L, H, P, N)) return 0;

@@ -1115,3 +1115,358 @@ extern "C" mb_status mb_trap_ssd_bwd(const float* X, const float* logdecay, cons
     }
     return check_launch();
 }
+
+// ===========================================================================
+// Backward of the Mamba-3 MIMO recurrence (mb_mimo_ssd_bwd), the same way: with
+// rank R a step becomes RS = 3R - 1 rows of a plain SSD, in order
+//   rows 0 .. R-1      beta terms:  Bt_{t-1,r}, beta_t X_{t-1,r}   (row 0 decays by e^{ld_t})
+//   rows R .. 2R-1     gamma terms: Bt_{t,r},   gamma_t X_{t,r}    (row 2R-1 also outputs rank 0)
+//   rows 2R .. 3R-2    outputs of ranks 1 .. R-1 (no input)
+// so every output of step t follows all of its inputs.  B, C are per head (no
+// groups) with the rank innermost: (batch, L, H, N, R); X, dY (batch, L, H, P, R).
+// ===========================================================================
+namespace mb {
+namespace {
+
+struct MimoBwd {
+    const float *X, *ld, *B, *C, *beta, *gamma, *theta, *Xp, *Bp, *dY, *dh_out;
+    float *dX, *dld, *dB, *dC, *dbeta, *dgamma, *dtheta, *dXp, *dBp;
+    float *X2, *dY2, *B2, *C2, *ld2, *dX2, *dld2, *dB2, *dC2;
+    float *Th, *dTh, *seg, *hterm, *dh2, *hfin;
+    int L, H, N, P, R, RS, nseg, batch;
+};
+
+// TrapBwd view of the fields the shared angle kernels use
+TrapBwd as_trap(const MimoBwd& m) {
+    TrapBwd t{};
+    t.theta = m.theta; t.dh_out = m.dh_out; t.dtheta = m.dtheta;
+    t.Th = m.Th; t.dTh = m.dTh; t.seg = m.seg; t.hterm = m.hterm; t.dh2 = m.dh2; t.hfin = m.hfin;
+    t.L = m.L; t.H = m.H; t.G = m.H; t.N = m.N; t.P = m.P; t.nseg = m.nseg; t.batch = m.batch;
+    return t;
+}
+
+// angles and the rotated per-rank B, C rows of every row of a step: one wave per
+// (batch, head, segment), lane = pair
+template <int R>
+__global__ __launch_bounds__(64) void k_mb_prep_bc(MimoBwd a) {
+    const int sg = blockIdx.x % a.nseg, bh = blockIdx.x / a.nseg;
+    const int b = bh / a.H, h = bh % a.H, K = a.N / 2, k = threadIdx.x, RS = a.RS;
+    if (k >= K) return;
+    double th = 0.0;
+    if (a.theta)
+        for (int s2 = 0; s2 < sg; ++s2) th += (double)a.seg[((size_t)bh * a.nseg + s2) * K + k];
+    const size_t L2 = (size_t)RS * a.L;
+    auto row = [&](float* base, size_t t2) { return base + (((size_t)b * L2 + t2) * a.H + h) * a.N + 2 * k; };
+    const float2 z2 = make_float2(0.0f, 0.0f);
+    if (sg == 0)
+        for (int r = 0; r < R; ++r) {
+            // step 0's beta rows: the previous token, unrotated
+            const float* bp = a.Bp ? a.Bp + ((size_t)b * a.H + h) * a.N * R : nullptr;
+            *(float2*)row(a.B2, r) = bp ? make_float2(bp[(2 * k) * R + r], bp[(2 * k + 1) * R + r]) : z2;
+        }
+    const float* __restrict__ thv = a.theta;
+    const float* __restrict__ Bv = a.B;
+    const float* __restrict__ Cv = a.C;
+    const int t1 = min(a.L, (sg + 1) * kSeg);
+    for (int t = sg * kSeg; t < t1; ++t) {
+        const size_t bth = ((size_t)b * a.L + t) * a.H + h;
+        if (thv) th += (double)thv[bth * K + k];
+        const double rv = th * 0.15915494309189535;
+        const float f = (float)(rv - rint(rv));
+        a.Th[bth * K + k] = f;
+        float sn, cs;
+        sincos_frac(f, &sn, &cs);
+        const size_t t0 = (size_t)RS * t;
+        // the pair's R ranks of B and C, contiguous (rank innermost)
+        float bq0[R], bq1[R], cq0[R], cq1[R];
+        const float* bs = Bv + bth * a.N * R;
+        const float* cs_ = Cv + bth * a.N * R;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            bq0[r] = bs[(2 * k) * R + r];
+            bq1[r] = bs[(2 * k + 1) * R + r];
+            cq0[r] = cs_[(2 * k) * R + r];
+            cq1[r] = cs_[(2 * k + 1) * R + r];
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const float b0 = bq0[r], b1 = bq1[r], c0 = cq0[r], c1 = cq1[r];
+            const float2 br = make_float2(cs * b0 - sn * b1, sn * b0 + cs * b1);
+            const float2 cr = make_float2(cs * c0 - sn * c1, sn * c0 + cs * c1);
+            *(float2*)row(a.B2, t0 + R + r) = br;                               // gamma row r
+            if (t + 1 < a.L) *(float2*)row(a.B2, t0 + RS + r) = br;              // next step's beta row r
+            *(float2*)row(a.C2, t0 + 2 * R - 1 + r) = cr;                       // output row of rank r
+            *(float2*)row(a.C2, t0 + r) = z2;                                   // beta rows: no output
+            if (r < R - 1) *(float2*)row(a.C2, t0 + R + r) = z2;                // gamma rows but the last
+            if (r >= 1) *(float2*)row(a.B2, t0 + 2 * R - 1 + r) = z2;           // output-only rows: no input
+        }
+    }
+}
+
+// the per-row X, dY and log-decay: one thread per (batch, step, head, column)
+__global__ __launch_bounds__(256) void k_mb_prep_x(MimoBwd a) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int b = blockIdx.y, R = a.R, RS = a.RS;
+    if (i >= (int64_t)a.L * a.H * a.P) return;
+    const int p = (int)(i % a.P);
+    const int64_t th = i / a.P;
+    const int h = (int)(th % a.H), t = (int)(th / a.H);
+    const size_t bth = (size_t)b * a.L * a.H + th;
+    const float be = a.beta[bth], ga = a.gamma[bth];
+    const size_t rowbase = ((size_t)b * RS * a.L + (size_t)RS * t) * a.H + h;   // row (t, 0)
+    auto at = [&](float* base, int j) { return base + (rowbase + (size_t)j * a.H) * a.P + p; };
+    for (int r = 0; r < R; ++r) {
+        const float xt = a.X[(bth * a.P + p) * R + r];
+        const float xq = t > 0 ? a.X[((bth - a.H) * a.P + p) * R + r]
+                               : (a.Xp ? a.Xp[(((size_t)b * a.H + h) * a.P + p) * R + r] : 0.0f);
+        *at(a.X2, r) = be * xq;
+        *at(a.X2, R + r) = ga * xt;
+        *at(a.dY2, r) = 0.0f;
+        if (r < R - 1) *at(a.dY2, R + r) = 0.0f;
+        *at(a.dY2, 2 * R - 1 + r) = a.dY[(bth * a.P + p) * R + r];
+        if (r >= 1) *at(a.X2, 2 * R - 1 + r) = 0.0f;
+    }
+    if (p == 0)
+        for (int j = 0; j < RS; ++j) a.ld2[rowbase + (size_t)j * a.H] = j == 0 ? a.ld[bth] : 0.0f;
+}
+
+// dX, dgamma, dbeta, dlogdecay, dX_prev: one wave per (batch, step, head), lane = column
+__global__ __launch_bounds__(64) void k_mb_post_x(MimoBwd a) {
+    const int64_t bth = blockIdx.x;
+    const int h = (int)(bth % a.H);
+    const int t = (int)((bth / a.H) % a.L), b = (int)(bth / ((int64_t)a.H * a.L));
+    const int p = threadIdx.x, R = a.R, RS = a.RS;
+    const bool ok = p < a.P;
+    const size_t rowbase = ((size_t)b * RS * a.L + (size_t)RS * t) * a.H + h;
+    auto rowp = [&](int j) { return (rowbase + (size_t)j * a.H) * a.P + p; };
+    const float ga = a.gamma[bth], be = a.beta[bth];
+    const float bn = t + 1 < a.L ? a.beta[bth + a.H] : 0.0f;
+    float sg = 0.0f, sb = 0.0f;
+    for (int r = 0; r < R; ++r) {
+        const float d1 = ok ? a.dX2[rowp(R + r)] : 0.0f;                     // d(gamma_t X_{t,r})
+        const float d0 = ok ? a.dX2[rowp(r)] : 0.0f;                         // d(beta_t X_{t-1,r})
+        const float dn = (ok && t + 1 < a.L) ? a.dX2[rowp(RS + r)] : 0.0f;   // d(beta_{t+1} X_{t,r})
+        const float xt = ok ? a.X[(bth * a.P + p) * R + r] : 0.0f;
+        const float xq = !ok ? 0.0f : t > 0 ? a.X[((bth - a.H) * a.P + p) * R + r]
+                                           : (a.Xp ? a.Xp[(((size_t)b * a.H + h) * a.P + p) * R + r] : 0.0f);
+        if (ok) a.dX[(bth * a.P + p) * R + r] = fmaf(ga, d1, bn * dn);
+        if (ok && t == 0 && a.dXp) a.dXp[(((size_t)b * a.H + h) * a.P + p) * R + r] = be * d0;
+        sg = fmaf(xt, d1, sg);
+        sb = fmaf(xq, d0, sb);
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        sg += __shfl_xor(sg, off, 64);
+        sb += __shfl_xor(sb, off, 64);
+    }
+    if (p == 0) {
+        a.dgamma[bth] = sg;
+        a.dbeta[bth] = sb;
+        a.dld[bth] = a.dld2[rowbase];
+    }
+}
+
+// dB, dC per rank in the physical frame, the angle gradient summed over ranks,
+// dB_prev: one wave per (batch, step, head), lane = pair
+template <int R>
+__global__ __launch_bounds__(64) void k_mb_post_bc(MimoBwd a) {
+    const int64_t bth = blockIdx.x;
+    const int h = (int)(bth % a.H);
+    const int t = (int)((bth / a.H) % a.L), b = (int)(bth / ((int64_t)a.H * a.L));
+    const int K = a.N / 2, k = threadIdx.x, RS = a.RS;
+    if (k >= K) return;
+    const size_t rowbase = ((size_t)b * RS * a.L + (size_t)RS * t) * a.H + h;
+    auto ld2 = [&](const float* base, int j) {
+        return *(const float2*)(base + (rowbase + (size_t)j * a.H) * a.N + 2 * k);
+    };
+    const float th = a.theta ? a.Th[bth * K + k] : 0.0f;
+    float sn, cs;
+    sincos_frac(th, &sn, &cs);
+    float dth = 0.0f;
+    const float* bs = a.B + bth * a.N * R;
+    const float* cs_ = a.C + bth * a.N * R;
+    // the pair's R ranks, loaded and stored whole (rank innermost)
+    float bq0[R], bq1[R], cq0[R], cq1[R], ob0[R], ob1[R], oc0[R], oc1[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        bq0[r] = bs[(2 * k) * R + r];
+        bq1[r] = bs[(2 * k + 1) * R + r];
+        cq0[r] = cs_[(2 * k) * R + r];
+        cq1[r] = cs_[(2 * k + 1) * R + r];
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        float2 dbr = ld2(a.dB2, R + r);
+        if (t + 1 < a.L) {
+            const float2 u = ld2(a.dB2, RS + r);
+            dbr.x += u.x;
+            dbr.y += u.y;
+        }
+        const float2 dcr = ld2(a.dC2, 2 * R - 1 + r);
+        const float b0 = bq0[r], b1 = bq1[r], c0 = cq0[r], c1 = cq1[r];
+        const float2 br = make_float2(cs * b0 - sn * b1, sn * b0 + cs * b1);
+        const float2 cr = make_float2(cs * c0 - sn * c1, sn * c0 + cs * c1);
+        dth += (br.x * dbr.y - br.y * dbr.x) + (cr.x * dcr.y - cr.y * dcr.x);
+        ob0[r] = cs * dbr.x + sn * dbr.y;
+        ob1[r] = -sn * dbr.x + cs * dbr.y;
+        oc0[r] = cs * dcr.x + sn * dcr.y;
+        oc1[r] = -sn * dcr.x + cs * dcr.y;
+        if (t == 0 && a.dBp) {
+            const float2 u = ld2(a.dB2, r);   // step 0's beta rows: unrotated
+            float* dbp = a.dBp + ((size_t)b * a.H + h) * a.N * R;
+            dbp[(2 * k) * R + r] = u.x;
+            dbp[(2 * k + 1) * R + r] = u.y;
+        }
+    }
+    float* db = a.dB + bth * a.N * R;
+    float* dc = a.dC + bth * a.N * R;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        db[(2 * k) * R + r] = ob0[r];
+        db[(2 * k + 1) * R + r] = ob1[r];
+        dc[(2 * k) * R + r] = oc0[r];
+        dc[(2 * k + 1) * R + r] = oc1[r];
+    }
+    if (a.theta) a.dTh[bth * K + k] = dth;
+}
+
+struct MimoBwdPlan {
+    BwdPlan ssd;
+    size_t off_x2, off_dy2, off_b2, off_c2, off_ld2, off_dx2, off_dld2, off_db2, off_dc2, off_th, off_dth, off_seg,
+        off_hterm, off_dh2, off_hfin, bytes;
+};
+
+MimoBwdPlan mimo_bwd_plan(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N, int64_t R) {
+    MimoBwdPlan p{};
+    const int64_t L2 = (3 * R - 1) * L;
+    p.ssd = bwd_plan(batch, L2, H, P, N);
+    size_t off = p.ssd.bytes;
+    const size_t nx = (size_t)(batch * L2 * H * P) * 4, nb = (size_t)(batch * L2 * H * N) * 4;
+    const size_t nl = (size_t)(batch * L2 * H) * 4, nth = (size_t)(batch * L * H * (N / 2)) * 4;
+    const size_t nseg = (size_t)((L + kSeg - 1) / kSeg), nh = (size_t)(batch * H * N * P) * 4;
+    auto take = [&](size_t bytes) { const size_t o = off; off += align256(bytes); return o; };
+    p.off_x2 = take(nx); p.off_dy2 = take(nx); p.off_b2 = take(nb); p.off_c2 = take(nb); p.off_ld2 = take(nl);
+    p.off_dx2 = take(nx); p.off_dld2 = take(nl); p.off_db2 = take(nb); p.off_dc2 = take(nb);
+    p.off_th = take(nth); p.off_dth = take(nth);
+    p.off_seg = take((size_t)(batch * H) * nseg * (N / 2) * 4);
+    p.off_hterm = take((size_t)(batch * H * (N / 2)) * 4);
+    p.off_dh2 = take(nh); p.off_hfin = take(nh);
+    p.bytes = off;
+    return p;
+}
+
+bool mimo_bwd_ok(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N, int64_t R) {
+    if (R != 1 && R != 2 && R != 4 && R != 8 && R != 16) return false;
+    if (!bwd_dims_ok(batch, (3 * R - 1) * L, H, P, H, N)) return false;
+    if (batch * L * H > INT32_MAX) return false;
+    return true;
+}
+
+}  // namespace
+
+size_t mimo_bwd_workspace(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N, int64_t R) {
+    if (!mimo_bwd_ok(batch, L, H, P, N, R) || batch == 0 || L == 0) return 0;
+    return mimo_bwd_plan(batch, L, H, P, N, R).bytes;
+}
+
+}  // namespace mb
+
+extern "C" mb_status mb_mimo_ssd_bwd(const float* X, const float* logdecay, const float* B, const float* C,
+                                     const float* beta, const float* gamma, const float* theta, const float* h0,
+                                     const float* X_prev, const float* B_prev, const float* dY,
+                                     const float* dh_out, float* dX, float* dlogdecay, float* dB, float* dC,
+                                     float* dbeta, float* dgamma, float* dtheta, float* dh0, float* dX_prev,
+                                     float* dB_prev, int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N,
+                                     int64_t R, mb_dtype dtype, void* ws, size_t ws_bytes, hipStream_t stream)
+{
+    if (dtype != MB_F32) return MB_ERR_DTYPE;
+    if (!mimo_bwd_ok(batch, L, H, P, N, R)) return MB_ERR_SHAPE;
+    const size_t n_x = (size_t)(batch * L * H * P * R), n_b = (size_t)(batch * L * H * N * R);
+    const size_t n_l = (size_t)(batch * L * H), n_h = (size_t)(batch * H * N * P);
+    const size_t n_th = (size_t)(batch * L * H * (N / 2));
+    const size_t n_xp = (size_t)(batch * H * P * R), n_bp = (size_t)(batch * H * N * R);
+    if (n_x && (!X || !dY || !dX || !logdecay || !dlogdecay || !beta || !gamma || !dbeta || !dgamma))
+        return MB_ERR_NULL;
+    if (n_b && (!B || !C || !dB || !dC)) return MB_ERR_NULL;
+    if (theta && n_th && !dtheta) return MB_ERR_NULL;
+    if ((X_prev == nullptr) != (B_prev == nullptr)) return MB_ERR_NULL;
+    if (((uintptr_t)h0 | (uintptr_t)dh_out | (uintptr_t)dh0) & 15) return MB_ERR_ALIGN;
+    const Span ins[] = {{X, n_x * 4}, {logdecay, n_l * 4}, {B, n_b * 4}, {C, n_b * 4}, {beta, n_l * 4},
+                        {gamma, n_l * 4}, {theta, theta ? n_th * 4 : 0}, {h0, h0 ? n_h * 4 : 0},
+                        {X_prev, X_prev ? n_xp * 4 : 0}, {B_prev, B_prev ? n_bp * 4 : 0}, {dY, n_x * 4},
+                        {dh_out, dh_out ? n_h * 4 : 0}};
+    const Span outs[] = {{dX, n_x * 4}, {dlogdecay, n_l * 4}, {dB, n_b * 4}, {dC, n_b * 4}, {dbeta, n_l * 4},
+                         {dgamma, n_l * 4}, {dtheta, theta && dtheta ? n_th * 4 : 0}, {dh0, dh0 ? n_h * 4 : 0},
+                         {dX_prev, dX_prev ? n_xp * 4 : 0}, {dB_prev, dB_prev ? n_bp * 4 : 0}};
+    for (int i = 0; i < 10; ++i) {
+        if (overlaps_any(outs[i].p, outs[i].bytes, ins, 12)) return MB_ERR_ALIAS;
+        for (int j = i + 1; j < 10; ++j)
+            if (overlaps(outs[i].p, outs[i].bytes, outs[j].p, outs[j].bytes)) return MB_ERR_ALIAS;
+    }
+    if (batch == 0) return MB_OK;
+    if (L == 0) {
+        mb_status st = dh0 ? copy_state(dh_out, dh0, (int64_t)n_h, stream) : MB_OK;
+        if (st == MB_OK && dX_prev) st = copy_state(nullptr, dX_prev, (int64_t)n_xp, stream);
+        if (st == MB_OK && dB_prev) st = copy_state(nullptr, dB_prev, (int64_t)n_bp, stream);
+        return st;
+    }
+    const MimoBwdPlan pl = mimo_bwd_plan(batch, L, H, P, N, R);
+    if (!ws || ws_bytes < pl.bytes || ((uintptr_t)ws & 255)) return MB_ERR_WORKSPACE;
+    if (overlaps_any(ws, pl.bytes, ins, 12) || overlaps_any(ws, pl.bytes, outs, 10)) return MB_ERR_ALIAS;
+    char* w = (char*)ws;
+    MimoBwd m{};
+    m.X = X; m.ld = logdecay; m.B = B; m.C = C; m.beta = beta; m.gamma = gamma; m.theta = theta;
+    m.Xp = X_prev; m.Bp = B_prev; m.dY = dY; m.dh_out = dh_out;
+    m.dX = dX; m.dld = dlogdecay; m.dB = dB; m.dC = dC; m.dbeta = dbeta; m.dgamma = dgamma; m.dtheta = dtheta;
+    m.dXp = dX_prev; m.dBp = dB_prev;
+    m.X2 = (float*)(w + pl.off_x2); m.dY2 = (float*)(w + pl.off_dy2); m.B2 = (float*)(w + pl.off_b2);
+    m.C2 = (float*)(w + pl.off_c2); m.ld2 = (float*)(w + pl.off_ld2); m.dX2 = (float*)(w + pl.off_dx2);
+    m.dld2 = (float*)(w + pl.off_dld2); m.dB2 = (float*)(w + pl.off_db2); m.dC2 = (float*)(w + pl.off_dc2);
+    m.Th = (float*)(w + pl.off_th); m.dTh = (float*)(w + pl.off_dth); m.seg = (float*)(w + pl.off_seg);
+    m.hterm = (float*)(w + pl.off_hterm); m.dh2 = (float*)(w + pl.off_dh2); m.hfin = (float*)(w + pl.off_hfin);
+    m.L = (int)L; m.H = (int)H; m.N = (int)N; m.P = (int)P; m.R = (int)R; m.RS = (int)(3 * R - 1);
+    m.nseg = (int)((L + kSeg - 1) / kSeg);
+    m.batch = (int)batch;
+    const TrapBwd t = as_trap(m);
+    const unsigned nseg_all = (unsigned)(batch * H * m.nseg);
+    if (theta) hipLaunchKernelGGL(k_tb_segsum, dim3(nseg_all), dim3(64), 0, stream, t, theta, m.seg);
+#define MB_MIMO_R(KERNEL, GRID)                                                                   \
+    switch (R) {                                                                                  \
+    case 1: hipLaunchKernelGGL((KERNEL<1>), GRID, dim3(64), 0, stream, m); break;                 \
+    case 2: hipLaunchKernelGGL((KERNEL<2>), GRID, dim3(64), 0, stream, m); break;                 \
+    case 4: hipLaunchKernelGGL((KERNEL<4>), GRID, dim3(64), 0, stream, m); break;                 \
+    case 8: hipLaunchKernelGGL((KERNEL<8>), GRID, dim3(64), 0, stream, m); break;                 \
+    default: hipLaunchKernelGGL((KERNEL<16>), GRID, dim3(64), 0, stream, m); break;               \
+    }
+    MB_MIMO_R(k_mb_prep_bc, dim3(nseg_all));
+    hipLaunchKernelGGL(k_mb_prep_x, dim3((unsigned)((L * H * P + 255) / 256), (unsigned)batch), dim3(256), 0,
+                       stream, m);
+    if (dh_out)
+        hipLaunchKernelGGL(k_tb_rot_dh, dim3((unsigned)(((N / 2) * P + 255) / 256), (unsigned)(batch * H)),
+                           dim3(256), 0, stream, t);
+    BwdArgs a{};
+    a.X = m.X2; a.ld = m.ld2; a.B = m.B2; a.C = m.C2; a.h0 = h0; a.dY = m.dY2; a.dh_out = dh_out ? m.dh2 : nullptr;
+    a.dX = m.dX2; a.dld = m.dld2; a.dB = m.dB2; a.dC = m.dC2; a.dh0 = dh0;
+    a.st = (float*)w;
+    a.lam = (float*)(w + pl.ssd.off_lam);
+    a.tot = (float*)(w + pl.ssd.off_tot);
+    a.fin = (float*)(w + pl.ssd.off_fin);
+    a.h_final = m.hfin;
+    a.L = (int)((3 * R - 1) * L); a.H = (int)H; a.G = (int)H; a.N = (int)N; a.P = (int)P;
+    a.nch = (int)pl.ssd.nch; a.nfin = (int)pl.ssd.nfin;
+    mb_status st;
+    if (N == 128)
+        st = P == 64 ? bwd_launch<128, 64>(a, batch, stream) : bwd_launch<128, 32>(a, batch, stream);
+    else
+        st = P == 64 ? bwd_launch<64, 64>(a, batch, stream) : bwd_launch<64, 32>(a, batch, stream);
+    if (st != MB_OK) return st;
+    hipLaunchKernelGGL(k_mb_post_x, dim3((unsigned)(batch * L * H)), dim3(64), 0, stream, m);
+    MB_MIMO_R(k_mb_post_bc, dim3((unsigned)(batch * L * H)));
+#undef MB_MIMO_R
+    if (theta) {
+        if (dh_out) hipLaunchKernelGGL(k_tb_hterm, dim3((unsigned)(batch * H)), dim3(64), 0, stream, t);
+        hipLaunchKernelGGL(k_tb_segsum, dim3(nseg_all), dim3(64), 0, stream, t, (const float*)m.dTh, m.seg);
+        hipLaunchKernelGGL(k_tb_theta, dim3(nseg_all), dim3(64), 0, stream, t);
+    }
+    return check_launch();
+}

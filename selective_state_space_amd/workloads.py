@@ -256,6 +256,18 @@ def siso_bwd_block(seed=113):
     return d
 
 
+def mimo_bwd_block(seed=114):
+    """The Mamba-3 MIMO block inputs (seed 105) with the incoming gradients of
+    the backward: dY ~ N(0,1) like X and dh_out ~ N(0,1) like the state."""
+    d = mimo_block()
+    rng = np.random.default_rng(seed)
+    b, L, H, P, R = d["X"].shape
+    N = d["B"].shape[3]
+    d["dY"] = rng.standard_normal((b, L, H, P, R))
+    d["dh_out"] = rng.standard_normal((b, H, N, P))
+    return d
+
+
 def m1_bwd_block(seed=112):
     """The Mamba-1 block inputs (seed 102) with the incoming gradients of the
     backward: dy ~ N(0,1) like x and dh_out ~ N(0,1) like the state."""

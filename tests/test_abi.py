@@ -34,7 +34,7 @@ def declared_functions():
 def test_exports_every_declared_function(lib):
     names = declared_functions()
     assert {"mb_selective_scan", "mb_ssm_step", "mb_ssd_chunked", "mb_trap_ssd", "mb_mimo_ssd",
-            "mb_ssd_step", "mb_selective_scan_fused", "mb_ssd_chunked_bwd", "mb_selective_scan_bwd", "mb_trap_ssd_bwd", "mb_workspace_size", "mb_status_str", "mb_last_hip_error", "mb_version"} <= set(names)
+            "mb_ssd_step", "mb_selective_scan_fused", "mb_ssd_chunked_bwd", "mb_selective_scan_bwd", "mb_trap_ssd_bwd", "mb_mimo_ssd_bwd", "mb_workspace_size", "mb_status_str", "mb_last_hip_error", "mb_version"} <= set(names)
     for n in names:
         assert hasattr(lib, n), "libmb.so does not export " + n
 
@@ -246,6 +246,27 @@ def test_trap_bwd_validation(lib):
     assert trap_bwd(lib, ws_bytes=1 << 12) == E_WS
     assert mb.mb_workspace_size(mb.MB_OP_TRAP_SSD_BWD, 2, 50, 4, 64, 1, 128) > 0
     assert mb.mb_workspace_size(mb.MB_OP_TRAP_SSD_BWD, 2, 50, 4, 48, 1, 128) == 0
+
+
+def test_mimo_bwd_validation(lib):
+    def call(N=128, P_=64, R=4, dtype=F32, X=FAKE, dX=FAKE + (1 << 25), dh0=None, ws=FAKE + (1 << 28)):
+        q = lambda v: P(v) if v else None
+        return lib.mb_mimo_ssd_bwd(q(X), P(FAKE + (1 << 22)), P(FAKE + (1 << 23)), P(FAKE + (1 << 23) + (1 << 21)),
+                                   P(FAKE + (1 << 22) + (1 << 20)), P(FAKE + (1 << 22) + (1 << 21)), None, None,
+                                   None, None, P(FAKE + (1 << 24)), None, q(dX), P(FAKE + (1 << 25) + (1 << 23)),
+                                   P(FAKE + (1 << 26)), P(FAKE + (1 << 26) + (1 << 22)), P(FAKE + (1 << 27)),
+                                   P(FAKE + (1 << 27) + (1 << 20)), None, q(dh0), None, None, 1, 20, 2, P_, N, R,
+                                   dtype, q(ws), 1 << 33, None)
+    assert call(dtype=BF16) == E_DTYPE
+    assert call(N=96) == E_SHAPE
+    assert call(R=17) == E_SHAPE
+    assert call(R=3) == E_SHAPE
+    assert call(X=0) == E_NULL
+    assert call(dh0=FAKE + (1 << 29) + 4) == E_ALIGN
+    assert call(dX=FAKE + 64) == E_ALIAS
+    assert call(ws=0) == E_WS
+    assert mb.mb_workspace_size(mb.MB_OP_MIMO_SSD_BWD, 1, 20, 2, 64, 1, 128, 4) > 0
+    assert mb.mb_workspace_size(mb.MB_OP_MIMO_SSD_BWD, 1, 20, 2, 64, 1, 128, 0) == 0
 
 
 def test_trap_and_mimo_validation(lib):
