@@ -785,24 +785,40 @@ __global__ __launch_bounds__(64) void k_tb_prep_bc(TrapBwd a) {
     const float* __restrict__ Bv = a.B;
     const float* __restrict__ Cv = a.C;
     float* __restrict__ Tho = a.Th;
-#pragma unroll 8
-    for (int t = sg * kSeg; t < t1; ++t) {
-        const size_t bth = ((size_t)b * a.L + t) * a.H + h;
-        if (thv) th += (double)thv[bth * K + k];
-        const double r = th * 0.15915494309189535;
-        const float f = (float)(r - rint(r));
-        Tho[bth * K + k] = f;
-        float sn, cs;
-        sincos_frac(f, &sn, &cs);
-        const float2 bv = *(const float2*)(Bv + (((size_t)b * a.L + t) * a.G + g) * a.N + 2 * k);
-        const float2 cv = *(const float2*)(Cv + (((size_t)b * a.L + t) * a.G + g) * a.N + 2 * k);
-        const float2 br = make_float2(cs * bv.x - sn * bv.y, sn * bv.x + cs * bv.y);
-        const float2 cr = make_float2(cs * cv.x - sn * cv.y, sn * cv.x + cs * cv.y);
-        *(float2*)row(a.B2, 2 * (size_t)t + 1) = br;
-        *(float2*)row(a.C2, 2 * (size_t)t + 1) = cr;
-        if (t + 1 < a.L) {
-            *(float2*)row(a.B2, 2 * (size_t)t + 2) = br;
-            *(float2*)row(a.C2, 2 * (size_t)t + 2) = make_float2(0.0f, 0.0f);
+    constexpr int KB = 8;   // steps whose loads are issued before any of their stores
+    for (int tb = sg * kSeg; tb < t1; tb += KB) {
+        float thb[KB];
+        float2 bvb[KB], cvb[KB];
+#pragma unroll
+        for (int j = 0; j < KB; ++j) {
+            const int t = tb + j;
+            const bool ok = t < t1;
+            const size_t bth = ((size_t)b * a.L + (ok ? t : tb)) * a.H + h;
+            const size_t o = (((size_t)b * a.L + (ok ? t : tb)) * a.G + g) * a.N + 2 * k;
+            thb[j] = thv ? thv[bth * K + k] : 0.0f;
+            bvb[j] = *(const float2*)(Bv + o);
+            cvb[j] = *(const float2*)(Cv + o);
+        }
+#pragma unroll
+        for (int j = 0; j < KB; ++j) {
+            const int t = tb + j;
+            if (t >= t1) break;
+            const size_t bth = ((size_t)b * a.L + t) * a.H + h;
+            th += (double)thb[j];
+            const double r = th * 0.15915494309189535;
+            const float f = (float)(r - rint(r));
+            Tho[bth * K + k] = f;
+            float sn, cs;
+            sincos_frac(f, &sn, &cs);
+            const float2 bv = bvb[j], cv = cvb[j];
+            const float2 br = make_float2(cs * bv.x - sn * bv.y, sn * bv.x + cs * bv.y);
+            const float2 cr = make_float2(cs * cv.x - sn * cv.y, sn * cv.x + cs * cv.y);
+            *(float2*)row(a.B2, 2 * (size_t)t + 1) = br;
+            *(float2*)row(a.C2, 2 * (size_t)t + 1) = cr;
+            if (t + 1 < a.L) {
+                *(float2*)row(a.B2, 2 * (size_t)t + 2) = br;
+                *(float2*)row(a.C2, 2 * (size_t)t + 2) = make_float2(0.0f, 0.0f);
+            }
         }
     }
 }
@@ -1168,29 +1184,40 @@ __global__ __launch_bounds__(64) void k_mb_prep_bc(MimoBwd a) {
     const float* __restrict__ Bv = a.B;
     const float* __restrict__ Cv = a.C;
     const int t1 = min(a.L, (sg + 1) * kSeg);
-    for (int t = sg * kSeg; t < t1; ++t) {
+    constexpr int KB = R <= 4 ? 4 : 1;   // steps whose loads are issued before any of their stores
+    for (int tb = sg * kSeg; tb < t1; tb += KB) {
+      // the pairs' R ranks of B and C of KB steps, contiguous (rank innermost)
+      float thb[KB], bq0[KB][R], bq1[KB][R], cq0[KB][R], cq1[KB][R];
+#pragma unroll
+      for (int j = 0; j < KB; ++j) {
+        const int t = tb + j < t1 ? tb + j : tb;
         const size_t bth = ((size_t)b * a.L + t) * a.H + h;
-        if (thv) th += (double)thv[bth * K + k];
+        thb[j] = thv ? thv[bth * K + k] : 0.0f;
+        const float* bs = Bv + bth * a.N * R;
+        const float* cs_ = Cv + bth * a.N * R;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            bq0[j][r] = bs[(2 * k) * R + r];
+            bq1[j][r] = bs[(2 * k + 1) * R + r];
+            cq0[j][r] = cs_[(2 * k) * R + r];
+            cq1[j][r] = cs_[(2 * k + 1) * R + r];
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < KB; ++j) {
+        const int t = tb + j;
+        if (t >= t1) break;
+        const size_t bth = ((size_t)b * a.L + t) * a.H + h;
+        th += (double)thb[j];
         const double rv = th * 0.15915494309189535;
         const float f = (float)(rv - rint(rv));
         a.Th[bth * K + k] = f;
         float sn, cs;
         sincos_frac(f, &sn, &cs);
         const size_t t0 = (size_t)RS * t;
-        // the pair's R ranks of B and C, contiguous (rank innermost)
-        float bq0[R], bq1[R], cq0[R], cq1[R];
-        const float* bs = Bv + bth * a.N * R;
-        const float* cs_ = Cv + bth * a.N * R;
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            bq0[r] = bs[(2 * k) * R + r];
-            bq1[r] = bs[(2 * k + 1) * R + r];
-            cq0[r] = cs_[(2 * k) * R + r];
-            cq1[r] = cs_[(2 * k + 1) * R + r];
-        }
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const float b0 = bq0[r], b1 = bq1[r], c0 = cq0[r], c1 = cq1[r];
+            const float b0 = bq0[j][r], b1 = bq1[j][r], c0 = cq0[j][r], c1 = cq1[j][r];
             const float2 br = make_float2(cs * b0 - sn * b1, sn * b0 + cs * b1);
             const float2 cr = make_float2(cs * c0 - sn * c1, sn * c0 + cs * c1);
             *(float2*)row(a.B2, t0 + R + r) = br;                               // gamma row r
@@ -1200,6 +1227,7 @@ __global__ __launch_bounds__(64) void k_mb_prep_bc(MimoBwd a) {
             if (r < R - 1) *(float2*)row(a.C2, t0 + R + r) = z2;                // gamma rows but the last
             if (r >= 1) *(float2*)row(a.B2, t0 + 2 * R - 1 + r) = z2;           // output-only rows: no input
         }
+      }
     }
 }
 
@@ -1311,9 +1339,12 @@ __global__ __launch_bounds__(64) void k_mb_post_bc(MimoBwd a) {
         ob1[r] = -sn * dbr.x + cs * dbr.y;
         oc0[r] = cs * dcr.x + sn * dcr.y;
         oc1[r] = -sn * dcr.x + cs * dcr.y;
-        if (t == 0 && a.dBp) {
+    }
+    if (t == 0 && a.dBp) {
+        float* dbp = a.dBp + ((size_t)b * a.H + h) * a.N * R;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
             const float2 u = ld2(a.dB2, r);   // step 0's beta rows: unrotated
-            float* dbp = a.dBp + ((size_t)b * a.H + h) * a.N * R;
             dbp[(2 * k) * R + r] = u.x;
             dbp[(2 * k + 1) * R + r] = u.y;
         }
