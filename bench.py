@@ -416,6 +416,28 @@ class SISO(Workload):
                             Y=self.Y, h_out=self.h, ws=self.ws)
 
 
+class SISOGated(SISO):
+    """Mamba-3 SISO with the block's output epilogue (skip term D[h] X and the
+    SiLU(z) gate) fused into the scan's store; outside the step, measured beside
+    it.  Bytes add the gate z; flops are the scan's (the epilogue adds a few
+    operations per output)."""
+    name = "siso_gated"
+
+    def __init__(self, mb, wl, torch):
+        super().__init__(mb, wl, torch)
+        inp = wl.siso_gated()
+        self.inp = inp
+        f = torch.float32
+        self.t = {k: _dev(inp[k], f) for k in ("X", "logdecay", "B", "C", "beta", "gamma", "theta", "D", "z")}
+        b, L, H, P = inp["X"].shape
+        self.bytes += 4 * (b * L * H * P + H)
+
+    def run(self):
+        t = self.t
+        self.mb.mb_trap_ssd_gated(t["X"], t["logdecay"], t["B"], t["C"], t["beta"], t["gamma"], t["theta"],
+                                  None, D=t["D"], z=t["z"], Y=self.Y, h_out=self.h, ws=self.ws)
+
+
 class MIMO(Workload):
     name = "mimo"
     kernel = "k_walk (state-only pass) + k_walk (full pass)"
@@ -475,9 +497,10 @@ class SSDDecode(Workload):
 
 ALL = ["m1_scan", "m1_step", "ssd_f32", "ssd_bf16", "siso", "mimo"]
 # measured beside the step, not part of it: the decode steps of the SSD family, the
-# Mamba-1 scan with the block prologue and epilogue fused, and the backwards of the
+# Mamba-1 scan with the block prologue and epilogue fused, Mamba-3 SISO with its output
+# epilogue fused, and the backwards of the
 # Mamba-2 SSD, the Mamba-1 scan, Mamba-3 SISO and MIMO
-NEXT = ["m2_decode", "siso_decode", "mimo_decode", "m1_fused", "ssd_bwd", "m1_bwd", "siso_bwd", "mimo_bwd"]
+NEXT = ["m2_decode", "siso_decode", "mimo_decode", "m1_fused", "siso_gated", "ssd_bwd", "m1_bwd", "siso_bwd", "mimo_bwd"]
 
 
 def make(name, mb, wl, torch):
@@ -487,6 +510,8 @@ def make(name, mb, wl, torch):
         return M1Step(mb, wl, torch)
     if name == "m1_fused":
         return M1Fused(mb, wl, torch)
+    if name == "siso_gated":
+        return SISOGated(mb, wl, torch)
     if name == "ssd_bwd":
         return SSDBwd(mb, wl, torch)
     if name == "m1_bwd":

@@ -194,6 +194,24 @@ mb_status mb_trap_ssd(const void* X, const float* logdecay, const void* B,
                       hipStream_t stream);
 
 /*
+ * mb_trap_ssd with the output epilogue of the Mamba-3 block fused into its
+ * store (mamba3-minimal README, Architecture: the SSD output plus D x, then
+ * gated by SiLU(z)):
+ *     Y_t = (S_t^T C~_t + Dskip[h] X_t) * SiLU(z_t),   SiLU(v) = v / (1 + e^-v)
+ * Dskip (H) fp32 or NULL (no skip term); z (batch, L, H, P) in the dtype of X,
+ * or NULL (no gate).  Both NULL gives mb_trap_ssd.  Other arguments, the state
+ * and the workspace as mb_trap_ssd; z must be 16-byte aligned (MB_ERR_ALIGN)
+ * and must not overlap Y or h_out (MB_ERR_ALIAS).
+ */
+mb_status mb_trap_ssd_gated(const void* X, const float* logdecay, const void* B,
+                            const void* C, const float* beta, const float* gamma,
+                            const float* theta, const float* h0, const void* X_prev,
+                            const void* B_prev, const float* Dskip, const void* z, void* Y,
+                            float* h_out, int64_t batch, int64_t L, int64_t H, int64_t P,
+                            int64_t G, int64_t N, int64_t chunk, mb_dtype dtype, void* ws,
+                            size_t ws_bytes, hipStream_t stream);
+
+/*
  * Mamba-3 MIMO rank-R SSD (TorchMamba README, Models table row "Mamba-3 MIMO"
  * and Math notes MIMO: the rank-R update is a matrix product on one shared
  * (N, P) state).  As mb_trap_ssd, with every rank r of step t rotated by the

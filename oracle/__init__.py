@@ -248,6 +248,20 @@ def trap(X, logdecay, B, C, beta, gamma, theta=None, h0=None, X_prev=None, B_pre
     return Y, h
 
 
+def trap_gated(X, logdecay, B, C, beta, gamma, theta=None, h0=None, X_prev=None, B_prev=None, D=None, z=None):
+    """Mamba-3 SISO followed by the block's output epilogue (mamba3-minimal
+    README, Architecture): Y = (trap output + D[h] X) * SiLU(z), SiLU(v) =
+    v / (1 + e^-v).  D (H,) or None; z like X or None.  Returns (Y, h_out)."""
+    Y, h = trap(X, logdecay, B, C, beta, gamma, theta, h0, X_prev, B_prev)
+    X = _f64(X)
+    if D is not None:
+        Y = Y + _f64(D)[None, None, :, None] * X
+    if z is not None:
+        z = _f64(z)
+        Y = Y * (z / (1.0 + np.exp(-z)))
+    return Y, h
+
+
 def trap_bwd(X, logdecay, B, C, beta, gamma, dY, theta=None, h0=None, dh_out=None, X_prev=None, B_prev=None):
     """Backward of the Mamba-3 SISO recurrence: the gradients of sum dY . Y + sum
     dh_out . h_out with respect to X, logdecay, B, C, beta, gamma, theta, h0,

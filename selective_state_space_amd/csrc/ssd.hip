@@ -255,7 +255,25 @@ struct Args {
     float* seg_ld;   // their total log-decay, (batch, H, nseg-1)
     float* seg_rev;  // their total angle per pair in revolutions mod 1, (batch, H, nseg-1, N/2)
     int L, H, P, G, N, nch, nseg, cps, npg;
+    // SISO output epilogue (NULL: none): Y = (S^T C~ + Dh[h] X) SiLU(Zg)
+    const float* Dh;  // (H)
+    const void* Zg;   // (batch, L, H, P), the dtype of X
 };
+
+// four consecutive elements of an fp32 or bf16 tensor, as fp32
+template <typename IO>
+__device__ __forceinline__ void load4(const void* p, size_t e, float* o) {
+    if constexpr (sizeof(IO) == 4) {
+        const float4 v = *(const float4*)((const float*)p + e);
+        o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
+    } else {
+        const uint2 u = *(const uint2*)((const bf16*)p + e);
+        o[0] = __uint_as_float(u.x << 16);
+        o[1] = __uint_as_float(u.x & 0xffff0000u);
+        o[2] = __uint_as_float(u.y << 16);
+        o[3] = __uint_as_float(u.y & 0xffff0000u);
+    }
+}
 
 // Per-batch-row views of the inputs.  B/C: element (step t, n, rank r) at
 //   t * bc_step + bc_head + n * R + r   with bc_step = G*N (grouped layout,
@@ -937,11 +955,26 @@ __global__ __launch_bounds__(kWalkThreads, SO ? 4 : 2) void k_walk(Args a) {
                         const int pp = p0 + 16 * pw + 4 * lk;
                         IO* yrow = (IO*)a.Y + (((size_t)b * a.L + tg) * a.H + h) * (size_t)a.P * R;
                         if (R == 1) {
+                            float yv[4] = {y[0], y[1], y[2], y[3]};
+                            if (a.Dh || a.Zg) {
+                                // gated output: (y + Dh x) SiLU(z) of the same elements
+                                const size_t e = (((size_t)b * a.L + tg) * a.H + h) * (size_t)a.P + pp;
+                                float xv[4], zv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+                                load4<IO>(a.X, e, xv);
+                                if (a.Zg) load4<IO>(a.Zg, e, zv);
+                                const float dh = a.Dh ? a.Dh[h] : 0.0f;
+#pragma unroll
+                                for (int r = 0; r < 4; ++r) {
+                                    const float v = fmaf(dh, xv[r], yv[r]);
+                                    const float sg = zv[r] * __builtin_amdgcn_rcpf(1.0f + exp2_fast(-zv[r] * kLog2e));
+                                    yv[r] = a.Zg ? v * sg : v;
+                                }
+                            }
                             if constexpr (sizeof(IO) == 4) {
-                                *(float4*)((float*)yrow + pp) = make_float4(y[0], y[1], y[2], y[3]);
+                                *(float4*)((float*)yrow + pp) = make_float4(yv[0], yv[1], yv[2], yv[3]);
                             } else {
-                                const uint32_t u0 = f32_to_bf16(y[0]) | ((uint32_t)f32_to_bf16(y[1]) << 16);
-                                const uint32_t u1 = f32_to_bf16(y[2]) | ((uint32_t)f32_to_bf16(y[3]) << 16);
+                                const uint32_t u0 = f32_to_bf16(yv[0]) | ((uint32_t)f32_to_bf16(yv[1]) << 16);
+                                const uint32_t u1 = f32_to_bf16(yv[2]) | ((uint32_t)f32_to_bf16(yv[3]) << 16);
                                 *(uint2*)((bf16*)yrow + pp) = make_uint2(u0, u1);
                             }
                         } else {
@@ -1990,6 +2023,32 @@ extern "C" mb_status mb_trap_ssd(const void* X, const float* logdecay, const voi
     if ((st = check_ws(ws, ws_bytes, pl.bytes)) != MB_OK) return st;
     Args a{X, logdecay, B, C, beta, gamma, theta, h0, X_prev, B_prev, Y, h_out, nullptr, nullptr,
            nullptr, nullptr, nullptr, (int)L, (int)H, (int)P, (int)G, (int)N, 0, 0, 0, 0};
+    return dispatch<1, true, true>(a, batch, pl, (char*)ws, dtype, stream);
+}
+
+extern "C" mb_status mb_trap_ssd_gated(const void* X, const float* logdecay, const void* B,
+                                       const void* C, const float* beta, const float* gamma,
+                                       const float* theta, const float* h0, const void* X_prev,
+                                       const void* B_prev, const float* Dskip, const void* z, void* Y,
+                                       float* h_out, int64_t batch, int64_t L, int64_t H, int64_t P,
+                                       int64_t G, int64_t N, int64_t chunk, mb_dtype dtype, void* ws,
+                                       size_t ws_bytes, hipStream_t stream) {
+    if (G < 1 || H < 1 || H % G) return MB_ERR_SHAPE;
+    mb_status st = ssd_common_checks(X, logdecay, B, C, h0, Y, h_out, beta, gamma, theta, X_prev,
+                                     B_prev, batch, L, H, P, G, N, 1, dtype, chunk, true);
+    if (st != MB_OK) return st;
+    if (((uintptr_t)z & 15) || ((uintptr_t)Dskip & 3)) return MB_ERR_ALIGN;
+    const size_t ny = (size_t)(batch * L * H * P) * dtype_size(dtype);
+    if (overlaps(Y, ny, z, z ? ny : 0) || overlaps(Y, ny, Dskip, Dskip ? (size_t)H * 4 : 0)) return MB_ERR_ALIAS;
+    if (h_out && (overlaps(h_out, (size_t)(batch * H * N * P) * 4, z, z ? ny : 0) ||
+                  overlaps(h_out, (size_t)(batch * H * N * P) * 4, Dskip, Dskip ? (size_t)H * 4 : 0)))
+        return MB_ERR_ALIAS;
+    if (batch == 0) return MB_OK;
+    if (L == 0) return copy_state(h0, h_out, batch * H * N * P, stream);
+    const Plan pl = plan_for(MB_OP_TRAP_SSD, batch, L, H, P, G, N, 1);
+    if ((st = check_ws(ws, ws_bytes, pl.bytes)) != MB_OK) return st;
+    Args a{X, logdecay, B, C, beta, gamma, theta, h0, X_prev, B_prev, Y, h_out, nullptr, nullptr,
+           nullptr, nullptr, nullptr, (int)L, (int)H, (int)P, (int)G, (int)N, 0, 0, 0, 0, Dskip, z};
     return dispatch<1, true, true>(a, batch, pl, (char*)ws, dtype, stream);
 }
 

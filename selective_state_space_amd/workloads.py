@@ -158,6 +158,16 @@ def siso_block(seed=104, batch=4, L=4096, H=24, P=64, N=128, G=1):
     return trap_inputs(np.random.default_rng(seed), batch, L, H, P, N, G)
 
 
+def siso_gated(seed=115, batch=4, L=4096, H=24, P=64, N=128, G=1):
+    """The SISO block with its output epilogue: the skip weight D (H,) ~ N(0,1)
+    and the gate z (b,L,H,P) ~ N(0,1), drawn after the scan inputs."""
+    rng = np.random.default_rng(seed)
+    inp = trap_inputs(rng, batch, L, H, P, N, G)
+    inp["D"] = rng.standard_normal(H)
+    inp["z"] = rng.standard_normal((batch, L, H, P))
+    return inp
+
+
 def mimo_inputs(rng, batch, L, H, P, N, R, h0_sd=0.0, rotate=True):
     """Xr (b,L,H,P,R), Br, Cr (b,L,H,N,R) ~ N(0,1)/sqrt(N*R); then the SISO
     coefficients.  Order: X, B, C, coefficients, (h0)."""

@@ -203,3 +203,20 @@ def test_mimo_physical_frame_step(oracle_mod):
     Yp, hp = forms.mimo_physical_step_loop(**inp)
     close(Y, Yp, rtol=1e-9, atol=1e-11)
     close(h, hp, rtol=1e-9, atol=1e-11)
+
+
+def test_gated_epilogue_special_cases(oracle_mod):
+    """The SISO output epilogue: z = 0 closes the gate; without z the skip term
+    adds D[h] X; SiLU matches scipy's logistic sigmoid times z."""
+    from scipy.special import expit
+    rng = np.random.default_rng(41)
+    inp = wl.trap_inputs(rng, 1, 20, 3, 4, 6, G=1, h0_sd=0.2)
+    Y, h = oracle_mod.trap(**inp)
+    D = rng.standard_normal(3)
+    z = rng.standard_normal(inp["X"].shape)
+    Yz, hz = oracle_mod.trap_gated(**inp, D=D, z=np.zeros_like(z))
+    assert np.all(Yz == 0.0) and np.array_equal(hz, h)
+    Yd, _ = oracle_mod.trap_gated(**inp, D=D)
+    assert np.allclose(Yd - Y, D[None, None, :, None] * inp["X"], rtol=1e-13, atol=1e-15)
+    Yg, _ = oracle_mod.trap_gated(**inp, D=D, z=z)
+    assert np.allclose(Yg, (Y + D[None, None, :, None] * inp["X"]) * z * expit(z), rtol=1e-12, atol=1e-15)
