@@ -406,8 +406,9 @@ __device__ __forceinline__ int state_row(int t, int r, int lk, int nh) {
 __constant__ int kTrapTiles[8][2] = {{0x33, 0x00}, {0x32, 0x11}, {0x22, -1}, {0x20, -1},
                                      {0x30, -1}, {0x31, -1}, {0x21, -1}, {0x10, -1}};
 
-template <int NP, int R, bool TRAP, bool ROT, bool GROUPED, typename IO, bool SO>
+template <int NP, int R, bool TRAP, bool ROT, bool GROUPED, typename IO, bool SO, bool EPI = false>
 __global__ __launch_bounds__(kWalkThreads, SO ? 4 : 2) void k_walk(Args a) {
+    static_assert(!EPI || (R == 1 && TRAP && !SO), "the output epilogue is a SISO full-pass feature");
     using Gm = Geo<R, TRAP>;
     constexpr int QT = Gm::QT, EXTRA = Gm::EXTRA, JX = Gm::JX;
     constexpr int JC = Gm::JC, JP = Gm::JP;
@@ -802,6 +803,22 @@ __global__ __launch_bounds__(kWalkThreads, SO ? 4 : 2) void k_walk(Args a) {
 
         if constexpr (FULL) {
             floatx4 acc_y[4];
+            // SISO output epilogue: X and z of this lane's outputs load now, under the
+            // chunk's matrix work, rather than in front of the store
+            float ex[4][4] = {}, ez[4][4] = {};
+            if constexpr (EPI) {
+                if (active && nh == 0) {
+#pragma unroll
+                    for (int it = 0; it < 4; ++it) {
+                        const int tg = t0g + 16 * it + li;
+                        if (tg < a.L) {
+                            const size_t e = (((size_t)b * a.L + tg) * a.H + h) * (size_t)a.P + p0 + 16 * pw + 4 * lk;
+                            if (a.Dh) load4<IO>(a.X, e, ex[it]);
+                            if (a.Zg) load4<IO>(a.Zg, e, ez[it]);
+                        }
+                    }
+                }
+            }
             // The two waves of a SIMD (same column group, other state half) take the
             // score tiles and the state part in opposite orders, so that one
             // wave's vector work on the score weights meets the other's matrix
@@ -956,17 +973,13 @@ __global__ __launch_bounds__(kWalkThreads, SO ? 4 : 2) void k_walk(Args a) {
                         IO* yrow = (IO*)a.Y + (((size_t)b * a.L + tg) * a.H + h) * (size_t)a.P * R;
                         if (R == 1) {
                             float yv[4] = {y[0], y[1], y[2], y[3]};
-                            if (a.Dh || a.Zg) {
+                            if constexpr (EPI) {
                                 // gated output: (y + Dh x) SiLU(z) of the same elements
-                                const size_t e = (((size_t)b * a.L + tg) * a.H + h) * (size_t)a.P + pp;
-                                float xv[4], zv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-                                load4<IO>(a.X, e, xv);
-                                if (a.Zg) load4<IO>(a.Zg, e, zv);
                                 const float dh = a.Dh ? a.Dh[h] : 0.0f;
 #pragma unroll
                                 for (int r = 0; r < 4; ++r) {
-                                    const float v = fmaf(dh, xv[r], yv[r]);
-                                    const float sg = zv[r] * __builtin_amdgcn_rcpf(1.0f + exp2_fast(-zv[r] * kLog2e));
+                                    const float v = fmaf(dh, ex[it][r], yv[r]);
+                                    const float sg = ez[it][r] * __builtin_amdgcn_rcpf(1.0f + exp2_fast(-ez[it][r] * kLog2e));
                                     yv[r] = a.Zg ? v * sg : v;
                                 }
                             }
@@ -1882,7 +1895,14 @@ mb_status launch(Args a, int64_t batch, const Plan& pl, char* ws, hipStream_t st
     if constexpr (!TRAP && !ROT && sizeof(IO) == 4)
         hipLaunchKernelGGL((k_walk_m2s<NP>), dim3((unsigned)(per_seg * a.nseg)), dim3(kWalkThreads), 0,
                            stream, a);
-    else
+    else if constexpr (R == 1 && TRAP) {
+        if (a.Dh || a.Zg)
+            hipLaunchKernelGGL((k_walk<NP, R, TRAP, ROT, GROUPED, IO, false, true>),
+                               dim3((unsigned)(per_seg * a.nseg)), dim3(kWalkThreads), 0, stream, a);
+        else
+            hipLaunchKernelGGL((k_walk<NP, R, TRAP, ROT, GROUPED, IO, false>),
+                               dim3((unsigned)(per_seg * a.nseg)), dim3(kWalkThreads), 0, stream, a);
+    } else
         hipLaunchKernelGGL((k_walk<NP, R, TRAP, ROT, GROUPED, IO, false>),
                            dim3((unsigned)(per_seg * a.nseg)), dim3(kWalkThreads), 0, stream, a);
     return check_launch();
