@@ -438,6 +438,31 @@ class SISOGated(SISO):
                                   None, D=t["D"], z=t["z"], Y=self.Y, h_out=self.h, ws=self.ws)
 
 
+class SISOBlock(SISO):
+    """Mamba-3 SISO with both ends of its block fused into the scan: BCNorm +
+    bias on B, C before the rotations, skip term and SiLU gate at the store;
+    outside the step, measured beside it.  Bytes add z and the parameters;
+    flops are the scan's."""
+    name = "siso_block"
+
+    def __init__(self, mb, wl, torch):
+        super().__init__(mb, wl, torch)
+        inp = wl.siso_block_full()
+        self.inp = inp
+        f = torch.float32
+        self.t = {k: _dev(inp[k], f) for k in ("X", "logdecay", "B", "C", "beta", "gamma", "theta", "normB_w",
+                                               "normC_w", "biasB", "biasC", "D", "z")}
+        b, L, H, P = inp["X"].shape
+        N = inp["B"].shape[3]
+        self.bytes += 4 * (b * L * H * P + H + 2 * N + 2 * H * N)
+
+    def run(self):
+        t = self.t
+        self.mb.mb_trap_ssd_block(t["X"], t["logdecay"], t["B"], t["C"], t["beta"], t["gamma"], t["theta"],
+                                  None, normB_w=t["normB_w"], normC_w=t["normC_w"], biasB=t["biasB"],
+                                  biasC=t["biasC"], D=t["D"], z=t["z"], Y=self.Y, h_out=self.h, ws=self.ws)
+
+
 class MIMO(Workload):
     name = "mimo"
     kernel = "k_walk (state-only pass) + k_walk (full pass)"
@@ -498,9 +523,9 @@ class SSDDecode(Workload):
 ALL = ["m1_scan", "m1_step", "ssd_f32", "ssd_bf16", "siso", "mimo"]
 # measured beside the step, not part of it: the decode steps of the SSD family, the
 # Mamba-1 scan with the block prologue and epilogue fused, Mamba-3 SISO with its output
-# epilogue fused, and the backwards of the
+# epilogue and with both ends of its block fused, and the backwards of the
 # Mamba-2 SSD, the Mamba-1 scan, Mamba-3 SISO and MIMO
-NEXT = ["m2_decode", "siso_decode", "mimo_decode", "m1_fused", "siso_gated", "ssd_bwd", "m1_bwd", "siso_bwd", "mimo_bwd"]
+NEXT = ["m2_decode", "siso_decode", "mimo_decode", "m1_fused", "siso_gated", "siso_block", "ssd_bwd", "m1_bwd", "siso_bwd", "mimo_bwd"]
 
 
 def make(name, mb, wl, torch):
@@ -510,6 +535,8 @@ def make(name, mb, wl, torch):
         return M1Step(mb, wl, torch)
     if name == "m1_fused":
         return M1Fused(mb, wl, torch)
+    if name == "siso_block":
+        return SISOBlock(mb, wl, torch)
     if name == "siso_gated":
         return SISOGated(mb, wl, torch)
     if name == "ssd_bwd":

@@ -212,6 +212,35 @@ mb_status mb_trap_ssd_gated(const void* X, const float* logdecay, const void* B,
                             size_t ws_bytes, hipStream_t stream);
 
 /*
+ * The Mamba-3 SISO layer with both ends of the block fused into the scan
+ * (mamba3-minimal README, Architecture: B and C pass a QK-style norm, then a
+ * bias, then the rotations; TorchMamba README, Math notes M3 SISO: BCNorm and
+ * bias take the place of the short convolution).  Before the rotations each
+ * raw row of B and of C (one step, one group, N states) becomes
+ *     B^_t[h][n] = B_t[g][n] / sqrt(mean_n' B_t[g][n']^2 + eps) * normB_w[n] + biasB[h][n]
+ * (C likewise with normC_w, biasC), g the group of head h; the scan then runs
+ * on the per-head rows B^, C^ exactly as mb_trap_ssd, and the output takes the
+ * epilogue of mb_trap_ssd_gated.  B_prev (given with X_prev) is the previous
+ * token's raw row and passes the same prologue.
+ *   normB_w, normC_w : (N) fp32 or NULL (ones)
+ *   biasB, biasC     : (H, N) fp32 or NULL (zeros)
+ *   eps              : > 0 and finite (MB_ERR_SHAPE otherwise)
+ *   Dskip, z         : as mb_trap_ssd_gated (NULL: no skip term / no gate)
+ * The five parameter arrays must be 4-byte aligned (MB_ERR_ALIGN) and none of
+ * them nor z may overlap Y or h_out (MB_ERR_ALIAS).  Other arguments, the
+ * state and the workspace as mb_trap_ssd.
+ */
+mb_status mb_trap_ssd_block(const void* X, const float* logdecay, const void* B,
+                            const void* C, const float* beta, const float* gamma,
+                            const float* theta, const float* h0, const void* X_prev,
+                            const void* B_prev, const float* normB_w, const float* normC_w,
+                            const float* biasB, const float* biasC, float eps,
+                            const float* Dskip, const void* z, void* Y, float* h_out,
+                            int64_t batch, int64_t L, int64_t H, int64_t P, int64_t G, int64_t N,
+                            int64_t chunk, mb_dtype dtype, void* ws, size_t ws_bytes,
+                            hipStream_t stream);
+
+/*
  * Mamba-3 MIMO rank-R SSD (TorchMamba README, Models table row "Mamba-3 MIMO"
  * and Math notes MIMO: the rank-R update is a matrix product on one shared
  * (N, P) state).  As mb_trap_ssd, with every rank r of step t rotated by the

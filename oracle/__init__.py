@@ -262,6 +262,37 @@ def trap_gated(X, logdecay, B, C, beta, gamma, theta=None, h0=None, X_prev=None,
     return Y, h
 
 
+def bc_norm_bias(Bg, H, w=None, bias=None, eps=1e-5):
+    """The Mamba-3 B / C prologue (mamba3-minimal README, Architecture: a QK-style
+    norm, then a bias, before the rotations): each row of the last axis (N
+    states) divided by its root mean square (with eps inside the root), times
+    the per-state weight w (N,), then the head's bias (H, N).  Bg (..., G, N)
+    with the group axis second to last; returns (..., H, N), head h reading
+    group h // (H / G)."""
+    Bg = _f64(Bg)
+    G, N = Bg.shape[-2], Bg.shape[-1]
+    rms = np.sqrt(np.mean(Bg * Bg, axis=-1, keepdims=True) + eps)
+    v = Bg / rms
+    if w is not None:
+        v = v * _f64(w)
+    v = np.repeat(v, H // G, axis=-2)
+    if bias is not None:
+        v = v + _f64(bias)
+    return v
+
+
+def trap_block(X, logdecay, B, C, beta, gamma, theta=None, h0=None, X_prev=None, B_prev=None, normB_w=None,
+               normC_w=None, biasB=None, biasC=None, eps=1e-5, D=None, z=None):
+    """Mamba-3 SISO with both ends of its block: bc_norm_bias on B, C (and on the
+    previous token's B), the trapezoid scan on the per-head rows, then the output
+    epilogue of trap_gated.  Returns (Y, h_out)."""
+    H = _f64(X).shape[2]
+    Bh = bc_norm_bias(B, H, normB_w, biasB, eps)
+    Ch = bc_norm_bias(C, H, normC_w, biasC, eps)
+    Bp = None if B_prev is None else bc_norm_bias(B_prev, H, normB_w, biasB, eps)
+    return trap_gated(X, logdecay, Bh, Ch, beta, gamma, theta, h0, X_prev, Bp, D=D, z=z)
+
+
 def trap_bwd(X, logdecay, B, C, beta, gamma, dY, theta=None, h0=None, dh_out=None, X_prev=None, B_prev=None):
     """Backward of the Mamba-3 SISO recurrence: the gradients of sum dY . Y + sum
     dh_out . h_out with respect to X, logdecay, B, C, beta, gamma, theta, h0,

@@ -258,6 +258,15 @@ struct Args {
     // SISO output epilogue (NULL: none): Y = (S^T C~ + Dh[h] X) SiLU(Zg)
     const float* Dh;  // (H)
     const void* Zg;   // (batch, L, H, P), the dtype of X
+    // SISO BCNorm + bias prologue on B and C (bcn != 0): each row scaled by
+    // 1/sqrt(mean over N of its squares + eps), times the per-state weight
+    // (NULL: ones), plus the head's bias (NULL: zeros)
+    const float* nwB;    // (N)
+    const float* nwC;    // (N)
+    const float* biasB;  // (H, N)
+    const float* biasC;  // (H, N)
+    float eps;
+    int bcn;
 };
 
 // four consecutive elements of an fp32 or bf16 tensor, as fp32
@@ -406,9 +415,11 @@ __device__ __forceinline__ int state_row(int t, int r, int lk, int nh) {
 __constant__ int kTrapTiles[8][2] = {{0x33, 0x00}, {0x32, 0x11}, {0x22, -1}, {0x20, -1},
                                      {0x30, -1}, {0x31, -1}, {0x21, -1}, {0x10, -1}};
 
-template <int NP, int R, bool TRAP, bool ROT, bool GROUPED, typename IO, bool SO, bool EPI = false>
+template <int NP, int R, bool TRAP, bool ROT, bool GROUPED, typename IO, bool SO, bool EPI = false,
+          bool BCN = false>
 __global__ __launch_bounds__(kWalkThreads, SO ? 4 : 2) void k_walk(Args a) {
     static_assert(!EPI || (R == 1 && TRAP && !SO), "the output epilogue is a SISO full-pass feature");
+    static_assert(!BCN || (R == 1 && TRAP), "the B / C prologue is a SISO feature");
     using Gm = Geo<R, TRAP>;
     constexpr int QT = Gm::QT, EXTRA = Gm::EXTRA, JX = Gm::JX;
     constexpr int JC = Gm::JC, JP = Gm::JP;
@@ -486,6 +497,17 @@ __global__ __launch_bounds__(kWalkThreads, SO ? 4 : 2) void k_walk(Args a) {
     const bool x_in = xtq < NXG;
     const bool x_ok = x_in && p0 + xpl < a.P;
     const int si = tid / 8, sq = tid % 8;   // Mamba-2 score staging: row, 8-column block
+    // BCNorm + bias: this lane's states (2 sk, 2 sk + 1)
+    float nwb[2] = {1.0f, 1.0f}, nbb[2] = {0.0f, 0.0f}, nwc[2] = {1.0f, 1.0f}, nbc[2] = {0.0f, 0.0f};
+    if constexpr (BCN) if (k_ok) {
+        const int n = 2 * sk;
+        if (a.nwB) { nwb[0] = a.nwB[n]; nwb[1] = a.nwB[n + 1]; }
+        if (a.biasB) { nbb[0] = a.biasB[(size_t)h * a.N + n]; nbb[1] = a.biasB[(size_t)h * a.N + n + 1]; }
+        if constexpr (FULL) {
+            if (a.nwC) { nwc[0] = a.nwC[n]; nwc[1] = a.nwC[n + 1]; }
+            if (a.biasC) { nbc[0] = a.biasC[(size_t)h * a.N + n]; nbc[1] = a.biasC[(size_t)h * a.N + n + 1]; }
+        }
+    }
 
     // ---- one-time zero fill of padding that staging never writes ------------
     if constexpr (TRAP) {
@@ -760,6 +782,27 @@ __global__ __launch_bounds__(kWalkThreads, SO ? 4 : 2) void k_walk(Args a) {
         }
     }
 
+    // BCNorm + bias on the raw rows, before the rotations: a row (one step) lies
+    // on lanes sk of its step group's wave, pair sk on lane sk; lanes past N add
+    // zero to the sum of squares, and staging zeroes what they hold
+    auto bc_prologue = [&](Pre& p) {
+        if constexpr (BCN) if (ssg < NSG) {   // wave-uniform
+            const float rN = 1.0f / (float)a.N;
+            auto norm = [&](float& v0, float& v1, const float* w, const float* bi) {
+                const float sq2 = k_ok ? fmaf(v0, v0, v1 * v1) : 0.0f;
+                const float inv = rsqrtf(fmaf(readlane_f(wave_scan_dpp(sq2), 63), rN, a.eps));
+                v0 = fmaf(v0 * inv, w[0], bi[0]);
+                v1 = fmaf(v1 * inv, w[1], bi[1]);
+            };
+#pragma unroll
+            for (int i = 0; i < QSG; ++i) {
+                norm(p.b[i][0], p.b[i][1], nwb, nbb);
+                if constexpr (FULL) norm(p.c[i][0], p.c[i][1], nwc, nbc);
+            }
+            if (ssg * PRG < R) norm(p.bp[0], p.bp[PRG], nwb, nbb);
+        }
+    };
+
     Pre pre;
     if (c_begin < c_end) {
         prefetch(c_begin, pre, Par<1>{});
@@ -769,6 +812,7 @@ __global__ __launch_bounds__(kWalkThreads, SO ? 4 : 2) void k_walk(Args a) {
     for (int c = c_begin; c < c_end; ++c) {
         const int t0g = c * QT;
         __syncthreads();                 // the previous chunk's LDS reads are done
+        bc_prologue(pre);
         stage(pre);
         if constexpr (SO) {
             if (c + 1 < c_end) prefetch(c + 1, pre, Par<0>{});
@@ -1887,8 +1931,18 @@ mb_status launch(Args a, int64_t batch, const Plan& pl, char* ws, hipStream_t st
         }
     }
     if (a.nseg > 1) {
-        hipLaunchKernelGGL((k_walk<NP, R, TRAP, ROT, GROUPED, IO, true>),
-                           dim3((unsigned)(per_seg * (a.nseg - 1))), dim3(kWalkThreads), 0, stream, a);
+        const dim3 g((unsigned)(per_seg * (a.nseg - 1)));
+        if constexpr (R == 1 && TRAP) {
+            if (a.bcn)
+                hipLaunchKernelGGL((k_walk<NP, R, TRAP, ROT, GROUPED, IO, true, false, true>), g,
+                                   dim3(kWalkThreads), 0, stream, a);
+            else
+                hipLaunchKernelGGL((k_walk<NP, R, TRAP, ROT, GROUPED, IO, true>), g, dim3(kWalkThreads), 0,
+                                   stream, a);
+        } else {
+            hipLaunchKernelGGL((k_walk<NP, R, TRAP, ROT, GROUPED, IO, true>), g, dim3(kWalkThreads), 0, stream,
+                               a);
+        }
         mb_status st = check_launch();
         if (st != MB_OK) return st;
     }
@@ -1896,7 +1950,15 @@ mb_status launch(Args a, int64_t batch, const Plan& pl, char* ws, hipStream_t st
         hipLaunchKernelGGL((k_walk_m2s<NP>), dim3((unsigned)(per_seg * a.nseg)), dim3(kWalkThreads), 0,
                            stream, a);
     else if constexpr (R == 1 && TRAP) {
-        if (a.Dh || a.Zg)
+        const dim3 g((unsigned)(per_seg * a.nseg));
+        const bool epi = a.Dh || a.Zg;
+        if (a.bcn && epi)
+            hipLaunchKernelGGL((k_walk<NP, R, TRAP, ROT, GROUPED, IO, false, true, true>), g, dim3(kWalkThreads),
+                               0, stream, a);
+        else if (a.bcn)
+            hipLaunchKernelGGL((k_walk<NP, R, TRAP, ROT, GROUPED, IO, false, false, true>), g, dim3(kWalkThreads),
+                               0, stream, a);
+        else if (epi)
             hipLaunchKernelGGL((k_walk<NP, R, TRAP, ROT, GROUPED, IO, false, true>),
                                dim3((unsigned)(per_seg * a.nseg)), dim3(kWalkThreads), 0, stream, a);
         else
@@ -2069,6 +2131,42 @@ extern "C" mb_status mb_trap_ssd_gated(const void* X, const float* logdecay, con
     if ((st = check_ws(ws, ws_bytes, pl.bytes)) != MB_OK) return st;
     Args a{X, logdecay, B, C, beta, gamma, theta, h0, X_prev, B_prev, Y, h_out, nullptr, nullptr,
            nullptr, nullptr, nullptr, (int)L, (int)H, (int)P, (int)G, (int)N, 0, 0, 0, 0, Dskip, z};
+    return dispatch<1, true, true>(a, batch, pl, (char*)ws, dtype, stream);
+}
+
+extern "C" mb_status mb_trap_ssd_block(const void* X, const float* logdecay, const void* B,
+                                       const void* C, const float* beta, const float* gamma,
+                                       const float* theta, const float* h0, const void* X_prev,
+                                       const void* B_prev, const float* normB_w, const float* normC_w,
+                                       const float* biasB, const float* biasC, float eps,
+                                       const float* Dskip, const void* z, void* Y, float* h_out,
+                                       int64_t batch, int64_t L, int64_t H, int64_t P, int64_t G,
+                                       int64_t N, int64_t chunk, mb_dtype dtype, void* ws,
+                                       size_t ws_bytes, hipStream_t stream) {
+    if (G < 1 || H < 1 || H % G) return MB_ERR_SHAPE;
+    if (!(eps > 0.0f) || !(eps < 3.0e38f)) return MB_ERR_SHAPE;
+    mb_status st = ssd_common_checks(X, logdecay, B, C, h0, Y, h_out, beta, gamma, theta, X_prev,
+                                     B_prev, batch, L, H, P, G, N, 1, dtype, chunk, true);
+    if (st != MB_OK) return st;
+    const float* pars[6] = {normB_w, normC_w, biasB, biasC, Dskip, nullptr};
+    const size_t pbytes[6] = {(size_t)N * 4, (size_t)N * 4, (size_t)(H * N) * 4, (size_t)(H * N) * 4,
+                              (size_t)H * 4, 0};
+    if ((uintptr_t)z & 15) return MB_ERR_ALIGN;
+    const size_t ny = (size_t)(batch * L * H * P) * dtype_size(dtype);
+    const size_t nh = (size_t)(batch * H * N * P) * 4;
+    if (overlaps(Y, ny, z, z ? ny : 0) || (h_out && overlaps(h_out, nh, z, z ? ny : 0))) return MB_ERR_ALIAS;
+    for (int k = 0; k < 5; ++k) {
+        if ((uintptr_t)pars[k] & 3) return MB_ERR_ALIGN;
+        const size_t nb = pars[k] ? pbytes[k] : 0;
+        if (overlaps(Y, ny, pars[k], nb) || (h_out && overlaps(h_out, nh, pars[k], nb))) return MB_ERR_ALIAS;
+    }
+    if (batch == 0) return MB_OK;
+    if (L == 0) return copy_state(h0, h_out, batch * H * N * P, stream);
+    const Plan pl = plan_for(MB_OP_TRAP_SSD, batch, L, H, P, G, N, 1);
+    if ((st = check_ws(ws, ws_bytes, pl.bytes)) != MB_OK) return st;
+    Args a{X, logdecay, B, C, beta, gamma, theta, h0, X_prev, B_prev, Y, h_out, nullptr, nullptr,
+           nullptr, nullptr, nullptr, (int)L, (int)H, (int)P, (int)G, (int)N, 0, 0, 0, 0, Dskip, z,
+           normB_w, normC_w, biasB, biasC, eps, 1};
     return dispatch<1, true, true>(a, batch, pl, (char*)ws, dtype, stream);
 }
 

@@ -168,6 +168,21 @@ def siso_gated(seed=115, batch=4, L=4096, H=24, P=64, N=128, G=1):
     return inp
 
 
+def siso_block_full(seed=116, batch=4, L=4096, H=24, P=64, N=128, G=1):
+    """The SISO block with both ends: the scan inputs, then the B / C norm
+    weights ~ 1 + N(0, 0.3^2) (N,), the biases ~ N(0, 0.5^2) (H, N), the skip
+    weight D ~ N(0,1) (H,) and the gate z ~ N(0,1) like X."""
+    rng = np.random.default_rng(seed)
+    inp = trap_inputs(rng, batch, L, H, P, N, G)
+    inp["normB_w"] = 1.0 + 0.3 * rng.standard_normal(N)
+    inp["normC_w"] = 1.0 + 0.3 * rng.standard_normal(N)
+    inp["biasB"] = 0.5 * rng.standard_normal((H, N))
+    inp["biasC"] = 0.5 * rng.standard_normal((H, N))
+    inp["D"] = rng.standard_normal(H)
+    inp["z"] = rng.standard_normal((batch, L, H, P))
+    return inp
+
+
 def mimo_inputs(rng, batch, L, H, P, N, R, h0_sd=0.0, rotate=True):
     """Xr (b,L,H,P,R), Br, Cr (b,L,H,N,R) ~ N(0,1)/sqrt(N*R); then the SISO
     coefficients.  Order: X, B, C, coefficients, (h0)."""

@@ -33,7 +33,7 @@ def declared_functions():
 
 def test_exports_every_declared_function(lib):
     names = declared_functions()
-    assert {"mb_selective_scan", "mb_ssm_step", "mb_ssd_chunked", "mb_trap_ssd", "mb_trap_ssd_gated", "mb_mimo_ssd",
+    assert {"mb_selective_scan", "mb_ssm_step", "mb_ssd_chunked", "mb_trap_ssd", "mb_trap_ssd_gated", "mb_trap_ssd_block", "mb_mimo_ssd",
             "mb_ssd_step", "mb_selective_scan_fused", "mb_ssd_chunked_bwd", "mb_selective_scan_bwd", "mb_trap_ssd_bwd", "mb_mimo_ssd_bwd", "mb_workspace_size", "mb_status_str", "mb_last_hip_error", "mb_version"} <= set(names)
     for n in names:
         assert hasattr(lib, n), "libmb.so does not export " + n
@@ -297,6 +297,16 @@ def test_trap_and_mimo_validation(lib):
     assert lib.mb_trap_ssd_gated(*args[:10], P(FAKE + (1 << 31)), P(FAKE + (1 << 31) + 256), *args[10:],
                                  0, *dims[1:], *ws) == OK
     assert lib.mb_trap_ssd_gated(*args[:10], None, None, *args[10:], 1, 10, 2, 16, 1, 6, 0, F32, *ws) == E_SHAPE
+    # the block: eps > 0; parameter arrays 4-byte aligned and not under an output
+    par = P(FAKE + (1 << 31))
+    blk = lambda nb, nc, bb, bc, eps, d, z, *rest: lib.mb_trap_ssd_block(
+        *args[:10], nb, nc, bb, bc, eps, d, z, *args[10:], *rest)
+    assert blk(par, par, None, None, 0.0, None, None, *dims, *ws) == E_SHAPE
+    assert blk(par, par, None, None, float("nan"), None, None, *dims, *ws) == E_SHAPE
+    assert blk(P(FAKE + (1 << 31) + 2), None, None, None, 1e-5, None, None, *dims, *ws) == E_ALIGN
+    assert blk(None, None, P(FAKE + (1 << 27) + 8), None, 1e-5, None, None, *dims, *ws) == E_ALIAS
+    assert blk(None, None, None, P(FAKE + (1 << 26)), 1e-5, None, None, *dims, *ws) == E_ALIAS
+    assert blk(par, par, par, par, 1e-5, par, P(FAKE + (1 << 31) + 4096), 0, *dims[1:], *ws) == OK
     # unsupported rank
     assert lib.mb_mimo_ssd(*args, 1, 10, 2, 16, 8, 3, 0, F32, P(FAKE + (1 << 28)), 1 << 30, None) == E_SHAPE
     assert lib.mb_mimo_ssd(*args, 0, 10, 2, 16, 8, 4, 0, F32, P(FAKE + (1 << 28)), 1 << 30, None) == OK

@@ -220,3 +220,40 @@ def test_gated_epilogue_special_cases(oracle_mod):
     assert np.allclose(Yd - Y, D[None, None, :, None] * inp["X"], rtol=1e-13, atol=1e-15)
     Yg, _ = oracle_mod.trap_gated(**inp, D=D, z=z)
     assert np.allclose(Yg, (Y + D[None, None, :, None] * inp["X"]) * z * expit(z), rtol=1e-12, atol=1e-15)
+
+
+def test_bc_prologue_against_library_rms_norm(oracle_mod):
+    """The B / C prologue equals torch's own RMS normalisation over the state
+    axis (weight, eps) followed by the head's bias, heads reading their group."""
+    import torch
+    rng = np.random.default_rng(43)
+    Bg = rng.standard_normal((2, 7, 2, 12)) * 3.0
+    w = rng.standard_normal(12)
+    bias = rng.standard_normal((4, 12))
+    got = oracle_mod.bc_norm_bias(Bg, 4, w, bias, eps=1e-3)
+    ref = torch.nn.functional.rms_norm(torch.from_numpy(Bg), (12,), torch.from_numpy(w), eps=1e-3).numpy()
+    ref = np.repeat(ref, 2, axis=2) + bias
+    assert np.allclose(got, ref, rtol=1e-13, atol=1e-13)
+
+
+def test_block_scale_invariance_and_reduction(oracle_mod):
+    """With the prologue, a positive rescaling of any row of B or C (eps -> 0)
+    leaves the output unchanged; with unit-RMS rows, unit weights, zero bias and
+    eps = 0 the block is trap_gated on the same rows."""
+    rng = np.random.default_rng(47)
+    inp = wl.trap_inputs(rng, 1, 30, 2, 4, 8, G=1, h0_sd=0.2)
+    D = rng.standard_normal(2)
+    z = rng.standard_normal(inp["X"].shape)
+    Y, h = oracle_mod.trap_block(**inp, biasB=rng.standard_normal((2, 8)), eps=1e-30, D=D, z=z)
+    sc = np.exp(rng.standard_normal((1, 30, 1, 1)))
+    inp2 = dict(inp, B=inp["B"] * sc, C=inp["C"] * sc[:, ::-1])
+    Y2, h2 = oracle_mod.trap_block(**inp2, biasB=None, eps=1e-30, D=D, z=z)
+    Y1, h1 = oracle_mod.trap_block(**inp, biasB=None, eps=1e-30, D=D, z=z)
+    assert np.allclose(Y2, Y1, rtol=1e-10, atol=1e-12) and np.allclose(h2, h1, rtol=1e-10, atol=1e-12)
+    assert not np.allclose(Y, Y1)     # the bias matters
+    unit = dict(inp)
+    for k in ("B", "C"):
+        unit[k] = inp[k] / np.sqrt(np.mean(inp[k] ** 2, axis=-1, keepdims=True))
+    Yb, hb = oracle_mod.trap_block(**unit, eps=0.0, D=D, z=z)
+    Yg, hg = oracle_mod.trap_gated(**unit, D=D, z=z)
+    assert np.allclose(Yb, Yg, rtol=1e-12, atol=1e-14) and np.allclose(hb, hg, rtol=1e-12, atol=1e-14)
