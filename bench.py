@@ -463,6 +463,41 @@ class SISOBlock(SISO):
                                   biasC=t["biasC"], D=t["D"], z=t["z"], Y=self.Y, h_out=self.h, ws=self.ws)
 
 
+class M2Prologue(Workload):
+    """The Mamba-2 block prologue in one pass (conv1d + SiLU over the x, B, C
+    channels, softplus of dt, split into the SSD's inputs) at the Mamba-2 block
+    shape; outside the step, measured beside it.  HBM-bound: xBC and dt read
+    once, X, B, C, logdecay written once."""
+    name = "m2_prologue"
+    kernel = "k_ssd_prologue"
+    source = "selective_state_space_amd/csrc/ssd_prologue.hip"
+    bound = "hbm"
+
+    def __init__(self, mb, wl, torch):
+        self.mb = mb
+        b, L, H, P, G, N, K = 4, 4096, 24, 64, 1, 128, 4
+        self.dims = (H, P, G, N)
+        self.shape = dict(batch=b, L=L, H=H, P=P, N=N, G=G, K=K)
+        inp = wl.m2_prologue_block()
+        self.inp = inp
+        f = torch.float32
+        self.t = {k: (_dev(v, f) if v is not None else None) for k, v in inp.items()}
+        self.out = (torch.empty((b, L, H, P), dtype=f, device="cuda"), torch.empty((b, L, G, N), dtype=f, device="cuda"),
+                    torch.empty((b, L, G, N), dtype=f, device="cuda"), torch.empty((b, L, H), dtype=f, device="cuda"))
+        cin = H * P + 2 * G * N
+        self.tokens = b * L
+        self.bytes = 4 * (2 * b * L * cin + 2 * b * L * H + cin * (K + 1) + 2 * H)
+        self.flops = None
+        self.exps = None
+
+    def run(self):
+        t = self.t
+        H, P, G, N = self.dims
+        X, B, C, ld = self.out
+        self.mb.mb_ssd_prologue(t["xBC"], t["conv_w"], t["dt"], t["A"], H, P, G, N, conv_b=t["conv_b"],
+                                dt_bias=t["dt_bias"], X=X, B=B, C=C, logdecay=ld)
+
+
 class MIMO(Workload):
     name = "mimo"
     kernel = "k_walk (state-only pass) + k_walk (full pass)"
@@ -522,10 +557,10 @@ class SSDDecode(Workload):
 
 ALL = ["m1_scan", "m1_step", "ssd_f32", "ssd_bf16", "siso", "mimo"]
 # measured beside the step, not part of it: the decode steps of the SSD family, the
-# Mamba-1 scan with the block prologue and epilogue fused, Mamba-3 SISO with its output
+# Mamba-1 scan with the block prologue and epilogue fused, the Mamba-2 block prologue, Mamba-3 SISO with its output
 # epilogue and with both ends of its block fused, and the backwards of the
 # Mamba-2 SSD, the Mamba-1 scan, Mamba-3 SISO and MIMO
-NEXT = ["m2_decode", "siso_decode", "mimo_decode", "m1_fused", "siso_gated", "siso_block", "ssd_bwd", "m1_bwd", "siso_bwd", "mimo_bwd"]
+NEXT = ["m2_decode", "siso_decode", "mimo_decode", "m1_fused", "m2_prologue", "siso_gated", "siso_block", "ssd_bwd", "m1_bwd", "siso_bwd", "mimo_bwd"]
 
 
 def make(name, mb, wl, torch):
@@ -535,6 +570,8 @@ def make(name, mb, wl, torch):
         return M1Step(mb, wl, torch)
     if name == "m1_fused":
         return M1Fused(mb, wl, torch)
+    if name == "m2_prologue":
+        return M2Prologue(mb, wl, torch)
     if name == "siso_block":
         return SISOBlock(mb, wl, torch)
     if name == "siso_gated":

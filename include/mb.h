@@ -212,6 +212,33 @@ mb_status mb_trap_ssd_gated(const void* X, const float* logdecay, const void* B,
                             size_t ws_bytes, hipStream_t stream);
 
 /*
+ * The Mamba-2 block prologue in one pass (TorchMamba README, API reference:
+ * Mamba2Block, d_conv taps and psi = SiLU; Math notes M1: exp-Euler, the input
+ * scaled by dt and the decay exp(dt A)): from the block's projected channels
+ * xBC = (x | B | C) and the raw dt it makes the inputs of mb_ssd_chunked,
+ *     v_t[c]        = SiLU(conv_b[c] + sum_{k<K} conv_w[c][k] xBC_{t-K+1+k}[c])
+ *     dt'_t[h]      = softplus(dt_t[h] + dt_bias[h])
+ *     X_t[h][p]     = v_t[h P + p] dt'_t[h]
+ *     B_t[g][n]     = v_t[H P + g N + n],   C_t[g][n] = v_t[H P + G N + g N + n]
+ *     logdecay_t[h] = dt'_t[h] A[h]
+ *   xBC      : (batch, L, H P + 2 G N) fp32, channel-last
+ *   conv_w   : (H P + 2 G N, K) fp32;  conv_b: (H P + 2 G N) fp32 or NULL
+ *   x_hist   : (batch, K-1, H P + 2 G N) fp32 or NULL: the K-1 inputs before
+ *              step 0 (zeros when NULL), so a split sequence chains exactly
+ *   dt       : (batch, L, H) fp32;  dt_bias: (H) fp32 or NULL;  A: (H) fp32
+ *   X        : (batch, L, H, P) out;  B, C: (batch, L, G, N) out
+ *   logdecay : (batch, L, H) out;  dt_out: (batch, L, H) out (dt') or NULL
+ * 1 <= K <= 4; P and N multiples of 4; H % G == 0; ceil(L / 16) <= 65535.
+ * xBC, x_hist, X, B, C 16-byte aligned (MB_ERR_ALIGN); no output may overlap
+ * an input or another output (MB_ERR_ALIAS).  fp32 only.
+ */
+mb_status mb_ssd_prologue(const float* xBC, const float* conv_w, const float* conv_b,
+                          const float* x_hist, const float* dt, const float* dt_bias,
+                          const float* A, float* X, float* B, float* C, float* logdecay,
+                          float* dt_out, int64_t batch, int64_t L, int64_t H, int64_t P,
+                          int64_t G, int64_t N, int64_t K, hipStream_t stream);
+
+/*
  * The Mamba-3 SISO layer with both ends of the block fused into the scan
  * (mamba3-minimal README, Architecture: B and C pass a QK-style norm, then a
  * bias, then the rotations; TorchMamba README, Math notes M3 SISO: BCNorm and

@@ -293,6 +293,32 @@ def trap_block(X, logdecay, B, C, beta, gamma, theta=None, h0=None, X_prev=None,
     return trap_gated(X, logdecay, Bh, Ch, beta, gamma, theta, h0, X_prev, Bp, D=D, z=z)
 
 
+def ssd_prologue(xBC, conv_w, dt, A, H, P, G, N, conv_b=None, dt_bias=None, x_hist=None):
+    """The Mamba-2 block prologue (TorchMamba README, API reference Mamba2Block:
+    d_conv taps, psi = SiLU; Math notes M1: the input scaled by dt, decay dt A):
+    causal depthwise conv over time of each channel of xBC (the K - 1 steps
+    before the call from x_hist, zeros without it), plus conv_b, SiLU; dt' =
+    softplus(dt + dt_bias); X = x dt' per head, then B, C; logdecay = dt' A.
+    Returns (X, B, C, logdecay, dt')."""
+    xBC = _f64(xBC)
+    conv_w = _f64(conv_w)
+    b, L, cin = xBC.shape
+    K = conv_w.shape[1]
+    hist = np.zeros((b, K - 1, cin)) if x_hist is None else _f64(x_hist)
+    full = np.concatenate([hist, xBC], axis=1)          # step t of the call is row t + K - 1
+    pre = np.zeros((b, L, cin)) if conv_b is None else np.broadcast_to(_f64(conv_b), (b, L, cin)).copy()
+    for k in range(K):                                   # tap k reads step t - K + 1 + k
+        pre += conv_w[:, k] * full[:, k:k + L, :]
+    v = pre / (1.0 + np.exp(-pre))
+    u = _f64(dt) + (0.0 if dt_bias is None else _f64(dt_bias))
+    dtp = np.logaddexp(0.0, u)
+    HP, GN = H * P, G * N
+    X = v[..., :HP].reshape(b, L, H, P) * dtp[..., None]
+    Bo = v[..., HP:HP + GN].reshape(b, L, G, N)
+    Co = v[..., HP + GN:].reshape(b, L, G, N)
+    return X, Bo, Co, dtp * _f64(A), dtp
+
+
 def trap_bwd(X, logdecay, B, C, beta, gamma, dY, theta=None, h0=None, dh_out=None, X_prev=None, B_prev=None):
     """Backward of the Mamba-3 SISO recurrence: the gradients of sum dY . Y + sum
     dh_out . h_out with respect to X, logdecay, B, C, beta, gamma, theta, h0,

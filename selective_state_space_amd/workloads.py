@@ -183,6 +183,26 @@ def siso_block_full(seed=116, batch=4, L=4096, H=24, P=64, N=128, G=1):
     return inp
 
 
+def m2_prologue_inputs(rng, batch, L, H, P, G, N, K=4, hist=True):
+    """The Mamba-2 block's projected channels xBC ~ N(0,1) (b, L, H P + 2 G N);
+    conv_w ~ N(0, 1/K) (channels, K); conv_b ~ N(0, 0.1); raw dt ~ N(0, 0.5)
+    (b, L, H); dt_bias = softplus^-1(U(0.001, 0.1)); A = -U(1, 16) per head;
+    x_hist ~ N(0,1) (b, K-1, channels) or None."""
+    cin = H * P + 2 * G * N
+    xBC = rng.standard_normal((batch, L, cin))
+    conv_w = rng.standard_normal((cin, K)) / np.sqrt(K)
+    conv_b = rng.normal(0.0, 0.1, cin)
+    dt = rng.normal(0.0, 0.5, (batch, L, H))
+    dt_bias = np.log(np.expm1(rng.uniform(0.001, 0.1, H)))
+    A = -rng.uniform(1.0, 16.0, H)
+    x_hist = rng.standard_normal((batch, K - 1, cin)) if hist and K > 1 else None
+    return dict(xBC=xBC, conv_w=conv_w, dt=dt, A=A, conv_b=conv_b, dt_bias=dt_bias, x_hist=x_hist)
+
+
+def m2_prologue_block(seed=117, batch=4, L=4096, H=24, P=64, G=1, N=128, K=4):
+    return m2_prologue_inputs(np.random.default_rng(seed), batch, L, H, P, G, N, K, hist=False)
+
+
 def mimo_inputs(rng, batch, L, H, P, N, R, h0_sd=0.0, rotate=True):
     """Xr (b,L,H,P,R), Br, Cr (b,L,H,N,R) ~ N(0,1)/sqrt(N*R); then the SISO
     coefficients.  Order: X, B, C, coefficients, (h0)."""

@@ -33,7 +33,7 @@ def declared_functions():
 
 def test_exports_every_declared_function(lib):
     names = declared_functions()
-    assert {"mb_selective_scan", "mb_ssm_step", "mb_ssd_chunked", "mb_trap_ssd", "mb_trap_ssd_gated", "mb_trap_ssd_block", "mb_mimo_ssd",
+    assert {"mb_selective_scan", "mb_ssm_step", "mb_ssd_chunked", "mb_trap_ssd", "mb_trap_ssd_gated", "mb_trap_ssd_block", "mb_ssd_prologue", "mb_mimo_ssd",
             "mb_ssd_step", "mb_selective_scan_fused", "mb_ssd_chunked_bwd", "mb_selective_scan_bwd", "mb_trap_ssd_bwd", "mb_mimo_ssd_bwd", "mb_workspace_size", "mb_status_str", "mb_last_hip_error", "mb_version"} <= set(names)
     for n in names:
         assert hasattr(lib, n), "libmb.so does not export " + n
@@ -366,3 +366,24 @@ def test_workspace_sizes(lib):
     assert mb.mb_workspace_size(mb.MB_OP_TRAP_SSD, 1, 100, 2, 16, 1, 16) == 0
     assert mb.mb_workspace_size(mb.MB_OP_SSD_CHUNKED, 4, 4096, 24, 64, 5, 128) == 0   # invalid G
     assert mb.mb_workspace_size(mb.MB_OP_MIMO_SSD, 2, 8192, 16, 64, 1, 128, 3) == 0   # invalid R
+
+
+def test_ssd_prologue_validation(lib):
+    q = [P(FAKE + (k << 24)) for k in range(12)]     # xBC, conv_w, conv_b, x_hist, dt, dt_bias, A, X, B, C, ld, dt'
+    dims = (1, 10, 2, 16, 1, 8, 4)
+    a = list(q)
+    a[0] = None
+    assert lib.mb_ssd_prologue(*a, *dims, None) == E_NULL
+    assert lib.mb_ssd_prologue(*q, 1, 10, 2, 16, 1, 8, 5, None) == E_SHAPE        # K > 4
+    assert lib.mb_ssd_prologue(*q, 1, 10, 3, 16, 2, 8, 4, None) == E_SHAPE        # H % G
+    assert lib.mb_ssd_prologue(*q, 1, 16 * 65536, 2, 16, 1, 8, 4, None) == E_SHAPE
+    a = list(q)
+    a[8] = P(FAKE + (8 << 24) + 4)
+    assert lib.mb_ssd_prologue(*a, *dims, None) == E_ALIGN
+    a = list(q)
+    a[9] = P(FAKE + (8 << 24) + 16)                  # C over B
+    assert lib.mb_ssd_prologue(*a, *dims, None) == E_ALIAS
+    a = list(q)
+    a[7] = P(FAKE + 64)                              # X over xBC
+    assert lib.mb_ssd_prologue(*a, *dims, None) == E_ALIAS
+    assert lib.mb_ssd_prologue(*q, 0, *dims[1:], None) == OK
