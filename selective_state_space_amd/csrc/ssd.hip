@@ -50,6 +50,12 @@
 //             the accumulator tiles so that the accumulators are directly the
 //             operand of the next chunk's C~ H product: the state never leaves
 //             registers.
+//             Two SISO variants carry the Mamba-3 block's ends
+//             (mamba3-minimal README, Architecture): EPI (full pass) loads X
+//             and the gate z at the chunk's start and stores
+//             (y + D_h x) SiLU(z); BCN (both passes) turns each raw B, C row
+//             in the prefetch registers into row / rms(row) * weight + bias_h
+//             (one DPP sum over the row's wave) before the rotations.
 // All global reads go through buffer resources that cover one batch row of a
 // tensor, so reads before the first or after the last step return zero in
 // hardware and the hot loops carry no bounds branches.
