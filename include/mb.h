@@ -221,22 +221,24 @@ mb_status mb_trap_ssd_gated(const void* X, const float* logdecay, const void* B,
  *     X_t[h][p]     = v_t[h P + p] dt'_t[h]
  *     B_t[g][n]     = v_t[H P + g N + n],   C_t[g][n] = v_t[H P + G N + g N + n]
  *     logdecay_t[h] = dt'_t[h] A[h]
- *   xBC      : (batch, L, H P + 2 G N) fp32, channel-last
+ *   xBC      : (batch, L, H P + 2 G N) dtype, channel-last
  *   conv_w   : (H P + 2 G N, K) fp32;  conv_b: (H P + 2 G N) fp32 or NULL
- *   x_hist   : (batch, K-1, H P + 2 G N) fp32 or NULL: the K-1 inputs before
+ *   x_hist   : (batch, K-1, H P + 2 G N) dtype or NULL: the K-1 inputs before
  *              step 0 (zeros when NULL), so a split sequence chains exactly
  *   dt       : (batch, L, H) fp32;  dt_bias: (H) fp32 or NULL;  A: (H) fp32
- *   X        : (batch, L, H, P) out;  B, C: (batch, L, G, N) out
+ *   X        : (batch, L, H, P) dtype out;  B, C: (batch, L, G, N) dtype out
  *   logdecay : (batch, L, H) out;  dt_out: (batch, L, H) out (dt') or NULL
  * 1 <= K <= 4; P and N multiples of 4; H % G == 0; ceil(L / 16) <= 65535.
  * xBC, x_hist, X, B, C 16-byte aligned (MB_ERR_ALIGN); no output may overlap
- * an input or another output (MB_ERR_ALIAS).  fp32 only.
+ * an input or another output (MB_ERR_ALIAS).  dtype (MB_F32 or MB_BF16) is that
+ * of the activations xBC, x_hist, X, B, C; the arithmetic is fp32 and the
+ * bf16 outputs are rounded to nearest even once.
  */
-mb_status mb_ssd_prologue(const float* xBC, const float* conv_w, const float* conv_b,
-                          const float* x_hist, const float* dt, const float* dt_bias,
-                          const float* A, float* X, float* B, float* C, float* logdecay,
+mb_status mb_ssd_prologue(const void* xBC, const float* conv_w, const float* conv_b,
+                          const void* x_hist, const float* dt, const float* dt_bias,
+                          const float* A, void* X, void* B, void* C, float* logdecay,
                           float* dt_out, int64_t batch, int64_t L, int64_t H, int64_t P,
-                          int64_t G, int64_t N, int64_t K, hipStream_t stream);
+                          int64_t G, int64_t N, int64_t K, mb_dtype dtype, hipStream_t stream);
 
 /*
  * The Mamba-3 SISO layer with both ends of the block fused into the scan

@@ -74,7 +74,7 @@ def load_library():
             lib.mb_trap_ssd_gated.argtypes = [_vp] * 14 + [_i64] * 7 + [ctypes.c_int, _vp, ctypes.c_size_t, _vp]
             lib.mb_trap_ssd_gated.restype = ctypes.c_int
         if hasattr(lib, "mb_ssd_prologue"):
-            lib.mb_ssd_prologue.argtypes = [_vp] * 12 + [_i64] * 7 + [_vp]
+            lib.mb_ssd_prologue.argtypes = [_vp] * 12 + [_i64] * 7 + [ctypes.c_int, _vp]
             lib.mb_ssd_prologue.restype = ctypes.c_int
         if hasattr(lib, "mb_trap_ssd_block"):
             lib.mb_trap_ssd_block.argtypes = [_vp] * 14 + [ctypes.c_float] + [_vp] * 4 + [_i64] * 7 + \
@@ -488,28 +488,31 @@ def mb_trap_ssd_block(X, logdecay, B, C, beta, gamma, theta=None, h0=None, *, no
 def mb_ssd_prologue(xBC, conv_w, dt, A, H, P, G, N, *, conv_b=None, x_hist=None, dt_bias=None, X=None, B=None,
                     C=None, logdecay=None, dt_out=False):
     """Mamba-2 block prologue: conv1d + SiLU over xBC (batch, L, H*P + 2*G*N),
-    softplus(dt + dt_bias), split into the SSD inputs.  All float32.  Returns
+    softplus(dt + dt_bias), split into the SSD inputs.  xBC, x_hist and the
+    outputs X, B, C in one dtype (float32 or bfloat16); the rest float32.  Returns
     (X, B, C, logdecay) or, with dt_out=True, (X, B, C, logdecay, dt')."""
     torch = _torch()
     dev = _device_of(xBC)
     f32 = torch.float32
+    act = xBC.dtype
+    code = _dtype_code(xBC, "xBC")
     b, L, cin = xBC.shape
     K = conv_w.shape[1]
-    _check(xBC, "xBC", (b, L, H * P + 2 * G * N), f32, dev)
+    _check(xBC, "xBC", (b, L, H * P + 2 * G * N), act, dev)
     _check(conv_w, "conv_w", (cin, K), f32, dev)
     _check(conv_b, "conv_b", (cin,), f32, dev)
-    _check(x_hist, "x_hist", (b, K - 1, cin), f32, dev)
+    _check(x_hist, "x_hist", (b, K - 1, cin), act, dev)
     _check(dt, "dt", (b, L, H), f32, dev)
     _check(dt_bias, "dt_bias", (H,), f32, dev)
     _check(A, "A", (H,), f32, dev)
-    X = torch.empty((b, L, H, P), dtype=f32, device=dev) if X is None else _check(X, "X", (b, L, H, P), f32, dev)
-    B = torch.empty((b, L, G, N), dtype=f32, device=dev) if B is None else _check(B, "B", (b, L, G, N), f32, dev)
-    C = torch.empty((b, L, G, N), dtype=f32, device=dev) if C is None else _check(C, "C", (b, L, G, N), f32, dev)
+    X = torch.empty((b, L, H, P), dtype=act, device=dev) if X is None else _check(X, "X", (b, L, H, P), act, dev)
+    B = torch.empty((b, L, G, N), dtype=act, device=dev) if B is None else _check(B, "B", (b, L, G, N), act, dev)
+    C = torch.empty((b, L, G, N), dtype=act, device=dev) if C is None else _check(C, "C", (b, L, G, N), act, dev)
     logdecay = torch.empty((b, L, H), dtype=f32, device=dev) if logdecay is None else \
         _check(logdecay, "logdecay", (b, L, H), f32, dev)
     dto = torch.empty((b, L, H), dtype=f32, device=dev) if dt_out else None
     _call("mb_ssd_prologue", _ptr(xBC), _ptr(conv_w), _ptr(conv_b), _ptr(x_hist), _ptr(dt), _ptr(dt_bias),
-          _ptr(A), _ptr(X), _ptr(B), _ptr(C), _ptr(logdecay), _ptr(dto), b, L, H, P, G, N, K, _stream(dev))
+          _ptr(A), _ptr(X), _ptr(B), _ptr(C), _ptr(logdecay), _ptr(dto), b, L, H, P, G, N, K, code, _stream(dev))
     return (X, B, C, logdecay, dto) if dt_out else (X, B, C, logdecay)
 
 

@@ -12,7 +12,7 @@
 // chain exactly.
 //
 // Layout and mapping: xBC is channel-last, so a thread owns four adjacent
-// channels (one 16-byte load per step) and a run of kSteps steps, keeping the
+// channels (one 16-byte load per step, 8 bytes in bf16; the arithmetic is fp32) and a run of kSteps steps, keeping the
 // K - 1 previous inputs in registers: every input is read from HBM once, every
 // output written once, all accesses coalesced along the channels.  The work is
 // HBM-bound; the only arithmetic of note is one exp and one log per output.
@@ -34,22 +34,44 @@ __device__ __forceinline__ float silu(float v) { return v / (1.0f + __expf(-v));
 __device__ __forceinline__ float softplus(float v) { return v > 20.0f ? v : log1pf(__expf(v)); }
 
 struct ProArgs {
-    const float* xbc;
+    const void* xbc;     // activations (xBC, x_hist, X, B, C): fp32 or bf16
     const float* w;
     const float* cb;
-    const float* hist;
+    const void* hist;
     const float* dt;
     const float* dtb;
     const float* A;
-    float* X;
-    float* B;
-    float* C;
+    void* X;
+    void* B;
+    void* C;
     float* ld;
     float* dto;
     int L, H, P, G, N, K, cin;
 };
 
-template <int K>
+// four adjacent activations as fp32, and back
+template <typename IO>
+__device__ __forceinline__ float4 ld4(const void* p, size_t e) {
+    if constexpr (sizeof(IO) == 4) {
+        return *(const float4*)((const float*)p + e);
+    } else {
+        const uint2 u = *(const uint2*)((const bf16*)p + e);
+        return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+                           __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
+    }
+}
+template <typename IO>
+__device__ __forceinline__ void st4(void* p, size_t e, float v0, float v1, float v2, float v3) {
+    if constexpr (sizeof(IO) == 4) {
+        *(float4*)((float*)p + e) = make_float4(v0, v1, v2, v3);
+    } else {
+        const uint32_t u0 = f32_to_bf16(v0) | ((uint32_t)f32_to_bf16(v1) << 16);
+        const uint32_t u1 = f32_to_bf16(v2) | ((uint32_t)f32_to_bf16(v3) << 16);
+        *(uint2*)((bf16*)p + e) = make_uint2(u0, u1);
+    }
+}
+
+template <int K, typename IO>
 __global__ __launch_bounds__(kThreads) void k_ssd_prologue(ProArgs a) {
     const int c = 4 * (blockIdx.x * kThreads + threadIdx.x);
     if (c >= a.cin) return;
@@ -70,9 +92,9 @@ __global__ __launch_bounds__(kThreads) void k_ssd_prologue(ProArgs a) {
     for (int k = 0; k < K - 1; ++k) {
         const int t = t0 - K + 1 + k;
         if (t >= 0)
-            win[k] = *(const float4*)(a.xbc + ((size_t)b * a.L + t) * a.cin + c);
+            win[k] = ld4<IO>(a.xbc, ((size_t)b * a.L + t) * a.cin + c);
         else if (a.hist)
-            win[k] = *(const float4*)(a.hist + ((size_t)b * (K - 1) + (K - 1 + t)) * a.cin + c);
+            win[k] = ld4<IO>(a.hist, ((size_t)b * (K - 1) + (K - 1 + t)) * a.cin + c);
         else
             win[k] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     }
@@ -81,7 +103,7 @@ __global__ __launch_bounds__(kThreads) void k_ssd_prologue(ProArgs a) {
     const float dtbh = (c < HP && a.dtb) ? a.dtb[h] : 0.0f;
     for (int t = t0; t < t1; ++t) {
         const size_t row = (size_t)b * a.L + t;
-        win[K - 1] = *(const float4*)(a.xbc + row * a.cin + c);
+        win[K - 1] = ld4<IO>(a.xbc, row * a.cin + c);
         float v[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -98,15 +120,15 @@ __global__ __launch_bounds__(kThreads) void k_ssd_prologue(ProArgs a) {
         for (int k = 0; k < K - 1; ++k) win[k] = win[k + 1];
         if (c < HP) {
             const float d = softplus(a.dt[row * a.H + h] + dtbh);
-            *(float4*)(a.X + row * HP + c) = make_float4(v[0] * d, v[1] * d, v[2] * d, v[3] * d);
+            st4<IO>(a.X, row * HP + c, v[0] * d, v[1] * d, v[2] * d, v[3] * d);
             if (c % a.P == 0) {
                 a.ld[row * a.H + h] = d * Ah;
                 if (a.dto) a.dto[row * a.H + h] = d;
             }
         } else if (c < HP + GN) {
-            *(float4*)(a.B + row * GN + (c - HP)) = make_float4(v[0], v[1], v[2], v[3]);
+            st4<IO>(a.B, row * GN + (c - HP), v[0], v[1], v[2], v[3]);
         } else {
-            *(float4*)(a.C + row * GN + (c - HP - GN)) = make_float4(v[0], v[1], v[2], v[3]);
+            st4<IO>(a.C, row * GN + (c - HP - GN), v[0], v[1], v[2], v[3]);
         }
     }
 }
@@ -116,25 +138,27 @@ __global__ __launch_bounds__(kThreads) void k_ssd_prologue(ProArgs a) {
 
 using namespace mb;
 
-extern "C" mb_status mb_ssd_prologue(const float* xBC, const float* conv_w, const float* conv_b,
-                                     const float* x_hist, const float* dt, const float* dt_bias,
-                                     const float* A, float* X, float* B, float* C, float* logdecay,
+extern "C" mb_status mb_ssd_prologue(const void* xBC, const float* conv_w, const float* conv_b,
+                                     const void* x_hist, const float* dt, const float* dt_bias,
+                                     const float* A, void* X, void* B, void* C, float* logdecay,
                                      float* dt_out, int64_t batch, int64_t L, int64_t H, int64_t P,
-                                     int64_t G, int64_t N, int64_t K, hipStream_t stream) {
+                                     int64_t G, int64_t N, int64_t K, mb_dtype dtype, hipStream_t stream) {
     if (!xBC || !conv_w || !dt || !A || !X || !B || !C || !logdecay) return MB_ERR_NULL;
     if (batch < 0 || L < 0 || H < 1 || P < 1 || G < 1 || N < 1 || H % G || P % 4 || N % 4) return MB_ERR_SHAPE;
     if (K < 1 || K > kKMax || batch > 65535) return MB_ERR_SHAPE;
+    if (!dtype_ok(dtype)) return MB_ERR_DTYPE;
+    const size_t es = dtype_size(dtype);
     const int64_t cin = H * P + 2 * G * N;
     // grid: channel blocks x step runs (at most 65535) x batch
     if (cin > ((int64_t)1 << 28) || (L + kSteps - 1) / kSteps > 65535) return MB_ERR_SHAPE;
     for (const void* p : {(const void*)xBC, (const void*)x_hist, (const void*)X, (const void*)B, (const void*)C})
         if ((uintptr_t)p & 15) return MB_ERR_ALIGN;
-    const size_t nx = (size_t)(batch * L * cin) * 4, nh = (size_t)(batch * L * H) * 4;
+    const size_t nx = (size_t)(batch * L * cin) * es, nh = (size_t)(batch * L * H) * 4;
     const Span ins[7] = {{xBC, nx}, {conv_w, (size_t)(cin * K) * 4}, {conv_b, conv_b ? (size_t)cin * 4 : 0},
-                         {x_hist, x_hist ? (size_t)(batch * (K - 1) * cin) * 4 : 0}, {dt, nh},
+                         {x_hist, x_hist ? (size_t)(batch * (K - 1) * cin) * es : 0}, {dt, nh},
                          {dt_bias, dt_bias ? (size_t)H * 4 : 0}, {A, (size_t)H * 4}};
-    const Span outs[5] = {{X, (size_t)(batch * L * H * P) * 4}, {B, (size_t)(batch * L * G * N) * 4},
-                          {C, (size_t)(batch * L * G * N) * 4}, {logdecay, nh}, {dt_out, dt_out ? nh : 0}};
+    const Span outs[5] = {{X, (size_t)(batch * L * H * P) * es}, {B, (size_t)(batch * L * G * N) * es},
+                          {C, (size_t)(batch * L * G * N) * es}, {logdecay, nh}, {dt_out, dt_out ? nh : 0}};
     for (int i = 0; i < 5; ++i) {
         if (overlaps_any(outs[i].p, outs[i].bytes, ins, 7)) return MB_ERR_ALIAS;
         for (int j = 0; j < i; ++j)
@@ -145,11 +169,18 @@ extern "C" mb_status mb_ssd_prologue(const float* xBC, const float* conv_w, cons
               (int)L, (int)H, (int)P, (int)G, (int)N, (int)K, (int)cin};
     const dim3 grid((unsigned)((cin / 4 + kThreads - 1) / kThreads), (unsigned)((L + kSteps - 1) / kSteps),
                     (unsigned)batch);
+    const bool f32 = dtype == MB_F32;
+#define MB_PRO(KK)                                                                              \
+    if (f32)                                                                                    \
+        hipLaunchKernelGGL((k_ssd_prologue<KK, float>), grid, dim3(kThreads), 0, stream, a);   \
+    else                                                                                        \
+        hipLaunchKernelGGL((k_ssd_prologue<KK, bf16>), grid, dim3(kThreads), 0, stream, a);
     switch (K) {
-        case 1: hipLaunchKernelGGL(k_ssd_prologue<1>, grid, dim3(kThreads), 0, stream, a); break;
-        case 2: hipLaunchKernelGGL(k_ssd_prologue<2>, grid, dim3(kThreads), 0, stream, a); break;
-        case 3: hipLaunchKernelGGL(k_ssd_prologue<3>, grid, dim3(kThreads), 0, stream, a); break;
-        default: hipLaunchKernelGGL(k_ssd_prologue<4>, grid, dim3(kThreads), 0, stream, a); break;
+        case 1: MB_PRO(1) break;
+        case 2: MB_PRO(2) break;
+        case 3: MB_PRO(3) break;
+        default: MB_PRO(4) break;
     }
+#undef MB_PRO
     return check_launch();
 }

@@ -373,17 +373,18 @@ def test_ssd_prologue_validation(lib):
     dims = (1, 10, 2, 16, 1, 8, 4)
     a = list(q)
     a[0] = None
-    assert lib.mb_ssd_prologue(*a, *dims, None) == E_NULL
-    assert lib.mb_ssd_prologue(*q, 1, 10, 2, 16, 1, 8, 5, None) == E_SHAPE        # K > 4
-    assert lib.mb_ssd_prologue(*q, 1, 10, 3, 16, 2, 8, 4, None) == E_SHAPE        # H % G
-    assert lib.mb_ssd_prologue(*q, 1, 16 * 65536, 2, 16, 1, 8, 4, None) == E_SHAPE
+    assert lib.mb_ssd_prologue(*a, *dims, F32, None) == E_NULL
+    assert lib.mb_ssd_prologue(*q, 1, 10, 2, 16, 1, 8, 5, F32, None) == E_SHAPE        # K > 4
+    assert lib.mb_ssd_prologue(*q, 1, 10, 3, 16, 2, 8, 4, F32, None) == E_SHAPE        # H % G
+    assert lib.mb_ssd_prologue(*q, 1, 16 * 65536, 2, 16, 1, 8, 4, F32, None) == E_SHAPE
     a = list(q)
     a[8] = P(FAKE + (8 << 24) + 4)
-    assert lib.mb_ssd_prologue(*a, *dims, None) == E_ALIGN
+    assert lib.mb_ssd_prologue(*a, *dims, F32, None) == E_ALIGN
     a = list(q)
     a[9] = P(FAKE + (8 << 24) + 16)                  # C over B
-    assert lib.mb_ssd_prologue(*a, *dims, None) == E_ALIAS
+    assert lib.mb_ssd_prologue(*a, *dims, F32, None) == E_ALIAS
     a = list(q)
     a[7] = P(FAKE + 64)                              # X over xBC
-    assert lib.mb_ssd_prologue(*a, *dims, None) == E_ALIAS
-    assert lib.mb_ssd_prologue(*q, 0, *dims[1:], None) == OK
+    assert lib.mb_ssd_prologue(*a, *dims, F32, None) == E_ALIAS
+    assert lib.mb_ssd_prologue(*q, *dims, 7, None) == E_DTYPE
+    assert lib.mb_ssd_prologue(*q, 0, *dims[1:], F32, None) == OK

@@ -76,3 +76,22 @@ def test_prologue_then_ssd(oracle_mod):
     Yr, hr = oracle_mod.ssd(Xr, ldr, Br, Cr, None)
     assert_close(Y, Yr, "f32", "Y")
     assert_close(h, hr, "f32", "h")
+
+
+@pytest.mark.parametrize("shape", [(2, 37, 2, 16, 1, 8, 4), (1, 300, 24, 64, 1, 128, 4), (1, 65, 3, 32, 3, 32, 2)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_prologue_bf16(oracle_mod, shape):
+    """bf16 activations in and out: the oracle sees the bf16-rounded inputs;
+    the outputs are rounded once, within the bf16 tolerance."""
+    b, L, H, P, G, N, K = shape
+    i = wl.m2_prologue_inputs(np.random.default_rng(sum(shape) + 7), b, L, H, P, G, N, K, hist=True)
+    bf = {k: torch.from_numpy(np.ascontiguousarray(i[k])).to(torch.bfloat16) for k in ("xBC", "x_hist")}
+    got = mb.mb_ssd_prologue(bf["xBC"].cuda(), _dev(i["conv_w"]), _dev(i["dt"]), _dev(i["A"]), H, P, G, N,
+                             conv_b=_dev(i["conv_b"]), x_hist=bf["x_hist"].cuda(), dt_bias=_dev(i["dt_bias"]))
+    torch.cuda.synchronize()
+    r = {k: _ref(v) for k, v in i.items()}
+    r.update({k: v.double().numpy() for k, v in bf.items()})
+    ref = oracle_mod.ssd_prologue(**r, H=H, P=P, G=G, N=N)
+    for name, g, rr in zip(("X", "B", "C", "logdecay"), got, ref):
+        assert g.dtype == (torch.bfloat16 if name != "logdecay" else torch.float32)
+        assert_close(g, rr, "bf16", name)
