@@ -2006,6 +2006,13 @@ bool dims_ok(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N, int64_t 
     return true;
 }
 
+// Mamba-2 only: one batch row of the score workspace (a 64 x 64 fp32 block per
+// chunk and group) is read through a buffer resource with 32-bit byte offsets.
+bool m2_scores_ok(int64_t L, int64_t G) {
+    const int64_t nch = (L + kRows - 1) / kRows;
+    return nch * G * (int64_t)(kRows * kRows * 4) < ((int64_t)1 << 31);
+}
+
 Plan plan_for(mb_op op, int64_t batch, int64_t L, int64_t H, int64_t P, int64_t G, int64_t N,
               int64_t R) {
     return make_plan(op != MB_OP_SSD_CHUNKED, op == MB_OP_MIMO_SSD ? R : 1, batch, L, H, P,
@@ -2033,7 +2040,7 @@ extern "C" size_t mb_workspace_size(mb_op op, int64_t batch, int64_t L, int64_t 
     // Mamba-1 backward: the sizes (batch, L, D, N) travel as (batch, L, H, N)
     if (op == MB_OP_SELECTIVE_SCAN_BWD) return m1_bwd_workspace(batch, L, H, N);
     if (!dims_ok(batch, L, H, P, N)) return 0;
-    if (op == MB_OP_SSD_CHUNKED && (G < 1 || H % G)) return 0;
+    if (op == MB_OP_SSD_CHUNKED && (G < 1 || H % G || !m2_scores_ok(L, G))) return 0;
     if (op == MB_OP_MIMO_SSD && R != 1 && R != 2 && R != 4 && R != 8 && R != 16) return 0;
     if (batch == 0 || L == 0) return 0;
     return plan_for(op, batch, L, H, P, G, N, R).bytes;
@@ -2082,6 +2089,7 @@ extern "C" mb_status mb_ssd_chunked(const void* X, const float* logdecay, const 
                                     int64_t N, int64_t chunk, mb_dtype dtype, void* ws,
                                     size_t ws_bytes, hipStream_t stream) {
     if (G < 1 || H < 1 || H % G) return MB_ERR_SHAPE;
+    if (!m2_scores_ok(L, G)) return MB_ERR_SHAPE;
     mb_status st = ssd_common_checks(X, logdecay, B, C, h0, Y, h_out, nullptr, nullptr, nullptr,
                                      nullptr, nullptr, batch, L, H, P, G, N, 1, dtype, chunk, false);
     if (st != MB_OK) return st;

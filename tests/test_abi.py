@@ -161,6 +161,13 @@ def test_ssd_validation(lib):
     assert ssd(lib, Y=FAKE + 64) == E_ALIAS
     assert ssd(lib, Y=FAKE + (1 << 27) + 8) == E_ALIGN
     assert ssd(lib, batch=0) == OK
+    # one batch row of the score workspace (64 x 64 fp32 per chunk and group)
+    # must be addressable in 32-bit byte offsets: 64 chunks x 4096 groups is 2^32 bytes
+    assert ssd(lib, L=4096, H=4096, G=4096, P_=16, N=16) == E_SHAPE
+    ws_size = lib.mb_workspace_size
+    ws_size.restype = ctypes.c_size_t
+    assert ws_size(2, 1, 4096, 4096, 16, 4096, 16, 1, 0) == 0
+    assert ws_size(2, 1, 1984, 4096, 16, 4096, 16, 1, 0) > 0     # 31 chunks: below 2^31 bytes
 
 
 def ssd_bwd(lib, X=FAKE, dY=FAKE + (1 << 24), dX=FAKE + (1 << 25), dB=FAKE + (1 << 26), dh0=FAKE + (1 << 27),
