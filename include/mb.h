@@ -29,7 +29,8 @@
  * - A length-zero sequence is valid: the final state is h0 (or zeros) and no
  *   y is written.  A zero batch is a no-op.
  * - The library is re-entrant; its only global state is a per-device cache of
- *   the compute-unit count, filled once under a lock.
+ *   the compute-unit count and of the static workspace's address
+ *   (mb_ssd_chunked_noalloc), each filled once under a lock.
  */
 #ifndef MB_H
 #define MB_H
@@ -160,6 +161,27 @@ mb_status mb_ssd_chunked(const void* X, const float* logdecay, const void* B,
                          int64_t batch, int64_t L, int64_t H, int64_t P,
                          int64_t G, int64_t N, int64_t chunk, mb_dtype dtype,
                          void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * mb_ssd_chunked for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same computation, arguments and limits, without ws / ws_bytes.  The
+ * workspace is a static device buffer inside the library, one per device
+ * (32 MiB, held from the first call on that device until the process ends);
+ * the call allocates nothing.  The sizes must need at most 32 MiB of
+ * workspace (mb_workspace_size(MB_OP_SSD_CHUNKED, ...) <= 33554432), else
+ * MB_ERR_WORKSPACE and nothing is launched; the Mamba-2 block shape (batch 4,
+ * L 4096, H 24, P 64, N 128, G 1) needs 21 MB.  Every call on one device
+ * shares that buffer: calls that overlap in time on one device (different
+ * streams, or host threads) race and give wrong results; calls ordered on one
+ * stream are safe.  Nothing in the buffer needs clearing between calls.
+ * MB_ERR_HIP if the buffer's address cannot be obtained.
+ */
+mb_status mb_ssd_chunked_noalloc(const void* X, const float* logdecay, const void* B,
+                                 const void* C, const float* h0, void* Y, float* h_out,
+                                 int64_t batch, int64_t L, int64_t H, int64_t P,
+                                 int64_t G, int64_t N, int64_t chunk, mb_dtype dtype,
+                                 hipStream_t stream);
 
 /*
  * Mamba-3 SISO exponential-trapezoidal SSD with data-dependent rotations

@@ -59,6 +59,8 @@
 // All global reads go through buffer resources that cover one batch row of a
 // tensor, so reads before the first or after the last step return zero in
 // hardware and the hot loops carry no bounds branches.
+#include <mutex>
+
 #include "mb_internal.h"
 
 namespace mb {
@@ -2019,6 +2021,38 @@ Plan plan_for(mb_op op, int64_t batch, int64_t L, int64_t H, int64_t P, int64_t 
                      op == MB_OP_SSD_CHUNKED ? G : H, N);
 }
 
+// Device scratch of the allocation-free Mamba-2 entry point: file-scope, one
+// copy per device, alive until the process ends.  Host code never uses the
+// array's name as an address: scratch_ptr() takes the device address of the
+// current device's copy from the runtime, once per device.
+constexpr size_t kScratchBytes = (size_t)32 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+mb_status scratch_ptr(char** out) {
+    constexpr int kMaxDev = 64;
+    static std::mutex mu;
+    static void* ptr[kMaxDev] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) {
+        set_last_hip_error((int)e);
+        return MB_ERR_HIP;
+    }
+    if (dev < 0 || dev >= kMaxDev) return MB_ERR_HIP;
+    std::lock_guard<std::mutex> lk(mu);
+    if (!ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) {
+            set_last_hip_error((int)e);
+            return MB_ERR_HIP;
+        }
+        ptr[dev] = p;
+    }
+    *out = (char*)ptr[dev];
+    return MB_OK;
+}
+
 mb_status check_ws(void* ws, size_t ws_bytes, size_t need) {
     if (need == 0) return MB_OK;
     if (!ws || ws_bytes < need || ((uintptr_t)ws & 255)) return MB_ERR_WORKSPACE;
@@ -2100,6 +2134,27 @@ extern "C" mb_status mb_ssd_chunked(const void* X, const float* logdecay, const 
     Args a{X, logdecay, B, C, nullptr, nullptr, nullptr, h0, nullptr, nullptr, Y, h_out, nullptr,
            nullptr, nullptr, nullptr, nullptr, (int)L, (int)H, (int)P, (int)G, (int)N, 0, 0, 0, 0};
     return dispatch<1, false, true>(a, batch, pl, (char*)ws, dtype, stream);
+}
+
+extern "C" mb_status mb_ssd_chunked_noalloc(const void* X, const float* logdecay, const void* B,
+                                            const void* C, const float* h0, void* Y, float* h_out,
+                                            int64_t batch, int64_t L, int64_t H, int64_t P,
+                                            int64_t G, int64_t N, int64_t chunk, mb_dtype dtype,
+                                            hipStream_t stream) {
+    if (G < 1 || H < 1 || H % G) return MB_ERR_SHAPE;
+    if (!m2_scores_ok(L, G)) return MB_ERR_SHAPE;
+    mb_status st = ssd_common_checks(X, logdecay, B, C, h0, Y, h_out, nullptr, nullptr, nullptr,
+                                     nullptr, nullptr, batch, L, H, P, G, N, 1, dtype, chunk, false);
+    if (st != MB_OK) return st;
+    if (batch == 0) return MB_OK;
+    if (L == 0) return copy_state(h0, h_out, batch * H * N * P, stream);
+    const Plan pl = plan_for(MB_OP_SSD_CHUNKED, batch, L, H, P, G, N, 1);
+    if (pl.bytes > kScratchBytes) return MB_ERR_WORKSPACE;
+    char* ws = nullptr;
+    if ((st = scratch_ptr(&ws)) != MB_OK) return st;
+    Args a{X, logdecay, B, C, nullptr, nullptr, nullptr, h0, nullptr, nullptr, Y, h_out, nullptr,
+           nullptr, nullptr, nullptr, nullptr, (int)L, (int)H, (int)P, (int)G, (int)N, 0, 0, 0, 0};
+    return dispatch<1, false, true>(a, batch, pl, ws, dtype, stream);
 }
 
 extern "C" mb_status mb_trap_ssd(const void* X, const float* logdecay, const void* B,
