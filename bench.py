@@ -14,15 +14,25 @@ already resident in HBM:
 
 The printed metric is scanned tokens per second over the whole step (a token
 is one (batch, time) position of a workload; the decode step counts its 256
-sequences).  Per-workload times come from HIP events recorded on the stream the
-kernels run on, over the same timed steps.  The `roofline` object is for the
-workload whose kernels take the largest share of the step; `kernels` lists
-every workload.  `cpu_baseline` times the fp64 oracle on a bounded sample of the
-same workloads on the host cores.  `next` times, beside the step and outside its
-token count, the decode steps of the SSD family (one token for 256 sequences:
-Mamba-2, SISO and MIMO on the block shapes; bound by HBM).
+sequences), the step timed back to back.  Per-workload times come from HIP
+events recorded on the stream the kernels run on: the headline `ms` of each
+workload is the mean over calls that each follow a flush of the last-level
+cache (every input read from HBM), with the back-to-back mean (`warm_ms`)
+beside it.  The `roofline` object is for the workload whose kernels take the
+largest share of the step, `rooflines` for the two workloads the metric names,
+and `kernels` lists every workload.  `cpu_baseline` times the fp64 oracle on
+the same workloads on the host cores.  `next` times, beside the step and
+outside its token count, the decode steps of the SSD family, the fused block
+variants and the backwards.
+
+The run has two phases, so that a rocprofv3 kernel trace of it splits cleanly:
+every warm call (warm-up and back-to-back timing, the step's workloads and
+then those beside it) comes before the first cache flush, and every flushed
+call after it.  `--summarize DIR...` prints markdown tables of rocprofv3 csv
+output directories (kernel trace split by phase; counter means per dispatch).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--only a,b] [--no-cpu] [--no-next]
+                    [--next a,b] [--no-cold] [--copy-calibration] [--summarize DIR...]
 """
 from __future__ import annotations
 
@@ -41,10 +51,18 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 FP32_PEAK_TFLOPS = 157.3       # MI355X dense fp32 (vector and MFMA)
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
-VALU_F32_LANE_OPS = 256 * 2.4e9 * 64   # non-packed fp32 VALU lane-ops/s (256 CU x 2.4 GHz x 64 lanes)
-# Minimal VALU issue slots per Mamba-1 (t, c, n) element: dt*A (1), exp (2: the
-# transcendental unit runs at half rate), (dt*x)*B (1), a*h + u (1), y += C*h (1).
-M1_SLOTS_PER_ELEM = 6
+# fp32 vector issue slots per second: 256 CUs x 4 SIMDs x 32 lanes x 2.4 GHz =
+# 78.6e12 (the 157.3 TFLOP/s fp32 vector peak counts an FMA as two flops).  A
+# wave64 FMA issues in two cycles: measured on MI355X at 8 waves per SIMD.
+VALU_LANE_SLOTS = 256 * 4 * 32 * 2.4e9
+# v_exp_f32 throughput, measured on MI355X (8 independent chains per lane, 1..8
+# waves per SIMD): a quarter of the FMA rate, and it does not overlap with the
+# FMA stream (1 exp + 4 FMA take the sum of their times), so an exp costs four
+# full-rate slots.
+EXP_SLOTS = 4
+# Minimal VALU issue slots per Mamba-1 (t, c, n) element: dt*A, (dt*x)*B,
+# a*h + u, y += C*h (one slot each) and one exp.
+M1_SLOTS_PER_ELEM = 4 + EXP_SLOTS
 
 
 # ----------------------------------------------------------------------------
@@ -57,10 +75,10 @@ def m1_scan_work(b, L, D, N, es=4):
 
 
 # Minimal VALU issue slots per (t, c, n) element of the Mamba-1 backward: the
-# recomputed forward (6) and the adjoint step: G += C dy, dB and dC products,
-# U += G B, exp (2) and its argument, G a h_prev (2), V += A w, dA += dt w,
-# G *= a (12).
-M1_BWD_SLOTS_PER_ELEM = 18
+# recomputed forward (4 + an exp) and the adjoint step: G += C dy, dB and dC
+# products, U += G B, the exp's argument and the exp, G a h_prev (2), V += A w,
+# dA += dt w, G *= a (10 + an exp).
+M1_BWD_SLOTS_PER_ELEM = 14 + 2 * EXP_SLOTS
 
 
 def m1_bwd_work(b, L, D, N):
@@ -603,8 +621,8 @@ def roofline_of(w, ms, bound=None):
     bound = bound or w.bound
     if bound == "alu":
         ach = w.exps * getattr(w, "slots", M1_SLOTS_PER_ELEM) / s / 1e9
-        peak = VALU_F32_LANE_OPS / 1e9
-        return {"bound": "alu", "achieved": ach, "peak": peak, "unit": "Gop/s", "frac": ach / peak}
+        peak = VALU_LANE_SLOTS / 1e9
+        return {"bound": "alu", "achieved": ach, "peak": peak, "unit": "G lane-slots/s", "frac": ach / peak}
     if bound == "mfma":
         peak = BF16_PEAK_TFLOPS if getattr(w, "dtype", "f32") == "bf16" else FP32_PEAK_TFLOPS
         ach = w.flops / s / 1e12
@@ -632,11 +650,22 @@ def traffic_for(w):
 
 
 # ----------------------------------------------------------------------------
-# CPU baseline: the fp64 oracle on a bounded sample of each workload
+# CPU baseline: the fp64 oracle on the host cores
 # ----------------------------------------------------------------------------
-def cpu_baseline(ws):
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline(ws, wl):
     """Time the fp64 oracle on the host cores on the same inputs (bf16 inputs are
-    timed with their fp32 values: the oracle's cost does not depend on them)."""
+    timed with their fp32 values: the oracle's cost does not depend on them),
+    then the two small workloads (Mamba-1 tiny, Mamba-1 decode) on one thread."""
     import oracle
     oracle.build()
     threads = oracle.get_threads()
@@ -658,58 +687,88 @@ def cpu_baseline(ws):
         total_tok += w.tokens
         total_s += dt
         parts.append("%s full (%d tokens, %.2f s)" % (w.name, w.tokens, dt))
+    single = {}
+    oracle.set_threads(1)
+    try:
+        tiny = wl.m1_tiny()
+        dec = wl.m1_decode()
+        for name, fn, tok in (("m1_tiny", lambda: oracle.m1_scan(**tiny), 64),
+                              ("m1_step", lambda: oracle.m1_step(dec["x"], dec["dt"], dec["A"], dec["B"],
+                                                                 dec["C"], dec["D"], dec["h"]), 256)):
+            reps, t0 = 0, time.perf_counter()
+            while True:
+                fn()
+                reps += 1
+                el = time.perf_counter() - t0
+                if el > 0.5 or reps >= 1000:
+                    break
+            single[name] = {"tokens_per_s": tok * reps / el, "ms_per_call": el * 1e3 / reps}
+    finally:
+        oracle.set_threads(threads)
     return {"value": total_tok / total_s if total_s else None, "unit": "scanned tokens/s",
-            "cores": threads, "kind": "oracle", "sample": "; ".join(parts)}
+            "cores": threads, "kind": "oracle", "cpu_model": cpu_model(),
+            "sample": "; ".join(parts), "single_thread": single}
 
 
-_FLUSH = []
+_FLUSH = {}
 
 
-def cold_ms(torch, w, reps=5):
-    """Median time of one call of workload w after overwriting a 512 MiB buffer,
-    which evicts the 256 MB last-level cache: every input comes from HBM."""
-    if not _FLUSH:
-        _FLUSH.append(torch.empty(128 << 20, dtype=torch.float32, device="cuda"))
-    buf = _FLUSH[0]
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ms = []
-    for r in range(reps):
-        buf.fill_(float(r))
+def flush(torch):
+    """Overwrite a 512 MiB buffer: evicts the 256 MB last-level cache, so the
+    next call reads every input from HBM."""
+    if "buf" not in _FLUSH:
+        _FLUSH["buf"] = torch.empty(128 << 20, dtype=torch.float32, device="cuda")
+        _FLUSH["n"] = 0
+    _FLUSH["n"] += 1
+    _FLUSH["buf"].fill_(float(_FLUSH["n"]))
+
+
+def time_flushed(torch, w, reps):
+    """Event times (ms) of `reps` calls of workload w, each after a cache flush."""
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for e0, e1 in ev:
+        flush(torch)
         e0.record()
         w.run()
         e1.record()
-        torch.cuda.synchronize()
-        ms.append(e0.elapsed_time(e1))
-    return float(np.median(ms))
+    torch.cuda.synchronize()
+    return [e0.elapsed_time(e1) for e0, e1 in ev]
 
 
-def time_next(args, mb, wl, torch):
-    """Decode steps of the SSD family, the fused Mamba-1 block scan and the
-    backwards, timed with
-    HIP events on the stream they run on, outside the step (they are not part of
-    its token count)."""
-    res = []
-    for n in NEXT:
-        print("# preparing %s" % n, file=sys.stderr, flush=True)
-        w = make(n, mb, wl, torch)
-        for _ in range(args.warmup):
-            w.run()
-        torch.cuda.synchronize()
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(args.steps)]
-        for e0, e1 in ev:
-            e0.record()
-            w.run()
-            e1.record()
-        torch.cuda.synchronize()
-        ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev]))
-        r = roofline_of(w, ms)
-        roof = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}
-        roof["traffic"] = traffic_for(w)
-        res.append({"workload": w.name, "kernel": w.kernel, "shape": w.shape, "ms": round(ms, 5),
-                    "tokens_per_s": w.tokens / (ms * 1e-3), "roofline": roof})
-        del w
-    return res
+def time_warm(torch, w, warmup, reps):
+    """Event times (ms) of `reps` back-to-back calls after `warmup` calls."""
+    for _ in range(warmup):
+        w.run()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for e0, e1 in ev:
+        e0.record()
+        w.run()
+        e1.record()
+    torch.cuda.synchronize()
+    return [e0.elapsed_time(e1) for e0, e1 in ev]
+
+
+def _roof(w, ms):
+    r = roofline_of(w, ms)
+    roof = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}
+    roof["traffic"] = traffic_for(w)
+    return roof
+
+
+def entry(w, flushed, warm):
+    """One workload's record: the headline time is the mean over calls after a
+    cache flush; the warm (back-to-back) mean beside it."""
+    ms = float(np.mean(flushed))
+    d = {"workload": w.name, "kernel": w.kernel, "shape": w.shape, "ms": round(ms, 5),
+         "ms_median": round(float(np.median(flushed)), 5), "ms_min": round(float(np.min(flushed)), 5),
+         "warm_ms": round(float(np.mean(warm)), 5) if warm else None,
+         "tokens_per_s": w.tokens / (ms * 1e-3), "roofline": _roof(w, ms)}
+    hbm = roofline_of(w, ms, "hbm")
+    d["hbm_gbs"] = round(hbm["achieved"], 1)
+    d["hbm_frac"] = round(hbm["frac"], 4)
+    if w.exps:
+        d["exp_per_s"] = w.exps / (ms * 1e-3)
+    return d
 
 
 def copy_calibration(torch, reps=5):
@@ -727,6 +786,90 @@ def copy_calibration(torch, reps=5):
     return 0
 
 
+# ----------------------------------------------------------------------------
+# rocprofv3 summaries (markdown) of this script's own runs
+# ----------------------------------------------------------------------------
+def _short(name):
+    n = name.replace("mb::(anonymous namespace)::", "")
+    if n.startswith("void "):
+        n = n[5:]
+    k = n.find("(")
+    return n[:k] if k > 0 else n
+
+
+def summarize(paths):
+    """Markdown tables from rocprofv3 csv output directories of bench.py runs.
+
+    Kernel trace: every dispatch before the first 512 MiB fill (the cache
+    flush) is in the warm phase (warm-up and back-to-back calls); every dispatch
+    after it is in the flushed phase (each workload call follows a flush).
+    Counter collection: the mean per dispatch of each counter, with the MFMA
+    busy fraction (SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE / 8 XCDs x
+    1024 SIMDs), the VALU busy fraction of a wave's life (SQ_ACTIVE_INST_VALU /
+    SQ_WAVE_CYCLES) and the LDS bank-conflict share (SQ_LDS_BANK_CONFLICT /
+    SQ_LDS_IDX_ACTIVE)."""
+    import csv
+    import glob
+    out = []
+    for d in paths:
+        for f in sorted(glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)):
+            rows = list(csv.DictReader(open(f)))
+            rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+            phase, stats = "warm", {}
+            for r in rows:
+                name = _short(r["Kernel_Name"])
+                if "FillFunctor" in name:
+                    phase = "flushed"
+                    continue
+                us = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+                stats.setdefault((name, phase), []).append(us)
+            out.append("Kernel trace `%s`\n" % os.path.relpath(f, d))
+            out.append("| kernel | phase | calls | avg µs | median µs | min µs | max µs |")
+            out.append("|---|---|---:|---:|---:|---:|---:|")
+            for (name, ph), v in sorted(stats.items(), key=lambda kv: (kv[0][0], kv[0][1] != "flushed")):
+                out.append("| `%s` | %s | %d | %.2f | %.2f | %.2f | %.2f |" % (
+                    name, ph, len(v), np.mean(v), np.median(v), np.min(v), np.max(v)))
+            out.append("")
+    # counters: every counter file of every directory in one table (one pass per
+    # directory; a kernel's mean per dispatch in each)
+    acc, files = {}, []
+    for d in paths:
+        for f in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
+            files.append(os.path.basename(f))
+            for r in csv.DictReader(open(f)):
+                name = _short(r["Kernel_Name"])
+                if "FillFunctor" in name or "copyBuffer" in name:
+                    continue
+                acc.setdefault(name, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    if acc:
+        cnames = sorted({c for v in acc.values() for c in v})
+        out.append("Counters from %s (mean per dispatch)\n" % ", ".join("`%s`" % f for f in files))
+        extra = []
+        if {"SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE"} <= set(cnames):
+            extra.append("MFMA busy")
+        if {"SQ_ACTIVE_INST_VALU", "SQ_WAVE_CYCLES"} <= set(cnames):
+            extra.append("VALU busy")
+        if {"SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE"} <= set(cnames):
+            extra.append("LDS conflict")
+        out.append("| kernel | dispatches | " + " | ".join(cnames + extra) + " |")
+        out.append("|---|---:|" + "---:|" * (len(cnames) + len(extra)))
+        for name, cv in acc.items():
+            m = {c: float(np.mean(v)) for c, v in cv.items()}
+            cells = ["%.0f" % m[c] if c in m else "" for c in cnames]
+            if "MFMA busy" in extra:
+                cells.append("%.1f%%" % (100 * m.get("SQ_VALU_MFMA_BUSY_CYCLES", 0) /
+                                         max(1.0, m.get("GRBM_GUI_ACTIVE", 0) / 8 * 1024)))
+            if "VALU busy" in extra:
+                cells.append("%.1f%%" % (100 * m.get("SQ_ACTIVE_INST_VALU", 0) / max(1.0, m.get("SQ_WAVE_CYCLES", 0))))
+            if "LDS conflict" in extra:
+                cells.append("%.1f%%" % (100 * m.get("SQ_LDS_BANK_CONFLICT", 0) / max(1.0, m.get("SQ_LDS_IDX_ACTIVE", 0))))
+            n = len(next(iter(cv.values())))
+            out.append("| `%s` | %d | %s |" % (name, n, " | ".join(cells)))
+        out.append("")
+    print("\n".join(out))
+    return 0
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -737,10 +880,15 @@ def main():
     ap.add_argument("--no-cold", action="store_true",
                     help="skip the per-workload timings after a last-level-cache flush")
     ap.add_argument("--no-next", action="store_true",
-                    help="skip the decode steps of the SSD family measured beside the step")
+                    help="skip the workloads measured beside the step")
+    ap.add_argument("--next", default="", help="comma-separated subset of the workloads beside the step")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy (reference for rocprofv3 byte counters)")
+    ap.add_argument("--summarize", nargs="+", metavar="DIR",
+                    help="print markdown summaries of rocprofv3 csv output directories and exit")
     args = ap.parse_args()
+    if args.summarize:
+        return summarize(args.summarize)
     if args.gpus != 1:
         print("bench.py measures one GPU; this library has no multi-GPU path (run with --gpus 1)",
               file=sys.stderr)
@@ -763,6 +911,7 @@ def main():
         ws.append(make(n, mb, wl, torch))
     torch.cuda.synchronize()
 
+    # ---- warm phase: the step, back to back --------------------------------------
     for _ in range(args.warmup):
         for w in ws:
             w.run()
@@ -779,37 +928,38 @@ def main():
             ev[k][i][1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-
-    per = []
-    for i, w in enumerate(ws):
-        ms = [ev[k][i][0].elapsed_time(ev[k][i][1]) for k in range(args.steps)]
-        per.append(float(np.mean(ms)))
+    warm = [[ev[k][i][0].elapsed_time(ev[k][i][1]) for k in range(args.steps)] for i in range(len(ws))]
     ms_per_step = wall * 1e3 / args.steps
     tokens = sum(w.tokens for w in ws)
-    kernels = []
-    for w, ms in zip(ws, per):
-        r = roofline_of(w, ms)
-        d = {"workload": w.name, "ms": round(ms, 5), "tokens_per_s": w.tokens / (ms * 1e-3),
-             "roofline": {k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}}
-        hbm = roofline_of(w, ms, "hbm")
-        d["hbm_gbs"] = round(hbm["achieved"], 1)
-        d["hbm_frac"] = round(hbm["frac"], 4)
-        if w.exps:
-            d["exp_per_s"] = w.exps / (ms * 1e-3)
-        kernels.append(d)
-    dom = int(np.argmax(per))
-    w = ws[dom]
-    r = roofline_of(w, per[dom])
-    roof = {"bound": r["bound"], "achieved": round(r["achieved"], 3), "peak": r["peak"],
-            "unit": r["unit"], "frac": round(r["frac"], 4), "traffic": traffic_for(w),
-            "kernel": w.kernel, "workload": w.name}
 
+    nxt_names = [] if (args.no_next or args.only) else (
+        [n for n in args.next.split(",") if n] if args.next else NEXT)
+    nxt_warm = []
+    for n in nxt_names:
+        print("# preparing %s" % n, file=sys.stderr, flush=True)
+        w = make(n, mb, wl, torch)
+        nxt_warm.append((w, time_warm(torch, w, args.warmup, args.steps)))
+        if not args.no_cold:
+            w.inp = None   # keep the device tensors only
+        else:
+            del w
+
+    # ---- flushed phase: every call after a last-level-cache flush -----------------
     if not args.no_cold:
-        print("# cold timings (last-level cache flushed before each call)", file=sys.stderr, flush=True)
-        for w, d in zip(ws, kernels):
-            cms = cold_ms(torch, w)
-            d["cold_ms"] = round(cms, 5)
-            d["cold_hbm_frac"] = round(w.bytes / (cms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+        print("# flushed timings (last-level cache flushed before each call)", file=sys.stderr, flush=True)
+        flushed = [time_flushed(torch, w, args.steps) for w in ws]
+        nxt = [entry(w, time_flushed(torch, w, args.steps), t) for w, t in nxt_warm]
+    else:
+        flushed = warm
+        nxt = [entry(w, t, t) for w, t in nxt_warm]
+    del nxt_warm
+
+    kernels = [entry(w, f, t) for w, f, t in zip(ws, flushed, warm)]
+    dom = int(np.argmax([np.mean(t) for t in warm]))
+    roof = dict(kernels[dom]["roofline"])
+    roof.update({"kernel": ws[dom].kernel, "workload": ws[dom].name,
+                 "timing": "mean event time per call after a last-level-cache flush" if not args.no_cold
+                 else "mean event time per call, back to back"})
 
     out = {
         "metric": "scanned tokens/sec, SSD fwd L=4096 + M1 scan; % MFMA / % HBM roofline",
@@ -823,13 +973,15 @@ def main():
         "config": {"workload": "+".join(names), "tokens_per_step": tokens,
                    "shapes": {w.name: w.shape for w in ws}},
         "roofline": roof,
+        # the two workloads the metric names, beside the dominant one
+        "rooflines": {d["workload"]: d["roofline"] for d in kernels if d["workload"] in ("ssd_f32", "m1_scan")},
         "kernels": kernels,
     }
-    if not args.no_next and not args.only:
-        out["next"] = time_next(args, mb, wl, torch)
+    if nxt:
+        out["next"] = nxt
     if not args.no_cpu:
         print("# timing the oracle on the host", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(ws)
+        out["cpu_baseline"] = cpu_baseline(ws, wl)
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out))
