@@ -177,7 +177,7 @@ def _dev(a, dtype):
 
 class M1Scan(Workload):
     name = "m1_scan"
-    kernel = "k_m1_scan"
+    kernel = "k_m1_scan_w"
     bound = "alu"
     source = "selective_state_space_amd/csrc/m1.hip"
 
@@ -198,6 +198,43 @@ class M1Scan(Workload):
 
     def run(self):
         self.mb.mb_selective_scan(self.x, self.dt, self.A, self.B, self.C, self.D, None, y=self.y, h_out=self.h)
+
+
+class M1Long(M1Scan):
+    """One long sequence of the Mamba-1 block model's width (batch 1, L 16384,
+    D 1536, N 16: as many (t, c, n) elements as the block workload, but 24
+    channel groups for 256 compute units): the scan cut into sequence blocks
+    with the carry pass (the default), or in one block (`m1_long_one_block`);
+    outside the step, measured beside it."""
+    name = "m1_long"
+    kernel = "k_m1_scan_w (carry pass) + k_m1_scan_w (sequence blocks)"
+
+    def __init__(self, mb, wl, torch, one_block=False):
+        self.mb = mb
+        b, L, D, N = 1, 16384, 1536, 16
+        self.shape = dict(batch=b, L=L, D=D, N=N, sequence_blocks=not one_block)
+        inp = wl.m1_block(batch=b, L=L)
+        self.inp = inp
+        f = torch.float32
+        self.x, self.dt, self.B, self.C = (_dev(inp[k], f) for k in ("x", "dt", "B", "C"))
+        self.A, self.D = _dev(inp["A"], f), _dev(inp["D"], f)
+        self.y = torch.empty_like(self.x)
+        self.h = torch.empty((b, D, N), dtype=f, device="cuda")
+        self.one_block = one_block
+        if one_block:
+            self.name = "m1_long_one_block"
+            self.kernel = "k_m1_scan_w"
+            self.ws = None
+        else:
+            self.ws = torch.empty(max(256, mb.mb_workspace_size(mb.MB_OP_SELECTIVE_SCAN, b, L, D, 1, 1, N)),
+                                  dtype=torch.uint8, device="cuda")
+        self.tokens = b * L
+        self.bytes, self.exps = m1_scan_work(b, L, D, N)
+        self.flops = None
+
+    def run(self):
+        self.mb.mb_selective_scan(self.x, self.dt, self.A, self.B, self.C, self.D, None, y=self.y, h_out=self.h,
+                                  ws=self.ws, seq_blocks=not self.one_block)
 
 
 class M1Fused(Workload):
@@ -578,7 +615,7 @@ ALL = ["m1_scan", "m1_step", "ssd_f32", "ssd_bf16", "siso", "mimo"]
 # Mamba-1 scan with the block prologue and epilogue fused, the Mamba-2 block prologue, Mamba-3 SISO with its output
 # epilogue and with both ends of its block fused, and the backwards of the
 # Mamba-2 SSD, the Mamba-1 scan, Mamba-3 SISO and MIMO
-NEXT = ["m2_decode", "siso_decode", "mimo_decode", "m1_fused", "m2_prologue", "siso_gated", "siso_block", "ssd_bwd", "m1_bwd", "siso_bwd", "mimo_bwd"]
+NEXT = ["m2_decode", "siso_decode", "mimo_decode", "m1_long", "m1_long_one_block", "m1_fused", "m2_prologue", "siso_gated", "siso_block", "ssd_bwd", "m1_bwd", "siso_bwd", "mimo_bwd"]
 
 
 def make(name, mb, wl, torch):
@@ -588,6 +625,10 @@ def make(name, mb, wl, torch):
         return M1Step(mb, wl, torch)
     if name == "m1_fused":
         return M1Fused(mb, wl, torch)
+    if name == "m1_long":
+        return M1Long(mb, wl, torch)
+    if name == "m1_long_one_block":
+        return M1Long(mb, wl, torch, one_block=True)
     if name == "m2_prologue":
         return M2Prologue(mb, wl, torch)
     if name == "siso_block":
@@ -932,8 +973,12 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
     tokens = sum(w.tokens for w in ws)
 
-    nxt_names = [] if (args.no_next or args.only) else (
-        [n for n in args.next.split(",") if n] if args.next else NEXT)
+    if args.no_next:
+        nxt_names = []
+    elif args.next:
+        nxt_names = [n for n in args.next.split(",") if n]
+    else:
+        nxt_names = [] if args.only else NEXT
     nxt_warm = []
     for n in nxt_names:
         print("# preparing %s" % n, file=sys.stderr, flush=True)

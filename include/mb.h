@@ -85,12 +85,26 @@ typedef enum {
  * Supported: 1 <= N <= 64, and one batch row of x and of B addressed in
  * 32-bit offsets: (L + 64) * D * 4 < 2^31 and (L + 64) * N * 4 < 2^31
  * (MB_ERR_SHAPE otherwise); any batch >= 0.
+ * ws / ws_bytes: optional device workspace for sequence blocks (the Math
+ * notes M1 recurrence is time-varying and is computed as a scan; a scan splits
+ * into blocks because the pair (decay product, state) of consecutive blocks
+ * composes associatively: (P1, h1) then (P2, h2) is (P1 P2, P2 h1 + h2), and
+ * a block's decay product is exp(A * sum of its dt)).  With ws != NULL of at
+ * least mb_workspace_size(MB_OP_SELECTIVE_SCAN, batch, L, D, 1, 1, N) bytes,
+ * 256-byte aligned (MB_ERR_WORKSPACE otherwise), the fp32 path with N in
+ * {4, 8, 16} and 16-byte aligned x, dt, B, C cuts the sequence into as many
+ * blocks as it takes to fill the device (the size is 0 when one block does):
+ * a first pass computes every block's own (decay product, end state), a
+ * second starts each block from the composition of the blocks before it.  The
+ * result equals the one-block scan up to rounding.  ws = NULL (or bf16, other
+ * N): the whole sequence in one block.  ws must not overlap any argument;
+ * contents on entry are ignored.
  */
 mb_status mb_selective_scan(const void* x, const void* dt, const float* A,
                             const void* B, const void* C, const float* Dskip,
                             const float* h0, void* y, float* h_out,
                             int64_t batch, int64_t L, int64_t D, int64_t N,
-                            mb_dtype dtype, hipStream_t stream);
+                            mb_dtype dtype, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * Mamba-1 single-token decode step (burn_mamba `struct Mamba1` docs,

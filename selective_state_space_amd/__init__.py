@@ -60,7 +60,7 @@ def load_library():
         if not os.path.exists(_LIB_PATH):
             raise ImportError("libmb.so not built: run `python -m selective_state_space_amd._build`")
         lib = ctypes.CDLL(_LIB_PATH)
-        lib.mb_selective_scan.argtypes = [_vp] * 9 + [_i64] * 4 + [ctypes.c_int, _vp]
+        lib.mb_selective_scan.argtypes = [_vp] * 9 + [_i64] * 4 + [ctypes.c_int, _vp, ctypes.c_size_t, _vp]
         lib.mb_ssm_step.argtypes = [_vp] * 9 + [_i64] * 3 + [ctypes.c_int, _vp]
         if hasattr(lib, "mb_ssd_chunked"):
             lib.mb_ssd_chunked.argtypes = [_vp] * 7 + [_i64] * 7 + [ctypes.c_int, _vp, ctypes.c_size_t, _vp]
@@ -187,10 +187,12 @@ def _workspace(op, device, ws, dims):
 # ----------------------------------------------------------------------------
 # entry points
 # ----------------------------------------------------------------------------
-def mb_selective_scan(x, dt, A, B, C, D=None, h0=None, *, y=None, h_out=None):
+def mb_selective_scan(x, dt, A, B, C, D=None, h0=None, *, y=None, h_out=None, ws=None, seq_blocks=True):
     """Mamba-1 selective scan.  x, dt (batch, L, D) and B, C (batch, L, N) share
     one dtype (float32 or bfloat16); A (D, N), D (D,), h0 (batch, D, N) float32.
-    Returns (y, h_out)."""
+    With seq_blocks (the default) the library may cut the sequence into blocks
+    run in parallel (a workspace is allocated here unless `ws` is given);
+    seq_blocks=False runs the whole sequence in one block.  Returns (y, h_out)."""
     torch = _torch()
     dev = _device_of(x)
     dtype = x.dtype
@@ -207,8 +209,13 @@ def mb_selective_scan(x, dt, A, B, C, D=None, h0=None, *, y=None, h_out=None):
     y = torch.empty((b, L, Dm), dtype=dtype, device=dev) if y is None else _check(y, "y", (b, L, Dm), dtype, dev)
     h_out = torch.empty((b, Dm, N), dtype=torch.float32, device=dev) if h_out is None else \
         _check(h_out, "h_out", (b, Dm, N), torch.float32, dev)
+    nws = 0
+    if seq_blocks and mb_workspace_size(MB_OP_SELECTIVE_SCAN, b, L, Dm, 1, 1, N) > 0:
+        ws, nws = _workspace(MB_OP_SELECTIVE_SCAN, dev, ws, (b, L, Dm, 1, 1, N, 1, 0))
+    else:
+        ws = None
     _call("mb_selective_scan", _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(h0),
-          _ptr(y), _ptr(h_out), b, L, Dm, N, code, _stream(dev))
+          _ptr(y), _ptr(h_out), b, L, Dm, N, code, _ptr(ws), nws, _stream(dev))
     return y, h_out
 
 

@@ -12,6 +12,8 @@
 //                tiles copied into LDS by DMA, no barriers.
 //   k_m1_scan    any other case: workgroups of 64 channels x ceil(N/4) waves,
 //                partial sums over states reduced through LDS once per tile.
+#include <algorithm>
+
 #include "mb_internal.h"
 
 namespace mb {
@@ -213,9 +215,9 @@ constexpr int kScanT = 32;   // steps per tile
 
 // one tile in LDS: dt[T][16], x[T][16], B[T][N], C[T][N], and with the block
 // prologue / epilogue the gate z[T][16]
-template <int S, bool Z = false>
+template <int S, bool Z = false, int T = kScanT>
 struct ScanTile {
-    float v[kScanT * (32 + 8 * S + (Z ? 16 : 0))];
+    float v[T * (32 + 8 * S + (Z ? 16 : 0))];
 };
 
 // The block prologue / epilogue of the fused scan (its extra inputs).
@@ -227,6 +229,21 @@ struct Fuse {
     const float* z;         // (batch, L, D) gate, or NULL
     int K;
     float* ck;              // checkpoint mode: (batch, ntiles, D, N) state entering every tile
+};
+
+// Sequence blocks (the cross-block carry of the scan).  The sequence is cut
+// into nblk blocks of blk_tiles tiles.  The carry pass (MODE 1) runs blocks
+// 0 .. nblk - 2 at once, each on its own: block 0 from h0, the others from
+// zero, and writes per (batch, block) the block's end state and the sum of its
+// step sizes.  Since the decay product of a block is exp(A sum dt), the pair
+// (exp(A sdt_k), hloc_k) of block k composes with the state h entering it as
+// exp(A sdt_k) h + hloc_k, and the scan pass (MODE 0) starts block j from the
+// composition of blocks 0 .. j - 1.  nblk <= 1: the whole sequence in one
+// block, no carry pass, no workspace.
+struct Seq {
+    int nblk, blk_tiles, units;   // units: batch x channel groups (workgroups per block)
+    float* hblk;   // (batch, nblk, D, N): slot 0 = h0 (zeros when NULL), slot k + 1 = end of block k
+    float* sdt;    // (batch, nblk, D): sum of dt over block k
 };
 
 // lane j's value of a quad, to every lane of the quad
@@ -300,13 +317,16 @@ __device__ __forceinline__ void dma_lds(const Buf& src, lds_f* dst, uint32_t off
         __builtin_amdgcn_raw_ptr_buffer_load_lds(src.r, (__attribute__((address_space(3))) void*)dst, 4, off, 0, 0, 0);
 }
 
-template <int S, bool V16, bool FUSED = false, bool CK = false>
+// MODE 0: the scan (y and the final state) over the whole sequence or over one
+// sequence block; MODE 1: the carry pass (state only, no C, no y).
+template <int S, bool V16, bool FUSED = false, bool CK = false, int MODE = 0, int T = kScanT>
 __global__ __launch_bounds__(256) void k_m1_scan_w(
     const float* __restrict__ x, const float* __restrict__ dt, const float* __restrict__ A,
     const float* __restrict__ Bm, const float* __restrict__ Cm, const float* __restrict__ Dskip,
-    const float* h0, float* y, float* h_out, int L, int D, int n_cg, Fuse fz = Fuse{})
+    const float* h0, float* y, float* h_out, int L, int D, int n_cg, Fuse fz = Fuse{}, Seq sq = Seq{})
 {
-    constexpr int T = kScanT;
+    constexpr bool CARRY = MODE == 1;
+    static_assert(!(CARRY && (FUSED || CK)), "the carry pass is a plain state-only scan");
     constexpr int N = 4 * S;
     constexpr int NG = T / 4;                   // groups of four steps per tile
     constexpr bool BC16 = (T * N) % 256 == 0;   // 16-byte copies for the B / C tile
@@ -314,20 +334,24 @@ __global__ __launch_bounds__(256) void k_m1_scan_w(
     constexpr int BW = BC16 ? 16 : 4;
     constexpr int NDX = T * 16 * 4 / (64 * XW); // copies per dt / x tile
     constexpr int NDB = T * N * 4 / (64 * BW);  // copies per B / C tile
-    constexpr int NDMA = (FUSED ? 3 : 2) * NDX + 2 * NDB;   // copies per tile
+    constexpr int NDMA = CARRY ? 2 * NDX + NDB : (FUSED ? 3 : 2) * NDX + 2 * NDB;   // copies per tile
     constexpr int OX = T * 16, OB = 2 * T * 16, OC = 2 * T * 16 + T * N;   // offsets in a tile
     constexpr int OZ = OC + T * N;
     // three tile buffers, separate objects so that a copy into one never orders
     // the reads of another
-    __shared__ __attribute__((aligned(16))) ScanTile<S, FUSED> tb0[4];
-    __shared__ __attribute__((aligned(16))) ScanTile<S, FUSED> tb1[4];
-    __shared__ __attribute__((aligned(16))) ScanTile<S, FUSED> tb2[4];
+    __shared__ __attribute__((aligned(16))) ScanTile<S, FUSED, T> tb0[4];
+    __shared__ __attribute__((aligned(16))) ScanTile<S, FUSED, T> tb1[4];
+    __shared__ __attribute__((aligned(16))) ScanTile<S, FUSED, T> tb2[4];
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
     lds_f* const p0 = (lds_f*)tb0[w].v;
     lds_f* const p1 = (lds_f*)tb1[w].v;
     lds_f* const p2 = (lds_f*)tb2[w].v;
 
-    const int b = blockIdx.x / n_cg, c0 = (blockIdx.x % n_cg) * 64 + 16 * w;
+    // workgroup -> (sequence block, batch, channel group); blocks are the slowest
+    const bool blocks = sq.nblk > 1;
+    const int ub = blocks ? (int)(blockIdx.x % sq.units) : (int)blockIdx.x;
+    const int jb = blocks ? (int)(blockIdx.x / sq.units) : 0;
+    const int b = ub / n_cg, c0 = (ub % n_cg) * 64 + 16 * w;
     const int lane = threadIdx.x % 64;
     const int cl = lane >> 2, q = lane & 3;
     const int c = c0 + cl;
@@ -347,20 +371,27 @@ __global__ __launch_bounds__(256) void k_m1_scan_w(
     const uint32_t xo = V16 ? (uint32_t)(((lane >> 2) * D + c0 + 4 * (lane & 3)) * 4)
                             : (uint32_t)(((lane >> 4) * D + c0 + (lane & 15)) * 4);
     const uint32_t bo = (uint32_t)(BW * lane);
+    // tiles of this wave's sequence block: kb0 .. kb1 - 1
+    const int ntiles = (L + T - 1) / T;
+    const int kb0 = blocks ? jb * sq.blk_tiles : 0;
+    const int kb1 = blocks ? min(ntiles, kb0 + sq.blk_tiles) : ntiles;
     auto dma = [&](int k, lds_f* dst) __attribute__((always_inline)) {
         const int t0 = k * T;
+        // copies of tiles past the block read zeros without touching memory (the
+        // copy count stays fixed, so the waits stay exact)
+        const uint32_t kill = k < kb1 ? 0u : 0x80000000u;
 #pragma unroll
         for (int m = 0; m < NDX; ++m) {
-            const uint32_t off = xo + (uint32_t)((t0 + XW * m) * D) * 4u;   // XW steps per copy
+            const uint32_t off = (xo + (uint32_t)((t0 + XW * m) * D) * 4u) | kill;   // XW steps per copy
             dma_lds<XW>(bdt, dst + 16 * XW * m, off);
             dma_lds<XW>(bx, dst + OX + 16 * XW * m, off);
             if constexpr (FUSED) dma_lds<XW>(bz, dst + OZ + 16 * XW * m, off);
         }
 #pragma unroll
         for (int m = 0; m < NDB; ++m) {
-            const uint32_t off = bo + (uint32_t)(t0 * N + 16 * BW * m) * 4u;
+            const uint32_t off = (bo + (uint32_t)(t0 * N + 16 * BW * m) * 4u) | kill;
             dma_lds<BW>(bB, dst + OB + 16 * BW * m, off);
-            dma_lds<BW>(bC, dst + OC + 16 * BW * m, off);
+            if constexpr (!CARRY) dma_lds<BW>(bC, dst + OC + 16 * BW * m, off);
         }
     };
 
@@ -377,9 +408,9 @@ __global__ __launch_bounds__(256) void k_m1_scan_w(
             g.dt[j] = cur[t * 16 + cl];
             g.x[j] = cur[OX + t * 16 + cl];
             lds_row<S>(cur + OB + t * N + S * q, g.b[j]);
-            lds_row<S>(cur + OC + t * N + S * q, g.c[j]);
+            if constexpr (!CARRY) lds_row<S>(cur + OC + t * N + S * q, g.c[j]);
         }
-        g.xs = cur[(FUSED ? OZ : OX) + (4 * i + q) * 16 + cl];
+        if constexpr (!CARRY) g.xs = cur[(FUSED ? OZ : OX) + (4 * i + q) * 16 + cl];
     };
 
     float A2[S], h[S];
@@ -387,9 +418,37 @@ __global__ __launch_bounds__(256) void k_m1_scan_w(
     for (int s = 0; s < S; ++s) {
         const int n = S * q + s;
         A2[s] = cok ? A[(size_t)c * N + n] * kLog2e : 0.0f;
-        h[s] = (cok && h0) ? h0[((size_t)b * D + c) * N + n] : 0.0f;
+        h[s] = (cok && h0 && (!blocks || (CARRY && jb == 0))) ? h0[((size_t)b * D + c) * N + n] : 0.0f;
+    }
+    // the state entering the block
+    auto slot = [&](int k) __attribute__((always_inline)) {
+        return sq.hblk + (((size_t)b * sq.nblk + k) * D + c) * N + S * q;
+    };
+    if (blocks && cok) {
+        if constexpr (CARRY) {
+            // block 0 keeps the initial state for the scan pass (h0 itself may
+            // be overwritten by the scan pass as its h_out)
+            if (jb == 0) {
+#pragma unroll
+                for (int s = 0; s < S; ++s) slot(0)[s] = h[s];
+            }
+        } else if (jb == 0) {
+#pragma unroll
+            for (int s = 0; s < S; ++s) h[s] = slot(0)[s];
+        } else {
+            // compose (exp(A sdt_k), hloc_k) over the blocks before this one
+#pragma unroll
+            for (int s = 0; s < S; ++s) h[s] = slot(1)[s];
+            for (int k = 1; k < jb; ++k) {
+                const float sd = sq.sdt[((size_t)b * sq.nblk + k) * D + c];
+                const float* hl = slot(k + 1);
+#pragma unroll
+                for (int s = 0; s < S; ++s) h[s] = fmaf(exp2_fast(sd * A2[s]), h[s], hl[s]);
+            }
+        }
     }
     const float Dv = (cok && Dskip) ? Dskip[c] : 0.0f;
+    float sdt_acc = 0.0f;   // carry pass: sum of this channel's step sizes over the block
     const bool lo = (q & 2) == 0, ev = (q & 1) == 0;
 
     // fused: the convolution taps (right-aligned to four), the biases and the
@@ -441,12 +500,11 @@ __global__ __launch_bounds__(256) void k_m1_scan_w(
         g.dt[2] = quad_bcast<2>(dq); g.dt[3] = quad_bcast<3>(dq);
     };
 
-    const int ntiles = (L + T - 1) / T;
     Grp g;
-    dma(0, p0);
-    vm_wait<0>();         // tile 0 (and the initial state) has arrived
+    dma(kb0, p0);
+    vm_wait<0>();         // the block's first tile (and the initial state) has arrived
     asm volatile("" ::: "memory");
-    dma(1, p1);
+    dma(kb0 + 1, p1);
     read_grp(p0, 0, g);
     if constexpr (FUSED) prologue(g, 0);
 
@@ -472,8 +530,8 @@ __global__ __launch_bounds__(256) void k_m1_scan_w(
             } else {
                 // tile k + 1's copies were followed by at most the previous
                 // tile's stores, tile k + 2's copies and this tile's first NG - 1
-                // stores
-                vm_wait<NDMA + NG - 1>();
+                // stores (the carry pass stores nothing)
+                vm_wait<CARRY ? NDMA : NDMA + NG - 1>();
                 asm volatile("" ::: "memory");
                 read_grp(nxt, 0, gn);
             }
@@ -484,6 +542,18 @@ __global__ __launch_bounds__(256) void k_m1_scan_w(
             for (int j = 0; j < 4; ++j) {
                 xcv[j] = g.x[j];
                 dtev[j] = g.dt[j];
+            }
+            if constexpr (CARRY) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float dtv = dtev[j];
+                    const float dtx = dtv * xcv[j];
+#pragma unroll
+                    for (int s = 0; s < S; ++s) h[s] = fmaf(exp2_fast(dtv * A2[s]), h[s], dtx * g.b[j][s]);
+                    sdt_acc += dtv;
+                }
+                g = gn;
+                continue;
             }
             float ps[4];
 #pragma unroll
@@ -518,13 +588,19 @@ __global__ __launch_bounds__(256) void k_m1_scan_w(
             g = gn;
         }
     };
-    for (int k = 0; k < ntiles; k += 3) {
+    for (int k = kb0; k < kb1; k += 3) {
         tile(k, p0, p1, p2);
-        if (k + 1 < ntiles) tile(k + 1, p1, p2, p0);
-        if (k + 2 < ntiles) tile(k + 2, p2, p0, p1);
+        if (k + 1 < kb1) tile(k + 1, p1, p2, p0);
+        if (k + 2 < kb1) tile(k + 2, p2, p0, p1);
     }
     vm_wait<0>();   // no copy into LDS may be in flight when the wave ends
-    if (h_out && cok) {
+    if constexpr (CARRY) {
+        if (cok) {
+#pragma unroll
+            for (int s = 0; s < S; ++s) slot(jb + 1)[s] = h[s];
+            if (q == 0) sq.sdt[((size_t)b * sq.nblk + jb) * D + c] = sdt_acc;
+        }
+    } else if (h_out && cok && (!blocks || jb == sq.nblk - 1)) {
 #pragma unroll
         for (int s = 0; s < S; ++s) h_out[((size_t)b * D + c) * N + S * q + s] = h[s];
     }
@@ -932,11 +1008,68 @@ __global__ __launch_bounds__(256) void k_m1_step_any(
     store_out(&y[bc], fmaf(dv, xv, p));
 }
 
+constexpr int kScanTB = 16;   // steps per tile of the sequence-block scan
+
+struct M1Plan {
+    int nblk, blk_tiles;
+    size_t off_sdt, bytes;
+};
+
+// Sequence blocks of the fp32 scan (N in {4, 8, 16}, the k_m1_scan_w layout).
+// The carry pass repeats most of the scan's work without its output, so blocks
+// pay only where batch x channel groups leave SIMDs idle: with workgroups of
+// four waves for at least three quarters of the SIMDs the scan runs in one
+// block; otherwise in enough blocks for about three workgroups (three waves
+// per SIMD) on every compute unit, each block at least four tiles long.
+// Measured on MI355X (fp32, N 16, D 1536, cache flushed): batch 1, L 16384:
+// 1.007 ms in one block, 0.186 ms in 32; batch 4, L 4096: 0.269 -> 0.182 ms
+// in 8; batch 8, L 2048 (192 workgroups): 0.153 ms in one block, 0.175 in 4.
+// Depends on the sizes and the device's compute-unit count only, so
+// mb_workspace_size agrees with the call on the same device.
+M1Plan m1_plan(int64_t batch, int64_t L, int64_t D, int64_t N) {
+    M1Plan p{1, 0, 0, 0};
+    if ((N != 4 && N != 8 && N != 16) || batch <= 0 || L <= 0 || D <= 0) return p;
+    const int64_t units = batch * ((D + 63) / 64);
+    const int64_t ntiles = (L + kScanTB - 1) / kScanTB;
+    const int64_t cus = device_cu_count();
+    if (4 * units >= 3 * cus) return p;
+    int64_t nb = std::min<int64_t>((3 * cus + units - 1) / units, ntiles / 4);
+    if (nb <= 1) return p;
+    const int64_t bt = (ntiles + nb - 1) / nb;
+    nb = (ntiles + bt - 1) / bt;
+    if (nb <= 1 || units * nb > INT32_MAX) return p;
+    auto al = [](size_t v) { return (v + 255) & ~(size_t)255; };
+    p.nblk = (int)nb;
+    p.blk_tiles = (int)bt;
+    p.off_sdt = al((size_t)(batch * nb * D * N) * 4);
+    p.bytes = p.off_sdt + al((size_t)(batch * nb * D) * 4);
+    return p;
+}
+
+template <int S, bool V16>
+mb_status launch_scan_blocks(const float* x, const float* dt, const float* A, const float* B,
+                             const float* C, const float* Dskip, const float* h0, float* y,
+                             float* h_out, int64_t batch, int64_t L, int64_t D, const M1Plan& pl,
+                             char* ws, hipStream_t stream) {
+    const int n_cg = (int)((D + 63) / 64);
+    const int units = (int)(batch * n_cg);
+    const Seq sq{pl.nblk, pl.blk_tiles, units, (float*)ws, (float*)(ws + pl.off_sdt)};
+    hipLaunchKernelGGL((k_m1_scan_w<S, V16, false, false, 1, kScanTB>), dim3((unsigned)(units * (pl.nblk - 1))),
+                       dim3(256), 0, stream, x, dt, A, B, C, Dskip, h0, nullptr, nullptr, (int)L, (int)D,
+                       n_cg, Fuse{}, sq);
+    mb_status st = check_launch();
+    if (st != MB_OK) return st;
+    hipLaunchKernelGGL((k_m1_scan_w<S, V16, false, false, 0, kScanTB>), dim3((unsigned)(units * pl.nblk)),
+                       dim3(256), 0, stream, x, dt, A, B, C, Dskip, h0, y, h_out, (int)L, (int)D, n_cg,
+                       Fuse{}, sq);
+    return check_launch();
+}
+
 template <typename IO>
 mb_status launch_scan(const void* x, const void* dt, const float* A, const void* B,
                       const void* C, const float* Dskip, const float* h0, void* y,
                       float* h_out, int64_t batch, int64_t L, int64_t D, int64_t N,
-                      hipStream_t stream)
+                      void* ws, size_t ws_bytes, hipStream_t stream)
 {
     if constexpr (sizeof(IO) == 4) {
         // 16-byte LDS copies need 16-byte aligned rows
@@ -945,6 +1078,23 @@ mb_status launch_scan(const void* x, const void* dt, const float* A, const void*
             const int n_cg = (int)((D + 63) / 64);
             const int n_wg = (int)(batch * n_cg);
             const bool v16 = D % 4 == 0;
+            const M1Plan pl = m1_plan(batch, L, D, N);
+            if (ws && pl.nblk > 1) {
+                if (ws_bytes < pl.bytes || ((uintptr_t)ws & 255)) return MB_ERR_WORKSPACE;
+#define MB_SCAN_B(S)                                                                                   \
+    return v16 ? launch_scan_blocks<S, true>((const float*)x, (const float*)dt, A, (const float*)B,        \
+                                             (const float*)C, Dskip, h0, (float*)y, h_out, batch, L, D, pl, \
+                                             (char*)ws, stream)                                            \
+               : launch_scan_blocks<S, false>((const float*)x, (const float*)dt, A, (const float*)B,       \
+                                              (const float*)C, Dskip, h0, (float*)y, h_out, batch, L, D,    \
+                                              pl, (char*)ws, stream)
+                switch (N) {
+                case 4: MB_SCAN_B(1);
+                case 8: MB_SCAN_B(2);
+                default: MB_SCAN_B(4);
+                }
+#undef MB_SCAN_B
+            }
 #define MB_SCAN_W(S)                                                                          \
     do {                                                                                     \
         if (v16)                                                                             \
@@ -1035,7 +1185,7 @@ extern "C" mb_status mb_selective_scan(const void* x, const void* dt, const floa
                                        const void* B, const void* C, const float* Dskip,
                                        const float* h0, void* y, float* h_out,
                                        int64_t batch, int64_t L, int64_t D, int64_t N,
-                                       mb_dtype dtype, hipStream_t stream)
+                                       mb_dtype dtype, void* ws, size_t ws_bytes, hipStream_t stream)
 {
     if (!dtype_ok(dtype)) return MB_ERR_DTYPE;
     if (batch < 0 || L < 0 || D < 0 || N < 1 || N > 64) return MB_ERR_SHAPE;
@@ -1060,9 +1210,15 @@ extern "C" mb_status mb_selective_scan(const void* x, const void* dt, const floa
     }
     if (batch == 0 || D == 0) return MB_OK;
     if (L == 0) return copy_state(h0, h_out, (int64_t)n_h, stream);
+    if (ws) {
+        const size_t need = m1_plan(batch, L, D, N).bytes;
+        if (need && (overlaps_any(ws, need, ins, 7) || overlaps(ws, need, y, n_x * es) ||
+                     overlaps(ws, need, h_out, h_out ? n_h * 4 : 0)))
+            return MB_ERR_ALIAS;
+    }
     if (dtype == MB_F32)
-        return launch_scan<float>(x, dt, A, B, C, Dskip, h0, y, h_out, batch, L, D, N, stream);
-    return launch_scan<bf16>(x, dt, A, B, C, Dskip, h0, y, h_out, batch, L, D, N, stream);
+        return launch_scan<float>(x, dt, A, B, C, Dskip, h0, y, h_out, batch, L, D, N, ws, ws_bytes, stream);
+    return launch_scan<bf16>(x, dt, A, B, C, Dskip, h0, y, h_out, batch, L, D, N, nullptr, 0, stream);
 }
 
 extern "C" mb_status mb_selective_scan_fused(const float* x, const float* conv_w, const float* conv_b,
@@ -1149,6 +1305,13 @@ bool m1_bwd_dims_ok(int64_t batch, int64_t L, int64_t D, int64_t N) {
     return true;
 }
 }  // namespace
+
+size_t m1_scan_workspace(int64_t batch, int64_t L, int64_t D, int64_t N) {
+    if (batch < 0 || L < 0 || D < 0 || N < 1 || N > 64) return 0;
+    if (batch > INT32_MAX || L > INT32_MAX || D > INT32_MAX) return 0;
+    if ((L + 64) * D * 4 >= ((int64_t)1 << 31) || (L + 64) * N * 4 >= ((int64_t)1 << 31)) return 0;
+    return m1_plan(batch, L, D, N).bytes;
+}
 
 size_t m1_bwd_workspace(int64_t batch, int64_t L, int64_t D, int64_t N) {
     if (!m1_bwd_dims_ok(batch, L, D, N) || batch == 0 || L == 0 || D == 0) return 0;

@@ -49,6 +49,9 @@ inline bool dtype_ok(mb_dtype d) { return d == MB_F32 || d == MB_BF16; }
 // Number of compute units of the current device (cached per device).
 int device_cu_count();
 
+// Workspace bytes of the Mamba-1 scan's sequence blocks (0: one block).
+size_t m1_scan_workspace(int64_t batch, int64_t L, int64_t D, int64_t N);
+
 // Workspace bytes of the Mamba-1 scan backward (0 for unsupported sizes).
 size_t m1_bwd_workspace(int64_t batch, int64_t L, int64_t D, int64_t N);
 

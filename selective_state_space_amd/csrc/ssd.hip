@@ -2067,7 +2067,9 @@ using namespace mb;
 extern "C" size_t mb_workspace_size(mb_op op, int64_t batch, int64_t L, int64_t H, int64_t P,
                                     int64_t G, int64_t N, int64_t R, int64_t chunk) {
     (void)chunk;
-    if (op == MB_OP_SELECTIVE_SCAN || op == MB_OP_SSM_STEP) return 0;
+    if (op == MB_OP_SSM_STEP) return 0;
+    // Mamba-1 scan: the sizes (batch, L, D, N) travel as (batch, L, H, N)
+    if (op == MB_OP_SELECTIVE_SCAN) return m1_scan_workspace(batch, L, H, N);
     if (op == MB_OP_SSD_CHUNKED_BWD) return ssd_bwd_workspace(batch, L, H, P, G, N);
     if (op == MB_OP_TRAP_SSD_BWD) return trap_bwd_workspace(batch, L, H, P, G, N);
     if (op == MB_OP_MIMO_SSD_BWD) return mimo_bwd_workspace(batch, L, H, P, N, R);

@@ -52,11 +52,12 @@ def P(x=FAKE):
 
 
 def scan(lib, x=FAKE, dt=FAKE, A=FAKE, B=FAKE, C=FAKE, D=None, h0=None, y=FAKE + (1 << 24),
-         h_out=FAKE + (1 << 25), batch=2, L=8, Dm=16, N=16, dtype=F32):
+         h_out=FAKE + (1 << 25), batch=2, L=8, Dm=16, N=16, dtype=F32, ws=None, ws_bytes=0):
     return lib.mb_selective_scan(P(x) if x else None, P(dt) if dt else None, P(A) if A else None,
                                  P(B) if B else None, P(C) if C else None, P(D) if D else None,
                                  P(h0) if h0 else None, P(y) if y else None,
-                                 P(h_out) if h_out else None, batch, L, Dm, N, dtype, None)
+                                 P(h_out) if h_out else None, batch, L, Dm, N, dtype, P(ws) if ws else None,
+                                 ws_bytes, None)
 
 
 def test_scan_validation(lib):
@@ -77,6 +78,26 @@ def test_scan_validation(lib):
     L_max = (1 << 31) // (4 * 512) - 64        # (L + 64) * D * 4 == 2^31 at D = 512
     assert scan(lib, **base, L=L_max, Dm=512) == E_SHAPE
     assert scan(lib, **dict(base, x=0), L=L_max - 1, Dm=512) == E_NULL
+
+
+def test_scan_workspace(lib):
+    """Sequence blocks: the workspace is optional; when given it must hold the
+    planned size, be 256-byte aligned and overlap nothing (checked before any
+    launch: the pointers are never dereferenced)."""
+    ws_size = lib.mb_workspace_size
+    b, L, Dm, N = 1, 4096, 64, 16          # one channel group: the planner cuts the sequence
+    need = ws_size(0, b, L, Dm, 1, 1, N, 1, 0)
+    assert need > 0 and need % 256 == 0
+    assert ws_size(0, 64, 64, 1536, 1, 1, 16, 1, 0) == 0     # enough parallel work: one block
+    assert ws_size(0, b, L, Dm, 1, 1, 64, 1, 0) == 0         # N = 64: one block
+    span = b * L * Dm * 4
+    base = dict(x=FAKE, dt=FAKE + span, A=FAKE + 2 * span, B=FAKE + 3 * span, C=FAKE + 4 * span,
+                y=FAKE + 5 * span, h_out=FAKE + 6 * span, batch=b, L=L, Dm=Dm, N=N)
+    W = FAKE + 8 * span
+    assert scan(lib, **base, ws=W, ws_bytes=need - 1) == E_WS
+    assert scan(lib, **base, ws=W + 16, ws_bytes=need) == E_WS           # not 256-byte aligned
+    assert scan(lib, **base, ws=FAKE + span, ws_bytes=need) == E_ALIAS   # over dt
+    assert scan(lib, **dict(base, x=0), ws=W, ws_bytes=need) == E_NULL
 
 
 def step(lib, h_in=FAKE + (1 << 26), h_out=FAKE + (1 << 26), y=FAKE + (1 << 27), **kw):
@@ -357,7 +378,14 @@ def _ws(op, batch, L, H, P, G, N, R=1):
 
 
 def test_workspace_sizes(lib):
-    assert mb.mb_workspace_size(mb.MB_OP_SELECTIVE_SCAN, 8, 2048, 1, 1, 1, 16) == 0
+    # Mamba-1 block workload (batch 8, L 2048, D 1536, N 16): 192 workgroups of 64
+    # channels fill three quarters of the SIMDs (256 compute units without a
+    # device), so one sequence block and no workspace; batch 1 at L 16384 has 24
+    # workgroups and runs in 32 blocks: a state and a step-size sum per (batch,
+    # block, channel)
+    assert mb.mb_workspace_size(mb.MB_OP_SELECTIVE_SCAN, 8, 2048, 1536, 1, 1, 16) == 0
+    assert mb.mb_workspace_size(mb.MB_OP_SELECTIVE_SCAN, 1, 16384, 1536, 1, 1, 16) == \
+        32 * 1536 * 16 * 4 + 32 * 1536 * 4
     # Mamba-2 block workload: 5 segments of 13 chunks; scores 4 MiB + B^T 4 MiB + 4
     # segment states
     assert mb.mb_workspace_size(mb.MB_OP_SSD_CHUNKED, 4, 4096, 24, 64, 1, 128) == \

@@ -137,6 +137,69 @@ def test_block_workload_full(oracle_mod, dtype):
     assert_close(h, hr, dtype, "h")
 
 
+# ------------------------------------------------------- sequence blocks ----
+def _blocks(b, L, D, N):
+    return mb.mb_workspace_size(mb.MB_OP_SELECTIVE_SCAN, b, L, D, 1, 1, N) > 0
+
+
+BLOCK_SHAPES = [(1, 8192, 64, 16),   # one channel group: 128 blocks of 64 steps
+                (2, 3000, 100, 16),  # ragged channels and last block
+                (1, 2000, 30, 8),    # D not a multiple of 4 (4-byte copies), N = 8
+                (3, 1111, 64, 4)]    # N = 4
+
+
+@pytest.mark.parametrize("shape", BLOCK_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_scan_sequence_blocks(oracle_mod, shape):
+    """The sequence cut into blocks (carry pass, then each block from the
+    composed carries) against the oracle and against the one-block scan."""
+    b, L, D, N = shape
+    assert _blocks(b, L, D, N)
+    rng = np.random.default_rng(sum(shape))
+    inp = wl.m1_inputs(rng, b, L, D, N, h0_sd=0.5, A=-rng.uniform(0.01, 2.0, (D, N)))
+    dev, ref = prepare(inp, "f32")
+    y, h = run_scan(dev)
+    y1, h1 = run_scan(dev, seq_blocks=False)
+    yr, hr = oracle_mod.m1_scan(**ref)
+    assert_close(y, yr, "f32", "y")
+    assert_close(h, hr, "f32", "h")
+    assert torch.max(torch.abs(y - y1)).item() <= 1e-5 * torch.max(torch.abs(y1)).item()
+    assert torch.max(torch.abs(h - h1)).item() <= 1e-5 * torch.max(torch.abs(h1)).item()
+
+
+def test_scan_sequence_blocks_state_in_place(oracle_mod):
+    """h_out == h0 with sequence blocks: the carry pass keeps its own copy of h0."""
+    b, L, D, N = 1, 4000, 64, 16
+    assert _blocks(b, L, D, N)
+    rng = np.random.default_rng(21)
+    inp = wl.m1_inputs(rng, b, L, D, N, h0_sd=1.0, A=-rng.uniform(0.001, 0.05, (D, N)))
+    dev, ref = prepare(inp, "f32")
+    h = dev["h0"].clone()
+    y, h2 = mb.mb_selective_scan(dev["x"], dev["dt"], dev["A"], dev["B"], dev["C"], dev["D"], h, h_out=h)
+    yr, hr = oracle_mod.m1_scan(**ref)
+    assert h2.data_ptr() == h.data_ptr()
+    assert_close(y, yr, "f32", "y")
+    assert_close(h, hr, "f32", "h")
+
+
+@pytest.mark.slow
+def test_long_sequence_blocks_with_state(oracle_mod):
+    """One sequence of the block model's width (batch 1, L 16384, D 1536, N 16:
+    as many (t, c, n) elements as the block workload) runs in 32 sequence
+    blocks; with h0 != 0 and a weak decay the initial state reaches every block."""
+    assert _blocks(1, 16384, 1536, 16)
+    rng = np.random.default_rng(22)
+    inp = wl.m1_block(batch=1, L=16384)
+    inp["h0"] = rng.normal(0.0, 0.5, size=(1, 1536, 16))
+    inp["A"] = inp["A"] * 0.01
+    dev, ref = prepare(inp, "f32")
+    y, h = run_scan(dev)
+    torch.cuda.synchronize()
+    yr, hr = oracle_mod.m1_scan(**ref)
+    assert np.max(np.abs(yr[:, -1])) > 1e-2 * np.max(np.abs(yr))
+    assert_close(y, yr, "f32", "y")
+    assert_close(h, hr, "f32", "h")
+
+
 # ------------------------------------------------------------------- step ----
 STEP_SHAPES = [(1, 1, 1), (3, 7, 4), (5, 33, 8), (4, 70, 16), (2, 40, 32), (2, 20, 64),
                (3, 9, 5), (2, 11, 13), (7, 129, 16)]
