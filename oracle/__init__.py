@@ -379,6 +379,41 @@ def mimo(X, logdecay, B, C, beta, gamma, theta=None, h0=None, X_prev=None, B_pre
     return Y, h
 
 
+def mimo_block(X, logdecay, B, C, beta, gamma, theta=None, h0=None, X_prev=None, B_prev=None, normB_w=None,
+               normC_w=None, biasB=None, biasC=None, eps=1e-5, D=None, z=None):
+    """Mamba-3 MIMO with both ends of its block (mamba3-minimal README,
+    Architecture: B, C through the QK-style norm and the bias before the
+    rotations; y + D x, then gated by SiLU(z); TorchMamba README, API reference:
+    the MIMO block takes the SISO block's parameters plus the rank).  Reading:
+    every rank's row of B and C over the N states (and of the previous token's
+    B) goes through bc_norm_bias with the per-state weight and the head's bias,
+    the same for all ranks; then the MIMO scan; then per rank Y_r = (Y_r + D[h]
+    X_r) * SiLU(z_r), z like X.  B, C (b, L, H, N, R); B_prev (b, H, N, R) or
+    None; D (H,) or None.  Returns (Y, h_out)."""
+    X = _f64(X)
+    H, R = X.shape[2], X.shape[4]
+
+    def pro(Bv, w, bias):
+        # rows (head, rank) over the states: head-major, rank-minor
+        Bv = _f64(Bv)
+        lead, (Hh, N, Rr) = Bv.shape[:-3], Bv.shape[-3:]
+        rows = np.moveaxis(Bv, -1, -2).reshape(lead + (Hh * Rr, N))
+        bias_rows = None if bias is None else np.repeat(_f64(bias), Rr, axis=0)
+        v = bc_norm_bias(rows, Hh * Rr, w, bias_rows, eps)
+        return np.moveaxis(v.reshape(lead + (Hh, Rr, N)), -1, -2)
+
+    Bh = pro(B, normB_w, biasB)
+    Ch = pro(C, normC_w, biasC)
+    Bp = None if B_prev is None else pro(B_prev, normB_w, biasB)
+    Y, h = mimo(X, logdecay, Bh, Ch, beta, gamma, theta, h0, X_prev, Bp)
+    if D is not None:
+        Y = Y + _f64(D)[None, None, :, None, None] * X
+    if z is not None:
+        z = _f64(z)
+        Y = Y * (z / (1.0 + np.exp(-z)))
+    return Y, h
+
+
 def mimo_bwd(X, logdecay, B, C, beta, gamma, dY, theta=None, h0=None, dh_out=None, X_prev=None, B_prev=None):
     """Backward of the Mamba-3 MIMO recurrence: the gradients of sum dY . Y + sum
     dh_out . h_out with respect to X, logdecay, B, C, beta, gamma, theta, h0,

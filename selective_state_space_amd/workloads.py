@@ -20,6 +20,8 @@ expand 2 for Mamba-1, d_head 64 / d_state 128 for the SSD family):
               sequences on the block shapes, state ~ N(0, 0.1).
 * m1_fused    seed 110: the Mamba-1 block shapes with the block's prologue and
               epilogue inputs (conv1d width 4, dt bias, gate z).
+* mimo_block_full  seed 118: the MIMO block shape with the block's B / C norm
+              weights and biases, skip weight and gate.
 """
 from __future__ import annotations
 
@@ -218,6 +220,30 @@ def mimo_inputs(rng, batch, L, H, P, N, R, h0_sd=0.0, rotate=True):
 
 def mimo_block(seed=105, batch=2, L=8192, H=16, P=64, N=128, R=4):
     return mimo_inputs(np.random.default_rng(seed), batch, L, H, P, N, R)
+
+
+def mimo_block_inputs(rng, batch, L, H, P, N, R, h0_sd=0.0, rotate=True, prev=False):
+    """The MIMO inputs (mimo_inputs), then the block's parameters: B / C norm
+    weights ~ 1 + N(0, 0.3^2) (N,), biases ~ N(0, 0.5^2) (H, N), the skip weight
+    D ~ N(0,1) (H,), the gate z ~ N(0,1) like X, and with `prev` the previous
+    token's X (b, H, P, R) and raw B (b, H, N, R) at the scale of X and B."""
+    inp = mimo_inputs(rng, batch, L, H, P, N, R, h0_sd=h0_sd, rotate=rotate)
+    inp["normB_w"] = 1.0 + 0.3 * rng.standard_normal(N)
+    inp["normC_w"] = 1.0 + 0.3 * rng.standard_normal(N)
+    inp["biasB"] = 0.5 * rng.standard_normal((H, N))
+    inp["biasC"] = 0.5 * rng.standard_normal((H, N))
+    inp["D"] = rng.standard_normal(H)
+    inp["z"] = rng.standard_normal((batch, L, H, P, R))
+    if prev:
+        s = 1.0 / np.sqrt(N * R)
+        inp["X_prev"] = rng.standard_normal((batch, H, P, R)) * s
+        inp["B_prev"] = rng.standard_normal((batch, H, N, R)) * s
+    return inp
+
+
+def mimo_block_full(seed=118, batch=2, L=8192, H=16, P=64, N=128, R=4):
+    """The MIMO block shape with both ends of the block (mimo_block_inputs)."""
+    return mimo_block_inputs(np.random.default_rng(seed), batch, L, H, P, N, R)
 
 
 def ssd_step_inputs(rng, batch, H, P, G, N, R, kind, h_sd=0.1):
