@@ -518,6 +518,40 @@ class SISOBlock(SISO):
                                   biasC=t["biasC"], D=t["D"], z=t["z"], Y=self.Y, h_out=self.h, ws=self.ws)
 
 
+class MIMOBlock(Workload):
+    """Mamba-3 MIMO with both ends of its block fused into the scan: BCNorm +
+    bias on every rank row of B, C before the rotations, skip term and SiLU gate
+    per rank at the store; outside the step, measured beside it.  Bytes add z and
+    the parameters; flops are the scan's."""
+    name = "mimo_block"
+    kernel = "k_walk (state-only pass, prologue) + k_walk (full pass, both ends)"
+    source = "selective_state_space_amd/csrc/ssd.hip"
+    bound = "mfma"
+
+    def __init__(self, mb, wl, torch):
+        self.mb = mb
+        b, L, H, P, N, R = 2, 8192, 16, 64, 128, 4
+        self.shape = dict(batch=b, L=L, H=H, P=P, N=N, R=R)
+        inp = wl.mimo_block_full()
+        self.inp = inp
+        f = torch.float32
+        self.t = {k: _dev(v, f) for k, v in inp.items() if v is not None}
+        self.Y = torch.empty_like(self.t["X"])
+        self.h = torch.empty((b, H, N, P), dtype=f, device="cuda")
+        self.ws = torch.empty(mb.mb_workspace_size(mb.MB_OP_MIMO_SSD, b, L, H, P, 1, N, R, 0),
+                              dtype=torch.uint8, device="cuda")
+        self.tokens = b * L
+        nbytes, self.flops = mimo_work(b, L, H, P, N, R)
+        self.bytes = nbytes + 4 * (b * L * H * P * R + H + 2 * N + 2 * H * N)
+        self.exps = None
+
+    def run(self):
+        t = self.t
+        self.mb.mb_mimo_ssd_block(t["X"], t["logdecay"], t["B"], t["C"], t["beta"], t["gamma"], t["theta"], None,
+                                  normB_w=t["normB_w"], normC_w=t["normC_w"], biasB=t["biasB"], biasC=t["biasC"],
+                                  D=t["D"], z=t["z"], Y=self.Y, h_out=self.h, ws=self.ws)
+
+
 class M2Prologue(Workload):
     """The Mamba-2 block prologue in one pass (conv1d + SiLU over the x, B, C
     channels, softplus of dt, split into the SSD's inputs) at the Mamba-2 block
@@ -615,7 +649,7 @@ ALL = ["m1_scan", "m1_step", "ssd_f32", "ssd_bf16", "siso", "mimo"]
 # Mamba-1 scan with the block prologue and epilogue fused, the Mamba-2 block prologue, Mamba-3 SISO with its output
 # epilogue and with both ends of its block fused, and the backwards of the
 # Mamba-2 SSD, the Mamba-1 scan, Mamba-3 SISO and MIMO
-NEXT = ["m2_decode", "siso_decode", "mimo_decode", "m1_long", "m1_long_one_block", "m1_fused", "m2_prologue", "siso_gated", "siso_block", "ssd_bwd", "m1_bwd", "siso_bwd", "mimo_bwd"]
+NEXT = ["m2_decode", "siso_decode", "mimo_decode", "m1_long", "m1_long_one_block", "m1_fused", "m2_prologue", "siso_gated", "siso_block", "mimo_block", "ssd_bwd", "m1_bwd", "siso_bwd", "mimo_bwd"]
 
 
 def make(name, mb, wl, torch):
@@ -633,6 +667,8 @@ def make(name, mb, wl, torch):
         return M2Prologue(mb, wl, torch)
     if name == "siso_block":
         return SISOBlock(mb, wl, torch)
+    if name == "mimo_block":
+        return MIMOBlock(mb, wl, torch)
     if name == "siso_gated":
         return SISOGated(mb, wl, torch)
     if name == "ssd_bwd":

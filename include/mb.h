@@ -329,6 +329,33 @@ mb_status mb_mimo_ssd(const void* X, const float* logdecay, const void* B,
                       hipStream_t stream);
 
 /*
+ * The Mamba-3 MIMO layer with both ends of its block fused into the scan
+ * (mamba3-minimal README, Architecture: QK-style norm, bias, rotations on B
+ * and C; y + D x gated by SiLU(z); TorchMamba README, API reference: the MIMO
+ * block takes the SISO block's parameters and the rank).  Every rank's raw row
+ * of B and of C (one step, one head, one rank, N states) becomes
+ *     B^_{t,r}[h][n] = B_{t,r}[h][n] / sqrt(mean_n' B_{t,r}[h][n']^2 + eps) * normB_w[n] + biasB[h][n]
+ * (C likewise), the bias the same for every rank; the scan runs on B^, C^ as
+ * mb_mimo_ssd; then per rank
+ *     Y_{t,r} = (S_t^T C~_{t,r} + Dskip[h] X_{t,r}) * SiLU(z_{t,r}),  SiLU(v) = v / (1 + e^-v).
+ * B_prev (with X_prev) is the previous token's raw rows and passes the prologue.
+ *   z                : (batch, L, H, P, R) dtype, or NULL (no gate), 16-byte aligned
+ *   Dskip            : (H) fp32 or NULL (no skip term)
+ *   normB_w, normC_w, biasB, biasC, eps : as mb_trap_ssd_block
+ * Supported: R in {1, 4} (MB_ERR_SHAPE otherwise); other arguments, limits,
+ * state and workspace as mb_mimo_ssd.
+ */
+mb_status mb_mimo_ssd_block(const void* X, const float* logdecay, const void* B,
+                            const void* C, const float* beta, const float* gamma,
+                            const float* theta, const float* h0, const void* X_prev,
+                            const void* B_prev, const float* normB_w, const float* normC_w,
+                            const float* biasB, const float* biasC, float eps,
+                            const float* Dskip, const void* z, void* Y, float* h_out,
+                            int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N, int64_t R,
+                            int64_t chunk, mb_dtype dtype, void* ws, size_t ws_bytes,
+                            hipStream_t stream);
+
+/*
  * Decode step of the SSD family: one token per sequence, state in the physical
  * (unrotated) frame (TorchMamba README, Math notes M3 SISO and MIMO: plane
  * rotations compose additively, so the rotated-frame recurrence needs only the

@@ -16,7 +16,7 @@ import threading
 
 __all__ = [
     "mb_selective_scan", "mb_ssm_step", "mb_ssd_chunked", "mb_trap_ssd", "mb_mimo_ssd",
-    "mb_ssd_step", "mb_selective_scan_fused", "mb_ssd_chunked_bwd", "mb_selective_scan_bwd", "mb_trap_ssd_bwd", "mb_mimo_ssd_bwd", "mb_trap_ssd_gated", "mb_trap_ssd_block", "mb_ssd_prologue", "mb_ssd_chunked_noalloc", "mb_workspace_size", "mb_status_str", "lib_path", "load_library", "MBError",
+    "mb_ssd_step", "mb_selective_scan_fused", "mb_ssd_chunked_bwd", "mb_selective_scan_bwd", "mb_trap_ssd_bwd", "mb_mimo_ssd_bwd", "mb_trap_ssd_gated", "mb_trap_ssd_block", "mb_ssd_prologue", "mb_mimo_ssd_block", "mb_ssd_chunked_noalloc", "mb_workspace_size", "mb_status_str", "lib_path", "load_library", "MBError",
     "MB_OP_SELECTIVE_SCAN", "MB_OP_SSM_STEP", "MB_OP_SSD_CHUNKED", "MB_OP_TRAP_SSD",
     "MB_OP_MIMO_SSD", "MB_OP_SSD_CHUNKED_BWD", "MB_OP_SELECTIVE_SCAN_BWD", "MB_OP_TRAP_SSD_BWD",
     "MB_OP_MIMO_SSD_BWD",
@@ -83,6 +83,10 @@ def load_library():
             lib.mb_trap_ssd_block.argtypes = [_vp] * 14 + [ctypes.c_float] + [_vp] * 4 + [_i64] * 7 + \
                 [ctypes.c_int, _vp, ctypes.c_size_t, _vp]
             lib.mb_trap_ssd_block.restype = ctypes.c_int
+        if hasattr(lib, "mb_mimo_ssd_block"):
+            lib.mb_mimo_ssd_block.argtypes = [_vp] * 14 + [ctypes.c_float] + [_vp] * 4 + [_i64] * 7 + \
+                [ctypes.c_int, _vp, ctypes.c_size_t, _vp]
+            lib.mb_mimo_ssd_block.restype = ctypes.c_int
         if hasattr(lib, "mb_mimo_ssd_bwd"):
             lib.mb_mimo_ssd_bwd.argtypes = [_vp] * 22 + [_i64] * 6 + [ctypes.c_int, _vp, ctypes.c_size_t, _vp]
             lib.mb_mimo_ssd_bwd.restype = ctypes.c_int
@@ -515,6 +519,47 @@ def mb_trap_ssd_block(X, logdecay, B, C, beta, gamma, theta=None, h0=None, *, no
     _call("mb_trap_ssd_block", _ptr(X), _ptr(logdecay), _ptr(B), _ptr(C), _ptr(beta), _ptr(gamma),
           _ptr(theta), _ptr(h0), _ptr(X_prev), _ptr(B_prev), _ptr(normB_w), _ptr(normC_w), _ptr(biasB),
           _ptr(biasC), float(eps), _ptr(D), _ptr(z), _ptr(Y), _ptr(h_out), b, L, H, P, G, N, chunk, code,
+          _ptr(ws), nws, _stream(dev))
+    return Y, h_out
+
+
+def mb_mimo_ssd_block(X, logdecay, B, C, beta, gamma, theta=None, h0=None, *, normB_w=None, normC_w=None,
+                      biasB=None, biasC=None, eps=1e-5, D=None, z=None, X_prev=None, B_prev=None, chunk=0,
+                      Y=None, h_out=None, ws=None):
+    """Mamba-3 MIMO with the block's BCNorm + bias prologue on every rank row of
+    B, C and the skip term and SiLU(z) gate per rank fused into the scan.  X, z
+    (batch, L, H, P, R), B, C (batch, L, H, N, R) in one dtype; normB_w, normC_w
+    (N,), biasB, biasC (H, N), D (H,) float32 or None; the rest as mb_mimo_ssd.
+    R in {1, 4}.  Returns (Y, h_out)."""
+    torch = _torch()
+    dev = _device_of(X)
+    dtype = X.dtype
+    code = _dtype_code(X, "X")
+    b, L, H, P, R = X.shape
+    N = B.shape[3]
+    f32 = torch.float32
+    for t, n in ((logdecay, "logdecay"), (beta, "beta"), (gamma, "gamma")):
+        _check(t, n, (b, L, H), f32, dev)
+    _check(B, "B", (b, L, H, N, R), dtype, dev)
+    _check(C, "C", (b, L, H, N, R), dtype, dev)
+    _check(theta, "theta", (b, L, H, N // 2), f32, dev)
+    _check(h0, "h0", (b, H, N, P), f32, dev)
+    _check(X_prev, "X_prev", (b, H, P, R), dtype, dev)
+    _check(B_prev, "B_prev", (b, H, N, R), dtype, dev)
+    _check(normB_w, "normB_w", (N,), f32, dev)
+    _check(normC_w, "normC_w", (N,), f32, dev)
+    _check(biasB, "biasB", (H, N), f32, dev)
+    _check(biasC, "biasC", (H, N), f32, dev)
+    _check(D, "D", (H,), f32, dev)
+    _check(z, "z", (b, L, H, P, R), dtype, dev)
+    Y = torch.empty((b, L, H, P, R), dtype=dtype, device=dev) if Y is None else \
+        _check(Y, "Y", (b, L, H, P, R), dtype, dev)
+    h_out = torch.empty((b, H, N, P), dtype=f32, device=dev) if h_out is None else \
+        _check(h_out, "h_out", (b, H, N, P), f32, dev)
+    ws, nws = _workspace(MB_OP_MIMO_SSD, dev, ws, (b, L, H, P, 1, N, R, chunk))
+    _call("mb_mimo_ssd_block", _ptr(X), _ptr(logdecay), _ptr(B), _ptr(C), _ptr(beta), _ptr(gamma),
+          _ptr(theta), _ptr(h0), _ptr(X_prev), _ptr(B_prev), _ptr(normB_w), _ptr(normC_w), _ptr(biasB),
+          _ptr(biasC), float(eps), _ptr(D), _ptr(z), _ptr(Y), _ptr(h_out), b, L, H, P, N, R, chunk, code,
           _ptr(ws), nws, _stream(dev))
     return Y, h_out
 

@@ -426,8 +426,9 @@ __constant__ int kTrapTiles[8][2] = {{0x33, 0x00}, {0x32, 0x11}, {0x22, -1}, {0x
 template <int NP, int R, bool TRAP, bool ROT, bool GROUPED, typename IO, bool SO, bool EPI = false,
           bool BCN = false>
 __global__ __launch_bounds__(kWalkThreads, SO ? 4 : 2) void k_walk(Args a) {
-    static_assert(!EPI || (R == 1 && TRAP && !SO), "the output epilogue is a SISO full-pass feature");
-    static_assert(!BCN || (R == 1 && TRAP), "the B / C prologue is a SISO feature");
+    static_assert(!EPI || (TRAP && !SO && (R == 1 || R >= 4)),
+                  "the output epilogue is a Mamba-3 full-pass feature (one rank, or rank rows)");
+    static_assert(!BCN || TRAP, "the B / C prologue is a Mamba-3 feature");
     using Gm = Geo<R, TRAP>;
     constexpr int QT = Gm::QT, EXTRA = Gm::EXTRA, JX = Gm::JX;
     constexpr int JC = Gm::JC, JP = Gm::JP;
@@ -790,9 +791,10 @@ __global__ __launch_bounds__(kWalkThreads, SO ? 4 : 2) void k_walk(Args a) {
         }
     }
 
-    // BCNorm + bias on the raw rows, before the rotations: a row (one step) lies
-    // on lanes sk of its step group's wave, pair sk on lane sk; lanes past N add
-    // zero to the sum of squares, and staging zeroes what they hold
+    // BCNorm + bias on the raw rows, before the rotations: a row (one step and
+    // rank) lies on lanes sk of its step group's wave, pair sk on lane sk; lanes
+    // past N add zero to the sum of squares, and staging zeroes what they hold.
+    // Every rank of a step is its own row; the head's bias is the same for all.
     auto bc_prologue = [&](Pre& p) {
         if constexpr (BCN) if (ssg < NSG) {   // wave-uniform
             const float rN = 1.0f / (float)a.N;
@@ -803,11 +805,17 @@ __global__ __launch_bounds__(kWalkThreads, SO ? 4 : 2) void k_walk(Args a) {
                 v1 = fmaf(v1 * inv, w[1], bi[1]);
             };
 #pragma unroll
-            for (int i = 0; i < QSG; ++i) {
-                norm(p.b[i][0], p.b[i][1], nwb, nbb);
-                if constexpr (FULL) norm(p.c[i][0], p.c[i][1], nwc, nbc);
+            for (int i = 0; i < QSG; ++i)
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    norm(p.b[i][r], p.b[i][R + r], nwb, nbb);
+                    if constexpr (FULL) norm(p.c[i][r], p.c[i][R + r], nwc, nbc);
+                }
+            if (ssg * PRG < R) {
+#pragma unroll
+                for (int q = 0; q < PRG; ++q)
+                    if (ssg * PRG + q < R) norm(p.bp[q], p.bp[PRG + q], nwb, nbb);   // wave-uniform
             }
-            if (ssg * PRG < R) norm(p.bp[0], p.bp[PRG], nwb, nbb);
         }
     };
 
@@ -855,22 +863,38 @@ __global__ __launch_bounds__(kWalkThreads, SO ? 4 : 2) void k_walk(Args a) {
 
         if constexpr (FULL) {
             floatx4 acc_y[4];
-            // SISO output epilogue: X and z of this lane's outputs load now, under the
-            // chunk's matrix work, rather than in front of the store
+            // output epilogue: X and z of this lane's outputs load now, under the
+            // chunk's matrix work, rather than in front of the store (one rank: four
+            // columns of a step; rank rows: four ranks of a step and column)
             float ex[4][4] = {}, ez[4][4] = {};
             if constexpr (EPI) {
                 if (active && nh == 0) {
 #pragma unroll
                     for (int it = 0; it < 4; ++it) {
-                        const int tg = t0g + 16 * it + li;
+                        const int i0 = YROW ? 16 * it + 4 * lk : 16 * it + li;
+                        const int tg = t0g + i0 / R;
                         if (tg < a.L) {
-                            const size_t e = (((size_t)b * a.L + tg) * a.H + h) * (size_t)a.P + p0 + 16 * pw + 4 * lk;
+                            const size_t e = YROW
+                                ? (((size_t)b * a.L + tg) * a.H + h) * (size_t)a.P * R + (size_t)(p0 + 16 * pw + li) * R + i0 % R
+                                : (((size_t)b * a.L + tg) * a.H + h) * (size_t)a.P + p0 + 16 * pw + 4 * lk;
                             if (a.Dh) load4<IO>(a.X, e, ex[it]);
                             if (a.Zg) load4<IO>(a.Zg, e, ez[it]);
                         }
                     }
                 }
             }
+            // (y + Dh x) SiLU(z) of the four outputs of tile it
+            auto epilogue = [&](float* yv, int it) __attribute__((always_inline)) {
+                if constexpr (EPI) {
+                    const float dh = a.Dh ? a.Dh[h] : 0.0f;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const float v = fmaf(dh, ex[it][r], yv[r]);
+                        const float sg = ez[it][r] * __builtin_amdgcn_rcpf(1.0f + exp2_fast(-ez[it][r] * kLog2e));
+                        yv[r] = a.Zg ? v * sg : v;
+                    }
+                }
+            };
             // The two waves of a SIMD (same column group, other state half) take the
             // score tiles and the state part in opposite orders, so that one
             // wave's vector work on the score weights meets the other's matrix
@@ -1007,11 +1031,13 @@ __global__ __launch_bounds__(kWalkThreads, SO ? 4 : 2) void k_walk(Args a) {
                         if (tg < a.L) {
                             IO* yrow = (IO*)a.Y + (((size_t)b * a.L + tg) * a.H + h) * (size_t)a.P * R;
                             const size_t e = (size_t)(p0 + 16 * pw + li) * R + rk;
+                            float yv[4] = {y[0], y[1], y[2], y[3]};
+                            epilogue(yv, it);
                             if constexpr (sizeof(IO) == 4) {
-                                *(float4*)((float*)yrow + e) = make_float4(y[0], y[1], y[2], y[3]);
+                                *(float4*)((float*)yrow + e) = make_float4(yv[0], yv[1], yv[2], yv[3]);
                             } else {
-                                const uint32_t u0 = f32_to_bf16(y[0]) | ((uint32_t)f32_to_bf16(y[1]) << 16);
-                                const uint32_t u1 = f32_to_bf16(y[2]) | ((uint32_t)f32_to_bf16(y[3]) << 16);
+                                const uint32_t u0 = f32_to_bf16(yv[0]) | ((uint32_t)f32_to_bf16(yv[1]) << 16);
+                                const uint32_t u1 = f32_to_bf16(yv[2]) | ((uint32_t)f32_to_bf16(yv[3]) << 16);
                                 *(uint2*)((bf16*)yrow + e) = make_uint2(u0, u1);
                             }
                         }
@@ -1025,16 +1051,7 @@ __global__ __launch_bounds__(kWalkThreads, SO ? 4 : 2) void k_walk(Args a) {
                         IO* yrow = (IO*)a.Y + (((size_t)b * a.L + tg) * a.H + h) * (size_t)a.P * R;
                         if (R == 1) {
                             float yv[4] = {y[0], y[1], y[2], y[3]};
-                            if constexpr (EPI) {
-                                // gated output: (y + Dh x) SiLU(z) of the same elements
-                                const float dh = a.Dh ? a.Dh[h] : 0.0f;
-#pragma unroll
-                                for (int r = 0; r < 4; ++r) {
-                                    const float v = fmaf(dh, ex[it][r], yv[r]);
-                                    const float sg = ez[it][r] * __builtin_amdgcn_rcpf(1.0f + exp2_fast(-ez[it][r] * kLog2e));
-                                    yv[r] = a.Zg ? v * sg : v;
-                                }
-                            }
+                            epilogue(yv, it);   // gated output of the same elements
                             if constexpr (sizeof(IO) == 4) {
                                 *(float4*)((float*)yrow + pp) = make_float4(yv[0], yv[1], yv[2], yv[3]);
                             } else {
@@ -1940,7 +1957,7 @@ mb_status launch(Args a, int64_t batch, const Plan& pl, char* ws, hipStream_t st
     }
     if (a.nseg > 1) {
         const dim3 g((unsigned)(per_seg * (a.nseg - 1)));
-        if constexpr (R == 1 && TRAP) {
+        if constexpr ((R == 1 || (R == 4 && !GROUPED)) && TRAP) {
             if (a.bcn)
                 hipLaunchKernelGGL((k_walk<NP, R, TRAP, ROT, GROUPED, IO, true, false, true>), g,
                                    dim3(kWalkThreads), 0, stream, a);
@@ -1972,6 +1989,19 @@ mb_status launch(Args a, int64_t batch, const Plan& pl, char* ws, hipStream_t st
         else
             hipLaunchKernelGGL((k_walk<NP, R, TRAP, ROT, GROUPED, IO, false>),
                                dim3((unsigned)(per_seg * a.nseg)), dim3(kWalkThreads), 0, stream, a);
+    } else if constexpr (R == 4 && TRAP && !GROUPED) {
+        // MIMO rank 4 with both ends of its block (the prologue always, the
+        // epilogue when D or z is given)
+        const dim3 g((unsigned)(per_seg * a.nseg));
+        const bool epi = a.Dh || a.Zg;
+        if (a.bcn && epi)
+            hipLaunchKernelGGL((k_walk<NP, R, TRAP, ROT, GROUPED, IO, false, true, true>), g, dim3(kWalkThreads),
+                               0, stream, a);
+        else if (a.bcn)
+            hipLaunchKernelGGL((k_walk<NP, R, TRAP, ROT, GROUPED, IO, false, false, true>), g, dim3(kWalkThreads),
+                               0, stream, a);
+        else
+            hipLaunchKernelGGL((k_walk<NP, R, TRAP, ROT, GROUPED, IO, false>), g, dim3(kWalkThreads), 0, stream, a);
     } else
         hipLaunchKernelGGL((k_walk<NP, R, TRAP, ROT, GROUPED, IO, false>),
                            dim3((unsigned)(per_seg * a.nseg)), dim3(kWalkThreads), 0, stream, a);
@@ -2239,6 +2269,43 @@ extern "C" mb_status mb_trap_ssd_block(const void* X, const float* logdecay, con
            nullptr, nullptr, nullptr, (int)L, (int)H, (int)P, (int)G, (int)N, 0, 0, 0, 0, Dskip, z,
            normB_w, normC_w, biasB, biasC, eps, 1};
     return dispatch<1, true, true>(a, batch, pl, (char*)ws, dtype, stream);
+}
+
+extern "C" mb_status mb_mimo_ssd_block(const void* X, const float* logdecay, const void* B,
+                                       const void* C, const float* beta, const float* gamma,
+                                       const float* theta, const float* h0, const void* X_prev,
+                                       const void* B_prev, const float* normB_w, const float* normC_w,
+                                       const float* biasB, const float* biasC, float eps,
+                                       const float* Dskip, const void* z, void* Y, float* h_out,
+                                       int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N,
+                                       int64_t R, int64_t chunk, mb_dtype dtype, void* ws,
+                                       size_t ws_bytes, hipStream_t stream) {
+    if (R != 1 && R != 4) return MB_ERR_SHAPE;
+    if (!(eps > 0.0f) || !(eps < 3.0e38f)) return MB_ERR_SHAPE;
+    mb_status st = ssd_common_checks(X, logdecay, B, C, h0, Y, h_out, beta, gamma, theta, X_prev,
+                                     B_prev, batch, L, H, P, H, N, R, dtype, chunk, true);
+    if (st != MB_OK) return st;
+    const float* pars[5] = {normB_w, normC_w, biasB, biasC, Dskip};
+    const size_t pbytes[5] = {(size_t)N * 4, (size_t)N * 4, (size_t)(H * N) * 4, (size_t)(H * N) * 4,
+                              (size_t)H * 4};
+    if ((uintptr_t)z & 15) return MB_ERR_ALIGN;
+    const size_t ny = (size_t)(batch * L * H * P * R) * dtype_size(dtype);
+    const size_t nh = (size_t)(batch * H * N * P) * 4;
+    if (overlaps(Y, ny, z, z ? ny : 0) || (h_out && overlaps(h_out, nh, z, z ? ny : 0))) return MB_ERR_ALIAS;
+    for (int k = 0; k < 5; ++k) {
+        if ((uintptr_t)pars[k] & 3) return MB_ERR_ALIGN;
+        const size_t nb = pars[k] ? pbytes[k] : 0;
+        if (overlaps(Y, ny, pars[k], nb) || (h_out && overlaps(h_out, nh, pars[k], nb))) return MB_ERR_ALIAS;
+    }
+    if (batch == 0) return MB_OK;
+    if (L == 0) return copy_state(h0, h_out, batch * H * N * P, stream);
+    const Plan pl = plan_for(MB_OP_MIMO_SSD, batch, L, H, P, 1, N, R);
+    if ((st = check_ws(ws, ws_bytes, pl.bytes)) != MB_OK) return st;
+    Args a{X, logdecay, B, C, beta, gamma, theta, h0, X_prev, B_prev, Y, h_out, nullptr, nullptr,
+           nullptr, nullptr, nullptr, (int)L, (int)H, (int)P, (int)H, (int)N, 0, 0, 0, 0, Dskip, z,
+           normB_w, normC_w, biasB, biasC, eps, 1};
+    if (R == 1) return dispatch<1, true, false>(a, batch, pl, (char*)ws, dtype, stream);
+    return dispatch<4, true, false>(a, batch, pl, (char*)ws, dtype, stream);
 }
 
 extern "C" mb_status mb_mimo_ssd(const void* X, const float* logdecay, const void* B,
