@@ -791,13 +791,14 @@ _FLUSH = {}
 
 
 def flush(torch):
-    """Overwrite a 512 MiB buffer: evicts the 256 MB last-level cache, so the
-    next call reads every input from HBM."""
+    """Read a 512 MiB buffer (a sum over it): evicts the 256 MB last-level cache,
+    so the next call reads every input from HBM.  A read rather than a write:
+    overwriting the buffer leaves dirty lines whose write-back then competes
+    with the measured call (the Mamba-1 decode step measured 0.5-0.8 us slower
+    after a fill than after a read)."""
     if "buf" not in _FLUSH:
-        _FLUSH["buf"] = torch.empty(128 << 20, dtype=torch.float32, device="cuda")
-        _FLUSH["n"] = 0
-    _FLUSH["n"] += 1
-    _FLUSH["buf"].fill_(float(_FLUSH["n"]))
+        _FLUSH["buf"] = torch.ones(128 << 20, dtype=torch.float32, device="cuda")
+    _FLUSH["sum"] = _FLUSH["buf"].sum()
 
 
 def time_flushed(torch, w, reps):
@@ -877,9 +878,10 @@ def _short(name):
 def summarize(paths):
     """Markdown tables from rocprofv3 csv output directories of bench.py runs.
 
-    Kernel trace: every dispatch before the first 512 MiB fill (the cache
-    flush) is in the warm phase (warm-up and back-to-back calls); every dispatch
-    after it is in the flushed phase (each workload call follows a flush).
+    Kernel trace: every dispatch before the first cache flush (a reduction over
+    the 512 MiB flush buffer) is in the warm phase (warm-up and back-to-back
+    calls); every dispatch after it is in the flushed phase (each workload call
+    follows a flush).  The flush kernels and torch's fills are left out.
     Counter collection: the mean per dispatch of each counter, with the MFMA
     busy fraction (SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE / 8 XCDs x
     1024 SIMDs), the VALU busy fraction of a wave's life (SQ_ACTIVE_INST_VALU /
@@ -895,8 +897,10 @@ def summarize(paths):
             phase, stats = "warm", {}
             for r in rows:
                 name = _short(r["Kernel_Name"])
-                if "FillFunctor" in name:
+                if "reduce_kernel" in name:
                     phase = "flushed"
+                    continue
+                if "FillFunctor" in name:
                     continue
                 us = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
                 stats.setdefault((name, phase), []).append(us)
@@ -915,7 +919,7 @@ def summarize(paths):
             files.append(os.path.basename(f))
             for r in csv.DictReader(open(f)):
                 name = _short(r["Kernel_Name"])
-                if "FillFunctor" in name or "copyBuffer" in name:
+                if "FillFunctor" in name or "copyBuffer" in name or "reduce_kernel" in name:
                     continue
                 acc.setdefault(name, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
     if acc:
