@@ -248,6 +248,22 @@ def trap(X, logdecay, B, C, beta, gamma, theta=None, h0=None, X_prev=None, B_pre
     return Y, h
 
 
+def ssd_gated(X, logdecay, B, C, h0=None, D=None, z=None):
+    """The Mamba-2 SSD followed by the block's output side (TorchMamba README, API
+    reference Mamba2Block, psi = SiLU; the same skip-and-gate epilogue as the
+    Mamba-3 block's, mamba3-minimal README, Architecture): Y = (ssd output + D[h]
+    X) * SiLU(z), SiLU(v) = v / (1 + e^-v), x the scan's own input X.  D (H,) or
+    None; z like X or None.  Returns (Y, h_out)."""
+    Y, h = ssd(X, logdecay, B, C, h0)
+    X = _f64(X)
+    if D is not None:
+        Y = Y + _f64(D)[None, None, :, None] * X
+    if z is not None:
+        z = _f64(z)
+        Y = Y * (z / (1.0 + np.exp(-z)))
+    return Y, h
+
+
 def trap_gated(X, logdecay, B, C, beta, gamma, theta=None, h0=None, X_prev=None, B_prev=None, D=None, z=None):
     """Mamba-3 SISO followed by the block's output epilogue (mamba3-minimal
     README, Architecture): Y = (trap output + D[h] X) * SiLU(z), SiLU(v) =

@@ -130,3 +130,26 @@ def test_step_unrolled(oracle_mod):
         Yt, S = forms.ssd_step(inp["X"][:, t], inp["logdecay"][:, t], inp["B"][:, t], inp["C"][:, t], S)
         close(Yt, Y[:, t])
     close(S, h)
+
+
+def test_gated_output_side(oracle_mod):
+    """The Mamba-2 output side: z = 0 closes the gate with the state unchanged;
+    without z the skip term adds D[h] X; the gate matches scipy's logistic
+    sigmoid times z; and the whole equals the SISO epilogue on the trapezoid
+    with beta = 0, gamma = 1 and no rotation (the Mamba-2 reduction)."""
+    from scipy.special import expit
+    rng = np.random.default_rng(71)
+    inp = wl.ssd_inputs(rng, 2, 37, 3, 4, 6, G=1, h0_sd=0.2)
+    Y, h = oracle_mod.ssd(**inp)
+    D = rng.standard_normal(3)
+    z = rng.standard_normal(inp["X"].shape)
+    Yz, hz = oracle_mod.ssd_gated(**inp, D=D, z=np.zeros_like(z))
+    assert np.all(Yz == 0.0) and np.array_equal(hz, h)
+    Yd, _ = oracle_mod.ssd_gated(**inp, D=D)
+    assert np.allclose(Yd - Y, D[None, None, :, None] * inp["X"], rtol=1e-13, atol=1e-15)
+    Yg, hg = oracle_mod.ssd_gated(**inp, D=D, z=z)
+    assert np.allclose(Yg, (Y + D[None, None, :, None] * inp["X"]) * z * expit(z), rtol=1e-12, atol=1e-15)
+    ones = np.ones_like(inp["logdecay"])
+    Yt, ht = oracle_mod.trap_gated(inp["X"], inp["logdecay"], inp["B"], inp["C"], 0.0 * ones, ones, None,
+                                   inp["h0"], D=D, z=z)
+    assert np.allclose(Yg, Yt, rtol=1e-11, atol=1e-13) and np.allclose(hg, ht, rtol=1e-11, atol=1e-13)
