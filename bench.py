@@ -326,6 +326,27 @@ class SSD(Workload):
         self.mb.mb_ssd_chunked(self.X, self.ld, self.B, self.C, None, Y=self.Y, h_out=self.h, ws=self.ws)
 
 
+class SSDGated(SSD):
+    """The Mamba-2 SSD with the block's output side (skip term D[h] X and SiLU(z)
+    gate) fused into the store; outside the step, measured beside it.  Bytes add
+    z and D; flops are the scan's."""
+
+    def __init__(self, mb, wl, torch, dtype):
+        super().__init__(mb, wl, torch, dtype)
+        self.name = "ssd_gated_" + dtype
+        rng = np.random.default_rng(119)
+        act = torch.bfloat16 if dtype == "bf16" else torch.float32
+        self.D = _dev(rng.standard_normal(self.shape["H"]), torch.float32)
+        self.z = _dev(rng.standard_normal(tuple(self.X.shape)), act)
+        b, L, H, P = self.X.shape
+        self.bytes += (2 if dtype == "bf16" else 4) * b * L * H * P + 4 * H
+        self.kernel = self.kernel.replace("(full pass)", "(full pass, output side)")
+
+    def run(self):
+        self.mb.mb_ssd_chunked_gated(self.X, self.ld, self.B, self.C, None, D=self.D, z=self.z, Y=self.Y,
+                                     h_out=self.h, ws=self.ws)
+
+
 class M1Bwd(Workload):
     """Backward of the Mamba-1 scan at the block shape (outside the step,
     measured beside it)."""
@@ -649,7 +670,7 @@ ALL = ["m1_scan", "m1_step", "ssd_f32", "ssd_bf16", "siso", "mimo"]
 # Mamba-1 scan with the block prologue and epilogue fused, the Mamba-2 block prologue, Mamba-3 SISO with its output
 # epilogue and with both ends of its block fused, and the backwards of the
 # Mamba-2 SSD, the Mamba-1 scan, Mamba-3 SISO and MIMO
-NEXT = ["m2_decode", "siso_decode", "mimo_decode", "m1_long", "m1_long_one_block", "m1_fused", "m2_prologue", "siso_gated", "siso_block", "mimo_block", "ssd_bwd", "m1_bwd", "siso_bwd", "mimo_bwd"]
+NEXT = ["m2_decode", "siso_decode", "mimo_decode", "m1_long", "m1_long_one_block", "m1_fused", "m2_prologue", "ssd_gated_f32", "ssd_gated_bf16", "siso_gated", "siso_block", "mimo_block", "ssd_bwd", "m1_bwd", "siso_bwd", "mimo_bwd"]
 
 
 def make(name, mb, wl, torch):
@@ -667,6 +688,8 @@ def make(name, mb, wl, torch):
         return M2Prologue(mb, wl, torch)
     if name == "siso_block":
         return SISOBlock(mb, wl, torch)
+    if name.startswith("ssd_gated_"):
+        return SSDGated(mb, wl, torch, name[len("ssd_gated_"):])
     if name == "mimo_block":
         return MIMOBlock(mb, wl, torch)
     if name == "siso_gated":

@@ -177,6 +177,23 @@ mb_status mb_ssd_chunked(const void* X, const float* logdecay, const void* B,
                          void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * mb_ssd_chunked with the output side of the Mamba-2 block fused into its store
+ * (TorchMamba README, API reference: Mamba2Block with psi = SiLU; the skip and
+ * gate as in the Mamba-3 block, mamba3-minimal README, Architecture):
+ *     Y_t = (S_t^T C_t + Dskip[h] X_t) * SiLU(z_t),   SiLU(v) = v / (1 + e^-v)
+ * with X the scan's own input.  Dskip (H) fp32 or NULL (no skip term); z like X
+ * (same dtype, 16-byte aligned) or NULL (no gate); with both NULL the result is
+ * mb_ssd_chunked's.  Neither may overlap Y or h_out (MB_ERR_ALIAS); Dskip
+ * 4-byte aligned.  Other arguments, limits, state and workspace as
+ * mb_ssd_chunked.
+ */
+mb_status mb_ssd_chunked_gated(const void* X, const float* logdecay, const void* B,
+                               const void* C, const float* h0, const float* Dskip, const void* z,
+                               void* Y, float* h_out, int64_t batch, int64_t L, int64_t H,
+                               int64_t P, int64_t G, int64_t N, int64_t chunk, mb_dtype dtype,
+                               void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
  * mb_ssd_chunked for callers that cannot allocate device memory (code under
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
  * the same computation, arguments and limits, without ws / ws_bytes.  The

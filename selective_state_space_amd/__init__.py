@@ -16,7 +16,7 @@ import threading
 
 __all__ = [
     "mb_selective_scan", "mb_ssm_step", "mb_ssd_chunked", "mb_trap_ssd", "mb_mimo_ssd",
-    "mb_ssd_step", "mb_selective_scan_fused", "mb_ssd_chunked_bwd", "mb_selective_scan_bwd", "mb_trap_ssd_bwd", "mb_mimo_ssd_bwd", "mb_trap_ssd_gated", "mb_trap_ssd_block", "mb_ssd_prologue", "mb_mimo_ssd_block", "mb_ssd_chunked_noalloc", "mb_workspace_size", "mb_status_str", "lib_path", "load_library", "MBError",
+    "mb_ssd_step", "mb_selective_scan_fused", "mb_ssd_chunked_bwd", "mb_selective_scan_bwd", "mb_trap_ssd_bwd", "mb_mimo_ssd_bwd", "mb_trap_ssd_gated", "mb_trap_ssd_block", "mb_ssd_prologue", "mb_mimo_ssd_block", "mb_ssd_chunked_gated", "mb_ssd_chunked_noalloc", "mb_workspace_size", "mb_status_str", "lib_path", "load_library", "MBError",
     "MB_OP_SELECTIVE_SCAN", "MB_OP_SSM_STEP", "MB_OP_SSD_CHUNKED", "MB_OP_TRAP_SSD",
     "MB_OP_MIMO_SSD", "MB_OP_SSD_CHUNKED_BWD", "MB_OP_SELECTIVE_SCAN_BWD", "MB_OP_TRAP_SSD_BWD",
     "MB_OP_MIMO_SSD_BWD",
@@ -70,6 +70,9 @@ def load_library():
             lib.mb_workspace_size.restype = ctypes.c_size_t
             for f in ("mb_ssd_chunked", "mb_trap_ssd", "mb_mimo_ssd"):
                 getattr(lib, f).restype = ctypes.c_int
+        if hasattr(lib, "mb_ssd_chunked_gated"):
+            lib.mb_ssd_chunked_gated.argtypes = [_vp] * 9 + [_i64] * 7 + [ctypes.c_int, _vp, ctypes.c_size_t, _vp]
+            lib.mb_ssd_chunked_gated.restype = ctypes.c_int
         if hasattr(lib, "mb_ssd_chunked_noalloc"):
             lib.mb_ssd_chunked_noalloc.argtypes = [_vp] * 7 + [_i64] * 7 + [ctypes.c_int, _vp]
             lib.mb_ssd_chunked_noalloc.restype = ctypes.c_int
@@ -265,6 +268,31 @@ def mb_ssd_chunked(X, logdecay, B, C, h0=None, *, chunk=0, Y=None, h_out=None, w
     ws, nws = _workspace(MB_OP_SSD_CHUNKED, dev, ws, (b, L, H, P, G, N, 1, chunk))
     _call("mb_ssd_chunked", _ptr(X), _ptr(logdecay), _ptr(B), _ptr(C), _ptr(h0), _ptr(Y), _ptr(h_out),
           b, L, H, P, G, N, chunk, code, _ptr(ws), nws, _stream(dev))
+    return Y, h_out
+
+
+def mb_ssd_chunked_gated(X, logdecay, B, C, h0=None, *, D=None, z=None, chunk=0, Y=None, h_out=None, ws=None):
+    """Mamba-2 SSD with the block's output side fused into the store: Y = (SSD
+    output + D[h] X) * SiLU(z).  D (H,) float32 or None; z like X (same dtype) or
+    None; the rest as mb_ssd_chunked.  Returns (Y, h_out)."""
+    torch = _torch()
+    dev = _device_of(X)
+    dtype = X.dtype
+    code = _dtype_code(X, "X")
+    b, L, H, P = X.shape
+    G, N = B.shape[2], B.shape[3]
+    _check(logdecay, "logdecay", (b, L, H), torch.float32, dev)
+    _check(B, "B", (b, L, G, N), dtype, dev)
+    _check(C, "C", (b, L, G, N), dtype, dev)
+    _check(h0, "h0", (b, H, N, P), torch.float32, dev)
+    _check(D, "D", (H,), torch.float32, dev)
+    _check(z, "z", (b, L, H, P), dtype, dev)
+    Y = torch.empty((b, L, H, P), dtype=dtype, device=dev) if Y is None else _check(Y, "Y", (b, L, H, P), dtype, dev)
+    h_out = torch.empty((b, H, N, P), dtype=torch.float32, device=dev) if h_out is None else \
+        _check(h_out, "h_out", (b, H, N, P), torch.float32, dev)
+    ws, nws = _workspace(MB_OP_SSD_CHUNKED, dev, ws, (b, L, H, P, G, N, 1, chunk))
+    _call("mb_ssd_chunked_gated", _ptr(X), _ptr(logdecay), _ptr(B), _ptr(C), _ptr(h0), _ptr(D), _ptr(z), _ptr(Y),
+          _ptr(h_out), b, L, H, P, G, N, chunk, code, _ptr(ws), nws, _stream(dev))
     return Y, h_out
 
 

@@ -426,8 +426,8 @@ __constant__ int kTrapTiles[8][2] = {{0x33, 0x00}, {0x32, 0x11}, {0x22, -1}, {0x
 template <int NP, int R, bool TRAP, bool ROT, bool GROUPED, typename IO, bool SO, bool EPI = false,
           bool BCN = false>
 __global__ __launch_bounds__(kWalkThreads, SO ? 4 : 2) void k_walk(Args a) {
-    static_assert(!EPI || (TRAP && !SO && (R == 1 || R >= 4)),
-                  "the output epilogue is a Mamba-3 full-pass feature (one rank, or rank rows)");
+    static_assert(!EPI || (!SO && (R == 1 || R >= 4)),
+                  "the output epilogue is a full-pass feature (one rank, or rank rows)");
     static_assert(!BCN || TRAP, "the B / C prologue is a Mamba-3 feature");
     using Gm = Geo<R, TRAP>;
     constexpr int QT = Gm::QT, EXTRA = Gm::EXTRA, JX = Gm::JX;
@@ -1174,14 +1174,15 @@ __global__ __launch_bounds__(kWalkThreads, SO ? 4 : 2) void k_walk(Args a) {
 // chunk-end-weighted X^T and the masked scores.  Per chunk c, three phases
 // separated by workgroup barriers:
 //   1. matrix: Y^T = H^T C^T x e^{cum}      staging: B(c) -> LDS; loads for c+1
-//   2. matrix: Y^T += X^T M^T, store Y(c)   staging: C(c+1) -> LDS
+//   2. matrix: Y^T += X^T M^T, store Y(c)   staging: C(c+1) -> LDS (in flight
+//                                            until the end of phase 3)
 //   3. matrix: H = e^{cum_last} H + B^T Xd  staging: X^T, Xd^T, M, cum of c+1
 // Each buffer is written in the phase after its last reader, so single LDS
 // buffers suffice (Xd^T and cum, read in phase 3, are double-buffered).  Every
 // copy and load of the staging waves is issued unconditionally (offsets past a
 // buffer read zeros), so their vmcnt waits are exact.
 // ---------------------------------------------------------------------------
-template <int NP>
+template <int NP, bool EPI = false>
 __global__ __launch_bounds__(kWalkThreads) void k_walk_m2s(Args a) {
     constexpr int JP = kRows + 4;   // LDS row stride of X^T / Xd^T / M (4 mod 32)
     constexpr int NT = NP / 16;     // state tiles per matrix wave
@@ -1363,6 +1364,22 @@ __global__ __launch_bounds__(kWalkThreads) void k_walk_m2s(Args a) {
     if (mma) {
         for (int c = c_begin; c < c_end; ++c) {
             const int t0g = c * kRows;
+            // output side: X and z of this lane's outputs load now, under the
+            // chunk's matrix work (four columns of a step per tile)
+            float ex[4][4] = {}, ez[4][4] = {};
+            if constexpr (EPI) {
+                if (active) {
+#pragma unroll
+                    for (int it = 0; it < 4; ++it) {
+                        const int tg = t0g + 16 * it + li;
+                        if (tg < a.L) {
+                            const size_t e = (((size_t)b * a.L + tg) * a.H + h) * (size_t)a.P + p0 + 16 * pw + 4 * lk;
+                            if (a.Dh) load4<float>(a.X, e, ex[it]);
+                            if (a.Zg) load4<float>(a.Zg, e, ez[it]);
+                        }
+                    }
+                }
+            }
             // ---- phase 1: Y^T = H^T C^T, scaled by e^{cum} per row ------------------------
             floatx4 acc_y[4];
             if (active) {
@@ -1408,9 +1425,19 @@ __global__ __launch_bounds__(kWalkThreads) void k_walk_m2s(Args a) {
                     // lane holds Y[i = 16 it + li][p = p0 + 16 pw + 4 lk + r]
                     const int tg = t0g + 16 * it + li;
                     if (tg < a.L) {
+                        float yv[4] = {acc_y[it][0], acc_y[it][1], acc_y[it][2], acc_y[it][3]};
+                        if constexpr (EPI) {
+                            // (y + Dh x) SiLU(z)
+                            const float dh = a.Dh ? a.Dh[h] : 0.0f;
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) {
+                                const float v = fmaf(dh, ex[it][r], yv[r]);
+                                const float sg = ez[it][r] * __builtin_amdgcn_rcpf(1.0f + exp2_fast(-ez[it][r] * kLog2e));
+                                yv[r] = a.Zg ? v * sg : v;
+                            }
+                        }
                         float* yrow = (float*)a.Y + (((size_t)b * a.L + tg) * a.H + h) * (size_t)a.P;
-                        *(float4*)(yrow + p0 + 16 * pw + 4 * lk) =
-                            make_float4(acc_y[it][0], acc_y[it][1], acc_y[it][2], acc_y[it][3]);
+                        *(float4*)(yrow + p0 + 16 * pw + 4 * lk) = make_float4(yv[0], yv[1], yv[2], yv[3]);
                     }
                 }
             }
@@ -1449,10 +1476,17 @@ __global__ __launch_bounds__(kWalkThreads) void k_walk_m2s(Args a) {
             dma_rows(vw.B, sB, c);
             prefetch(c + 1);
             __syncthreads();
-            // phase 2: nothing to stage
-            __syncthreads();
-            // phase 3: C(c + 1) -> LDS (C(c) was last read in phase 1); stage c + 1
+            // phase 2: C(c + 1) -> LDS (C(c) was last read in phase 1).  The barrier
+            // closing phase 2 has no fence, so it does not wait for this copy: it
+            // lands during phases 2 and 3 and is waited for before the barrier
+            // closing phase 3 (phase 2 writes nothing else the matrix waves read
+            // before then; the empty asm keeps the compiler from moving LDS
+            // accesses across the barrier)
             dma_rows(vw.C, sC, c + 1);
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+            // phase 3: stage c + 1
             if (c + 1 < c_end) stage(c + 1);
             vm_wait<0>();
             __syncthreads();
@@ -1509,7 +1543,7 @@ __device__ __forceinline__ int swz_bt(int n) {   // B^T: rows n of 8 pieces, rea
     return ((n & 3) | (((n >> 3) & 1) << 2)) ^ ((n >> 4) & 1);
 }
 
-template <int NP, bool SO>
+template <int NP, bool SO, bool EPI = false>
 __global__ __launch_bounds__(kBfThreads, 2) void k_walk_bf(Args a) {
     constexpr bool FULL = !SO;
     constexpr int NT = NP / 16;      // state tiles per wave
@@ -1764,6 +1798,20 @@ __global__ __launch_bounds__(kBfThreads, 2) void k_walk_bf(Args a) {
         }
         if (active) {
             if constexpr (FULL) {
+                // output side: X and z of this lane's outputs, loaded ahead of the
+                // products and held as packed bf16 (two registers per four values)
+                uint2 rx[4] = {}, rz[4] = {};
+                if constexpr (EPI) {
+#pragma unroll
+                    for (int it = 0; it < 4; ++it) {
+                        const int tg = t0g + 16 * it + li;
+                        if (tg < a.L) {
+                            const size_t e = (((size_t)b * a.L + tg) * a.H + h) * (size_t)a.P + p0 + 16 * wave + 4 * lk;
+                            if (a.Dh) rx[it] = *(const uint2*)((const bf16*)a.X + e);
+                            if (a.Zg) rz[it] = *(const uint2*)((const bf16*)a.Zg + e);
+                        }
+                    }
+                }
                 const bf16* cb;
                 const bf16* mb;
                 if constexpr (PB) {
@@ -1808,9 +1856,24 @@ __global__ __launch_bounds__(kBfThreads, 2) void k_walk_bf(Args a) {
                 for (int it = 0; it < 4; ++it) {
                     const int tg = t0g + 16 * it + li;
                     if (tg < a.L) {
+                        float yv[4] = {acc_y[it][0], acc_y[it][1], acc_y[it][2], acc_y[it][3]};
+                        if constexpr (EPI) {
+                            // (y + Dh x) SiLU(z)
+                            const float dh = a.Dh ? a.Dh[h] : 0.0f;
+                            const float ex[4] = {__uint_as_float(rx[it].x << 16), __uint_as_float(rx[it].x & 0xffff0000u),
+                                                 __uint_as_float(rx[it].y << 16), __uint_as_float(rx[it].y & 0xffff0000u)};
+                            const float ez[4] = {__uint_as_float(rz[it].x << 16), __uint_as_float(rz[it].x & 0xffff0000u),
+                                                 __uint_as_float(rz[it].y << 16), __uint_as_float(rz[it].y & 0xffff0000u)};
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) {
+                                const float v = fmaf(dh, ex[r], yv[r]);
+                                const float sg = ez[r] * __builtin_amdgcn_rcpf(1.0f + exp2_fast(-ez[r] * kLog2e));
+                                yv[r] = a.Zg ? v * sg : v;
+                            }
+                        }
                         bf16* yrow = (bf16*)a.Y + (((size_t)b * a.L + tg) * a.H + h) * (size_t)a.P;
                         *(uint2*)(yrow + p0 + 16 * wave + 4 * lk) =
-                            make_uint2(pack_bf(acc_y[it][0], acc_y[it][1]), pack_bf(acc_y[it][2], acc_y[it][3]));
+                            make_uint2(pack_bf(yv[0], yv[1]), pack_bf(yv[2], yv[3]));
                     }
                 }
             }
@@ -1950,8 +2013,12 @@ mb_status launch(Args a, int64_t batch, const Plan& pl, char* ws, hipStream_t st
                 mb_status st = check_launch();
                 if (st != MB_OK) return st;
             }
-            hipLaunchKernelGGL((k_walk_bf<NP, false>), dim3((unsigned)(per_seg * a.nseg)), dim3(kBfThreads),
-                               0, stream, a);
+            if (a.Dh || a.Zg)
+                hipLaunchKernelGGL((k_walk_bf<NP, false, true>), dim3((unsigned)(per_seg * a.nseg)),
+                                   dim3(kBfThreads), 0, stream, a);
+            else
+                hipLaunchKernelGGL((k_walk_bf<NP, false>), dim3((unsigned)(per_seg * a.nseg)), dim3(kBfThreads),
+                                   0, stream, a);
             return check_launch();
         }
     }
@@ -1971,9 +2038,22 @@ mb_status launch(Args a, int64_t batch, const Plan& pl, char* ws, hipStream_t st
         mb_status st = check_launch();
         if (st != MB_OK) return st;
     }
-    if constexpr (!TRAP && !ROT && sizeof(IO) == 4)
-        hipLaunchKernelGGL((k_walk_m2s<NP>), dim3((unsigned)(per_seg * a.nseg)), dim3(kWalkThreads), 0,
-                           stream, a);
+    if constexpr (!TRAP && !ROT && sizeof(IO) == 4) {
+        if (a.Dh || a.Zg)
+            hipLaunchKernelGGL((k_walk_m2s<NP, true>), dim3((unsigned)(per_seg * a.nseg)), dim3(kWalkThreads), 0,
+                               stream, a);
+        else
+            hipLaunchKernelGGL((k_walk_m2s<NP>), dim3((unsigned)(per_seg * a.nseg)), dim3(kWalkThreads), 0,
+                               stream, a);
+    } else if constexpr (!TRAP && !ROT) {
+        // bf16 Mamba-2 with N not a multiple of 8: the general walk
+        if (a.Dh || a.Zg)
+            hipLaunchKernelGGL((k_walk<NP, R, TRAP, ROT, GROUPED, IO, false, true>),
+                               dim3((unsigned)(per_seg * a.nseg)), dim3(kWalkThreads), 0, stream, a);
+        else
+            hipLaunchKernelGGL((k_walk<NP, R, TRAP, ROT, GROUPED, IO, false>),
+                               dim3((unsigned)(per_seg * a.nseg)), dim3(kWalkThreads), 0, stream, a);
+    }
     else if constexpr (R == 1 && TRAP) {
         const dim3 g((unsigned)(per_seg * a.nseg));
         const bool epi = a.Dh || a.Zg;
@@ -2165,6 +2245,31 @@ extern "C" mb_status mb_ssd_chunked(const void* X, const float* logdecay, const 
     if ((st = check_ws(ws, ws_bytes, pl.bytes)) != MB_OK) return st;
     Args a{X, logdecay, B, C, nullptr, nullptr, nullptr, h0, nullptr, nullptr, Y, h_out, nullptr,
            nullptr, nullptr, nullptr, nullptr, (int)L, (int)H, (int)P, (int)G, (int)N, 0, 0, 0, 0};
+    return dispatch<1, false, true>(a, batch, pl, (char*)ws, dtype, stream);
+}
+
+extern "C" mb_status mb_ssd_chunked_gated(const void* X, const float* logdecay, const void* B,
+                                          const void* C, const float* h0, const float* Dskip, const void* z,
+                                          void* Y, float* h_out, int64_t batch, int64_t L, int64_t H,
+                                          int64_t P, int64_t G, int64_t N, int64_t chunk, mb_dtype dtype,
+                                          void* ws, size_t ws_bytes, hipStream_t stream) {
+    if (G < 1 || H < 1 || H % G) return MB_ERR_SHAPE;
+    if (!m2_scores_ok(L, G)) return MB_ERR_SHAPE;
+    mb_status st = ssd_common_checks(X, logdecay, B, C, h0, Y, h_out, nullptr, nullptr, nullptr,
+                                     nullptr, nullptr, batch, L, H, P, G, N, 1, dtype, chunk, false);
+    if (st != MB_OK) return st;
+    if (((uintptr_t)z & 15) || ((uintptr_t)Dskip & 3)) return MB_ERR_ALIGN;
+    const size_t ny = (size_t)(batch * L * H * P) * dtype_size(dtype);
+    if (overlaps(Y, ny, z, z ? ny : 0) || overlaps(Y, ny, Dskip, Dskip ? (size_t)H * 4 : 0)) return MB_ERR_ALIAS;
+    if (h_out && (overlaps(h_out, (size_t)(batch * H * N * P) * 4, z, z ? ny : 0) ||
+                  overlaps(h_out, (size_t)(batch * H * N * P) * 4, Dskip, Dskip ? (size_t)H * 4 : 0)))
+        return MB_ERR_ALIAS;
+    if (batch == 0) return MB_OK;
+    if (L == 0) return copy_state(h0, h_out, batch * H * N * P, stream);
+    const Plan pl = plan_for(MB_OP_SSD_CHUNKED, batch, L, H, P, G, N, 1);
+    if ((st = check_ws(ws, ws_bytes, pl.bytes)) != MB_OK) return st;
+    Args a{X, logdecay, B, C, nullptr, nullptr, nullptr, h0, nullptr, nullptr, Y, h_out, nullptr,
+           nullptr, nullptr, nullptr, nullptr, (int)L, (int)H, (int)P, (int)G, (int)N, 0, 0, 0, 0, Dskip, z};
     return dispatch<1, false, true>(a, batch, pl, (char*)ws, dtype, stream);
 }
 
