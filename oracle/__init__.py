@@ -335,6 +335,22 @@ def ssd_prologue(xBC, conv_w, dt, A, H, P, G, N, conv_b=None, dt_bias=None, x_hi
     return X, Bo, Co, dtp * _f64(A), dtp
 
 
+def ssd_block(xBC, conv_w, dt, A, H, P, G, N, conv_b=None, dt_bias=None, x_hist=None, h0=None, D=None, z=None):
+    """The Mamba-2 layer around its scan (TorchMamba README, API reference
+    Mamba2Block: d_conv taps, psi = SiLU; Math notes M2): ssd_prologue, the SSD
+    on its outputs, then the output side Y = (ssd output + D[h] x) * SiLU(z),
+    where x is the convolved, activated channel before the step size scales it
+    (x = X / dt').  D (H,) or None; z (b, L, H, P) or None.  Returns (Y, h_out)."""
+    X, Bo, Co, ld, dtp = ssd_prologue(xBC, conv_w, dt, A, H, P, G, N, conv_b, dt_bias, x_hist)
+    Y, h = ssd(X, ld, Bo, Co, h0)
+    if D is not None:
+        Y = Y + _f64(D)[None, None, :, None] * (X / dtp[..., None])
+    if z is not None:
+        z = _f64(z)
+        Y = Y * (z / (1.0 + np.exp(-z)))
+    return Y, h
+
+
 def trap_bwd(X, logdecay, B, C, beta, gamma, dY, theta=None, h0=None, dh_out=None, X_prev=None, B_prev=None):
     """Backward of the Mamba-3 SISO recurrence: the gradients of sum dY . Y + sum
     dh_out . h_out with respect to X, logdecay, B, C, beta, gamma, theta, h0,
