@@ -608,6 +608,65 @@ class M2Prologue(Workload):
                                 dt_bias=t["dt_bias"], X=X, B=B, C=C, logdecay=ld)
 
 
+class M2Block(Workload):
+    """The Mamba-2 layer around its scan in one call (mb_ssd_block: conv1d + SiLU
+    over xBC and softplus of dt fused into the chunked SSD, skip term and SiLU
+    gate at the store) at the Mamba-2 block shape; with `unfused`, the same work
+    as two calls, the prologue pass (mb_ssd_prologue) and then the SSD with its
+    output side (mb_ssd_chunked_gated); outside the step, measured beside it.
+    Bytes: xBC, dt, z read and Y written once plus the parameters; flops are the
+    SSD's."""
+    source = "selective_state_space_amd/csrc/ssd.hip"
+    bound = "mfma"
+
+    def __init__(self, mb, wl, torch, dtype, unfused=False):
+        self.mb = mb
+        b, L, H, P, G, N, K = 4, 4096, 24, 64, 1, 128, 4
+        self.dims = (H, P, G, N)
+        self.dtype = dtype
+        self.unfused = unfused
+        self.name = ("m2_unfused_" if unfused else "m2_block_") + dtype
+        self.kernel = ("k_ssd_prologue + k_scores + k_walk (state-only) + k_walk_m2s / k_walk_bf (output side)"
+                       if unfused or dtype == "bf16" else "k_scores (B, C prologue) + k_walk (state-only, x prologue) "
+                       "+ k_walk_m2s (x prologue, output side)")
+        self.shape = dict(batch=b, L=L, H=H, P=P, G=G, N=N, K=K)
+        inp = wl.m2_block_full()
+        self.inp = inp
+        act = torch.bfloat16 if dtype == "bf16" else torch.float32
+        f = torch.float32
+        self.t = {k: (_dev(v, act if k in ("xBC", "z") else f) if v is not None else None) for k, v in inp.items()}
+        self.Y = torch.empty((b, L, H, P), dtype=act, device="cuda")
+        self.h = torch.empty((b, H, N, P), dtype=f, device="cuda")
+        es = 2 if dtype == "bf16" else 4
+        cin = H * P + 2 * G * N
+        if unfused:
+            self.X = torch.empty((b, L, H, P), dtype=act, device="cuda")
+            self.B = torch.empty((b, L, G, N), dtype=act, device="cuda")
+            self.C = torch.empty((b, L, G, N), dtype=act, device="cuda")
+            self.ld = torch.empty((b, L, H), dtype=f, device="cuda")
+            self.ws = torch.empty(mb.mb_workspace_size(mb.MB_OP_SSD_CHUNKED, b, L, H, P, G, N, 1, 0),
+                                  dtype=torch.uint8, device="cuda")
+        else:
+            op = mb.MB_OP_SSD_BLOCK_BF16 if dtype == "bf16" else mb.MB_OP_SSD_BLOCK
+            self.ws = torch.empty(mb.mb_workspace_size(op, b, L, H, P, G, N, 1, 0), dtype=torch.uint8, device="cuda")
+        self.tokens = b * L
+        self.bytes = es * (b * L * cin + 2 * b * L * H * P) + 4 * (b * L * H + cin * (K + 1) + 3 * H + b * H * N * P)
+        _, self.flops = ssd_work(b, L, H, P, N, G, es)
+        self.exps = None
+
+    def run(self):
+        t = self.t
+        H, P, G, N = self.dims
+        if self.unfused:
+            self.mb.mb_ssd_prologue(t["xBC"], t["conv_w"], t["dt"], t["A"], H, P, G, N, conv_b=t["conv_b"],
+                                    dt_bias=t["dt_bias"], X=self.X, B=self.B, C=self.C, logdecay=self.ld)
+            self.mb.mb_ssd_chunked_gated(self.X, self.ld, self.B, self.C, None, D=t["D"], z=t["z"], Y=self.Y,
+                                         h_out=self.h, ws=self.ws)
+        else:
+            self.mb.mb_ssd_block(t["xBC"], t["conv_w"], t["dt"], t["A"], H, P, G, N, conv_b=t["conv_b"],
+                                 dt_bias=t["dt_bias"], D=t["D"], z=t["z"], Y=self.Y, h_out=self.h, ws=self.ws)
+
+
 class MIMO(Workload):
     name = "mimo"
     kernel = "k_walk (state-only pass) + k_walk (full pass)"
@@ -670,7 +729,7 @@ ALL = ["m1_scan", "m1_step", "ssd_f32", "ssd_bf16", "siso", "mimo"]
 # Mamba-1 scan with the block prologue and epilogue fused, the Mamba-2 block prologue, Mamba-3 SISO with its output
 # epilogue and with both ends of its block fused, and the backwards of the
 # Mamba-2 SSD, the Mamba-1 scan, Mamba-3 SISO and MIMO
-NEXT = ["m2_decode", "siso_decode", "mimo_decode", "m1_long", "m1_long_one_block", "m1_fused", "m2_prologue", "ssd_gated_f32", "ssd_gated_bf16", "siso_gated", "siso_block", "mimo_block", "ssd_bwd", "m1_bwd", "siso_bwd", "mimo_bwd"]
+NEXT = ["m2_decode", "siso_decode", "mimo_decode", "m1_long", "m1_long_one_block", "m1_fused", "m2_prologue", "m2_block_f32", "m2_unfused_f32", "m2_block_bf16", "m2_unfused_bf16", "ssd_gated_f32", "ssd_gated_bf16", "siso_gated", "siso_block", "mimo_block", "ssd_bwd", "m1_bwd", "siso_bwd", "mimo_bwd"]
 
 
 def make(name, mb, wl, torch):
@@ -688,6 +747,10 @@ def make(name, mb, wl, torch):
         return M2Prologue(mb, wl, torch)
     if name == "siso_block":
         return SISOBlock(mb, wl, torch)
+    if name.startswith("m2_block_"):
+        return M2Block(mb, wl, torch, name[len("m2_block_"):])
+    if name.startswith("m2_unfused_"):
+        return M2Block(mb, wl, torch, name[len("m2_unfused_"):], unfused=True)
     if name.startswith("ssd_gated_"):
         return SSDGated(mb, wl, torch, name[len("ssd_gated_"):])
     if name == "mimo_block":

@@ -65,7 +65,9 @@ typedef enum {
     MB_OP_SSD_CHUNKED_BWD = 5,
     MB_OP_SELECTIVE_SCAN_BWD = 6,
     MB_OP_TRAP_SSD_BWD = 7,
-    MB_OP_MIMO_SSD_BWD = 8
+    MB_OP_MIMO_SSD_BWD = 8,
+    MB_OP_SSD_BLOCK = 9,        /* mb_ssd_block with MB_F32 */
+    MB_OP_SSD_BLOCK_BF16 = 10   /* mb_ssd_block with MB_BF16 */
 } mb_op;
 
 /*
@@ -192,6 +194,39 @@ mb_status mb_ssd_chunked_gated(const void* X, const float* logdecay, const void*
                                void* Y, float* h_out, int64_t batch, int64_t L, int64_t H,
                                int64_t P, int64_t G, int64_t N, int64_t chunk, mb_dtype dtype,
                                void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * The Mamba-2 layer around its scan in one call: the block prologue of
+ * mb_ssd_prologue (causal depthwise conv1d of K taps over the projected channels
+ * xBC = (x | B | C), SiLU, dt' = softplus(dt + dt_bias), X = x dt', log-decay
+ * dt' A) fused into the chunked SSD, and the output side
+ *     Y_t = (S_t^T C_t + Dskip[h] x_t) * SiLU(z_t)
+ * with x_t the convolved, activated x before dt' scales it (TorchMamba README,
+ * API reference Mamba2Block: d_conv taps, psi = SiLU; Math notes M2).  X, B and
+ * With MB_F32, X, B and C never pass through memory as tensors of their own:
+ * the scores kernel convolves B and C, the walks convolve x as they stage it.
+ * With MB_BF16 the call runs as two passes (the prologue pass into the
+ * workspace, then the SSD with the output side): the bf16 walk is bound by
+ * latency per chunk, and measured faster so (0.19 against 0.26 ms at batch 4,
+ * L 4096, H 24, P 64, N 128).
+ *   xBC     : (batch, L, H*P + 2*G*N)  dtype   raw projected channels
+ *   conv_w  : (H*P + 2*G*N, K) fp32; conv_b (H*P + 2*G*N) fp32 or NULL; K in 1..4
+ *   x_hist  : (batch, K-1, H*P + 2*G*N) dtype, the raw rows before the call, or NULL (zeros)
+ *   dt      : (batch, L, H) fp32 raw;  dt_bias (H) fp32 or NULL;  A (H) fp32
+ *   Dskip   : (H) fp32 or NULL;  z : (batch, L, H, P) dtype or NULL (no gate)
+ *   h0, h_out : (batch, H, N, P) fp32 as mb_ssd_chunked;  Y : (batch, L, H, P) dtype
+ * A split sequence chains exactly with h0 = the previous h_out and x_hist = the
+ * previous call's last K-1 rows of xBC.  ws: at least
+ * mb_workspace_size(MB_OP_SSD_BLOCK or MB_OP_SSD_BLOCK_BF16, batch, L, H, P, G,
+ * N) bytes, 256-byte aligned.  Limits as mb_ssd_chunked; with MB_BF16,
+ * N % 8 == 0 (MB_ERR_SHAPE otherwise); xBC, x_hist, z and Y 16-byte aligned.
+ */
+mb_status mb_ssd_block(const void* xBC, const float* conv_w, const float* conv_b,
+                       const void* x_hist, const float* dt, const float* dt_bias,
+                       const float* A, const float* Dskip, const void* z, const float* h0,
+                       void* Y, float* h_out, int64_t batch, int64_t L, int64_t H, int64_t P,
+                       int64_t G, int64_t N, int64_t K, mb_dtype dtype, void* ws,
+                       size_t ws_bytes, hipStream_t stream);
 
 /*
  * mb_ssd_chunked for callers that cannot allocate device memory (code under

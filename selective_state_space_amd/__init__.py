@@ -19,7 +19,7 @@ __all__ = [
     "mb_ssd_step", "mb_selective_scan_fused", "mb_ssd_chunked_bwd", "mb_selective_scan_bwd", "mb_trap_ssd_bwd", "mb_mimo_ssd_bwd", "mb_trap_ssd_gated", "mb_trap_ssd_block", "mb_ssd_prologue", "mb_mimo_ssd_block", "mb_ssd_chunked_gated", "mb_ssd_chunked_noalloc", "mb_workspace_size", "mb_status_str", "lib_path", "load_library", "MBError",
     "MB_OP_SELECTIVE_SCAN", "MB_OP_SSM_STEP", "MB_OP_SSD_CHUNKED", "MB_OP_TRAP_SSD",
     "MB_OP_MIMO_SSD", "MB_OP_SSD_CHUNKED_BWD", "MB_OP_SELECTIVE_SCAN_BWD", "MB_OP_TRAP_SSD_BWD",
-    "MB_OP_MIMO_SSD_BWD",
+    "MB_OP_MIMO_SSD_BWD", "MB_OP_SSD_BLOCK", "MB_OP_SSD_BLOCK_BF16", "mb_ssd_block",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -30,7 +30,7 @@ _lib = None
 MB_F32, MB_BF16 = 0, 1
 (MB_OP_SELECTIVE_SCAN, MB_OP_SSM_STEP, MB_OP_SSD_CHUNKED, MB_OP_TRAP_SSD,
  MB_OP_MIMO_SSD, MB_OP_SSD_CHUNKED_BWD, MB_OP_SELECTIVE_SCAN_BWD, MB_OP_TRAP_SSD_BWD,
- MB_OP_MIMO_SSD_BWD) = range(9)
+ MB_OP_MIMO_SSD_BWD, MB_OP_SSD_BLOCK, MB_OP_SSD_BLOCK_BF16) = range(11)
 
 _vp = ctypes.c_void_p
 _i64 = ctypes.c_int64
@@ -70,6 +70,9 @@ def load_library():
             lib.mb_workspace_size.restype = ctypes.c_size_t
             for f in ("mb_ssd_chunked", "mb_trap_ssd", "mb_mimo_ssd"):
                 getattr(lib, f).restype = ctypes.c_int
+        if hasattr(lib, "mb_ssd_block"):
+            lib.mb_ssd_block.argtypes = [_vp] * 12 + [_i64] * 7 + [ctypes.c_int, _vp, ctypes.c_size_t, _vp]
+            lib.mb_ssd_block.restype = ctypes.c_int
         if hasattr(lib, "mb_ssd_chunked_gated"):
             lib.mb_ssd_chunked_gated.argtypes = [_vp] * 9 + [_i64] * 7 + [ctypes.c_int, _vp, ctypes.c_size_t, _vp]
             lib.mb_ssd_chunked_gated.restype = ctypes.c_int
@@ -268,6 +271,42 @@ def mb_ssd_chunked(X, logdecay, B, C, h0=None, *, chunk=0, Y=None, h_out=None, w
     ws, nws = _workspace(MB_OP_SSD_CHUNKED, dev, ws, (b, L, H, P, G, N, 1, chunk))
     _call("mb_ssd_chunked", _ptr(X), _ptr(logdecay), _ptr(B), _ptr(C), _ptr(h0), _ptr(Y), _ptr(h_out),
           b, L, H, P, G, N, chunk, code, _ptr(ws), nws, _stream(dev))
+    return Y, h_out
+
+
+def mb_ssd_block(xBC, conv_w, dt, A, H, P, G, N, *, conv_b=None, dt_bias=None, x_hist=None, D=None, z=None,
+                 h0=None, Y=None, h_out=None, ws=None):
+    """The Mamba-2 layer around its scan in one call: conv1d + SiLU over xBC
+    (batch, L, H*P + 2*G*N), softplus(dt + dt_bias), the chunked SSD and the
+    output side (y + D[h] x) * SiLU(z).  xBC, x_hist, z and Y share one dtype
+    (float32 or bfloat16); conv_w (channels, K), conv_b, dt (batch, L, H),
+    dt_bias, A, D float32.  Returns (Y, h_out)."""
+    torch = _torch()
+    dev = _device_of(xBC)
+    dtype = xBC.dtype
+    code = _dtype_code(xBC, "xBC")
+    b, L, cin = xBC.shape
+    if cin != H * P + 2 * G * N:
+        raise ValueError("xBC has %d channels; H*P + 2*G*N = %d" % (cin, H * P + 2 * G * N))
+    K = conv_w.shape[1]
+    f32 = torch.float32
+    _check(xBC, "xBC", (b, L, cin), dtype, dev)
+    _check(conv_w, "conv_w", (cin, K), f32, dev)
+    _check(conv_b, "conv_b", (cin,), f32, dev)
+    _check(x_hist, "x_hist", (b, K - 1, cin), dtype, dev)
+    _check(dt, "dt", (b, L, H), f32, dev)
+    _check(dt_bias, "dt_bias", (H,), f32, dev)
+    _check(A, "A", (H,), f32, dev)
+    _check(D, "D", (H,), f32, dev)
+    _check(z, "z", (b, L, H, P), dtype, dev)
+    _check(h0, "h0", (b, H, N, P), f32, dev)
+    Y = torch.empty((b, L, H, P), dtype=dtype, device=dev) if Y is None else _check(Y, "Y", (b, L, H, P), dtype, dev)
+    h_out = torch.empty((b, H, N, P), dtype=f32, device=dev) if h_out is None else \
+        _check(h_out, "h_out", (b, H, N, P), f32, dev)
+    ws, nws = _workspace(MB_OP_SSD_BLOCK_BF16 if code == MB_BF16 else MB_OP_SSD_BLOCK, dev, ws,
+                         (b, L, H, P, G, N, 1, 0))
+    _call("mb_ssd_block", _ptr(xBC), _ptr(conv_w), _ptr(conv_b), _ptr(x_hist), _ptr(dt), _ptr(dt_bias), _ptr(A),
+          _ptr(D), _ptr(z), _ptr(h0), _ptr(Y), _ptr(h_out), b, L, H, P, G, N, K, code, _ptr(ws), nws, _stream(dev))
     return Y, h_out
 
 

@@ -201,6 +201,18 @@ def m2_prologue_inputs(rng, batch, L, H, P, G, N, K=4, hist=True):
     return dict(xBC=xBC, conv_w=conv_w, dt=dt, A=A, conv_b=conv_b, dt_bias=dt_bias, x_hist=x_hist)
 
 
+def m2_block_full(seed=120, batch=4, L=4096, H=24, P=64, G=1, N=128, K=4):
+    """The Mamba-2 layer at the block shape: the prologue inputs (m2_prologue_inputs,
+    no history), then the skip weight D ~ N(0,1) (H,) and the gate z ~ N(0,1)
+    (b, L, H, P); h0 = 0."""
+    rng = np.random.default_rng(seed)
+    i = m2_prologue_inputs(rng, batch, L, H, P, G, N, K, hist=False)
+    i["D"] = rng.standard_normal(H)
+    i["z"] = rng.standard_normal((batch, L, H, P))
+    i["h0"] = None
+    return i
+
+
 def m2_prologue_block(seed=117, batch=4, L=4096, H=24, P=64, G=1, N=128, K=4):
     return m2_prologue_inputs(np.random.default_rng(seed), batch, L, H, P, G, N, K, hist=False)
 
