@@ -168,9 +168,12 @@ mb_status mb_selective_scan_fused(const float* x, const float* conv_w, const flo
  * chunk: 0 selects the library's chunk length; otherwise must be 64.
  * ws / ws_bytes: device workspace of at least mb_workspace_size(MB_OP_SSD_CHUNKED, ...)
  * bytes, 256-byte aligned; contents on entry are ignored.
- * Supported: N <= 128 and N % 4 == 0, P % 16 == 0.
- * With MB_BF16 and N % 8 == 0 the products take bf16 operands (fp32
- * accumulation, fp32 state; see the dtype note at the top).
+ * Supported: 1 <= N <= 128, P >= 1.  Shapes with P % 16 != 0 or N % 4 != 0
+ * (e.g. P = 1, the Mamba-1 -> Mamba-2 reduction of the Math notes) run on the
+ * same kernels through zero-padded copies in the workspace (P rounded up to a
+ * multiple of 16, N to a multiple of 4): exact, at the cost of the copies.
+ * With MB_BF16 and N % 8 == 0 (after that rounding) the products take bf16
+ * operands (fp32 accumulation, fp32 state; see the dtype note at the top).
  */
 mb_status mb_ssd_chunked(const void* X, const float* logdecay, const void* B,
                          const void* C, const float* h0, void* Y, float* h_out,
@@ -202,7 +205,7 @@ mb_status mb_ssd_chunked_gated(const void* X, const float* logdecay, const void*
  * dt' A) fused into the chunked SSD, and the output side
  *     Y_t = (S_t^T C_t + Dskip[h] x_t) * SiLU(z_t)
  * with x_t the convolved, activated x before dt' scales it (TorchMamba README,
- * API reference Mamba2Block: d_conv taps, psi = SiLU; Math notes M2).  X, B and
+ * API reference Mamba2Block: d_conv taps, psi = SiLU; Math notes M2).
  * With MB_F32, X, B and C never pass through memory as tensors of their own:
  * the scores kernel convolves B and C, the walks convolve x as they stage it.
  * With MB_BF16 the call runs as two passes (the prologue pass into the

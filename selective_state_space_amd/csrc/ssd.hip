@@ -2457,6 +2457,139 @@ mb_status check_ws(void* ws, size_t ws_bytes, size_t need) {
     return MB_OK;
 }
 
+// Mamba-2 shapes outside the tiles of the walks (P not a multiple of 16, N not
+// a multiple of 4; e.g. P = 1, the Mamba-1 -> Mamba-2 reduction) run on the
+// same kernels through zero-padded copies in the workspace: X, Y and z padded
+// to P' columns, B and C to N' states, the state to N' x P'.  The added state
+// rows see B = 0 and start at 0, the added columns see X = 0, and C = 0 on the
+// added rows, so they add exact zeros to every sum and the result is that of
+// the unpadded recurrence.
+int64_t pad_p(int64_t P) { return (P + 15) / 16 * 16; }
+int64_t pad_n(int64_t N) { return (N + 3) / 4 * 4; }
+bool needs_pad(int64_t P, int64_t N) { return P % 16 != 0 || N % 4 != 0; }
+
+// (rows, n_small, p_small) <-> (rows, n_big, p_big) copies of E-sized
+// elements; PAD widens with zeros, !PAD takes the leading block back
+template <typename E, bool PAD>
+__global__ __launch_bounds__(256) void k_pad(const E* __restrict__ src, E* __restrict__ dst, int64_t rows,
+                                             int n_small, int p_small, int n_big, int p_big) {
+    const int64_t total = rows * (PAD ? (int64_t)n_big * p_big : (int64_t)n_small * p_small);
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
+        if constexpr (PAD) {
+            const int j = (int)(i % p_big);
+            const int64_t q = i / p_big;
+            const int k = (int)(q % n_big);
+            const int64_t r = q / n_big;
+            dst[i] = (j < p_small && k < n_small) ? src[(r * n_small + k) * p_small + j] : (E)0;
+        } else {
+            const int j = (int)(i % p_small);
+            const int64_t q = i / p_small;
+            const int k = (int)(q % n_small);
+            const int64_t r = q / n_small;
+            dst[i] = src[(r * n_big + k) * p_big + j];
+        }
+    }
+}
+
+mb_status pad_copy(bool pad, const void* src, void* dst, size_t es, int64_t rows, int64_t n_small, int64_t p_small,
+                   int64_t n_big, int64_t p_big, hipStream_t stream) {
+    const int64_t total = rows * (pad ? n_big * p_big : n_small * p_small);
+    if (total == 0) return MB_OK;
+    const unsigned grid = (unsigned)std::min<int64_t>((total + 255) / 256, 8192);
+    const int ns = (int)n_small, ps = (int)p_small, nb = (int)n_big, pb = (int)p_big;
+    if (es == 2) {
+        if (pad)
+            hipLaunchKernelGGL((k_pad<uint16_t, true>), dim3(grid), dim3(256), 0, stream, (const uint16_t*)src,
+                               (uint16_t*)dst, rows, ns, ps, nb, pb);
+        else
+            hipLaunchKernelGGL((k_pad<uint16_t, false>), dim3(grid), dim3(256), 0, stream, (const uint16_t*)src,
+                               (uint16_t*)dst, rows, ns, ps, nb, pb);
+    } else {
+        if (pad)
+            hipLaunchKernelGGL((k_pad<uint32_t, true>), dim3(grid), dim3(256), 0, stream, (const uint32_t*)src,
+                               (uint32_t*)dst, rows, ns, ps, nb, pb);
+        else
+            hipLaunchKernelGGL((k_pad<uint32_t, false>), dim3(grid), dim3(256), 0, stream, (const uint32_t*)src,
+                               (uint32_t*)dst, rows, ns, ps, nb, pb);
+    }
+    return check_launch();
+}
+
+// workspace of the Mamba-2 SSD: the plan's (at the padded sizes), then, for
+// padded shapes, X, Y and z (P' columns), B and C (N' states) and one state;
+// sized for 4-byte elements whatever the dtype
+struct SsdWs {
+    Plan pl;
+    int64_t P2, N2;
+    size_t off_x, off_y, off_z, off_b, off_c, off_h, bytes;
+};
+SsdWs ssd_ws(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t G, int64_t N) {
+    SsdWs w{};
+    const bool pad = needs_pad(P, N);
+    w.P2 = pad ? pad_p(P) : P;
+    w.N2 = pad ? pad_n(N) : N;
+    w.pl = plan_for(MB_OP_SSD_CHUNKED, batch, L, H, w.P2, G, w.N2, 1);
+    size_t off = w.pl.bytes;
+    if (pad) {
+        const size_t nx = align256((size_t)(batch * L * H * w.P2) * 4);
+        const size_t nbc = align256((size_t)(batch * L * G * w.N2) * 4);
+        w.off_x = off;
+        off += nx;
+        w.off_y = off;
+        off += nx;
+        w.off_z = off;
+        off += nx;
+        w.off_b = off;
+        off += nbc;
+        w.off_c = off;
+        off += nbc;
+        w.off_h = off;
+        off += align256((size_t)(batch * H * w.N2 * w.P2) * 4);
+    }
+    w.bytes = off;
+    return w;
+}
+
+// the Mamba-2 SSD (with the output side when Dskip or z is given), after the
+// caller's checks; batch > 0, L > 0
+mb_status ssd_run(const void* X, const float* logdecay, const void* B, const void* C, const float* h0,
+                  const float* Dskip, const void* z, void* Y, float* h_out, int64_t batch, int64_t L, int64_t H,
+                  int64_t P, int64_t G, int64_t N, mb_dtype dtype, char* ws, size_t ws_bytes, hipStream_t stream) {
+    const SsdWs w = ssd_ws(batch, L, H, P, G, N);
+    mb_status st;
+    if ((st = check_ws(ws, ws_bytes, w.bytes)) != MB_OK) return st;
+    if (!needs_pad(P, N)) {
+        Args a{X, logdecay, B, C, nullptr, nullptr, nullptr, h0, nullptr, nullptr, Y, h_out, nullptr,
+               nullptr, nullptr, nullptr, nullptr, (int)L, (int)H, (int)P, (int)G, (int)N, 0, 0, 0, 0, Dskip, z};
+        return dispatch<1, false, true>(a, batch, w.pl, ws, dtype, stream);
+    }
+    const size_t es = dtype_size(dtype);
+    const int64_t P2 = w.P2, N2 = w.N2;
+    void* Xp = ws + w.off_x;
+    void* Yp = ws + w.off_y;
+    void* zp = z ? (void*)(ws + w.off_z) : nullptr;
+    const void* Bp = B;
+    const void* Cp = C;
+    float* hs = (float*)(ws + w.off_h);
+    if ((st = pad_copy(true, X, Xp, es, batch * L * H, 1, P, 1, P2, stream)) != MB_OK) return st;
+    if (z && (st = pad_copy(true, z, zp, es, batch * L * H, 1, P, 1, P2, stream)) != MB_OK) return st;
+    if (N2 != N) {
+        if ((st = pad_copy(true, B, ws + w.off_b, es, batch * L * G, 1, N, 1, N2, stream)) != MB_OK) return st;
+        if ((st = pad_copy(true, C, ws + w.off_c, es, batch * L * G, 1, N, 1, N2, stream)) != MB_OK) return st;
+        Bp = ws + w.off_b;
+        Cp = ws + w.off_c;
+    }
+    if (h0 && (st = pad_copy(true, h0, hs, 4, batch * H, N, P, N2, P2, stream)) != MB_OK) return st;
+    // one padded state serves as h0 and h_out (the walks allow them equal)
+    Args a{Xp, logdecay, Bp, Cp, nullptr, nullptr, nullptr, h0 ? hs : nullptr, nullptr, nullptr, Yp,
+           h_out ? hs : nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, (int)L, (int)H, (int)P2, (int)G,
+           (int)N2, 0, 0, 0, 0, Dskip, zp};
+    if ((st = dispatch<1, false, true>(a, batch, w.pl, ws, dtype, stream)) != MB_OK) return st;
+    if ((st = pad_copy(false, Yp, Y, es, batch * L * H, 1, P, 1, P2, stream)) != MB_OK) return st;
+    if (h_out) return pad_copy(false, hs, h_out, 4, batch * H, N, P, N2, P2, stream);
+    return MB_OK;
+}
+
 }  // namespace
 }  // namespace mb
 
@@ -2473,9 +2606,14 @@ extern "C" size_t mb_workspace_size(mb_op op, int64_t batch, int64_t L, int64_t 
     if (op == MB_OP_MIMO_SSD_BWD) return mimo_bwd_workspace(batch, L, H, P, N, R);
     // Mamba-1 backward: the sizes (batch, L, D, N) travel as (batch, L, H, N)
     if (op == MB_OP_SELECTIVE_SCAN_BWD) return m1_bwd_workspace(batch, L, H, N);
+    if (op == MB_OP_SSD_CHUNKED) {
+        if (P < 1 || N < 1 || !dims_ok(batch, L, H, pad_p(P), pad_n(N))) return 0;
+        if (G < 1 || H % G || !m2_scores_ok(L, G) || batch == 0 || L == 0) return 0;
+        return ssd_ws(batch, L, H, P, G, N).bytes;
+    }
     if (!dims_ok(batch, L, H, P, N)) return 0;
     const bool blk = op == MB_OP_SSD_BLOCK || op == MB_OP_SSD_BLOCK_BF16;
-    if ((op == MB_OP_SSD_CHUNKED || blk) && (G < 1 || H % G || !m2_scores_ok(L, G))) return 0;
+    if (blk && (G < 1 || H % G || !m2_scores_ok(L, G))) return 0;
     if (blk) {
         if (batch == 0 || L == 0) return 0;
         const Plan pl = plan_for(MB_OP_SSD_CHUNKED, batch, L, H, P, G, N, 1);
@@ -2492,9 +2630,10 @@ static mb_status ssd_common_checks(const void* X, const float* logdecay, const v
                                    const void* X_prev, const void* B_prev,
                                    int64_t batch, int64_t L, int64_t H, int64_t P, int64_t nBC,
                                    int64_t N, int64_t R, mb_dtype dtype, int64_t chunk,
-                                   bool trap) {
+                                   bool trap, bool pad = false) {
     if (!dtype_ok(dtype)) return MB_ERR_DTYPE;
-    if (!dims_ok(batch, L, H, P, N, R)) return MB_ERR_SHAPE;
+    if (pad ? (P < 1 || N < 1 || !dims_ok(batch, L, H, pad_p(P), pad_n(N), R)) : !dims_ok(batch, L, H, P, N, R))
+        return MB_ERR_SHAPE;
     if (chunk != 0 && chunk != kRows) return MB_ERR_SHAPE;
     if (theta && (N % 2)) return MB_ERR_SHAPE;
     const size_t es = dtype_size(dtype);
@@ -2531,15 +2670,12 @@ extern "C" mb_status mb_ssd_chunked(const void* X, const float* logdecay, const 
     if (G < 1 || H < 1 || H % G) return MB_ERR_SHAPE;
     if (!m2_scores_ok(L, G)) return MB_ERR_SHAPE;
     mb_status st = ssd_common_checks(X, logdecay, B, C, h0, Y, h_out, nullptr, nullptr, nullptr,
-                                     nullptr, nullptr, batch, L, H, P, G, N, 1, dtype, chunk, false);
+                                     nullptr, nullptr, batch, L, H, P, G, N, 1, dtype, chunk, false, true);
     if (st != MB_OK) return st;
     if (batch == 0) return MB_OK;
     if (L == 0) return copy_state(h0, h_out, batch * H * N * P, stream);
-    const Plan pl = plan_for(MB_OP_SSD_CHUNKED, batch, L, H, P, G, N, 1);
-    if ((st = check_ws(ws, ws_bytes, pl.bytes)) != MB_OK) return st;
-    Args a{X, logdecay, B, C, nullptr, nullptr, nullptr, h0, nullptr, nullptr, Y, h_out, nullptr,
-           nullptr, nullptr, nullptr, nullptr, (int)L, (int)H, (int)P, (int)G, (int)N, 0, 0, 0, 0};
-    return dispatch<1, false, true>(a, batch, pl, (char*)ws, dtype, stream);
+    return ssd_run(X, logdecay, B, C, h0, nullptr, nullptr, Y, h_out, batch, L, H, P, G, N, dtype, (char*)ws,
+                   ws_bytes, stream);
 }
 
 extern "C" mb_status mb_ssd_chunked_gated(const void* X, const float* logdecay, const void* B,
@@ -2550,7 +2686,7 @@ extern "C" mb_status mb_ssd_chunked_gated(const void* X, const float* logdecay, 
     if (G < 1 || H < 1 || H % G) return MB_ERR_SHAPE;
     if (!m2_scores_ok(L, G)) return MB_ERR_SHAPE;
     mb_status st = ssd_common_checks(X, logdecay, B, C, h0, Y, h_out, nullptr, nullptr, nullptr,
-                                     nullptr, nullptr, batch, L, H, P, G, N, 1, dtype, chunk, false);
+                                     nullptr, nullptr, batch, L, H, P, G, N, 1, dtype, chunk, false, true);
     if (st != MB_OK) return st;
     if (((uintptr_t)z & 15) || ((uintptr_t)Dskip & 3)) return MB_ERR_ALIGN;
     const size_t ny = (size_t)(batch * L * H * P) * dtype_size(dtype);
@@ -2560,11 +2696,8 @@ extern "C" mb_status mb_ssd_chunked_gated(const void* X, const float* logdecay, 
         return MB_ERR_ALIAS;
     if (batch == 0) return MB_OK;
     if (L == 0) return copy_state(h0, h_out, batch * H * N * P, stream);
-    const Plan pl = plan_for(MB_OP_SSD_CHUNKED, batch, L, H, P, G, N, 1);
-    if ((st = check_ws(ws, ws_bytes, pl.bytes)) != MB_OK) return st;
-    Args a{X, logdecay, B, C, nullptr, nullptr, nullptr, h0, nullptr, nullptr, Y, h_out, nullptr,
-           nullptr, nullptr, nullptr, nullptr, (int)L, (int)H, (int)P, (int)G, (int)N, 0, 0, 0, 0, Dskip, z};
-    return dispatch<1, false, true>(a, batch, pl, (char*)ws, dtype, stream);
+    return ssd_run(X, logdecay, B, C, h0, Dskip, z, Y, h_out, batch, L, H, P, G, N, dtype, (char*)ws, ws_bytes,
+                   stream);
 }
 
 extern "C" mb_status mb_ssd_block(const void* xBC, const float* conv_w, const float* conv_b,
@@ -2659,17 +2792,15 @@ extern "C" mb_status mb_ssd_chunked_noalloc(const void* X, const float* logdecay
     if (G < 1 || H < 1 || H % G) return MB_ERR_SHAPE;
     if (!m2_scores_ok(L, G)) return MB_ERR_SHAPE;
     mb_status st = ssd_common_checks(X, logdecay, B, C, h0, Y, h_out, nullptr, nullptr, nullptr,
-                                     nullptr, nullptr, batch, L, H, P, G, N, 1, dtype, chunk, false);
+                                     nullptr, nullptr, batch, L, H, P, G, N, 1, dtype, chunk, false, true);
     if (st != MB_OK) return st;
     if (batch == 0) return MB_OK;
     if (L == 0) return copy_state(h0, h_out, batch * H * N * P, stream);
-    const Plan pl = plan_for(MB_OP_SSD_CHUNKED, batch, L, H, P, G, N, 1);
-    if (pl.bytes > kScratchBytes) return MB_ERR_WORKSPACE;
+    if (ssd_ws(batch, L, H, P, G, N).bytes > kScratchBytes) return MB_ERR_WORKSPACE;
     char* ws = nullptr;
     if ((st = scratch_ptr(&ws)) != MB_OK) return st;
-    Args a{X, logdecay, B, C, nullptr, nullptr, nullptr, h0, nullptr, nullptr, Y, h_out, nullptr,
-           nullptr, nullptr, nullptr, nullptr, (int)L, (int)H, (int)P, (int)G, (int)N, 0, 0, 0, 0};
-    return dispatch<1, false, true>(a, batch, pl, ws, dtype, stream);
+    return ssd_run(X, logdecay, B, C, h0, nullptr, nullptr, Y, h_out, batch, L, H, P, G, N, dtype, ws,
+                   kScratchBytes, stream);
 }
 
 extern "C" mb_status mb_trap_ssd(const void* X, const float* logdecay, const void* B,

@@ -173,8 +173,13 @@ def test_ssd_validation(lib):
     assert ssd(lib, dtype=2) == E_DTYPE
     assert ssd(lib, G=3) == E_SHAPE            # H % G != 0
     assert ssd(lib, N=130) == E_SHAPE
-    assert ssd(lib, N=6) == E_SHAPE            # N % 4 != 0
-    assert ssd(lib, P_=40) == E_SHAPE          # P % 16 != 0
+    assert ssd(lib, N=0) == E_SHAPE
+    assert ssd(lib, P_=0) == E_SHAPE
+    # P % 16 != 0 or N % 4 != 0 run through padded copies: they pass the shape
+    # checks and then need the larger workspace
+    assert ssd(lib, N=6, ws_bytes=16) == E_WS
+    assert ssd(lib, P_=40, ws_bytes=16) == E_WS
+    assert ssd(lib, P_=1, N=2, ws_bytes=16) == E_WS
     assert ssd(lib, chunk=32) == E_SHAPE
     assert ssd(lib, ws=0) == E_WS
     assert ssd(lib, ws_bytes=16) == E_WS
@@ -397,6 +402,15 @@ def test_workspace_sizes(lib):
     for R in (1, 2, 4, 8, 16):
         args = (mb.MB_OP_MIMO_SSD, 2, 8192, 16, 64, 1, 128, R)
         assert mb.mb_workspace_size(*args) == _ws(*args), args
+    # padded shapes: the plan at P' = 48, N' = 8, then X, Y, z (P' columns), B, C
+    # (N' states) and one N' x P' state per (batch, head)
+    a = _a256
+    assert mb.mb_workspace_size(mb.MB_OP_SSD_CHUNKED, 2, 100, 4, 40, 1, 6) == \
+        _ws(mb.MB_OP_SSD_CHUNKED, 2, 100, 4, 48, 1, 8) + 3 * a(2 * 100 * 4 * 48 * 4) + \
+        2 * a(2 * 100 * 1 * 8 * 4) + a(2 * 4 * 8 * 48 * 4)
+    assert mb.mb_workspace_size(mb.MB_OP_SSD_CHUNKED, 1, 50, 3, 1, 1, 2) == \
+        _ws(mb.MB_OP_SSD_CHUNKED, 1, 50, 3, 16, 1, 4) + 3 * a(50 * 3 * 16 * 4) + 2 * a(50 * 4 * 4) + \
+        a(3 * 4 * 16 * 4)
     # short sequences need no segments; the trapezoid then needs no workspace
     assert mb.mb_workspace_size(mb.MB_OP_TRAP_SSD, 1, 100, 2, 16, 1, 16) == 0
     assert mb.mb_workspace_size(mb.MB_OP_SSD_CHUNKED, 4, 4096, 24, 64, 5, 128) == 0   # invalid G
