@@ -2162,6 +2162,352 @@ __global__ __launch_bounds__(kBfThreads, 2) void k_walk_bf(Args a) {
 }
 
 // ---------------------------------------------------------------------------
+// Mamba-2 walk with bf16 inputs (full pass), wave-specialised as k_walk_m2s.
+// Waves 0-3 are the matrix waves: wave w owns state columns p0 + 16 w .. + 15
+// for all NP state rows (the accumulator layout of k_walk_bf) and does every
+// product of the chunk for them on the bf16 matrix instruction.  Waves 4-7 are
+// the staging waves: they copy C and the transposed B into LDS by LDS DMA, load
+// X, the scores and the log-decay of the next chunk into registers, and stage
+// X^T, the chunk-end-weighted Xd^T and the masked scores M as bf16 rows in LDS.
+// The matrix waves read every operand with 16-byte LDS reads and never wait on
+// the decay scan, the exponentials or global memory.  Per chunk c, three phases
+// separated by workgroup barriers:
+//   1. matrix: Y^T = H^T C^T x e^{cum}       staging: B^T(c) -> LDS; loads for c+1
+//   2. matrix: Y^T += X^T M^T, store Y(c)    staging: C(c+1) -> LDS (in flight
+//                                             until the end of phase 3)
+//   3. matrix: H = e^{cum_last} H + B^T Xd   staging: X^T, Xd^T, M, cum of c+1
+// Xd^T and cum are double-buffered, the other buffers single: each is written
+// in the phase after its last reader.  The matrix waves only read LDS, and use
+// every value they read within the phase, so their barriers carry no wait:
+// their stores of Y drain while the next phase runs.  The staging waves issue
+// the loads of chunk c + 2 right after staging c + 1, so a whole chunk covers
+// their latency; their barriers wait only for the copies the next phase reads
+// (exact vmcnt counts: the loads and copies are issued unconditionally).
+// ---------------------------------------------------------------------------
+template <int NP>
+__global__ __launch_bounds__(kWalkThreads, 4) void k_walk_bfs(Args a) {
+    constexpr int NT = NP / 16;      // state tiles per matrix wave
+    constexpr int KB = NP / 32;      // 32-row blocks of the output contraction
+    constexpr int GPR = NP / 8;      // 16-byte pieces per row of C
+    constexpr int NDMA = NP / 32;    // 1 KB copies per staging wave for C or B^T
+    constexpr int CB = kRows * NP;   // bf16 elements of the C or B^T buffer
+    constexpr int MB = kRows * kRows;
+    constexpr uint32_t kOut = 0x80000000u;   // byte offset past any buffer: reads zero
+
+    __shared__ __attribute__((aligned(16))) bf16 sC[CB];
+    __shared__ __attribute__((aligned(16))) bf16 sBT[CB];
+    __shared__ __attribute__((aligned(16))) bf16 sXT[kPG * kRows];
+    __shared__ __attribute__((aligned(16))) bf16 sXdT[2][kPG * kRows];
+    __shared__ __attribute__((aligned(16))) bf16 sM[MB];
+    __shared__ float s_cum[2][kRows + 1];
+    __shared__ __attribute__((aligned(16))) float s_bc[4][2][kRows];   // per staging wave: cum, wl
+
+    // ---- workgroup -> (batch, segment, head, column group), as k_walk ------------
+    const int gsize = a.H * a.npg;
+    const int ngroups = (int)(gridDim.x / gsize);
+    const int id = blockIdx.x;
+    const int full = ngroups / 8 * 8 * gsize;
+    int grp, wi;
+    if (id < full) {
+        const int x = id % 8, k = id / 8;
+        grp = x + 8 * (k / gsize);
+        wi = k % gsize;
+    } else {
+        grp = id / gsize;
+        wi = id % gsize;
+    }
+    const int b = grp / a.nseg, seg = grp % a.nseg;
+    const int h = wi / a.npg, pg = wi % a.npg;
+    const int hg = h / (a.H / a.G);
+    const int p0 = pg * kPG;
+    const int c_begin = seg * a.cps;
+    const int c_end = min(a.nch, c_begin + a.cps);
+
+    const int tid = threadIdx.x, lane = tid % 64;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
+    const bool mma = wave < 4;         // uniform
+    const int pw = wave & 3;           // matrix wave: column block; staging wave: step block
+    const int li = lane % 16, lk = lane / 16;
+    const int pw_n = min(kPG, a.P - p0) / 16;
+    const bool active = mma && pw < pw_n;   // uniform
+    const int pcol = p0 + 16 * pw + li;
+    const Views<1, true, bf16> vw(a, b, h, hg);
+    const size_t sh_off = (size_t)(b * a.H + h) * a.N * a.P;
+    const size_t bt_rows = (size_t)a.nch * a.G * (NP * kRows);
+    const Buf BTbuf = make_buf(a.BT + (size_t)b * bt_rows, bt_rows * 2);
+    const Buf Sbuf = make_buf(a.S + (size_t)b * a.nch * a.G * MB, (size_t)a.nch * a.G * MB * 4);
+    // state row of tile t, row rho of the tile (rho = 4 lk + r in the accumulators)
+    auto srow = [](int t, int rho) { return 32 * (t >> 1) + 8 * (rho >> 2) + 4 * (t & 1) + (rho & 3); };
+
+    // ---- staging waves ------------------------------------------------------------
+    // LDS DMA of C and B^T of chunk c (the k_walk_bf copies, staging wave pw
+    // moving pieces 64 (pw + 4 m) + lane)
+    auto dma_c = [&](int c) {
+        const int t0g = c * kRows;
+        const int gi0 = 64 * pw + lane;
+        const int i0 = gi0 / GPR, g = (gi0 % GPR) ^ swz_c<NP>(i0);
+        const uint32_t base = opaque((uint32_t)(((t0g + i0) * vw.bc_step + vw.bc_head + 8 * g) * 2) |
+                                     (8 * g < a.N ? 0u : kOut));
+#pragma unroll
+        for (int m = 0; m < NDMA; ++m) {
+            const int q = pw + 4 * m;
+            const uint32_t off = base + (uint32_t)(m * (256 / GPR) * vw.bc_step * 2);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                vw.C.r, (__attribute__((address_space(3))) void*)(sC + 512 * q), 16, off, 0, 0, 0);
+        }
+    };
+    auto dma_bt = [&](int c) {
+        const int gi0 = 64 * pw + lane;
+        const int n0 = gi0 / 8, g = (gi0 % 8) ^ swz_bt(n0);
+        const uint32_t base = opaque((uint32_t)((((c * a.G + hg) * NP + n0) * kRows + 8 * g) * 2));
+#pragma unroll
+        for (int m = 0; m < NDMA; ++m) {
+            const int q = pw + 4 * m;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                BTbuf.r, (__attribute__((address_space(3))) void*)(sBT + 512 * q), 16,
+                base + (uint32_t)(m * 32 * kRows * 2), 0, 0, 0);
+        }
+    };
+    // registers of the next chunk: X column p0 + lane at steps 16 pw + i (raw bf16
+    // bits); score row `lane`, columns 16 pw .. + 15; log-decay of step `lane`.
+    // Lanes without a value read past the buffer (zeros), so the loads stay one
+    // straight block and the waits stay exact.
+    uint32_t px[16];
+    float psc[16], pld = 0.0f;
+    constexpr int kPf = 16 + 4 + 1;   // vector memory operations of one prefetch
+    const uint32_t xbad = p0 + lane < a.P ? 0u : kOut;
+    const uint32_t sbad = 16 * pw <= lane ? 0u : kOut;   // score rows before the block: masked
+    auto prefetch = [&](int c) {
+        const int t0g = c * kRows;
+        const uint32_t xo = opaque((uint32_t)(((t0g + 16 * pw) * vw.x_step + vw.x_head + p0 + lane) * 2));
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            px[i] = __builtin_amdgcn_raw_buffer_load_b16(vw.X.r, (xo + (uint32_t)(i * vw.x_step * 2)) | xbad, 0, 0);
+        // blocked score layout: columns 8 (2 pw + q) .. + 7 of row `lane`
+        const uint32_t so = (uint32_t)(((c * a.G + hg) * MB + (2 * pw) * (kRows * 8) + lane * 8) * 4);
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+            for (int v = 0; v < 2; ++v) {
+                const uintx4 u = __builtin_amdgcn_raw_buffer_load_b128(
+                    Sbuf.r, (so + (uint32_t)(q * kRows * 8 * 4 + v * 16)) | sbad, 0, 0);
+                psc[8 * q + 4 * v] = __uint_as_float(u.x);
+                psc[8 * q + 4 * v + 1] = __uint_as_float(u.y);
+                psc[8 * q + 4 * v + 2] = __uint_as_float(u.z);
+                psc[8 * q + 4 * v + 3] = __uint_as_float(u.w);
+            }
+        pld = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+            vw.ld.r, (uint32_t)(((t0g + lane) * a.H + h) * 4), 0, 0));
+    };
+    // X^T, Xd^T and M rows of chunk c: row `lane` (X column p0 + lane, score row
+    // `lane`), 16-byte pieces 2 pw and 2 pw + 1 (steps / columns 16 pw .. + 15)
+    auto stage = [&](int c) {
+        const float cum = wave_scan_dpp(pld);
+        const float cum_last = readlane_f(cum, kRows - 1);
+        const float wl = exp_e(cum_last - cum);   // chunk-end weight of step `lane`
+        if (pw == 0) {
+            s_cum[c & 1][lane + 1] = cum;
+            if (lane == 0) s_cum[c & 1][0] = 0.0f;
+        }
+        // the 16 steps of this wave's block, broadcast through the wave's own LDS slots
+        s_bc[pw][0][lane] = cum;
+        s_bc[pw][1][lane] = wl;
+        float cumv[16], wlv[16];
+#pragma unroll
+        for (int q = 0; q < 16; q += 4) {
+            const float4 u = *(const float4*)&s_bc[pw][0][16 * pw + q];
+            const float4 v = *(const float4*)&s_bc[pw][1][16 * pw + q];
+            cumv[q] = u.x; cumv[q + 1] = u.y; cumv[q + 2] = u.z; cumv[q + 3] = u.w;
+            wlv[q] = v.x; wlv[q + 1] = v.y; wlv[q + 2] = v.z; wlv[q + 3] = v.w;
+        }
+        uint32_t xv[8], xw[8], mv[8];
+#pragma unroll
+        for (int i = 0; i < 16; i += 2) {
+            const uint32_t lo = px[i] & 0xffffu, hi = px[i + 1] & 0xffffu;
+            xv[i / 2] = lo | (hi << 16);
+            xw[i / 2] = pack_bf(__uint_as_float(lo << 16) * wlv[i], __uint_as_float(hi << 16) * wlv[i + 1]);
+            const int t = 16 * pw + i;
+            const float e0 = exp_e(t <= lane ? cum - cumv[i] : 0.0f);
+            const float e1 = exp_e(t + 1 <= lane ? cum - cumv[i + 1] : 0.0f);
+            mv[i / 2] = pack_bf(t <= lane ? psc[i] * e0 : 0.0f, t + 1 <= lane ? psc[i + 1] * e1 : 0.0f);
+        }
+        bf16* xd = sXdT[c & 1];
+        const int sw = swz_m(lane);
+#pragma unroll
+        for (int g2 = 0; g2 < 2; ++g2) {
+            const int o = lane * kRows + 8 * ((2 * pw + g2) ^ sw);
+            *(uint4*)&sXT[o] = make_uint4(xv[4 * g2], xv[4 * g2 + 1], xv[4 * g2 + 2], xv[4 * g2 + 3]);
+            *(uint4*)&xd[o] = make_uint4(xw[4 * g2], xw[4 * g2 + 1], xw[4 * g2 + 2], xw[4 * g2 + 3]);
+            *(uint4*)&sM[o] = make_uint4(mv[4 * g2], mv[4 * g2 + 1], mv[4 * g2 + 2], mv[4 * g2 + 3]);
+        }
+    };
+
+    // ---- matrix waves: entering state (h0 and the earlier segments) -----------------
+    floatx4 acc_h[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc_h[t] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+    if (active) {
+        if (a.h0) {
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int n = srow(t, 4 * lk + r);
+                    acc_h[t][r] = n < a.N ? a.h0[sh_off + (size_t)n * a.P + pcol] : 0.0f;
+                }
+        }
+        for (int s2 = 0; s2 < seg; ++s2) {
+            const size_t u = (size_t)(b * a.H + h) * (a.nseg - 1) + s2;
+            const float d = exp_e(a.seg_ld[u]);
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int n = srow(t, 4 * lk + r);
+                    const float hl = n < a.N ? a.seg_h[(u * a.N + n) * a.P + pcol] : 0.0f;
+                    acc_h[t][r] = fmaf(d, acc_h[t][r], hl);
+                }
+        }
+    }
+
+    // A barrier with no wait for this wave's memory operations; the empty asm
+    // keeps the compiler from moving LDS accesses across it.
+    auto bare_barrier = []() {
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+    };
+    // A barrier after this wave's LDS writes have landed and at most kPf vector
+    // memory operations (the loads of a prefetch) are outstanding.
+    auto stage_barrier = []() {
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_waitcnt((kPf & 15) | (7 << 4) | (0 << 8) | ((kPf >> 4) << 14));
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+    };
+
+    // ---- first chunk ------------------------------------------------------------
+    if (mma) {
+        __syncthreads();
+    } else {
+        dma_c(c_begin);
+        prefetch(c_begin);
+        vm_wait<0>();
+        if (c_begin < c_end) stage(c_begin);
+        prefetch(c_begin + 1);
+        stage_barrier();
+    }
+
+    // The two roles run separate loops with the same three barriers per chunk.
+    if (mma) {
+        const int pr = 16 * pw + li;   // this lane's row of X^T and Xd^T
+        for (int c = c_begin; c < c_end; ++c) {
+            const int t0g = c * kRows;
+            // ---- phase 1: Y^T = H^T C^T, scaled by e^{cum} per step ---------------------
+            floatx4 acc_y[4];
+            if (active) {
+                // H^T as bf16 operand: rows 32 k + 8 lk .. + 7 from tiles 2k, 2k + 1
+                uintx4 hb[KB];
+#pragma unroll
+                for (int k = 0; k < KB; ++k)
+                    hb[k] = uintx4{pack_bf(acc_h[2 * k][0], acc_h[2 * k][1]), pack_bf(acc_h[2 * k][2], acc_h[2 * k][3]),
+                                   pack_bf(acc_h[2 * k + 1][0], acc_h[2 * k + 1][1]),
+                                   pack_bf(acc_h[2 * k + 1][2], acc_h[2 * k + 1][3])};
+#pragma unroll
+                for (int it = 0; it < 4; ++it) {
+                    const int i = 16 * it + li;
+                    floatx4 y0 = {0.0f, 0.0f, 0.0f, 0.0f}, y1 = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                    for (int k = 0; k < KB; ++k) {
+                        const uintx4 cv = *(const uintx4*)&sC[i * NP + 8 * ((4 * k + lk) ^ swz_c<NP>(i))];
+                        if (k % 2 == 0) y0 = mfma_bf(hb[k], cv, y0);
+                        else y1 = mfma_bf(hb[k], cv, y1);
+                    }
+                    acc_y[it] = (y0 + y1) * exp_e(s_cum[c & 1][i + 1]);
+                }
+            }
+            bare_barrier();
+            // ---- phase 2: Y^T += X^T M^T; store Y(c) -------------------------------------
+            if (active) {
+                uintx4 xo[2];
+#pragma unroll
+                for (int k = 0; k < 2; ++k) xo[k] = *(const uintx4*)&sXT[pr * kRows + 8 * ((4 * k + lk) ^ swz_m(pr))];
+#pragma unroll
+                for (int it = 0; it < 4; ++it) {
+                    const int i = 16 * it + li;
+#pragma unroll
+                    for (int k = 0; k < 2; ++k) {
+                        if (32 * k > 16 * it + 15) continue;   // above the diagonal
+                        const uintx4 mv = *(const uintx4*)&sM[i * kRows + 8 * ((4 * k + lk) ^ swz_m(i))];
+                        acc_y[it] = mfma_bf(xo[k], mv, acc_y[it]);
+                    }
+                }
+                // lane holds Y[t0 + 16 it + li][p0 + 16 w + 4 lk + r]
+#pragma unroll
+                for (int it = 0; it < 4; ++it) {
+                    const int tg = t0g + 16 * it + li;
+                    if (tg < a.L) {
+                        bf16* yrow = (bf16*)a.Y + (((size_t)b * a.L + tg) * a.H + h) * (size_t)a.P;
+                        *(uint2*)(yrow + p0 + 16 * pw + 4 * lk) =
+                            make_uint2(pack_bf(acc_y[it][0], acc_y[it][1]), pack_bf(acc_y[it][2], acc_y[it][3]));
+                    }
+                }
+            }
+            bare_barrier();
+            // ---- phase 3: H = e^{cum_last} H + B^T Xd -------------------------------------
+            if (active) {
+                const float tot = exp_e(s_cum[c & 1][kRows]);   // decay over this chunk
+#pragma unroll
+                for (int t = 0; t < NT; ++t) acc_h[t] *= tot;
+                const bf16* xdb = sXdT[c & 1];
+                uintx4 xd[2];
+#pragma unroll
+                for (int k = 0; k < 2; ++k) xd[k] = *(const uintx4*)&xdb[pr * kRows + 8 * ((4 * k + lk) ^ swz_m(pr))];
+#pragma unroll
+                for (int t = 0; t < NT; ++t) {
+                    const int n = srow(t, li);
+#pragma unroll
+                    for (int k = 0; k < 2; ++k) {
+                        const uintx4 bv = *(const uintx4*)&sBT[n * kRows + 8 * ((4 * k + lk) ^ swz_bt(n))];
+                        acc_h[t] = mfma_bf(bv, xd[k], acc_h[t]);
+                    }
+                }
+            }
+            bare_barrier();
+        }
+    } else {
+        // outstanding on entry to chunk c: the loads of chunk c + 1
+        for (int c = c_begin; c < c_end; ++c) {
+            // phase 1: B^T(c) -> LDS (read in phase 3)
+            dma_bt(c);
+            bare_barrier();
+            // phase 2: C(c + 1) -> LDS (C(c) was last read in phase 1); B^T(c) and
+            // the loads of c + 1 have landed before the barrier, C(c + 1) before the
+            // one closing phase 3
+            dma_c(c + 1);
+            vm_wait<NDMA>();
+            bare_barrier();
+            // phase 3: stage c + 1, then the loads of c + 2 (past the segment:
+            // unused; past the sequence: zeros)
+            if (c + 1 < c_end) stage(c + 1);
+            prefetch(c + 2);
+            stage_barrier();
+        }
+        vm_wait<0>();   // no copy into LDS may be in flight when the wave ends
+    }
+
+    if (a.h_out && seg == a.nseg - 1 && active) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int n = srow(t, 4 * lk + r);
+                if (n < a.N) a.h_out[sh_off + (size_t)n * a.P + pcol] = acc_h[t][r];
+            }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
 struct Plan {
@@ -2251,7 +2597,7 @@ mb_status launch(Args a, int64_t batch, const Plan& pl, char* ws, hipStream_t st
                 hipLaunchKernelGGL((k_walk_bf<NP, false, true>), dim3((unsigned)(per_seg * a.nseg)),
                                    dim3(kBfThreads), 0, stream, a);
             else
-                hipLaunchKernelGGL((k_walk_bf<NP, false>), dim3((unsigned)(per_seg * a.nseg)), dim3(kBfThreads),
+                hipLaunchKernelGGL((k_walk_bfs<NP>), dim3((unsigned)(per_seg * a.nseg)), dim3(kWalkThreads),
                                    0, stream, a);
             return check_launch();
         }
