@@ -812,6 +812,110 @@ def traffic_for(w):
     return rec.get("bytes_per_call")
 
 
+TRAFFIC_REPS = 3
+
+
+def traffic_run(mb, wl, torch):
+    """The calls the byte counters are read on: every workload in turn, called
+    TRAFFIC_REPS times between two one-element fills (marker kernels; the set-up
+    and first call of each workload fall outside them).  Prints the order, with
+    each workload's kernel source and algorithmic bytes, as one JSON line."""
+    order = []
+    for n in ALL + NEXT:
+        print("# traffic run: %s" % n, file=sys.stderr, flush=True)
+        w = make(n, mb, wl, torch)
+        w.run()   # first call outside the measured ones (library set-up, first-touch)
+        torch.cuda.synchronize()
+        torch.full((1,), 1.0, device="cuda")
+        for _ in range(TRAFFIC_REPS):
+            w.run()
+        torch.full((1,), 2.0, device="cuda")
+        torch.cuda.synchronize()
+        order.append({"name": n, "source": w.source, "bytes": getattr(w, "bytes", None)})
+        del w
+        torch.cuda.empty_cache()
+    print(json.dumps({"traffic_order": order, "reps": TRAFFIC_REPS}))
+    return 0
+
+
+def _counter_rows(d):
+    import csv
+    import glob
+    rows = []
+    for f in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
+        rows += list(csv.DictReader(open(f)))
+    rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+    return rows
+
+
+def traffic(run_log, fetch_dir, write_dir, cfetch_dir, cwrite_dir):
+    """profiles/traffic.json and a markdown table from four rocprofv3 counter
+    passes: FETCH_SIZE and WRITE_SIZE over `bench.py --traffic-run` (run_log: the
+    output of one such run, with its JSON line), and the same two over `bench.py
+    --copy-calibration` (a plain 256 MiB copy, whose bytes are known: the counters
+    are scaled so that they read them).  The traffic run's dispatches are split
+    into workloads at the marker fills (the segments after the first, third, ...
+    fill are the measured calls); a workload's bytes per call are the sum over
+    its dispatches divided by the number of calls."""
+    spec = None
+    for line in open(run_log):
+        if line.startswith("{") and "traffic_order" in line:
+            spec = json.loads(line)["traffic_order"]
+    if spec is None:
+        raise SystemExit("no traffic_order line in %s" % run_log)
+
+    def kib_by_kernel(rows):
+        return [(_short(r["Kernel_Name"]), float(r["Counter_Value"])) for r in rows]
+
+    def copy_kib(d):
+        v = [x for n, x in kib_by_kernel(_counter_rows(d)) if "copyBuffer" in n or "copy" in n.lower()]
+        return float(np.median(v))
+
+    copy_bytes = 256 << 20
+    ff = copy_bytes / 1024.0 / copy_kib(cfetch_dir)
+    wf = copy_bytes / 1024.0 / copy_kib(cwrite_dir)
+
+    def segments(d):
+        segs, cur = [], None
+        for n, v in kib_by_kernel(_counter_rows(d)):
+            if "FillFunctor" in n:
+                cur = []
+                segs.append(cur)
+            elif cur is not None:
+                cur.append((n, v))
+        return segs
+
+    order = [d["name"] for d in spec]
+    fs, ws_ = segments(fetch_dir)[0::2], segments(write_dir)[0::2]
+    if len(fs) != len(order) or len(ws_) != len(order):
+        raise SystemExit("counter runs hold %d / %d measured segments, expected %d" % (len(fs), len(ws_), len(order)))
+    out = {"_calibration": {"fetch_factor": ff, "write_factor": wf, "copy_bytes": copy_bytes,
+                            "copy_fetch_kib": copy_kib(cfetch_dir), "copy_write_kib": copy_kib(cwrite_dir)}}
+    lines = ["| workload | kernels | read MB | written MB | total MB | algorithmic MB | ratio |",
+             "|---|---|---:|---:|---:|---:|---:|"]
+    for d, f, w in zip(spec, fs, ws_):
+        n = d["name"]
+        rd = sum(v for _, v in f) * 1024 * ff / TRAFFIC_REPS
+        wr = sum(v for _, v in w) * 1024 * wf / TRAFFIC_REPS
+        kern = []
+        for k, _ in f:
+            if k not in kern:
+                kern.append(k)
+        alg = d["bytes"]
+        out[n] = {"bytes_per_call": int(rd + wr), "read_bytes": int(rd), "write_bytes": int(wr),
+                  "source": d["source"], "source_sha": source_hash(d["source"]), "kernels": kern}
+        lines.append("| %s | %s | %.1f | %.1f | %.1f | %s | %s |" % (
+            n, " + ".join("`%s`" % k for k in kern), rd / 1e6, wr / 1e6, (rd + wr) / 1e6,
+            "%.1f" % (alg / 1e6) if alg else "", "%.2f" % ((rd + wr) / alg) if alg else ""))
+    with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as fh:
+        json.dump(out, fh, indent=1, sort_keys=True)
+    print("Calibration: the plain 256 MiB device copy reads FETCH_SIZE = %.0f KiB and WRITE_SIZE = %.0f KiB per "
+          "dispatch, so FETCH_SIZE is scaled by %.4f and WRITE_SIZE by %.4f (bytes = KiB x 1024 x factor).\n"
+          % (copy_kib(cfetch_dir), copy_kib(cwrite_dir), ff, wf))
+    print("\n".join(lines))
+    return 0
+
+
 # ----------------------------------------------------------------------------
 # CPU baseline: the fp64 oracle on the host cores
 # ----------------------------------------------------------------------------
@@ -967,7 +1071,9 @@ def summarize(paths):
     Kernel trace: every dispatch before the first cache flush (a reduction over
     the 512 MiB flush buffer) is in the warm phase (warm-up and back-to-back
     calls); every dispatch after it is in the flushed phase (each workload call
-    follows a flush).  The flush kernels and torch's fills are left out.
+    follows a flush).  Dispatches are grouped by kernel and launch size
+    (workgroups), which tells apart the workloads that share a kernel.  The
+    flush kernels and torch's fills are left out.
     Counter collection: the mean per dispatch of each counter, with the MFMA
     busy fraction (SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE / 8 XCDs x
     1024 SIMDs), the VALU busy fraction of a wave's life (SQ_ACTIVE_INST_VALU /
@@ -989,13 +1095,16 @@ def summarize(paths):
                 if "FillFunctor" in name:
                     continue
                 us = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
-                stats.setdefault((name, phase), []).append(us)
+                wg = 1
+                for ax in "XYZ":
+                    wg *= max(1, int(r["Grid_Size_" + ax]) // max(1, int(r["Workgroup_Size_" + ax])))
+                stats.setdefault((name, wg, phase), []).append(us)
             out.append("Kernel trace `%s`\n" % os.path.relpath(f, d))
-            out.append("| kernel | phase | calls | avg µs | median µs | min µs | max µs |")
-            out.append("|---|---|---:|---:|---:|---:|---:|")
-            for (name, ph), v in sorted(stats.items(), key=lambda kv: (kv[0][0], kv[0][1] != "flushed")):
-                out.append("| `%s` | %s | %d | %.2f | %.2f | %.2f | %.2f |" % (
-                    name, ph, len(v), np.mean(v), np.median(v), np.min(v), np.max(v)))
+            out.append("| kernel | workgroups | phase | calls | avg µs | median µs | min µs | max µs |")
+            out.append("|---|---:|---|---:|---:|---:|---:|---:|")
+            for (name, wg, ph), v in sorted(stats.items(), key=lambda kv: (kv[0][0], kv[0][1], kv[0][2] != "flushed")):
+                out.append("| `%s` | %d | %s | %d | %.2f | %.2f | %.2f | %.2f |" % (
+                    name, wg, ph, len(v), np.mean(v), np.median(v), np.min(v), np.max(v)))
             out.append("")
     # counters: every counter file of every directory in one table (one pass per
     # directory; a kernel's mean per dispatch in each)
@@ -1053,9 +1162,15 @@ def main():
                     help="only run a plain 256 MiB device copy (reference for rocprofv3 byte counters)")
     ap.add_argument("--summarize", nargs="+", metavar="DIR",
                     help="print markdown summaries of rocprofv3 csv output directories and exit")
+    ap.add_argument("--traffic-run", action="store_true",
+                    help="only run every workload behind a marker fill (the calls the byte counters read)")
+    ap.add_argument("--traffic", nargs=5, metavar=("RUN_LOG", "FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
+                    help="write profiles/traffic.json from the byte-counter passes and print a table")
     args = ap.parse_args()
     if args.summarize:
         return summarize(args.summarize)
+    if args.traffic:
+        return traffic(*args.traffic)
     if args.gpus != 1:
         print("bench.py measures one GPU; this library has no multi-GPU path (run with --gpus 1)",
               file=sys.stderr)
@@ -1071,6 +1186,8 @@ def main():
     if args.copy_calibration:
         return copy_calibration(torch)
     mb.load_library()
+    if args.traffic_run:
+        return traffic_run(mb, wl, torch)
     names = [n for n in (args.only.split(",") if args.only else ALL) if n]
     ws = []
     for n in names:
