@@ -2184,7 +2184,7 @@ __global__ __launch_bounds__(kBfThreads, 2) void k_walk_bf(Args a) {
 // their latency; their barriers wait only for the copies the next phase reads
 // (exact vmcnt counts: the loads and copies are issued unconditionally).
 // ---------------------------------------------------------------------------
-template <int NP>
+template <int NP, bool EPI = false>
 __global__ __launch_bounds__(kWalkThreads, 4) void k_walk_bfs(Args a) {
     constexpr int NT = NP / 16;      // state tiles per matrix wave
     constexpr int KB = NP / 32;      // 32-row blocks of the output contraction
@@ -2403,6 +2403,22 @@ __global__ __launch_bounds__(kWalkThreads, 4) void k_walk_bfs(Args a) {
         const int pr = 16 * pw + li;   // this lane's row of X^T and Xd^T
         for (int c = c_begin; c < c_end; ++c) {
             const int t0g = c * kRows;
+            // output side: X and z of this lane's outputs, loaded now under the
+            // chunk's products and held as packed bf16 (two registers per four values)
+            uint2 rx[4] = {}, rz[4] = {};
+            if constexpr (EPI) {
+                if (active) {
+#pragma unroll
+                    for (int it = 0; it < 4; ++it) {
+                        const int tg = t0g + 16 * it + li;
+                        if (tg < a.L) {
+                            const size_t e = (((size_t)b * a.L + tg) * a.H + h) * (size_t)a.P + p0 + 16 * pw + 4 * lk;
+                            if (a.Dh) rx[it] = *(const uint2*)((const bf16*)a.X + e);
+                            if (a.Zg) rz[it] = *(const uint2*)((const bf16*)a.Zg + e);
+                        }
+                    }
+                }
+            }
             // ---- phase 1: Y^T = H^T C^T, scaled by e^{cum} per step ---------------------
             floatx4 acc_y[4];
             if (active) {
@@ -2447,9 +2463,25 @@ __global__ __launch_bounds__(kWalkThreads, 4) void k_walk_bfs(Args a) {
                 for (int it = 0; it < 4; ++it) {
                     const int tg = t0g + 16 * it + li;
                     if (tg < a.L) {
+                        float yv[4] = {acc_y[it][0], acc_y[it][1], acc_y[it][2], acc_y[it][3]};
+                        if constexpr (EPI) {
+                            // (y + Dh x) SiLU(z); the two-pass Mamba-2 layer takes x = X / dt'
+                            float dh = a.Dh ? a.Dh[h] : 0.0f;
+                            if (a.skip_dt) dh /= a.skip_dt[((size_t)b * a.L + tg) * a.H + h];
+                            const float ex[4] = {__uint_as_float(rx[it].x << 16), __uint_as_float(rx[it].x & 0xffff0000u),
+                                                 __uint_as_float(rx[it].y << 16), __uint_as_float(rx[it].y & 0xffff0000u)};
+                            const float ez[4] = {__uint_as_float(rz[it].x << 16), __uint_as_float(rz[it].x & 0xffff0000u),
+                                                 __uint_as_float(rz[it].y << 16), __uint_as_float(rz[it].y & 0xffff0000u)};
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) {
+                                const float v = fmaf(dh, ex[r], yv[r]);
+                                const float sg = ez[r] * __builtin_amdgcn_rcpf(1.0f + exp2_fast(-ez[r] * kLog2e));
+                                yv[r] = a.Zg ? v * sg : v;
+                            }
+                        }
                         bf16* yrow = (bf16*)a.Y + (((size_t)b * a.L + tg) * a.H + h) * (size_t)a.P;
                         *(uint2*)(yrow + p0 + 16 * pw + 4 * lk) =
-                            make_uint2(pack_bf(acc_y[it][0], acc_y[it][1]), pack_bf(acc_y[it][2], acc_y[it][3]));
+                            make_uint2(pack_bf(yv[0], yv[1]), pack_bf(yv[2], yv[3]));
                     }
                 }
             }
@@ -2594,8 +2626,8 @@ mb_status launch(Args a, int64_t batch, const Plan& pl, char* ws, hipStream_t st
                 if (st != MB_OK) return st;
             }
             if (a.Dh || a.Zg)
-                hipLaunchKernelGGL((k_walk_bf<NP, false, true>), dim3((unsigned)(per_seg * a.nseg)),
-                                   dim3(kBfThreads), 0, stream, a);
+                hipLaunchKernelGGL((k_walk_bfs<NP, true>), dim3((unsigned)(per_seg * a.nseg)), dim3(kWalkThreads),
+                                   0, stream, a);
             else
                 hipLaunchKernelGGL((k_walk_bfs<NP>), dim3((unsigned)(per_seg * a.nseg)), dim3(kWalkThreads),
                                    0, stream, a);
