@@ -40,6 +40,9 @@
 //             four matrix waves hold the state and do every product, four
 //             staging waves copy B and C into LDS and stage X and the masked
 //             scores of the next chunk.
+//   k_walk_bfs  (Mamba-2, bf16 full pass) the same split on the bf16 matrix
+//             instruction; k_walk_bf is its state-only pass.
+//   k_pad     zero-padded copies for Mamba-2 shapes outside the walks' tiles.
 //   k_walk    one workgroup (8 waves) per (batch, head, segment, 64 state
 //             columns), walking the segment's chunks in order.  Per chunk the
 //             workgroup stages B~ and C~ (rotated once, for all columns), X and
@@ -50,12 +53,14 @@
 //             the accumulator tiles so that the accumulators are directly the
 //             operand of the next chunk's C~ H product: the state never leaves
 //             registers.
-//             Two SISO variants carry the Mamba-3 block's ends
-//             (mamba3-minimal README, Architecture): EPI (full pass) loads X
-//             and the gate z at the chunk's start and stores
+//             Two variants carry the Mamba-3 block's ends for SISO and MIMO
+//             ranks 1 and 4 (mamba3-minimal README, Architecture): EPI (full
+//             pass) loads X and the gate z at the chunk's start and stores
 //             (y + D_h x) SiLU(z); BCN (both passes) turns each raw B, C row
 //             in the prefetch registers into row / rms(row) * weight + bias_h
-//             (one DPP sum over the row's wave) before the rotations.
+//             (one DPP sum over the row's wave) before the rotations.  PRO
+//             (Mamba-2 state-only pass of the layer) convolves x as it stages
+//             it.
 // All global reads go through buffer resources that cover one batch row of a
 // tensor, so reads before the first or after the last step return zero in
 // hardware and the hot loops carry no bounds branches.
@@ -1683,23 +1688,20 @@ __global__ __launch_bounds__(kWalkThreads) void k_walk_m2s(Args a) {
 }
 
 // ---------------------------------------------------------------------------
-// Mamba-2 walk with bf16 inputs on the bf16 matrix instruction (SO = state-only
-// pre-pass).  Four waves, one workgroup per (batch, segment, head, 64 columns);
-// wave w owns state columns p0 + 16 w .. + 15 for all NP state rows in NT =
-// NP/16 fp32 accumulator tiles, and computes the output for those columns.
-// The state stays fp32 and is rounded to bf16 only as an operand of the output
-// product.  Tile t, register r of lane (li, lk) holds state row
-//     n = 32 (t / 2) + 8 lk + 4 (t % 2) + r,
-// so that tiles 2k and 2k + 1 are directly the eight consecutive rows 32 k +
-// 8 lk .. + 7 that lane group lk supplies to the output product.  Per chunk:
-//   Y^T = H^T C^T x e^{cum} + X^T M^T        (M: masked scores, bf16)
-//   H   = e^{cum_last} H + B^T Xd            (Xd = X weighted to the chunk end)
-// C and B^T (a transposed copy that k_scores writes) come into double-buffered
-// LDS by LDS DMA; X is loaded straight into operand registers (the eight steps
-// of a lane group per register quad), and the masked scores are built once per
-// chunk in LDS by all waves.  One workgroup barrier per chunk: every buffer a
-// chunk reads is written before that chunk's barrier and rewritten only after
-// the next one.
+// Mamba-2 state-only pass with bf16 inputs on the bf16 matrix instruction: the
+// local end state of every sequence segment but the last, for the full pass
+// (k_walk_bfs) to compose.  Four waves, one workgroup per (batch, segment,
+// head, 64 columns); wave w owns state columns p0 + 16 w .. + 15 for all NP
+// state rows in NT = NP/16 fp32 accumulator tiles.  Tile t, register r of lane
+// (li, lk) holds state row
+//     n = 32 (t / 2) + 8 lk + 4 (t % 2) + r
+// (the layout k_walk_bfs uses).  Per chunk:
+//   H = e^{cum_last} H + B^T Xd            (Xd = X weighted to the chunk end)
+// B^T (a transposed copy that k_scores writes) comes into double-buffered LDS
+// by LDS DMA; X is loaded straight into operand registers (the eight steps of
+// a lane group per register quad).  One workgroup barrier per chunk: every
+// buffer a chunk reads is written before that chunk's barrier and rewritten
+// only after the next one.
 // ---------------------------------------------------------------------------
 constexpr int kBfThreads = 256;
 
@@ -1721,17 +1723,11 @@ __device__ __forceinline__ int swz_bt(int n) {   // B^T: rows n of 8 pieces, rea
     return ((n & 3) | (((n >> 3) & 1) << 2)) ^ ((n >> 4) & 1);
 }
 
-template <int NP, bool SO, bool EPI = false, bool PRO = false>
+template <int NP>
 __global__ __launch_bounds__(kBfThreads, 2) void k_walk_bf(Args a) {
-    static_assert(!PRO || SO || EPI, "the block's full pass stores through the output side");
-    constexpr bool FULL = !SO;
     constexpr int NT = NP / 16;      // state tiles per wave
-    constexpr int KB = NP / 32;      // 32-row blocks of the state contraction
-    constexpr int GPR = NP / 8;      // 16-byte pieces per row of C
-    constexpr int NDMA = NP / 32;    // 1 KB copies per wave for C or B^T
-    constexpr int CB = kRows * NP;   // bf16 elements of one C or B^T buffer
-    constexpr int MB = kRows * kRows;
-    constexpr uint32_t kOut = 0x80000000u;   // byte offset past any buffer: reads zero
+    constexpr int NDMA = NP / 32;    // 1 KB copies per wave for B^T
+    constexpr int CB = kRows * NP;   // bf16 elements of one B^T buffer
 
     // Double buffers as separate objects, and the chunk loop unrolled by two so
     // that every access names its buffer at compile time: the compiler then sees
@@ -1739,13 +1735,9 @@ __global__ __launch_bounds__(kBfThreads, 2) void k_walk_bf(Args a) {
     // wait for the copies of the next chunk before reading this one.
     __shared__ __attribute__((aligned(16))) bf16 sBT0[CB];
     __shared__ __attribute__((aligned(16))) bf16 sBT1[CB];
-    __shared__ __attribute__((aligned(16))) bf16 sC0[FULL ? CB : 8];
-    __shared__ __attribute__((aligned(16))) bf16 sC1[FULL ? CB : 8];
-    __shared__ __attribute__((aligned(16))) bf16 sM0[FULL ? MB : 8];
-    __shared__ __attribute__((aligned(16))) bf16 sM1[FULL ? MB : 8];
 
     // ---- workgroup -> (batch, segment, head, column group), as k_walk ------------
-    const int nsegL = SO ? a.nseg - 1 : a.nseg;
+    const int nsegL = a.nseg - 1;
     const int gsize = a.H * a.npg;
     const int ngroups = (int)(gridDim.x / gsize);
     const int id = blockIdx.x;
@@ -1772,41 +1764,19 @@ __global__ __launch_bounds__(kBfThreads, 2) void k_walk_bf(Args a) {
     const bool active = 16 * wave < a.P - p0;   // uniform (P is a multiple of 16)
     const int pcol = p0 + 16 * wave + li;
     const Views<1, true, bf16> vw(a, b, h, hg);
-    const size_t sh_off = (size_t)(b * a.H + h) * a.N * a.P;
     const size_t bt_rows = (size_t)a.nch * a.G * (NP * kRows);
     const Buf BTbuf = make_buf(a.BT + (size_t)b * bt_rows, bt_rows * 2);
-    const Buf Sbuf = FULL ? make_buf(a.S + (size_t)b * a.nch * a.G * MB, (size_t)a.nch * a.G * MB * 4)
-                          : make_buf(a.ld, 0);
     // state row of tile t, row rho of the tile (rho = 4 lk + r in the accumulators)
     auto srow = [](int t, int rho) { return 32 * (t >> 1) + 8 * (rho >> 2) + 4 * (t & 1) + (rho & 3); };
 
-    // ---- LDS DMA of C and B^T of chunk c into buffer PB: wave w moves pieces
-    // 64 (w + 4 m) + lane ------------------------------------------------------------
-    auto dma_c = [&](int c, auto par) {
-        constexpr int PB = decltype(par)::value;
-        const int t0g = c * kRows;
-        bf16* dst;
-        if constexpr (PB) dst = sC1;
-        else dst = sC0;
-        // piece m is row i0 + (4 m)(64 / GPR) of the same swizzled column group
-        const int gi0 = 64 * wave + lane;
-        const int i0 = gi0 / GPR, g = (gi0 % GPR) ^ swz_c<NP>(i0);
-        const uint32_t base = opaque((uint32_t)(((t0g + i0) * vw.bc_step + vw.bc_head + 8 * g) * 2) |
-                                     (8 * g < a.N ? 0u : kOut));
-#pragma unroll
-        for (int m = 0; m < NDMA; ++m) {
-            const int q = wave + 4 * m;
-            const uint32_t off = base + (uint32_t)(m * (256 / GPR) * vw.bc_step * 2);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                vw.C.r, (__attribute__((address_space(3))) void*)(dst + 512 * q), 16, off, 0, 0, 0);
-        }
-    };
+    // ---- LDS DMA of B^T of chunk c into buffer PB: wave w moves pieces
+    // 64 (w + 4 m) + lane; piece m is row n0 + 32 m of the same swizzled column
+    // group --------------------------------------------------------------------------
     auto dma_bt = [&](int c, auto par) {
         constexpr int PB = decltype(par)::value;
         bf16* dst;
         if constexpr (PB) dst = sBT1;
         else dst = sBT0;
-        // piece m is row n0 + 32 m of the same swizzled column group
         const int gi0 = 64 * wave + lane;
         const int n0 = gi0 / 8, g = (gi0 % 8) ^ swz_bt(n0);
         const uint32_t base = opaque((uint32_t)((((c * a.G + hg) * NP + n0) * kRows + 8 * g) * 2));
@@ -1819,30 +1789,9 @@ __global__ __launch_bounds__(kBfThreads, 2) void k_walk_bf(Args a) {
         }
     };
 
-    // ---- masked-score items of this thread: causal (row, 8-column block) pairs,
-    // numbered row block by row block; 288 of them, so thread t takes item t and
-    // threads 0..31 also item 256 + t ------------------------------------------
-    int mi[2], mj[2];
-#pragma unroll
-    for (int m = 0; m < 2; ++m) {
-        const int k = m == 0 ? tid : min(256 + tid, 287);
-        int r = 0;
-        while (r < 7 && 4 * (r + 1) * (r + 2) <= k) ++r;
-        const int loc = k - 4 * r * (r + 1);
-        mi[m] = 8 * r + loc / (r + 1);
-        mj[m] = loc % (r + 1);
-    }
-    const bool m2 = tid < 32;
-
     // ---- prefetch registers -------------------------------------------------------
     uint32_t px[16];     // X[32 k + 8 lk + q][pcol] (k = q / 8): raw bf16 bits
-    float ps[2][8];      // scores of the items
     float pld = 0.0f;    // log-decay of step `lane`
-    // block prologue: raw x of the three steps before each run of eight, dt' of step `lane`
-    float pxh[2][3] = {{0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f}}, pdt = 0.0f;
-    const Buf dtpb = PRO ? make_buf(a.dtp + (size_t)b * a.L * a.H, (size_t)a.L * a.H * 4) : make_buf(a.ld, 0);
-    float cw4[4] = {0.0f, 0.0f, 0.0f, 0.0f}, cwb = 0.0f;
-    if constexpr (PRO) conv_taps(a, h * a.P + pcol, active, cw4, &cwb);
     const uint32_t xlane = (uint32_t)(((8 * lk) * vw.x_step + vw.x_head + pcol) * 2);
     auto prefetch = [&](int c) {
         const int t0g = c * kRows;
@@ -1854,263 +1803,45 @@ __global__ __launch_bounds__(kBfThreads, 2) void k_walk_bf(Args a) {
             for (int q = 0; q < 16; ++q)
                 px[q] = __builtin_amdgcn_raw_buffer_load_b16(
                     vw.X.r, xo + (uint32_t)((32 * (q / 8) + q % 8) * vw.x_step * 2), 0, 0);
-            if constexpr (PRO) {
-                const int ch = h * a.P + pcol;
-#pragma unroll
-                for (int k = 0; k < 2; ++k)
-#pragma unroll
-                    for (int j = 0; j < 3; ++j) {
-                        const int t = t0g + 32 * k + 8 * lk - 3 + j;
-                        pxh[k][j] = t < 0 ? hist_in<bf16>(a, b, t, ch)
-                                          : __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(
-                                                vw.X.r, (uint32_t)((t * vw.x_step + ch) * 2), 0, 0) << 16);
-                    }
-            }
-        }
-        if constexpr (PRO) pdt = bload<float>(dtpb, (t0g + lane) * a.H + h);
-        if constexpr (FULL) {
-#pragma unroll
-            for (int m = 0; m < 2; ++m) {
-                if (m == 1 && !m2) continue;
-                const uint32_t so = (uint32_t)(((c * a.G + hg) * MB + mj[m] * (kRows * 8) + mi[m] * 8) * 4);
-                const uintx4 u0 = __builtin_amdgcn_raw_buffer_load_b128(Sbuf.r, so, 0, 0);
-                const uintx4 u1 = __builtin_amdgcn_raw_buffer_load_b128(Sbuf.r, so + 16, 0, 0);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    ps[m][e] = __uint_as_float(u0[e]);
-                    ps[m][4 + e] = __uint_as_float(u1[e]);
-                }
-            }
         }
         pld = bload<float>(vw.ld, (t0g + lane) * a.H + h);
     };
 
-    // ---- state: h0 and the earlier segments --------------------------------------
     floatx4 acc_h[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc_h[t] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
-    if constexpr (FULL) if (active) {
-        if (a.h0) {
-#pragma unroll
-            for (int t = 0; t < NT; ++t)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int n = srow(t, 4 * lk + r);
-                    acc_h[t][r] = n < a.N ? a.h0[sh_off + (size_t)n * a.P + pcol] : 0.0f;
-                }
-        }
-        for (int s2 = 0; s2 < seg; ++s2) {
-            const size_t u = (size_t)(b * a.H + h) * (a.nseg - 1) + s2;
-            const float d = exp_e(a.seg_ld[u]);
-#pragma unroll
-            for (int t = 0; t < NT; ++t)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int n = srow(t, 4 * lk + r);
-                    const float hl = n < a.N ? a.seg_h[(u * a.N + n) * a.P + pcol] : 0.0f;
-                    acc_h[t][r] = fmaf(d, acc_h[t][r], hl);
-                }
-        }
-    }
-
-    // the score blocks above the diagonal stay zero in both buffers
-    if constexpr (FULL) {
-#pragma unroll
-        for (int m = 0; m < 2; ++m) {
-            const int e = tid + 256 * m;
-            const int i = e / 8, jb = e % 8;
-            if (8 * jb > i) {
-                *(uint4*)&sM0[i * kRows + 8 * (jb ^ swz_m(i))] = make_uint4(0, 0, 0, 0);
-                *(uint4*)&sM1[i * kRows + 8 * (jb ^ swz_m(i))] = make_uint4(0, 0, 0, 0);
-            }
-        }
-    }
 
     if (c_begin < c_end) {
-        if constexpr (FULL) dma_c(c_begin, Par<0>{});
         dma_bt(c_begin, Par<0>{});
         prefetch(c_begin);
     }
-    float seg_acc = 0.0f;   // state-only pass: total log-decay of the segment
+    float seg_acc = 0.0f;   // total log-decay of the segment
 
     // one chunk; its operands sit in buffer PB, the next chunk's go to 1 - PB
     auto chunk = [&](int c, auto par) __attribute__((always_inline)) {
         constexpr int PB = decltype(par)::value;
-        const int t0g = c * kRows;
         vm_wait<0>();   // this wave's copies and loads of chunk c
         const float cum = wave_scan_dpp(pld);
         const float cum_last = readlane_f(cum, kRows - 1);
-        if constexpr (SO) seg_acc += cum_last;
+        seg_acc += cum_last;
         const float wl = exp_e(cum_last - cum);   // chunk-end weight of step `lane`
-        // X operands: xo = X, xd = X weighted to the chunk end (steps 32 k + 8 lk + q)
-        uintx4 xo[2], xd[2];
-        if constexpr (PRO) {
-            // block prologue: convolved, activated x (zero past the sequence) as the
-            // operand, dt' with the chunk-end weights
-#pragma unroll
-            for (int k = 0; k < 2; ++k) {
-                float win[3] = {pxh[k][0], pxh[k][1], pxh[k][2]};
-                float xc[8];
-#pragma unroll
-                for (int q = 0; q < 8; ++q) {
-                    const float v = __uint_as_float((px[8 * k + q] & 0xffffu) << 16);
-                    const float pre = fmaf(cw4[3], v, fmaf(cw4[2], win[2], fmaf(cw4[1], win[1], fmaf(cw4[0], win[0], cwb))));
-                    win[0] = win[1];
-                    win[1] = win[2];
-                    win[2] = v;
-                    xc[q] = (active && t0g + 32 * k + 8 * lk + q < a.L) ? silu_acc(pre) : 0.0f;
-                }
-#pragma unroll
-                for (int q2 = 0; q2 < 4; ++q2) {
-                    const int t = 32 * k + 8 * lk + 2 * q2;
-                    xo[k][q2] = pack_bf(xc[2 * q2], xc[2 * q2 + 1]);
-                    const float w0 = __shfl(wl, t, 64) * __shfl(pdt, t, 64);
-                    const float w1 = __shfl(wl, t + 1, 64) * __shfl(pdt, t + 1, 64);
-                    xd[k][q2] = pack_bf(xc[2 * q2] * w0, xc[2 * q2 + 1] * w1);
-                }
-            }
-        } else {
+        // Xd: X weighted to the chunk end (steps 32 k + 8 lk + q)
+        uintx4 xd[2];
 #pragma unroll
         for (int k = 0; k < 2; ++k)
 #pragma unroll
             for (int q2 = 0; q2 < 4; ++q2) {
                 const uint32_t lo = px[8 * k + 2 * q2] & 0xffffu, hi = px[8 * k + 2 * q2 + 1] & 0xffffu;
-                xo[k][q2] = lo | (hi << 16);
                 const int t = 32 * k + 8 * lk + 2 * q2;
                 const float w0 = __shfl(wl, t, 64), w1 = __shfl(wl, t + 1, 64);
                 xd[k][q2] = pack_bf(__uint_as_float(lo << 16) * w0, __uint_as_float(hi << 16) * w1);
             }
-        }
-        float ey[4];
-        if constexpr (FULL) {
-            // masked scores M[i][j] = S[i][j] e^{cum_i - cum_j}, j <= i, into buffer PB
-            bf16* mb;
-            if constexpr (PB) mb = sM1;
-            else mb = sM0;
-#pragma unroll
-            for (int m = 0; m < 2; ++m) {
-                // the lane reads run with all lanes on (a read from a lane that is
-                // off returns zero)
-                const int i = mi[m], jb = mj[m];
-                const float ci = __shfl(cum, i, 64);
-                float cjs[8], djs[8];
-#pragma unroll
-                for (int q = 0; q < 8; ++q) cjs[q] = __shfl(cum, 8 * jb + q, 64);
-                if constexpr (PRO) {
-#pragma unroll
-                    for (int q = 0; q < 8; ++q) djs[q] = __shfl(pdt, 8 * jb + q, 64);
-                }
-                if (m == 1 && !m2) continue;
-                float mv[8];
-                const float dh = (PRO && a.Dh) ? a.Dh[h] : 0.0f;
-#pragma unroll
-                for (int q = 0; q < 8; ++q) {
-                    const int j = 8 * jb + q;
-                    const float cj = cjs[q];
-                    const bool ok = j <= i;
-                    const float e = exp_e(ok ? ci - cj : 0.0f);
-                    if constexpr (PRO)   // dt' of the input step; the skip term on the diagonal
-                        mv[q] = ok ? fmaf(ps[m][q] * e, djs[q], j == i ? dh : 0.0f) : 0.0f;
-                    else
-                        mv[q] = ok ? ps[m][q] * e : 0.0f;
-                }
-                *(uint4*)&mb[i * kRows + 8 * (jb ^ swz_m(i))] =
-                    make_uint4(pack_bf(mv[0], mv[1]), pack_bf(mv[2], mv[3]), pack_bf(mv[4], mv[5]),
-                               pack_bf(mv[6], mv[7]));
-            }
-            // decay of the entering state at the output rows 16 it + li
-#pragma unroll
-            for (int it = 0; it < 4; ++it) ey[it] = exp_e(__shfl(cum, 16 * it + li, 64));
-        }
         __syncthreads();
         if (c + 1 < c_end) {
-            if constexpr (FULL) dma_c(c + 1, Par<1 - PB>{});
             dma_bt(c + 1, Par<1 - PB>{});
             prefetch(c + 1);
         }
         if (active) {
-            if constexpr (FULL) {
-                // output side: X and z of this lane's outputs, loaded ahead of the
-                // products and held as packed bf16 (two registers per four values)
-                uint2 rx[4] = {}, rz[4] = {};
-                if constexpr (EPI) {
-#pragma unroll
-                    for (int it = 0; it < 4; ++it) {
-                        const int tg = t0g + 16 * it + li;
-                        if (tg < a.L) {
-                            const size_t e = (((size_t)b * a.L + tg) * a.H + h) * (size_t)a.P + p0 + 16 * wave + 4 * lk;
-                            if (!PRO && a.Dh) rx[it] = *(const uint2*)((const bf16*)a.X + e);
-                            if (a.Zg) rz[it] = *(const uint2*)((const bf16*)a.Zg + e);
-                        }
-                    }
-                }
-                const bf16* cb;
-                const bf16* mb;
-                if constexpr (PB) {
-                    cb = sC1;
-                    mb = sM1;
-                } else {
-                    cb = sC0;
-                    mb = sM0;
-                }
-                // H^T as bf16 operand: rows 32 k + 8 lk .. + 7 from tiles 2k, 2k + 1
-                uintx4 hb[KB];
-#pragma unroll
-                for (int k = 0; k < KB; ++k)
-                    hb[k] = uintx4{pack_bf(acc_h[2 * k][0], acc_h[2 * k][1]), pack_bf(acc_h[2 * k][2], acc_h[2 * k][3]),
-                                   pack_bf(acc_h[2 * k + 1][0], acc_h[2 * k + 1][1]),
-                                   pack_bf(acc_h[2 * k + 1][2], acc_h[2 * k + 1][3])};
-                floatx4 acc_y[4];
-#pragma unroll
-                for (int it = 0; it < 4; ++it) {
-                    const int i = 16 * it + li;
-                    floatx4 y0 = {0.0f, 0.0f, 0.0f, 0.0f}, y1 = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-                    for (int k = 0; k < KB; ++k) {
-                        const uintx4 cv = *(const uintx4*)&cb[i * NP + 8 * ((4 * k + lk) ^ swz_c<NP>(i))];
-                        if (k % 2 == 0) y0 = mfma_bf(hb[k], cv, y0);
-                        else y1 = mfma_bf(hb[k], cv, y1);
-                    }
-                    acc_y[it] = (y0 + y1) * ey[it];
-                }
-#pragma unroll
-                for (int it = 0; it < 4; ++it) {
-                    const int i = 16 * it + li;
-#pragma unroll
-                    for (int k = 0; k < 2; ++k) {
-                        if (32 * k > 16 * it + 15) continue;   // above the diagonal
-                        const uintx4 mv = *(const uintx4*)&mb[i * kRows + 8 * ((4 * k + lk) ^ swz_m(i))];
-                        acc_y[it] = mfma_bf(xo[k], mv, acc_y[it]);
-                    }
-                }
-                // lane holds Y[t0 + 16 it + li][p0 + 16 w + 4 lk + r]
-#pragma unroll
-                for (int it = 0; it < 4; ++it) {
-                    const int tg = t0g + 16 * it + li;
-                    if (tg < a.L) {
-                        float yv[4] = {acc_y[it][0], acc_y[it][1], acc_y[it][2], acc_y[it][3]};
-                        if constexpr (EPI) {
-                            // (y + Dh x) SiLU(z) (block prologue: the skip term is already in y;
-                            // two-pass layer: x = X / dt')
-                            float dh = (!PRO && a.Dh) ? a.Dh[h] : 0.0f;
-                            if (!PRO && a.skip_dt) dh /= a.skip_dt[((size_t)b * a.L + tg) * a.H + h];
-                            const float ex[4] = {__uint_as_float(rx[it].x << 16), __uint_as_float(rx[it].x & 0xffff0000u),
-                                                 __uint_as_float(rx[it].y << 16), __uint_as_float(rx[it].y & 0xffff0000u)};
-                            const float ez[4] = {__uint_as_float(rz[it].x << 16), __uint_as_float(rz[it].x & 0xffff0000u),
-                                                 __uint_as_float(rz[it].y << 16), __uint_as_float(rz[it].y & 0xffff0000u)};
-#pragma unroll
-                            for (int r = 0; r < 4; ++r) {
-                                const float v = fmaf(dh, ex[r], yv[r]);
-                                const float sg = ez[r] * __builtin_amdgcn_rcpf(1.0f + exp2_fast(-ez[r] * kLog2e));
-                                yv[r] = a.Zg ? v * sg : v;
-                            }
-                        }
-                        bf16* yrow = (bf16*)a.Y + (((size_t)b * a.L + tg) * a.H + h) * (size_t)a.P;
-                        *(uint2*)(yrow + p0 + 16 * wave + 4 * lk) =
-                            make_uint2(pack_bf(yv[0], yv[1]), pack_bf(yv[2], yv[3]));
-                    }
-                }
-            }
             // H = e^{cum_last} H + B^T Xd
             const bf16* btb;
             if constexpr (PB) btb = sBT1;
@@ -2135,30 +1866,18 @@ __global__ __launch_bounds__(kBfThreads, 2) void k_walk_bf(Args a) {
     }
     vm_wait<0>();
 
-    // ---- outputs of the walk --------------------------------------------------------
-    if constexpr (SO) {
-        const size_t u = (size_t)(b * a.H + h) * (a.nseg - 1) + seg;
-        if (active) {
+    // ---- the segment's local end state and total log-decay --------------------------
+    const size_t u = (size_t)(b * a.H + h) * (a.nseg - 1) + seg;
+    if (active) {
 #pragma unroll
-            for (int t = 0; t < NT; ++t)
+        for (int t = 0; t < NT; ++t)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int n = srow(t, 4 * lk + r);
-                    if (n < a.N) a.seg_h[(u * a.N + n) * a.P + pcol] = acc_h[t][r];
-                }
-        }
-        if (pg == 0 && tid == 0) a.seg_ld[u] = seg_acc;
-    } else {
-        if (a.h_out && seg == a.nseg - 1 && active) {
-#pragma unroll
-            for (int t = 0; t < NT; ++t)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int n = srow(t, 4 * lk + r);
-                    if (n < a.N) a.h_out[sh_off + (size_t)n * a.P + pcol] = acc_h[t][r];
-                }
-        }
+            for (int r = 0; r < 4; ++r) {
+                const int n = srow(t, 4 * lk + r);
+                if (n < a.N) a.seg_h[(u * a.N + n) * a.P + pcol] = acc_h[t][r];
+            }
     }
+    if (pg == 0 && tid == 0) a.seg_ld[u] = seg_acc;
 }
 
 // ---------------------------------------------------------------------------
@@ -2620,7 +2339,7 @@ mb_status launch(Args a, int64_t batch, const Plan& pl, char* ws, hipStream_t st
         // C rows need N to be a multiple of 8)
         if (a.N % 8 == 0) {
             if (a.nseg > 1) {
-                hipLaunchKernelGGL((k_walk_bf<NP, true>), dim3((unsigned)(per_seg * (a.nseg - 1))),
+                hipLaunchKernelGGL((k_walk_bf<NP>), dim3((unsigned)(per_seg * (a.nseg - 1))),
                                    dim3(kBfThreads), 0, stream, a);
                 mb_status st = check_launch();
                 if (st != MB_OK) return st;
