@@ -320,7 +320,7 @@ class SSD(Workload):
         self.dtype = dtype
         if dtype == "bf16":
             self.bound = "hbm"
-            self.kernel = "k_scores + k_walk_bf (state-only pass) + k_walk_bf (full pass)"
+            self.kernel = "k_scores + k_walk_bf (state-only pass) + k_walk_bfs (full pass)"
 
     def run(self):
         self.mb.mb_ssd_chunked(self.X, self.ld, self.B, self.C, None, Y=self.Y, h_out=self.h, ws=self.ws)
@@ -626,9 +626,15 @@ class M2Block(Workload):
         self.dtype = dtype
         self.unfused = unfused
         self.name = ("m2_unfused_" if unfused else "m2_block_") + dtype
-        self.kernel = ("k_ssd_prologue + k_scores + k_walk (state-only) + k_walk_m2s / k_walk_bf (output side)"
-                       if unfused or dtype == "bf16" else "k_scores (B, C prologue) + k_walk (state-only, x prologue) "
-                       "+ k_walk_m2s (x prologue, output side)")
+        if dtype == "bf16":
+            # bf16 runs on the bf16 matrix instruction, where the SSD is bound by HBM
+            self.bound = "hbm"
+            self.kernel = "k_ssd_prologue + k_scores + k_walk_bf (state-only) + k_walk_bfs (output side)"
+        elif unfused:
+            self.kernel = "k_ssd_prologue + k_scores + k_walk (state-only) + k_walk_m2s (output side)"
+        else:
+            self.kernel = ("k_scores (B, C prologue) + k_walk (state-only, x prologue) + "
+                           "k_walk_m2s (x prologue, output side)")
         self.shape = dict(batch=b, L=L, H=H, P=P, G=G, N=N, K=K)
         inp = wl.m2_block_full()
         self.inp = inp

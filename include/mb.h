@@ -572,7 +572,10 @@ mb_status mb_ssd_chunked_bwd(const float* X, const float* logdecay, const float*
  * Bytes of device workspace an entry point needs for the given sizes (0 if it
  * needs none).  Unused sizes are ignored: G for MB_OP_TRAP_SSD / MIMO, R for
  * the others.  Returns 0 for invalid sizes as well (the call itself reports
- * the error).
+ * the error).  The Mamba-1 sequence blocks and the SSD segments are planned
+ * for the current device's compute-unit count: query with the device current
+ * that the call will run on (a call given less than its plan needs returns
+ * MB_ERR_WORKSPACE).
  */
 size_t mb_workspace_size(mb_op op, int64_t batch, int64_t L, int64_t H,
                          int64_t P, int64_t G, int64_t N, int64_t R,

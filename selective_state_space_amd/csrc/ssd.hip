@@ -79,7 +79,6 @@ constexpr int kRows = 64;      // rows per chunk (time steps x ranks)
 constexpr int kPG = 64;        // state / output columns per walk workgroup
 constexpr int kNMax = 128;     // largest supported state size
 constexpr int kThreads = 256;
-constexpr int kCUs = 256;       // compute units of an MI355X (segment planning only)
 
 __device__ __forceinline__ floatx4 mfma4(float a, float b, floatx4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
@@ -2268,8 +2267,9 @@ struct Plan {
 
 inline size_t align256(size_t v) { return (v + 255) / 256 * 256; }
 
-// Chunks, segments and workspace for a problem (depends on the sizes only, so
-// mb_workspace_size agrees with the call).
+// Chunks, segments and workspace for a problem (depends on the sizes and the
+// current device's compute-unit count only, so mb_workspace_size agrees with a
+// call on the same device).
 Plan make_plan(bool trap, int64_t R, int64_t batch, int64_t L, int64_t H, int64_t P, int64_t G,
                int64_t N) {
     Plan p{};
@@ -2277,19 +2277,20 @@ Plan make_plan(bool trap, int64_t R, int64_t batch, int64_t L, int64_t H, int64_
     p.nch = (L + QT - 1) / QT;
     p.npg = (P + kPG - 1) / kPG;
     const int64_t units = batch * H * p.npg;
-    // Segment count: minimise an estimate of the walk time on 256 compute units,
-    // with one full-pass workgroup and two state-only workgroups per unit, a
-    // state-only chunk costing about 0.45 of a full one and every workgroup a
-    // start-up of about two chunks; at least 4 chunks per segment.  Depends on
-    // the sizes only, so mb_workspace_size agrees.
+    // Segment count: minimise an estimate of the walk time on the device's
+    // compute units, with one full-pass workgroup and two state-only workgroups
+    // per unit, a state-only chunk costing about 0.45 of a full one and every
+    // workgroup a start-up of about two chunks (both fitted to a sweep of the
+    // segment count on MI355X); at least 4 chunks per segment.
+    const int64_t cus = device_cu_count();
     int64_t best = 1;
     double best_cost = -1.0;
     for (int64_t ns = 1; ns <= 64; ++ns) {
         if (ns > 1 && p.nch / ns < 4) break;
         const int64_t cps = p.nch > 0 ? (p.nch + ns - 1) / ns : 1;
         const int64_t nse = p.nch > 0 ? (p.nch + cps - 1) / cps : 1;
-        const double full_rounds = (double)((nse * units + kCUs - 1) / kCUs);
-        const double so_rounds = (double)(((nse - 1) * units + 2 * kCUs - 1) / (2 * kCUs));
+        const double full_rounds = (double)((nse * units + cus - 1) / cus);
+        const double so_rounds = (double)(((nse - 1) * units + 2 * cus - 1) / (2 * cus));
         const double cost = (full_rounds + 0.45 * so_rounds) * (double)(cps + 2);
         if (best_cost < 0.0 || cost < best_cost - 1e-9) {
             best_cost = cost;
