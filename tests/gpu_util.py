@@ -45,3 +45,27 @@ def assert_close(got, ref, dtype, what=""):
     e = rel_err(got, ref)
     assert e <= TOL[dtype], "%s: max|err|/max|ref| = %.3e > %.0e" % (what, e, TOL[dtype])
     return e
+
+
+def assert_close_slices(got, ref, dtype, what, axes):
+    """The tolerance per slice (e.g. per batch row and head): max|gpu - ref|
+    over the slice divided by the slice's own max|ref|, floored at 1e-2 of the
+    whole tensor's, so a slice whose output is small next to the others is
+    held to its own scale."""
+    g = got.detach().to(torch.float64).cpu().numpy() if isinstance(got, torch.Tensor) else np.asarray(got)
+    r = np.asarray(ref, dtype=np.float64)
+    assert g.shape == r.shape, (g.shape, r.shape)
+    if r.size == 0:
+        return 0.0
+    assert np.all(np.isfinite(g)), "%s: non-finite output" % what
+    other = tuple(i for i in range(r.ndim) if i not in axes)
+    den = np.max(np.abs(r), axis=other)
+    num = np.max(np.abs(g - r), axis=other)
+    floor = 1e-2 * float(np.max(np.abs(r)))
+    if floor == 0.0:
+        assert float(np.max(num)) == 0.0, "%s: output should be exactly zero" % what
+        return 0.0
+    e = num / np.maximum(den, floor)
+    k = np.unravel_index(int(np.argmax(e)), e.shape)
+    assert e[k] <= TOL[dtype], "%s: slice %s max|err|/max|ref| = %.3e > %.0e" % (what, k, e[k], TOL[dtype])
+    return float(e[k])

@@ -26,7 +26,7 @@ import torch
 
 import selective_state_space_amd as mb
 from selective_state_space_amd import workloads as wl
-from gpu_util import assert_close, prepare, require_gpu
+from gpu_util import assert_close, assert_close_slices, prepare, require_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -97,6 +97,7 @@ def test_ssd_strong_decay(oracle_mod, dtype):
     assert np.all(np.isfinite(Y.float().cpu().numpy()))
     assert_close(Y, Yr, dtype, "Y")
     assert_close(h, hr, dtype, "h")
+    assert_close_slices(Y, Yr, dtype, "Y per head", (0, 2))
 
 
 def test_siso_strong_decay(oracle_mod):
@@ -110,6 +111,7 @@ def test_siso_strong_decay(oracle_mod):
     Yr, hr = oracle_mod.trap(**ref)
     assert_close(Y, Yr, "f32", "Y")
     assert_close(h, hr, "f32", "h")
+    assert_close_slices(Y, Yr, "f32", "Y per head", (0, 2))
 
 
 def test_mimo_strong_decay(oracle_mod):
@@ -121,6 +123,7 @@ def test_mimo_strong_decay(oracle_mod):
     Yr, hr = oracle_mod.mimo(**ref)
     assert_close(Y, Yr, "f32", "Y")
     assert_close(h, hr, "f32", "h")
+    assert_close_slices(Y, Yr, "f32", "Y per head", (0, 2))
 
 
 # ------------------------------------------ no input, carried initial state ----

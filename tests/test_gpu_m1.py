@@ -6,7 +6,7 @@ import torch
 
 import selective_state_space_amd as mb
 from selective_state_space_amd import workloads as wl
-from gpu_util import assert_close, prepare, require_gpu
+from gpu_util import assert_close, assert_close_slices, prepare, require_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -135,6 +135,9 @@ def test_block_workload_full(oracle_mod, dtype):
     yr, hr = oracle_mod.m1_scan(**ref)
     assert_close(y, yr, dtype, "y")
     assert_close(h, hr, dtype, "h")
+    # and per (batch, channel): every channel to its own scale
+    assert_close_slices(y, yr, dtype, "y per channel", (0, 2))
+    assert_close_slices(h, hr, dtype, "h per channel", (0, 1))
 
 
 # ------------------------------------------------------- sequence blocks ----

@@ -6,7 +6,7 @@ import torch
 
 import selective_state_space_amd as mb
 from selective_state_space_amd import workloads as wl
-from gpu_util import assert_close, prepare, require_gpu
+from gpu_util import assert_close, assert_close_slices, prepare, require_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -85,6 +85,9 @@ def test_ssd_block_workload_full(oracle_mod, dtype):
     Yr, hr = oracle_mod.ssd(**ref)
     assert_close(Y, Yr, dtype, "Y")
     assert_close(h, hr, dtype, "h")
+    # and per (batch, head): every head to its own scale
+    assert_close_slices(Y, Yr, dtype, "Y per head", (0, 2))
+    assert_close_slices(h, hr, dtype, "h per head", (0, 1))
 
 
 # ------------------------------------------------------------------- SISO ----
@@ -177,6 +180,8 @@ def test_siso_block_workload_full(oracle_mod):
     Yr, hr = oracle_mod.trap(**ref)
     assert_close(Y, Yr, "f32", "Y")
     assert_close(h, hr, "f32", "h")
+    assert_close_slices(Y, Yr, "f32", "Y per head", (0, 2))
+    assert_close_slices(h, hr, "f32", "h per head", (0, 1))
 
 
 # ------------------------------------------------------------------- MIMO ----
@@ -222,3 +227,5 @@ def test_mimo_block_workload_full(oracle_mod):
     Yr, hr = oracle_mod.mimo(**ref)
     assert_close(Y, Yr, "f32", "Y")
     assert_close(h, hr, "f32", "h")
+    assert_close_slices(Y, Yr, "f32", "Y per head", (0, 2))
+    assert_close_slices(h, hr, "f32", "h per head", (0, 1))
