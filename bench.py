@@ -938,28 +938,37 @@ def cpu_model():
 def cpu_baseline(ws, wl):
     """Time the fp64 oracle on the host cores on the same inputs (bf16 inputs are
     timed with their fp32 values: the oracle's cost does not depend on them),
-    then the two small workloads (Mamba-1 tiny, Mamba-1 decode) on one thread."""
+    in passes over the step's workloads until about 10 s of host time (a bounded
+    sample), then the two small workloads (Mamba-1 tiny, Mamba-1 decode) on one
+    thread."""
     import oracle
     oracle.build()
     threads = oracle.get_threads()
-    total_tok, total_s, parts = 0, 0.0, []
-    for w in ws:
-        i = w.inp
-        t0 = time.perf_counter()
-        if w.name == "m1_scan":
-            oracle.m1_scan(**i)
-        elif w.name == "m1_step":
-            oracle.m1_step(i["x"], i["dt"], i["A"], i["B"], i["C"], i["D"], i["h"])
-        elif w.name.startswith("ssd"):
-            oracle.ssd(**i)
-        elif w.name == "siso":
-            oracle.trap(**i)
-        elif w.name == "mimo":
-            oracle.mimo(**i)
-        dt = time.perf_counter() - t0
-        total_tok += w.tokens
-        total_s += dt
-        parts.append("%s full (%d tokens, %.2f s)" % (w.name, w.tokens, dt))
+    total_tok, total_s, passes = 0, 0.0, 0
+    per = {w.name: 0.0 for w in ws}
+    while True:
+        for w in ws:
+            i = w.inp
+            t0 = time.perf_counter()
+            if w.name == "m1_scan":
+                oracle.m1_scan(**i)
+            elif w.name == "m1_step":
+                oracle.m1_step(i["x"], i["dt"], i["A"], i["B"], i["C"], i["D"], i["h"])
+            elif w.name.startswith("ssd"):
+                oracle.ssd(**i)
+            elif w.name == "siso":
+                oracle.trap(**i)
+            elif w.name == "mimo":
+                oracle.mimo(**i)
+            dt = time.perf_counter() - t0
+            total_tok += w.tokens
+            total_s += dt
+            per[w.name] += dt
+        passes += 1
+        if total_s >= 10.0 or passes >= 50:
+            break
+    sample = "%d passes over the full workloads of the step, %.1f s in all; per pass: %s" % (
+        passes, total_s, ", ".join("%s %d tokens %.3f s" % (w.name, w.tokens, per[w.name] / passes) for w in ws))
     single = {}
     oracle.set_threads(1)
     try:
@@ -980,7 +989,7 @@ def cpu_baseline(ws, wl):
         oracle.set_threads(threads)
     return {"value": total_tok / total_s if total_s else None, "unit": "scanned tokens/s",
             "cores": threads, "kind": "oracle", "cpu_model": cpu_model(),
-            "sample": "; ".join(parts), "single_thread": single}
+            "sample": sample, "single_thread": single}
 
 
 _FLUSH = {}
