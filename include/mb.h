@@ -397,7 +397,7 @@ mb_status mb_mimo_ssd(const void* X, const float* logdecay, const void* B,
  *   z                : (batch, L, H, P, R) dtype, or NULL (no gate), 16-byte aligned
  *   Dskip            : (H) fp32 or NULL (no skip term)
  *   normB_w, normC_w, biasB, biasC, eps : as mb_trap_ssd_block
- * Supported: R in {1, 4} (MB_ERR_SHAPE otherwise); other arguments, limits,
+ * Supported: R in {1, 2, 4, 8, 16} (MB_ERR_SHAPE otherwise); other arguments, limits,
  * state and workspace as mb_mimo_ssd.
  */
 mb_status mb_mimo_ssd_block(const void* X, const float* logdecay, const void* B,

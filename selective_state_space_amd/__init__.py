@@ -597,7 +597,7 @@ def mb_mimo_ssd_block(X, logdecay, B, C, beta, gamma, theta=None, h0=None, *, no
     B, C and the skip term and SiLU(z) gate per rank fused into the scan.  X, z
     (batch, L, H, P, R), B, C (batch, L, H, N, R) in one dtype; normB_w, normC_w
     (N,), biasB, biasC (H, N), D (H,) float32 or None; the rest as mb_mimo_ssd.
-    R in {1, 4}.  Returns (Y, h_out)."""
+    R in {1, 2, 4, 8, 16}.  Returns (Y, h_out)."""
     torch = _torch()
     dev = _device_of(X)
     dtype = X.dtype

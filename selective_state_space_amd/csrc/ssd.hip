@@ -53,8 +53,8 @@
 //             the accumulator tiles so that the accumulators are directly the
 //             operand of the next chunk's C~ H product: the state never leaves
 //             registers.
-//             Two variants carry the Mamba-3 block's ends for SISO and MIMO
-//             ranks 1 and 4 (mamba3-minimal README, Architecture): EPI (full
+//             Two variants carry the Mamba-3 block's ends for SISO and every
+//             MIMO rank (mamba3-minimal README, Architecture): EPI (full
 //             pass) loads X and the gate z at the chunk's start and stores
 //             (y + D_h x) SiLU(z); BCN (both passes) turns each raw B, C row
 //             in the prefetch registers into row / rms(row) * weight + bias_h
@@ -538,8 +538,7 @@ template <int NP, int R, bool TRAP, bool ROT, bool GROUPED, typename IO, bool SO
           bool BCN = false, bool PRO = false>
 __global__ __launch_bounds__(kWalkThreads, SO ? 4 : 2) void k_walk(Args a) {
     static_assert(!PRO || (!TRAP && R == 1 && SO), "the block prologue here: the Mamba-2 state-only pass");
-    static_assert(!EPI || (!SO && (R == 1 || R >= 4)),
-                  "the output epilogue is a full-pass feature (one rank, or rank rows)");
+    static_assert(!EPI || !SO, "the output epilogue is a full-pass feature");
     static_assert(!BCN || TRAP, "the B / C prologue is a Mamba-3 feature");
     using Gm = Geo<R, TRAP>;
     constexpr int QT = Gm::QT, EXTRA = Gm::EXTRA, JX = Gm::JX;
@@ -1003,7 +1002,8 @@ __global__ __launch_bounds__(kWalkThreads, SO ? 4 : 2) void k_walk(Args a) {
             floatx4 acc_y[4];
             // output epilogue: X and z of this lane's outputs load now, under the
             // chunk's matrix work, rather than in front of the store (one rank: four
-            // columns of a step; rank rows: four ranks of a step and column)
+            // columns of a step; rank rows: four ranks of a step and column; rank 2:
+            // four columns of one rank of a step, R elements apart)
             float ex[4][4] = {}, ez[4][4] = {};
             if constexpr (EPI) {
                 if (active && nh == 0) {
@@ -1014,9 +1014,17 @@ __global__ __launch_bounds__(kWalkThreads, SO ? 4 : 2) void k_walk(Args a) {
                         if (tg < a.L) {
                             const size_t e = YROW
                                 ? (((size_t)b * a.L + tg) * a.H + h) * (size_t)a.P * R + (size_t)(p0 + 16 * pw + li) * R + i0 % R
-                                : (((size_t)b * a.L + tg) * a.H + h) * (size_t)a.P + p0 + 16 * pw + 4 * lk;
-                            if (a.Dh) load4<IO>(a.X, e, ex[it]);
-                            if (a.Zg) load4<IO>(a.Zg, e, ez[it]);
+                                : (((size_t)b * a.L + tg) * a.H + h) * (size_t)a.P * R + (size_t)(p0 + 16 * pw + 4 * lk) * R + i0 % R;
+                            if constexpr (YROW || R == 1) {
+                                if (a.Dh) load4<IO>(a.X, e, ex[it]);
+                                if (a.Zg) load4<IO>(a.Zg, e, ez[it]);
+                            } else {
+#pragma unroll
+                                for (int r = 0; r < 4; ++r) {
+                                    if (a.Dh) ex[it][r] = to_f32(((const IO*)a.X)[e + (size_t)r * R]);
+                                    if (a.Zg) ez[it][r] = to_f32(((const IO*)a.Zg)[e + (size_t)r * R]);
+                                }
+                            }
                         }
                     }
                 }
@@ -1198,8 +1206,10 @@ __global__ __launch_bounds__(kWalkThreads, SO ? 4 : 2) void k_walk(Args a) {
                                 *(uint2*)((bf16*)yrow + pp) = make_uint2(u0, u1);
                             }
                         } else {
+                            float yv[4] = {y[0], y[1], y[2], y[3]};
+                            epilogue(yv, it);
 #pragma unroll
-                            for (int r = 0; r < 4; ++r) store_out(&yrow[(size_t)(pp + r) * R + i % R], y[r]);
+                            for (int r = 0; r < 4; ++r) store_out(&yrow[(size_t)(pp + r) * R + i % R], yv[r]);
                         }
                     }
                 }
@@ -2356,7 +2366,7 @@ mb_status launch(Args a, int64_t batch, const Plan& pl, char* ws, hipStream_t st
     }
     if (a.nseg > 1) {
         const dim3 g((unsigned)(per_seg * (a.nseg - 1)));
-        if constexpr ((R == 1 || (R == 4 && !GROUPED)) && TRAP) {
+        if constexpr (TRAP && (R == 1 || !GROUPED)) {
             if (a.bcn)
                 hipLaunchKernelGGL((k_walk<NP, R, TRAP, ROT, GROUPED, IO, true, false, true>), g,
                                    dim3(kWalkThreads), 0, stream, a);
@@ -2401,9 +2411,9 @@ mb_status launch(Args a, int64_t batch, const Plan& pl, char* ws, hipStream_t st
         else
             hipLaunchKernelGGL((k_walk<NP, R, TRAP, ROT, GROUPED, IO, false>),
                                dim3((unsigned)(per_seg * a.nseg)), dim3(kWalkThreads), 0, stream, a);
-    } else if constexpr (R == 4 && TRAP && !GROUPED) {
-        // MIMO rank 4 with both ends of its block (the prologue always, the
-        // epilogue when D or z is given)
+    } else if constexpr (TRAP && !GROUPED) {
+        // MIMO with both ends of its block (the prologue always, the epilogue
+        // when D or z is given)
         const dim3 g((unsigned)(per_seg * a.nseg));
         const bool epi = a.Dh || a.Zg;
         if (a.bcn && epi)
@@ -2992,7 +3002,7 @@ extern "C" mb_status mb_mimo_ssd_block(const void* X, const float* logdecay, con
                                        int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N,
                                        int64_t R, int64_t chunk, mb_dtype dtype, void* ws,
                                        size_t ws_bytes, hipStream_t stream) {
-    if (R != 1 && R != 4) return MB_ERR_SHAPE;
+    if (R != 1 && R != 2 && R != 4 && R != 8 && R != 16) return MB_ERR_SHAPE;
     if (!(eps > 0.0f) || !(eps < 3.0e38f)) return MB_ERR_SHAPE;
     mb_status st = ssd_common_checks(X, logdecay, B, C, h0, Y, h_out, beta, gamma, theta, X_prev,
                                      B_prev, batch, L, H, P, H, N, R, dtype, chunk, true);
@@ -3016,8 +3026,13 @@ extern "C" mb_status mb_mimo_ssd_block(const void* X, const float* logdecay, con
     Args a{X, logdecay, B, C, beta, gamma, theta, h0, X_prev, B_prev, Y, h_out, nullptr, nullptr,
            nullptr, nullptr, nullptr, (int)L, (int)H, (int)P, (int)H, (int)N, 0, 0, 0, 0, Dskip, z,
            normB_w, normC_w, biasB, biasC, eps, 1};
-    if (R == 1) return dispatch<1, true, false>(a, batch, pl, (char*)ws, dtype, stream);
-    return dispatch<4, true, false>(a, batch, pl, (char*)ws, dtype, stream);
+    switch (R) {
+        case 1: return dispatch<1, true, false>(a, batch, pl, (char*)ws, dtype, stream);
+        case 2: return dispatch<2, true, false>(a, batch, pl, (char*)ws, dtype, stream);
+        case 4: return dispatch<4, true, false>(a, batch, pl, (char*)ws, dtype, stream);
+        case 8: return dispatch<8, true, false>(a, batch, pl, (char*)ws, dtype, stream);
+        default: return dispatch<16, true, false>(a, batch, pl, (char*)ws, dtype, stream);
+    }
 }
 
 extern "C" mb_status mb_mimo_ssd(const void* X, const float* logdecay, const void* B,

@@ -343,6 +343,14 @@ def test_trap_and_mimo_validation(lib):
     # unsupported rank
     assert lib.mb_mimo_ssd(*args, 1, 10, 2, 16, 8, 3, 0, F32, P(FAKE + (1 << 28)), 1 << 30, None) == E_SHAPE
     assert lib.mb_mimo_ssd(*args, 0, 10, 2, 16, 8, 4, 0, F32, P(FAKE + (1 << 28)), 1 << 30, None) == OK
+    # the MIMO block takes every rank the plain MIMO scan takes
+    mblk = lambda R, batch: lib.mb_mimo_ssd_block(*args[:10], None, None, None, None, 1e-5, None, None,
+                                                  *args[10:], batch, 10, 2, 16, 8, R, 0, F32,
+                                                  P(FAKE + (1 << 28)), 1 << 30, None)
+    for R in (1, 2, 4, 8, 16):
+        assert mblk(R, 0) == OK
+    for R in (3, 32):
+        assert mblk(R, 1) == E_SHAPE
 
 
 def _a256(v):

@@ -63,7 +63,10 @@ SHAPES = [  # batch, L, H, P, N, R
     (1, 1, 1, 16, 4, 4), (2, 130, 3, 32, 64, 4), (1, 333, 2, 64, 128, 4),
     (1, 150, 2, 32, 96, 4),        # state rows padded to 128
     (1, 2000, 2, 64, 128, 4),      # several sequence segments
-    (2, 200, 3, 32, 64, 1)]        # rank 1 (the SISO walk on per-head rows)
+    (2, 200, 3, 32, 64, 1),        # rank 1 (the SISO walk on per-head rows)
+    (2, 150, 2, 32, 64, 2), (1, 1300, 2, 64, 128, 2),     # rank 2 (four columns of one rank per lane)
+    (2, 120, 2, 32, 64, 8), (1, 700, 2, 64, 128, 8),      # rank 8 (rank rows)
+    (1, 90, 3, 16, 32, 16), (1, 1500, 2, 64, 128, 16)]    # rank 16
 
 
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
@@ -76,14 +79,16 @@ def test_mimo_block_shapes(oracle_mod, shape, rotate):
 
 @pytest.mark.parametrize("drop", [("D",), ("z",), ("D", "z"), ("normB_w", "biasC"), ("biasB", "normC_w", "z")],
                          ids=lambda d: "-".join(d))
-def test_mimo_block_optional_parts(oracle_mod, drop):
-    Y, h, Yr, hr = _run(oracle_mod, (2, 300, 2, 64, 128, 4), drop=drop, seed=len(drop))
+@pytest.mark.parametrize("R", [4, 2])
+def test_mimo_block_optional_parts(oracle_mod, drop, R):
+    Y, h, Yr, hr = _run(oracle_mod, (2, 300, 2, 64, 128, R), drop=drop, seed=len(drop) + R)
     assert_close(Y, Yr, "f32", "Y")
     assert_close(h, hr, "f32", "h")
 
 
-def test_mimo_block_previous_token_and_split(oracle_mod):
-    shape = (2, 500, 2, 64, 128, 4)
+@pytest.mark.parametrize("R", [4, 2])
+def test_mimo_block_previous_token_and_split(oracle_mod, R):
+    shape = (2, 500, 2, 64, 128, R)
     Y, h, Yr, hr = _run(oracle_mod, shape, prev=True, seed=7)
     assert_close(Y, Yr, "f32", "Y")
     assert_close(h, hr, "f32", "h")
@@ -92,16 +97,17 @@ def test_mimo_block_previous_token_and_split(oracle_mod):
     assert_close(h, hr, "f32", "h (split)")
 
 
-def test_mimo_block_bf16(oracle_mod):
-    Y, h, Yr, hr = _run(oracle_mod, (2, 400, 2, 64, 128, 4), dtype="bf16", seed=9)
+@pytest.mark.parametrize("R", [4, 2, 16])
+def test_mimo_block_bf16(oracle_mod, R):
+    Y, h, Yr, hr = _run(oracle_mod, (2, 400, 2, 64, 128, R), dtype="bf16", seed=9 + R)
     assert Y.dtype == torch.bfloat16
     assert_close(Y, Yr, "bf16", "Y")
     assert_close(h, hr, "bf16", "h")
 
 
 def test_mimo_block_rejects_unsupported_rank():
-    X = torch.zeros(1, 4, 1, 16, 2, device="cuda")
-    B = torch.zeros(1, 4, 1, 8, 2, device="cuda")
+    X = torch.zeros(1, 4, 1, 16, 3, device="cuda")
+    B = torch.zeros(1, 4, 1, 8, 3, device="cuda")
     s = torch.zeros(1, 4, 1, device="cuda")
     with pytest.raises(mb.MBError):
         mb.mb_mimo_ssd_block(X, s, B, B, s, s)
