@@ -295,7 +295,7 @@ class M1Step(Workload):
 
 
 class SSD(Workload):
-    kernel = "k_scores + k_walk (state-only pass) + k_walk_m2s (full pass)"
+    kernel = "k_scores + k_seg_state (state-only pass) + k_walk_m2s (full pass)"
     source = "selective_state_space_amd/csrc/ssd.hip"
     bound = "mfma"
 
@@ -631,7 +631,7 @@ class M2Block(Workload):
             self.bound = "hbm"
             self.kernel = "k_ssd_prologue + k_scores + k_walk_bf (state-only) + k_walk_bfs (output side)"
         elif unfused:
-            self.kernel = "k_ssd_prologue + k_scores + k_walk (state-only) + k_walk_m2s (output side)"
+            self.kernel = "k_ssd_prologue + k_scores + k_seg_state (state-only) + k_walk_m2s (output side)"
         else:
             self.kernel = ("k_scores (B, C prologue) + k_walk (state-only, x prologue) + "
                            "k_walk_m2s (x prologue, output side)")

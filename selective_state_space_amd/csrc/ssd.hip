@@ -42,6 +42,8 @@
 //             scores of the next chunk.
 //   k_walk_bfs  (Mamba-2, bf16 full pass) the same split on the bf16 matrix
 //             instruction; k_walk_bf is its state-only pass.
+//   k_seg_state  (Mamba-2, fp32 state-only pass) each segment's local end
+//             state as one weighted product over its steps, without a walk.
 //   k_pad     zero-padded copies for Mamba-2 shapes outside the walks' tiles.
 //   k_walk    one workgroup (8 waves) per (batch, head, segment, 64 state
 //             columns), walking the segment's chunks in order.  Per chunk the
@@ -2268,6 +2270,189 @@ __global__ __launch_bounds__(kWalkThreads, 4) void k_walk_bfs(Args a) {
 }
 
 // ---------------------------------------------------------------------------
+// k_seg_state: the Mamba-2 state-only pass with fp32 inputs.  H_loc(s), the
+// state that h_t = e^{ld_t} h_{t-1} + B_t x_t^T reaches at the end of segment
+// s from zero, is one weighted product over the segment's steps,
+//     H_loc(s) = sum_t B_t^T (e^{D_t} x_t),   D_t = sum of ld over the later steps of s,
+// the chunk-state term of the chunkwise form (TorchMamba README, Math notes
+// M2) with the whole segment as the chunk.  It runs as a plain contraction:
+// no chunk staging and no barriers until the end, in work items small enough
+// to spread evenly over the compute units.
+//  - One workgroup of 4 waves per (batch, segment, head, 64 state rows, 64
+//    columns); wave k takes the k-th quarter of the segment's steps for the
+//    whole 64 x 64 block (4 x 4 accumulator tiles), and the four partial
+//    blocks are summed through LDS at the end, each wave storing 16 rows.
+//  - Operands go from global memory (B comes mostly from L2: the heads of a
+//    group share it) straight into the operand registers of the 16 x 16 x 4
+//    instruction: in K step ks of a block at step t0, lane (i, k) supplies
+//    B[t][n0 + 16 j + i] and the weighted X[t][p0 + 16 q + i], t = t0 + 4 ks
+//    + k, so the 16 lanes of a group read 64 contiguous bytes, and each
+//    operand feeds four products.  The next block of 8 steps is loaded while
+//    the current one is multiplied.
+//  - Blocks go from the quarter's end backwards: a step's weight is
+//    e^{S + T - cum}, cum the block's inclusive prefix sum of ld (DPP scan),
+//    T its total and S the total of the steps after the block in the segment,
+//    so every weight is at most 1 for decaying states and the first quarter's S
+//    ends as the segment's total log-decay.
+// ---------------------------------------------------------------------------
+constexpr int kSegThreads = 256;
+constexpr int kSegStep = 8;    // steps per block
+
+template <int NP>
+__global__ __launch_bounds__(kSegThreads, 3) void k_seg_state(Args a) {
+    constexpr int NH = NP / 64;                 // 64-row blocks of the state
+    constexpr uint32_t kOut = 0x80000000u;      // byte offset past any buffer: reads zero
+    const int nsegL = a.nseg - 1;
+    const int npt = (a.P + 63) / 64;
+    const int gsize = a.H * NH * npt;
+    const int ngroups = (int)(gridDim.x / gsize);
+    // ids i, i + 8, ... run on one XCD: give them the heads of one (batch, segment)
+    const int id = blockIdx.x;
+    const int full = ngroups / 8 * 8 * gsize;
+    int grp, wi;
+    if (id < full) {
+        const int x = id % 8, k = id / 8;
+        grp = x + 8 * (k / gsize);
+        wi = k % gsize;
+    } else {
+        grp = id / gsize;
+        wi = id % gsize;
+    }
+    const int b = grp / nsegL, seg = grp % nsegL;
+    const int h = wi / (NH * npt), nb = (wi / npt) % NH, pt = wi % npt;
+    const int g = h / (a.H / a.G);
+    const int n0 = 64 * nb, p0 = 64 * pt;
+    const int lane = threadIdx.x % 64;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
+    const int li = lane % 16, lk = lane / 16;
+    // Segments before the last hold cps whole chunks inside the sequence
+    // ((nseg - 1) cps < nch), so a quarter is 2 cps blocks of 8 steps, all in
+    // range; the step of K step ks goes into the scalar offset.
+    constexpr int KS = kSegStep / 4;   // K steps per block
+    const int seg_t0 = seg * a.cps * kRows;
+    const int q_t0 = seg_t0 + wave * a.cps * 16;
+    const int nblk = a.cps * 16 / kSegStep;
+
+    // one batch row of each input
+    const Buf bB = make_buf((const float*)a.B + (size_t)b * a.L * a.G * a.N, (size_t)a.L * a.G * a.N * 4);
+    const Buf bX = make_buf((const float*)a.X + (size_t)b * a.L * a.H * a.P, (size_t)a.L * a.H * a.P * 4);
+    const float* ldb = a.ld + (size_t)b * a.L * a.H + h;
+
+    // byte offsets of this lane's operands at step 0 (or past the buffer)
+    uint32_t ob[4], ox[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int n = n0 + 16 * j + li, p = p0 + 16 * j + li;
+        ob[j] = n < a.N ? (uint32_t)(g * a.N + n) * 4u : kOut;
+        ox[j] = p < a.P ? (uint32_t)(h * a.P + p) * 4u : kOut;
+    }
+    const uint32_t sb = (uint32_t)a.G * a.N * 4u, sx = (uint32_t)a.H * a.P * 4u;
+
+    float vb[2][4 * KS], vx[2][4 * KS], vl[2];
+    auto load = [&](int slot, int kb) __attribute__((always_inline)) {
+        const int t0 = q_t0 + kb * kSegStep;
+        const uint32_t tk = (uint32_t)(t0 + lk);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t vbo = ob[j] + tk * sb, vxo = ox[j] + tk * sx;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                vb[slot][4 * ks + j] = __uint_as_float(
+                    __builtin_amdgcn_raw_buffer_load_b32(bB.r, (int)vbo, (int)(4 * ks * sb), 0));
+                vx[slot][4 * ks + j] = __uint_as_float(
+                    __builtin_amdgcn_raw_buffer_load_b32(bX.r, (int)vxo, (int)(4 * ks * sx), 0));
+            }
+        }
+        vl[slot] = lane < kSegStep ? ldb[(size_t)(t0 + lane) * a.H] : 0.0f;
+    };
+
+    floatx4 acc[4][4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[j][q] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+    float S = 0.0f;   // the log-decay of the segment's steps after the current block
+    auto step = [&](int slot) __attribute__((always_inline)) {
+        const float cum = wave_scan_dpp(vl[slot]);   // lanes past the block add zero
+        const float T = readlane_f(cum, 63);
+        const float wl = exp_e(S + (T - cum));
+        S += T;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const float w = __shfl(wl, 4 * ks + lk, 64);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float xw = vx[slot][4 * ks + q] * w;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[j][q] = mfma4(vb[slot][4 * ks + j], xw, acc[j][q]);
+            }
+        }
+    };
+    // blocks from the last to the first, two per iteration (the register
+    // slots alternate, so no copies); the first block's loads fly while the
+    // quarters' total log-decays are summed (lane l takes steps l, l + 64, ...)
+    // and exchanged: S starts as the total of the later quarters
+    int kb = nblk - 1;
+    load(0, kb);
+    __shared__ float s_tot[4];
+    {
+        const int q_t1 = q_t0 + nblk * kSegStep;
+        float T = 0.0f;
+        for (int t0 = q_t0; t0 < q_t1; t0 += 256) {
+            float v[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int t = t0 + 64 * i + lane;
+                v[i] = t < q_t1 ? ldb[(size_t)t * a.H] : 0.0f;
+            }
+            T += (v[0] + v[1]) + (v[2] + v[3]);
+        }
+        T = readlane_f(wave_scan_dpp(T), 63);
+        if (lane == 0) s_tot[wave] = T;
+    }
+    __syncthreads();
+    for (int k = 3; k > wave; --k) S += s_tot[k];
+    for (; kb >= 1; kb -= 2) {
+        load(1, kb - 1);
+        step(0);
+        if (kb >= 2) load(0, kb - 2);
+        step(1);
+    }
+    if (kb == 0) step(0);
+
+    // sum the quarters: wave v parks the 12 tiles of the other waves' rows
+    // (tile (j, q) belongs to wave j), then each wave adds its 4 tiles
+    __shared__ __attribute__((aligned(16))) floatx4 red[4 * 12 * 64];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        if (j == wave) continue;
+        const int base = wave * 12 + 4 * (j < wave ? j : j - 1);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) red[(base + q) * 64 + lane] = acc[j][q];
+    }
+    __syncthreads();
+    const size_t u = (size_t)(b * a.H + h) * nsegL + seg;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        if (j != wave) continue;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            floatx4 s = acc[j][q];
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                if (v != j) s += red[(v * 12 + 4 * (j < v ? j : j - 1) + q) * 64 + lane];
+            const int p = p0 + 16 * q + li;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int n = n0 + 16 * j + 4 * lk + r;
+                if (n < a.N && p < a.P) a.seg_h[(u * a.N + n) * a.P + p] = s[r];
+            }
+        }
+    }
+    if (nb == 0 && pt == 0 && wave == 0 && lane == 0) a.seg_ld[u] = S;
+}
+
+// ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
 struct Plan {
@@ -2366,7 +2551,11 @@ mb_status launch(Args a, int64_t batch, const Plan& pl, char* ws, hipStream_t st
     }
     if (a.nseg > 1) {
         const dim3 g((unsigned)(per_seg * (a.nseg - 1)));
-        if constexpr (TRAP && (R == 1 || !GROUPED)) {
+        if constexpr (!TRAP && !ROT && sizeof(IO) == 4) {
+            // Mamba-2 with fp32 inputs: the segment states as plain products
+            const int64_t nwg = batch * a.H * (NP / 64) * ((a.P + 63) / 64) * (a.nseg - 1);
+            hipLaunchKernelGGL((k_seg_state<NP>), dim3((unsigned)nwg), dim3(kSegThreads), 0, stream, a);
+        } else if constexpr (TRAP && (R == 1 || !GROUPED)) {
             if (a.bcn)
                 hipLaunchKernelGGL((k_walk<NP, R, TRAP, ROT, GROUPED, IO, true, false, true>), g,
                                    dim3(kWalkThreads), 0, stream, a);

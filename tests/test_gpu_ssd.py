@@ -56,6 +56,29 @@ def test_ssd_split_chaining(oracle_mod):
     assert_close(hb, hr, "f32", "h")
 
 
+SEG_SHAPES = [  # batch, L, H, P, N, G: long enough for several sequence segments
+    (2, 1500, 4, 48, 128, 2),   # 128 state rows; a column tile half past P
+    (1, 2600, 3, 16, 64, 1),    # 64 state rows: two of the four waves past P
+    (2, 1800, 2, 96, 32, 1),    # 32 state rows: two of the four waves past N
+    (1, 2100, 4, 64, 96, 4),    # one head per group; one wave past N
+    (1, 2049, 2, 128, 12, 2)]   # two column tiles, N = 12, a one-step last chunk
+
+
+@pytest.mark.parametrize("shape", SEG_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_ssd_segment_states(oracle_mod, shape):
+    """The state-only pass (the segments' local end states as weighted
+    products over their steps) at the tile edges, through the sequences'
+    outputs and final states."""
+    b, L, H, P, N, G = shape
+    inp = wl.ssd_inputs(np.random.default_rng(_seed(shape, 5)), b, L, H, P, N, G=G, h0_sd=0.05)
+    dev, ref = prepare(inp, "f32")
+    Y, h = mb.mb_ssd_chunked(dev["X"], dev["logdecay"], dev["B"], dev["C"], dev["h0"])
+    Yr, hr = oracle_mod.ssd(**ref)
+    assert_close(Y, Yr, "f32", "Y")
+    assert_close(h, hr, "f32", "h")
+    assert_close_slices(h, hr, "f32", "h per head", (0, 1))
+
+
 def test_ssd_zero_length_and_in_place_state():
     X = torch.empty(2, 0, 2, 16, device="cuda")
     ld = torch.empty(2, 0, 2, device="cuda")
