@@ -466,7 +466,7 @@ class MIMOBwd(Workload):
 
 class SISO(Workload):
     name = "siso"
-    kernel = "k_walk (state-only pass) + k_walk (full pass)"
+    kernel = "k_seg_trap (state-only pass) + k_walk (full pass)"
     source = "selective_state_space_amd/csrc/ssd.hip"
     bound = "mfma"
 

@@ -43,7 +43,8 @@
 //   k_walk_bfs  (Mamba-2, bf16 full pass) the same split on the bf16 matrix
 //             instruction; k_walk_bf is its state-only pass.
 //   k_seg_state  (Mamba-2, fp32 state-only pass) each segment's local end
-//             state as one weighted product over its steps, without a walk.
+//             state as one weighted product over its steps, without a walk;
+//             k_seg_trap the same for SISO (trapezoid weights, rotations).
 //   k_pad     zero-padded copies for Mamba-2 shapes outside the walks' tiles.
 //   k_walk    one workgroup (8 waves) per (batch, head, segment, 64 state
 //             columns), walking the segment's chunks in order.  Per chunk the
@@ -2453,6 +2454,304 @@ __global__ __launch_bounds__(kSegThreads, 3) void k_seg_state(Args a) {
 }
 
 // ---------------------------------------------------------------------------
+// k_seg_trap: the Mamba-3 SISO state-only pass (rank 1, fp32, B and C without
+// the block prologue), as k_seg_state with the trapezoid's two terms and the
+// rotations.  In the frame of the last step of quarter k (steps q0 .. q1 - 1),
+// step t contributes
+//     R(-Th_t) B_t (w_t x_t)^T,   w_t = gamma_t e^{D_t} + [t + 1 < q1] beta_{t+1} e^{D_t - ld_{t+1}},
+// D_t and Th_t the log-decay and the angle of each state pair over the
+// quarter's steps after t (TorchMamba README, Math notes M3 SISO: after step t
+// the state decays and turns by the later steps' factors, and step t's x
+// enters once with gamma_t and once, a step later, with beta_{t+1}).  The
+// step before the quarter contributes its beta term,
+// R(-Th_{q0-1}) B_{q0-1} (beta_{q0} e^{D_{q0}} x_{q0-1})^T.  A quarter's block
+// is then carried to the segment's end by the later quarters' total decay and
+// angles, e^{S} R(-Th), and the four are summed; the quarters' totals also
+// give the segment's log-decay and angles.
+//  - Layout, loads and reduction as k_seg_state; B's operand is turned by its
+//    pair's angle, the partner state of lane i being lane i ^ 1 (a DPP swap).
+//  - Per block of 4 steps (8 without angles), lane (k, h) of a wave sums the
+//    angles of pair k of its 64 rows over steps 2h, 2h + 1, in revolutions,
+//    and writes the cos and sin of every (step, pair) to LDS for the operand
+//    lanes.
+// ---------------------------------------------------------------------------
+template <int NP, bool GROUPED, bool ROT>
+__global__ __launch_bounds__(kSegThreads, 3) void k_seg_trap(Args a) {
+    constexpr int NH = NP / 64;                 // 64-row blocks of the state
+    constexpr uint32_t kOut = 0x80000000u;      // byte offset past any buffer: reads zero
+    constexpr int KS = ROT ? 1 : 2;             // K steps per block (fewer registers with the angles)
+    constexpr int SPB = 4 * KS;                 // steps per block
+    constexpr int APL = SPB / 2;                // angles staged per lane and block
+    constexpr float kInv2Pi = 0.15915494309189535f;
+    constexpr int RS = 33;                      // LDS row stride (float2) of the cos / sin table
+    const int nsegL = a.nseg - 1;
+    const int npt = (a.P + 63) / 64;
+    const int gsize = a.H * NH * npt;
+    const int ngroups = (int)(gridDim.x / gsize);
+    // ids i, i + 8, ... run on one XCD: give them the heads of one (batch, segment)
+    const int id = blockIdx.x;
+    const int full = ngroups / 8 * 8 * gsize;
+    int grp, wi;
+    if (id < full) {
+        const int x = id % 8, k = id / 8;
+        grp = x + 8 * (k / gsize);
+        wi = k % gsize;
+    } else {
+        grp = id / gsize;
+        wi = id % gsize;
+    }
+    const int b = grp / nsegL, seg = grp % nsegL;
+    const int h = wi / (NH * npt), nb = (wi / npt) % NH, pt = wi % npt;
+    const int hg = GROUPED ? h / (a.H / a.G) : h;
+    const int n0 = 64 * nb, p0 = 64 * pt;
+    const int lane = threadIdx.x % 64;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
+    const int li = lane % 16, lk = lane / 16;
+    // segments before the last: cps whole chunks of 64 steps inside the sequence
+    const int q0 = seg * a.cps * kRows + wave * a.cps * 16;
+    const int q1 = q0 + a.cps * 16;
+    const int nblk = a.cps * 16 / SPB;
+    const int NP2 = a.N / 2;
+
+    // one batch row of each input; B rows (step) are G N (grouped) or H N apart
+    const int bc_step = GROUPED ? a.G * a.N : a.H * a.N;
+    const int x_step = a.H * a.P;
+    const Buf bB = make_buf((const float*)a.B + (size_t)b * a.L * bc_step, (size_t)a.L * bc_step * 4);
+    const Buf bX = make_buf((const float*)a.X + (size_t)b * a.L * x_step, (size_t)a.L * x_step * 4);
+    const size_t so = (size_t)b * a.L * a.H + h;   // (batch, step 0, head) of the per-head inputs
+    const float* ldp = a.ld + so;
+    const float* gmp = a.gamma + so;
+    const float* btp = a.beta + so;
+    const float* thp = ROT ? a.theta + so * NP2 : nullptr;
+    const size_t th_step = (size_t)a.H * NP2;
+
+    uint32_t ob[4], ox[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int n = n0 + 16 * j + li, p = p0 + 16 * j + li;
+        ob[j] = n < a.N ? (uint32_t)(hg * a.N + n) * 4u : kOut;
+        ox[j] = p < a.P ? (uint32_t)(h * a.P + p) * 4u : kOut;
+    }
+    const uint32_t sb = (uint32_t)bc_step * 4u, sx = (uint32_t)x_step * 4u;
+    const int kk = lane % 32, hf = lane / 32;   // angle staging: pair kk of the 64 rows, steps 4 hf ..
+    const int pk = n0 / 2 + kk;
+    const bool pk_ok = pk < NP2;
+
+    // the LDS of the final sum; during the walk its start holds each wave's
+    // cos / sin tables of two blocks (4 steps x 32 pairs each)
+    __shared__ __attribute__((aligned(16))) floatx4 red[4 * 12 * 64];
+    __shared__ float s_S[4];
+    __shared__ float s_A[ROT ? 4 * 32 : 1];
+    float2* rot = (float2*)red + wave * 2 * SPB * RS;
+
+    float vb[2][4 * KS], vx[2][4 * KS];
+    float sld[2], sgm[2], sbn[2], sldn[2];   // step t0 + lane: ld, gamma; step t0 + lane + 1: beta, ld
+    float sth[2][APL];                        // angles of pair pk at steps t0 + APL hf + i
+    auto load = [&](int slot, int kb) __attribute__((always_inline)) {
+        const int t0 = q0 + kb * SPB;
+        const uint32_t tk = (uint32_t)(t0 + lk);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t vbo = ob[j] + tk * sb, vxo = ox[j] + tk * sx;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                vb[slot][4 * ks + j] = __uint_as_float(
+                    __builtin_amdgcn_raw_buffer_load_b32(bB.r, (int)vbo, (int)(4 * ks * sb), 0));
+                vx[slot][4 * ks + j] = __uint_as_float(
+                    __builtin_amdgcn_raw_buffer_load_b32(bX.r, (int)vxo, (int)(4 * ks * sx), 0));
+            }
+        }
+        const int tu = t0 + lane;
+        const bool in = lane < SPB, nx = in && tu + 1 < q1;
+        sld[slot] = in ? ldp[(size_t)tu * a.H] : 0.0f;
+        sgm[slot] = in ? gmp[(size_t)tu * a.H] : 0.0f;
+        sldn[slot] = nx ? ldp[(size_t)(tu + 1) * a.H] : 0.0f;
+        sbn[slot] = nx ? btp[(size_t)(tu + 1) * a.H] : 0.0f;
+        if constexpr (ROT) {
+#pragma unroll
+            for (int i = 0; i < APL; ++i)
+                sth[slot][i] = pk_ok ? thp[(size_t)(t0 + APL * hf + i) * th_step + pk] : 0.0f;
+        }
+    };
+
+    floatx4 acc[4][4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[j][q] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+    float S = 0.0f;      // log-decay of the quarter's steps after the current block
+    float arev = 0.0f;   // angle of pair pk over those steps, revolutions mod 1
+    // B's operand of state n0 + 16 j + li turned by its pair's angle (cos, sin)
+    auto turn = [&](float v, float2 cr) __attribute__((always_inline)) {
+        const float partner = __int_as_float(
+            __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xf, 0xf, false));   // quad_perm 1,0,3,2
+        return fmaf((li & 1) ? -cr.y : cr.y, partner, cr.x * v);
+    };
+    // Staging of a block (its weights, and the cos / sin of its steps and
+    // pairs into table slot `slot`) and its products are separate, so a block
+    // is staged right after the products of the block before it are issued.
+    float wl[2];
+    auto stage = [&](int slot) __attribute__((always_inline)) {
+        const float cum = wave_scan_dpp(sld[slot]);   // lanes past the block add zero
+        const float T = readlane_f(cum, 63);
+        const float D = S + (T - cum);                 // after step t0 + lane
+        wl[slot] = sgm[slot] * exp_e(D) + sbn[slot] * exp_e(D - sldn[slot]);
+        S += T;
+        if constexpr (ROT) {
+            // suffix sums over this lane's steps (revolutions), then the other half's total
+            float suf[APL], ht = 0.0f;
+#pragma unroll
+            for (int i = APL - 1; i >= 0; --i) {
+                suf[i] = ht;
+                ht += sth[slot][i] * kInv2Pi;
+            }
+            const float other = __shfl_xor(ht, 32, 64);
+            const float base = arev + (hf == 0 ? other : 0.0f);
+#pragma unroll
+            for (int i = 0; i < APL; ++i) {
+                float r = base + suf[i];
+                r -= rintf(r);
+                rot[(slot * SPB + APL * hf + i) * RS + kk] =
+                    make_float2(__builtin_amdgcn_cosf(r), __builtin_amdgcn_sinf(r));
+            }
+            arev += ht + other;
+            arev -= rintf(arev);
+        }
+    };
+    auto mult = [&](int slot) __attribute__((always_inline)) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const float w = __shfl(wl[slot], 4 * ks + lk, 64);
+            float bh[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                bh[j] = vb[slot][4 * ks + j];
+                if constexpr (ROT) bh[j] = turn(bh[j], rot[(slot * SPB + 4 * ks + lk) * RS + 8 * j + li / 2]);
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float xw = vx[slot][4 * ks + q] * w;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[j][q] = mfma4(bh[j], xw, acc[j][q]);
+            }
+        }
+    };
+    // blocks from the quarter's last to its first (register and table slots
+    // alternate)
+    int kb = nblk - 1;
+    load(0, kb);
+    stage(0);
+    for (; kb >= 1; kb -= 2) {
+        load(1, kb - 1);
+        mult(0);
+        stage(1);
+        if (kb >= 2) load(0, kb - 2);
+        mult(1);
+        if (kb >= 2) stage(0);
+    }
+    if (kb == 0) mult(0);
+
+    // the step before the quarter (before the call's first step: the given
+    // previous token, or zeros), on lane group 0 of one more K step
+    {
+        const int tp = q0 - 1;
+        const bool given = tp < 0 && a.B_prev != nullptr;
+        const Buf bBp = make_buf(given ? (const float*)a.B_prev + (size_t)b * bc_step : (const float*)a.B,
+                                 given ? (size_t)bc_step * 4 : 0);
+        const Buf bXp = make_buf(given ? (const float*)a.X_prev + (size_t)b * x_step : (const float*)a.X,
+                                 given ? (size_t)x_step * 4 : 0);
+        float pb[4], px[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const bool on = lk == 0;
+            const uint32_t offb = on ? (tp >= 0 ? ob[j] + (uint32_t)tp * sb : ob[j]) : kOut;
+            const uint32_t offx = on ? (tp >= 0 ? ox[j] + (uint32_t)tp * sx : ox[j]) : kOut;
+            pb[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(tp >= 0 ? bB.r : bBp.r, (int)offb, 0, 0));
+            px[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(tp >= 0 ? bX.r : bXp.r, (int)offx, 0, 0));
+        }
+        const float wp = btp[(size_t)q0 * a.H] * exp_e(S - ldp[(size_t)q0 * a.H]);
+        if constexpr (ROT) {
+            // the quarter's total angle of each pair, from the staging lane of the pair
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float r = __shfl(arev, 8 * j + li / 2, 64);
+                pb[j] = turn(pb[j], make_float2(__builtin_amdgcn_cosf(r), __builtin_amdgcn_sinf(r)));
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float xw = px[q] * wp;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[j][q] = mfma4(pb[j], xw, acc[j][q]);
+        }
+    }
+
+    // the later quarters' totals carry this block to the segment's end
+    if (lane == 0) s_S[wave] = S;
+    if constexpr (ROT) if (lane < 32) s_A[wave * 32 + lane] = arev;
+    __syncthreads();
+    float Sl = 0.0f;
+    for (int k = 3; k > wave; --k) Sl += s_S[k];
+    const float dS = exp_e(Sl);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+#pragma unroll
+        for (int pr = 0; pr < 2; ++pr) {
+            // rows n0 + 16 j + 4 lk + 2 pr, + 1: pair 8 j + 2 lk + pr of the block
+            float cs = 1.0f, sn = 0.0f;
+            if constexpr (ROT) {
+                float r = 0.0f;
+                for (int k = 3; k > wave; --k) r += s_A[k * 32 + 8 * j + 2 * lk + pr];
+                r -= rintf(r);
+                cs = __builtin_amdgcn_cosf(r);
+                sn = __builtin_amdgcn_sinf(r);
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float v0 = acc[j][q][2 * pr], v1 = acc[j][q][2 * pr + 1];
+                acc[j][q][2 * pr] = dS * fmaf(sn, v1, cs * v0);
+                acc[j][q][2 * pr + 1] = dS * fmaf(-sn, v0, cs * v1);
+            }
+        }
+    }
+    // sum the quarters (as k_seg_state)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        if (j == wave) continue;
+        const int base = wave * 12 + 4 * (j < wave ? j : j - 1);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) red[(base + q) * 64 + lane] = acc[j][q];
+    }
+    __syncthreads();
+    const size_t u = (size_t)(b * a.H + h) * nsegL + seg;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        if (j != wave) continue;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            floatx4 s = acc[j][q];
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                if (v != j) s += red[(v * 12 + 4 * (j < v ? j : j - 1) + q) * 64 + lane];
+            const int p = p0 + 16 * q + li;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int n = n0 + 16 * j + 4 * lk + r;
+                if (n < a.N && p < a.P) a.seg_h[(u * a.N + n) * a.P + p] = s[r];
+            }
+        }
+    }
+    if (pt == 0 && wave == 0) {
+        if (nb == 0 && lane == 0) a.seg_ld[u] = S + Sl;
+        if constexpr (ROT) if (lane < 32 && pk_ok) {
+            float r = 0.0f;
+            for (int k = 3; k >= 0; --k) r += s_A[k * 32 + lane];
+            a.seg_rev[u * NP2 + pk] = r - rintf(r);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
 struct Plan {
@@ -2555,6 +2854,16 @@ mb_status launch(Args a, int64_t batch, const Plan& pl, char* ws, hipStream_t st
             // Mamba-2 with fp32 inputs: the segment states as plain products
             const int64_t nwg = batch * a.H * (NP / 64) * ((a.P + 63) / 64) * (a.nseg - 1);
             hipLaunchKernelGGL((k_seg_state<NP>), dim3((unsigned)nwg), dim3(kSegThreads), 0, stream, a);
+        } else if constexpr (TRAP && R == 1 && sizeof(IO) == 4) {
+            if (!a.bcn) {
+                // SISO with fp32 inputs: the segment states as plain products
+                const int64_t nwg = batch * a.H * (NP / 64) * ((a.P + 63) / 64) * (a.nseg - 1);
+                hipLaunchKernelGGL((k_seg_trap<NP, GROUPED, ROT>), dim3((unsigned)nwg), dim3(kSegThreads), 0,
+                                   stream, a);
+            } else {
+                hipLaunchKernelGGL((k_walk<NP, R, TRAP, ROT, GROUPED, IO, true, false, true>), g,
+                                   dim3(kWalkThreads), 0, stream, a);
+            }
         } else if constexpr (TRAP && (R == 1 || !GROUPED)) {
             if (a.bcn)
                 hipLaunchKernelGGL((k_walk<NP, R, TRAP, ROT, GROUPED, IO, true, false, true>), g,

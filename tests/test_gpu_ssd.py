@@ -134,6 +134,32 @@ def test_siso_shapes(oracle_mod, shape, rotate):
     assert_close(h, hr, "f32", "h")
 
 
+TRAP_SEG_SHAPES = [  # batch, L, H, P, N, G: several sequence segments
+    (2, 1500, 4, 48, 128, 2),   # 128 state rows; a column tile half past P
+    (1, 2600, 3, 16, 64, 1),    # 64 state rows, P = 16
+    (2, 1800, 2, 96, 32, 1),    # 32 state rows (16 pairs)
+    (1, 2100, 4, 64, 96, 4),    # one head per group; the second row block half past N
+    (1, 2049, 2, 128, 12, 2)]   # two column tiles, N = 12, a one-step last chunk
+
+
+@pytest.mark.parametrize("shape", TRAP_SEG_SHAPES, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("rotate", [True, False])
+def test_siso_segment_states(oracle_mod, shape, rotate):
+    """The SISO state-only pass (each quarter of a segment a weighted, turned
+    product, carried to the segment's end) at the tile edges, through the
+    outputs and final states."""
+    b, L, H, P, N, G = shape
+    inp = wl.trap_inputs(np.random.default_rng(_seed(shape, 7 + rotate)), b, L, H, P, N, G=G,
+                         h0_sd=0.05, rotate=rotate)
+    dev, ref = prepare(inp, "f32")
+    Y, h = mb.mb_trap_ssd(dev["X"], dev["logdecay"], dev["B"], dev["C"], dev["beta"], dev["gamma"],
+                          dev["theta"], dev["h0"])
+    Yr, hr = oracle_mod.trap(**ref)
+    assert_close(Y, Yr, "f32", "Y")
+    assert_close(h, hr, "f32", "h")
+    assert_close_slices(h, hr, "f32", "h per head", (0, 1))
+
+
 def test_siso_bf16(oracle_mod):
     inp = wl.trap_inputs(np.random.default_rng(5), 2, 200, 3, 32, 64, h0_sd=0.05)
     dev, ref = prepare(inp, "bf16")
