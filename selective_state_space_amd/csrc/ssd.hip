@@ -149,6 +149,17 @@ __device__ __forceinline__ float readlane_f(float v, int l) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
 }
 
+// A chunk's decay factors e^{cum_i - cum_t} (i >= t) may be taken as
+// e^{cum_i - cum_31} e^{cum_31 - cum_t} when neither factor can leave the fp32
+// range: every |cum_i - cum_31| is at most the sum of |ld| over steps 0..31 or
+// over 32..63, so both sums at most 80 suffice.  ld: step `lane`'s log-decay
+// (zero past the chunk); the result is the same on every lane.
+__device__ __forceinline__ bool decay_factors_safe(float ld) {
+    const float sa = wave_scan_dpp(fabsf(ld));
+    const float lo = readlane_f(sa, 31), all = readlane_f(sa, 63);
+    return fmaxf(lo, all - lo) <= 80.0f;
+}
+
 // ---------------------------------------------------------------------------
 // buffer resources: raw buffers (stride 0) whose size is the byte length of one
 // batch row of a tensor; an offset at or past the size (negative offsets wrap
@@ -1461,9 +1472,13 @@ __global__ __launch_bounds__(kWalkThreads) void k_walk_m2s(Args a) {
             s_cum[c & 1][lane + 1] = cum;
             if (lane == 0) s_cum[c & 1][0] = 0.0f;
         }
+        // the masked scores' decay e^{cum_i - cum_t} as e^{cum_i - cum_m} e^{cum_m - cum_t}
+        // around the middle step m when neither factor can overflow, else directly
+        const float cmid = readlane_f(cum, 31);
+        const bool fact = decay_factors_safe(pld);
         // the 16 steps of this wave's block, broadcast through the wave's own LDS
-        // slots (cheaper than one readlane per value)
-        s_bc[pw][0][lane] = cum;
+        // slots (cheaper than one readlane per value): cum, or the column factor
+        s_bc[pw][0][lane] = fact ? exp_e(cmid - cum) : cum;
         s_bc[pw][1][lane] = wl;
         if constexpr (PRO) s_bc[pw][2][lane] = pdt;
         float cumv[16], wlv[16], dtv[16];
@@ -1484,7 +1499,6 @@ __global__ __launch_bounds__(kWalkThreads) void k_walk_m2s(Args a) {
             // block prologue: convolved, activated x (zero past the sequence); dt'
             // goes to the chunk-end weights and the masked scores, the skip term
             // to the scores' diagonal
-            const float dh = a.Dh ? a.Dh[h] : 0.0f;
             float win[3] = {pxh[0], pxh[1], pxh[2]};
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
@@ -1496,17 +1510,31 @@ __global__ __launch_bounds__(kWalkThreads) void k_walk_m2s(Args a) {
                 const float xc = (p0 + lane < a.P && c * kRows + t < a.L) ? silu_acc(pre) : 0.0f;
                 xv[i] = xc;
                 xw[i] = xc * (wlv[i] * dtv[i]);
-                const float e = exp_e(t <= lane ? cum - cumv[i] : 0.0f);
-                mv[i] = t <= lane ? fmaf(psc[i] * e, dtv[i], t == lane ? dh : 0.0f) : 0.0f;
             }
         } else {
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                const int t = 16 * pw + i;
                 xv[i] = px[i];
                 xw[i] = px[i] * wlv[i];
-                const float e = exp_e(t <= lane ? cum - cumv[i] : 0.0f);
-                mv[i] = t <= lane ? psc[i] * e : 0.0f;
+            }
+        }
+        float ev[16];
+        if (fact) {
+            const float er = exp_e(cum - cmid);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) ev[i] = er * cumv[i];
+        } else {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) ev[i] = exp_e(16 * pw + i <= lane ? cum - cumv[i] : 0.0f);
+        }
+        const float dh = (PRO && a.Dh) ? a.Dh[h] : 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int t = 16 * pw + i;
+            if constexpr (PRO) {
+                mv[i] = t <= lane ? fmaf(psc[i] * ev[i], dtv[i], t == lane ? dh : 0.0f) : 0.0f;
+            } else {
+                mv[i] = t <= lane ? psc[i] * ev[i] : 0.0f;
             }
         }
         // X^T[p][t] for p = p0 + lane (rows of X^T are columns of X); M[lane][t]
