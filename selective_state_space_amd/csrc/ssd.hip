@@ -2313,11 +2313,13 @@ __global__ __launch_bounds__(kWalkThreads, 4) void k_walk_bfs(Args a) {
 //    blocks are summed through LDS at the end, each wave storing 16 rows.
 //  - Operands go from global memory (B comes mostly from L2: the heads of a
 //    group share it) straight into the operand registers of the 16 x 16 x 4
-//    instruction: in K step ks of a block at step t0, lane (i, k) supplies
-//    B[t][n0 + 16 j + i] and the weighted X[t][p0 + 16 q + i], t = t0 + 4 ks
-//    + k, so the 16 lanes of a group read 64 contiguous bytes, and each
-//    operand feeds four products.  The next block of 8 steps is loaded while
-//    the current one is multiplied.
+//    instruction.  Row i of accumulator tile j is state n0 + 4 i + j and
+//    column i of tile q is column p0 + 4 i + q, so in K step ks of a block at
+//    step t0 lane (i, k) supplies B[t][n0 + 4 i + j] for the four tiles j
+//    with one 16-byte load, and the weighted X[t][p0 + 4 i + q] likewise,
+//    t = t0 + 4 ks + k (the 16 lanes of a group read 256 contiguous bytes);
+//    each operand feeds four products.  The next block of 8 steps is loaded
+//    while the current one is multiplied.
 //  - Blocks go from the quarter's end backwards: a step's weight is
 //    e^{S + T - cum}, cum the block's inclusive prefix sum of ld (DPP scan),
 //    T its total and S the total of the steps after the block in the segment,
@@ -2367,29 +2369,25 @@ __global__ __launch_bounds__(kSegThreads, 3) void k_seg_state(Args a) {
     const Buf bX = make_buf((const float*)a.X + (size_t)b * a.L * a.H * a.P, (size_t)a.L * a.H * a.P * 4);
     const float* ldb = a.ld + (size_t)b * a.L * a.H + h;
 
-    // byte offsets of this lane's operands at step 0 (or past the buffer)
-    uint32_t ob[4], ox[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int n = n0 + 16 * j + li, p = p0 + 16 * j + li;
-        ob[j] = n < a.N ? (uint32_t)(g * a.N + n) * 4u : kOut;
-        ox[j] = p < a.P ? (uint32_t)(h * a.P + p) * 4u : kOut;
-    }
+    // byte offsets of this lane's four operands at step 0 (or past the buffer;
+    // N and P are multiples of 4, so the four are in range or out together)
+    const uint32_t ob = n0 + 4 * li < a.N ? (uint32_t)(g * a.N + n0 + 4 * li) * 4u : kOut;
+    const uint32_t ox = p0 + 4 * li < a.P ? (uint32_t)(h * a.P + p0 + 4 * li) * 4u : kOut;
     const uint32_t sb = (uint32_t)a.G * a.N * 4u, sx = (uint32_t)a.H * a.P * 4u;
 
     float vb[2][4 * KS], vx[2][4 * KS], vl[2];
     auto load = [&](int slot, int kb) __attribute__((always_inline)) {
         const int t0 = q_t0 + kb * kSegStep;
         const uint32_t tk = (uint32_t)(t0 + lk);
+        const uint32_t vbo = ob + tk * sb, vxo = ox + tk * sx;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const uint32_t vbo = ob[j] + tk * sb, vxo = ox[j] + tk * sx;
+        for (int ks = 0; ks < KS; ++ks) {
+            const uintx4 ub = __builtin_amdgcn_raw_buffer_load_b128(bB.r, (int)vbo, (int)(4 * ks * sb), 0);
+            const uintx4 ux = __builtin_amdgcn_raw_buffer_load_b128(bX.r, (int)vxo, (int)(4 * ks * sx), 0);
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                vb[slot][4 * ks + j] = __uint_as_float(
-                    __builtin_amdgcn_raw_buffer_load_b32(bB.r, (int)vbo, (int)(4 * ks * sb), 0));
-                vx[slot][4 * ks + j] = __uint_as_float(
-                    __builtin_amdgcn_raw_buffer_load_b32(bX.r, (int)vxo, (int)(4 * ks * sx), 0));
+            for (int j = 0; j < 4; ++j) {
+                vb[slot][4 * ks + j] = __uint_as_float(ub[j]);
+                vx[slot][4 * ks + j] = __uint_as_float(ux[j]);
             }
         }
         vl[slot] = lane < kSegStep ? ldb[(size_t)(t0 + lane) * a.H] : 0.0f;
@@ -2464,18 +2462,21 @@ __global__ __launch_bounds__(kSegThreads, 3) void k_seg_state(Args a) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         if (j != wave) continue;
+        floatx4 s[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            floatx4 s = acc[j][q];
+            s[q] = acc[j][q];
 #pragma unroll
             for (int v = 0; v < 4; ++v)
-                if (v != j) s += red[(v * 12 + 4 * (j < v ? j : j - 1) + q) * 64 + lane];
-            const int p = p0 + 16 * q + li;
+                if (v != j) s[q] += red[(v * 12 + 4 * (j < v ? j : j - 1) + q) * 64 + lane];
+        }
+        // tile row 4 lk + r is state n0 + 16 lk + 4 r + j; columns p0 + 4 li + q
+        const int p = p0 + 4 * li;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int n = n0 + 16 * j + 4 * lk + r;
-                if (n < a.N && p < a.P) a.seg_h[(u * a.N + n) * a.P + p] = s[r];
-            }
+        for (int r = 0; r < 4; ++r) {
+            const int n = n0 + 16 * lk + 4 * r + j;
+            if (n < a.N && p < a.P)
+                *(float4*)&a.seg_h[(u * a.N + n) * a.P + p] = make_float4(s[0][r], s[1][r], s[2][r], s[3][r]);
         }
     }
     if (nb == 0 && pt == 0 && wave == 0 && lane == 0) a.seg_ld[u] = S;
@@ -2496,8 +2497,8 @@ __global__ __launch_bounds__(kSegThreads, 3) void k_seg_state(Args a) {
 // is then carried to the segment's end by the later quarters' total decay and
 // angles, e^{S} R(-Th), and the four are summed; the quarters' totals also
 // give the segment's log-decay and angles.
-//  - Layout, loads and reduction as k_seg_state; B's operand is turned by its
-//    pair's angle, the partner state of lane i being lane i ^ 1 (a DPP swap).
+//  - Layout, loads and reduction as k_seg_state; B's operands are turned by
+//    their pairs' angles, a pair being tiles 2 m and 2 m + 1 of one lane.
 //  - Per block of 4 steps (8 without angles), lane (k, h) of a wave sums the
 //    angles of pair k of its 64 rows over steps 2h, 2h + 1, in revolutions,
 //    and writes the cos and sin of every (step, pair) to LDS for the operand
@@ -2511,7 +2512,7 @@ __global__ __launch_bounds__(kSegThreads, 3) void k_seg_trap(Args a) {
     constexpr int SPB = 4 * KS;                 // steps per block
     constexpr int APL = SPB / 2;                // angles staged per lane and block
     constexpr float kInv2Pi = 0.15915494309189535f;
-    constexpr int RS = 33;                      // LDS row stride (float2) of the cos / sin table
+    constexpr int RS = 34;                      // LDS row stride (float2) of the cos / sin table
     const int nsegL = a.nseg - 1;
     const int npt = (a.P + 63) / 64;
     const int gsize = a.H * NH * npt;
@@ -2553,13 +2554,11 @@ __global__ __launch_bounds__(kSegThreads, 3) void k_seg_trap(Args a) {
     const float* thp = ROT ? a.theta + so * NP2 : nullptr;
     const size_t th_step = (size_t)a.H * NP2;
 
-    uint32_t ob[4], ox[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int n = n0 + 16 * j + li, p = p0 + 16 * j + li;
-        ob[j] = n < a.N ? (uint32_t)(hg * a.N + n) * 4u : kOut;
-        ox[j] = p < a.P ? (uint32_t)(h * a.P + p) * 4u : kOut;
-    }
+    // operand layout as k_seg_state: row i of tile j is state n0 + 4 i + j
+    // (so a rotation pair is tiles 2 m, 2 m + 1 of one lane), column i of tile
+    // q is p0 + 4 i + q; one 16-byte load per operand and K step
+    const uint32_t ob = n0 + 4 * li < a.N ? (uint32_t)(hg * a.N + n0 + 4 * li) * 4u : kOut;
+    const uint32_t ox = p0 + 4 * li < a.P ? (uint32_t)(h * a.P + p0 + 4 * li) * 4u : kOut;
     const uint32_t sb = (uint32_t)bc_step * 4u, sx = (uint32_t)x_step * 4u;
     const int kk = lane % 32, hf = lane / 32;   // angle staging: pair kk of the 64 rows, steps 4 hf ..
     const int pk = n0 / 2 + kk;
@@ -2578,15 +2577,15 @@ __global__ __launch_bounds__(kSegThreads, 3) void k_seg_trap(Args a) {
     auto load = [&](int slot, int kb) __attribute__((always_inline)) {
         const int t0 = q0 + kb * SPB;
         const uint32_t tk = (uint32_t)(t0 + lk);
+        const uint32_t vbo = ob + tk * sb, vxo = ox + tk * sx;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const uint32_t vbo = ob[j] + tk * sb, vxo = ox[j] + tk * sx;
+        for (int ks = 0; ks < KS; ++ks) {
+            const uintx4 ub = __builtin_amdgcn_raw_buffer_load_b128(bB.r, (int)vbo, (int)(4 * ks * sb), 0);
+            const uintx4 ux = __builtin_amdgcn_raw_buffer_load_b128(bX.r, (int)vxo, (int)(4 * ks * sx), 0);
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                vb[slot][4 * ks + j] = __uint_as_float(
-                    __builtin_amdgcn_raw_buffer_load_b32(bB.r, (int)vbo, (int)(4 * ks * sb), 0));
-                vx[slot][4 * ks + j] = __uint_as_float(
-                    __builtin_amdgcn_raw_buffer_load_b32(bX.r, (int)vxo, (int)(4 * ks * sx), 0));
+            for (int j = 0; j < 4; ++j) {
+                vb[slot][4 * ks + j] = __uint_as_float(ub[j]);
+                vx[slot][4 * ks + j] = __uint_as_float(ux[j]);
             }
         }
         const int tu = t0 + lane;
@@ -2609,11 +2608,14 @@ __global__ __launch_bounds__(kSegThreads, 3) void k_seg_trap(Args a) {
         for (int q = 0; q < 4; ++q) acc[j][q] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
     float S = 0.0f;      // log-decay of the quarter's steps after the current block
     float arev = 0.0f;   // angle of pair pk over those steps, revolutions mod 1
-    // B's operand of state n0 + 16 j + li turned by its pair's angle (cos, sin)
-    auto turn = [&](float v, float2 cr) __attribute__((always_inline)) {
-        const float partner = __int_as_float(
-            __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xf, 0xf, false));   // quad_perm 1,0,3,2
-        return fmaf((li & 1) ? -cr.y : cr.y, partner, cr.x * v);
+    // B's operands of this lane's two state pairs (tiles 0, 1 and 2, 3) turned
+    // by the pairs' angles: cs = (cos, sin, cos, sin)
+    auto turn = [&](float* v, float4 cs) __attribute__((always_inline)) {
+        const float b0 = v[0], b1 = v[1], b2 = v[2], b3 = v[3];
+        v[0] = fmaf(cs.y, b1, cs.x * b0);
+        v[1] = fmaf(-cs.y, b0, cs.x * b1);
+        v[2] = fmaf(cs.w, b3, cs.z * b2);
+        v[3] = fmaf(-cs.w, b2, cs.z * b3);
     };
     // Staging of a block (its weights, and the cos / sin of its steps and
     // pairs into table slot `slot`) and its products are separate, so a block
@@ -2652,10 +2654,8 @@ __global__ __launch_bounds__(kSegThreads, 3) void k_seg_trap(Args a) {
             const float w = __shfl(wl[slot], 4 * ks + lk, 64);
             float bh[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                bh[j] = vb[slot][4 * ks + j];
-                if constexpr (ROT) bh[j] = turn(bh[j], rot[(slot * SPB + 4 * ks + lk) * RS + 8 * j + li / 2]);
-            }
+            for (int j = 0; j < 4; ++j) bh[j] = vb[slot][4 * ks + j];
+            if constexpr (ROT) turn(bh, *(const float4*)&rot[(slot * SPB + 4 * ks + lk) * RS + 2 * li]);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const float xw = vx[slot][4 * ks + q] * w;
@@ -2689,22 +2689,25 @@ __global__ __launch_bounds__(kSegThreads, 3) void k_seg_trap(Args a) {
         const Buf bXp = make_buf(given ? (const float*)a.X_prev + (size_t)b * x_step : (const float*)a.X,
                                  given ? (size_t)x_step * 4 : 0);
         float pb[4], px[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        {
             const bool on = lk == 0;
-            const uint32_t offb = on ? (tp >= 0 ? ob[j] + (uint32_t)tp * sb : ob[j]) : kOut;
-            const uint32_t offx = on ? (tp >= 0 ? ox[j] + (uint32_t)tp * sx : ox[j]) : kOut;
-            pb[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(tp >= 0 ? bB.r : bBp.r, (int)offb, 0, 0));
-            px[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(tp >= 0 ? bX.r : bXp.r, (int)offx, 0, 0));
+            const uint32_t offb = on ? (tp >= 0 ? ob + (uint32_t)tp * sb : ob) : kOut;
+            const uint32_t offx = on ? (tp >= 0 ? ox + (uint32_t)tp * sx : ox) : kOut;
+            const uintx4 ub = __builtin_amdgcn_raw_buffer_load_b128(tp >= 0 ? bB.r : bBp.r, (int)offb, 0, 0);
+            const uintx4 ux = __builtin_amdgcn_raw_buffer_load_b128(tp >= 0 ? bX.r : bXp.r, (int)offx, 0, 0);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                pb[j] = __uint_as_float(ub[j]);
+                px[j] = __uint_as_float(ux[j]);
+            }
         }
         const float wp = btp[(size_t)q0 * a.H] * exp_e(S - ldp[(size_t)q0 * a.H]);
         if constexpr (ROT) {
-            // the quarter's total angle of each pair, from the staging lane of the pair
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const float r = __shfl(arev, 8 * j + li / 2, 64);
-                pb[j] = turn(pb[j], make_float2(__builtin_amdgcn_cosf(r), __builtin_amdgcn_sinf(r)));
-            }
+            // the quarter's total angle of this lane's pairs 2 li, 2 li + 1, from
+            // their staging lanes
+            const float r0 = __shfl(arev, 2 * li, 64), r1 = __shfl(arev, 2 * li + 1, 64);
+            turn(pb, make_float4(__builtin_amdgcn_cosf(r0), __builtin_amdgcn_sinf(r0), __builtin_amdgcn_cosf(r1),
+                                 __builtin_amdgcn_sinf(r1)));
         }
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -2722,23 +2725,24 @@ __global__ __launch_bounds__(kSegThreads, 3) void k_seg_trap(Args a) {
     for (int k = 3; k > wave; --k) Sl += s_S[k];
     const float dS = exp_e(Sl);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int r = 0; r < 4; ++r) {
 #pragma unroll
-        for (int pr = 0; pr < 2; ++pr) {
-            // rows n0 + 16 j + 4 lk + 2 pr, + 1: pair 8 j + 2 lk + pr of the block
+        for (int m = 0; m < 2; ++m) {
+            // tile rows 4 lk + r of tiles 2 m, 2 m + 1: states n0 + 16 lk + 4 r + 2 m,
+            // + 1, pair 8 lk + 2 r + m of the block
             float cs = 1.0f, sn = 0.0f;
             if constexpr (ROT) {
-                float r = 0.0f;
-                for (int k = 3; k > wave; --k) r += s_A[k * 32 + 8 * j + 2 * lk + pr];
-                r -= rintf(r);
-                cs = __builtin_amdgcn_cosf(r);
-                sn = __builtin_amdgcn_sinf(r);
+                float rv = 0.0f;
+                for (int k = 3; k > wave; --k) rv += s_A[k * 32 + 8 * lk + 2 * r + m];
+                rv -= rintf(rv);
+                cs = __builtin_amdgcn_cosf(rv);
+                sn = __builtin_amdgcn_sinf(rv);
             }
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const float v0 = acc[j][q][2 * pr], v1 = acc[j][q][2 * pr + 1];
-                acc[j][q][2 * pr] = dS * fmaf(sn, v1, cs * v0);
-                acc[j][q][2 * pr + 1] = dS * fmaf(-sn, v0, cs * v1);
+                const float v0 = acc[2 * m][q][r], v1 = acc[2 * m + 1][q][r];
+                acc[2 * m][q][r] = dS * fmaf(sn, v1, cs * v0);
+                acc[2 * m + 1][q][r] = dS * fmaf(-sn, v0, cs * v1);
             }
         }
     }
@@ -2755,18 +2759,21 @@ __global__ __launch_bounds__(kSegThreads, 3) void k_seg_trap(Args a) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         if (j != wave) continue;
+        floatx4 s[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            floatx4 s = acc[j][q];
+            s[q] = acc[j][q];
 #pragma unroll
             for (int v = 0; v < 4; ++v)
-                if (v != j) s += red[(v * 12 + 4 * (j < v ? j : j - 1) + q) * 64 + lane];
-            const int p = p0 + 16 * q + li;
+                if (v != j) s[q] += red[(v * 12 + 4 * (j < v ? j : j - 1) + q) * 64 + lane];
+        }
+        // tile row 4 lk + r is state n0 + 16 lk + 4 r + j; columns p0 + 4 li + q
+        const int p = p0 + 4 * li;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int n = n0 + 16 * j + 4 * lk + r;
-                if (n < a.N && p < a.P) a.seg_h[(u * a.N + n) * a.P + p] = s[r];
-            }
+        for (int r = 0; r < 4; ++r) {
+            const int n = n0 + 16 * lk + 4 * r + j;
+            if (n < a.N && p < a.P)
+                *(float4*)&a.seg_h[(u * a.N + n) * a.P + p] = make_float4(s[0][r], s[1][r], s[2][r], s[3][r]);
         }
     }
     if (pt == 0 && wave == 0) {
