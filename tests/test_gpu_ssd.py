@@ -61,7 +61,9 @@ SEG_SHAPES = [  # batch, L, H, P, N, G: long enough for several sequence segment
     (1, 2600, 3, 16, 64, 1),    # 64 state rows: two of the four waves past P
     (2, 1800, 2, 96, 32, 1),    # 32 state rows: two of the four waves past N
     (1, 2100, 4, 64, 96, 4),    # one head per group; one wave past N
-    (1, 2049, 2, 128, 12, 2)]   # two column tiles, N = 12, a one-step last chunk
+    (1, 2049, 2, 128, 12, 2),   # two column tiles, N = 12, a one-step last chunk
+    (1, 1700, 2, 16, 4, 1),     # N = 4: one lane row of four in range
+    (2, 1600, 3, 32, 8, 3)]     # N = 8, one head per group
 
 
 @pytest.mark.parametrize("shape", SEG_SHAPES, ids=lambda s: "x".join(map(str, s)))
@@ -139,7 +141,9 @@ TRAP_SEG_SHAPES = [  # batch, L, H, P, N, G: several sequence segments
     (1, 2600, 3, 16, 64, 1),    # 64 state rows, P = 16
     (2, 1800, 2, 96, 32, 1),    # 32 state rows (16 pairs)
     (1, 2100, 4, 64, 96, 4),    # one head per group; the second row block half past N
-    (1, 2049, 2, 128, 12, 2)]   # two column tiles, N = 12, a one-step last chunk
+    (1, 2049, 2, 128, 12, 2),   # two column tiles, N = 12, a one-step last chunk
+    (1, 1700, 2, 16, 4, 1),     # N = 4: two pairs
+    (2, 1600, 3, 32, 8, 3)]     # N = 8, one head per group
 
 
 @pytest.mark.parametrize("shape", TRAP_SEG_SHAPES, ids=lambda s: "x".join(map(str, s)))
