@@ -51,15 +51,20 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 FP32_PEAK_TFLOPS = 157.3       # MI355X dense fp32 (vector and MFMA)
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
-# fp32 vector issue slots per second: 256 CUs x 4 SIMDs x 32 lanes x 2.4 GHz =
-# 78.6e12 (the 157.3 TFLOP/s fp32 vector peak counts an FMA as two flops).  A
-# wave64 FMA issues in two cycles: measured on MI355X at 8 waves per SIMD.
-VALU_LANE_SLOTS = 256 * 4 * 32 * 2.4e9
-# v_exp_f32 throughput, measured on MI355X (8 independent chains per lane, 1..8
-# waves per SIMD): a quarter of the FMA rate, and it does not overlap with the
-# FMA stream (1 exp + 4 FMA take the sum of their times), so an exp costs four
-# full-rate slots.
-EXP_SLOTS = 4
+# fp32 vector issue slots per second without packed fp32 (disabled in this
+# library): 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz = 39.3e12, one FMA per lane
+# per clock.  The published 157.3 TFLOP/s fp32 vector peak counts packed FMA
+# (two per lane per clock, two flops each).  Measured on MI355X with a
+# throughput probe (8 independent chains per lane, shader clock read at
+# 2.32-2.39 GHz): v_fma_f32 takes 4.3-4.6 cycles per wave instruction per SIMD
+# at 2 to 8 waves per SIMD (35.9 T lane-ops/s at 8 waves); one wave alone
+# issues one only every ~8.6 cycles.
+VALU_LANE_SLOTS = 256 * 4 * 16 * 2.4e9
+PACKED_VALU_LANE_SLOTS = 2 * VALU_LANE_SLOTS   # the published peak, in FMA lane-slots
+# v_exp_f32 throughput from the same probe: 9.2 cycles per wave instruction at
+# 8 waves per SIMD, about two FMA slots; one exp beside four FMA chains takes
+# the sum of their times (the two do not overlap), so an exp counts 2 slots.
+EXP_SLOTS = 2
 # Minimal VALU issue slots per Mamba-1 (t, c, n) element: dt*A, (dt*x)*B,
 # a*h + u, y += C*h (one slot each) and one exp.
 M1_SLOTS_PER_ELEM = 4 + EXP_SLOTS
@@ -791,7 +796,9 @@ def roofline_of(w, ms, bound=None):
     if bound == "alu":
         ach = w.exps * getattr(w, "slots", M1_SLOTS_PER_ELEM) / s / 1e9
         peak = VALU_LANE_SLOTS / 1e9
-        return {"bound": "alu", "achieved": ach, "peak": peak, "unit": "G lane-slots/s", "frac": ach / peak}
+        return {"bound": "alu", "achieved": ach, "peak": peak, "unit": "G lane-slots/s", "frac": ach / peak,
+                "peak_note": "fp32 FMA without packed math: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz",
+                "frac_of_packed_peak": ach / (PACKED_VALU_LANE_SLOTS / 1e9)}
     if bound == "mfma":
         peak = BF16_PEAK_TFLOPS if getattr(w, "dtype", "f32") == "bf16" else FP32_PEAK_TFLOPS
         ach = w.flops / s / 1e12

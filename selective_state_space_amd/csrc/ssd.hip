@@ -2368,6 +2368,7 @@ __global__ __launch_bounds__(kSegThreads, 3) void k_seg_state(Args a) {
     const Buf bB = make_buf((const float*)a.B + (size_t)b * a.L * a.G * a.N, (size_t)a.L * a.G * a.N * 4);
     const Buf bX = make_buf((const float*)a.X + (size_t)b * a.L * a.H * a.P, (size_t)a.L * a.H * a.P * 4);
     const float* ldb = a.ld + (size_t)b * a.L * a.H + h;
+    const Buf bL = make_buf(a.ld + (size_t)b * a.L * a.H, (size_t)a.L * a.H * 4);
 
     // byte offsets of this lane's four operands at step 0 (or past the buffer;
     // N and P are multiples of 4, so the four are in range or out together)
@@ -2375,11 +2376,23 @@ __global__ __launch_bounds__(kSegThreads, 3) void k_seg_state(Args a) {
     const uint32_t ox = p0 + 4 * li < a.P ? (uint32_t)(h * a.P + p0 + 4 * li) * 4u : kOut;
     const uint32_t sb = (uint32_t)a.G * a.N * 4u, sx = (uint32_t)a.H * a.P * 4u;
 
+    // Every load is issued unconditionally (a block before the quarter's
+    // first reads zeros: all its offsets past the buffers), so the compiler's
+    // waits on the memory counter stay exact and the next block's loads stay
+    // in flight while the current one is multiplied.
     float vb[2][4 * KS], vx[2][4 * KS], vl[2];
     auto load = [&](int slot, int kb) __attribute__((always_inline)) {
+        const uint32_t kill = kb >= 0 ? 0u : kOut;
         const int t0 = q_t0 + kb * kSegStep;
         const uint32_t tk = (uint32_t)(t0 + lk);
-        const uint32_t vbo = ob + tk * sb, vxo = ox + tk * sx;
+        const uint32_t vbo = (ob + tk * sb) | kill, vxo = (ox + tk * sx) | kill;
+        // the block's log-decay first, then its operands, in this order at this
+        // point of the program: a wait for one slot then never covers the
+        // loads of the other
+        const uint32_t lo = lane < kSegStep ? ((uint32_t)((t0 + lane) * a.H + h) * 4u) | kill : kOut;
+        __builtin_amdgcn_sched_barrier(0);
+        vl[slot] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(bL.r, (int)lo, 0, 0));
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             const uintx4 ub = __builtin_amdgcn_raw_buffer_load_b128(bB.r, (int)vbo, (int)(4 * ks * sb), 0);
@@ -2390,7 +2403,7 @@ __global__ __launch_bounds__(kSegThreads, 3) void k_seg_state(Args a) {
                 vx[slot][4 * ks + j] = __uint_as_float(ux[j]);
             }
         }
-        vl[slot] = lane < kSegStep ? ldb[(size_t)(t0 + lane) * a.H] : 0.0f;
+        __builtin_amdgcn_sched_barrier(0);
     };
 
     floatx4 acc[4][4];
@@ -2442,7 +2455,7 @@ __global__ __launch_bounds__(kSegThreads, 3) void k_seg_state(Args a) {
     for (; kb >= 1; kb -= 2) {
         load(1, kb - 1);
         step(0);
-        if (kb >= 2) load(0, kb - 2);
+        load(0, kb - 2);
         step(1);
     }
     if (kb == 0) step(0);

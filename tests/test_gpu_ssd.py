@@ -67,18 +67,19 @@ SEG_SHAPES = [  # batch, L, H, P, N, G: long enough for several sequence segment
 
 
 @pytest.mark.parametrize("shape", SEG_SHAPES, ids=lambda s: "x".join(map(str, s)))
-def test_ssd_segment_states(oracle_mod, shape):
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_ssd_segment_states(oracle_mod, shape, dtype):
     """The state-only pass (the segments' local end states as weighted
-    products over their steps) at the tile edges, through the sequences'
-    outputs and final states."""
+    products over their steps; fp32 and bf16 inputs) at the tile edges,
+    through the sequences' outputs and final states."""
     b, L, H, P, N, G = shape
     inp = wl.ssd_inputs(np.random.default_rng(_seed(shape, 5)), b, L, H, P, N, G=G, h0_sd=0.05)
-    dev, ref = prepare(inp, "f32")
+    dev, ref = prepare(inp, dtype)
     Y, h = mb.mb_ssd_chunked(dev["X"], dev["logdecay"], dev["B"], dev["C"], dev["h0"])
     Yr, hr = oracle_mod.ssd(**ref)
-    assert_close(Y, Yr, "f32", "Y")
-    assert_close(h, hr, "f32", "h")
-    assert_close_slices(h, hr, "f32", "h per head", (0, 1))
+    assert_close(Y, Yr, dtype, "Y")
+    assert_close(h, hr, dtype, "h")
+    assert_close_slices(h, hr, dtype, "h per head", (0, 1))
 
 
 def test_ssd_zero_length_and_in_place_state():
