@@ -2562,10 +2562,12 @@ __global__ __launch_bounds__(kSegThreads, 3) void k_seg_trap(Args a) {
     const Buf bX = make_buf((const float*)a.X + (size_t)b * a.L * x_step, (size_t)a.L * x_step * 4);
     const size_t so = (size_t)b * a.L * a.H + h;   // (batch, step 0, head) of the per-head inputs
     const float* ldp = a.ld + so;
-    const float* gmp = a.gamma + so;
     const float* btp = a.beta + so;
-    const float* thp = ROT ? a.theta + so * NP2 : nullptr;
-    const size_t th_step = (size_t)a.H * NP2;
+    const size_t nsh = (size_t)a.L * a.H;
+    const Buf bL = make_buf(a.ld + (size_t)b * nsh, nsh * 4);
+    const Buf bG = make_buf(a.gamma + (size_t)b * nsh, nsh * 4);
+    const Buf bE = make_buf(a.beta + (size_t)b * nsh, nsh * 4);
+    const Buf bT = make_buf(ROT ? a.theta + (size_t)b * nsh * NP2 : a.ld, ROT ? nsh * NP2 * 4 : 0);
 
     // operand layout as k_seg_state: row i of tile j is state n0 + 4 i + j
     // (so a rotation pair is tiles 2 m, 2 m + 1 of one lane), column i of tile
@@ -2576,6 +2578,8 @@ __global__ __launch_bounds__(kSegThreads, 3) void k_seg_trap(Args a) {
     const int kk = lane % 32, hf = lane / 32;   // angle staging: pair kk of the 64 rows, steps 4 hf ..
     const int pk = n0 / 2 + kk;
     const bool pk_ok = pk < NP2;
+    // pairs past N read zeros (a mask the compiler cannot turn into branches)
+    const uint32_t pk_kill = opaque(pk_ok ? 0u : kOut);
 
     // the LDS of the final sum; during the walk its start holds each wave's
     // cos / sin tables of two blocks (4 steps x 32 pairs each)
@@ -2587,10 +2591,18 @@ __global__ __launch_bounds__(kSegThreads, 3) void k_seg_trap(Args a) {
     float vb[2][4 * KS], vx[2][4 * KS];
     float sld[2], sgm[2], sbn[2], sldn[2];   // step t0 + lane: ld, gamma; step t0 + lane + 1: beta, ld
     float sth[2][APL];                        // angles of pair pk at steps t0 + APL hf + i
-    auto load = [&](int slot, int kb) __attribute__((always_inline)) {
-        const int t0 = q0 + kb * SPB;
-        const uint32_t tk = (uint32_t)(t0 + lk);
-        const uint32_t vbo = ob + tk * sb, vxo = ox + tk * sx;
+    // Every load is a buffer load issued unconditionally (a block before the
+    // quarter's first reads zeros: all its offsets past the buffers), in a
+    // fixed order at a fixed point of the program, so the compiler's waits on
+    // the memory counter never cover loads issued after the ones it needs.
+    // A block's operands are loaded one block ahead of its products, its
+    // per-step inputs (log-decay, gamma, the next step's beta and log-decay,
+    // the angles) two blocks ahead of its staging.
+    auto load_ops = [&](int slot, int kb) __attribute__((always_inline)) {
+        const uint32_t kill = kb >= 0 ? 0u : kOut;
+        const uint32_t tk = (uint32_t)(q0 + kb * SPB + lk);
+        const uint32_t vbo = (ob + tk * sb) | kill, vxo = (ox + tk * sx) | kill;
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             const uintx4 ub = __builtin_amdgcn_raw_buffer_load_b128(bB.r, (int)vbo, (int)(4 * ks * sb), 0);
@@ -2601,17 +2613,28 @@ __global__ __launch_bounds__(kSegThreads, 3) void k_seg_trap(Args a) {
                 vx[slot][4 * ks + j] = __uint_as_float(ux[j]);
             }
         }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    auto load_par = [&](int slot, int kb) __attribute__((always_inline)) {
+        const uint32_t kill = kb >= 0 ? 0u : kOut;
+        const int t0 = q0 + kb * SPB;
         const int tu = t0 + lane;
         const bool in = lane < SPB, nx = in && tu + 1 < q1;
-        sld[slot] = in ? ldp[(size_t)tu * a.H] : 0.0f;
-        sgm[slot] = in ? gmp[(size_t)tu * a.H] : 0.0f;
-        sldn[slot] = nx ? ldp[(size_t)(tu + 1) * a.H] : 0.0f;
-        sbn[slot] = nx ? btp[(size_t)(tu + 1) * a.H] : 0.0f;
+        const uint32_t o0 = in ? ((uint32_t)(tu * a.H + h) * 4u) | kill : kOut;
+        const uint32_t o1 = nx ? ((uint32_t)((tu + 1) * a.H + h) * 4u) | kill : kOut;
+        __builtin_amdgcn_sched_barrier(0);
+        sld[slot] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(bL.r, (int)o0, 0, 0));
+        sgm[slot] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(bG.r, (int)o0, 0, 0));
+        sldn[slot] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(bL.r, (int)o1, 0, 0));
+        sbn[slot] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(bE.r, (int)o1, 0, 0));
         if constexpr (ROT) {
 #pragma unroll
-            for (int i = 0; i < APL; ++i)
-                sth[slot][i] = pk_ok ? thp[(size_t)(t0 + APL * hf + i) * th_step + pk] : 0.0f;
+            for (int i = 0; i < APL; ++i) {
+                const uint32_t ot = ((uint32_t)(((t0 + APL * hf + i) * a.H + h) * NP2 + pk) * 4u) | kill | pk_kill;
+                sth[slot][i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(bT.r, (int)ot, 0, 0));
+            }
         }
+        __builtin_amdgcn_sched_barrier(0);
     };
 
     floatx4 acc[4][4];
@@ -2679,16 +2702,23 @@ __global__ __launch_bounds__(kSegThreads, 3) void k_seg_trap(Args a) {
     };
     // blocks from the quarter's last to its first (register and table slots
     // alternate)
+    // (blocks before the first read zeros: their staging leaves S and the
+    // angle unchanged)
     int kb = nblk - 1;
-    load(0, kb);
+    load_ops(0, kb);
+    load_par(0, kb);
+    load_par(1, kb - 1);
     stage(0);
+    load_par(0, kb - 2);
     for (; kb >= 1; kb -= 2) {
-        load(1, kb - 1);
+        load_ops(1, kb - 1);
         mult(0);
         stage(1);
-        if (kb >= 2) load(0, kb - 2);
+        load_par(1, kb - 3);
+        load_ops(0, kb - 2);
         mult(1);
-        if (kb >= 2) stage(0);
+        stage(0);
+        load_par(0, kb - 4);
     }
     if (kb == 0) mult(0);
 
