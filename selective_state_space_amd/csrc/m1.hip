@@ -371,12 +371,15 @@ __global__ __launch_bounds__(256) void k_m1_scan_w(
     const uint32_t xo = V16 ? (uint32_t)(((lane >> 2) * D + c0 + 4 * (lane & 3)) * 4)
                             : (uint32_t)(((lane >> 4) * D + c0 + (lane & 15)) * 4);
     const uint32_t bo = (uint32_t)(BW * lane);
+    // byte offset of this lane's output (step q of a group, channel c) relative
+    // to the group's first step; channels past D store past the buffer
+    const uint32_t yl = cok ? (uint32_t)(q * D + c) * 4u : 0x80000000u;
     // tiles of this wave's sequence block: kb0 .. kb1 - 1
     const int ntiles = (L + T - 1) / T;
     const int kb0 = blocks ? jb * sq.blk_tiles : 0;
     const int kb1 = blocks ? min(ntiles, kb0 + sq.blk_tiles) : ntiles;
     auto dma = [&](int k, lds_f* dst) __attribute__((always_inline)) {
-        const int t0 = k * T;
+        const int t0 = __builtin_amdgcn_readfirstlane(k * T);   // uniform: scalar offsets
         // copies of tiles past the block read zeros without touching memory (the
         // copy count stays fixed, so the waits stay exact)
         const uint32_t kill = k < kb1 ? 0u : 0x80000000u;
@@ -580,7 +583,9 @@ __global__ __launch_bounds__(256) void k_m1_scan_w(
                 kk = fmaf(Dv, g.xs, kk) * g.gate;
             else
                 kk = fmaf(Dv, g.xs, kk);
-            const uint32_t off = cok ? (uint32_t)((t0 + 4 * i + q) * D + c) * 4u : 0x80000000u;
+            // the lane's part of the offset is fixed; the group's step adds a
+            // uniform term (steps past the sequence land past the buffer)
+            const uint32_t off = yl + (uint32_t)((t0 + 4 * i) * D) * 4u;
             __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(kk), by.r, off, 0, 0);
             // fused: the next group's prologue, a group ahead of its use, so that
             // its dependent chain overlaps this group's recurrence
