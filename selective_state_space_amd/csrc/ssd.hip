@@ -186,21 +186,6 @@ __device__ __forceinline__ float bload<bf16>(const Buf& b, int e) {
     return __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(b.r, e * 2, 0, 0) << 16);
 }
 
-template <typename T>
-__device__ __forceinline__ float4 bload4(const Buf& b, int e);
-template <>
-__device__ __forceinline__ float4 bload4<float>(const Buf& b, int e) {
-    uintx4 u = __builtin_amdgcn_raw_buffer_load_b128(b.r, e * 4, 0, 0);
-    return make_float4(__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z),
-                       __uint_as_float(u.w));
-}
-template <>
-__device__ __forceinline__ float4 bload4<bf16>(const Buf& b, int e) {
-    uintx2 u = __builtin_amdgcn_raw_buffer_load_b64(b.r, e * 2, 0, 0);
-    return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
-                       __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
-}
-
 
 // CNT contiguous elements starting at element e, widened to fp32.
 template <typename IO, int CNT>
